@@ -1,0 +1,326 @@
+/*
+ * lsh_oracle.c -- plain double-precision CPU oracle for the forward pass of
+ * Reformer's LSH attention.
+ *
+ * TEST INFRASTRUCTURE. Only the test-suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library. The GPU library
+ * never calls it and shares no code, header or table with it.
+ *
+ * Every step follows the method as the source pages state it, in their order,
+ * with no blocking, fusion or reordering of the arithmetic. All arithmetic is
+ * in IEEE double; inputs arrive already widened to double (bf16 and fp32
+ * values widen exactly). Parallelism (OpenMP) is only over independent units
+ * (token, segment, head) and never changes any unit's arithmetic.
+ *
+ * Sources, cited by page and section:
+ *   [GLOSSARY]  ultralytics.com glossary entry "Reformer", section
+ *               "Atenção LSH": angular LSH -- multiply by a random matrix R,
+ *               bucket = index of the largest entry of [xR, -xR]; sort tokens
+ *               by bucket, cut the sorted sequence into equal blocks, each
+ *               token attends within its own block and the one before it;
+ *               several hash rounds in parallel. Its worked example uses
+ *               R of shape [rounds, dim, n_buckets/2] and torch's argmax
+ *               over the concatenation [proj, -proj].
+ *   [WALKTHRU]  twgreatdaily.com walkthrough of the ICLR 2020 paper, section
+ *               "1 LSH Attention": attention restricted to a set P_i through a
+ *               mask over a larger set, shared Q = K, sort by bucket and then
+ *               by position inside the bucket, chunks of m consecutive sorted
+ *               items where a chunk looks back exactly one chunk, and
+ *               multi-round hashing whose attended set is the union over the
+ *               rounds' sets.
+ *   [SCHOLAR]   ai-scholar.tech summary, section "Transformerの問題点とは":
+ *               scaled dot-product attention with the 1/sqrt(d_k) factor;
+ *               section "・LSH Attention": Q = K, bucket, sort, equal chunks,
+ *               attend own chunk and the preceding one.
+ *
+ * Readings where the pages are silent (each is listed with its reason in the
+ * design notes):
+ *   - keys are the queries themselves, not normalised;
+ *   - a query may not attend to itself unless nothing else is valid: its own
+ *     score is lowered by ORACLE_SELF_PENALTY;
+ *   - causal masking compares original positions (key position <= query
+ *     position);
+ *   - chunk 0 has no look-back and windows never wrap or cross rounds;
+ *   - rounds are combined with weights exp(lse_r - logsumexp_r lse_r), with
+ *     no de-duplication of keys seen in several rounds;
+ *   - ties in the argmax go to the first (lowest) index, as torch's argmax.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_SELF_PENALTY 1.0e5
+
+/* ------------------------------------------------------------------------ */
+/* O1. Angular LSH ([GLOSSARY] "Atenção LSH"; [WALKTHRU] "1 LSH Attention"   */
+/* for the different hash function per round).                              */
+/*                                                                           */
+/*   x        [n, d]             token vectors (one (batch, head) slice or    */
+/*                               any list of tokens)                          */
+/*   R        [n_hashes, d, n_buckets/2]   one random matrix per round        */
+/*   buckets  [n_hashes, n]      out: first index of the max of [xR, -xR]     */
+/*   margin   [n_hashes, n]      out (may be NULL): max minus the largest     */
+/*                               entry at any other index (0 on exact ties)   */
+/* ------------------------------------------------------------------------ */
+int oracle_hash(const double *x, int64_t n, int d, const double *R,
+                int n_hashes, int n_buckets, int32_t *buckets, double *margin)
+{
+    if (n_buckets < 2 || (n_buckets % 2) != 0 || d < 1 || n_hashes < 1 || n < 0)
+        return -1;
+    const int half = n_buckets / 2;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *c = (double *)malloc(sizeof(double) * (size_t)n_buckets);
+        if (!c) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(static) collapse(2)
+        for (int r = 0; r < n_hashes; ++r) {
+            for (int64_t i = 0; i < n; ++i) {
+                if (!c) continue;
+                const double *xi = x + i * d;
+                /* projection p = x R_r, then the concatenation [p, -p] */
+                for (int b = 0; b < half; ++b) {
+                    double p = 0.0;
+                    for (int k = 0; k < d; ++k)
+                        p += xi[k] * R[((int64_t)r * d + k) * half + b];
+                    c[b] = p;
+                    c[b + half] = -p;
+                }
+                /* first index attaining the maximum */
+                int best = 0;
+                for (int b = 1; b < n_buckets; ++b)
+                    if (c[b] > c[best]) best = b;
+                buckets[(int64_t)r * n + i] = best;
+                if (margin) {
+                    double second = -INFINITY;
+                    for (int b = 0; b < n_buckets; ++b)
+                        if (b != best && c[b] > second) second = c[b];
+                    margin[(int64_t)r * n + i] = c[best] - second;
+                }
+            }
+        }
+        free(c);
+    }
+    return failed ? -2 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O2. Sort of one round's positions by (bucket, position)                   */
+/* ([WALKTHRU] "1 LSH Attention": two-level sort, bucket first, then the     */
+/* position inside the bucket; [SCHOLAR] "・LSH Attention").                */
+/*                                                                           */
+/*   bucket [L]   bucket of each position                                    */
+/*   perm   [L]   out: perm[s] = position held by sorted slot s              */
+/*   inv    [L]   out: inv[i]  = sorted slot of position i                   */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    int32_t bucket;
+    int32_t pos;
+} oracle_key;
+
+static int oracle_key_cmp(const void *pa, const void *pb)
+{
+    const oracle_key *a = (const oracle_key *)pa, *b = (const oracle_key *)pb;
+    if (a->bucket != b->bucket) return a->bucket < b->bucket ? -1 : 1;
+    if (a->pos != b->pos) return a->pos < b->pos ? -1 : 1;
+    return 0;
+}
+
+int oracle_sort(const int32_t *bucket, int64_t L, int32_t *perm, int32_t *inv)
+{
+    if (L < 0) return -1;
+    if (L == 0) return 0;
+    oracle_key *k = (oracle_key *)malloc(sizeof(oracle_key) * (size_t)L);
+    if (!k) return -2;
+    for (int64_t i = 0; i < L; ++i) {
+        k[i].bucket = bucket[i];
+        k[i].pos = (int32_t)i;
+    }
+    /* (bucket, position) pairs are all distinct, so the order is total */
+    qsort(k, (size_t)L, sizeof(oracle_key), oracle_key_cmp);
+    for (int64_t s = 0; s < L; ++s) {
+        perm[s] = k[s].pos;
+        inv[k[s].pos] = (int32_t)s;
+    }
+    free(k);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O3 + O4. Chunked attention of one (batch, head, round) segment.           */
+/* Windows: [WALKTHRU] "1 LSH Attention" (chunks of m sorted items, each     */
+/* looking back one chunk); [GLOSSARY] "Atenção LSH" (own block and the      */
+/* previous block). Scores and restriction: [SCHOLAR] (1/sqrt(d_k) scaling),  */
+/* [WALKTHRU] (only keys in the query's bucket take part; the rest are       */
+/* masked out of a larger candidate set; keys are the queries, Q = K).       */
+/*                                                                           */
+/*   x, v    [L, d]  by original position                                    */
+/*   bucket  [L]     this round's bucket of each position                    */
+/*   perm    [L]     this round's sorted order (from O2)                     */
+/*   slots   list of query slots to compute (NULL: all L)                    */
+/*   o       [L, d]  out, by sorted slot: softmax-weighted sum of v           */
+/*   lse     [L]     out, by sorted slot: natural-log partition function     */
+/* ------------------------------------------------------------------------ */
+int oracle_attend(const double *x, const double *v, int64_t L, int d,
+                  const int32_t *bucket, const int32_t *perm, int m, int causal,
+                  const int64_t *slots, int64_t n_slots, double *o, double *lse)
+{
+    if (L < 0 || d < 1 || m < 1 || (L % m) != 0) return -1;
+    const int64_t n_q = slots ? n_slots : L;
+    const double scale = 1.0 / sqrt((double)d);
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *score = (double *)malloc(sizeof(double) * 2 * (size_t)m);
+        int *valid = (int *)malloc(sizeof(int) * 2 * (size_t)m);
+        if (!score || !valid) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 64)
+        for (int64_t q = 0; q < n_q; ++q) {
+            if (!score || !valid) continue;
+            const int64_t s = slots ? slots[q] : q;
+            const int64_t i = perm[s];
+            const int64_t c = s / m;
+            const int64_t t0 = (c > 0) ? (c - 1) * m : 0; /* no look-back for chunk 0 */
+            const int64_t t1 = (c + 1) * m;                /* end of the query's own chunk */
+            const double *xi = x + i * d;
+            double mx = -INFINITY;
+            for (int64_t t = t0; t < t1; ++t) {
+                const int64_t j = perm[t];
+                int ok = (bucket[j] == bucket[i]) && (!causal || j <= i);
+                valid[t - t0] = ok;
+                if (!ok) continue;
+                const double *xj = x + j * d;
+                double dot = 0.0;
+                for (int k = 0; k < d; ++k) dot += xi[k] * xj[k];
+                double sc = dot * scale;
+                if (j == i) sc -= ORACLE_SELF_PENALTY;
+                score[t - t0] = sc;
+                if (sc > mx) mx = sc;
+            }
+            /* self is always valid, so the set is never empty */
+            double sum = 0.0;
+            for (int64_t t = t0; t < t1; ++t)
+                if (valid[t - t0]) sum += exp(score[t - t0] - mx);
+            const double l = mx + log(sum);
+            lse[s] = l;
+            double *os = o + s * d;
+            for (int k = 0; k < d; ++k) os[k] = 0.0;
+            for (int64_t t = t0; t < t1; ++t) {
+                if (!valid[t - t0]) continue;
+                const double w = exp(score[t - t0] - l);
+                const double *vj = v + (int64_t)perm[t] * d;
+                for (int k = 0; k < d; ++k) os[k] += w * vj[k];
+            }
+        }
+        free(score);
+        free(valid);
+    }
+    return failed ? -2 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* O5. Un-sort and combine the rounds of one (batch, head)                   */
+/* ([WALKTHRU] "1 LSH Attention": the attended set is the union of the       */
+/* rounds' sets; each round's partial result is weighted by its share of     */
+/* the total partition function, i.e. by exp(lse_r - logsumexp over r)).     */
+/*                                                                           */
+/*   o    [n_hashes, L, d]  per-round outputs by sorted slot                 */
+/*   lse  [n_hashes, L]     per-round log partition functions by sorted slot */
+/*   inv  [n_hashes, L]     per-round slot of each position                  */
+/*   toks list of positions to compute (NULL: all L)                         */
+/*   out  [L, d]            out, by original position                        */
+/* ------------------------------------------------------------------------ */
+int oracle_combine(const double *o, const double *lse, const int32_t *inv,
+                   int n_hashes, int64_t L, int d, const int64_t *toks,
+                   int64_t n_toks, double *out)
+{
+    if (n_hashes < 1 || L < 0 || d < 1) return -1;
+    const int64_t n_t = toks ? n_toks : L;
+#pragma omp parallel for schedule(static)
+    for (int64_t q = 0; q < n_t; ++q) {
+        const int64_t i = toks ? toks[q] : q;
+        double mx = -INFINITY;
+        for (int r = 0; r < n_hashes; ++r) {
+            const double l = lse[(int64_t)r * L + inv[(int64_t)r * L + i]];
+            if (l > mx) mx = l;
+        }
+        double sum = 0.0;
+        for (int r = 0; r < n_hashes; ++r)
+            sum += exp(lse[(int64_t)r * L + inv[(int64_t)r * L + i]] - mx);
+        const double z = mx + log(sum);
+        double *oi = out + i * d;
+        for (int k = 0; k < d; ++k) oi[k] = 0.0;
+        for (int r = 0; r < n_hashes; ++r) {
+            const int64_t s = inv[(int64_t)r * L + i];
+            const double w = exp(lse[(int64_t)r * L + s] - z);
+            const double *os = o + ((int64_t)r * L + s) * d;
+            for (int k = 0; k < d; ++k) oi[k] += w * os[k];
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Whole forward over [B, H]: O1 -> O2 -> O3/O4 -> O5 for every (b, h).      */
+/*                                                                           */
+/*   qk, v  [B, H, L, d]                                                     */
+/*   R      [n_hashes, d, n_buckets/2] shared by every batch and head        */
+/*   out    [B, H, L, d]                                                     */
+/*   optional outputs (each may be NULL):                                    */
+/*     buckets, perm, inv [B, H, n_hashes, L]; margin, lse [B, H, n_hashes, L]*/
+/*     o_sorted           [B, H, n_hashes, L, d]                             */
+/* ------------------------------------------------------------------------ */
+int oracle_forward(const double *qk, const double *v, const double *R,
+                   int B, int H, int64_t L, int d, int n_buckets, int n_hashes,
+                   int chunk_len, int causal, double *out, int32_t *buckets_out,
+                   double *margin_out, int32_t *perm_out, int32_t *inv_out,
+                   double *o_sorted_out, double *lse_out)
+{
+    if (B < 0 || H < 0 || L < 0 || d < 1 || n_hashes < 1 || chunk_len < 1 ||
+        n_buckets < 2 || (n_buckets % 2) != 0 || (L % chunk_len) != 0)
+        return -1;
+    const int64_t seg = (int64_t)n_hashes * L;
+    for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
+        const double *x = qk + bh * L * d;
+        const double *vv = v + bh * L * d;
+        int32_t *bk = (int32_t *)malloc(sizeof(int32_t) * (size_t)(seg ? seg : 1));
+        int32_t *pm = (int32_t *)malloc(sizeof(int32_t) * (size_t)(seg ? seg : 1));
+        int32_t *iv = (int32_t *)malloc(sizeof(int32_t) * (size_t)(seg ? seg : 1));
+        double *mg = (double *)malloc(sizeof(double) * (size_t)(seg ? seg : 1));
+        double *ls = (double *)malloc(sizeof(double) * (size_t)(seg ? seg : 1));
+        double *os = (double *)malloc(sizeof(double) * (size_t)(seg ? seg * d : 1));
+        int rc = (bk && pm && iv && mg && ls && os) ? 0 : -2;
+        if (!rc) rc = oracle_hash(x, L, d, R, n_hashes, n_buckets, bk, mg);
+        for (int r = 0; !rc && r < n_hashes; ++r)
+            rc = oracle_sort(bk + r * L, L, pm + r * L, iv + r * L);
+        for (int r = 0; !rc && r < n_hashes; ++r)
+            rc = oracle_attend(x, vv, L, d, bk + r * L, pm + r * L, chunk_len,
+                               causal, NULL, 0, os + r * L * d, ls + r * L);
+        if (!rc)
+            rc = oracle_combine(os, ls, iv, n_hashes, L, d, NULL, 0, out + bh * L * d);
+        if (!rc) {
+            if (buckets_out) memcpy(buckets_out + bh * seg, bk, sizeof(int32_t) * (size_t)seg);
+            if (margin_out) memcpy(margin_out + bh * seg, mg, sizeof(double) * (size_t)seg);
+            if (perm_out) memcpy(perm_out + bh * seg, pm, sizeof(int32_t) * (size_t)seg);
+            if (inv_out) memcpy(inv_out + bh * seg, iv, sizeof(int32_t) * (size_t)seg);
+            if (lse_out) memcpy(lse_out + bh * seg, ls, sizeof(double) * (size_t)seg);
+            if (o_sorted_out)
+                memcpy(o_sorted_out + bh * seg * d, os, sizeof(double) * (size_t)(seg * d));
+        }
+        free(bk);
+        free(pm);
+        free(iv);
+        free(mg);
+        free(ls);
+        free(os);
+        if (rc) return rc;
+    }
+    return 0;
+}

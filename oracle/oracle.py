@@ -1,0 +1,182 @@
+"""Python access to the double-precision C oracle in ``lsh_oracle.c``.
+
+TEST INFRASTRUCTURE. Only the test-suite, the smoke check and the
+CPU-baseline leg of the benchmark import this module. The GPU library never
+does, and this module imports nothing from it.
+
+Each function widens its inputs to float64 (bf16 and fp32 values widen
+exactly), calls the matching C routine and returns NumPy arrays. The steps and
+their sources are documented in ``lsh_oracle.c``:
+
+  hash     -- O1, angular LSH: first argmax of [xR, -xR] per round
+  sort     -- O2, positions ordered by (bucket, position)
+  attend   -- O3/O4, chunk windows (own chunk + previous one), same-bucket,
+              causal and self rules, softmax in double
+  combine  -- O5, un-sort and logsumexp-weighted sum over rounds
+  forward  -- O1..O5 over every (batch, head)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import pathlib
+import subprocess
+
+import numpy as np
+
+_DIR = pathlib.Path(__file__).resolve().parent
+_SRC = _DIR / "lsh_oracle.c"
+_LIB_PATH = _DIR / "liblsh_oracle.so"
+_lib = None
+
+_f64p = ctypes.POINTER(ctypes.c_double)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+
+
+def build(force: bool = True) -> pathlib.Path:
+    """Compile the oracle with gcc (plain -O2, no FMA contraction, OpenMP)."""
+    if force or not _LIB_PATH.exists():
+        tmp = _LIB_PATH.with_suffix(".so.tmp")
+        cmd = ["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math",
+               "-fopenmp", "-shared", "-fPIC", str(_SRC), "-o", str(tmp), "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not _LIB_PATH.exists():
+            build(force=False)
+        lib = ctypes.CDLL(str(_LIB_PATH))
+        lib.oracle_hash.argtypes = [_f64p, ctypes.c_int64, ctypes.c_int, _f64p, ctypes.c_int,
+                                    ctypes.c_int, _i32p, _f64p]
+        lib.oracle_sort.argtypes = [_i32p, ctypes.c_int64, _i32p, _i32p]
+        lib.oracle_attend.argtypes = [_f64p, _f64p, ctypes.c_int64, ctypes.c_int, _i32p, _i32p,
+                                      ctypes.c_int, ctypes.c_int, _i64p, ctypes.c_int64, _f64p,
+                                      _f64p]
+        lib.oracle_combine.argtypes = [_f64p, _f64p, _i32p, ctypes.c_int, ctypes.c_int64,
+                                       ctypes.c_int, _i64p, ctypes.c_int64, _f64p]
+        lib.oracle_forward.argtypes = [_f64p, _f64p, _f64p, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_int, _f64p, _i32p, _f64p, _i32p,
+                                       _i32p, _f64p, _f64p]
+        for fn in (lib.oracle_hash, lib.oracle_sort, lib.oracle_attend, lib.oracle_combine,
+                   lib.oracle_forward):
+            fn.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _p(a, t):
+    return None if a is None else a.ctypes.data_as(t)
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise ValueError(f"oracle {what} failed with code {rc}")
+
+
+def hash(x, R, n_buckets: int):
+    """O1. x: [n, d]; R: [n_hashes, d, n_buckets/2].
+
+    Returns (buckets [n_hashes, n] int32, margin [n_hashes, n] float64).
+    """
+    x = _f64(x)
+    R = _f64(R)
+    n, d = x.shape
+    nh = R.shape[0]
+    if R.shape != (nh, d, n_buckets // 2):
+        raise ValueError(f"R has shape {R.shape}, expected {(nh, d, n_buckets // 2)}")
+    buckets = np.empty((nh, n), np.int32)
+    margin = np.empty((nh, n), np.float64)
+    _check(_load().oracle_hash(_p(x, _f64p), n, d, _p(R, _f64p), nh, n_buckets,
+                               _p(buckets, _i32p), _p(margin, _f64p)), "hash")
+    return buckets, margin
+
+
+def sort(bucket):
+    """O2. bucket: [L] for one round. Returns (perm [L], inv [L]) int32."""
+    bucket = _i32(bucket)
+    L = bucket.shape[0]
+    perm = np.empty(L, np.int32)
+    inv = np.empty(L, np.int32)
+    _check(_load().oracle_sort(_p(bucket, _i32p), L, _p(perm, _i32p), _p(inv, _i32p)), "sort")
+    return perm, inv
+
+
+def attend(x, v, bucket, perm, chunk_len: int, causal: bool, slots=None):
+    """O3/O4 for one round. x, v: [L, d]; bucket, perm: [L].
+
+    Returns (o [L, d], lse [L]) indexed by sorted slot. With ``slots`` only
+    those query slots are computed; the other rows are NaN.
+    """
+    x = _f64(x)
+    v = _f64(v)
+    bucket = _i32(bucket)
+    perm = _i32(perm)
+    L, d = x.shape
+    o = np.full((L, d), np.nan)
+    lse = np.full(L, np.nan)
+    sl = None if slots is None else np.ascontiguousarray(np.asarray(slots, dtype=np.int64))
+    _check(_load().oracle_attend(_p(x, _f64p), _p(v, _f64p), L, d, _p(bucket, _i32p),
+                                 _p(perm, _i32p), chunk_len, int(bool(causal)), _p(sl, _i64p),
+                                 0 if sl is None else sl.shape[0], _p(o, _f64p), _p(lse, _f64p)),
+           "attend")
+    return o, lse
+
+
+def combine(o, lse, inv, tokens=None):
+    """O5 for one (batch, head). o: [nh, L, d]; lse, inv: [nh, L].
+
+    Returns out [L, d] by original position (NaN rows outside ``tokens``).
+    """
+    o = _f64(o)
+    lse = _f64(lse)
+    inv = _i32(inv)
+    nh, L, d = o.shape
+    out = np.full((L, d), np.nan)
+    tk = None if tokens is None else np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))
+    _check(_load().oracle_combine(_p(o, _f64p), _p(lse, _f64p), _p(inv, _i32p), nh, L, d,
+                                  _p(tk, _i64p), 0 if tk is None else tk.shape[0],
+                                  _p(out, _f64p)), "combine")
+    return out
+
+
+def forward(qk, v, R, n_buckets: int, chunk_len: int, causal: bool, return_all: bool = False):
+    """O1..O5 over every (batch, head). qk, v: [B, H, L, d]; R: [nh, d, nb/2].
+
+    Returns out [B, H, L, d]; with ``return_all`` also a dict of the
+    intermediate results (buckets, margin, perm, inv, lse, o_sorted).
+    """
+    qk = _f64(qk)
+    v = _f64(v)
+    R = _f64(R)
+    B, H, L, d = qk.shape
+    nh = R.shape[0]
+    out = np.empty((B, H, L, d))
+    extra = {}
+    if return_all:
+        extra = dict(buckets=np.empty((B, H, nh, L), np.int32),
+                     margin=np.empty((B, H, nh, L)),
+                     perm=np.empty((B, H, nh, L), np.int32),
+                     inv=np.empty((B, H, nh, L), np.int32),
+                     o_sorted=np.empty((B, H, nh, L, d)),
+                     lse=np.empty((B, H, nh, L)))
+    g = extra.get
+    _check(_load().oracle_forward(_p(qk, _f64p), _p(v, _f64p), _p(R, _f64p), B, H, L, d,
+                                  n_buckets, nh, chunk_len, int(bool(causal)), _p(out, _f64p),
+                                  _p(g("buckets"), _i32p), _p(g("margin"), _f64p),
+                                  _p(g("perm"), _i32p), _p(g("inv"), _i32p),
+                                  _p(g("o_sorted"), _f64p), _p(g("lse"), _f64p)), "forward")
+    return (out, extra) if return_all else out

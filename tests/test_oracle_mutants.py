@@ -1,0 +1,106 @@
+"""The pins must catch plausible slips in the oracle.
+
+Each case plants one mistake in a temporary copy of ``oracle/lsh_oracle.c``
+(the committed oracle is never touched), builds it with gcc, and runs every
+pin of ``test_oracle_pins.py`` against it: at least one pin must fail.
+"""
+from __future__ import annotations
+
+import importlib.util
+import inspect
+import pathlib
+import subprocess
+
+import numpy as np
+import pytest
+
+from tests import test_oracle_pins as pins
+
+ROOT = pathlib.Path(__file__).resolve().parent.parent
+SRC = ROOT / "oracle" / "lsh_oracle.c"
+PY = ROOT / "oracle" / "oracle.py"
+
+MUTANTS = {
+    "halves_swapped": ("c[b] = p;\n                    c[b + half] = -p;",
+                       "c[b] = -p;\n                    c[b + half] = p;"),
+    "last_index_ties": ("if (c[b] > c[best]) best = b;", "if (c[b] >= c[best]) best = b;"),
+    "R_transposed": ("R[((int64_t)r * d + k) * half + b]", "R[((int64_t)r * half + b) * d + k]"),
+    "sort_position_descending": ("if (a->pos != b->pos) return a->pos < b->pos ? -1 : 1;",
+                                 "if (a->pos != b->pos) return a->pos < b->pos ? 1 : -1;"),
+    # windows stay within 2m slots so the mutant never writes past its buffers
+    "next_chunk_instead_of_previous": (
+        "const int64_t t0 = (c > 0) ? (c - 1) * m : 0; /* no look-back for chunk 0 */\n"
+        "            const int64_t t1 = (c + 1) * m; ",
+        "const int64_t t0 = c * m;\n"
+        "            const int64_t t1 = ((c + 2) * m < L) ? (c + 2) * m : L; "),
+    "own_chunk_only": ("const int64_t t0 = (c > 0) ? (c - 1) * m : 0;",
+                       "const int64_t t0 = c * m;"),
+    "scale_one_over_d": ("const double scale = 1.0 / sqrt((double)d);",
+                         "const double scale = 1.0 / (double)d;"),
+    "no_self_penalty": ("if (j == i) sc -= ORACLE_SELF_PENALTY;", "(void)0;"),
+    "causal_strict": ("(!causal || j <= i)", "(!causal || j < i)"),
+    "causal_ignored": ("(!causal || j <= i)", "(1)"),
+    "no_bucket_mask": ("int ok = (bucket[j] == bucket[i]) &&", "int ok = 1 &&"),
+    "uniform_round_weights": ("const double w = exp(lse[(int64_t)r * L + s] - z);",
+                              "const double w = 1.0 / n_hashes;"),
+    "combine_wrong_round_slot": ("const int64_t s = inv[(int64_t)r * L + i];",
+                                 "const int64_t s = inv[i];"),
+    "lse_log2": ("const double l = mx + log(sum);", "const double l = mx + log2(sum);"),
+}
+
+
+def _pin_calls():
+    calls = []
+    for name, fn in inspect.getmembers(pins, inspect.isfunction):
+        if not name.startswith("test_"):
+            continue
+        params = list(inspect.signature(fn).parameters)
+        if "oracle_mod" not in params:
+            continue
+        grid = [{}]
+        for mark in getattr(fn, "pytestmark", []):
+            if mark.name == "parametrize":
+                argname, values = mark.args
+                grid = [dict(g, **{argname: v}) for g in grid for v in values]
+        for kw in grid:
+            calls.append((name, fn, kw))
+    return calls
+
+
+def _load_mutant(tmp: pathlib.Path, name: str, old: str, new: str):
+    text = SRC.read_text()
+    assert text.count(old) >= 1, f"mutation {name}: pattern not found"
+    mutated = text.replace(old, new)
+    c_path = tmp / f"{name}.c"
+    so_path = tmp / f"lib{name}.so"
+    c_path.write_text(mutated)
+    subprocess.run(["gcc", "-std=c11", "-O1", "-ffp-contract=off", "-fopenmp", "-shared",
+                    "-fPIC", str(c_path), "-o", str(so_path), "-lm"], check=True)
+    spec = importlib.util.spec_from_file_location(f"oracle_mutant_{name}", PY)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    mod._LIB_PATH = so_path
+    mod._lib = None
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    mod = _load_mutant(tmp_path, name, old, new)
+    caught = []
+    with np.errstate(all="ignore"):
+        for pin, fn, kw in _pin_calls():
+            try:
+                fn(mod, **kw)
+            except (AssertionError, ValueError, FloatingPointError, IndexError):
+                caught.append(pin)
+    assert caught, f"no pin catches the planted mistake {name!r}"
+
+
+def test_unmutated_copy_passes(tmp_path):
+    """Control: the copy-and-build route itself does not make pins fail."""
+    mod = _load_mutant(tmp_path, "control", "#define ORACLE_SELF_PENALTY 1.0e5",
+                       "#define ORACLE_SELF_PENALTY 1.0e5")
+    for pin, fn, kw in _pin_calls():
+        fn(mod, **kw)

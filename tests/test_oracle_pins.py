@@ -1,0 +1,343 @@
+"""Pins of the CPU oracle against facts fixed outside it (no GPU needed).
+
+Each test names what it pins. Together they are chosen so that a plausible
+slip anywhere in the oracle (a swapped half of [xR, -xR], last-index ties, a
+transposed R, an unstable sort, a window that looks ahead or wraps, a wrong
+score scale, a missing self or causal rule, uniform instead of logsumexp
+round weights) makes at least one of them fail; ``test_oracle_mutants.py``
+checks that claim by planting such slips in a copy of the oracle.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from tests import brute
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------------- O1 hash
+
+def test_hash_glossary_worked_example(oracle_mod):
+    """P-a: the glossary page's printed result of its seeded hashing example."""
+    g = _golden("glossary_hash_example.json")
+    x, R = workloads.glossary_hash_example()
+    buckets, _ = oracle_mod.hash(x, R, 16)
+    assert buckets.shape == (g["rounds"], 3)
+    for row, name in ((1, "near"), (2, "far")):
+        cos = float(x[0] @ x[row] / np.linalg.norm(x[0]) / np.linalg.norm(x[row]))
+        assert f"{cos:.2f}" == g["printed"][name]["cosine"]
+        # the example averages a float32 tensor, so the share is a float32
+        share = float((buckets[:, row] == buckets[:, 0]).astype(np.float32).mean(dtype=np.float32))
+        assert f"{share:.0%}" == g["printed"][name]["shared_rounds"]
+
+
+def test_hash_two_axis_closed_form(oracle_mod):
+    """With R = [e0, e1] the bucket is the first index of max(x0, x1, -x0, -x1):
+    pins the [p, -p] order and the R layout [round, dim, bucket]."""
+    R = np.zeros((1, 3, 2))
+    R[0, 0, 0] = 1.0   # column 0 reads x[0]
+    R[0, 2, 1] = 1.0   # column 1 reads x[2] (dim 1 is ignored)
+    cases = {
+        (3.0, 9.0, 1.0): 0, (1.0, 9.0, 3.0): 1, (-3.0, 9.0, 1.0): 2, (1.0, 9.0, -3.0): 3,
+        (-1.0, -9.0, -3.0): 3, (2.0, 0.0, -2.0): 0, (-2.0, 0.0, 2.0): 1, (0.0, 5.0, 0.0): 0,
+        (-2.0, 0.0, -2.0): 2,
+    }
+    x = np.array(list(cases.keys()))
+    b, margin = oracle_mod.hash(x, R, 4)
+    assert b[0].tolist() == list(cases.values())
+    # exact ties have zero margin
+    assert margin[0, 5] == 0.0 and margin[0, 6] == 0.0 and margin[0, 7] == 0.0
+
+
+def test_hash_sign_hashing_nb2(oracle_mod):
+    """P-b: with two buckets the hash is random-hyperplane sign hashing
+    (rdly.ru summary, section on LSH): bucket 0 iff x.r >= 0, and the collision
+    rate of two vectors at angle theta is 1 - theta/pi (Charikar, 2002)."""
+    rng = np.random.default_rng(7)
+    d = 16
+    x = rng.standard_normal((50, d))
+    R = rng.standard_normal((4, d, 1))
+    b, _ = oracle_mod.hash(x, R, 2)
+    expect = np.where(np.einsum("nd,rd->rn", x, R[:, :, 0]) >= 0, 0, 1)
+    assert np.array_equal(b, expect)
+
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    w = rng.standard_normal(d)
+    w -= (w @ u) * u
+    w /= np.linalg.norm(w)
+    rounds = 20000
+    R = rng.standard_normal((rounds, d, 1))
+    for theta in (0.3, math.pi / 3, 2.0):
+        y = math.cos(theta) * u + math.sin(theta) * w
+        b, _ = oracle_mod.hash(np.stack([u, y]), R, 2)
+        rate = float((b[:, 0] == b[:, 1]).mean())
+        assert abs(rate - (1 - theta / math.pi)) < 0.015
+
+
+def test_hash_invariants(oracle_mod):
+    """P-c: range, invariance to positive scaling, and h(-x) = h(x) + nb/2 mod nb."""
+    rng = np.random.default_rng(11)
+    nb, d = 32, 24
+    x = rng.standard_normal((300, d))
+    R = rng.standard_normal((3, d, nb // 2))
+    b, margin = oracle_mod.hash(x, R, nb)
+    assert b.min() >= 0 and b.max() < nb
+    safe = margin > 1e-9
+    for alpha in (2.0, 0.5, 3.7):
+        b2, _ = oracle_mod.hash(alpha * x, R, nb)
+        assert np.array_equal(b2[safe], b[safe])
+    bn, _ = oracle_mod.hash(-x, R, nb)
+    assert np.array_equal(bn[safe], ((b + nb // 2) % nb)[safe])
+    # every bucket is used over many random rotations
+    b_many, _ = oracle_mod.hash(x[:1], rng.standard_normal((4000, d, nb // 2)), nb)
+    counts = np.bincount(b_many[:, 0], minlength=nb)
+    assert counts.min() > 60
+
+
+def test_hash_zero_vector_and_margin(oracle_mod):
+    """Ties go to the first index: the zero vector hashes to bucket 0 with margin 0;
+    the margin equals the gap between the two largest entries of [p, -p]."""
+    rng = np.random.default_rng(3)
+    R = rng.standard_normal((2, 8, 5))
+    x = np.vstack([np.zeros(8), rng.standard_normal(8)])
+    b, margin = oracle_mod.hash(x, R, 10)
+    assert b[:, 0].tolist() == [0, 0] and margin[:, 0].tolist() == [0.0, 0.0]
+    for r in range(2):
+        p = x[1] @ R[r]
+        c = np.sort(np.concatenate([p, -p]))
+        assert margin[r, 1] == pytest.approx(c[-1] - c[-2], rel=1e-12)
+
+
+# --------------------------------------------------------------------------- O2 sort
+
+def test_sort_matches_stable_argsort(oracle_mod):
+    """P-d: the two-level sort equals numpy's stable argsort of the buckets."""
+    rng = np.random.default_rng(5)
+    for L, nb in ((1, 2), (17, 4), (1000, 16), (4096, 1024)):
+        bucket = rng.integers(0, nb, L).astype(np.int32)
+        perm, inv = oracle_mod.sort(bucket)
+        assert np.array_equal(perm, np.argsort(bucket, kind="stable"))
+        assert np.array_equal(inv[perm], np.arange(L))
+        key = bucket[perm].astype(np.int64) * L + perm
+        assert np.all(np.diff(key) > 0)
+
+
+def test_sort_skewed_and_constant(oracle_mod):
+    rng = np.random.default_rng(6)
+    bucket = np.where(rng.random(5000) < 0.7, 3, rng.integers(0, 64, 5000)).astype(np.int32)
+    perm, _ = oracle_mod.sort(bucket)
+    assert np.array_equal(perm, np.argsort(bucket, kind="stable"))
+    perm, inv = oracle_mod.sort(np.zeros(300, np.int32))
+    assert np.array_equal(perm, np.arange(300)) and np.array_equal(inv, np.arange(300))
+
+
+# --------------------------------------------------------------------------- O3/O4 attend
+
+def _one_round(oracle_mod, x, v, R, nb, m, causal):
+    b, _ = oracle_mod.hash(x, R, nb)
+    perm, inv = oracle_mod.sort(b[0])
+    o, lse = oracle_mod.attend(x, v, b[0], perm, m, causal)
+    return b[0], perm, inv, o, lse
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_attend_one_chunk_is_dense_same_bucket(oracle_mod, causal):
+    """P-e: with one chunk spanning the sequence, the output equals dense
+    softmax attention restricted to same-bucket pairs."""
+    rng = np.random.default_rng(21)
+    L, d, nb = 48, 8, 4
+    x = rng.standard_normal((L, d))
+    v = rng.standard_normal((L, d))
+    R = rng.standard_normal((1, d, nb // 2))
+    b, perm, inv, o, _ = _one_round(oracle_mod, x, v, R, nb, L, causal)
+    ref = brute.dense_same_bucket(x, v, b, causal)
+    np.testing.assert_allclose(o[inv], ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_attend_single_bucket_matches_torch_sdpa(oracle_mod, causal):
+    """P-f: all tokens in one bucket and one chunk: plain softmax attention with
+    scale 1/sqrt(d) (ai-scholar.tech summary, section 'Transformerの問題点とは'),
+    checked against torch's scaled_dot_product_attention with an additive mask."""
+    rng = np.random.default_rng(22)
+    L, d = 40, 16
+    x = rng.standard_normal((L, d))
+    x[:, 0] = np.abs(x[:, 0]) + 0.1
+    v = rng.standard_normal((L, d))
+    R = np.zeros((1, d, 1))
+    R[0, 0, 0] = 1.0
+    b, perm, inv, o, lse = _one_round(oracle_mod, x, v, R, 2, L, causal)
+    assert np.all(b == 0)
+    mask = torch.zeros(L, L, dtype=torch.float64)
+    mask.fill_diagonal_(-brute.SELF_PENALTY)
+    if causal:
+        mask.masked_fill_(torch.ones(L, L, dtype=torch.bool).triu(1), float("-inf"))
+    xt = torch.from_numpy(x)[None, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        xt, xt, torch.from_numpy(v)[None, None], attn_mask=mask)[0, 0].numpy()
+    np.testing.assert_allclose(o[inv], ref, rtol=1e-10, atol=1e-12)
+    # lse is the natural-log partition function of the masked scores
+    s = (x @ x.T) / math.sqrt(d) + mask.numpy()
+    ref_lse = np.log(np.exp(s - s.max(1, keepdims=True)).sum(1)) + s.max(1)
+    np.testing.assert_allclose(lse[inv], ref_lse, rtol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_attend_hand_built_windows(oracle_mod, causal):
+    """P-l: look-back of exactly one chunk, no look-ahead, no wrap, bucket masking
+    and the self rule, on a hand-derived 8-token case."""
+    g = _golden("chunk_window_cases.json")
+    x = np.array(g["x"], np.float64)
+    R = np.array(g["R"], np.float64)
+    rng = np.random.default_rng(23)
+    v = rng.standard_normal((8, 2))
+    b, perm, inv, o, _ = _one_round(oracle_mod, x, v, R, 2, 2, causal)
+    assert b.tolist() == g["buckets"]
+    assert perm.tolist() == g["perm"]
+    keys = g["keys"]["causal" if causal else "non_causal"]
+    for pos, ks in keys.items():
+        np.testing.assert_allclose(o[inv[int(pos)]], v[ks].mean(0), rtol=1e-12, atol=1e-12)
+
+
+def test_attend_slots_subset_matches_full(oracle_mod):
+    rng = np.random.default_rng(24)
+    L, d, nb, m = 256, 8, 8, 32
+    x = rng.standard_normal((L, d))
+    v = rng.standard_normal((L, d))
+    R = rng.standard_normal((1, d, nb // 2))
+    b, perm, inv, o, lse = _one_round(oracle_mod, x, v, R, nb, m, True)
+    slots = np.array([0, 5, 31, 32, 100, 255])
+    o2, lse2 = oracle_mod.attend(x, v, b, perm, m, True, slots=slots)
+    assert np.array_equal(o2[slots], o[slots]) and np.array_equal(lse2[slots], lse[slots])
+    assert np.isnan(o2[1]).all()
+
+
+# --------------------------------------------------------------------------- O5 + forward
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("m", [4, 8])
+def test_forward_matches_multiset_closed_form(oracle_mod, causal, m):
+    """P-g: logsumexp-weighted rounds == one softmax over the multiset of hits."""
+    rng = np.random.default_rng(31 + m)
+    L, d, nb, nh = 32, 8, 4, 3
+    qk = rng.standard_normal((1, 1, L, d))
+    v = rng.standard_normal((1, 1, L, d))
+    R = rng.standard_normal((nh, d, nb // 2))
+    out, extra = oracle_mod.forward(qk, v, R, nb, m, causal, return_all=True)
+    ref = brute.multiset_closed_form(qk[0, 0], v[0, 0], extra["buckets"][0, 0], m, causal)
+    np.testing.assert_allclose(out[0, 0], ref, rtol=1e-11, atol=1e-12)
+
+
+def test_forward_identity_values_give_weights(oracle_mod):
+    """P-h: with V = I the output rows are the attention weights: non-negative,
+    summing to one, zero above the diagonal under causality, zero on pairs
+    that never share a bucket and a window."""
+    rng = np.random.default_rng(41)
+    L, d, nb, nh, m = 16, 16, 4, 2, 4
+    qk = rng.standard_normal((1, 1, L, d))
+    v = np.eye(L)[None, None]
+    R = rng.standard_normal((nh, d, nb // 2))
+    out, extra = oracle_mod.forward(qk, v, R, nb, m, True, return_all=True)
+    w = out[0, 0]
+    assert np.all(w >= 0)
+    # self-only rounds carry scores near -1e5, whose ulp (~1.5e-11) bounds the rounding
+    np.testing.assert_allclose(w.sum(1), 1.0, rtol=1e-10)
+    assert np.all(np.triu(w, 1) == 0)
+    c = brute.multiplicity(extra["buckets"][0, 0], m, True)
+    assert np.all(w[c == 0] == 0)
+    np.testing.assert_allclose(w, brute.attention_weights(qk[0, 0], extra["buckets"][0, 0], m, True),
+                               rtol=1e-11, atol=1e-14)
+
+
+def test_forward_convexity(oracle_mod):
+    """P-i: constant V gives that constant; every output lies between the
+    column-wise min and max of V."""
+    rng = np.random.default_rng(42)
+    B, H, L, d, nb, nh, m = 2, 2, 64, 8, 8, 3, 8
+    qk = rng.standard_normal((B, H, L, d))
+    R = rng.standard_normal((nh, d, nb // 2))
+    vc = np.broadcast_to(rng.standard_normal(d), (B, H, L, d)).copy()
+    out = oracle_mod.forward(qk, vc, R, nb, m, True)
+    np.testing.assert_allclose(out, vc, rtol=1e-10)
+    v = rng.standard_normal((B, H, L, d))
+    out = oracle_mod.forward(qk, v, R, nb, m, False)
+    lo = v.min(axis=2, keepdims=True)
+    hi = v.max(axis=2, keepdims=True)
+    assert np.all(out >= lo - 1e-10) and np.all(out <= hi + 1e-10)
+
+
+def test_forward_round_symmetry(oracle_mod):
+    """P-j: permuting the rounds leaves the output unchanged; duplicating every
+    round gives the same output as the rounds once."""
+    rng = np.random.default_rng(43)
+    L, d, nb, nh, m = 64, 8, 8, 3, 8
+    qk = rng.standard_normal((1, 2, L, d))
+    v = rng.standard_normal((1, 2, L, d))
+    R = rng.standard_normal((nh, d, nb // 2))
+    out = oracle_mod.forward(qk, v, R, nb, m, True)
+    out_p = oracle_mod.forward(qk, v, R[[2, 0, 1]], nb, m, True)
+    np.testing.assert_allclose(out_p, out, rtol=1e-10, atol=1e-10)
+    out_d = oracle_mod.forward(qk, v, np.concatenate([R, R]), nb, m, True)
+    np.testing.assert_allclose(out_d, out, rtol=1e-10, atol=1e-10)
+
+
+def test_forward_causal_first_row_is_v0(oracle_mod):
+    """P-k: under causality position 0 only sees itself, in every round."""
+    rng = np.random.default_rng(44)
+    qk = rng.standard_normal((2, 3, 32, 8))
+    v = rng.standard_normal((2, 3, 32, 8))
+    R = rng.standard_normal((4, 8, 4))
+    out = oracle_mod.forward(qk, v, R, 8, 4, True)
+    np.testing.assert_allclose(out[:, :, 0], v[:, :, 0], rtol=1e-10)
+
+
+def test_forward_steps_compose(oracle_mod):
+    """forward() is exactly hash -> sort -> attend -> combine per (batch, head)."""
+    rng = np.random.default_rng(45)
+    B, H, L, d, nb, nh, m = 1, 2, 128, 8, 16, 2, 16
+    qk = rng.standard_normal((B, H, L, d))
+    v = rng.standard_normal((B, H, L, d))
+    R = rng.standard_normal((nh, d, nb // 2))
+    out, ex = oracle_mod.forward(qk, v, R, nb, m, True, return_all=True)
+    for h in range(H):
+        b, _ = oracle_mod.hash(qk[0, h], R, nb)
+        assert np.array_equal(b, ex["buckets"][0, h])
+        os_, ls_, iv_ = [], [], []
+        for r in range(nh):
+            perm, inv = oracle_mod.sort(b[r])
+            assert np.array_equal(perm, ex["perm"][0, h, r])
+            o, lse = oracle_mod.attend(qk[0, h], v[0, h], b[r], perm, m, True)
+            os_.append(o), ls_.append(lse), iv_.append(inv)
+        comb = oracle_mod.combine(np.stack(os_), np.stack(ls_), np.stack(iv_))
+        assert np.array_equal(comb, out[0, h])
+
+
+def test_forward_empty_and_errors(oracle_mod):
+    R = np.ones((1, 4, 2))
+    out = oracle_mod.forward(np.zeros((1, 1, 0, 4)), np.zeros((1, 1, 0, 4)), R, 4, 2, True)
+    assert out.shape == (1, 1, 0, 4)
+    with pytest.raises(ValueError):
+        oracle_mod.forward(np.zeros((1, 1, 6, 4)), np.zeros((1, 1, 6, 4)), R, 4, 4, True)
+    with pytest.raises(ValueError):
+        oracle_mod.hash(np.zeros((3, 4)), np.ones((1, 4, 2)), 3)
+
+
+def test_forward_bf16_inputs_widen_exactly():
+    """The generator's bf16 rounding agrees with torch's conversion."""
+    a = np.random.default_rng(1).standard_normal(100000).astype(np.float32) * 7
+    ref = torch.from_numpy(a).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(workloads.round_to_bf16(a), ref)
