@@ -1,0 +1,181 @@
+"""Benchmark of the LSH-attention forward on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one lsh_attention_fwd (hash -> sort -> chunk attention -> combine)
+over one batch of synthetic input already resident in HBM. The default
+workload is the 64K-token, 8-head, 8-round configuration (d_head 128,
+n_buckets 1024, chunk 64, causal, bf16). Prints one JSON line.
+
+The per-kernel durations come from lsh_attention_fwd_timed (HIP events recorded
+after every kernel on the launch stream), averaged over the timed repeats; the
+roofline object reports the longest-running kernel against MI355X's published
+peak for the bound that limits it, with that kernel's algorithmic work.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "LSH-attention fwd tokens/s at L=64K, 8 heads, 8 hashes; % of MFMA/HBM roofline"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 (vector / matrix), TFLOP/s
+
+
+def algorithmic_work(w):
+    """Per-launch algorithmic flops or HBM bytes of each kernel, by kernel name.
+
+    Returns {name: (bound, amount, unit)} with bound 'mfma' (amount in flops) or
+    'hbm' (amount in bytes)."""
+    e = 2 if w.dtype == "bf16" else 4
+    T = w.B * w.H * w.L                      # token-heads
+    TR = T * w.n_hashes                      # token-rounds
+    d, half = w.d, w.n_buckets // 2
+    hash_flops = 2.0 * d * half * w.n_hashes * T
+    return {
+        # projection x R for every round: one fp32-exact contraction, evaluated
+        # on bf16 matrix cores (two passes of the split R; counted once)
+        "hash_fast_mfma": ("mfma", hash_flops, "flop"),
+        "hash_fast_fp32": ("alu", hash_flops, "flop"),
+        # read buckets twice (count, scatter), write perm and inv
+        "sort_count": ("hbm", 4.0 * TR, "B"),
+        "sort_scatter": ("hbm", 12.0 * TR, "B"),
+        # gather qk and v rows once per token-round, read perm and the bucket,
+        # write o (fp32) and lse
+        "attend_fp32": ("hbm", TR * (2 * d * e + 8 + 4 * d + 4), "B"),
+        "attend_mfma": ("hbm", TR * (2 * d * e + 8 + 4 * d + 4), "B"),
+        # read every round's o row, lse and inv; write out
+        "combine": ("hbm", T * (w.n_hashes * (4 * d + 8) + d * e), "B"),
+    }
+
+
+def cpu_baseline(w, qk, v, R, target_s=20.0):
+    """Times the oracle (as it is) on a bounded sample: one (batch, head) slice
+    of the workload with every round, L shortened until one run is ~target_s."""
+    import numpy as np
+
+    from oracle import oracle
+
+    L = w.L
+    while True:
+        t0 = time.perf_counter()
+        oracle.forward(qk[:1, :1, :L], v[:1, :1, :L], R, w.n_buckets, w.chunk_len, w.causal)
+        dt = time.perf_counter() - t0
+        if dt * 4 <= target_s or L <= 4 * w.chunk_len:
+            break
+        L //= 2
+    _ = np
+    return {"value": L / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"1 of {w.B * w.H} (batch, head) slices, first {L} positions, all "
+                      f"{w.n_hashes} rounds; {dt:.1f} s for one forward"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the forward shards "
+                                   "by (batch, head) with no communication, so --gpus must be 1"}))
+        return 2
+
+    import numpy as np
+    import torch
+
+    import lsh_attention_fp32_amd as lsh
+    import workloads
+
+    name = args.workload or workloads.HEADLINE
+    w = workloads.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    lsh.load_library()
+    qk, v, R = workloads.make_inputs(w)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    qk_t = torch.from_numpy(qk).to(dev, dt)
+    v_t = torch.from_numpy(v).to(dev, dt)
+    R_t = torch.from_numpy(R).to(dev)
+    shape = lsh.shape_of(qk_t, w.n_buckets, w.n_hashes, w.chunk_len, w.causal)
+    ws = torch.empty(lsh.lsh_workspace_size("fwd", shape), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(qk_t)
+
+    for _ in range(args.warmup):
+        lsh.lsh_attention_fwd(qk_t, v_t, R_t, shape, out, ws)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        lsh.lsh_attention_fwd(qk_t, v_t, R_t, shape, out, ws)
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = start.elapsed_time(stop) / args.steps
+    refined = int(ws[:4].view(torch.int32).item())
+
+    # per-kernel durations, same launches with an event after each kernel
+    reps = max(3, min(args.steps, 10))
+    acc = {}
+    for _ in range(reps):
+        for kname, ms in lsh.lsh_attention_fwd_timed(qk_t, v_t, R_t, shape, out, ws):
+            acc.setdefault(kname, []).append(ms)
+    kernels = {k: float(np.mean(x)) for k, x in acc.items()}
+    work = algorithmic_work(w)
+    dominant = max((k for k in kernels if k in work), key=lambda k: kernels[k])
+    bound, amount, _unit = work[dominant]
+    secs = kernels[dominant] / 1e3
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": amount / secs / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    elif bound == "mfma":
+        roof = {"bound": "mfma", "achieved": amount / secs / 1e12, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "alu", "achieved": amount / secs / 1e12, "peak": PEAK_FP32_TFLOPS,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = dominant
+    roof["kernel_ms"] = kernels[dominant]
+
+    tokens = w.B * w.L
+    line = {
+        "metric": METRIC,
+        "value": tokens / (ms_per_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "fp32",
+        "data": "synthetic",
+        "config": {"workload": name, "B": w.B, "H": w.H, "L": w.L, "d_head": w.d,
+                   "n_buckets": w.n_buckets, "n_hashes": w.n_hashes, "chunk_len": w.chunk_len,
+                   "causal": w.causal, "qk_dist": w.qk_dist},
+        "roofline": roof,
+        "kernels_ms": kernels,
+        "hash_redecided": refined,
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, qk, v, R)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,159 @@
+/*
+ * lsh_attn.h -- C ABI of the MI355X (gfx950) LSH-attention forward pass.
+ *
+ * The method is the LSH attention of "Reformer: The Efficient Transformer"
+ * (ICLR 2020) as the following pages describe it:
+ *   - ultralytics.com glossary entry "Reformer", section "Atenção LSH":
+ *     angular LSH (bucket = index of the largest entry of [xR, -xR] for a
+ *     random matrix R of shape [rounds, d, n_buckets/2]), sort by bucket,
+ *     equal blocks, attention within the own block and the previous block,
+ *     several hash rounds in parallel;
+ *   - twgreatdaily.com walkthrough, section "1 LSH Attention": shared
+ *     queries and keys (Q = K), attention restricted to the query's bucket by
+ *     masking a larger candidate set, sort by bucket then position, chunks
+ *     of m sorted items that look back one chunk, multi-round hashing whose
+ *     attended set is the union of the rounds' sets;
+ *   - ai-scholar.tech summary, section "Transformerの問題点とは": scaled
+ *     dot-product attention, softmax(q k^T / sqrt(d_k)) v.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument is caller-owned DEVICE memory (hipMalloc'd or a
+ *    torch CUDA tensor), except `shape`, which is a host struct, and the host
+ *    outputs of lsh_workspace_size / lsh_attention_fwd_timed. The library
+ *    never allocates or frees device memory and keeps no pointer after a call.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Work is enqueued asynchronously on it; inputs must stay valid and
+ *    unmodified until that work completes. Only lsh_attention_fwd_timed waits.
+ *  - Tensors are dense row-major with these shapes (T = B*H):
+ *      qk, v, out      [B, H, L, d]            dtype = shape->dtype
+ *      R               [n_hashes, d, n_buckets/2]   float32, shared by all
+ *                                              batches and heads
+ *      buckets         [B, H, n_hashes, L]     int32, by original position
+ *      perm            [B, H, n_hashes, L]     int32, perm[s] = position in
+ *                                              sorted slot s of that round
+ *      inv             [B, H, n_hashes, L]     int32, inv[i] = slot of position i
+ *      lse_sorted      [B, H, n_hashes, L]     float32, by sorted slot
+ *      o_sorted        [B, H, n_hashes, L, d]  float32, by sorted slot
+ *  - Inputs must be finite.
+ *  - Return value: LSH_OK (0) or a negative LSH_ERR_* code. Argument checks
+ *    run on the host before anything is enqueued; on any error nothing has
+ *    been enqueued unless the code is LSH_ERR_HIP, and lsh_last_error()
+ *    describes the failure. Output contents are unspecified after an error.
+ *  - An empty problem (B, H or L equal to 0) is valid and enqueues nothing.
+ *  - Calls on different streams that share a workspace race; give each
+ *    concurrent call its own workspace.
+ */
+#ifndef LSH_ATTN_H
+#define LSH_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { LSH_F32 = 0, LSH_BF16 = 1 };
+
+enum {
+    LSH_OK = 0,
+    LSH_ERR_ARG = -1,         /* an argument breaks the method's constraints    */
+    LSH_ERR_WORKSPACE = -2,   /* workspace pointer NULL or smaller than needed  */
+    LSH_ERR_HIP = -3,         /* a HIP launch or runtime call failed            */
+    LSH_ERR_UNSUPPORTED = -4  /* valid for the method but not built (e.g. d)    */
+};
+
+/* Problem description (host struct, read during the call only).
+ *   B, H, L, d   batch, heads, sequence length, head dimension. d must be 64
+ *                or 128 (others: LSH_ERR_UNSUPPORTED).
+ *   n_buckets    even, 2 <= n_buckets <= 4096.
+ *   n_hashes     hash rounds, 1 <= n_hashes <= 4096.
+ *   chunk_len    m >= 1 with L % m == 0 (the pages cut the sorted sequence
+ *                into equal chunks).
+ *   causal       0 or 1: key position must not exceed the query position.
+ *   dtype        LSH_F32 or LSH_BF16 for qk, v and out.
+ * Also required: B*H*n_hashes*L < 2^31. */
+typedef struct lsh_shape {
+    int32_t B, H, L, d;
+    int32_t n_buckets, n_hashes, chunk_len, causal;
+    int32_t dtype;
+} lsh_shape_t;
+
+/* Bytes of workspace needed by `stage` ("hash", "sort" or "fwd") for `shape`,
+ * written to *bytes (host). Returns LSH_ERR_ARG for an unknown stage or an
+ * invalid shape. */
+int lsh_workspace_size(const char *stage, const lsh_shape_t *shape, size_t *bytes);
+
+/* Step 1 -- angular LSH over n_hashes rounds (glossary "Atenção LSH";
+ * walkthrough "1 LSH Attention" for one hash function per round).
+ * buckets[b,h,r,i] = first index of the maximum of [x R_r, -x R_r] where
+ * x = qk[b,h,i,:], evaluated as if in exact arithmetic: a fast pass on the
+ * matrix cores bounds its own rounding error, and every token-round whose
+ * decision that bound cannot certify is recomputed in double precision, so
+ * the result matches an exact evaluation except where two entries differ by
+ * less than about 1e-12 relative. Deterministic.
+ *   qk       [B,H,L,d] shape->dtype      R   [n_hashes, d, n_buckets/2] f32
+ *   buckets  [B,H,n_hashes,L] int32 (out)
+ *   ws       device workspace of at least lsh_workspace_size("hash") bytes.
+ *            After the work completes, the first int32 of ws holds the number
+ *            of token-rounds that were re-decided in double precision. */
+int lsh_hash(const void *qk, const float *R, const lsh_shape_t *shape, int32_t *buckets,
+             void *ws, size_t ws_bytes, void *stream);
+
+/* Step 2 -- stable sort of each (b,h,round) by (bucket, position)
+ * (walkthrough "1 LSH Attention": sort by bucket, then by position inside the
+ * bucket). Bit-exact and deterministic.
+ *   buckets  [B,H,n_hashes,L] int32, values in [0, n_buckets)
+ *   perm     [B,H,n_hashes,L] int32 (out)   inv [B,H,n_hashes,L] int32 (out)
+ *   ws       at least lsh_workspace_size("sort") bytes. */
+int lsh_sort(const int32_t *buckets, const lsh_shape_t *shape, int32_t *perm, int32_t *inv,
+             void *ws, size_t ws_bytes, void *stream);
+
+/* Steps 3+4 -- gather into sorted order and chunked attention (walkthrough
+ * "1 LSH Attention"; glossary "Atenção LSH"). For sorted slot s of a round,
+ * with chunk c = s / m, the candidate keys are the slots of chunks c-1 and c
+ * of the same round (chunk 0 has no look-back). Key position j is valid for
+ * query position i when bucket(j) == bucket(i) and, if causal, j <= i. The
+ * score is (x_i . x_j) / sqrt(d), lowered by 1e5 when j == i, so a query
+ * attends to itself only when no other key is valid. Softmax in float32.
+ *   qk, v     [B,H,L,d] shape->dtype
+ *   buckets   [B,H,n_hashes,L] int32     perm [B,H,n_hashes,L] int32
+ *   o_sorted  [B,H,n_hashes,L,d] f32 (out)
+ *   lse_sorted[B,H,n_hashes,L] f32 (out), natural-log partition function. */
+int lsh_chunk_attend(const void *qk, const void *v, const int32_t *buckets, const int32_t *perm,
+                     const lsh_shape_t *shape, float *o_sorted, float *lse_sorted, void *stream);
+
+/* Step 5 -- un-sort and combine the rounds (walkthrough "1 LSH Attention":
+ * multi-round hashing attends to the union of the rounds' sets). For each
+ * position i: l_r = lse_sorted[r, inv_r[i]], Z = logsumexp_r l_r,
+ * out_i = sum_r exp(l_r - Z) * o_sorted[r, inv_r[i]].
+ *   o_sorted [B,H,n_hashes,L,d] f32   lse_sorted [B,H,n_hashes,L] f32
+ *   inv      [B,H,n_hashes,L] int32   out [B,H,L,d] shape->dtype (out) */
+int lsh_unsort_combine(const float *o_sorted, const float *lse_sorted, const int32_t *inv,
+                       const lsh_shape_t *shape, void *out, void *stream);
+
+/* Whole forward: steps 1-5 on `stream`, intermediates in `ws`
+ * (at least lsh_workspace_size("fwd") bytes; the first int32 of ws is the
+ * hash stage's re-decided count, as in lsh_hash). */
+int lsh_attention_fwd(const void *qk, const void *v, const float *R, const lsh_shape_t *shape,
+                      void *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Diagnostic twin of lsh_attention_fwd: the same launches, with a HIP event
+ * recorded after each kernel. It waits for the stream, then writes each
+ * kernel's duration in milliseconds to kernel_ms[k] and its static name to
+ * kernel_names[k] (both host arrays of max_kernels entries; names may be
+ * NULL) and the number of kernels to *n_kernels. */
+int lsh_attention_fwd_timed(const void *qk, const void *v, const float *R,
+                            const lsh_shape_t *shape, void *out, void *ws, size_t ws_bytes,
+                            void *stream, float *kernel_ms, const char **kernel_names,
+                            int32_t max_kernels, int32_t *n_kernels);
+
+/* Message for the last error on the calling thread ("" if none). */
+const char *lsh_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LSH_ATTN_H */

@@ -1,0 +1,37 @@
+"""LSH attention (Reformer) forward pass for AMD MI355X (gfx950).
+
+A thin ctypes binding over the C ABI of ``liblsh_attn.so`` (declared in
+``include/lsh_attn.h``). Every step runs in the library's HIP kernels; this
+module only checks tensors and passes their device pointers and torch's
+current HIP stream. It raises if the library has not been built -- there is
+no other implementation to fall back to.
+
+Low-level functions keep the C names and argument order (tensors in place of
+pointers): ``lsh_workspace_size``, ``lsh_hash``, ``lsh_sort``,
+``lsh_chunk_attend``, ``lsh_unsort_combine``, ``lsh_attention_fwd``,
+``lsh_attention_fwd_timed``. The allocating helpers ``hash``, ``sort``,
+``chunk_attend``, ``unsort_combine`` and ``attention_fwd`` create the outputs
+and workspaces with torch.
+"""
+from ._binding import (  # noqa: F401
+    LSH_BF16,
+    LSH_F32,
+    LshError,
+    Shape,
+    attention_fwd,
+    chunk_attend,
+    hash,
+    library_path,
+    load_library,
+    lsh_attention_fwd,
+    lsh_attention_fwd_timed,
+    lsh_chunk_attend,
+    lsh_hash,
+    lsh_last_error,
+    lsh_sort,
+    lsh_unsort_combine,
+    lsh_workspace_size,
+    shape_of,
+    sort,
+    unsort_combine,
+)

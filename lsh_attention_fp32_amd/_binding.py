@@ -1,0 +1,218 @@
+"""ctypes binding of ``liblsh_attn.so`` (argument marshalling only)."""
+from __future__ import annotations
+
+import ctypes
+import pathlib
+
+import torch
+
+LSH_F32 = 0
+LSH_BF16 = 1
+_DTYPES = {torch.float32: LSH_F32, torch.bfloat16: LSH_BF16}
+_ERRORS = {-1: "LSH_ERR_ARG", -2: "LSH_ERR_WORKSPACE", -3: "LSH_ERR_HIP", -4: "LSH_ERR_UNSUPPORTED"}
+
+_PKG = pathlib.Path(__file__).resolve().parent
+_LIB_PATH = _PKG / "liblsh_attn.so"
+_lib = None
+
+
+class LshError(RuntimeError):
+    def __init__(self, code: int, fn: str, msg: str):
+        super().__init__(f"{fn}: {_ERRORS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class Shape(ctypes.Structure):
+    """Mirror of ``lsh_shape_t``."""
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("L", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("n_buckets", ctypes.c_int32),
+                ("n_hashes", ctypes.c_int32), ("chunk_len", ctypes.c_int32),
+                ("causal", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+    def __repr__(self):
+        return "Shape(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
+def library_path() -> pathlib.Path:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not _LIB_PATH.exists():
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it first "
+                           "(python -m lsh_attention_fp32_amd.build or __graft_entry__.build())")
+    lib = ctypes.CDLL(str(_LIB_PATH))
+    vp, sz, i32, sp = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.POINTER(Shape)
+    lib.lsh_workspace_size.argtypes = [ctypes.c_char_p, sp, ctypes.POINTER(sz)]
+    lib.lsh_hash.argtypes = [vp, vp, sp, vp, vp, sz, vp]
+    lib.lsh_sort.argtypes = [vp, sp, vp, vp, vp, sz, vp]
+    lib.lsh_chunk_attend.argtypes = [vp, vp, vp, vp, sp, vp, vp, vp]
+    lib.lsh_unsort_combine.argtypes = [vp, vp, vp, sp, vp, vp]
+    lib.lsh_attention_fwd.argtypes = [vp, vp, vp, sp, vp, vp, sz, vp]
+    lib.lsh_attention_fwd_timed.argtypes = [vp, vp, vp, sp, vp, vp, sz, vp,
+                                            ctypes.POINTER(ctypes.c_float),
+                                            ctypes.POINTER(ctypes.c_char_p), i32,
+                                            ctypes.POINTER(i32)]
+    for name in ("lsh_workspace_size", "lsh_hash", "lsh_sort", "lsh_chunk_attend",
+                 "lsh_unsort_combine", "lsh_attention_fwd", "lsh_attention_fwd_timed"):
+        getattr(lib, name).restype = ctypes.c_int
+    lib.lsh_last_error.argtypes = []
+    lib.lsh_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def lsh_last_error() -> str:
+    return load_library().lsh_last_error().decode()
+
+
+def _check(rc: int, fn: str) -> None:
+    if rc != 0:
+        raise LshError(rc, fn, lsh_last_error())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch tensor")
+    if t.numel() and not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr()) if t.numel() else None
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def shape_of(qk: torch.Tensor, n_buckets: int, n_hashes: int, chunk_len: int,
+             causal: bool) -> Shape:
+    """Shape for qk of shape [B, H, L, d] (float32 or bfloat16)."""
+    if qk.dim() != 4:
+        raise ValueError(f"qk must be [B, H, L, d], got {tuple(qk.shape)}")
+    if qk.dtype not in _DTYPES:
+        raise ValueError(f"qk dtype must be float32 or bfloat16, got {qk.dtype}")
+    B, H, L, d = qk.shape
+    return Shape(B, H, L, d, n_buckets, n_hashes, chunk_len, int(bool(causal)), _DTYPES[qk.dtype])
+
+
+# ---------------------------------------------------------------- C-named calls
+
+def lsh_workspace_size(stage: str, shape: Shape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().lsh_workspace_size(stage.encode(), ctypes.byref(shape), ctypes.byref(n)),
+           "lsh_workspace_size")
+    return n.value
+
+
+def lsh_hash(qk, R, shape: Shape, buckets, ws, stream=None) -> None:
+    _check(load_library().lsh_hash(_ptr(qk), _ptr(R), ctypes.byref(shape), _ptr(buckets), _ptr(ws),
+                                   ws.numel() * ws.element_size() if ws is not None else 0,
+                                   _stream(stream)), "lsh_hash")
+
+
+def lsh_sort(buckets, shape: Shape, perm, inv, ws, stream=None) -> None:
+    _check(load_library().lsh_sort(_ptr(buckets), ctypes.byref(shape), _ptr(perm), _ptr(inv),
+                                   _ptr(ws),
+                                   ws.numel() * ws.element_size() if ws is not None else 0,
+                                   _stream(stream)), "lsh_sort")
+
+
+def lsh_chunk_attend(qk, v, buckets, perm, shape: Shape, o_sorted, lse_sorted, stream=None) -> None:
+    _check(load_library().lsh_chunk_attend(_ptr(qk), _ptr(v), _ptr(buckets), _ptr(perm),
+                                           ctypes.byref(shape), _ptr(o_sorted), _ptr(lse_sorted),
+                                           _stream(stream)), "lsh_chunk_attend")
+
+
+def lsh_unsort_combine(o_sorted, lse_sorted, inv, shape: Shape, out, stream=None) -> None:
+    _check(load_library().lsh_unsort_combine(_ptr(o_sorted), _ptr(lse_sorted), _ptr(inv),
+                                             ctypes.byref(shape), _ptr(out), _stream(stream)),
+           "lsh_unsort_combine")
+
+
+def lsh_attention_fwd(qk, v, R, shape: Shape, out, ws, stream=None) -> None:
+    _check(load_library().lsh_attention_fwd(_ptr(qk), _ptr(v), _ptr(R), ctypes.byref(shape),
+                                            _ptr(out), _ptr(ws),
+                                            ws.numel() * ws.element_size() if ws is not None else 0,
+                                            _stream(stream)), "lsh_attention_fwd")
+
+
+def lsh_attention_fwd_timed(qk, v, R, shape: Shape, out, ws, stream=None, max_kernels: int = 16):
+    """Runs the forward and returns [(kernel name, milliseconds), ...] (waits for the GPU)."""
+    ms = (ctypes.c_float * max_kernels)()
+    names = (ctypes.c_char_p * max_kernels)()
+    n = ctypes.c_int32(0)
+    _check(load_library().lsh_attention_fwd_timed(
+        _ptr(qk), _ptr(v), _ptr(R), ctypes.byref(shape), _ptr(out), _ptr(ws),
+        ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream), ms, names,
+        max_kernels, ctypes.byref(n)), "lsh_attention_fwd_timed")
+    return [(names[k].decode(), float(ms[k])) for k in range(n.value)]
+
+
+# ---------------------------------------------------------------- allocating helpers
+
+def _workspace(stage: str, shape: Shape, device) -> torch.Tensor:
+    return torch.empty(max(1, lsh_workspace_size(stage, shape)), dtype=torch.uint8, device=device)
+
+
+def _rounds_shape(shape: Shape):
+    return (shape.B, shape.H, shape.n_hashes, shape.L)
+
+
+def hash(qk, R, n_buckets: int, ws=None, stream=None):
+    """Returns (buckets [B,H,n_hashes,L] int32, number of token-rounds re-decided in fp64)."""
+    shape = shape_of(qk, n_buckets, R.shape[0], 1, False)
+    shape.chunk_len = max(1, shape.L)  # any divisor of L: the hash does not use it
+    buckets = torch.empty(_rounds_shape(shape), dtype=torch.int32, device=qk.device)
+    ws = _workspace("hash", shape, qk.device) if ws is None else ws
+    lsh_hash(qk, R, shape, buckets, ws, stream)
+    refined = int(ws[:4].view(torch.int32).item()) if shape.B * shape.H * shape.L else 0
+    return buckets, refined
+
+
+def sort(buckets, n_buckets: int, stream=None):
+    """Returns (perm, inv), both [B,H,n_hashes,L] int32."""
+    B, H, nh, L = buckets.shape
+    shape = Shape(B, H, L, 64, n_buckets, nh, max(1, L), 0, LSH_BF16)
+    perm = torch.empty_like(buckets)
+    inv = torch.empty_like(buckets)
+    ws = _workspace("sort", shape, buckets.device)
+    lsh_sort(buckets, shape, perm, inv, ws, stream)
+    return perm, inv
+
+
+def chunk_attend(qk, v, buckets, perm, n_buckets: int, chunk_len: int, causal: bool, stream=None):
+    """Returns (o_sorted [B,H,n_hashes,L,d] f32, lse_sorted [B,H,n_hashes,L] f32)."""
+    shape = shape_of(qk, n_buckets, buckets.shape[2], chunk_len, causal)
+    o = torch.empty(_rounds_shape(shape) + (shape.d,), dtype=torch.float32, device=qk.device)
+    lse = torch.empty(_rounds_shape(shape), dtype=torch.float32, device=qk.device)
+    lsh_chunk_attend(qk, v, buckets, perm, shape, o, lse, stream)
+    return o, lse
+
+
+def unsort_combine(o_sorted, lse_sorted, inv, dtype=torch.bfloat16, stream=None):
+    """Returns out [B,H,L,d] in ``dtype``."""
+    B, H, nh, L, d = o_sorted.shape
+    shape = Shape(B, H, L, d, 2, nh, max(1, L), 0, _DTYPES[dtype])
+    out = torch.empty((B, H, L, d), dtype=dtype, device=o_sorted.device)
+    lsh_unsort_combine(o_sorted, lse_sorted, inv, shape, out, stream)
+    return out
+
+
+def attention_fwd(qk, v, R, n_buckets: int, chunk_len: int, causal: bool, ws=None, out=None,
+                  stream=None):
+    """Whole forward; returns out [B,H,L,d] in qk's dtype."""
+    shape = shape_of(qk, n_buckets, R.shape[0], chunk_len, causal)
+    if v.shape != qk.shape or v.dtype != qk.dtype:
+        raise ValueError("v must match qk in shape and dtype")
+    out = torch.empty_like(qk) if out is None else out
+    ws = _workspace("fwd", shape, qk.device) if ws is None else ws
+    lsh_attention_fwd(qk, v, R, shape, out, ws, stream)
+    return out

@@ -1,0 +1,248 @@
+// lsh_api.hip -- the C ABI declared in include/lsh_attn.h: host-side argument
+// checks, workspace layout and launch order. Nothing here touches the device
+// before the arguments have been validated, and loading the library does not
+// initialise HIP.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "lsh_internal.h"
+
+using namespace lsh;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+    return fail(LSH_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+int validate(const lsh_shape_t* s) {
+    if (!s) return fail(LSH_ERR_ARG, "shape is NULL");
+    if (s->B < 0 || s->H < 0 || s->L < 0)
+        return fail(LSH_ERR_ARG, "negative B/H/L (%d, %d, %d)", s->B, s->H, s->L);
+    if (s->d < 1) return fail(LSH_ERR_ARG, "d must be positive (got %d)", s->d);
+    if (s->n_buckets < 2 || (s->n_buckets % 2) != 0)
+        return fail(LSH_ERR_ARG, "n_buckets must be even and >= 2 (got %d)", s->n_buckets);
+    if (s->n_buckets > kMaxBuckets)
+        return fail(LSH_ERR_UNSUPPORTED, "n_buckets above %d is not built (got %d)", kMaxBuckets,
+                    s->n_buckets);
+    if (s->n_hashes < 1 || s->n_hashes > kMaxHashes)
+        return fail(LSH_ERR_ARG, "n_hashes must be in [1, %d] (got %d)", kMaxHashes, s->n_hashes);
+    if (s->chunk_len < 1) return fail(LSH_ERR_ARG, "chunk_len must be >= 1 (got %d)", s->chunk_len);
+    if (s->L % s->chunk_len != 0)
+        return fail(LSH_ERR_ARG, "L (%d) must be a multiple of chunk_len (%d)", s->L, s->chunk_len);
+    if (s->causal != 0 && s->causal != 1)
+        return fail(LSH_ERR_ARG, "causal must be 0 or 1 (got %d)", s->causal);
+    if (s->dtype != LSH_F32 && s->dtype != LSH_BF16)
+        return fail(LSH_ERR_ARG, "dtype must be LSH_F32 or LSH_BF16 (got %d)", s->dtype);
+    if ((int64_t)s->B * s->H * s->n_hashes * s->L >= ((int64_t)1 << 31))
+        return fail(LSH_ERR_ARG, "B*H*n_hashes*L must stay below 2^31");
+    if (s->d != 64 && s->d != 128)
+        return fail(LSH_ERR_UNSUPPORTED, "head size d=%d is not built (64 or 128)", s->d);
+    return LSH_OK;
+}
+
+bool empty(const lsh_shape_t* s) { return s->B == 0 || s->H == 0 || s->L == 0; }
+
+struct FwdLayout {
+    size_t hash, sort, buckets, perm, inv, lse, o, total;
+};
+
+FwdLayout fwd_layout(const Dims& d) {
+    FwdLayout f;
+    const size_t n = (size_t)d.segs * d.L;
+    size_t off = 0;
+    f.hash = off;
+    off += align_up(hash_workspace_bytes(d), 256);
+    f.sort = off;
+    off += align_up(sort_workspace_bytes(d), 256);
+    f.buckets = off;
+    off += align_up(sizeof(int32_t) * n, 256);
+    f.perm = off;
+    off += align_up(sizeof(int32_t) * n, 256);
+    f.inv = off;
+    off += align_up(sizeof(int32_t) * n, 256);
+    f.lse = off;
+    off += align_up(sizeof(float) * n, 256);
+    f.o = off;
+    off += align_up(sizeof(float) * n * d.d, 256);
+    f.total = off;
+    return f;
+}
+
+int check_ws(const char* stage, const Dims& d, void* ws, size_t ws_bytes, size_t need) {
+    (void)d;
+    if (!ws) return fail(LSH_ERR_WORKSPACE, "%s: workspace is NULL", stage);
+    if (ws_bytes < need)
+        return fail(LSH_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", stage, ws_bytes,
+                    need);
+    return LSH_OK;
+}
+
+int run_fwd(const void* qk, const void* v, const float* R, const lsh_shape_t* shape, void* out,
+            void* ws, size_t ws_bytes, hipStream_t st, hipEvent_t* ev, int* nev,
+            const char** names) {
+    const Dims d = make_dims(*shape);
+    const FwdLayout f = fwd_layout(d);
+    int rc = check_ws("lsh_attention_fwd", d, ws, ws_bytes, f.total);
+    if (rc) return rc;
+    char* base = (char*)ws;
+    int32_t* buckets = (int32_t*)(base + f.buckets);
+    int32_t* perm = (int32_t*)(base + f.perm);
+    int32_t* inv = (int32_t*)(base + f.inv);
+    float* lse = (float*)(base + f.lse);
+    float* o = (float*)(base + f.o);
+    hipError_t e;
+    if ((e = launch_hash(qk, R, d, buckets, carve_hash_workspace(base + f.hash, d), st, ev, nev,
+                         names)) != hipSuccess)
+        return hip_fail(e, "hash");
+    if ((e = launch_sort(buckets, d, perm, inv, base + f.sort, st, ev, nev, names)) != hipSuccess)
+        return hip_fail(e, "sort");
+    if ((e = launch_attend(qk, v, buckets, perm, d, o, lse, st, ev, nev, names)) != hipSuccess)
+        return hip_fail(e, "chunk_attend");
+    if ((e = launch_combine(o, lse, inv, d, out, st, ev, nev, names)) != hipSuccess)
+        return hip_fail(e, "unsort_combine");
+    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "launch");
+    return LSH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lsh_last_error(void) { return g_err; }
+
+int lsh_workspace_size(const char* stage, const lsh_shape_t* shape, size_t* bytes) {
+    g_err[0] = 0;
+    if (!stage || !bytes) return fail(LSH_ERR_ARG, "stage and bytes must not be NULL");
+    int rc = validate(shape);
+    if (rc) return rc;
+    const Dims d = make_dims(*shape);
+    if (!strcmp(stage, "hash")) *bytes = hash_workspace_bytes(d);
+    else if (!strcmp(stage, "sort")) *bytes = sort_workspace_bytes(d);
+    else if (!strcmp(stage, "fwd")) *bytes = fwd_layout(d).total;
+    else return fail(LSH_ERR_ARG, "unknown stage '%s' (hash, sort or fwd)", stage);
+    return LSH_OK;
+}
+
+int lsh_hash(const void* qk, const float* R, const lsh_shape_t* shape, int32_t* buckets,
+             void* ws, size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    int rc = validate(shape);
+    if (rc) return rc;
+    if (empty(shape)) return LSH_OK;
+    if (!qk || !R || !buckets) return fail(LSH_ERR_ARG, "lsh_hash: NULL tensor pointer");
+    const Dims d = make_dims(*shape);
+    if ((rc = check_ws("lsh_hash", d, ws, ws_bytes, hash_workspace_bytes(d)))) return rc;
+    hipError_t e = launch_hash(qk, R, d, buckets, carve_hash_workspace(ws, d), (hipStream_t)stream,
+                               nullptr, nullptr, nullptr);
+    if (e == hipSuccess) e = hipGetLastError();
+    return e == hipSuccess ? LSH_OK : hip_fail(e, "lsh_hash");
+}
+
+int lsh_sort(const int32_t* buckets, const lsh_shape_t* shape, int32_t* perm, int32_t* inv,
+             void* ws, size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    int rc = validate(shape);
+    if (rc) return rc;
+    if (empty(shape)) return LSH_OK;
+    if (!buckets || !perm || !inv) return fail(LSH_ERR_ARG, "lsh_sort: NULL tensor pointer");
+    const Dims d = make_dims(*shape);
+    if ((rc = check_ws("lsh_sort", d, ws, ws_bytes, sort_workspace_bytes(d)))) return rc;
+    hipError_t e = launch_sort(buckets, d, perm, inv, ws, (hipStream_t)stream, nullptr, nullptr,
+                               nullptr);
+    if (e == hipSuccess) e = hipGetLastError();
+    return e == hipSuccess ? LSH_OK : hip_fail(e, "lsh_sort");
+}
+
+int lsh_chunk_attend(const void* qk, const void* v, const int32_t* buckets, const int32_t* perm,
+                     const lsh_shape_t* shape, float* o_sorted, float* lse_sorted, void* stream) {
+    g_err[0] = 0;
+    int rc = validate(shape);
+    if (rc) return rc;
+    if (empty(shape)) return LSH_OK;
+    if (!qk || !v || !buckets || !perm || !o_sorted || !lse_sorted)
+        return fail(LSH_ERR_ARG, "lsh_chunk_attend: NULL tensor pointer");
+    const Dims d = make_dims(*shape);
+    hipError_t e = launch_attend(qk, v, buckets, perm, d, o_sorted, lse_sorted, (hipStream_t)stream,
+                                 nullptr, nullptr, nullptr);
+    if (e == hipSuccess) e = hipGetLastError();
+    return e == hipSuccess ? LSH_OK : hip_fail(e, "lsh_chunk_attend");
+}
+
+int lsh_unsort_combine(const float* o_sorted, const float* lse_sorted, const int32_t* inv,
+                       const lsh_shape_t* shape, void* out, void* stream) {
+    g_err[0] = 0;
+    int rc = validate(shape);
+    if (rc) return rc;
+    if (empty(shape)) return LSH_OK;
+    if (!o_sorted || !lse_sorted || !inv || !out)
+        return fail(LSH_ERR_ARG, "lsh_unsort_combine: NULL tensor pointer");
+    const Dims d = make_dims(*shape);
+    hipError_t e = launch_combine(o_sorted, lse_sorted, inv, d, out, (hipStream_t)stream, nullptr,
+                                  nullptr, nullptr);
+    if (e == hipSuccess) e = hipGetLastError();
+    return e == hipSuccess ? LSH_OK : hip_fail(e, "lsh_unsort_combine");
+}
+
+int lsh_attention_fwd(const void* qk, const void* v, const float* R, const lsh_shape_t* shape,
+                      void* out, void* ws, size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    int rc = validate(shape);
+    if (rc) return rc;
+    if (empty(shape)) return LSH_OK;
+    if (!qk || !v || !R || !out) return fail(LSH_ERR_ARG, "lsh_attention_fwd: NULL tensor pointer");
+    return run_fwd(qk, v, R, shape, out, ws, ws_bytes, (hipStream_t)stream, nullptr, nullptr,
+                   nullptr);
+}
+
+int lsh_attention_fwd_timed(const void* qk, const void* v, const float* R,
+                            const lsh_shape_t* shape, void* out, void* ws, size_t ws_bytes,
+                            void* stream, float* kernel_ms, const char** kernel_names,
+                            int32_t max_kernels, int32_t* n_kernels) {
+    g_err[0] = 0;
+    int rc = validate(shape);
+    if (rc) return rc;
+    if (!kernel_ms || !n_kernels || max_kernels < 1)
+        return fail(LSH_ERR_ARG, "lsh_attention_fwd_timed: NULL timing output");
+    *n_kernels = 0;
+    if (empty(shape)) return LSH_OK;
+    if (!qk || !v || !R || !out)
+        return fail(LSH_ERR_ARG, "lsh_attention_fwd_timed: NULL tensor pointer");
+    constexpr int kMaxMarks = 16;
+    hipEvent_t ev[kMaxMarks + 1];
+    int created = 0;
+    hipError_t e = hipSuccess;
+    for (; created < kMaxMarks + 1; ++created)
+        if ((e = hipEventCreate(&ev[created])) != hipSuccess) break;
+    hipStream_t st = (hipStream_t)stream;
+    const char* names[kMaxMarks] = {};
+    int nev = 0;
+    if (e == hipSuccess) e = hipEventRecord(ev[0], st);
+    if (e == hipSuccess) {
+        rc = run_fwd(qk, v, R, shape, out, ws, ws_bytes, st, ev, &nev, names);
+        if (rc == LSH_OK) {
+            e = hipEventSynchronize(ev[nev]);
+            for (int k = 0; e == hipSuccess && k < nev && k < max_kernels; ++k) {
+                e = hipEventElapsedTime(&kernel_ms[k], ev[k], ev[k + 1]);
+                if (kernel_names) kernel_names[k] = names[k];
+            }
+            *n_kernels = nev < max_kernels ? nev : max_kernels;
+        }
+    }
+    for (int k = 0; k < created; ++k) (void)hipEventDestroy(ev[k]);
+    if (rc) return rc;
+    return e == hipSuccess ? LSH_OK : hip_fail(e, "lsh_attention_fwd_timed");
+}
+
+}  // extern "C"

@@ -1,0 +1,463 @@
+// lsh_hash.hip -- step 1: angular LSH, bucket = first argmax of [x R_r, -x R_r].
+//
+// Method: ultralytics.com glossary "Reformer", section "Atenção LSH" (random
+// matrix R of shape [rounds, d, n_buckets/2], bucket = index of the largest
+// entry of [xR, -xR]); twgreatdaily.com walkthrough, section "1 LSH Attention"
+// (one hash function per round, rounds independent).
+//
+// The argmax over [p, -p] is the column with the largest |p|, on the "-" half
+// when that p is negative; exact ties resolve to the lowest index of the
+// concatenation.
+//
+// Design (gfx950):
+//  * Fast pass on the matrix cores. R is split exactly enough into two bf16
+//    terms, R = r_hi + r_lo + e with |e| <= 2^-16 |R|; with bf16 inputs every
+//    product x*r is exact in fp32 and the MFMA accumulates in fp32. Each lane
+//    keeps the three largest |p| of its token as packed keys (|p| with the low
+//    mantissa bits replaced by (column << 1 | sign)), three integer min/max
+//    operations per value.
+//  * Certification. With the Cauchy-Schwarz bound sum_k |x_k R_kb| <=
+//    |x| |R_b|, every fast value is within E = coef * |x| * max_b |R_b| of the
+//    exact one. If the top key beats the second by more than 2E (plus the key
+//    quantisation), the bucket is the exact argmax. If only the third is
+//    certainly out, the token-round is queued with its two candidate columns;
+//    otherwise with a request to scan every column.
+//  * Re-decision in fp64 on the GPU for the queued token-rounds (typically a
+//    fraction of a percent).
+//  * fp32 inputs (or head sizes without a matrix-core kernel) use a plain fp32
+//    FMA pass with the same certification and re-decision.
+#include "lsh_internal.h"
+
+namespace lsh {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+static constexpr float kTwoM24 = 5.9604644775390625e-8f;   // 2^-24
+
+// ------------------------------------------------------------------ workspace
+static size_t rfrag_elems(const Dims& d) {
+    // [nh][ntiles][d/16 k-steps][2 splits][64 lanes][8] bf16
+    return (size_t)d.nh * hash_ntiles(d) * kHashColTile * d.d * 2;
+}
+
+size_t hash_workspace_bytes(const Dims& d) {
+    size_t b = 256;                                              // counter
+    b += align_up(sizeof(float) * d.nh, 256);                    // rnorm
+    b += align_up(sizeof(uint16_t) * rfrag_elems(d), 256);       // rfrag
+    b += align_up(sizeof(RefineItem) * (size_t)d.T * d.nh, 256); // queue
+    return b;
+}
+
+HashWorkspace carve_hash_workspace(void* ws, const Dims& d) {
+    char* p = (char*)ws;
+    HashWorkspace w;
+    w.counter = (int32_t*)p;
+    p += 256;
+    w.rnorm = (float*)p;
+    p += align_up(sizeof(float) * d.nh, 256);
+    w.rfrag = (uint16_t*)p;
+    p += align_up(sizeof(uint16_t) * rfrag_elems(d), 256);
+    w.queue = (RefineItem*)p;
+    return w;
+}
+
+// ------------------------------------------------------------------ R prep
+__global__ void zero_counter_kernel(int32_t* counter) {
+    if (threadIdx.x == 0) counter[0] = 0;
+}
+
+// rnorm[r] = max over columns of the 2-norm of R[r, :, col], rounded up.
+__global__ __launch_bounds__(256) void rnorm_kernel(const float* __restrict__ R, int d, int half,
+                                                    float* __restrict__ rnorm) {
+    const int r = blockIdx.x;
+    const float* Rr = R + (int64_t)r * d * half;
+    float best = 0.f;
+    for (int col = threadIdx.x; col < half; col += blockDim.x) {
+        float s = 0.f;
+        for (int k = 0; k < d; ++k) s = fmaf(Rr[(int64_t)k * half + col], Rr[(int64_t)k * half + col], s);
+        best = fmaxf(best, s);
+    }
+    __shared__ float red[256];
+    red[threadIdx.x] = best;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if ((int)threadIdx.x < o) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + o]);
+        __syncthreads();
+    }
+    // fp32 sum of d squares: relative error below d * 2^-24; sqrt halves it
+    if (threadIdx.x == 0) rnorm[r] = sqrtf(red[0]) * (1.0f + (float)(d + 4) * kTwoM24);
+}
+
+// Writes the bf16 hi/lo split of R in the A-operand order of
+// v_mfma_f32_32x32x16_bf16: for (round, column tile, k-step, split), 64 lanes
+// of 8 values, lane l holding column tile*32 + l%32 and k = kstep*16 + 8*(l/32) + e.
+__global__ __launch_bounds__(256) void rsplit_kernel(const float* __restrict__ R, int d, int half,
+                                                     int ntiles, int64_t nfrag,
+                                                     uint16_t* __restrict__ rfrag) {
+    const int64_t f = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (f >= nfrag) return;
+    const int ks = d / 16;
+    const int lane = (int)(f & 63);
+    int64_t rest = f >> 6;
+    const int q = (int)(rest & 1);
+    rest >>= 1;
+    const int s = (int)(rest % ks);
+    rest /= ks;
+    const int t = (int)(rest % ntiles);
+    const int r = (int)(rest / ntiles);
+    const int col = t * kHashColTile + (lane & 31);
+    const int k0 = s * 16 + 8 * (lane >> 5);
+    uint16_t out[8];
+    for (int e = 0; e < 8; ++e) {
+        const float val = (col < half) ? R[((int64_t)r * d + k0 + e) * half + col] : 0.f;
+        const uint16_t hi = f32_to_bf16(val);
+        const uint16_t lo = f32_to_bf16(val - bf16_to_f32(hi));  // the difference is exact
+        out[e] = q ? lo : hi;
+    }
+    u32x4 pk;
+    pk.x = out[0] | ((uint32_t)out[1] << 16);
+    pk.y = out[2] | ((uint32_t)out[3] << 16);
+    pk.z = out[4] | ((uint32_t)out[5] << 16);
+    pk.w = out[6] | ((uint32_t)out[7] << 16);
+    *(u32x4*)(rfrag + f * 8) = pk;
+}
+
+// ------------------------------------------------------------------ helpers
+__device__ __forceinline__ void top3_insert(uint32_t& k1, uint32_t& k2, uint32_t& k3, uint32_t key) {
+    k3 = max(min(k2, key), k3);
+    k2 = max(min(k1, key), k2);
+    k1 = max(k1, key);
+}
+
+__device__ __forceinline__ uint64_t lanes_below(int lane) {
+    return lane ? (~0ull >> (64 - lane)) : 0ull;
+}
+
+// Appends the flagged lanes' items to the queue (one atomic per wave).
+__device__ __forceinline__ void queue_push(bool flag, RefineItem it, int32_t* counter,
+                                           RefineItem* queue, int lane) {
+    const uint64_t mask = __ballot(flag);
+    if (!mask) return;
+    const int leader = __ffsll((long long)mask) - 1;
+    int base = 0;
+    if (lane == leader) base = atomicAdd(counter, __popcll(mask));
+    base = __shfl(base, leader);
+    if (flag) queue[base + __popcll(mask & lanes_below(lane))] = it;
+}
+
+// Decision shared by both fast passes. v1 >= v2 >= v3 are the three largest
+// fast |p| values (as floats), thr the certification threshold.
+__device__ __forceinline__ int classify(float v1, float v2, float v3, float thr) {
+    if (v1 - v2 > thr) return -1;  // certified
+    if (v1 - v3 > thr) return 0;   // two candidates
+    return 1;                      // scan every column
+}
+
+// ------------------------------------------------------------------ fast pass (MFMA)
+// One workgroup = 4 waves; a wave owns 32*TOKF tokens (TOKF B-operand
+// fragments kept in registers for the whole kernel) and sweeps every column
+// tile of every round; R tiles stream through LDS, double-buffered.
+template <int D, int TOKF>
+__global__ __launch_bounds__(256) void hash_mfma_kernel(const uint16_t* __restrict__ qk,
+                                                        const u32x4* __restrict__ rfrag,
+                                                        const float* __restrict__ rnorm, Dims dm,
+                                                        int32_t* __restrict__ buckets,
+                                                        int32_t* __restrict__ counter,
+                                                        RefineItem* __restrict__ queue) {
+    constexpr int KS = D / 16;
+    constexpr int TILE_U4 = KS * 2 * kWave;     // 16-byte lane fragments per column tile
+    constexpr int PRE = TILE_U4 / 256;          // fragments each thread stages
+    constexpr int TOK_WAVE = 32 * TOKF;
+    constexpr int TOK_WG = 4 * TOK_WAVE;
+    constexpr float kCoef = (float)(4 * D + 8) * kTwoM24 + 3.0517578125e-5f;  // + 2^-15
+    __shared__ u32x4 lds[2][TILE_U4];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int half = dm.nb / 2;
+    const int ntiles = (half + kHashColTile - 1) / kHashColTile;
+    const int total = dm.nh * ntiles;
+    const int64_t tok0 = (int64_t)blockIdx.x * TOK_WG + (int64_t)wave * TOK_WAVE;
+    const int bits = 32 - __clz(2 * ntiles * kHashColTile - 1);
+    const uint32_t keymask = 0x7FFFFFFFu & ~((1u << bits) - 1u);
+    const float qerr = __uint_as_float((uint32_t)(127 + bits - 22) << 23) + 9.5367431640625e-7f;
+
+    // B operand: lane holds x[tok0 + f*32 + lane%32][16 s + 8 (lane/32) + e]
+    bf16x8 xb[TOKF][KS];
+    float xn2[TOKF];
+#pragma unroll
+    for (int f = 0; f < TOKF; ++f) {
+        const int64_t tok = tok0 + f * 32 + (lane & 31);
+        xn2[f] = 0.f;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            u32x4 u = {0u, 0u, 0u, 0u};
+            if (tok < dm.T) u = ((const u32x4*)(qk + tok * D))[2 * s + (lane >> 5)];
+            xb[f][s] = __builtin_bit_cast(bf16x8, u);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float a = __uint_as_float(u[e] << 16), b = __uint_as_float(u[e] & 0xFFFF0000u);
+                xn2[f] = fmaf(a, a, fmaf(b, b, xn2[f]));
+            }
+        }
+        xn2[f] += __shfl_xor(xn2[f], 32);
+    }
+
+    for (int i = threadIdx.x; i < TILE_U4; i += 256) lds[0][i] = rfrag[i];
+    __syncthreads();
+
+    uint32_t k1[TOKF], k2[TOKF], k3[TOKF];
+#pragma unroll
+    for (int f = 0; f < TOKF; ++f) k1[f] = k2[f] = k3[f] = 0u;
+
+    for (int g = 0; g < total; ++g) {
+        const int r = g / ntiles;
+        const int t = g - r * ntiles;
+        u32x4 pre[PRE];
+        if (g + 1 < total) {
+            const u32x4* src = rfrag + (int64_t)(g + 1) * TILE_U4;
+#pragma unroll
+            for (int j = 0; j < PRE; ++j) pre[j] = src[threadIdx.x + j * 256];
+        }
+        const u32x4* cur = lds[g & 1];
+        f32x16 acc[TOKF];
+#pragma unroll
+        for (int f = 0; f < TOKF; ++f) acc[f] = (f32x16){};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const bf16x8 ahi = __builtin_bit_cast(bf16x8, cur[(2 * s + 0) * kWave + lane]);
+            const bf16x8 alo = __builtin_bit_cast(bf16x8, cur[(2 * s + 1) * kWave + lane]);
+#pragma unroll
+            for (int f = 0; f < TOKF; ++f) {
+                acc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, xb[f][s], acc[f], 0, 0, 0);
+                acc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, xb[f][s], acc[f], 0, 0, 0);
+            }
+        }
+        // D layout: register j of lane l is row (column of R) 8*(j/4) + 4*(l/32) + j%4,
+        // column (token) l%32.
+        const uint32_t cb2 = (uint32_t)(t * kHashColTile + 4 * (lane >> 5)) << 1;
+#pragma unroll
+        for (int f = 0; f < TOKF; ++f) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const uint32_t u = __float_as_uint(acc[f][j]);
+                const uint32_t idx = cb2 + (uint32_t)(2 * (8 * (j / 4) + (j % 4))) + (u >> 31);
+                top3_insert(k1[f], k2[f], k3[f], (u & keymask) | idx);
+            }
+        }
+        if (t == ntiles - 1) {
+            const float E2 = 2.f * kCoef * rnorm[r];
+#pragma unroll
+            for (int f = 0; f < TOKF; ++f) {
+                const uint32_t p1 = __shfl_xor(k1[f], 32);
+                const uint32_t p2 = __shfl_xor(k2[f], 32);
+                const uint32_t p3 = __shfl_xor(k3[f], 32);
+                top3_insert(k1[f], k2[f], k3[f], p1);
+                top3_insert(k1[f], k2[f], k3[f], p2);
+                top3_insert(k1[f], k2[f], k3[f], p3);
+                const int64_t tok = tok0 + f * 32 + (lane & 31);
+                const bool mine = lane < 32 && tok < dm.T;
+                const float v1 = __uint_as_float(k1[f] & keymask);
+                const float v2 = __uint_as_float(k2[f] & keymask);
+                const float v3 = __uint_as_float(k3[f] & keymask);
+                const float xn = sqrtf(xn2[f]) * (1.0f + (float)(D + 4) * kTwoM24);
+                const float thr = E2 * xn + v1 * qerr + 1e-30f;
+                const int mode = classify(v1, v2, v3, thr);
+                const uint32_t i1 = (k1[f] & ~keymask & 0x7FFFFFFFu), i2 = (k2[f] & ~keymask & 0x7FFFFFFFu);
+                const int c1 = (int)(i1 >> 1), c2 = (int)(i2 >> 1);
+                int bucket = c1 < half ? c1 + ((i1 & 1u) ? half : 0) : 0;
+                int64_t item = 0;
+                if (mine) {
+                    const int64_t bh = tok / dm.L, i = tok - bh * dm.L;
+                    item = (bh * dm.nh + r) * dm.L + i;
+                    buckets[item] = bucket;
+                }
+                RefineItem it{(int32_t)item, c1, c2, mode};
+                queue_push(mine && mode >= 0, it, counter, queue, lane);
+                k1[f] = k2[f] = k3[f] = 0u;
+            }
+        }
+        if (g + 1 < total) {
+            u32x4* dst = lds[(g + 1) & 1];
+#pragma unroll
+            for (int j = 0; j < PRE; ++j) dst[threadIdx.x + j * 256] = pre[j];
+        }
+        __syncthreads();
+    }
+}
+
+// ------------------------------------------------------------------ fast pass (fp32 FMA)
+// One thread per (token, round); the block's round is uniform so R reads are
+// scalar. Used for fp32 inputs (and any dtype when requested).
+template <int D, typename T>
+__global__ __launch_bounds__(256) void hash_valu_kernel(const T* __restrict__ qk,
+                                                        const float* __restrict__ R,
+                                                        const float* __restrict__ rnorm, Dims dm,
+                                                        int32_t* __restrict__ buckets,
+                                                        int32_t* __restrict__ counter,
+                                                        RefineItem* __restrict__ queue) {
+    constexpr float kCoef = (float)(2 * D + 8) * kTwoM24;
+    const int lane = threadIdx.x & 63;
+    const int r = blockIdx.y;
+    const int half = dm.nb / 2;
+    const int64_t tok = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const bool live = tok < dm.T;
+    float x[D];
+    float xn2 = 0.f;
+#pragma unroll
+    for (int k = 0; k < D; ++k) {
+        x[k] = live ? IO<T>::load(qk, tok * D + k) : 0.f;
+        xn2 = fmaf(x[k], x[k], xn2);
+    }
+    const float* Rr = R + (int64_t)r * D * half;
+    float v1 = -1.f, v2 = -1.f, v3 = -1.f;
+    int i1 = 0, i2 = 0;
+    bool neg1 = false;
+    for (int col = 0; col < half; ++col) {
+        float p = 0.f;
+#pragma unroll
+        for (int k = 0; k < D; ++k) p = fmaf(x[k], Rr[(int64_t)k * half + col], p);
+        const float a = fabsf(p);
+        if (a > v1) {
+            v3 = v2; v2 = v1; i2 = i1; v1 = a; i1 = col; neg1 = p < 0.f;
+        } else if (a > v2) {
+            v3 = v2; v2 = a; i2 = col;
+        } else if (a > v3) {
+            v3 = a;
+        }
+    }
+    if (half == 1) { v2 = 0.f; v3 = 0.f; i2 = 0; }     // a single column: compare with -p only
+    if (half == 2) v3 = 0.f;
+    const float xn = sqrtf(xn2) * (1.0f + (float)(D + 4) * kTwoM24);
+    const float thr = 2.f * kCoef * xn * rnorm[r] + v1 * 9.5367431640625e-7f + 1e-30f;
+    int mode = classify(v1, v2, v3, thr);
+    if (half == 1) mode = (v1 > thr) ? -1 : 1;
+    int64_t item = 0;
+    if (live) {
+        const int64_t bh = tok / dm.L, i = tok - bh * dm.L;
+        item = (bh * dm.nh + r) * dm.L + i;
+        buckets[item] = i1 + (neg1 ? half : 0);
+    }
+    RefineItem it{(int32_t)item, i1, i2, mode};
+    queue_push(live && mode >= 0, it, counter, queue, lane);
+}
+
+// ------------------------------------------------------------------ re-decision in fp64
+// One wave per queued token-round. Mode 0 computes the two candidate columns
+// (half a wave each); mode 1 scans every column. The exact rule: largest |p|,
+// ties to the lowest index of [p, -p] (a p of either zero sign counts as "+").
+template <typename T>
+__global__ __launch_bounds__(256) void hash_refine_kernel(const T* __restrict__ qk,
+                                                          const float* __restrict__ R, Dims dm,
+                                                          const int32_t* __restrict__ counter,
+                                                          const RefineItem* __restrict__ queue,
+                                                          int32_t* __restrict__ buckets) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    const int n = *counter;
+    const int half = dm.nb / 2;
+    const int D = dm.d;
+    for (int64_t q = wave; q < n; q += nwaves) {
+        const RefineItem it = queue[q];
+        const int64_t item = it.item;
+        const int64_t i = item % dm.L;
+        const int64_t rest = item / dm.L;
+        const int r = (int)(rest % dm.nh);
+        const int64_t bh = rest / dm.nh;
+        const T* x = qk + (bh * dm.L + i) * D;
+        const float* Rr = R + (int64_t)r * D * half;
+        if (it.mode == 0) {
+            const int col = (lane < 32) ? it.a : it.b;
+            double acc = 0.0;
+            if (col >= 0 && col < half)
+                for (int k = lane & 31; k < D; k += 32)
+                    acc += (double)IO<T>::load(x, k) * (double)Rr[(int64_t)k * half + col];
+            for (int off = 16; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+            const double pa = __shfl(acc, 0), pb = __shfl(acc, 32);
+            if (lane == 0) {
+                const bool va = it.a >= 0 && it.a < half, vb = it.b >= 0 && it.b < half && it.b != it.a;
+                const int ca = it.a + (pa < 0.0 ? half : 0), cb = it.b + (pb < 0.0 ? half : 0);
+                int pick;
+                if (!vb) pick = ca;
+                else if (!va) pick = cb;
+                else if (fabs(pa) > fabs(pb)) pick = ca;
+                else if (fabs(pb) > fabs(pa)) pick = cb;
+                else pick = min(ca, cb);
+                buckets[item] = pick;
+            }
+        } else {
+            double bestv = -1.0;
+            int besti = 0x7FFFFFFF;
+            for (int col = lane; col < half; col += kWave) {
+                double p = 0.0;
+                for (int k = 0; k < D; ++k)
+                    p += (double)IO<T>::load(x, k) * (double)Rr[(int64_t)k * half + col];
+                const double v = fabs(p);
+                const int ci = col + (p < 0.0 ? half : 0);
+                if (v > bestv || (v == bestv && ci < besti)) { bestv = v; besti = ci; }
+            }
+            for (int off = 32; off > 0; off >>= 1) {
+                const double ov = __shfl_xor(bestv, off);
+                const int oi = __shfl_xor(besti, off);
+                if (ov > bestv || (ov == bestv && oi < besti)) { bestv = ov; besti = oi; }
+            }
+            if (lane == 0) buckets[item] = besti;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ launcher
+template <typename T>
+static hipError_t launch_valu_and_refine(const T* qk, const float* R, const Dims& d,
+                                         int32_t* buckets, const HashWorkspace& w, hipStream_t st,
+                                         hipEvent_t* ev, int* nev, const char** names) {
+    dim3 grid((unsigned)((d.T + 255) / 256), (unsigned)d.nh);
+    if (d.d == 64)
+        hash_valu_kernel<64, T><<<grid, 256, 0, st>>>(qk, R, w.rnorm, d, buckets, w.counter, w.queue);
+    else
+        hash_valu_kernel<128, T><<<grid, 256, 0, st>>>(qk, R, w.rnorm, d, buckets, w.counter, w.queue);
+    hipError_t e = mark(st, ev, nev, names, "hash_fast_fp32");
+    if (e != hipSuccess) return e;
+    return hipSuccess;
+}
+
+hipError_t launch_hash(const void* qk, const float* R, const Dims& d, int32_t* buckets,
+                       const HashWorkspace& w, hipStream_t st, hipEvent_t* ev, int* nev,
+                       const char** names) {
+    const int half = d.nb / 2;
+    const int ntiles = hash_ntiles(d);
+    hipError_t e;
+    zero_counter_kernel<<<1, 64, 0, st>>>(w.counter);
+    rnorm_kernel<<<d.nh, 256, 0, st>>>(R, d.d, half, w.rnorm);
+    if ((e = mark(st, ev, nev, names, "hash_prep")) != hipSuccess) return e;
+
+    if (d.dtype == LSH_BF16) {
+        const int64_t nfrag = (int64_t)d.nh * ntiles * (d.d / 16) * 2 * kWave;
+        rsplit_kernel<<<(unsigned)((nfrag + 255) / 256), 256, 0, st>>>(R, d.d, half, ntiles, nfrag,
+                                                                      w.rfrag);
+        if ((e = mark(st, ev, nev, names, "hash_rsplit")) != hipSuccess) return e;
+        constexpr int TOKF = 2;
+        const int64_t per_wg = 4 * 32 * TOKF;
+        const unsigned grid = (unsigned)((d.T + per_wg - 1) / per_wg);
+        const uint16_t* x = (const uint16_t*)qk;
+        if (d.d == 64)
+            hash_mfma_kernel<64, TOKF><<<grid, 256, 0, st>>>(x, (const u32x4*)w.rfrag, w.rnorm, d,
+                                                           buckets, w.counter, w.queue);
+        else
+            hash_mfma_kernel<128, TOKF><<<grid, 256, 0, st>>>(x, (const u32x4*)w.rfrag, w.rnorm, d,
+                                                            buckets, w.counter, w.queue);
+        if ((e = mark(st, ev, nev, names, "hash_fast_mfma")) != hipSuccess) return e;
+        hash_refine_kernel<uint16_t><<<256, 256, 0, st>>>(x, R, d, w.counter, w.queue, buckets);
+    } else {
+        e = launch_valu_and_refine((const float*)qk, R, d, buckets, w, st, ev, nev, names);
+        if (e != hipSuccess) return e;
+        hash_refine_kernel<float><<<256, 256, 0, st>>>((const float*)qk, R, d, w.counter, w.queue,
+                                                       buckets);
+    }
+    return mark(st, ev, nev, names, "hash_refine_fp64");
+}
+
+}  // namespace lsh

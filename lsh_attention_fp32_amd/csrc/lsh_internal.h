@@ -1,0 +1,127 @@
+// lsh_internal.h -- shared declarations of the gfx950 LSH-attention kernels.
+//
+// Host launchers are defined next to their kernels (lsh_hash.hip, lsh_sort.hip,
+// lsh_attend.hip, lsh_combine.hip) and called by the C ABI in lsh_api.hip.
+// Every launcher enqueues on the given stream and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lsh_attn.h"
+
+namespace lsh {
+
+constexpr int kWave = 64;
+constexpr float kSelfPenalty = 1.0e5f;   // subtracted from a query's score against itself
+
+// Device-side problem description (plain values, passed by value to kernels).
+struct Dims {
+    int32_t B, H, L, d;
+    int32_t nb, nh, m, causal;
+    int32_t dtype;
+    int64_t T;        // B*H*L token-heads
+    int64_t segs;     // B*H*nh (batch, head, round) segments
+};
+
+inline Dims make_dims(const lsh_shape_t& s) {
+    Dims d{};
+    d.B = s.B; d.H = s.H; d.L = s.L; d.d = s.d;
+    d.nb = s.n_buckets; d.nh = s.n_hashes; d.m = s.chunk_len; d.causal = s.causal;
+    d.dtype = s.dtype;
+    d.T = (int64_t)s.B * s.H * s.L;
+    d.segs = (int64_t)s.B * s.H * s.n_hashes;
+    return d;
+}
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---------------------------------------------------------------- hash stage
+// Column tile of the matrix-core hash pass: 32 projection columns.
+constexpr int kHashColTile = 32;
+
+inline int hash_ntiles(const Dims& d) { return (d.nb / 2 + kHashColTile - 1) / kHashColTile; }
+
+// One entry of the re-decision queue written by the fast hash pass.
+//   item : flat index into buckets [B,H,nh,L]
+//   a, b : the two candidate columns (mode 0) -- unused for mode 1
+//   mode : 0 = decide between columns a and b, 1 = scan every column
+struct RefineItem {
+    int32_t item, a, b, mode;
+};
+
+struct HashWorkspace {
+    int32_t* counter;     // [1] number of queued items (also the public count)
+    float* rnorm;         // [nh] max column 2-norm of R per round, rounded up
+    uint16_t* rfrag;      // bf16 hi/lo split of R in matrix-core fragment order
+    RefineItem* queue;    // [T*nh]
+};
+size_t hash_workspace_bytes(const Dims& d);
+HashWorkspace carve_hash_workspace(void* ws, const Dims& d);
+
+hipError_t launch_hash(const void* qk, const float* R, const Dims& d, int32_t* buckets,
+                       const HashWorkspace& w, hipStream_t st, hipEvent_t* ev, int* nev,
+                       const char** names);
+
+// ---------------------------------------------------------------- sort stage
+constexpr int kSortTile = 4096;          // elements per sort tile (one workgroup)
+constexpr int kSortWaves = 4;            // waves per sort workgroup
+constexpr int kMaxBuckets = 4096;
+constexpr int kMaxHashes = 4096;
+
+inline int64_t sort_ntiles(const Dims& d) { return (d.L + kSortTile - 1) / kSortTile; }
+size_t sort_workspace_bytes(const Dims& d);
+hipError_t launch_sort(const int32_t* buckets, const Dims& d, int32_t* perm, int32_t* inv,
+                       void* ws, hipStream_t st, hipEvent_t* ev, int* nev, const char** names);
+
+// ------------------------------------------------------------ attend stage
+hipError_t launch_attend(const void* qk, const void* v, const int32_t* buckets,
+                         const int32_t* perm, const Dims& d, float* o_sorted, float* lse_sorted,
+                         hipStream_t st, hipEvent_t* ev, int* nev, const char** names);
+
+// ----------------------------------------------------------- combine stage
+hipError_t launch_combine(const float* o_sorted, const float* lse_sorted, const int32_t* inv,
+                          const Dims& d, void* out, hipStream_t st, hipEvent_t* ev, int* nev,
+                          const char** names);
+
+// Records a timing event after a kernel when the caller asked for timing.
+inline hipError_t mark(hipStream_t st, hipEvent_t* ev, int* nev, const char** names,
+                       const char* name) {
+    if (!ev) return hipSuccess;
+    if (names) names[*nev] = name;
+    hipError_t e = hipEventRecord(ev[*nev + 1], st);
+    ++*nev;
+    return e;
+}
+
+// ------------------------------------------------------------ device helpers
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float((uint32_t)h << 16);
+}
+
+// float -> bf16, round to nearest even (finite inputs; NaN stays NaN)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+template <typename T>
+struct IO;
+template <>
+struct IO<float> {
+    __device__ __forceinline__ static float load(const float* p, int64_t i) { return p[i]; }
+    __device__ __forceinline__ static void store(float* p, int64_t i, float v) { p[i] = v; }
+};
+template <>
+struct IO<uint16_t> {
+    __device__ __forceinline__ static float load(const uint16_t* p, int64_t i) {
+        return bf16_to_f32(p[i]);
+    }
+    __device__ __forceinline__ static void store(uint16_t* p, int64_t i, float v) {
+        p[i] = f32_to_bf16(v);
+    }
+};
+
+}  // namespace lsh

@@ -1,0 +1,185 @@
+// lsh_sort.hip -- step 2: stable sort of each (batch, head, round) segment by
+// (bucket, position).
+//
+// Method: twgreatdaily.com walkthrough, section "1 LSH Attention" (two-level
+// sort: by bucket number, then by position inside the bucket); ai-scholar.tech
+// summary, section "・LSH Attention" (sort per bucket before chunking).
+//
+// Positions arrive in increasing order, so a stable counting sort on the
+// bucket alone yields the (bucket, position) order. Three kernels:
+//   count   per 4096-element tile: bucket histogram in LDS
+//   scan    per segment: exclusive scan of the histograms in (bucket, tile)
+//           order -> the first slot of every (bucket, tile) run
+//   scatter per tile: each wave walks its 1024 elements in order; lanes with
+//           equal buckets are grouped by a ballot match, so ranks are exact
+//           and the LDS counter of a hot bucket is bumped once per wave step
+//           (skewed buckets do not serialise on LDS atomics).
+#include "lsh_internal.h"
+
+namespace lsh {
+
+size_t sort_workspace_bytes(const Dims& d) {
+    return align_up(sizeof(int32_t) * (size_t)d.segs * d.nb * (size_t)sort_ntiles(d), 256);
+}
+
+// Mask of the lanes whose bucket equals this lane's (0 for inactive lanes).
+__device__ __forceinline__ uint64_t match_bucket(int b, int nbits, bool active) {
+    uint64_t m = __ballot(active);
+    for (int k = 0; k < nbits; ++k) {
+        const bool bit = (b >> k) & 1;
+        const uint64_t s = __ballot(active && bit);
+        m &= bit ? s : ~s;
+    }
+    return active ? m : 0ull;
+}
+
+// Bucket ids outside [0, nb) are a caller error; clamping keeps every LDS
+// access in bounds (the result is then unspecified, never a fault).
+__device__ __forceinline__ int clamp_bucket(int b, int nb) {
+    return (int)min((unsigned)b, (unsigned)(nb - 1));
+}
+
+__device__ __forceinline__ uint64_t lanes_below_s(int lane) {
+    return lane ? (~0ull >> (64 - lane)) : 0ull;
+}
+
+// counts layout: [seg][bucket][tile]
+__global__ __launch_bounds__(256) void sort_count_kernel(const int32_t* __restrict__ buckets,
+                                                         Dims dm, int ntiles, int nbits,
+                                                         int32_t* __restrict__ counts) {
+    extern __shared__ int32_t hist[];
+    const int tile = blockIdx.x;
+    const int64_t seg = blockIdx.y;
+    const int lane = threadIdx.x & 63;
+    for (int b = threadIdx.x; b < dm.nb; b += 256) hist[b] = 0;
+    __syncthreads();
+    const int32_t* src = buckets + seg * dm.L;
+    const int64_t beg = (int64_t)tile * kSortTile;
+    const int64_t end = min(beg + (int64_t)kSortTile, (int64_t)dm.L);
+    for (int64_t i0 = beg + (threadIdx.x & ~63); i0 < end; i0 += 256) {
+        const int64_t i = i0 + lane;
+        const bool active = i < end;
+        const int b = active ? clamp_bucket(src[i], dm.nb) : 0;
+        const uint64_t m = match_bucket(b, nbits, active);
+        if (active && (__ffsll((long long)m) - 1) == lane) atomicAdd(&hist[b], __popcll(m));
+    }
+    __syncthreads();
+    for (int b = threadIdx.x; b < dm.nb; b += 256)
+        counts[(seg * dm.nb + b) * ntiles + tile] = hist[b];
+}
+
+// In-place exclusive scan of each segment's nb*ntiles counts (one block per segment).
+__global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t* __restrict__ counts, int64_t n) {
+    constexpr int ITEMS = 8;
+    __shared__ int32_t wsum[16];
+    int32_t* c = counts + (int64_t)blockIdx.x * n;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int32_t carry = 0;
+    for (int64_t base = 0; base < n; base += 1024 * ITEMS) {
+        int32_t v[ITEMS];
+        int32_t tsum = 0;
+        const int64_t my = base + (int64_t)threadIdx.x * ITEMS;
+#pragma unroll
+        for (int k = 0; k < ITEMS; ++k) {
+            v[k] = (my + k < n) ? c[my + k] : 0;
+            tsum += v[k];
+        }
+        // inclusive scan of tsum across the wave
+        int32_t incl = tsum;
+        for (int off = 1; off < 64; off <<= 1) {
+            const int32_t o = __shfl_up(incl, off);
+            if (lane >= off) incl += o;
+        }
+        if (lane == 63) wsum[wave] = incl;
+        __syncthreads();
+        int32_t wprefix = 0, total = 0;
+        for (int w = 0; w < 16; ++w) {
+            const int32_t s = wsum[w];
+            if (w < wave) wprefix += s;
+            total += s;
+        }
+        int32_t run = carry + wprefix + incl - tsum;
+#pragma unroll
+        for (int k = 0; k < ITEMS; ++k) {
+            if (my + k < n) c[my + k] = run;
+            run += v[k];
+        }
+        carry += total;
+        __syncthreads();
+    }
+}
+
+__global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __restrict__ buckets,
+                                                           const int32_t* __restrict__ offs,
+                                                           Dims dm, int ntiles, int nbits,
+                                                           int32_t* __restrict__ perm,
+                                                           int32_t* __restrict__ inv) {
+    extern __shared__ int32_t sh[];   // [kSortWaves][nb]: counts, then running slots
+    constexpr int SUB = kSortTile / kSortWaves;
+    const int tile = blockIdx.x;
+    const int64_t seg = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nb = dm.nb;
+    for (int k = threadIdx.x; k < kSortWaves * nb; k += 256) sh[k] = 0;
+    __syncthreads();
+    const int32_t* src = buckets + seg * dm.L;
+    const int64_t wbeg = (int64_t)tile * kSortTile + (int64_t)wave * SUB;
+    const int64_t wend = min(wbeg + (int64_t)SUB, (int64_t)dm.L);
+    int32_t* mine = sh + wave * nb;
+    // pass 1: this wave's count per bucket
+    for (int64_t i0 = wbeg; i0 < wend; i0 += kWave) {
+        const int64_t i = i0 + lane;
+        const bool active = i < wend;
+        const int b = active ? clamp_bucket(src[i], nb) : 0;
+        const uint64_t m = match_bucket(b, nbits, active);
+        if (active && (__ffsll((long long)m) - 1) == lane) mine[b] += __popcll(m);
+    }
+    __syncthreads();
+    // first slot of each (wave, bucket) run
+    for (int b = threadIdx.x; b < nb; b += 256) {
+        int32_t run = offs[(seg * nb + b) * ntiles + tile];
+        for (int w = 0; w < kSortWaves; ++w) {
+            const int32_t cnt = sh[w * nb + b];
+            sh[w * nb + b] = run;
+            run += cnt;
+        }
+    }
+    __syncthreads();
+    // pass 2: ranks in position order
+    int32_t* P = perm + seg * dm.L;
+    int32_t* I = inv + seg * dm.L;
+    for (int64_t i0 = wbeg; i0 < wend; i0 += kWave) {
+        const int64_t i = i0 + lane;
+        const bool active = i < wend;
+        const int b = active ? clamp_bucket(src[i], nb) : 0;
+        const uint64_t m = match_bucket(b, nbits, active);
+        if (active) {
+            const int32_t slot = mine[b] + __popcll(m & lanes_below_s(lane));
+            P[slot] = (int32_t)i;
+            I[i] = slot;
+        }
+        // every lane has read its run start; leaders now advance them
+        __builtin_amdgcn_wave_barrier();
+        if (active && (__ffsll((long long)m) - 1) == lane) mine[b] += __popcll(m);
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+hipError_t launch_sort(const int32_t* buckets, const Dims& d, int32_t* perm, int32_t* inv,
+                       void* ws, hipStream_t st, hipEvent_t* ev, int* nev, const char** names) {
+    const int ntiles = (int)sort_ntiles(d);
+    int nbits = 0;
+    while ((1 << nbits) < d.nb) ++nbits;
+    int32_t* counts = (int32_t*)ws;
+    dim3 grid((unsigned)ntiles, (unsigned)d.segs);
+    hipError_t e;
+    sort_count_kernel<<<grid, 256, sizeof(int32_t) * d.nb, st>>>(buckets, d, ntiles, nbits, counts);
+    if ((e = mark(st, ev, nev, names, "sort_count")) != hipSuccess) return e;
+    sort_scan_kernel<<<(unsigned)d.segs, 1024, 0, st>>>(counts, (int64_t)d.nb * ntiles);
+    if ((e = mark(st, ev, nev, names, "sort_scan")) != hipSuccess) return e;
+    sort_scatter_kernel<<<grid, 256, sizeof(int32_t) * kSortWaves * d.nb, st>>>(
+        buckets, counts, d, ntiles, nbits, perm, inv);
+    return mark(st, ev, nev, names, "sort_scatter");
+}
+
+}  // namespace lsh

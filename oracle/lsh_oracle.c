@@ -47,10 +47,23 @@
  */
 #include <math.h>
 #include <stdint.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdlib.h>
 #include <string.h>
 
 #define ORACLE_SELF_PENALTY 1.0e5
+
+/* Number of threads the oracle's parallel loops use (for reporting). */
+int oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* ------------------------------------------------------------------------ */
 /* O1. Angular LSH ([GLOSSARY] "Atenção LSH"; [WALKTHRU] "1 LSH Attention"   */

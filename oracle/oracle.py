@@ -63,11 +63,18 @@ def _load():
                                        ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                        ctypes.c_int, ctypes.c_int, _f64p, _i32p, _f64p, _i32p,
                                        _i32p, _f64p, _f64p]
+        lib.oracle_threads.argtypes = []
+        lib.oracle_threads.restype = ctypes.c_int
         for fn in (lib.oracle_hash, lib.oracle_sort, lib.oracle_attend, lib.oracle_combine,
                    lib.oracle_forward):
             fn.restype = ctypes.c_int
         _lib = lib
     return _lib
+
+
+def threads() -> int:
+    """Threads the oracle's OpenMP loops run on."""
+    return int(_load().oracle_threads())
 
 
 def _f64(a) -> np.ndarray:

@@ -1,0 +1,101 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched).
+
+The library must load without a GPU, export every function that
+include/lsh_attn.h declares, and reject bad arguments on the host with the
+documented error codes before touching the device.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import lsh_attention_fp32_amd as lsh
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lsh_attn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(lsh_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not lsh.library_path().exists():
+        pytest.fail("liblsh_attn.so is not built (run __graft_entry__.build())")
+    return lsh.load_library()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ("lsh_hash", "lsh_sort", "lsh_chunk_attend", "lsh_unsort_combine",
+              "lsh_attention_fwd", "lsh_workspace_size", "lsh_last_error",
+              "lsh_attention_fwd_timed"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), f"{name} declared in lsh_attn.h but not exported"
+
+
+def _shape(**kw):
+    base = dict(B=1, H=2, L=256, d=64, n_buckets=16, n_hashes=2, chunk_len=64, causal=1,
+                dtype=lsh.LSH_BF16)
+    base.update(kw)
+    return lsh.Shape(**base)
+
+
+@pytest.mark.parametrize("kw, code", [
+    (dict(n_buckets=15), -1), (dict(n_buckets=0), -1), (dict(n_hashes=0), -1),
+    (dict(chunk_len=0), -1), (dict(L=100, chunk_len=64), -1), (dict(causal=2), -1),
+    (dict(dtype=7), -1), (dict(B=-1), -1), (dict(d=96), -4), (dict(n_buckets=8192), -4),
+    (dict(B=64, H=64, L=65536, n_hashes=8, chunk_len=64), -1),
+])
+def test_workspace_size_rejects_bad_shapes(lib, kw, code):
+    with pytest.raises(lsh.LshError) as ei:
+        lsh.lsh_workspace_size("fwd", _shape(**kw))
+    assert ei.value.code == code
+    assert lsh.lsh_last_error()
+
+
+def test_workspace_sizes_are_consistent(lib):
+    s = _shape()
+    h, so, f = (lsh.lsh_workspace_size(k, s) for k in ("hash", "sort", "fwd"))
+    n = s.B * s.H * s.n_hashes * s.L
+    assert h > 0 and so > 0
+    assert f >= h + so + n * (4 * 4 + 4 * s.d)
+    with pytest.raises(lsh.LshError):
+        lsh.lsh_workspace_size("nope", s)
+
+
+def test_entry_points_reject_on_host(lib):
+    s = _shape(d=96)
+    vp = ctypes.c_void_p
+    assert lib.lsh_attention_fwd(None, None, None, ctypes.byref(s), None, None, 0, None) == -4
+    s = _shape()
+    # NULL tensors are refused before anything reaches the device
+    assert lib.lsh_hash(None, None, ctypes.byref(s), None, None, 0, None) == -1
+    assert lib.lsh_sort(None, ctypes.byref(s), None, None, None, 0, None) == -1
+    assert lib.lsh_chunk_attend(None, None, None, None, ctypes.byref(s), None, None, None) == -1
+    assert lib.lsh_unsort_combine(None, None, None, ctypes.byref(s), None, None) == -1
+    # a missing or short workspace is LSH_ERR_WORKSPACE
+    fake = vp(0x1000)
+    assert lib.lsh_hash(fake, fake, ctypes.byref(s), fake, None, 0, None) == -2
+    assert lib.lsh_hash(fake, fake, ctypes.byref(s), fake, fake, 16, None) == -2
+    assert lib.lsh_sort(fake, ctypes.byref(s), fake, fake, fake, 16, None) == -2
+    assert lib.lsh_attention_fwd(fake, fake, fake, ctypes.byref(s), fake, fake, 16, None) == -2
+    assert b"workspace" in lib.lsh_last_error()
+    assert lib.lsh_attention_fwd(None, None, None, None, None, None, 0, None) == -1
+
+
+def test_empty_problems_enqueue_nothing(lib):
+    for kw in (dict(L=0), dict(B=0), dict(H=0)):
+        s = _shape(**kw)
+        assert lib.lsh_attention_fwd(None, None, None, ctypes.byref(s), None, None, 0, None) == 0
+        assert lib.lsh_hash(None, None, ctypes.byref(s), None, None, 0, None) == 0

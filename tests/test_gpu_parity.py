@@ -1,0 +1,236 @@
+"""GPU parity of every step against the double-precision oracle.
+
+Every call goes through the C ABI (lsh_attention_fp32_amd -> liblsh_attn.so).
+Each step is compared with the oracle step fed the GPU's outputs of the
+previous step, so a near-tie upstream cannot cascade. The bars:
+  * bucket ids: equal to the oracle wherever its margin is >= 1e-5 (near-ties
+    are counted); in practice the fp64 re-decision makes them equal wherever
+    the margin is >= 1e-9, which is asserted too;
+  * sort: bit-exact;
+  * attention outputs: max-abs 1e-4 (fp32 I/O) or 2e-2 (bf16 I/O).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import oracle
+
+lsh = pytest.importorskip("lsh_attention_fp32_amd")
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL = {"fp32": 1e-4, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lsh.load_library()
+
+
+def _tensors(w, seed=None):
+    qk, v, R = workloads.make_inputs(w, seed)
+    dt = torch.float32 if w.dtype == "fp32" else torch.bfloat16
+    return (qk, v, R, torch.from_numpy(qk).to(DEV, dt), torch.from_numpy(v).to(DEV, dt),
+            torch.from_numpy(R).to(DEV))
+
+
+def _wl(dtype="bf16", B=1, H=2, L=1024, d=64, nb=16, nh=2, m=64, causal=True, seed=7,
+        dist="normal"):
+    return workloads.Workload(f"t_{dtype}_{L}_{d}_{nb}_{nh}", B, H, L, d, dtype, nb, nh, m, causal,
+                              seed, dist)
+
+
+def _oracle_hash(qk, R, nb):
+    B, H, L, d = qk.shape
+    b = np.empty((B, H, R.shape[0], L), np.int32)
+    mg = np.empty((B, H, R.shape[0], L))
+    for bi in range(B):
+        for h in range(H):
+            b[bi, h], mg[bi, h] = oracle.hash(qk[bi, h], R, nb)
+    return b, mg
+
+
+def _check_buckets(gpu, ref, margin):
+    differ = gpu != ref
+    assert not np.any(differ & (margin >= 1e-5)), "bucket ids differ away from near-ties"
+    assert not np.any(differ & (margin >= 1e-9)), "bucket ids differ at margins above 1e-9"
+    return int((margin < 1e-5).sum()), int(differ.sum())
+
+
+HASH_CASES = [
+    ("bf16", 64, 16, 2, 1024), ("bf16", 128, 1024, 2, 2048), ("bf16", 64, 2, 3, 512),
+    ("bf16", 64, 4, 2, 256), ("bf16", 64, 6, 2, 320), ("bf16", 64, 2048, 1, 4096),
+    ("bf16", 128, 4096, 1, 1024), ("bf16", 128, 64, 3, 999),
+    ("fp32", 64, 16, 1, 1024), ("fp32", 128, 64, 2, 512), ("fp32", 64, 2, 2, 256),
+]
+
+
+@pytest.mark.parametrize("dtype,d,nb,nh,L", HASH_CASES)
+def test_hash_matches_oracle(dtype, d, nb, nh, L):
+    w = _wl(dtype, L=L, d=d, nb=nb, nh=nh, m=1)
+    qk, v, R, qk_t, v_t, R_t = _tensors(w)
+    buckets, refined = lsh.hash(qk_t, R_t, nb)
+    ref, margin = _oracle_hash(qk, R, nb)
+    near, differ = _check_buckets(buckets.cpu().numpy(), ref, margin)
+    total = ref.size
+    print(f"hash {dtype} d={d} nb={nb} nh={nh} L={L}: near-ties {near}, differ {differ}, "
+          f"re-decided {refined} of {total}")
+    assert refined <= 0.1 * total
+
+
+def test_hash_glossary_example_on_gpu():
+    """The glossary page's seeded example (fp32, 1000 rounds) on the GPU."""
+    x, R = workloads.glossary_hash_example()
+    qk_t = torch.from_numpy(x).reshape(1, 1, 3, 64).to(DEV)
+    R_t = torch.from_numpy(R).to(DEV)
+    buckets, _ = lsh.hash(qk_t, R_t, 16)
+    b = buckets.cpu().numpy()[0, 0]          # [1000, 3]
+    ref, _ = oracle.hash(x, R, 16)
+    assert np.array_equal(b, ref)
+    near = np.float32((b[:, 1] == b[:, 0]).mean(dtype=np.float32))
+    far = np.float32((b[:, 2] == b[:, 0]).mean(dtype=np.float32))
+    assert f"{float(near):.0%}" == "72%" and f"{float(far):.0%}" == "9%"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_hash_exact_ties_and_zero_rows(dtype):
+    """Duplicate columns of R give exact ties (lowest index of [p, -p] wins);
+    zero vectors tie everywhere (bucket 0)."""
+    w = _wl(dtype, L=256, d=64, nb=32, nh=2, m=1)
+    qk, v, R, qk_t, v_t, R_t = _tensors(w)
+    R[:, :, 9] = R[:, :, 3]
+    R[1, :, 12] = -R[1, :, 5]
+    qk[0, 0, :17] = 0.0
+    dt = qk_t.dtype
+    qk_t = torch.from_numpy(qk).to(DEV, dt)
+    R_t = torch.from_numpy(R).to(DEV)
+    buckets, refined = lsh.hash(qk_t, R_t, 32)
+    ref, margin = _oracle_hash(qk, R, 32)
+    assert np.array_equal(buckets.cpu().numpy(), ref)
+    assert (ref[0, 0, :, :17] == 0).all()
+    assert refined >= 2 * 17
+
+
+SORT_CASES = [("uniform", 1024, 4096 + 192), ("uniform", 64, 4096 * 3), ("skewed", 256, 16384),
+              ("constant", 64, 5000 // 8 * 8), ("uniform", 4096, 8192), ("uniform", 2, 100)]
+
+
+@pytest.mark.parametrize("kind,nb,L", SORT_CASES)
+def test_sort_matches_oracle(kind, nb, L):
+    rng = np.random.default_rng(nb + L)
+    B, H, nh = 1, 2, 3
+    if kind == "uniform":
+        b = rng.integers(0, nb, (B, H, nh, L))
+    elif kind == "skewed":
+        b = np.where(rng.random((B, H, nh, L)) < 0.3, 17, rng.integers(0, nb, (B, H, nh, L)))
+    else:
+        b = np.full((B, H, nh, L), nb - 1)
+    b = b.astype(np.int32)
+    perm, inv = lsh.sort(torch.from_numpy(b).to(DEV), nb)
+    perm, inv = perm.cpu().numpy(), inv.cpu().numpy()
+    for h in range(H):
+        for r in range(nh):
+            p_ref, i_ref = oracle.sort(b[0, h, r])
+            assert np.array_equal(perm[0, h, r], p_ref)
+            assert np.array_equal(inv[0, h, r], i_ref)
+
+
+def _steps(w, seed=None):
+    qk, v, R, qk_t, v_t, R_t = _tensors(w, seed)
+    buckets, refined = lsh.hash(qk_t, R_t, w.n_buckets)
+    perm, inv = lsh.sort(buckets, w.n_buckets)
+    o, lse = lsh.chunk_attend(qk_t, v_t, buckets, perm, w.n_buckets, w.chunk_len, w.causal)
+    out = lsh.unsort_combine(o, lse, inv, dtype=qk_t.dtype)
+    fwd = lsh.attention_fwd(qk_t, v_t, R_t, w.n_buckets, w.chunk_len, w.causal)
+    torch.cuda.synchronize()
+    g = dict(buckets=buckets.cpu().numpy(), perm=perm.cpu().numpy(), inv=inv.cpu().numpy(),
+             o=o.cpu().numpy(), lse=lse.cpu().numpy(), out=out.float().cpu().numpy(),
+             fwd=fwd.float().cpu().numpy(), refined=refined)
+    return qk, v, R, g
+
+
+STEP_CASES = [
+    _wl("fp32", B=1, H=1, L=1024, d=64, nb=16, nh=1, m=64, causal=False, seed=1001),
+    _wl("bf16", B=2, H=2, L=1024, d=64, nb=64, nh=4, m=64, causal=True, seed=11),
+    _wl("bf16", B=1, H=2, L=2048, d=128, nb=128, nh=3, m=64, causal=True, seed=12),
+    _wl("bf16", B=1, H=2, L=1024, d=64, nb=32, nh=8, m=64, causal=False, seed=13,
+        dist="clusters"),
+    _wl("fp32", B=1, H=2, L=768, d=128, nb=8, nh=2, m=32, causal=True, seed=14),
+    _wl("bf16", B=1, H=1, L=256, d=64, nb=2, nh=2, m=256, causal=True, seed=15),
+    _wl("bf16", B=1, H=3, L=192, d=64, nb=4, nh=5, m=64, causal=False, seed=16),
+]
+
+
+def _wid(w):
+    return (f"{w.dtype}_B{w.B}H{w.H}L{w.L}d{w.d}nb{w.n_buckets}nh{w.n_hashes}m{w.chunk_len}"
+            f"c{int(w.causal)}_{w.qk_dist}")
+
+
+@pytest.mark.parametrize("w", STEP_CASES, ids=_wid)
+def test_steps_match_oracle(w):
+    qk, v, R, g = _steps(w)
+    tol = TOL[w.dtype]
+    ref_b, margin = _oracle_hash(qk, R, w.n_buckets)
+    near, differ = _check_buckets(g["buckets"], ref_b, margin)
+    worst_o = worst_l = worst_c = 0.0
+    for b in range(w.B):
+        for h in range(w.H):
+            os_, ls_, iv_ = [], [], []
+            for r in range(w.n_hashes):
+                bk = g["buckets"][b, h, r]
+                p_ref, i_ref = oracle.sort(bk)
+                assert np.array_equal(g["perm"][b, h, r], p_ref)
+                assert np.array_equal(g["inv"][b, h, r], i_ref)
+                o_ref, l_ref = oracle.attend(qk[b, h], v[b, h], bk, p_ref, w.chunk_len, w.causal)
+                worst_o = max(worst_o, float(np.abs(g["o"][b, h, r] - o_ref).max()))
+                worst_l = max(worst_l, float((np.abs(g["lse"][b, h, r] - l_ref) /
+                                              np.maximum(1.0, np.abs(l_ref))).max()))
+                os_.append(o_ref), ls_.append(l_ref), iv_.append(i_ref)
+            out_ref = oracle.combine(np.stack(os_), np.stack(ls_), np.stack(iv_))
+            worst_c = max(worst_c, float(np.abs(g["out"][b, h] - out_ref).max()))
+            # the GPU combine alone, fed the GPU's own per-round results
+            comb = oracle.combine(g["o"][b, h], g["lse"][b, h], g["inv"][b, h])
+            # fp32 arithmetic, plus one bf16 rounding of the output for bf16 I/O
+            rel = 1e-5 if w.dtype == "fp32" else 2.0 ** -8
+            assert np.all(np.abs(g["out"][b, h] - comb) <= rel * np.abs(comb) + 1e-5)
+    print(f"{w.name}: near-ties {near} differ {differ} refined {g['refined']} "
+          f"|o| {worst_o:.2e} lse {worst_l:.2e} out {worst_c:.2e}")
+    assert worst_o <= tol
+    assert worst_l <= (1e-5 if w.dtype == "fp32" else 1e-3)
+    assert worst_c <= tol
+    assert np.array_equal(g["out"], g["fwd"]), "fused forward differs from the staged calls"
+    assert np.isfinite(g["fwd"]).all()
+
+
+def test_forward_matches_oracle_forward():
+    w = _wl("bf16", B=1, H=2, L=2048, d=128, nb=64, nh=4, m=64, causal=True, seed=21)
+    qk, v, R, qk_t, v_t, R_t = _tensors(w)
+    out = torch.full_like(qk_t, float("nan"))
+    lsh.attention_fwd(qk_t, v_t, R_t, w.n_buckets, w.chunk_len, w.causal, out=out)
+    ref, extra = oracle.forward(qk, v, R, w.n_buckets, w.chunk_len, w.causal, return_all=True)
+    got = out.float().cpu().numpy()
+    assert np.isfinite(got).all()
+    assert np.abs(got - ref).max() <= TOL["bf16"]
+    # causal: position 0 only sees itself (up to one bf16 rounding of the output)
+    assert np.all(np.abs(got[:, :, 0] - v[:, :, 0]) <= 2.0 ** -8 * np.abs(v[:, :, 0]))
+
+
+def test_forward_is_deterministic():
+    w = _wl("bf16", B=1, H=4, L=4096, d=64, nb=128, nh=4, m=64, causal=True, seed=31)
+    qk, v, R, qk_t, v_t, R_t = _tensors(w)
+    a = lsh.attention_fwd(qk_t, v_t, R_t, w.n_buckets, w.chunk_len, w.causal)
+    b = lsh.attention_fwd(qk_t, v_t, R_t, w.n_buckets, w.chunk_len, w.causal)
+    assert torch.equal(a, b)
+
+
+def test_empty_problem_is_a_no_op():
+    qk = torch.empty((1, 2, 0, 64), dtype=torch.bfloat16, device=DEV)
+    R = torch.randn(2, 64, 8, device=DEV)
+    out = lsh.attention_fwd(qk, qk, R, 16, 64, True)
+    assert out.shape == (1, 2, 0, 64)
