@@ -80,6 +80,259 @@ __global__ __launch_bounds__(128) void attend_valu_kernel(const T* __restrict__ 
     lse_sorted[seg * L + s] = mx + logf(sum);
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core kernel (bf16 I/O, m = 64, d in {64, 128}).
+//
+// A workgroup (4 waves) walks a run of consecutive chunks of one (batch, head,
+// round) segment. LDS holds a ring of two chunks: the qk rows (row-major,
+// padded) and the v rows transposed (vt[feature][key]), keys indexed in ring
+// order (slot * 64 + row) -- the window of chunk c is simply both ring slots.
+// Each chunk's rows are gathered from HBM once, into registers, while the
+// previous chunk is being computed, and serve as the look-back of the next.
+//
+// Wave w owns queries 16w..16w+15 of the chunk:
+//   S^T = K Q^T   (v_mfma_f32_16x16x32_bf16; keys on rows, queries on lanes)
+//   mask, fp32 softmax in the exp2 domain
+//   O^T = V^T P^T (P^T comes straight from the S^T registers: the MFMA k-index
+//                  is mapped to keys in the order the lane already holds them)
+// Lane layout of v_mfma_f32_16x16x32_bf16: A[m][k] in lane m%16 + 16*(k/8),
+// element k%8; B[k][n] in lane n + 16*(k/8); D[m][n] in lane n + 16*(m/4),
+// register m%4.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kM = 64;            // chunk length of the matrix-core kernel
+constexpr int kWin = 2 * kM;      // keys in a window
+constexpr int kRun = 16;          // chunks per workgroup
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+template <int D>
+struct alignas(16) AttendLds {
+    static constexpr int KS = D + 8;       // padded row of qk (bf16 elements)
+    static constexpr int VS = kWin + 8;    // padded row of vt (bf16 elements)
+    uint16_t k[2][kM][KS];
+    uint16_t vt[D][VS];
+    int32_t pos[kWin];
+    int32_t bkt[kWin];
+    int32_t nperm[2][kM];
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __restrict__ qk,
+                                                          const uint16_t* __restrict__ v,
+                                                          const int32_t* __restrict__ buckets,
+                                                          const int32_t* __restrict__ perm,
+                                                          Dims dm, int nruns,
+                                                          float* __restrict__ o_sorted,
+                                                          float* __restrict__ lse_sorted) {
+    constexpr int PIECES = D / 8;              // 16-byte pieces per row
+    constexpr int QPT = kM * PIECES / 256;     // qk pieces per thread
+    constexpr int QROWS = 256 / PIECES;        // rows covered per pass
+    constexpr int VPT = D / 64;                // (key pair, 8 features) items per thread
+    constexpr int KSTEPS = D / 32;
+    constexpr int DT = D / 16;                 // output feature tiles
+    __shared__ AttendLds<D> sm;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, r16 = lane & 15;
+    const int64_t seg = blockIdx.x / nruns;
+    const int run = blockIdx.x - (int)(seg * nruns);
+    const int64_t L = dm.L;
+    const int nchunks = dm.L / kM;
+    const int c0 = run * kRun;
+    const int c1 = min(c0 + kRun, nchunks);
+    const int64_t bh = seg / dm.nh;
+    const int32_t* P = perm + seg * L;
+    const int32_t* Bk = buckets + seg * L;
+    const uint16_t* X = qk + bh * L * D;
+    const uint16_t* V = v + bh * L * D;
+    const float c_log2 = 1.4426950408889634f / sqrtf((float)D);   // log2(e) / sqrt(d)
+    const float pen2 = kSelfPenalty * 1.4426950408889634f;
+
+    u32x4 qreg[QPT];
+    u32x4 vreg[VPT][2];
+    int my_pos = 0, my_bkt = 0;
+
+    // gather the rows of one chunk (positions from an LDS perm buffer) into registers
+    auto issue_rows = [&](const int32_t* pl) {
+#pragma unroll
+        for (int j = 0; j < QPT; ++j) {
+            const int row = tid / PIECES + QROWS * j;
+            qreg[j] = *(const u32x4*)(X + (int64_t)pl[row] * D + (tid % PIECES) * 8);
+        }
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            const int pr = tid & 31, ddg = (tid >> 5) + 8 * j;
+            vreg[j][0] = *(const u32x4*)(V + (int64_t)pl[2 * pr] * D + ddg * 8);
+            vreg[j][1] = *(const u32x4*)(V + (int64_t)pl[2 * pr + 1] * D + ddg * 8);
+        }
+    };
+    // registers -> ring slot
+    auto store_rows = [&](int slot) {
+#pragma unroll
+        for (int j = 0; j < QPT; ++j) {
+            const int row = tid / PIECES + QROWS * j;
+            *(u32x4*)&sm.k[slot][row][(tid % PIECES) * 8] = qreg[j];
+        }
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            const int pr = tid & 31, ddg = (tid >> 5) + 8 * j;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t lo = (vreg[j][0][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                const uint32_t hi = (vreg[j][1][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                *(uint32_t*)&sm.vt[ddg * 8 + e][slot * kM + 2 * pr] = lo | (hi << 16);
+            }
+        }
+        if (tid < kM) {
+            sm.pos[slot * kM + tid] = my_pos;
+            sm.bkt[slot * kM + tid] = my_bkt;
+        }
+    };
+
+    // ---- prologue: look-back chunk c0-1 (or an empty slot), then chunk c0 in flight
+    {
+        const int slot = (c0 + 1) & 1;   // slot of chunk c0-1
+        if (c0 > 0) {
+            if (tid < kM) {
+                my_pos = P[(int64_t)(c0 - 1) * kM + tid];
+                my_bkt = Bk[my_pos];
+                sm.nperm[0][tid] = my_pos;
+            }
+            __syncthreads();
+            issue_rows(sm.nperm[0]);
+            store_rows(slot);
+        } else {
+            for (int k = tid; k < kM * AttendLds<D>::KS; k += 256) (&sm.k[slot][0][0])[k] = 0;
+            for (int k = tid; k < D * kM; k += 256) sm.vt[k / kM][slot * kM + k % kM] = 0;
+            if (tid < kM) {
+                sm.pos[slot * kM + tid] = 0;
+                sm.bkt[slot * kM + tid] = -1;   // never equal to a bucket id
+            }
+        }
+        __syncthreads();
+        if (tid < kM) {
+            my_pos = P[(int64_t)c0 * kM + tid];
+            sm.nperm[c0 & 1][tid] = my_pos;
+            my_bkt = Bk[my_pos];
+            if (c0 + 1 < c1) sm.nperm[(c0 + 1) & 1][tid] = P[(int64_t)(c0 + 1) * kM + tid];
+        }
+        __syncthreads();
+        issue_rows(sm.nperm[c0 & 1]);
+    }
+
+    for (int c = c0; c < c1; ++c) {
+        const int cs = c & 1;
+        store_rows(cs);
+        __syncthreads();
+        // next chunk's rows and the chunk after's perm are fetched while this one computes
+        int pf = 0;
+        if (c + 1 < c1) {
+            const int32_t* pl = sm.nperm[(c + 1) & 1];
+            if (tid < kM) {
+                my_pos = pl[tid];
+                my_bkt = Bk[my_pos];
+            }
+            issue_rows(pl);
+            if (c + 2 < c1 && tid < kM) pf = P[(int64_t)(c + 2) * kM + tid];
+        }
+
+        // ---- S^T = K Q^T
+        const int qrow = 16 * wave + r16;
+        bf16x8 qf[KSTEPS];
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s)
+            qf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.k[cs][qrow][32 * s + 8 * g]);
+        const int qpos = sm.pos[cs * kM + qrow];
+        const int qb = sm.bkt[cs * kM + qrow];
+        f32x4 st[8];
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt) {
+            st[kt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KSTEPS; ++s) {
+                const bf16x8 a = __builtin_bit_cast(
+                    bf16x8, *(const u32x4*)&sm.k[kt >> 2][(kt & 3) * 16 + r16][32 * s + 8 * g]);
+                st[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[s], st[kt], 0, 0, 0);
+            }
+        }
+        // ---- mask and softmax (exp2 domain); lane holds keys kt*16 + 4g + i of query r16
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt) {
+            const i32x4 kb = *(const i32x4*)&sm.bkt[kt * 16 + 4 * g];
+            const i32x4 kp = *(const i32x4*)&sm.pos[kt * 16 + 4 * g];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float s2 = st[kt][i] * c_log2;
+                if (kp[i] == qpos) s2 -= pen2;
+                const bool ok = kb[i] == qb && (!dm.causal || kp[i] <= qpos);
+                s2 = ok ? s2 : -INFINITY;
+                st[kt][i] = s2;
+                mx = fmaxf(mx, s2);
+            }
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        float sum = 0.f, sumr = 0.f;
+        u32x4 pfrag[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                float pr[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pr[i] = exp2f(st[2 * kb + h][i] - mx);
+                    sum += pr[i];
+                }
+                const uint32_t w0 = pack_bf16x2(pr[0], pr[1]), w1 = pack_bf16x2(pr[2], pr[3]);
+                sumr += __uint_as_float(w0 << 16) + __uint_as_float(w0 & 0xFFFF0000u) +
+                        __uint_as_float(w1 << 16) + __uint_as_float(w1 & 0xFFFF0000u);
+                pfrag[kb][2 * h] = w0;
+                pfrag[kb][2 * h + 1] = w1;
+            }
+        }
+        sum += __shfl_xor(sum, 16);
+        sum += __shfl_xor(sum, 32);
+        sumr += __shfl_xor(sumr, 16);
+        sumr += __shfl_xor(sumr, 32);
+
+        // ---- O^T = V^T P^T; MFMA k-index 8g+e <-> key kb*32 + 4g + e (e<4), kb*32+16+4g+e-4
+        f32x4 oacc[DT];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const bf16x8 bfr = __builtin_bit_cast(bf16x8, pfrag[kb]);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const uint16_t* row = &sm.vt[dt * 16 + r16][kb * 32 + 4 * g];
+                const u32x2 lo = *(const u32x2*)row;
+                const u32x2 hi = *(const u32x2*)(row + 16);
+                const u32x4 af = {lo.x, lo.y, hi.x, hi.y};
+                oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af),
+                                                                   bfr, oacc[dt], 0, 0, 0);
+            }
+        }
+        const float inv = 1.0f / sumr;
+        const int64_t slot = seg * L + (int64_t)c * kM + qrow;
+        float* orow = o_sorted + slot * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) *(f32x4*)(orow + dt * 16 + 4 * g) = oacc[dt] * inv;
+        if (g == 0) lse_sorted[slot] = (mx + log2f(sum)) * 0.6931471805599453f;
+
+        if (c + 2 < c1 && tid < kM) sm.nperm[c & 1][tid] = pf;
+        __syncthreads();
+    }
+}
+
 template <typename T>
 static void launch_valu(const T* qk, const T* v, const int32_t* buckets, const int32_t* perm,
                         const Dims& d, float* o, float* lse, hipStream_t st) {
@@ -93,6 +346,20 @@ static void launch_valu(const T* qk, const T* v, const int32_t* buckets, const i
 hipError_t launch_attend(const void* qk, const void* v, const int32_t* buckets,
                          const int32_t* perm, const Dims& d, float* o_sorted, float* lse_sorted,
                          hipStream_t st, hipEvent_t* ev, int* nev, const char** names) {
+    if (d.dtype == LSH_BF16 && d.m == kM) {
+        const int nchunks = d.L / kM;
+        const int nruns = (nchunks + kRun - 1) / kRun;
+        const unsigned grid = (unsigned)(d.segs * nruns);
+        const uint16_t* x = (const uint16_t*)qk;
+        const uint16_t* vv = (const uint16_t*)v;
+        if (d.d == 64)
+            attend_mfma_kernel<64><<<grid, 256, 0, st>>>(x, vv, buckets, perm, d, nruns, o_sorted,
+                                                         lse_sorted);
+        else
+            attend_mfma_kernel<128><<<grid, 256, 0, st>>>(x, vv, buckets, perm, d, nruns, o_sorted,
+                                                          lse_sorted);
+        return mark(st, ev, nev, names, "attend_mfma");
+    }
     if (d.dtype == LSH_BF16)
         launch_valu((const uint16_t*)qk, (const uint16_t*)v, buckets, perm, d, o_sorted, lse_sorted,
                     st);

@@ -164,6 +164,10 @@ STEP_CASES = [
     _wl("fp32", B=1, H=2, L=768, d=128, nb=8, nh=2, m=32, causal=True, seed=14),
     _wl("bf16", B=1, H=1, L=256, d=64, nb=2, nh=2, m=256, causal=True, seed=15),
     _wl("bf16", B=1, H=3, L=192, d=64, nb=4, nh=5, m=64, causal=False, seed=16),
+    _wl("bf16", B=2, H=1, L=64, d=128, nb=8, nh=3, m=64, causal=True, seed=17),
+    _wl("bf16", B=1, H=2, L=64 * 17, d=64, nb=16, nh=2, m=64, causal=False, seed=18),
+    _wl("bf16", B=1, H=2, L=64 * 33, d=128, nb=64, nh=2, m=64, causal=True, seed=19,
+        dist="clusters"),
 ]
 
 
