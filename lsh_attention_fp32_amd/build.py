@@ -24,7 +24,10 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # Packed-fp32 instructions are disabled for every kernel; the flag belongs to
 # the device compiler (the host pass warns that it does not know it).
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                # keep MFMA accumulators in VGPRs: the epilogues read every
+                # accumulator once, and AGPR accumulators would each need a copy
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", str(INCLUDE), "-I",
           str(CSRC), "-Wall", "-Wno-unused-result"]
 

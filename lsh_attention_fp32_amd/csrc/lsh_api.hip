@@ -55,7 +55,7 @@ int validate(const lsh_shape_t* s) {
 bool empty(const lsh_shape_t* s) { return s->B == 0 || s->H == 0 || s->L == 0; }
 
 struct FwdLayout {
-    size_t hash, sort, buckets, perm, inv, lse, o, total;
+    size_t hash, sort, buckets, perm, inv, lse, vmax, o, total;
 };
 
 FwdLayout fwd_layout(const Dims& d) {
@@ -74,8 +74,10 @@ FwdLayout fwd_layout(const Dims& d) {
     off += align_up(sizeof(int32_t) * n, 256);
     f.lse = off;
     off += align_up(sizeof(float) * n, 256);
+    f.vmax = off;
+    off += 256;
     f.o = off;
-    off += align_up(sizeof(float) * n * d.d, 256);
+    off += align_up((compact_o_sorted(d) ? 2 : sizeof(float)) * n * d.d, 256);
     f.total = off;
     return f;
 }
@@ -101,13 +103,16 @@ int run_fwd(const void* qk, const void* v, const float* R, const lsh_shape_t* sh
     int32_t* perm = (int32_t*)(base + f.perm);
     int32_t* inv = (int32_t*)(base + f.inv);
     float* lse = (float*)(base + f.lse);
-    float* o = (float*)(base + f.o);
+    const OSorted o{base + f.o, compact_o_sorted(d), (const uint32_t*)(base + f.vmax)};
     hipError_t e;
     if ((e = launch_hash(qk, R, d, buckets, carve_hash_workspace(base + f.hash, d), st, ev, nev,
                          names)) != hipSuccess)
         return hip_fail(e, "hash");
     if ((e = launch_sort(buckets, d, perm, inv, base + f.sort, st, ev, nev, names)) != hipSuccess)
         return hip_fail(e, "sort");
+    if (o.half && (e = launch_vmax(v, d, (uint32_t*)(base + f.vmax), st, ev, nev, names)) !=
+                      hipSuccess)
+        return hip_fail(e, "vmax");
     if ((e = launch_attend(qk, v, buckets, perm, d, o, lse, st, ev, nev, names)) != hipSuccess)
         return hip_fail(e, "chunk_attend");
     if ((e = launch_combine(o, lse, inv, d, out, st, ev, nev, names)) != hipSuccess)
@@ -174,7 +179,8 @@ int lsh_chunk_attend(const void* qk, const void* v, const int32_t* buckets, cons
     if (!qk || !v || !buckets || !perm || !o_sorted || !lse_sorted)
         return fail(LSH_ERR_ARG, "lsh_chunk_attend: NULL tensor pointer");
     const Dims d = make_dims(*shape);
-    hipError_t e = launch_attend(qk, v, buckets, perm, d, o_sorted, lse_sorted, (hipStream_t)stream,
+    const OSorted o{o_sorted, false, nullptr};
+    hipError_t e = launch_attend(qk, v, buckets, perm, d, o, lse_sorted, (hipStream_t)stream,
                                  nullptr, nullptr, nullptr);
     if (e == hipSuccess) e = hipGetLastError();
     return e == hipSuccess ? LSH_OK : hip_fail(e, "lsh_chunk_attend");
@@ -189,7 +195,8 @@ int lsh_unsort_combine(const float* o_sorted, const float* lse_sorted, const int
     if (!o_sorted || !lse_sorted || !inv || !out)
         return fail(LSH_ERR_ARG, "lsh_unsort_combine: NULL tensor pointer");
     const Dims d = make_dims(*shape);
-    hipError_t e = launch_combine(o_sorted, lse_sorted, inv, d, out, (hipStream_t)stream, nullptr,
+    const OSorted o{(void*)o_sorted, false, nullptr};
+    hipError_t e = launch_combine(o, lse_sorted, inv, d, out, (hipStream_t)stream, nullptr,
                                   nullptr, nullptr);
     if (e == hipSuccess) e = hipGetLastError();
     return e == hipSuccess ? LSH_OK : hip_fail(e, "lsh_unsort_combine");

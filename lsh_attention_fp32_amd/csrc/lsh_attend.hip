@@ -11,6 +11,8 @@
 // (chunk 0 has no look-back, rounds never mix). Valid key: same bucket and,
 // when causal, key position <= query position. A query's score against itself
 // is lowered by kSelfPenalty, so it only counts when nothing else is valid.
+#include <algorithm>
+
 #include "lsh_internal.h"
 
 namespace lsh {
@@ -103,6 +105,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kM = 64;            // chunk length of the matrix-core kernel
 constexpr int kWin = 2 * kM;      // keys in a window
@@ -123,13 +126,14 @@ struct alignas(16) AttendLds {
     int32_t nperm[2][kM];
 };
 
-template <int D>
+template <int D, bool HALF>
 __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __restrict__ qk,
                                                           const uint16_t* __restrict__ v,
                                                           const int32_t* __restrict__ buckets,
                                                           const int32_t* __restrict__ perm,
                                                           Dims dm, int nruns,
-                                                          float* __restrict__ o_sorted,
+                                                          void* __restrict__ o_sorted,
+                                                          const uint32_t* __restrict__ vmax,
                                                           float* __restrict__ lse_sorted) {
     constexpr int PIECES = D / 8;              // 16-byte pieces per row
     constexpr int QPT = kM * PIECES / 256;     // qk pieces per thread
@@ -154,6 +158,7 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
     const uint16_t* V = v + bh * L * D;
     const float c_log2 = 1.4426950408889634f / sqrtf((float)D);   // log2(e) / sqrt(d)
     const float pen2 = kSelfPenalty * 1.4426950408889634f;
+    const float oscale = HALF ? o_scale(*vmax) : 1.0f;
 
     u32x4 qreg[QPT];
     u32x4 vreg[VPT][2];
@@ -321,12 +326,26 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
                                                                    bfr, oacc[dt], 0, 0, 0);
             }
         }
-        const float inv = 1.0f / sumr;
         const int64_t slot = seg * L + (int64_t)c * kM + qrow;
-        float* orow = o_sorted + slot * D;
+        // by sorted slot (fp32), or -- in the fused forward -- already un-sorted:
+        // row (b, h, position, round) in scaled fp16, so the combine streams
+        const int64_t orow_idx = HALF ? (bh * L + qpos) * dm.nh + (seg - bh * dm.nh) : slot;
+        if constexpr (HALF) {
+            const float inv = oscale / sumr;
+            _Float16* orow = (_Float16*)o_sorted + orow_idx * D;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) *(f32x4*)(orow + dt * 16 + 4 * g) = oacc[dt] * inv;
-        if (g == 0) lse_sorted[slot] = (mx + log2f(sum)) * 0.6931471805599453f;
+            for (int dt = 0; dt < DT; ++dt) {
+                const f32x4 o = oacc[dt] * inv;
+                f16x4 h = {(_Float16)o.x, (_Float16)o.y, (_Float16)o.z, (_Float16)o.w};
+                *(f16x4*)(orow + dt * 16 + 4 * g) = h;
+            }
+        } else {
+            const float inv = 1.0f / sumr;
+            float* orow = (float*)o_sorted + slot * D;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) *(f32x4*)(orow + dt * 16 + 4 * g) = oacc[dt] * inv;
+        }
+        if (g == 0) lse_sorted[orow_idx] = (mx + log2f(sum)) * 0.6931471805599453f;
 
         if (c + 2 < c1 && tid < kM) sm.nperm[c & 1][tid] = pf;
         __syncthreads();
@@ -343,8 +362,37 @@ static void launch_valu(const T* qk, const T* v, const int32_t* buckets, const i
         attend_valu_kernel<128, T><<<grid, 128, 0, st>>>(qk, v, buckets, perm, d, o, lse);
 }
 
+// max|v| as a bf16 bit pattern (atomic max over the 15 magnitude bits, order
+// independent); *vmax must be 0 on entry.
+__global__ __launch_bounds__(256) void vmax_kernel(const uint16_t* __restrict__ v, int64_t n,
+                                                   uint32_t* __restrict__ vmax) {
+    uint32_t m = 0;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x * 8;
+    for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8; i < n; i += stride) {
+        const u32x4 w = *(const u32x4*)(v + i);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m = max(m, max(w[e] & 0x7FFFu, (w[e] >> 16) & 0x7FFFu));
+    }
+    for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+    __shared__ uint32_t wmax[4];
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) atomicMax(vmax, max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3])));
+}
+
+__global__ void zero_u32_kernel(uint32_t* p) { *p = 0u; }
+
+hipError_t launch_vmax(const void* v, const Dims& d, uint32_t* vmax, hipStream_t st,
+                       hipEvent_t* ev, int* nev, const char** names) {
+    zero_u32_kernel<<<1, 1, 0, st>>>(vmax);
+    const int64_t n = d.T * d.d;   // a multiple of 8 (d is 64 or 128)
+    const unsigned grid = (unsigned)std::min<int64_t>(2048, (n / 8 + 255) / 256 + 1);
+    vmax_kernel<<<grid, 256, 0, st>>>((const uint16_t*)v, n, vmax);
+    return mark(st, ev, nev, names, "vmax");
+}
+
 hipError_t launch_attend(const void* qk, const void* v, const int32_t* buckets,
-                         const int32_t* perm, const Dims& d, float* o_sorted, float* lse_sorted,
+                         const int32_t* perm, const Dims& d, const OSorted& o, float* lse_sorted,
                          hipStream_t st, hipEvent_t* ev, int* nev, const char** names) {
     if (d.dtype == LSH_BF16 && d.m == kM) {
         const int nchunks = d.L / kM;
@@ -352,19 +400,28 @@ hipError_t launch_attend(const void* qk, const void* v, const int32_t* buckets,
         const unsigned grid = (unsigned)(d.segs * nruns);
         const uint16_t* x = (const uint16_t*)qk;
         const uint16_t* vv = (const uint16_t*)v;
-        if (d.d == 64)
-            attend_mfma_kernel<64><<<grid, 256, 0, st>>>(x, vv, buckets, perm, d, nruns, o_sorted,
-                                                         lse_sorted);
-        else
-            attend_mfma_kernel<128><<<grid, 256, 0, st>>>(x, vv, buckets, perm, d, nruns, o_sorted,
-                                                          lse_sorted);
+        if (o.half) {
+            if (d.d == 64)
+                attend_mfma_kernel<64, true><<<grid, 256, 0, st>>>(x, vv, buckets, perm, d, nruns,
+                                                                   o.ptr, o.vmax, lse_sorted);
+            else
+                attend_mfma_kernel<128, true><<<grid, 256, 0, st>>>(x, vv, buckets, perm, d, nruns,
+                                                                    o.ptr, o.vmax, lse_sorted);
+        } else {
+            if (d.d == 64)
+                attend_mfma_kernel<64, false><<<grid, 256, 0, st>>>(x, vv, buckets, perm, d, nruns,
+                                                                    o.ptr, nullptr, lse_sorted);
+            else
+                attend_mfma_kernel<128, false><<<grid, 256, 0, st>>>(x, vv, buckets, perm, d, nruns,
+                                                                     o.ptr, nullptr, lse_sorted);
+        }
         return mark(st, ev, nev, names, "attend_mfma");
     }
+    float* of = (float*)o.ptr;
     if (d.dtype == LSH_BF16)
-        launch_valu((const uint16_t*)qk, (const uint16_t*)v, buckets, perm, d, o_sorted, lse_sorted,
-                    st);
+        launch_valu((const uint16_t*)qk, (const uint16_t*)v, buckets, perm, d, of, lse_sorted, st);
     else
-        launch_valu((const float*)qk, (const float*)v, buckets, perm, d, o_sorted, lse_sorted, st);
+        launch_valu((const float*)qk, (const float*)v, buckets, perm, d, of, lse_sorted, st);
     return mark(st, ev, nev, names, "attend_fp32");
 }
 

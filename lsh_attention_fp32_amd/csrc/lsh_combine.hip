@@ -6,20 +6,52 @@
 // it by exp(lse_r - logsumexp_r lse_r) gives one softmax over every (round,
 // key) hit.
 //
-// One thread per (token, 4 features): the rounds' slots come through inv, the
-// float32 rows of o_sorted are read as 16-byte vectors.
+// One thread per (token, 8 features): the rounds' slots come through inv, the
+// float32 rows of o_sorted are read as 16-byte vectors and the outputs are
+// written with one vector store per thread.
 #include "lsh_internal.h"
 
 namespace lsh {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Stores 8 consecutive outputs with one vector store.
+__device__ __forceinline__ void store8(float* p, const f32x4& a, const f32x4& b) {
+    *(f32x4*)p = a;
+    *(f32x4*)(p + 4) = b;
+}
+__device__ __forceinline__ void store8(uint16_t* p, const f32x4& a, const f32x4& b) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 w;
+    w.x = (uint32_t)f32_to_bf16(a.x) | ((uint32_t)f32_to_bf16(a.y) << 16);
+    w.y = (uint32_t)f32_to_bf16(a.z) | ((uint32_t)f32_to_bf16(a.w) << 16);
+    w.z = (uint32_t)f32_to_bf16(b.x) | ((uint32_t)f32_to_bf16(b.y) << 16);
+    w.w = (uint32_t)f32_to_bf16(b.z) | ((uint32_t)f32_to_bf16(b.w) << 16);
+    *(u32x4*)p = w;
+}
+
+// 8 consecutive per-round outputs of one row, as two float4.
+template <bool HALF>
+__device__ __forceinline__ void load8(const void* base, int64_t off, f32x4& a, f32x4& b) {
+    if constexpr (HALF) {
+        typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+        const f16x8 h = *(const f16x8*)((const _Float16*)base + off);
+        a = (f32x4){(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+        b = (f32x4){(float)h[4], (float)h[5], (float)h[6], (float)h[7]};
+    } else {
+        a = *(const f32x4*)((const float*)base + off);
+        b = *(const f32x4*)((const float*)base + off + 4);
+    }
+}
+
+// Staged form: per-round rows by sorted slot, reached through inv.
 template <int D, typename T>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o_sorted,
                                                       const float* __restrict__ lse,
                                                       const int32_t* __restrict__ inv, Dims dm,
                                                       T* __restrict__ out) {
-    constexpr int TPT = D / 4;   // threads per token
+    constexpr int TPT = D / 8;   // threads per token, 8 features each
+    constexpr int G = 8;         // rounds whose loads are issued together
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t tok = gid / TPT;
     const int q = (int)(gid - tok * TPT);
@@ -28,47 +60,125 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     const int64_t bh = tok / L;
     const int64_t i = tok - bh * L;
     const int64_t seg0 = bh * dm.nh;
-    float mx = -INFINITY;
-    for (int r = 0; r < dm.nh; ++r) {
-        const int64_t row = (seg0 + r) * L;
-        mx = fmaxf(mx, lse[row + inv[row + i]]);
-    }
-    // exp(l_r - Z) is evaluated as exp(l_r - max) / sum_r exp(l_r - max): forming
-    // Z = max + log(sum) first would round it to the spacing of floats near |max|,
-    // which is 2^-7 when a round saw only the query itself (l_r ~ -1e5).
-    float sum = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int r = 0; r < dm.nh; ++r) {
-        const int64_t row = (seg0 + r) * L;
-        const int64_t s = inv[row + i];
-        const float e = expf(lse[row + s] - mx);
-        const f32x4 o = *(const f32x4*)(o_sorted + (row + s) * D + 4 * q);
-        sum += e;
-        acc += e * o;
+    // exp(l_r - Z) is evaluated as exp(l_r - max) / sum_r exp(l_r - max) with a
+    // running max: forming Z = max + log(sum) first would round it to the spacing
+    // of floats near |max|, which is 2^-7 when a round saw only the query itself
+    // (l_r ~ -1e5).
+    float mx = -INFINITY, sum = 0.f;
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+    for (int r0 = 0; r0 < dm.nh; r0 += G) {
+        const int n = min(G, dm.nh - r0);
+        int64_t slot[G];
+        float l[G];
+        f32x4 o0[G], o1[G];
+#pragma unroll
+        for (int k = 0; k < G; ++k)
+            if (k < n) slot[k] = (seg0 + r0 + k) * L + inv[(seg0 + r0 + k) * L + i];
+#pragma unroll
+        for (int k = 0; k < G; ++k)
+            if (k < n) {
+                l[k] = lse[slot[k]];
+                load8<false>(o_sorted, slot[k] * D + 8 * q, o0[k], o1[k]);
+            }
+        float gmx = mx;
+#pragma unroll
+        for (int k = 0; k < G; ++k)
+            if (k < n) gmx = fmaxf(gmx, l[k]);
+        const float rescale = expf(mx - gmx);   // 0 on the first group (mx = -inf)
+        sum *= rescale;
+        a0 *= rescale;
+        a1 *= rescale;
+#pragma unroll
+        for (int k = 0; k < G; ++k)
+            if (k < n) {
+                const float e = expf(l[k] - gmx);
+                sum += e;
+                a0 += e * o0[k];
+                a1 += e * o1[k];
+            }
+        mx = gmx;
     }
     const float inv_sum = 1.0f / sum;
+    store8(out + tok * D + 8 * q, a0 * inv_sum, a1 * inv_sum);
+}
+
+// Fused form: the chunk kernel already stored every round's row of a token
+// next to each other ([token][round][d], scaled fp16; lse [token][round]), so
+// the un-sort is done and this pass reads one contiguous block per token.
+template <int D, typename T>
+__global__ __launch_bounds__(256) void combine_bypos_kernel(const _Float16* __restrict__ o_pos,
+                                                            const uint32_t* __restrict__ vmax,
+                                                            const float* __restrict__ lse,
+                                                            Dims dm, T* __restrict__ out) {
+    constexpr int TPT = D / 8;
+    constexpr int G = 8;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t tok = gid / TPT;
+    const int q = (int)(gid - tok * TPT);
+    if (tok >= dm.T) return;
+    const int64_t row0 = tok * dm.nh;
+    float mx = -INFINITY, sum = 0.f;
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+    for (int r0 = 0; r0 < dm.nh; r0 += G) {
+        const int n = min(G, dm.nh - r0);
+        float l[G];
+        f32x4 o0[G], o1[G];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) IO<T>::store(out, tok * D + 4 * q + e, acc[e] * inv_sum);
+        for (int k = 0; k < G; ++k)
+            if (k < n) {
+                l[k] = lse[row0 + r0 + k];
+                load8<true>(o_pos, (row0 + r0 + k) * D + 8 * q, o0[k], o1[k]);
+            }
+        float gmx = mx;
+#pragma unroll
+        for (int k = 0; k < G; ++k)
+            if (k < n) gmx = fmaxf(gmx, l[k]);
+        const float rescale = expf(mx - gmx);
+        sum *= rescale;
+        a0 *= rescale;
+        a1 *= rescale;
+#pragma unroll
+        for (int k = 0; k < G; ++k)
+            if (k < n) {
+                const float e = expf(l[k] - gmx);
+                sum += e;
+                a0 += e * o0[k];
+                a1 += e * o1[k];
+            }
+        mx = gmx;
+    }
+    // the rows carry the power-of-two scale chosen from max|v|
+    const float inv_sum = 1.0f / (o_scale(*vmax) * sum);
+    store8(out + tok * D + 8 * q, a0 * inv_sum, a1 * inv_sum);
 }
 
 template <typename T>
-static void launch_t(const float* o, const float* lse, const int32_t* inv, const Dims& d, T* out,
+static void launch_t(const OSorted& o, const float* lse, const int32_t* inv, const Dims& d, T* out,
                      hipStream_t st) {
-    const int64_t threads = d.T * (d.d / 4);
+    const int64_t threads = d.T * (d.d / 8);
     const unsigned grid = (unsigned)((threads + 255) / 256);
-    if (d.d == 64)
-        combine_kernel<64, T><<<grid, 256, 0, st>>>(o, lse, inv, d, out);
-    else
-        combine_kernel<128, T><<<grid, 256, 0, st>>>(o, lse, inv, d, out);
+    if (o.half) {
+        const _Float16* op = (const _Float16*)o.ptr;
+        if (d.d == 64)
+            combine_bypos_kernel<64, T><<<grid, 256, 0, st>>>(op, o.vmax, lse, d, out);
+        else
+            combine_bypos_kernel<128, T><<<grid, 256, 0, st>>>(op, o.vmax, lse, d, out);
+    } else {
+        const float* op = (const float*)o.ptr;
+        if (d.d == 64)
+            combine_kernel<64, T><<<grid, 256, 0, st>>>(op, lse, inv, d, out);
+        else
+            combine_kernel<128, T><<<grid, 256, 0, st>>>(op, lse, inv, d, out);
+    }
 }
 
-hipError_t launch_combine(const float* o_sorted, const float* lse_sorted, const int32_t* inv,
+hipError_t launch_combine(const OSorted& o, const float* lse_sorted, const int32_t* inv,
                           const Dims& d, void* out, hipStream_t st, hipEvent_t* ev, int* nev,
                           const char** names) {
     if (d.dtype == LSH_BF16)
-        launch_t(o_sorted, lse_sorted, inv, d, (uint16_t*)out, st);
+        launch_t<uint16_t>(o, lse_sorted, inv, d, (uint16_t*)out, st);
     else
-        launch_t(o_sorted, lse_sorted, inv, d, (float*)out, st);
+        launch_t<float>(o, lse_sorted, inv, d, (float*)out, st);
     return mark(st, ev, nev, names, "combine");
 }
 

@@ -51,9 +51,10 @@ struct RefineItem {
 };
 
 struct HashWorkspace {
-    int32_t* counter;     // [1] number of queued items (also the public count)
+    int32_t* counter;     // [3] queued items: total (the public count), front, back
     float* rnorm;         // [nh] max column 2-norm of R per round, rounded up
     uint16_t* rfrag;      // bf16 hi/lo split of R in matrix-core fragment order
+    float* rt;            // R transposed to [nh][ntiles*32][d], fp32
     RefineItem* queue;    // [T*nh]
 };
 size_t hash_workspace_bytes(const Dims& d);
@@ -75,14 +76,40 @@ hipError_t launch_sort(const int32_t* buckets, const Dims& d, int32_t* perm, int
                        void* ws, hipStream_t st, hipEvent_t* ev, int* nev, const char** names);
 
 // ------------------------------------------------------------ attend stage
+// Per-round outputs: float32 by sorted slot ([B,H,nh,L,d], with lse
+// [B,H,nh,L]) for the staged entry points; inside the fused forward on the
+// matrix-core path ("half"), fp16 multiplied by a power of two derived from
+// max|v| (o_scale), so no value can overflow, stored already un-sorted by
+// position ([B,H,L,nh,d], with lse [B,H,L,nh]).
+struct OSorted {
+    void* ptr;                  // float* or _Float16*
+    bool half;                  // fp16 by position
+    const uint32_t* vmax;       // bf16 bit pattern of max|v| (used when half)
+};
+
+// True when the fused forward can keep o_sorted in scaled fp16.
+inline bool compact_o_sorted(const Dims& d) { return d.dtype == LSH_BF16 && d.m == 64; }
+
+hipError_t launch_vmax(const void* v, const Dims& d, uint32_t* vmax, hipStream_t st,
+                       hipEvent_t* ev, int* nev, const char** names);
 hipError_t launch_attend(const void* qk, const void* v, const int32_t* buckets,
-                         const int32_t* perm, const Dims& d, float* o_sorted, float* lse_sorted,
+                         const int32_t* perm, const Dims& d, const OSorted& o, float* lse_sorted,
                          hipStream_t st, hipEvent_t* ev, int* nev, const char** names);
 
 // ----------------------------------------------------------- combine stage
-hipError_t launch_combine(const float* o_sorted, const float* lse_sorted, const int32_t* inv,
+hipError_t launch_combine(const OSorted& o, const float* lse_sorted, const int32_t* inv,
                           const Dims& d, void* out, hipStream_t st, hipEvent_t* ev, int* nev,
                           const char** names);
+
+// Power of two s with max|v| * s <= 2^14: fp16 then holds every |o| <= max|v|.
+__device__ __forceinline__ float o_scale(uint32_t vmax_bf16) {
+    const uint32_t bits = (vmax_bf16 & 0x7FFFu) << 16;
+    if (bits == 0) return 1.0f;
+    const int e = (int)(bits >> 23) - 127;   // max|v| < 2^(e+1)
+    int k = 14 - (e + 1);
+    k = k < -126 ? -126 : (k > 100 ? 100 : k);
+    return __uint_as_float((uint32_t)(k + 127) << 23);
+}
 
 // Records a timing event after a kernel when the caller asked for timing.
 inline hipError_t mark(hipStream_t st, hipEvent_t* ev, int* nev, const char** names,

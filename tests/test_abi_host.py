@@ -65,11 +65,15 @@ def test_workspace_size_rejects_bad_shapes(lib, kw, code):
 
 
 def test_workspace_sizes_are_consistent(lib):
+    # the fused forward keeps per-round outputs in fp16 on the bf16 matrix-core
+    # path (chunk 64) and in fp32 otherwise
+    for dtype, m, o_bytes in ((lsh.LSH_BF16, 64, 2), (lsh.LSH_F32, 64, 4), (lsh.LSH_BF16, 32, 4)):
+        s = _shape(dtype=dtype, chunk_len=m)
+        h, so, f = (lsh.lsh_workspace_size(k, s) for k in ("hash", "sort", "fwd"))
+        n = s.B * s.H * s.n_hashes * s.L
+        assert h > 0 and so > 0
+        assert f >= h + so + n * (4 * 4 + o_bytes * s.d)
     s = _shape()
-    h, so, f = (lsh.lsh_workspace_size(k, s) for k in ("hash", "sort", "fwd"))
-    n = s.B * s.H * s.n_hashes * s.L
-    assert h > 0 and so > 0
-    assert f >= h + so + n * (4 * 4 + 4 * s.d)
     with pytest.raises(lsh.LshError):
         lsh.lsh_workspace_size("nope", s)
 

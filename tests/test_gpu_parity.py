@@ -208,7 +208,12 @@ def test_steps_match_oracle(w):
     assert worst_o <= tol
     assert worst_l <= (1e-5 if w.dtype == "fp32" else 1e-3)
     assert worst_c <= tol
-    assert np.array_equal(g["out"], g["fwd"]), "fused forward differs from the staged calls"
+    # the fused forward keeps per-round outputs in scaled fp16 on the bf16
+    # matrix-core path (relative error 2^-12) instead of the staged fp32
+    if w.dtype == "bf16" and w.chunk_len == 64:
+        assert np.all(np.abs(g["fwd"] - g["out"]) <= 2.0 ** -7 * np.abs(g["out"]) + 1e-3)
+    else:
+        assert np.array_equal(g["out"], g["fwd"]), "fused forward differs from the staged calls"
     assert np.isfinite(g["fwd"]).all()
 
 
@@ -223,6 +228,23 @@ def test_forward_matches_oracle_forward():
     assert np.abs(got - ref).max() <= TOL["bf16"]
     # causal: position 0 only sees itself (up to one bf16 rounding of the output)
     assert np.all(np.abs(got[:, :, 0] - v[:, :, 0]) <= 2.0 ** -8 * np.abs(v[:, :, 0]))
+
+
+@pytest.mark.parametrize("vscale", [1e6, 1e-6, 3.0e30])
+def test_forward_value_range_is_scale_free(vscale):
+    """Per-round outputs may be kept in fp16 internally; a power-of-two scale
+    chosen from max|v| keeps huge and tiny V exact to the same relative bar."""
+    w = _wl("bf16", B=1, H=2, L=1024, d=64, nb=32, nh=4, m=64, causal=True, seed=22)
+    qk, v, R = workloads.make_inputs(w)
+    v = workloads.round_to_bf16(v * np.float32(vscale))
+    qk_t = torch.from_numpy(qk).to(DEV, torch.bfloat16)
+    v_t = torch.from_numpy(v).to(DEV, torch.bfloat16)
+    out = lsh.attention_fwd(qk_t, v_t, torch.from_numpy(R).to(DEV), w.n_buckets, w.chunk_len,
+                            w.causal)
+    ref = oracle.forward(qk, v, R, w.n_buckets, w.chunk_len, w.causal)
+    got = out.float().cpu().numpy()
+    assert np.isfinite(got).all()
+    assert np.abs(got - ref).max() <= TOL["bf16"] * vscale
 
 
 def test_forward_is_deterministic():
