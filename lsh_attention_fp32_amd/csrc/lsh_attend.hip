@@ -93,10 +93,12 @@ __global__ __launch_bounds__(128) void attend_valu_kernel(const T* __restrict__ 
 // previous chunk is being computed, and serve as the look-back of the next.
 //
 // Wave w owns queries 16w..16w+15 of the chunk:
-//   S^T = K Q^T   (v_mfma_f32_16x16x32_bf16; keys on rows, queries on lanes)
+//   S^T = K Q^T   (v_mfma_f32_16x16x32_bf16; keys on rows, queries on lanes),
+//                 only for 32-key blocks that can hold a valid key
 //   mask, fp32 softmax in the exp2 domain
-//   O^T = V^T P^T (P^T comes straight from the S^T registers: the MFMA k-index
-//                  is mapped to keys in the order the lane already holds them)
+//   O^T = V^T P^T (P^T comes straight from the S^T registers: keys are
+//                  assigned to S^T rows so each lane ends up holding 8
+//                  consecutive keys, the B-operand layout)
 // Lane layout of v_mfma_f32_16x16x32_bf16: A[m][k] in lane m%16 + 16*(k/8),
 // element k%8; B[k][n] in lane n + 16*(k/8); D[m][n] in lane n + 16*(m/4),
 // register m%4.
@@ -106,14 +108,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kM = 64;            // chunk length of the matrix-core kernel
 constexpr int kWin = 2 * kM;      // keys in a window
 constexpr int kRun = 16;          // chunks per workgroup
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
-}
 
 template <int D>
 struct alignas(16) AttendLds {
@@ -248,8 +247,27 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
             if (c + 2 < c1 && tid < kM) pf = P[(int64_t)(c + 2) * kM + tid];
         }
 
-        // ---- S^T = K Q^T
+        // ---- which 32-key blocks can hold a valid key for any of this wave's
+        // queries (wave-uniform): the block's bucket range must meet the
+        // queries' (both are sorted within a chunk), and under causality an
+        // own-chunk block that starts after the last query holds only later
+        // positions of the same buckets.
         const int qrow = 16 * wave + r16;
+        const int qb_lo = sm.bkt[cs * kM + 16 * wave];
+        const int qb_hi = sm.bkt[cs * kM + 16 * wave + 15];
+        bool act[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const int first = sm.bkt[32 * kb], last = sm.bkt[32 * kb + 31];
+            bool a = first <= qb_hi && last >= qb_lo;
+            if (dm.causal && (kb >> 1) == cs && 32 * (kb & 1) > 16 * wave + 15) a = false;
+            act[kb] = __builtin_amdgcn_readfirstlane((int)a) != 0;
+        }
+
+        // ---- S^T = K Q^T. Tile kt = 2*kb + h; A-row m holds key
+        // 32*kb + 8*(m/4) + 4*h + m%4, so after both tiles of a block lane l
+        // holds keys 32*kb + 8*(l/16) + e, e < 8: contiguous, ready to be the
+        // B operand of the P^T V^T product.
         bf16x8 qf[KSTEPS];
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s)
@@ -257,27 +275,27 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
         const int qpos = sm.pos[cs * kM + qrow];
         const int qb = sm.bkt[cs * kM + qrow];
         f32x4 st[8];
-#pragma unroll
-        for (int kt = 0; kt < 8; ++kt) {
-            st[kt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < KSTEPS; ++s) {
-                const bf16x8 a = __builtin_bit_cast(
-                    bf16x8, *(const u32x4*)&sm.k[kt >> 2][(kt & 3) * 16 + r16][32 * s + 8 * g]);
-                st[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[s], st[kt], 0, 0, 0);
-            }
-        }
-        // ---- mask and softmax (exp2 domain); lane holds keys kt*16 + 4g + i of query r16
         float mx = -INFINITY;
 #pragma unroll
         for (int kt = 0; kt < 8; ++kt) {
-            const i32x4 kb = *(const i32x4*)&sm.bkt[kt * 16 + 4 * g];
-            const i32x4 kp = *(const i32x4*)&sm.pos[kt * 16 + 4 * g];
+            const int kb = kt >> 1, h = kt & 1;
+            st[kt] = (f32x4){-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+            if (!act[kb]) continue;
+            const int kw = 32 * kb + 8 * (r16 >> 2) + 4 * h + (r16 & 3);
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < KSTEPS; ++s) {
+                const bf16x8 a = __builtin_bit_cast(
+                    bf16x8, *(const u32x4*)&sm.k[kw >> 6][kw & 63][32 * s + 8 * g]);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[s], acc, 0, 0, 0);
+            }
+            // mask (exp2 domain); register i is key 32*kb + 8*g + 4*h + i
+            const i32x4 kbk = *(const i32x4*)&sm.bkt[32 * kb + 8 * g + 4 * h];
+            const i32x4 kps = *(const i32x4*)&sm.pos[32 * kb + 8 * g + 4 * h];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float s2 = st[kt][i] * c_log2;
-                if (kp[i] == qpos) s2 -= pen2;
-                const bool ok = kb[i] == qb && (!dm.causal || kp[i] <= qpos);
+                float s2 = acc[i] * c_log2 - (kps[i] == qpos ? pen2 : 0.f);
+                const bool ok = kbk[i] == qb && (!dm.causal || kps[i] <= qpos);
                 s2 = ok ? s2 : -INFINITY;
                 st[kt][i] = s2;
                 mx = fmaxf(mx, s2);
@@ -285,47 +303,51 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
         }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        float sum = 0.f, sumr = 0.f;
+
+        // ---- P = exp2(s - max) as bf16; the P-weight sum that normalises O is
+        // taken on the matrix cores from the same bf16 values (ones x P^T)
+        float sum = 0.f;
         u32x4 pfrag[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
+            if (!act[kb]) continue;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 float pr[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    pr[i] = exp2f(st[2 * kb + h][i] - mx);
+                    pr[i] = __builtin_amdgcn_exp2f(st[2 * kb + h][i] - mx);
                     sum += pr[i];
                 }
-                const uint32_t w0 = pack_bf16x2(pr[0], pr[1]), w1 = pack_bf16x2(pr[2], pr[3]);
-                sumr += __uint_as_float(w0 << 16) + __uint_as_float(w0 & 0xFFFF0000u) +
-                        __uint_as_float(w1 << 16) + __uint_as_float(w1 & 0xFFFF0000u);
-                pfrag[kb][2 * h] = w0;
-                pfrag[kb][2 * h + 1] = w1;
+                const bf16x2 w0 = {(__bf16)pr[0], (__bf16)pr[1]};
+                const bf16x2 w1 = {(__bf16)pr[2], (__bf16)pr[3]};
+                pfrag[kb][2 * h] = __builtin_bit_cast(uint32_t, w0);
+                pfrag[kb][2 * h + 1] = __builtin_bit_cast(uint32_t, w1);
             }
         }
         sum += __shfl_xor(sum, 16);
         sum += __shfl_xor(sum, 32);
-        sumr += __shfl_xor(sumr, 16);
-        sumr += __shfl_xor(sumr, 32);
 
-        // ---- O^T = V^T P^T; MFMA k-index 8g+e <-> key kb*32 + 4g + e (e<4), kb*32+16+4g+e-4
+        // ---- O^T = V^T P^T over the active blocks
         f32x4 oacc[DT];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) oacc[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        f32x4 osum = {0.f, 0.f, 0.f, 0.f};
+        const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
+            if (!act[kb]) continue;
             const bf16x8 bfr = __builtin_bit_cast(bf16x8, pfrag[kb]);
+            osum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ones), bfr,
+                                                           osum, 0, 0, 0);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                const uint16_t* row = &sm.vt[dt * 16 + r16][kb * 32 + 4 * g];
-                const u32x2 lo = *(const u32x2*)row;
-                const u32x2 hi = *(const u32x2*)(row + 16);
-                const u32x4 af = {lo.x, lo.y, hi.x, hi.y};
+                const u32x4 af = *(const u32x4*)&sm.vt[dt * 16 + r16][32 * kb + 8 * g];
                 oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af),
                                                                    bfr, oacc[dt], 0, 0, 0);
             }
         }
+        const float sumr = osum[0];
         const int64_t slot = seg * L + (int64_t)c * kM + qrow;
         // by sorted slot (fp32), or -- in the fused forward -- already un-sorted:
         // row (b, h, position, round) in scaled fp16, so the combine streams

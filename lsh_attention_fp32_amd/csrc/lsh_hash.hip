@@ -323,32 +323,40 @@ __global__ __launch_bounds__(256) void hash_mfma_kernel(const uint16_t* __restri
         }
     };
 
-    // one pipeline step: prefetch tile g+1, MFMAs of tile g, epilogue of tile g-1
-    auto step = [&](int g, f32x16(&acc_new)[TOKF], f32x16(&acc_old)[TOKF]) {
-        u32x4 pre[PRE];
-        if (g + 1 < total) {
-            const u32x4* src = rfrag + (int64_t)(g + 1) * TILE_U4;
+    // One pipeline step: start fetching tile g+2 from L2 into registers, MFMAs
+    // of tile g, epilogue of tile g-1, then park tile g+1 (fetched a step ago)
+    // in the LDS buffer tile g-1 used. Two register sets keep two tiles in
+    // flight, so L2 latency is hidden behind a whole step.
+    auto fetch = [&](int t, u32x4(&pre)[PRE]) {
+        if (t < total) {
+            const u32x4* src = rfrag + (int64_t)t * TILE_U4;
 #pragma unroll
             for (int j = 0; j < PRE; ++j) pre[j] = src[threadIdx.x + j * 256];
         }
+    };
+    auto step = [&](int g, f32x16(&acc_new)[TOKF], f32x16(&acc_old)[TOKF], u32x4(&pre_new)[PRE],
+                    u32x4(&pre_old)[PRE]) {
+        fetch(g + 2, pre_new);
         mfma_tile(g, acc_new);
         if (g > 0) epilogue(g - 1, acc_old);
         if (g + 1 < total) {
             u32x4* dst = lds[(g + 1) & 1];
 #pragma unroll
-            for (int j = 0; j < PRE; ++j) dst[threadIdx.x + j * 256] = pre[j];
+            for (int j = 0; j < PRE; ++j) dst[threadIdx.x + j * 256] = pre_old[j];
         }
         __syncthreads();
     };
 
-    step(0, accA, accB);
+    u32x4 preA[PRE], preB[PRE];
+    fetch(1, preA);
+    step(0, accA, accB, preB, preA);
     int g = 1;
     for (; g + 1 < total; g += 2) {
-        step(g, accB, accA);
-        step(g + 1, accA, accB);
+        step(g, accB, accA, preA, preB);
+        step(g + 1, accA, accB, preB, preA);
     }
     if (g < total) {
-        step(g, accB, accA);
+        step(g, accB, accA, preA, preB);
         epilogue(g, accB);
     } else {
         epilogue(g - 1, accA);
