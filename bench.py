@@ -48,33 +48,60 @@ def algorithmic_work(w):
         "sort_count": ("hbm", 4.0 * TR, "B"),
         "sort_scatter": ("hbm", 12.0 * TR, "B"),
         # gather qk and v rows once per token-round, read perm and the bucket,
-        # write o (fp32) and lse
+        # write the round's output row and lse (fp16 rows on the bf16
+        # matrix-core path, fp32 otherwise)
         "attend_fp32": ("hbm", TR * (2 * d * e + 8 + 4 * d + 4), "B"),
-        "attend_mfma": ("hbm", TR * (2 * d * e + 8 + 4 * d + 4), "B"),
-        # read every round's o row, lse and inv; write out
-        "combine": ("hbm", T * (w.n_hashes * (4 * d + 8) + d * e), "B"),
+        "attend_mfma": ("hbm", TR * (2 * d * e + 8 + 2 * d + 4), "B"),
+        # read every round's output row and lse of a token; write out
+        "combine": ("hbm", T * (w.n_hashes * ((2 if w.dtype == "bf16" else 4) * d + 4) + d * e),
+                    "B"),
+        # read v once
+        "vmax": ("hbm", T * d * e, "B"),
     }
 
 
-def cpu_baseline(w, qk, v, R, target_s=20.0):
-    """Times the oracle (as it is) on a bounded sample: one (batch, head) slice
-    of the workload with every round, L shortened until one run is ~target_s."""
-    import numpy as np
-
+def cpu_baseline(w, qk, v, R, target_s=12.0):
+    """Times the oracle (as it is) on a bounded sample of the workload: whole
+    (batch, head) slices with every round, as many heads of batch row 0 as fit
+    in about target_s (first shortening L if one slice alone is too long).
+    A token of the metric passes through all H heads, so the sample's rate is
+    scaled by (heads timed) / H."""
     from oracle import oracle
 
-    L = w.L
+    L, heads = w.L, 1
     while True:
         t0 = time.perf_counter()
-        oracle.forward(qk[:1, :1, :L], v[:1, :1, :L], R, w.n_buckets, w.chunk_len, w.causal)
+        oracle.forward(qk[:1, :heads, :L], v[:1, :heads, :L], R, w.n_buckets, w.chunk_len,
+                       w.causal)
         dt = time.perf_counter() - t0
-        if dt * 4 <= target_s or L <= 4 * w.chunk_len:
+        if dt * 2.5 <= target_s and heads < w.H and L == w.L:
+            heads = min(w.H, max(heads + 1, int(target_s / (dt / heads))))
+            continue
+        if dt <= 2.5 * target_s or L <= 4 * w.chunk_len:
             break
         L //= 2
-    _ = np
-    return {"value": L / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
-            "sample": f"1 of {w.B * w.H} (batch, head) slices, first {L} positions, all "
-                      f"{w.n_hashes} rounds; {dt:.1f} s for one forward"}
+    return {"value": L * heads / w.H / dt, "unit": "tokens/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"batch row 0, {heads} of {w.H} heads, first {L} positions, all "
+                      f"{w.n_hashes} rounds: {dt:.1f} s; rate scaled by {heads}/{w.H} heads"}
+
+
+def measured_traffic(name, kernel):
+    """HBM-side bytes per launch of `kernel` from the committed counter run
+    (FETCH_SIZE and WRITE_SIZE scaled by a plain copy's readings), or None
+    when the kernel's source has changed since the counters were taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get("kernels", {}).get(kernel)
+    if not rec:
+        return None
+    src = os.path.join(ROOT, "lsh_attention_fp32_amd", "csrc", rec["source"])
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+        return None
+    return rec["read_bytes"] + rec["write_bytes"]
 
 
 def main() -> int:
@@ -84,7 +111,18 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (to scale HBM byte counters)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": 1 << 30, "launches": 3}))
+        return 0
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the forward shards "
                                    "by (batch, head) with no communication, so --gpus must be 1"}))
@@ -145,7 +183,7 @@ def main() -> int:
         roof = {"bound": "alu", "achieved": amount / secs / 1e12, "peak": PEAK_FP32_TFLOPS,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(name, dominant)
     roof["kernel"] = dominant
     roof["kernel_ms"] = kernels[dominant]
 
