@@ -55,7 +55,7 @@ int validate(const lsh_shape_t* s) {
 bool empty(const lsh_shape_t* s) { return s->B == 0 || s->H == 0 || s->L == 0; }
 
 struct FwdLayout {
-    size_t hash, sort, buckets, perm, inv, lse, vmax, o, total;
+    size_t hash, sort, buckets, perm, inv, lse, o, total;
 };
 
 FwdLayout fwd_layout(const Dims& d) {
@@ -74,8 +74,6 @@ FwdLayout fwd_layout(const Dims& d) {
     off += align_up(sizeof(int32_t) * n, 256);
     f.lse = off;
     off += align_up(sizeof(float) * n, 256);
-    f.vmax = off;
-    off += 256;
     f.o = off;
     off += align_up((compact_o_sorted(d) ? 2 : sizeof(float)) * n * d.d, 256);
     f.total = off;
@@ -103,16 +101,17 @@ int run_fwd(const void* qk, const void* v, const float* R, const lsh_shape_t* sh
     int32_t* perm = (int32_t*)(base + f.perm);
     int32_t* inv = (int32_t*)(base + f.inv);
     float* lse = (float*)(base + f.lse);
-    const OSorted o{base + f.o, compact_o_sorted(d), (const uint32_t*)(base + f.vmax)};
+    const HashWorkspace hw = carve_hash_workspace(base + f.hash, d);
+    // the compact path (bf16 I/O) takes the matrix-core hash, which also
+    // produces max|v| for the scale of the fp16 per-round outputs
+    const bool compact = compact_o_sorted(d);
+    const OSorted o{base + f.o, compact, hw.vmax};
     hipError_t e;
-    if ((e = launch_hash(qk, R, d, buckets, carve_hash_workspace(base + f.hash, d), st, ev, nev,
-                         names)) != hipSuccess)
+    if ((e = launch_hash(qk, R, d, buckets, hw, st, ev, nev, names, compact ? v : nullptr)) !=
+        hipSuccess)
         return hip_fail(e, "hash");
     if ((e = launch_sort(buckets, d, perm, inv, base + f.sort, st, ev, nev, names)) != hipSuccess)
         return hip_fail(e, "sort");
-    if (o.half && (e = launch_vmax(v, d, (uint32_t*)(base + f.vmax), st, ev, nev, names)) !=
-                      hipSuccess)
-        return hip_fail(e, "vmax");
     if ((e = launch_attend(qk, v, buckets, perm, d, o, lse, st, ev, nev, names)) != hipSuccess)
         return hip_fail(e, "chunk_attend");
     if ((e = launch_combine(o, lse, inv, d, out, st, ev, nev, names)) != hipSuccess)

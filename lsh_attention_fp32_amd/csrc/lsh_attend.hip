@@ -11,8 +11,6 @@
 // (chunk 0 has no look-back, rounds never mix). Valid key: same bucket and,
 // when causal, key position <= query position. A query's score against itself
 // is lowered by kSelfPenalty, so it only counts when nothing else is valid.
-#include <algorithm>
-
 #include "lsh_internal.h"
 
 namespace lsh {
@@ -382,35 +380,6 @@ static void launch_valu(const T* qk, const T* v, const int32_t* buckets, const i
         attend_valu_kernel<64, T><<<grid, 128, 0, st>>>(qk, v, buckets, perm, d, o, lse);
     else
         attend_valu_kernel<128, T><<<grid, 128, 0, st>>>(qk, v, buckets, perm, d, o, lse);
-}
-
-// max|v| as a bf16 bit pattern (atomic max over the 15 magnitude bits, order
-// independent); *vmax must be 0 on entry.
-__global__ __launch_bounds__(256) void vmax_kernel(const uint16_t* __restrict__ v, int64_t n,
-                                                   uint32_t* __restrict__ vmax) {
-    uint32_t m = 0;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x * 8;
-    for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8; i < n; i += stride) {
-        const u32x4 w = *(const u32x4*)(v + i);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) m = max(m, max(w[e] & 0x7FFFu, (w[e] >> 16) & 0x7FFFu));
-    }
-    for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-    __shared__ uint32_t wmax[4];
-    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) atomicMax(vmax, max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3])));
-}
-
-__global__ void zero_u32_kernel(uint32_t* p) { *p = 0u; }
-
-hipError_t launch_vmax(const void* v, const Dims& d, uint32_t* vmax, hipStream_t st,
-                       hipEvent_t* ev, int* nev, const char** names) {
-    zero_u32_kernel<<<1, 1, 0, st>>>(vmax);
-    const int64_t n = d.T * d.d;   // a multiple of 8 (d is 64 or 128)
-    const unsigned grid = (unsigned)std::min<int64_t>(2048, (n / 8 + 255) / 256 + 1);
-    vmax_kernel<<<grid, 256, 0, st>>>((const uint16_t*)v, n, vmax);
-    return mark(st, ev, nev, names, "vmax");
 }
 
 hipError_t launch_attend(const void* qk, const void* v, const int32_t* buckets,

@@ -62,6 +62,7 @@ HashWorkspace carve_hash_workspace(void* ws, const Dims& d) {
     char* p = (char*)ws;
     HashWorkspace w;
     w.counter = (int32_t*)p;
+    w.vmax = (uint32_t*)(p + 3 * sizeof(int32_t));
     p += 256;
     w.rnorm = (float*)p;
     p += align_up(sizeof(float) * d.nh, 256);
@@ -75,7 +76,7 @@ HashWorkspace carve_hash_workspace(void* ws, const Dims& d) {
 
 // ------------------------------------------------------------------ R prep
 __global__ void zero_counter_kernel(int32_t* counter, float* rnorm, int nh) {
-    if (threadIdx.x < 3) counter[threadIdx.x] = 0;
+    if (threadIdx.x < 4) counter[threadIdx.x] = 0;   // three queue counters and max|v|
     for (int r = threadIdx.x; r < nh; r += blockDim.x) rnorm[r] = 0.f;
 }
 
@@ -184,13 +185,20 @@ __device__ __forceinline__ int classify(float v1, float v2, float v3, float thr)
 // One workgroup = 4 waves; a wave owns 32*TOKF tokens (TOKF B-operand
 // fragments kept in registers for the whole kernel) and sweeps every column
 // tile of every round; R tiles stream through LDS, double-buffered.
+//
+// When `v` is given, the kernel also folds max|v| over its tokens' value rows
+// into *vmax (as a bf16 bit pattern; one atomic max per workgroup): the scale
+// of the fp16 per-round outputs of the fused forward comes for the price of a
+// read that overlaps the matrix-core work.
 template <int D, int TOKF>
 __global__ __launch_bounds__(256) void hash_mfma_kernel(const uint16_t* __restrict__ qk,
                                                         const u32x4* __restrict__ rfrag,
                                                         const float* __restrict__ rnorm, Dims dm,
                                                         int32_t* __restrict__ buckets,
                                                         int32_t* __restrict__ counter,
-                                                        RefineItem* __restrict__ queue) {
+                                                        RefineItem* __restrict__ queue,
+                                                        const uint16_t* __restrict__ v,
+                                                        uint32_t* __restrict__ vmax) {
     constexpr int KS = D / 16;
     constexpr int TILE_U4 = KS * 2 * kWave;     // 16-byte lane fragments per column tile
     constexpr int PRE = TILE_U4 / 256;          // fragments each thread stages
@@ -241,8 +249,25 @@ __global__ __launch_bounds__(256) void hash_mfma_kernel(const uint16_t* __restri
         item0[f] = tok_live[f] ? (int32_t)(bh * dm.nh * dm.L + i) : 0;
     }
 
+    __shared__ uint32_t wvmax[4];
+    if (v) {
+        // this workgroup's tokens are one contiguous run of value rows
+        const int64_t first = (int64_t)blockIdx.x * TOK_WG;
+        const int64_t nvec = min((int64_t)TOK_WG, dm.T - first) * (D / 8);
+        const u32x4* src = (const u32x4*)(v + first * D);
+        uint32_t m = 0;
+        for (int64_t i = threadIdx.x; i < nvec; i += 256) {
+            const u32x4 w = src[i];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m = max(m, max(w[e] & 0x7FFFu, (w[e] >> 16) & 0x7FFFu));
+        }
+        for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+        if (lane == 0) wvmax[wave] = m;
+    }
     for (int i = threadIdx.x; i < TILE_U4; i += 256) lds[0][i] = rfrag[i];
     __syncthreads();
+    if (v && threadIdx.x == 0)
+        atomicMax(vmax, max(max(wvmax[0], wvmax[1]), max(wvmax[2], wvmax[3])));
 
     float k1[TOKF], k2[TOKF], k3[TOKF];
 #pragma unroll
@@ -552,7 +577,7 @@ static hipError_t launch_valu_and_refine(const T* qk, const float* R, const Dims
 
 hipError_t launch_hash(const void* qk, const float* R, const Dims& d, int32_t* buckets,
                        const HashWorkspace& w, hipStream_t st, hipEvent_t* ev, int* nev,
-                       const char** names) {
+                       const char** names, const void* v_for_max) {
     const int half = d.nb / 2;
     const int ntiles = hash_ntiles(d);
     hipError_t e;
@@ -572,10 +597,12 @@ hipError_t launch_hash(const void* qk, const float* R, const Dims& d, int32_t* b
         const uint16_t* x = (const uint16_t*)qk;
         if (d.d == 64)
             hash_mfma_kernel<64, TOKF><<<grid, 256, 0, st>>>(x, (const u32x4*)w.rfrag, w.rnorm, d,
-                                                           buckets, w.counter, w.queue);
+                                                           buckets, w.counter, w.queue,
+                                                           (const uint16_t*)v_for_max, w.vmax);
         else
             hash_mfma_kernel<128, TOKF><<<grid, 256, 0, st>>>(x, (const u32x4*)w.rfrag, w.rnorm, d,
-                                                            buckets, w.counter, w.queue);
+                                                            buckets, w.counter, w.queue,
+                                                            (const uint16_t*)v_for_max, w.vmax);
         if ((e = mark(st, ev, nev, names, "hash_fast_mfma")) != hipSuccess) return e;
         hash_refine_kernel<uint16_t><<<refine_blocks, 256, 0, st>>>(x, w.rt, d, w.counter, w.queue,
                                                                     buckets);

@@ -52,6 +52,7 @@ struct RefineItem {
 
 struct HashWorkspace {
     int32_t* counter;     // [3] queued items: total (the public count), front, back
+    uint32_t* vmax;       // max|v| (bf16 bits) when the fast pass is asked to fold it in
     float* rnorm;         // [nh] max column 2-norm of R per round, rounded up
     uint16_t* rfrag;      // bf16 hi/lo split of R in matrix-core fragment order
     float* rt;            // R transposed to [nh][ntiles*32][d], fp32
@@ -60,9 +61,11 @@ struct HashWorkspace {
 size_t hash_workspace_bytes(const Dims& d);
 HashWorkspace carve_hash_workspace(void* ws, const Dims& d);
 
+// v_for_max (bf16 values, or null): also fold max|v| into w.vmax during the
+// matrix-core pass (only bf16 inputs take that pass).
 hipError_t launch_hash(const void* qk, const float* R, const Dims& d, int32_t* buckets,
                        const HashWorkspace& w, hipStream_t st, hipEvent_t* ev, int* nev,
-                       const char** names);
+                       const char** names, const void* v_for_max = nullptr);
 
 // ---------------------------------------------------------------- sort stage
 constexpr int kSortTile = 4096;          // elements per sort tile (one workgroup)
@@ -90,8 +93,6 @@ struct OSorted {
 // True when the fused forward can keep o_sorted in scaled fp16.
 inline bool compact_o_sorted(const Dims& d) { return d.dtype == LSH_BF16 && d.m == 64; }
 
-hipError_t launch_vmax(const void* v, const Dims& d, uint32_t* vmax, hipStream_t st,
-                       hipEvent_t* ev, int* nev, const char** names);
 hipError_t launch_attend(const void* qk, const void* v, const int32_t* buckets,
                          const int32_t* perm, const Dims& d, const OSorted& o, float* lse_sorted,
                          hipStream_t st, hipEvent_t* ev, int* nev, const char** names);

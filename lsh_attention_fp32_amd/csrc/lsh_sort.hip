@@ -9,7 +9,7 @@
 // bucket alone yields the (bucket, position) order. Three kernels:
 //   count   per 4096-element tile: bucket histogram in LDS
 //   scan    per segment: exclusive scan of the histograms in (bucket, tile)
-//           order -> the first slot of every (bucket, tile) run
+//           order -> the first slot of every (tile, bucket) run
 //   scatter per tile: each wave walks its 1024 elements in order; lanes with
 //           equal buckets are grouped by a ballot match, so ranks are exact
 //           and the LDS counter of a hot bucket is bumped once per wave step
@@ -43,7 +43,7 @@ __device__ __forceinline__ uint64_t lanes_below_s(int lane) {
     return lane ? (~0ull >> (64 - lane)) : 0ull;
 }
 
-// counts layout: [seg][bucket][tile]
+// counts layout: [seg][tile][bucket] (each tile writes one contiguous row)
 __global__ __launch_bounds__(256) void sort_count_kernel(const int32_t* __restrict__ buckets,
                                                          Dims dm, int ntiles, int nbits,
                                                          int32_t* __restrict__ counts) {
@@ -65,47 +65,49 @@ __global__ __launch_bounds__(256) void sort_count_kernel(const int32_t* __restri
     }
     __syncthreads();
     for (int b = threadIdx.x; b < dm.nb; b += 256)
-        counts[(seg * dm.nb + b) * ntiles + tile] = hist[b];
+        counts[(seg * ntiles + tile) * dm.nb + b] = hist[b];
 }
 
-// In-place exclusive scan of each segment's nb*ntiles counts (one block per segment).
-__global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t* __restrict__ counts, int64_t n) {
-    constexpr int ITEMS = 8;
+// One block per segment: turns the [tile][bucket] counts into the first slot of
+// every (tile, bucket) run, in (bucket, tile) order: a bucket's runs follow
+// each other tile by tile, and buckets follow each other in increasing order.
+// Thread b owns buckets b, b+1024, ...: a column sum, a block-wide exclusive
+// scan of the bucket totals, then a running sum down the column (all reads
+// and writes are coalesced across threads).
+__global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t* __restrict__ counts, int nb,
+                                                         int ntiles) {
+    constexpr int BPT = kMaxBuckets / 1024;   // buckets per thread
     __shared__ int32_t wsum[16];
-    int32_t* c = counts + (int64_t)blockIdx.x * n;
+    int32_t* c = counts + (int64_t)blockIdx.x * ntiles * nb;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int32_t carry = 0;
-    for (int64_t base = 0; base < n; base += 1024 * ITEMS) {
-        int32_t v[ITEMS];
-        int32_t tsum = 0;
-        const int64_t my = base + (int64_t)threadIdx.x * ITEMS;
+    int32_t tot[BPT];
+    int32_t mine = 0;
 #pragma unroll
-        for (int k = 0; k < ITEMS; ++k) {
-            v[k] = (my + k < n) ? c[my + k] : 0;
-            tsum += v[k];
-        }
-        // inclusive scan of tsum across the wave
-        int32_t incl = tsum;
-        for (int off = 1; off < 64; off <<= 1) {
-            const int32_t o = __shfl_up(incl, off);
-            if (lane >= off) incl += o;
-        }
-        if (lane == 63) wsum[wave] = incl;
-        __syncthreads();
-        int32_t wprefix = 0, total = 0;
-        for (int w = 0; w < 16; ++w) {
-            const int32_t s = wsum[w];
-            if (w < wave) wprefix += s;
-            total += s;
-        }
-        int32_t run = carry + wprefix + incl - tsum;
+    for (int j = 0; j < BPT; ++j) {
+        const int b = threadIdx.x * BPT + j;
+        tot[j] = 0;
+        if (b < nb)
+            for (int t = 0; t < ntiles; ++t) tot[j] += c[(int64_t)t * nb + b];
+        mine += tot[j];
+    }
+    int32_t incl = mine;
+    for (int off = 1; off < 64; off <<= 1) {
+        const int32_t o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int32_t run = incl - mine;
+    for (int w = 0; w < wave; ++w) run += wsum[w];
 #pragma unroll
-        for (int k = 0; k < ITEMS; ++k) {
-            if (my + k < n) c[my + k] = run;
-            run += v[k];
-        }
-        carry += total;
-        __syncthreads();
+    for (int j = 0; j < BPT; ++j) {
+        const int b = threadIdx.x * BPT + j;
+        if (b < nb)
+            for (int t = 0; t < ntiles; ++t) {
+                const int32_t cnt = c[(int64_t)t * nb + b];
+                c[(int64_t)t * nb + b] = run;
+                run += cnt;
+            }
     }
 }
 
@@ -137,7 +139,7 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __rest
     __syncthreads();
     // first slot of each (wave, bucket) run
     for (int b = threadIdx.x; b < nb; b += 256) {
-        int32_t run = offs[(seg * nb + b) * ntiles + tile];
+        int32_t run = offs[(seg * ntiles + tile) * nb + b];
         for (int w = 0; w < kSortWaves; ++w) {
             const int32_t cnt = sh[w * nb + b];
             sh[w * nb + b] = run;
@@ -175,7 +177,7 @@ hipError_t launch_sort(const int32_t* buckets, const Dims& d, int32_t* perm, int
     hipError_t e;
     sort_count_kernel<<<grid, 256, sizeof(int32_t) * d.nb, st>>>(buckets, d, ntiles, nbits, counts);
     if ((e = mark(st, ev, nev, names, "sort_count")) != hipSuccess) return e;
-    sort_scan_kernel<<<(unsigned)d.segs, 1024, 0, st>>>(counts, (int64_t)d.nb * ntiles);
+    sort_scan_kernel<<<(unsigned)d.segs, 1024, 0, st>>>(counts, d.nb, ntiles);
     if ((e = mark(st, ev, nev, names, "sort_scan")) != hipSuccess) return e;
     sort_scatter_kernel<<<grid, 256, sizeof(int32_t) * kSortWaves * d.nb, st>>>(
         buckets, counts, d, ntiles, nbits, perm, inv);
