@@ -110,9 +110,14 @@ int run_fwd(const void* qk, const void* v, const float* R, const lsh_shape_t* sh
     if ((e = launch_hash(qk, R, d, buckets, hw, st, ev, nev, names, compact ? v : nullptr)) !=
         hipSuccess)
         return hip_fail(e, "hash");
-    if ((e = launch_sort(buckets, d, perm, inv, base + f.sort, st, ev, nev, names)) != hipSuccess)
+    // the fp16 by-position form un-sorts in the chunk pass, so the sort can
+    // hand it packed keys and skip the inverse permutation
+    const bool packed = compact && packed_sort_keys(d);
+    if ((e = launch_sort(buckets, d, perm, inv, base + f.sort, st, ev, nev, names, packed)) !=
+        hipSuccess)
         return hip_fail(e, "sort");
-    if ((e = launch_attend(qk, v, buckets, perm, d, o, lse, st, ev, nev, names)) != hipSuccess)
+    if ((e = launch_attend(qk, v, buckets, perm, d, o, lse, st, ev, nev, names, packed)) !=
+        hipSuccess)
         return hip_fail(e, "chunk_attend");
     if ((e = launch_combine(o, lse, inv, d, out, st, ev, nev, names)) != hipSuccess)
         return hip_fail(e, "unsort_combine");

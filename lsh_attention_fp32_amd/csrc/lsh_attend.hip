@@ -88,7 +88,10 @@ __global__ __launch_bounds__(128) void attend_valu_kernel(const T* __restrict__ 
 // padded) and the v rows transposed (vt[feature][key]), keys indexed in ring
 // order (slot * 64 + row) -- the window of chunk c is simply both ring slots.
 // Each chunk's rows are gathered from HBM once, into registers, while the
-// previous chunk is being computed, and serve as the look-back of the next.
+// previous chunk(s) are being computed (kDepth chunks in flight; one measures
+// as fast as two or three at 64K tokens), and serve as the look-back of the
+// next. In the fused forward the sorted keys carry the bucket next to the
+// position, so no bucket id is gathered.
 //
 // Wave w owns queries 16w..16w+15 of the chunk:
 //   S^T = K Q^T   (v_mfma_f32_16x16x32_bf16; keys on rows, queries on lanes),
@@ -111,6 +114,11 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr int kM = 64;            // chunk length of the matrix-core kernel
 constexpr int kWin = 2 * kM;      // keys in a window
 constexpr int kRun = 16;          // chunks per workgroup
+#ifndef LSH_ATTEND_DEPTH
+#define LSH_ATTEND_DEPTH 1
+#endif
+constexpr int kDepth = LSH_ATTEND_DEPTH;   // chunks whose gathers are in flight (1..3)
+static_assert(kDepth >= 1 && kDepth <= 3, "key buffers hold four chunks");
 
 template <int D>
 struct alignas(16) AttendLds {
@@ -120,10 +128,10 @@ struct alignas(16) AttendLds {
     uint16_t vt[D][VS];
     int32_t pos[kWin];
     int32_t bkt[kWin];
-    int32_t nperm[2][kM];
+    int32_t nperm[4][kM];   // sorted keys of chunks waiting to be gathered
 };
 
-template <int D, bool HALF>
+template <int D, bool HALF, bool PACKED>
 __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __restrict__ qk,
                                                           const uint16_t* __restrict__ v,
                                                           const int32_t* __restrict__ buckets,
@@ -157,59 +165,70 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
     const float pen2 = kSelfPenalty * 1.4426950408889634f;
     const float oscale = HALF ? o_scale(*vmax) : 1.0f;
 
-    u32x4 qreg[QPT];
-    u32x4 vreg[VPT][2];
-    int my_pos = 0, my_bkt = 0;
+    // sorted key of a slot: the position (plain perm) or bucket:position (packed)
+    auto key_pos = [&](int32_t k) -> int { return PACKED ? (int)((uint32_t)k & kPackPosMask) : k; };
 
-    // gather the rows of one chunk (positions from an LDS perm buffer) into registers
-    auto issue_rows = [&](const int32_t* pl) {
+    // One chunk's rows in flight: gathered from HBM into registers (positions
+    // from an LDS key buffer), parked in the LDS ring when the chunk's turn
+    // comes. Two sets keep two chunks in flight behind the one computing.
+    struct Rows {
+        u32x4 q[QPT];
+        u32x4 v[VPT][2];
+        int32_t pos, bkt;   // position and bucket of row tid (threads < 64)
+    };
+    auto issue_rows = [&](Rows& rw, const int32_t* kl) {
 #pragma unroll
         for (int j = 0; j < QPT; ++j) {
             const int row = tid / PIECES + QROWS * j;
-            qreg[j] = *(const u32x4*)(X + (int64_t)pl[row] * D + (tid % PIECES) * 8);
+            rw.q[j] = *(const u32x4*)(X + (int64_t)key_pos(kl[row]) * D + (tid % PIECES) * 8);
         }
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
             const int pr = tid & 31, ddg = (tid >> 5) + 8 * j;
-            vreg[j][0] = *(const u32x4*)(V + (int64_t)pl[2 * pr] * D + ddg * 8);
-            vreg[j][1] = *(const u32x4*)(V + (int64_t)pl[2 * pr + 1] * D + ddg * 8);
+            rw.v[j][0] = *(const u32x4*)(V + (int64_t)key_pos(kl[2 * pr]) * D + ddg * 8);
+            rw.v[j][1] = *(const u32x4*)(V + (int64_t)key_pos(kl[2 * pr + 1]) * D + ddg * 8);
+        }
+        if (tid < kM) {
+            const int32_t k = kl[tid];
+            rw.pos = key_pos(k);
+            rw.bkt = PACKED ? (int32_t)((uint32_t)k >> kPackPosBits) : Bk[k];
         }
     };
     // registers -> ring slot
-    auto store_rows = [&](int slot) {
+    auto store_rows = [&](const Rows& rw, int slot) {
 #pragma unroll
         for (int j = 0; j < QPT; ++j) {
             const int row = tid / PIECES + QROWS * j;
-            *(u32x4*)&sm.k[slot][row][(tid % PIECES) * 8] = qreg[j];
+            *(u32x4*)&sm.k[slot][row][(tid % PIECES) * 8] = rw.q[j];
         }
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
             const int pr = tid & 31, ddg = (tid >> 5) + 8 * j;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const uint32_t lo = (vreg[j][0][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-                const uint32_t hi = (vreg[j][1][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                const uint32_t lo = (rw.v[j][0][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                const uint32_t hi = (rw.v[j][1][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
                 *(uint32_t*)&sm.vt[ddg * 8 + e][slot * kM + 2 * pr] = lo | (hi << 16);
             }
         }
         if (tid < kM) {
-            sm.pos[slot * kM + tid] = my_pos;
-            sm.bkt[slot * kM + tid] = my_bkt;
+            sm.pos[slot * kM + tid] = rw.pos;
+            sm.bkt[slot * kM + tid] = rw.bkt;
         }
     };
 
-    // ---- prologue: look-back chunk c0-1 (or an empty slot), then chunk c0 in flight
+    // ---- prologue: the look-back chunk c0-1 (or an empty slot) parked in its
+    // ring slot; chunks c0 .. c0+DEPTH-1 in flight; the keys of c0+DEPTH in LDS.
+    // Key buffers rotate over four slots (chunk & 3).
+    Rows rw[kDepth];
     {
-        const int slot = (c0 + 1) & 1;   // slot of chunk c0-1
+        const int slot = (c0 + 1) & 1;   // ring slot of chunk c0-1
         if (c0 > 0) {
-            if (tid < kM) {
-                my_pos = P[(int64_t)(c0 - 1) * kM + tid];
-                my_bkt = Bk[my_pos];
-                sm.nperm[0][tid] = my_pos;
-            }
+            int32_t* kl = sm.nperm[(c0 - 1) & 3];
+            if (tid < kM) kl[tid] = P[(int64_t)(c0 - 1) * kM + tid];
             __syncthreads();
-            issue_rows(sm.nperm[0]);
-            store_rows(slot);
+            issue_rows(rw[0], kl);
+            store_rows(rw[0], slot);
         } else {
             for (int k = tid; k < kM * AttendLds<D>::KS; k += 256) (&sm.k[slot][0][0])[k] = 0;
             for (int k = tid; k < D * kM; k += 256) sm.vt[k / kM][slot * kM + k % kM] = 0;
@@ -218,32 +237,24 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
                 sm.bkt[slot * kM + tid] = -1;   // never equal to a bucket id
             }
         }
+        if (tid < kM)
+            for (int c = c0; c <= c0 + kDepth && c < c1; ++c)
+                sm.nperm[c & 3][tid] = P[(int64_t)c * kM + tid];
         __syncthreads();
-        if (tid < kM) {
-            my_pos = P[(int64_t)c0 * kM + tid];
-            sm.nperm[c0 & 1][tid] = my_pos;
-            my_bkt = Bk[my_pos];
-            if (c0 + 1 < c1) sm.nperm[(c0 + 1) & 1][tid] = P[(int64_t)(c0 + 1) * kM + tid];
-        }
-        __syncthreads();
-        issue_rows(sm.nperm[c0 & 1]);
+#pragma unroll
+        for (int j = 0; j < kDepth; ++j)
+            if (c0 + j < c1) issue_rows(rw[j], sm.nperm[(c0 + j) & 3]);
     }
 
-    for (int c = c0; c < c1; ++c) {
+    auto step = [&](int c, Rows& rows) {
         const int cs = c & 1;
-        store_rows(cs);
+        store_rows(rows, cs);
         __syncthreads();
-        // next chunk's rows and the chunk after's perm are fetched while this one computes
-        int pf = 0;
-        if (c + 1 < c1) {
-            const int32_t* pl = sm.nperm[(c + 1) & 1];
-            if (tid < kM) {
-                my_pos = pl[tid];
-                my_bkt = Bk[my_pos];
-            }
-            issue_rows(pl);
-            if (c + 2 < c1 && tid < kM) pf = P[(int64_t)(c + 2) * kM + tid];
-        }
+        // chunk c+DEPTH's rows go into the registers just parked, and the keys
+        // of the chunk after it are fetched, while this chunk computes
+        int32_t pf = 0;
+        if (c + kDepth < c1) issue_rows(rows, sm.nperm[(c + kDepth) & 3]);
+        if (c + kDepth + 1 < c1 && tid < kM) pf = P[(int64_t)(c + kDepth + 1) * kM + tid];
 
         // ---- which 32-key blocks can hold a valid key for any of this wave's
         // queries (wave-uniform): the block's bucket range must meet the
@@ -367,8 +378,14 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
         }
         if (g == 0) lse_sorted[orow_idx] = (mx + log2f(sum)) * 0.6931471805599453f;
 
-        if (c + 2 < c1 && tid < kM) sm.nperm[c & 1][tid] = pf;
+        if (c + kDepth + 1 < c1 && tid < kM) sm.nperm[(c + kDepth + 1) & 3][tid] = pf;
         __syncthreads();
+    };
+
+    for (int c = c0; c < c1; c += kDepth) {
+#pragma unroll
+        for (int j = 0; j < kDepth; ++j)
+            if (c + j < c1) step(c + j, rw[j]);
     }
 }
 
@@ -384,28 +401,29 @@ static void launch_valu(const T* qk, const T* v, const int32_t* buckets, const i
 
 hipError_t launch_attend(const void* qk, const void* v, const int32_t* buckets,
                          const int32_t* perm, const Dims& d, const OSorted& o, float* lse_sorted,
-                         hipStream_t st, hipEvent_t* ev, int* nev, const char** names) {
+                         hipStream_t st, hipEvent_t* ev, int* nev, const char** names,
+                         bool packed) {
+    if (packed && !(o.half && d.dtype == LSH_BF16 && d.m == kM)) return hipErrorInvalidValue;
     if (d.dtype == LSH_BF16 && d.m == kM) {
         const int nchunks = d.L / kM;
         const int nruns = (nchunks + kRun - 1) / kRun;
         const unsigned grid = (unsigned)(d.segs * nruns);
         const uint16_t* x = (const uint16_t*)qk;
         const uint16_t* vv = (const uint16_t*)v;
-        if (o.half) {
-            if (d.d == 64)
-                attend_mfma_kernel<64, true><<<grid, 256, 0, st>>>(x, vv, buckets, perm, d, nruns,
-                                                                   o.ptr, o.vmax, lse_sorted);
-            else
-                attend_mfma_kernel<128, true><<<grid, 256, 0, st>>>(x, vv, buckets, perm, d, nruns,
-                                                                    o.ptr, o.vmax, lse_sorted);
+#define LSH_ATTEND_LAUNCH(DD, HH, PP, VM)                                                       \
+    attend_mfma_kernel<DD, HH, PP><<<grid, 256, 0, st>>>(x, vv, buckets, perm, d, nruns, o.ptr, \
+                                                         VM, lse_sorted)
+        if (o.half && packed) {
+            if (d.d == 64) LSH_ATTEND_LAUNCH(64, true, true, o.vmax);
+            else LSH_ATTEND_LAUNCH(128, true, true, o.vmax);
+        } else if (o.half) {
+            if (d.d == 64) LSH_ATTEND_LAUNCH(64, true, false, o.vmax);
+            else LSH_ATTEND_LAUNCH(128, true, false, o.vmax);
         } else {
-            if (d.d == 64)
-                attend_mfma_kernel<64, false><<<grid, 256, 0, st>>>(x, vv, buckets, perm, d, nruns,
-                                                                    o.ptr, nullptr, lse_sorted);
-            else
-                attend_mfma_kernel<128, false><<<grid, 256, 0, st>>>(x, vv, buckets, perm, d, nruns,
-                                                                     o.ptr, nullptr, lse_sorted);
+            if (d.d == 64) LSH_ATTEND_LAUNCH(64, false, false, nullptr);
+            else LSH_ATTEND_LAUNCH(128, false, false, nullptr);
         }
+#undef LSH_ATTEND_LAUNCH
         return mark(st, ev, nev, names, "attend_mfma");
     }
     float* of = (float*)o.ptr;

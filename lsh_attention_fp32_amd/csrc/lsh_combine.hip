@@ -112,7 +112,10 @@ __global__ __launch_bounds__(256) void combine_bypos_kernel(const _Float16* __re
                                                             Dims dm, T* __restrict__ out) {
     constexpr int TPT = D / 8;
     constexpr int G = 8;
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    // Blocks run from the last token back: the chunk pass finishes with the
+    // last (batch, head) slices, whose rows are then still in the memory-side
+    // cache when this pass starts.
+    const int64_t gid = (int64_t)(gridDim.x - 1 - blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t tok = gid / TPT;
     const int q = (int)(gid - tok * TPT);
     if (tok >= dm.T) return;

@@ -75,8 +75,17 @@ constexpr int kMaxHashes = 4096;
 
 inline int64_t sort_ntiles(const Dims& d) { return (d.L + kSortTile - 1) / kSortTile; }
 size_t sort_workspace_bytes(const Dims& d);
+
+// Packed sorted keys: inside the fused forward the sort can store, per slot,
+// (bucket << kPackPosBits) | position instead of the plain position, so the
+// chunk pass reads both from one coalesced word; no inverse is written then.
+constexpr int kPackPosBits = 20;
+constexpr uint32_t kPackPosMask = (1u << kPackPosBits) - 1u;
+inline bool packed_sort_keys(const Dims& d) { return d.L <= (1 << kPackPosBits); }
+
 hipError_t launch_sort(const int32_t* buckets, const Dims& d, int32_t* perm, int32_t* inv,
-                       void* ws, hipStream_t st, hipEvent_t* ev, int* nev, const char** names);
+                       void* ws, hipStream_t st, hipEvent_t* ev, int* nev, const char** names,
+                       bool packed = false);
 
 // ------------------------------------------------------------ attend stage
 // Per-round outputs: float32 by sorted slot ([B,H,nh,L,d], with lse
@@ -93,9 +102,12 @@ struct OSorted {
 // True when the fused forward can keep o_sorted in scaled fp16.
 inline bool compact_o_sorted(const Dims& d) { return d.dtype == LSH_BF16 && d.m == 64; }
 
+// packed: perm holds packed sorted keys (buckets is then not read); only
+// the fp16 by-position form takes them.
 hipError_t launch_attend(const void* qk, const void* v, const int32_t* buckets,
                          const int32_t* perm, const Dims& d, const OSorted& o, float* lse_sorted,
-                         hipStream_t st, hipEvent_t* ev, int* nev, const char** names);
+                         hipStream_t st, hipEvent_t* ev, int* nev, const char** names,
+                         bool packed = false);
 
 // ----------------------------------------------------------- combine stage
 hipError_t launch_combine(const OSorted& o, const float* lse_sorted, const int32_t* inv,

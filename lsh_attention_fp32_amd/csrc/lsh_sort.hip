@@ -111,6 +111,8 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t* __restrict__ c
     }
 }
 
+// PACKED: perm[slot] = (bucket << kPackPosBits) | position and no inverse.
+template <bool PACKED>
 __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __restrict__ buckets,
                                                            const int32_t* __restrict__ offs,
                                                            Dims dm, int ntiles, int nbits,
@@ -149,7 +151,7 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __rest
     __syncthreads();
     // pass 2: ranks in position order
     int32_t* P = perm + seg * dm.L;
-    int32_t* I = inv + seg * dm.L;
+    int32_t* I = PACKED ? nullptr : inv + seg * dm.L;
     for (int64_t i0 = wbeg; i0 < wend; i0 += kWave) {
         const int64_t i = i0 + lane;
         const bool active = i < wend;
@@ -157,8 +159,12 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __rest
         const uint64_t m = match_bucket(b, nbits, active);
         if (active) {
             const int32_t slot = mine[b] + __popcll(m & lanes_below_s(lane));
-            P[slot] = (int32_t)i;
-            I[i] = slot;
+            if constexpr (PACKED) {
+                P[slot] = (int32_t)(((uint32_t)b << kPackPosBits) | (uint32_t)i);
+            } else {
+                P[slot] = (int32_t)i;
+                I[i] = slot;
+            }
         }
         // every lane has read its run start; leaders now advance them
         __builtin_amdgcn_wave_barrier();
@@ -168,7 +174,8 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __rest
 }
 
 hipError_t launch_sort(const int32_t* buckets, const Dims& d, int32_t* perm, int32_t* inv,
-                       void* ws, hipStream_t st, hipEvent_t* ev, int* nev, const char** names) {
+                       void* ws, hipStream_t st, hipEvent_t* ev, int* nev, const char** names,
+                       bool packed) {
     const int ntiles = (int)sort_ntiles(d);
     int nbits = 0;
     while ((1 << nbits) < d.nb) ++nbits;
@@ -179,8 +186,13 @@ hipError_t launch_sort(const int32_t* buckets, const Dims& d, int32_t* perm, int
     if ((e = mark(st, ev, nev, names, "sort_count")) != hipSuccess) return e;
     sort_scan_kernel<<<(unsigned)d.segs, 1024, 0, st>>>(counts, d.nb, ntiles);
     if ((e = mark(st, ev, nev, names, "sort_scan")) != hipSuccess) return e;
-    sort_scatter_kernel<<<grid, 256, sizeof(int32_t) * kSortWaves * d.nb, st>>>(
-        buckets, counts, d, ntiles, nbits, perm, inv);
+    const size_t lds = sizeof(int32_t) * kSortWaves * d.nb;
+    if (packed)
+        sort_scatter_kernel<true><<<grid, 256, lds, st>>>(buckets, counts, d, ntiles, nbits, perm,
+                                                          nullptr);
+    else
+        sort_scatter_kernel<false><<<grid, 256, lds, st>>>(buckets, counts, d, ntiles, nbits,
+                                                           perm, inv);
     return mark(st, ev, nev, names, "sort_scatter");
 }
 
