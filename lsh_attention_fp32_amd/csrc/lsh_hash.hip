@@ -10,20 +10,28 @@
 // concatenation.
 //
 // Design (gfx950):
-//  * Fast pass on the matrix cores. R is split exactly enough into two bf16
-//    terms, R = r_hi + r_lo + e with |e| <= 2^-16 |R|; with bf16 inputs every
-//    product x*r is exact in fp32 and the MFMA accumulates in fp32. Each lane
-//    keeps the three largest |p| of its token as packed keys (|p| with the low
-//    mantissa bits replaced by (column << 1 | sign)), three integer min/max
-//    operations per value.
-//  * Certification. With the Cauchy-Schwarz bound sum_k |x_k R_kb| <=
-//    |x| |R_b|, every fast value is within E = coef * |x| * max_b |R_b| of the
-//    exact one. If the top key beats the second by more than 2E (plus the key
-//    quantisation), the bucket is the exact argmax. If only the third is
-//    certainly out, the token-round is queued with its two candidate columns;
-//    otherwise with a request to scan every column.
-//  * Re-decision in fp64 on the GPU for the queued token-rounds (typically a
-//    fraction of a percent).
+//  * Fast pass on the matrix cores in fp16. Each round's R is scaled by the
+//    power of two that brings its largest |R| into [2^14, 2^15) and rounded to
+//    fp16 (R_s); each token's x (bf16: at most 8 significant bits) is scaled
+//    the same way by its own power of two (x_s), which makes the conversion
+//    exact except for elements more than 2^28 below the token's largest.
+//    Scaling a row or a whole round changes no argmax. fp16 products are exact
+//    in fp32 and the MFMA accumulates in fp32. Each lane keeps the three
+//    largest |p| of its token as packed keys (|p| with the low mantissa bits
+//    replaced by (column << 1 | sign)), three integer min/max operations per
+//    value.
+//  * Certification. Every fast value is within
+//        E = |x_s| (rho_r + c |R_s|max) + sqrt(d) 2^-14 |R_s|max
+//    of the exact scaled projection: rho_r bounds |R_s,b - fp16(R_s,b)| (the
+//    prep pass computes it from the actual roundings, Cauchy-Schwarz does the
+//    rest), c bounds the fp32 accumulation, and the last term covers x
+//    elements a matrix core may flush as fp16 subnormals. If the top key beats
+//    the second by more than 2E (plus the key quantisation), the bucket is the
+//    exact argmax. If only the third is certainly out, the token-round is
+//    queued with its two candidate columns; otherwise with a request to scan
+//    every column.
+//  * Re-decision in fp64 on the GPU for the queued token-rounds (a few
+//    percent for Gaussian x and R).
 //  * fp32 inputs (or head sizes without a matrix-core kernel) use a plain fp32
 //    FMA pass with the same certification and re-decision.
 #include <algorithm>
@@ -32,7 +40,7 @@
 
 namespace lsh {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -40,8 +48,8 @@ static constexpr float kTwoM24 = 5.9604644775390625e-8f;   // 2^-24
 
 // ------------------------------------------------------------------ workspace
 static size_t rfrag_elems(const Dims& d) {
-    // [nh][ntiles][d/16 k-steps][2 splits][64 lanes][8] bf16
-    return (size_t)d.nh * hash_ntiles(d) * kHashColTile * d.d * 2;
+    // [nh][ntiles][d/16 k-steps][64 lanes][8] fp16
+    return (size_t)d.nh * hash_ntiles(d) * kHashColTile * d.d;
 }
 
 static size_t rt_elems(const Dims& d) {
@@ -51,10 +59,14 @@ static size_t rt_elems(const Dims& d) {
 
 size_t hash_workspace_bytes(const Dims& d) {
     size_t b = 256;                                              // counter
-    b += align_up(sizeof(float) * d.nh, 256);                    // rnorm
+    b += align_up(sizeof(float) * 3 * d.nh, 256);                // rnorm, rnorm_s, resn_s
     b += align_up(sizeof(uint16_t) * rfrag_elems(d), 256);       // rfrag
     b += align_up(sizeof(float) * rt_elems(d), 256);             // rt
-    b += align_up(sizeof(RefineItem) * (size_t)d.T * d.nh, 256); // queue
+    b += align_up(sizeof(RefineItem) * (size_t)queue_tokens(d) * d.nh, 256);   // queue
+    b += align_up(sizeof(int32_t) * 2 * (size_t)queue_tokens(d) / kWave * d.nh, 256);   // rcount
+    b += align_up(sizeof(int32_t) * d.nh, 256);                                          // scount
+    b += align_up(sizeof(int32_t) * (size_t)queue_tokens(d) * d.nh, 256);                // slist
+    b += align_up(sizeof(uint64_t) * (size_t)queue_tokens(d) * d.nh, 256);               // sbest
     return b;
 }
 
@@ -65,48 +77,103 @@ HashWorkspace carve_hash_workspace(void* ws, const Dims& d) {
     w.vmax = (uint32_t*)(p + 3 * sizeof(int32_t));
     p += 256;
     w.rnorm = (float*)p;
-    p += align_up(sizeof(float) * d.nh, 256);
+    w.rnorm_s = w.rnorm + d.nh;
+    w.resn_s = w.rnorm + 2 * d.nh;
+    p += align_up(sizeof(float) * 3 * d.nh, 256);
     w.rfrag = (uint16_t*)p;
     p += align_up(sizeof(uint16_t) * rfrag_elems(d), 256);
     w.rt = (float*)p;
     p += align_up(sizeof(float) * rt_elems(d), 256);
     w.queue = (RefineItem*)p;
+    p += align_up(sizeof(RefineItem) * (size_t)queue_tokens(d) * d.nh, 256);
+    w.rcount = (int32_t*)p;
+    p += align_up(sizeof(int32_t) * 2 * (size_t)queue_tokens(d) / kWave * d.nh, 256);
+    w.scount = (int32_t*)p;
+    p += align_up(sizeof(int32_t) * d.nh, 256);
+    w.slist = (int32_t*)p;
+    p += align_up(sizeof(int32_t) * (size_t)queue_tokens(d) * d.nh, 256);
+    w.sbest = (uint64_t*)p;
     return w;
 }
 
 // ------------------------------------------------------------------ R prep
-__global__ void zero_counter_kernel(int32_t* counter, float* rnorm, int nh) {
-    if (threadIdx.x < 4) counter[threadIdx.x] = 0;   // three queue counters and max|v|
-    for (int r = threadIdx.x; r < nh; r += blockDim.x) rnorm[r] = 0.f;
+__global__ void zero_counter_kernel(int32_t* counter, float* rnorm, int32_t* scount, int nh) {
+    if (threadIdx.x < 4) counter[threadIdx.x] = 0;   // re-decided count and max|v|
+    for (int r = threadIdx.x; r < 3 * nh; r += blockDim.x) rnorm[r] = 0.f;
+    for (int r = threadIdx.x; r < nh; r += blockDim.x) scount[r] = 0;
 }
 
 // One workgroup per (round, 32-column tile) of R, staged through LDS:
-//  * rnorm[r]  = max over columns of |R[r, :, col]|_2, rounded up (atomic max on
-//               the bits of a non-negative float, order independent);
-//  * rt        = R transposed to [round][column][k] in fp32 (padded columns are 0),
-//               read by the fp64 re-decision;
-//  * rfrag     = the bf16 hi/lo split of R in the A-operand order of
-//               v_mfma_f32_32x32x16_bf16: for (round, tile, k-step, split), 64
-//               lanes of 8 values, lane l holding column tile*32 + l%32 and
-//               k = kstep*16 + 8*(l/32) + e.
+//  * e_r from max|R| of the round (every workgroup of the round reads the
+//    whole round and finds the same value);
+//  * rnorm / rnorm_s / resn_s: column norms (sums of squares in fp32, then
+//    rounded up), folded by an atomic max on the bits of non-negative floats,
+//    which is order independent;
+//  * rt    = R transposed to [round][column][k] in fp32 (padded columns are 0),
+//            read by the fp64 re-decision;
+//  * rfrag = fp16(R * 2^e_r) in the A-operand order of
+//            v_mfma_f32_32x32x16_f16: for (round, tile, k-step), 64 lanes of 8
+//            values, lane l holding column tile*32 + l%32 and
+//            k = kstep*16 + 8*(l/32) + e.
 __global__ __launch_bounds__(256) void rprep_kernel(const float* __restrict__ R, int d, int half,
                                                     int ntiles, float* __restrict__ rnorm,
                                                     float* __restrict__ rt,
                                                     uint16_t* __restrict__ rfrag) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
     __shared__ float tile[128][kHashColTile + 1];
-    const int t = blockIdx.x, r = blockIdx.y;
+    __shared__ float wmax[4];
+    const int t = blockIdx.x, r = blockIdx.y, nh = gridDim.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const float* Rr = R + (int64_t)r * d * half;
+    const int n = d * half;   // a multiple of 64
+    float m = 0.f;
+    if ((reinterpret_cast<uintptr_t>(Rr) & 15) == 0) {
+        const f32x4* R4 = (const f32x4*)Rr;
+#pragma unroll 8
+        for (int i = threadIdx.x; i < n / 4; i += 256) {
+            const f32x4 q = R4[i];
+            m = fmaxf(m, fmaxf(fmaxf(fabsf(q.x), fabsf(q.y)), fmaxf(fabsf(q.z), fabsf(q.w))));
+        }
+    } else {
+#pragma unroll 8
+        for (int i = threadIdx.x; i < n; i += 256) m = fmaxf(m, fabsf(Rr[i]));
+    }
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if (lane == 0) wmax[wave] = m;
     const int col0 = t * kHashColTile;
+#pragma unroll 8
     for (int idx = threadIdx.x; idx < d * kHashColTile; idx += 256) {
         const int k = idx / kHashColTile, c = idx % kHashColTile;
-        tile[k][c] = (col0 + c < half) ? R[((int64_t)r * d + k) * half + col0 + c] : 0.f;
+        tile[k][c] = (col0 + c < half) ? Rr[(int64_t)k * half + col0 + c] : 0.f;
     }
     __syncthreads();
-    if (threadIdx.x < kHashColTile) {
-        float ss = 0.f;
-        for (int k = 0; k < d; ++k) ss = fmaf(tile[k][threadIdx.x], tile[k][threadIdx.x], ss);
-        // fp32 sum of d squares: relative error below d * 2^-24; sqrt halves it
-        const float nrm = sqrtf(ss) * (1.0f + (float)(d + 4) * kTwoM24);
-        atomicMax((int*)&rnorm[r], __float_as_int(nrm));
+    const float M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    const int e = 15 - __builtin_amdgcn_frexp_expf(M);   // M * 2^e in [2^14, 2^15)
+
+    {   // 8 threads per column, d/8 rows each
+        const int c = threadIdx.x >> 3, part = threadIdx.x & 7, klen = d / 8;
+        float s0 = 0.f, s1 = 0.f, s2 = 0.f;
+        for (int k = part * klen; k < (part + 1) * klen; ++k) {
+            const float a = tile[k][c];
+            const float as = ldexpf(a, e);
+            const float res = as - (float)(_Float16)as;   // exact
+            s0 = fmaf(a, a, s0);
+            s1 = fmaf(as, as, s1);
+            s2 = fmaf(res, res, s2);
+        }
+        for (int off = 1; off < 8; off <<= 1) {
+            s0 += __shfl_xor(s0, off);
+            s1 += __shfl_xor(s1, off);
+            s2 += __shfl_xor(s2, off);
+        }
+        if (part == 0 && col0 + c < half) {
+            // fp32 sums of d squares: relative error below d * 2^-24; sqrt halves it
+            const float up = 1.0f + (float)(d + 4) * kTwoM24;
+            const float flush = sqrtf((float)d) * 1.0001f * 6.103515625e-05f;   // sqrt(d) 2^-14
+            atomicMax((int*)&rnorm[r], __float_as_int(sqrtf(s0) * up));
+            atomicMax((int*)&rnorm[nh + r], __float_as_int(sqrtf(s1) * up));
+            atomicMax((int*)&rnorm[2 * nh + r], __float_as_int(sqrtf(s2) * up + flush));
+        }
     }
     float* dst = rt + ((int64_t)r * ntiles * kHashColTile + col0) * d;
     for (int idx = threadIdx.x; idx < d * kHashColTile; idx += 256) {
@@ -114,22 +181,18 @@ __global__ __launch_bounds__(256) void rprep_kernel(const float* __restrict__ R,
         dst[idx] = tile[k][c];
     }
     const int ks = d / 16;
-    for (int f = threadIdx.x; f < ks * 2 * kWave; f += 256) {
-        const int lane = f & 63, q = (f >> 6) & 1, s = f >> 7;
-        const int c = lane & 31, k0 = s * 16 + 8 * (lane >> 5);
+    for (int f = threadIdx.x; f < ks * kWave; f += 256) {
+        const int l = f & 63, s = f >> 6;
+        const int c = l & 31, k0 = s * 16 + 8 * (l >> 5);
         uint32_t w[4];
         for (int e2 = 0; e2 < 4; ++e2) {
-            uint32_t pair = 0;
-            for (int h = 0; h < 2; ++h) {
-                const float val = tile[k0 + 2 * e2 + h][c];
-                const uint16_t hi = f32_to_bf16(val);
-                const uint16_t lo = f32_to_bf16(val - bf16_to_f32(hi));  // the difference is exact
-                pair |= (uint32_t)(q ? lo : hi) << (16 * h);
-            }
-            w[e2] = pair;
+            const _Float16 h0 = (_Float16)ldexpf(tile[k0 + 2 * e2][c], e);
+            const _Float16 h1 = (_Float16)ldexpf(tile[k0 + 2 * e2 + 1][c], e);
+            w[e2] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+                    ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
         }
         u32x4 pk = {w[0], w[1], w[2], w[3]};
-        *(u32x4*)(rfrag + ((((int64_t)r * ntiles + t) * ks * 2 + f / kWave) * kWave + lane) * 8) = pk;
+        *(u32x4*)(rfrag + (((int64_t)r * ntiles + t) * ks * kWave + f) * 8) = pk;
     }
 }
 
@@ -147,31 +210,34 @@ __device__ __forceinline__ uint64_t lanes_below(int lane) {
     return lane ? (~0ull >> (64 - lane)) : 0ull;
 }
 
-// Appends the flagged lanes' items to the queue, one atomic per wave and mode.
-// The queue has room for every token-round; two-candidate items (mode 0) fill
-// it from the front, full scans (mode 1) from the back. counter[0] counts all
-// items, counter[1] the front part, counter[2] the back part.
-__device__ __forceinline__ void queue_push(bool flag, RefineItem it, int32_t* counter,
-                                           RefineItem* queue, int capacity, int lane) {
-    const uint64_t any = __ballot(flag);
-    if (!any) return;
-    const uint64_t m1 = __ballot(flag && it.mode == 1);
-    const uint64_t m0 = any & ~m1;
-    const int leader = __ffsll((long long)any) - 1;
-    int b0 = 0, b1 = 0;
-    if (lane == leader) {
-        atomicAdd(&counter[0], __popcll(any));
-        if (m0) b0 = atomicAdd(&counter[1], __popcll(m0));
-        if (m1) b1 = atomicAdd(&counter[2], __popcll(m1));
+// A wave's appends to its own queue region (see RefineItem): ballots give
+// each flagged lane its place; the running counts stay wave-uniform.
+struct RegionWriter {
+    RefineItem* base;   // the region's first item
+    int size;           // items in the region
+    int n0, n1;         // two-candidate items (front), full scans (back)
+
+    __device__ __forceinline__ void push(bool flag, const RefineItem& it, int lane) {
+        const uint64_t any = __ballot(flag);
+        if (!any) return;
+        const uint64_t m1 = __ballot(flag && it.mode == 1);
+        const uint64_t m0 = any & ~m1;
+        if (flag) {
+            if (it.mode == 1)
+                base[size - 1 - (n1 + __popcll(m1 & lanes_below(lane)))] = it;
+            else
+                base[n0 + __popcll(m0 & lanes_below(lane))] = it;
+        }
+        n0 += __popcll(m0);
+        n1 += __popcll(m1);
     }
-    b0 = __shfl(b0, leader);
-    b1 = __shfl(b1, leader);
-    if (!flag) return;
-    if (it.mode == 1)
-        queue[capacity - 1 - (b1 + __popcll(m1 & lanes_below(lane)))] = it;
-    else
-        queue[b0 + __popcll(m0 & lanes_below(lane))] = it;
-}
+    __device__ __forceinline__ void finish(int32_t* rcount, int64_t region, int lane) const {
+        if (lane == 0) {
+            rcount[2 * region] = n0;
+            rcount[2 * region + 1] = n1;
+        }
+    }
+};
 
 // Decision shared by both fast passes. v1 >= v2 >= v3 are the three largest
 // fast |p| values (as floats), thr the certification threshold.
@@ -195,46 +261,63 @@ __global__ __launch_bounds__(256) void hash_mfma_kernel(const uint16_t* __restri
                                                         const u32x4* __restrict__ rfrag,
                                                         const float* __restrict__ rnorm, Dims dm,
                                                         int32_t* __restrict__ buckets,
-                                                        int32_t* __restrict__ counter,
                                                         RefineItem* __restrict__ queue,
+                                                        int32_t* __restrict__ rcount,
                                                         const uint16_t* __restrict__ v,
                                                         uint32_t* __restrict__ vmax) {
     constexpr int KS = D / 16;
-    constexpr int TILE_U4 = KS * 2 * kWave;     // 16-byte lane fragments per column tile
+    constexpr int TILE_U4 = KS * kWave;         // 16-byte lane fragments per column tile
     constexpr int PRE = TILE_U4 / 256;          // fragments each thread stages
     constexpr int TOK_WAVE = 32 * TOKF;
     constexpr int TOK_WG = 4 * TOK_WAVE;
-    constexpr float kCoef = (float)(4 * D + 8) * kTwoM24 + 3.0517578125e-5f;  // + 2^-15
+    constexpr float kAcc = (float)(4 * D + 8) * kTwoM24;          // fp32 accumulation
+    constexpr float kFlushX = (D == 64 ? 8.0001f : 11.3138f) * 6.103515625e-05f;   // sqrt(d) 2^-14
     __shared__ u32x4 lds[2][TILE_U4];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int half = dm.nb / 2;
-    const int capacity = (int)(dm.T * dm.nh);
     const int ntiles = (half + kHashColTile - 1) / kHashColTile;
     const int total = dm.nh * ntiles;
     const int64_t tok0 = (int64_t)blockIdx.x * TOK_WG + (int64_t)wave * TOK_WAVE;
+    // this wave's queue region: its tokens, every round
+    const int64_t region = (int64_t)blockIdx.x * 4 + wave;
+    RegionWriter qw{queue + region * TOK_WAVE * dm.nh, TOK_WAVE * dm.nh, 0, 0};
     const int bits = 32 - __clz(2 * ntiles * kHashColTile - 1);
     const uint32_t keymask = 0x7FFFFFFFu & ~((1u << bits) - 1u);
     const float qerr = __uint_as_float((uint32_t)(127 + bits - 22) << 23) + 9.5367431640625e-7f;
 
-    // B operand: lane holds x[tok0 + f*32 + lane%32][16 s + 8 (lane/32) + e]
-    bf16x8 xb[TOKF][KS];
+    // B operand: lane holds x_s[tok0 + f*32 + lane%32][16 s + 8 (lane/32) + e]
+    // in fp16, x_s = x * 2^e with the token's largest |x| brought into [2^14, 2^15)
+    f16x8 xb[TOKF][KS];
     float xn2[TOKF];
 #pragma unroll
     for (int f = 0; f < TOKF; ++f) {
         const int64_t tok = tok0 + f * 32 + (lane & 31);
+        u32x4 u[KS];
+        uint32_t mb = 0;   // largest |x| as bf16 bits (integer order = float order)
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            u[s] = (u32x4){0u, 0u, 0u, 0u};
+            if (tok < dm.T) u[s] = ((const u32x4*)(qk + tok * D))[2 * s + (lane >> 5)];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mb = max(mb, max(u[s][e] & 0x7FFFu, (u[s][e] >> 16) & 0x7FFFu));
+        }
+        mb = max(mb, (uint32_t)__shfl_xor((int)mb, 32));
+        const int xe = 15 - __builtin_amdgcn_frexp_expf(__uint_as_float(mb << 16));
         xn2[f] = 0.f;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            u32x4 u = {0u, 0u, 0u, 0u};
-            if (tok < dm.T) u = ((const u32x4*)(qk + tok * D))[2 * s + (lane >> 5)];
-            xb[f][s] = __builtin_bit_cast(bf16x8, u);
+            u32x4 h;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float a = __uint_as_float(u[e] << 16), b = __uint_as_float(u[e] & 0xFFFF0000u);
+                const float a = ldexpf(__uint_as_float(u[s][e] << 16), xe);
+                const float b = ldexpf(__uint_as_float(u[s][e] & 0xFFFF0000u), xe);
                 xn2[f] = fmaf(a, a, fmaf(b, b, xn2[f]));
+                h[e] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
+                       ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
             }
+            xb[f][s] = __builtin_bit_cast(f16x8, h);
         }
         xn2[f] += __shfl_xor(xn2[f], 32);
     }
@@ -282,14 +365,11 @@ __global__ __launch_bounds__(256) void hash_mfma_kernel(const uint16_t* __restri
         const u32x4* cur = lds[g & 1];
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            const bf16x8 ahi = __builtin_bit_cast(bf16x8, cur[(2 * s + 0) * kWave + lane]);
-            const bf16x8 alo = __builtin_bit_cast(bf16x8, cur[(2 * s + 1) * kWave + lane]);
+            const f16x8 a = __builtin_bit_cast(f16x8, cur[s * kWave + lane]);
 #pragma unroll
-            for (int f = 0; f < TOKF; ++f) {
-                acc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi, xb[f][s],
-                                                                 s ? acc[f] : (f32x16){}, 0, 0, 0);
-                acc[f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo, xb[f][s], acc[f], 0, 0, 0);
-            }
+            for (int f = 0; f < TOKF; ++f)
+                acc[f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, xb[f][s],
+                                                                s ? acc[f] : (f32x16){}, 0, 0, 0);
         }
     };
 
@@ -315,7 +395,8 @@ __global__ __launch_bounds__(256) void hash_mfma_kernel(const uint16_t* __restri
             }
         }
         if (t != ntiles - 1) return;
-        const float E2 = 2.f * kCoef * rnorm[r];
+        const float rn_s = rnorm[dm.nh + r], res_s = rnorm[2 * dm.nh + r];
+        const float Ea = 2.f * (res_s + kAcc * rn_s), Eb = 2.f * kFlushX * rn_s;
 #pragma unroll
         for (int f = 0; f < TOKF; ++f) {
             // keys are non-negative floats whose bit patterns stay below the
@@ -335,7 +416,7 @@ __global__ __launch_bounds__(256) void hash_mfma_kernel(const uint16_t* __restri
             const float v2 = __uint_as_float(b2 & keymask);
             const float v3 = __uint_as_float(__float_as_uint(k3[f]) & keymask);
             const float xn = sqrtf(xn2[f]) * (1.0f + (float)(D + 4) * kTwoM24);
-            const float thr = E2 * xn + v1 * qerr + 1e-30f;
+            const float thr = Ea * xn + Eb + v1 * qerr + 1e-30f;
             const int mode = classify(v1, v2, v3, thr);
             const uint32_t i1 = b1 & ~keymask & 0x7FFFFFFFu, i2 = b2 & ~keymask & 0x7FFFFFFFu;
             const int c1 = (int)(i1 >> 1), c2 = (int)(i2 >> 1);
@@ -343,7 +424,7 @@ __global__ __launch_bounds__(256) void hash_mfma_kernel(const uint16_t* __restri
             const int32_t item = item0[f] + r * dm.L;
             if (mine) buckets[item] = bucket;
             RefineItem it{item, c1, c2, mode};
-            queue_push(mine && mode >= 0, it, counter, queue, capacity, lane);
+            qw.push(mine && mode >= 0, it, lane);
             k1[f] = k2[f] = k3[f] = 0.f;
         }
     };
@@ -386,6 +467,7 @@ __global__ __launch_bounds__(256) void hash_mfma_kernel(const uint16_t* __restri
     } else {
         epilogue(g - 1, accA);
     }
+    qw.finish(rcount, region, lane);
 }
 
 // ------------------------------------------------------------------ fast pass (fp32 FMA)
@@ -396,13 +478,15 @@ __global__ __launch_bounds__(256) void hash_valu_kernel(const T* __restrict__ qk
                                                         const float* __restrict__ R,
                                                         const float* __restrict__ rnorm, Dims dm,
                                                         int32_t* __restrict__ buckets,
-                                                        int32_t* __restrict__ counter,
-                                                        RefineItem* __restrict__ queue) {
+                                                        RefineItem* __restrict__ queue,
+                                                        int32_t* __restrict__ rcount) {
     constexpr float kCoef = (float)(2 * D + 8) * kTwoM24;
     const int lane = threadIdx.x & 63;
     const int r = blockIdx.y;
     const int half = dm.nb / 2;
-    const int capacity = (int)(dm.T * dm.nh);
+    // queue region of this wave: its 64 tokens in round r
+    const int64_t region = (int64_t)r * gridDim.x * 4 + (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    RegionWriter qw{queue + region * kWave, kWave, 0, 0};
     const int64_t tok = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const bool live = tok < dm.T;
     float x[D];
@@ -442,137 +526,211 @@ __global__ __launch_bounds__(256) void hash_valu_kernel(const T* __restrict__ qk
         buckets[item] = i1 + (neg1 ? half : 0);
     }
     RefineItem it{(int32_t)item, i1, i2, mode};
-    queue_push(live && mode >= 0, it, counter, queue, capacity, lane);
+    qw.push(live && mode >= 0, it, lane);
+    qw.finish(rcount, region, lane);
 }
 
 // ------------------------------------------------------------------ re-decision in fp64
-// One wave per queued token-round. Mode 0 computes the two candidate columns
-// (half a wave each); mode 1 scans every column. The exact rule: largest |p|,
-// ties to the lowest index of [p, -p] (a p of either zero sign counts as "+").
+// The exact rule: largest |p| = |x . R_b| over [p, -p], ties to the lowest
+// index of the concatenation (a p of either zero sign counts as "+").
+//
+// Pass 1 (one wave per queue region, no barriers): two-candidate items are
+// decided here, four at a time, 16 lanes per item (each lane a sixteenth of
+// the row for both columns). Full-scan items are moved to their round's list
+// for pass 2 (a per-round atomic ticket; such items are rare). Workgroup 0
+// also sums the region counts into the public count.
 template <typename T>
 __global__ __launch_bounds__(256) void hash_refine_kernel(const T* __restrict__ qk,
                                                           const float* __restrict__ rt, Dims dm,
-                                                          const int32_t* __restrict__ counter,
+                                                          int32_t* __restrict__ counter,
                                                           const RefineItem* __restrict__ queue,
-                                                          int32_t* __restrict__ buckets) {
-    typedef float f32x4 __attribute__((ext_vector_type(4)));
+                                                          const int32_t* __restrict__ rcount,
+                                                          int64_t nregions, int region_size,
+                                                          int32_t* __restrict__ buckets,
+                                                          int32_t* __restrict__ scount,
+                                                          int32_t* __restrict__ slist,
+                                                          uint64_t* __restrict__ sbest,
+                                                          int64_t cap) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int half = dm.nb / 2;
     const int hpad = ((half + kHashColTile - 1) / kHashColTile) * kHashColTile;
     const int D = dm.d;
-    const int capacity = (int)(dm.T * dm.nh);
-    const int n0 = counter[1], n1 = counter[2];
 
-    auto locate = [&](int32_t item, const T*& x, const float*& Rr) {
-        const int i = item % dm.L;
-        const int rest = item / dm.L;
-        const int r = rest % dm.nh;
-        const int bh = rest / dm.nh;
-        x = qk + ((int64_t)bh * dm.L + i) * D;
-        Rr = rt + (int64_t)r * hpad * D;      // [column][k]
-    };
+    if (blockIdx.x == 0) {
+        __shared__ int32_t part_sum[4];
+        int32_t c = 0;
+#pragma unroll 16
+        for (int64_t i = threadIdx.x; i < 2 * nregions; i += 256) c += rcount[i];
+        for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+        if (lane == 0) part_sum[wave] = c;
+        __syncthreads();
+        if (threadIdx.x == 0) counter[0] = part_sum[0] + part_sum[1] + part_sum[2] + part_sum[3];
+    }
 
-    // two candidate columns: one wave per item, half a wave per column
-    const int64_t gwave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-    const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
-    for (int64_t q = gwave; q < n0; q += nwaves) {
-        const RefineItem it = queue[q];
-        const T* x;
-        const float* Rr;
-        locate(it.item, x, Rr);
-        const int col = (lane < 32) ? it.a : it.b;
-        double acc = 0.0;
-        if (col >= 0 && col < half) {
-            const float* rc = Rr + (int64_t)col * D;
-            for (int k = lane & 31; k < D; k += 32) acc += (double)IO<T>::load(x, k) * (double)rc[k];
-        }
-        for (int off = 16; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-        const double pa = __shfl(acc, 0), pb = __shfl(acc, 32);
-        if (lane == 0) {
+    const int sub = lane >> 4, l16 = lane & 15, kper = D / 16;
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    for (int64_t region = (int64_t)blockIdx.x * 4 + wave; region < nregions; region += nwaves) {
+        const int n0 = rcount[2 * region], n1 = rcount[2 * region + 1];
+        const RefineItem* rq = queue + region * region_size;
+        for (int q0 = 0; q0 < n0; q0 += 4) {
+            const int q = q0 + sub;
+            const bool ok = q < n0;
+            const RefineItem it = ok ? rq[q] : RefineItem{0, -1, -1, 0};
             const bool va = it.a >= 0 && it.a < half, vb = it.b >= 0 && it.b < half && it.b != it.a;
-            const int ca = it.a + (pa < 0.0 ? half : 0), cb = it.b + (pb < 0.0 ? half : 0);
-            int pick;
-            if (!vb) pick = ca;
-            else if (!va) pick = cb;
-            else if (fabs(pa) > fabs(pb)) pick = ca;
-            else if (fabs(pb) > fabs(pa)) pick = cb;
-            else pick = min(ca, cb);
-            buckets[it.item] = pick;
+            double pa = 0.0, pb = 0.0;
+            if (ok) {
+                const int i = it.item % dm.L, rest = it.item / dm.L;
+                const int r = rest % dm.nh, bh = rest / dm.nh;
+                const T* x = qk + ((int64_t)bh * dm.L + i) * D + l16 * kper;
+                const float* Rr = rt + (int64_t)r * hpad * D;      // [column][k]
+                const float* ra = Rr + (int64_t)(va ? it.a : 0) * D + l16 * kper;
+                const float* rb = Rr + (int64_t)(vb ? it.b : 0) * D + l16 * kper;
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    if (k < kper) {
+                        const double xv = (double)IO<T>::load(x, k);
+                        pa += xv * (double)ra[k];
+                        pb += xv * (double)rb[k];
+                    }
+            }
+            for (int off = 8; off > 0; off >>= 1) {
+                pa += __shfl_xor(pa, off);
+                pb += __shfl_xor(pb, off);
+            }
+            if (ok && l16 == 0) {
+                const int ca = it.a + (pa < 0.0 ? half : 0), cb = it.b + (pb < 0.0 ? half : 0);
+                int pick;
+                if (!vb) pick = ca;
+                else if (!va) pick = cb;
+                else if (fabs(pa) > fabs(pb)) pick = ca;
+                else if (fabs(pb) > fabs(pa)) pick = cb;
+                else pick = min(ca, cb);
+                buckets[it.item] = pick;
+            }
+        }
+        for (int q = lane; q < n1; q += kWave) {
+            const int32_t item = rq[region_size - 1 - q].item;
+            const int r = (item / dm.L) % dm.nh;
+            const int slot = atomicAdd(&scount[r], 1);
+            slist[(int64_t)r * cap + slot] = item;
+            sbest[(int64_t)r * cap + slot] = 0ull;
         }
     }
+}
 
-    // every column: one workgroup per item; 32 groups of 8 lanes each take a
-    // column per pass, each lane an eighth of the row (16-byte loads).
-    __shared__ double sv[4];
-    __shared__ int si[4];
-    const int part = lane & 7, grp = threadIdx.x >> 3;      // 32 column groups
-    const int klen = D / 8;
-    for (int64_t q = blockIdx.x; q < n1; q += gridDim.x) {
-        const RefineItem it = queue[capacity - 1 - q];
-        const T* x;
-        const float* Rr;
-        locate(it.item, x, Rr);
-        double xk[16];
-#pragma unroll
-        for (int k = 0; k < 16; ++k) xk[k] = k < klen ? (double)IO<T>::load(x, part * klen + k) : 0.0;
-        double bestv = -1.0;
-        int besti = 0x7FFFFFFF;
-        for (int col0 = 0; col0 < half; col0 += 32) {
-            const int col = col0 + grp;
+// Pass 2: every column for the listed items of a round, grouped so that a
+// workgroup reads one 32-column tile of R once for 64 items. Block (t, r, z)
+// takes groups z, z + Z, ... of round r's list. Each (item, column) product is
+// summed in fp64; the best of the tile goes into the item's key by a 64-bit
+// atomic max. Key = bits of |p| (a non-negative double, so integer order is
+// float order) with the low 12 bits replaced by 4095 - bucket: equal |p| then
+// prefer the lower bucket index, and values closer than 2^-40 relative count
+// as equal.
+template <int D, typename T>
+__global__ __launch_bounds__(256) void hash_scan_kernel(const T* __restrict__ qk,
+                                                        const float* __restrict__ rt, Dims dm,
+                                                        const int32_t* __restrict__ scount,
+                                                        const int32_t* __restrict__ slist,
+                                                        uint64_t* __restrict__ sbest,
+                                                        int64_t cap) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    constexpr int G = 64;
+    constexpr int S = D + 4;      // row stride: 16-byte aligned rows, rows 4 banks apart
+    __shared__ __attribute__((aligned(16))) float rtile[kHashColTile][S];
+    __shared__ __attribute__((aligned(16))) float xs[G][S];
+    __shared__ int64_t xrow[G];   // element offset of each item's row of x
+    const int t = blockIdx.x, r = blockIdx.y;
+    const int half = dm.nb / 2;
+    const int hpad = ((half + kHashColTile - 1) / kHashColTile) * kHashColTile;
+    const int n = min(scount[r], (int)cap);
+    const int64_t first = (int64_t)blockIdx.z * G;
+    if (first >= n) return;
+    const float* Rt = rt + ((int64_t)r * hpad + (int64_t)t * kHashColTile) * D;
+#pragma unroll 8
+    for (int i = threadIdx.x; i < kHashColTile * D; i += 256) rtile[i / D][i % D] = Rt[i];
+    const int it = threadIdx.x >> 2, cq = threadIdx.x & 3;   // item, column quarter
+    for (int64_t g0 = first; g0 < n; g0 += (int64_t)gridDim.z * G) {
+        const int gn = (int)min((int64_t)G, n - g0);
+        __syncthreads();
+        if (threadIdx.x < G) {
+            int64_t off = -1;
+            if ((int)threadIdx.x < gn) {
+                const int32_t item = slist[(int64_t)r * cap + g0 + threadIdx.x];
+                const int pos = item % dm.L, bh = item / dm.L / dm.nh;
+                off = ((int64_t)bh * dm.L + pos) * D;
+            }
+            xrow[threadIdx.x] = off;
+        }
+        __syncthreads();
+#pragma unroll 8
+        for (int i = threadIdx.x; i < G * D; i += 256) {
+            const int j = i / D, k = i % D;
+            const int64_t off = xrow[j];
+            xs[j][k] = off >= 0 ? IO<T>::load(qk, off + k) : 0.f;
+        }
+        __syncthreads();
+        if (it >= gn) continue;
+        uint64_t best = 0;
+#pragma unroll 2
+        for (int u = 0; u < kHashColTile / 4; ++u) {
+            const int c = cq + 4 * u, col = t * kHashColTile + c;
             double p = 0.0;
-            if (col < half) {
-                const f32x4* rc = (const f32x4*)(Rr + (int64_t)col * D + part * klen);
-                f32x4 rv[4];
+#pragma unroll 4
+            for (int k = 0; k < D; k += 4) {
+                const f32x4 a = *(const f32x4*)&xs[it][k];
+                const f32x4 b = *(const f32x4*)&rtile[c][k];
 #pragma unroll
-                for (int v4 = 0; v4 < 4; ++v4)
-                    if (4 * v4 < klen) rv[v4] = rc[v4];
-#pragma unroll
-                for (int v4 = 0; v4 < 4; ++v4)
-                    if (4 * v4 < klen)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) p += xk[4 * v4 + e] * (double)rv[v4][e];
+                for (int e = 0; e < 4; ++e) p += (double)a[e] * (double)b[e];
             }
-            p += __shfl_xor(p, 1);
-            p += __shfl_xor(p, 2);
-            p += __shfl_xor(p, 4);
             if (col < half) {
-                const double v = fabs(p);
-                const int ci = col + (p < 0.0 ? half : 0);
-                if (v > bestv || (v == bestv && ci < besti)) { bestv = v; besti = ci; }
+                const int bucket = col + (p < 0.0 ? half : 0);
+                const uint64_t key = (__double_as_longlong(fabs(p)) & ~0xFFFull) |
+                                     (uint64_t)(4095 - bucket);
+                best = key > best ? key : best;
             }
         }
-        for (int off = 32; off > 0; off >>= 1) {
-            const double ov = __shfl_xor(bestv, off);
-            const int oi = __shfl_xor(besti, off);
-            if (ov > bestv || (ov == bestv && oi < besti)) { bestv = ov; besti = oi; }
+        for (int off = 1; off < 4; off <<= 1) {
+            const uint64_t o = __shfl_xor(best, off);
+            best = o > best ? o : best;
         }
-        if (lane == 0) {
-            sv[wave] = bestv;
-            si[wave] = besti;
-        }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            for (int w = 1; w < 4; ++w)
-                if (sv[w] > bestv || (sv[w] == bestv && si[w] < besti)) { bestv = sv[w]; besti = si[w]; }
-            buckets[it.item] = besti;
-        }
-        __syncthreads();
+        if (cq == 0) atomicMax((unsigned long long*)&sbest[(int64_t)r * cap + g0 + it], best);
     }
+}
+
+// Pass 3: the listed items take the bucket of their best key.
+__global__ __launch_bounds__(256) void hash_scan_finish_kernel(const int32_t* __restrict__ scount,
+                                                               const int32_t* __restrict__ slist,
+                                                               const uint64_t* __restrict__ sbest,
+                                                               int64_t cap,
+                                                               int32_t* __restrict__ buckets) {
+    const int r = blockIdx.y;
+    const int n = min(scount[r], (int)cap);
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        buckets[slist[(int64_t)r * cap + i]] = 4095 - (int)(sbest[(int64_t)r * cap + i] & 0xFFFull);
 }
 
 // ------------------------------------------------------------------ launcher
 template <typename T>
-static hipError_t launch_valu_and_refine(const T* qk, const float* R, const Dims& d,
-                                         int32_t* buckets, const HashWorkspace& w, hipStream_t st,
-                                         hipEvent_t* ev, int* nev, const char** names) {
-    dim3 grid((unsigned)((d.T + 255) / 256), (unsigned)d.nh);
-    if (d.d == 64)
-        hash_valu_kernel<64, T><<<grid, 256, 0, st>>>(qk, R, w.rnorm, d, buckets, w.counter, w.queue);
-    else
-        hash_valu_kernel<128, T><<<grid, 256, 0, st>>>(qk, R, w.rnorm, d, buckets, w.counter, w.queue);
-    hipError_t e = mark(st, ev, nev, names, "hash_fast_fp32");
+static hipError_t launch_refine(const T* qk, const Dims& d, int32_t* buckets,
+                                const HashWorkspace& w, int64_t nregions, int region_size,
+                                hipStream_t st, hipEvent_t* ev, int* nev, const char** names) {
+    const int64_t cap = queue_tokens(d);
+    const unsigned blocks = (unsigned)std::min<int64_t>(2048, (nregions + 3) / 4);
+    hash_refine_kernel<T><<<blocks, 256, 0, st>>>(qk, w.rt, d, w.counter, w.queue, w.rcount,
+                                                  nregions, region_size, buckets, w.scount,
+                                                  w.slist, w.sbest, cap);
+    hipError_t e = mark(st, ev, nev, names, "hash_refine_pairs");
     if (e != hipSuccess) return e;
-    return hipSuccess;
+    // enough groups for a few thousand listed items per round; more loop
+    const unsigned z = (unsigned)std::min<int64_t>(16, (cap + 63) / 64);
+    const dim3 sgrid((unsigned)hash_ntiles(d), (unsigned)d.nh, z);
+    if (d.d == 64)
+        hash_scan_kernel<64, T><<<sgrid, 256, 0, st>>>(qk, w.rt, d, w.scount, w.slist, w.sbest, cap);
+    else
+        hash_scan_kernel<128, T><<<sgrid, 256, 0, st>>>(qk, w.rt, d, w.scount, w.slist, w.sbest, cap);
+    hash_scan_finish_kernel<<<dim3(4, (unsigned)d.nh), 256, 0, st>>>(w.scount, w.slist, w.sbest,
+                                                                    cap, buckets);
+    return mark(st, ev, nev, names, "hash_refine_scan");
 }
 
 hipError_t launch_hash(const void* qk, const float* R, const Dims& d, int32_t* buckets,
@@ -581,38 +739,43 @@ hipError_t launch_hash(const void* qk, const float* R, const Dims& d, int32_t* b
     const int half = d.nb / 2;
     const int ntiles = hash_ntiles(d);
     hipError_t e;
-    zero_counter_kernel<<<1, 256, 0, st>>>(w.counter, w.rnorm, d.nh);
+    zero_counter_kernel<<<1, 256, 0, st>>>(w.counter, w.rnorm, w.scount, d.nh);
     rprep_kernel<<<dim3((unsigned)ntiles, (unsigned)d.nh), 256, 0, st>>>(R, d.d, half, ntiles,
                                                                          w.rnorm, w.rt, w.rfrag);
     if ((e = mark(st, ev, nev, names, "hash_prep")) != hipSuccess) return e;
-    // enough waves that a typical queue is drained in one or two items per wave
-    const unsigned refine_blocks = (unsigned)std::min<int64_t>(4096, (d.T * d.nh + 255) / 256 + 1);
     if (d.dtype == LSH_BF16) {
 #ifndef LSH_HASH_TOKF
 #define LSH_HASH_TOKF 2
 #endif
         constexpr int TOKF = LSH_HASH_TOKF;
-        const int64_t per_wg = 4 * 32 * TOKF;
+        constexpr int per_wave = 32 * TOKF, per_wg = 4 * per_wave;
+        static_assert(per_wg <= kQueuePad, "queue regions must fit the padded capacity");
         const unsigned grid = (unsigned)((d.T + per_wg - 1) / per_wg);
         const uint16_t* x = (const uint16_t*)qk;
         if (d.d == 64)
             hash_mfma_kernel<64, TOKF><<<grid, 256, 0, st>>>(x, (const u32x4*)w.rfrag, w.rnorm, d,
-                                                           buckets, w.counter, w.queue,
+                                                           buckets, w.queue, w.rcount,
                                                            (const uint16_t*)v_for_max, w.vmax);
         else
             hash_mfma_kernel<128, TOKF><<<grid, 256, 0, st>>>(x, (const u32x4*)w.rfrag, w.rnorm, d,
-                                                            buckets, w.counter, w.queue,
+                                                            buckets, w.queue, w.rcount,
                                                             (const uint16_t*)v_for_max, w.vmax);
         if ((e = mark(st, ev, nev, names, "hash_fast_mfma")) != hipSuccess) return e;
-        hash_refine_kernel<uint16_t><<<refine_blocks, 256, 0, st>>>(x, w.rt, d, w.counter, w.queue,
-                                                                    buckets);
+        return launch_refine(x, d, buckets, w, (int64_t)grid * 4, per_wave * d.nh, st, ev, nev,
+                             names);
     } else {
-        e = launch_valu_and_refine((const float*)qk, R, d, buckets, w, st, ev, nev, names);
-        if (e != hipSuccess) return e;
-        hash_refine_kernel<float><<<refine_blocks, 256, 0, st>>>((const float*)qk, w.rt, d,
-                                                                 w.counter, w.queue, buckets);
+        const float* x = (const float*)qk;
+        dim3 grid((unsigned)((d.T + 255) / 256), (unsigned)d.nh);
+        if (d.d == 64)
+            hash_valu_kernel<64, float><<<grid, 256, 0, st>>>(x, R, w.rnorm, d, buckets, w.queue,
+                                                              w.rcount);
+        else
+            hash_valu_kernel<128, float><<<grid, 256, 0, st>>>(x, R, w.rnorm, d, buckets, w.queue,
+                                                               w.rcount);
+        if ((e = mark(st, ev, nev, names, "hash_fast_fp32")) != hipSuccess) return e;
+        return launch_refine(x, d, buckets, w, (int64_t)grid.x * 4 * d.nh, kWave, st, ev, nev,
+                             names);
     }
-    return mark(st, ev, nev, names, "hash_refine_fp64");
 }
 
 }  // namespace lsh

@@ -50,13 +50,37 @@ struct RefineItem {
     int32_t item, a, b, mode;
 };
 
+// The queue is cut into fixed regions, one per wave of the fast pass, so a
+// wave appends without any atomic: two-candidate items fill its region from
+// the front, full scans from the back, and the wave stores the two counts
+// (rcount[2 * region], rcount[2 * region + 1]) when it ends. Capacity covers
+// T rounded up to kQueuePad tokens, every round.
+constexpr int kQueuePad = 256;
+inline int64_t queue_tokens(const Dims& d) { return (d.T + kQueuePad - 1) / kQueuePad * kQueuePad; }
+
 struct HashWorkspace {
-    int32_t* counter;     // [3] queued items: total (the public count), front, back
+    int32_t* counter;     // [0]: items re-decided (the public count)
     uint32_t* vmax;       // max|v| (bf16 bits) when the fast pass is asked to fold it in
-    float* rnorm;         // [nh] max column 2-norm of R per round, rounded up
-    uint16_t* rfrag;      // bf16 hi/lo split of R in matrix-core fragment order
+    // Per-round bounds, each [nh] and contiguous, rounded up (atomic max over
+    // column tiles). With R_s = R * 2^e_r, e_r the power of two that brings
+    // max|R| of round r into [2^14, 2^15):
+    //   rnorm   max column 2-norm of R
+    //   rnorm_s max column 2-norm of R_s
+    //   resn_s  max column 2-norm of R_s - fp16(R_s), plus the fp16 subnormal
+    //           elements a matrix core may flush
+    float* rnorm;
+    float* rnorm_s;
+    float* resn_s;
+    uint16_t* rfrag;      // fp16(R_s) in matrix-core fragment order
     float* rt;            // R transposed to [nh][ntiles*32][d], fp32
-    RefineItem* queue;    // [T*nh]
+    RefineItem* queue;    // [queue_tokens * nh]
+    int32_t* rcount;      // [2 * queue_tokens * nh / 64]: per-region counts
+    // Full-scan items regrouped by round for the scan pass: per round r,
+    // scount[r] items, slist[r * queue_tokens + i] their flat bucket index and
+    // sbest[r * queue_tokens + i] the best packed key found so far.
+    int32_t* scount;      // [nh]
+    int32_t* slist;       // [nh * queue_tokens]
+    uint64_t* sbest;      // [nh * queue_tokens]
 };
 size_t hash_workspace_bytes(const Dims& d);
 HashWorkspace carve_hash_workspace(void* ws, const Dims& d);
