@@ -35,6 +35,9 @@
  *      inv             [B, H, n_hashes, L]     int32, inv[i] = slot of position i
  *      lse_sorted      [B, H, n_hashes, L]     float32, by sorted slot
  *      o_sorted        [B, H, n_hashes, L, d]  float32, by sorted slot
+ *  - Every tensor pointer and the workspace must be 16-byte aligned (the
+ *    kernels move rows in 16-byte pieces); a misaligned pointer is rejected
+ *    with LSH_ERR_ARG.
  *  - Inputs must be finite.
  *  - Return value: LSH_OK (0) or a negative LSH_ERR_* code. Argument checks
  *    run on the host before anything is enqueued; on any error nothing has

@@ -6,6 +6,8 @@
 #include <cstdio>
 #include <cstring>
 
+#include <initializer_list>
+
 #include "lsh_internal.h"
 
 using namespace lsh;
@@ -54,6 +56,13 @@ int validate(const lsh_shape_t* s) {
 
 bool empty(const lsh_shape_t* s) { return s->B == 0 || s->H == 0 || s->L == 0; }
 
+// Non-zero when any of the pointers is not 16-byte aligned (NULLs pass).
+int misaligned(std::initializer_list<const void*> ptrs) {
+    for (const void* p : ptrs)
+        if (reinterpret_cast<uintptr_t>(p) & 15u) return 1;
+    return 0;
+}
+
 struct FwdLayout {
     size_t hash, sort, buckets, perm, inv, lse, o, total;
 };
@@ -83,6 +92,7 @@ FwdLayout fwd_layout(const Dims& d) {
 int check_ws(const char* stage, const Dims& d, void* ws, size_t ws_bytes, size_t need) {
     (void)d;
     if (!ws) return fail(LSH_ERR_WORKSPACE, "%s: workspace is NULL", stage);
+    if (misaligned({ws})) return fail(LSH_ERR_ARG, "%s: workspace must be 16-byte aligned", stage);
     if (ws_bytes < need)
         return fail(LSH_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", stage, ws_bytes,
                     need);
@@ -151,6 +161,8 @@ int lsh_hash(const void* qk, const float* R, const lsh_shape_t* shape, int32_t* 
     if (rc) return rc;
     if (empty(shape)) return LSH_OK;
     if (!qk || !R || !buckets) return fail(LSH_ERR_ARG, "lsh_hash: NULL tensor pointer");
+    if (misaligned({qk, R, buckets}))
+        return fail(LSH_ERR_ARG, "lsh_hash: tensor pointers must be 16-byte aligned");
     const Dims d = make_dims(*shape);
     if ((rc = check_ws("lsh_hash", d, ws, ws_bytes, hash_workspace_bytes(d)))) return rc;
     hipError_t e = launch_hash(qk, R, d, buckets, carve_hash_workspace(ws, d), (hipStream_t)stream,
@@ -166,6 +178,8 @@ int lsh_sort(const int32_t* buckets, const lsh_shape_t* shape, int32_t* perm, in
     if (rc) return rc;
     if (empty(shape)) return LSH_OK;
     if (!buckets || !perm || !inv) return fail(LSH_ERR_ARG, "lsh_sort: NULL tensor pointer");
+    if (misaligned({buckets, perm, inv}))
+        return fail(LSH_ERR_ARG, "lsh_sort: tensor pointers must be 16-byte aligned");
     const Dims d = make_dims(*shape);
     if ((rc = check_ws("lsh_sort", d, ws, ws_bytes, sort_workspace_bytes(d)))) return rc;
     hipError_t e = launch_sort(buckets, d, perm, inv, ws, (hipStream_t)stream, nullptr, nullptr,
@@ -182,6 +196,8 @@ int lsh_chunk_attend(const void* qk, const void* v, const int32_t* buckets, cons
     if (empty(shape)) return LSH_OK;
     if (!qk || !v || !buckets || !perm || !o_sorted || !lse_sorted)
         return fail(LSH_ERR_ARG, "lsh_chunk_attend: NULL tensor pointer");
+    if (misaligned({qk, v, buckets, perm, o_sorted, lse_sorted}))
+        return fail(LSH_ERR_ARG, "lsh_chunk_attend: tensor pointers must be 16-byte aligned");
     const Dims d = make_dims(*shape);
     const OSorted o{o_sorted, false, nullptr};
     hipError_t e = launch_attend(qk, v, buckets, perm, d, o, lse_sorted, (hipStream_t)stream,
@@ -198,6 +214,8 @@ int lsh_unsort_combine(const float* o_sorted, const float* lse_sorted, const int
     if (empty(shape)) return LSH_OK;
     if (!o_sorted || !lse_sorted || !inv || !out)
         return fail(LSH_ERR_ARG, "lsh_unsort_combine: NULL tensor pointer");
+    if (misaligned({o_sorted, lse_sorted, inv, out}))
+        return fail(LSH_ERR_ARG, "lsh_unsort_combine: tensor pointers must be 16-byte aligned");
     const Dims d = make_dims(*shape);
     const OSorted o{(void*)o_sorted, false, nullptr};
     hipError_t e = launch_combine(o, lse_sorted, inv, d, out, (hipStream_t)stream, nullptr,
@@ -213,6 +231,8 @@ int lsh_attention_fwd(const void* qk, const void* v, const float* R, const lsh_s
     if (rc) return rc;
     if (empty(shape)) return LSH_OK;
     if (!qk || !v || !R || !out) return fail(LSH_ERR_ARG, "lsh_attention_fwd: NULL tensor pointer");
+    if (misaligned({qk, v, R, out}))
+        return fail(LSH_ERR_ARG, "lsh_attention_fwd: tensor pointers must be 16-byte aligned");
     return run_fwd(qk, v, R, shape, out, ws, ws_bytes, (hipStream_t)stream, nullptr, nullptr,
                    nullptr);
 }
@@ -230,6 +250,8 @@ int lsh_attention_fwd_timed(const void* qk, const void* v, const float* R,
     if (empty(shape)) return LSH_OK;
     if (!qk || !v || !R || !out)
         return fail(LSH_ERR_ARG, "lsh_attention_fwd_timed: NULL tensor pointer");
+    if (misaligned({qk, v, R, out}))
+        return fail(LSH_ERR_ARG, "lsh_attention_fwd_timed: tensor pointers must be 16-byte aligned");
     constexpr int kMaxMarks = 16;
     hipEvent_t ev[kMaxMarks + 1];
     int created = 0;

@@ -535,8 +535,8 @@ __global__ __launch_bounds__(256) void hash_valu_kernel(const T* __restrict__ qk
 // index of the concatenation (a p of either zero sign counts as "+").
 //
 // Pass 1 (one wave per queue region, no barriers): two-candidate items are
-// decided here, four at a time, 16 lanes per item (each lane a sixteenth of
-// the row for both columns). Full-scan items are moved to their round's list
+// decided here, 16 at a time, 4 lanes per item (each lane a quarter of the
+// row for both columns), the next items' records fetched a pass ahead. Full-scan items are moved to their round's list
 // for pass 2 (a per-round atomic ticket; such items are rare). Workgroup 0
 // also sums the region counts into the public count.
 template <typename T>
@@ -567,37 +567,52 @@ __global__ __launch_bounds__(256) void hash_refine_kernel(const T* __restrict__ 
         if (threadIdx.x == 0) counter[0] = part_sum[0] + part_sum[1] + part_sum[2] + part_sum[3];
     }
 
-    const int sub = lane >> 4, l16 = lane & 15, kper = D / 16;
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+    // 16 items per pass, 4 lanes each; lane l4 takes elements 16 j + 4 l4 + e,
+    // so the four lanes of an item read 64 contiguous bytes per load
+    const int sub = lane >> 2, l4 = lane & 3, ksteps = D / 16;
     const int64_t nwaves = (int64_t)gridDim.x * 4;
     for (int64_t region = (int64_t)blockIdx.x * 4 + wave; region < nregions; region += nwaves) {
-        const int n0 = rcount[2 * region], n1 = rcount[2 * region + 1];
         const RefineItem* rq = queue + region * region_size;
-        for (int q0 = 0; q0 < n0; q0 += 4) {
-            const int q = q0 + sub;
-            const bool ok = q < n0;
-            const RefineItem it = ok ? rq[q] : RefineItem{0, -1, -1, 0};
+        // the counts and the first items of both ends are loaded together (a
+        // region holds at least 64 entries, so the reads stay inside it; stale
+        // entries past the counts are never used)
+        const i32x2 cnt = *(const i32x2*)(rcount + 2 * region);
+        RefineItem nxt = rq[sub];
+        const int32_t back_item = rq[region_size - 1 - lane].item;
+        const int n0 = cnt.x, n1 = cnt.y;
+        for (int q0 = 0; q0 < n0; q0 += 16) {
+            const bool ok = q0 + sub < n0;
+            const RefineItem it = nxt;
+            if (q0 + 16 + sub < n0) nxt = rq[q0 + 16 + sub];   // next pass's item, in flight
             const bool va = it.a >= 0 && it.a < half, vb = it.b >= 0 && it.b < half && it.b != it.a;
             double pa = 0.0, pb = 0.0;
             if (ok) {
                 const int i = it.item % dm.L, rest = it.item / dm.L;
                 const int r = rest % dm.nh, bh = rest / dm.nh;
-                const T* x = qk + ((int64_t)bh * dm.L + i) * D + l16 * kper;
+                const T* x = qk + ((int64_t)bh * dm.L + i) * D + 4 * l4;
                 const float* Rr = rt + (int64_t)r * hpad * D;      // [column][k]
-                const float* ra = Rr + (int64_t)(va ? it.a : 0) * D + l16 * kper;
-                const float* rb = Rr + (int64_t)(vb ? it.b : 0) * D + l16 * kper;
+                const float* ra = Rr + (int64_t)(va ? it.a : 0) * D + 4 * l4;
+                const float* rb = Rr + (int64_t)(vb ? it.b : 0) * D + 4 * l4;
 #pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    if (k < kper) {
-                        const double xv = (double)IO<T>::load(x, k);
-                        pa += xv * (double)ra[k];
-                        pb += xv * (double)rb[k];
+                for (int j = 0; j < 8; ++j)
+                    if (j < ksteps) {
+                        const f32x4 A = *(const f32x4*)(ra + 16 * j);
+                        const f32x4 B = *(const f32x4*)(rb + 16 * j);
+                        const f32x4 X = IO<T>::load4(x, 16 * j);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            pa += (double)X[e] * (double)A[e];
+                            pb += (double)X[e] * (double)B[e];
+                        }
                     }
             }
-            for (int off = 8; off > 0; off >>= 1) {
+            for (int off = 2; off > 0; off >>= 1) {
                 pa += __shfl_xor(pa, off);
                 pb += __shfl_xor(pb, off);
             }
-            if (ok && l16 == 0) {
+            if (ok && l4 == 0) {
                 const int ca = it.a + (pa < 0.0 ? half : 0), cb = it.b + (pb < 0.0 ? half : 0);
                 int pick;
                 if (!vb) pick = ca;
@@ -609,7 +624,7 @@ __global__ __launch_bounds__(256) void hash_refine_kernel(const T* __restrict__ 
             }
         }
         for (int q = lane; q < n1; q += kWave) {
-            const int32_t item = rq[region_size - 1 - q].item;
+            const int32_t item = q < kWave ? back_item : rq[region_size - 1 - q].item;
             const int r = (item / dm.L) % dm.nh;
             const int slot = atomicAdd(&scount[r], 1);
             slist[(int64_t)r * cap + slot] = item;
@@ -646,8 +661,11 @@ __global__ __launch_bounds__(256) void hash_scan_kernel(const T* __restrict__ qk
     const int64_t first = (int64_t)blockIdx.z * G;
     if (first >= n) return;
     const float* Rt = rt + ((int64_t)r * hpad + (int64_t)t * kHashColTile) * D;
-#pragma unroll 8
-    for (int i = threadIdx.x; i < kHashColTile * D; i += 256) rtile[i / D][i % D] = Rt[i];
+#pragma unroll 4
+    for (int i = threadIdx.x; i < kHashColTile * D / 4; i += 256) {
+        const int c = i / (D / 4), k = 4 * (i % (D / 4));
+        *(f32x4*)&rtile[c][k] = *(const f32x4*)(Rt + (int64_t)c * D + k);
+    }
     const int it = threadIdx.x >> 2, cq = threadIdx.x & 3;   // item, column quarter
     for (int64_t g0 = first; g0 < n; g0 += (int64_t)gridDim.z * G) {
         const int gn = (int)min((int64_t)G, n - g0);
@@ -663,10 +681,10 @@ __global__ __launch_bounds__(256) void hash_scan_kernel(const T* __restrict__ qk
         }
         __syncthreads();
 #pragma unroll 8
-        for (int i = threadIdx.x; i < G * D; i += 256) {
-            const int j = i / D, k = i % D;
+        for (int i = threadIdx.x; i < G * D / 4; i += 256) {
+            const int j = i / (D / 4), k = 4 * (i % (D / 4));
             const int64_t off = xrow[j];
-            xs[j][k] = off >= 0 ? IO<T>::load(qk, off + k) : 0.f;
+            *(f32x4*)&xs[j][k] = off >= 0 ? IO<T>::load4(qk, off + k) : (f32x4){0.f, 0.f, 0.f, 0.f};
         }
         __syncthreads();
         if (it >= gn) continue;
@@ -750,6 +768,7 @@ hipError_t launch_hash(const void* qk, const float* R, const Dims& d, int32_t* b
         constexpr int TOKF = LSH_HASH_TOKF;
         constexpr int per_wave = 32 * TOKF, per_wg = 4 * per_wave;
         static_assert(per_wg <= kQueuePad, "queue regions must fit the padded capacity");
+        static_assert(per_wave >= kWave, "the re-decision pass reads 64 entries of a region ahead");
         const unsigned grid = (unsigned)((d.T + per_wg - 1) / per_wg);
         const uint16_t* x = (const uint16_t*)qk;
         if (d.d == 64)

@@ -173,15 +173,27 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 template <typename T>
 struct IO;
+typedef float io_f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t io_u32x2 __attribute__((ext_vector_type(2)));
 template <>
 struct IO<float> {
     __device__ __forceinline__ static float load(const float* p, int64_t i) { return p[i]; }
+    // four consecutive elements; p + i must be 16-byte aligned
+    __device__ __forceinline__ static io_f32x4 load4(const float* p, int64_t i) {
+        return *(const io_f32x4*)(p + i);
+    }
     __device__ __forceinline__ static void store(float* p, int64_t i, float v) { p[i] = v; }
 };
 template <>
 struct IO<uint16_t> {
     __device__ __forceinline__ static float load(const uint16_t* p, int64_t i) {
         return bf16_to_f32(p[i]);
+    }
+    // four consecutive elements; p + i must be 8-byte aligned
+    __device__ __forceinline__ static io_f32x4 load4(const uint16_t* p, int64_t i) {
+        const io_u32x2 w = *(const io_u32x2*)(p + i);
+        return (io_f32x4){__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                          __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
     }
     __device__ __forceinline__ static void store(uint16_t* p, int64_t i, float v) {
         p[i] = f32_to_bf16(v);

@@ -96,6 +96,15 @@ def test_entry_points_reject_on_host(lib):
     assert lib.lsh_attention_fwd(fake, fake, fake, ctypes.byref(s), fake, fake, 16, None) == -2
     assert b"workspace" in lib.lsh_last_error()
     assert lib.lsh_attention_fwd(None, None, None, None, None, None, 0, None) == -1
+    # pointers must be 16-byte aligned; the check runs before anything is enqueued
+    odd = vp(0x1008)
+    assert lib.lsh_hash(odd, fake, ctypes.byref(s), fake, fake, 1 << 40, None) == -1
+    assert b"aligned" in lib.lsh_last_error()
+    assert lib.lsh_sort(fake, ctypes.byref(s), fake, odd, fake, 1 << 40, None) == -1
+    assert lib.lsh_chunk_attend(fake, odd, fake, fake, ctypes.byref(s), fake, fake, None) == -1
+    assert lib.lsh_unsort_combine(fake, fake, fake, ctypes.byref(s), odd, None) == -1
+    assert lib.lsh_attention_fwd(fake, fake, fake, ctypes.byref(s), fake, odd, 1 << 40, None) == -1
+    assert b"aligned" in lib.lsh_last_error()
 
 
 def test_empty_problems_enqueue_nothing(lib):
