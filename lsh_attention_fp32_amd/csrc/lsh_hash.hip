@@ -288,21 +288,49 @@ __global__ __launch_bounds__(256) void hash_mfma_kernel(const uint16_t* __restri
     const float qerr = __uint_as_float((uint32_t)(127 + bits - 22) << 23) + 9.5367431640625e-7f;
 
     // B operand: lane holds x_s[tok0 + f*32 + lane%32][16 s + 8 (lane/32) + e]
-    // in fp16, x_s = x * 2^e with the token's largest |x| brought into [2^14, 2^15)
+    // in fp16, x_s = x * 2^e with the token's largest |x| brought into [2^14, 2^15).
+    // The raw rows and (when asked) this workgroup's value rows are all
+    // requested before any of them is used, so their latencies overlap.
+    u32x4 ux[TOKF][KS];
+#pragma unroll
+    for (int f = 0; f < TOKF; ++f) {
+        const int64_t tok = tok0 + f * 32 + (lane & 31);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            ux[f][s] = (u32x4){0u, 0u, 0u, 0u};
+            if (tok < dm.T) ux[f][s] = ((const u32x4*)(qk + tok * D))[2 * s + (lane >> 5)];
+        }
+    }
+    __shared__ uint32_t wvmax[4];
+    if (v) {
+        // this workgroup's tokens are one contiguous run of value rows
+        constexpr int NV = TOK_WG * (D / 8) / 256;   // 16-byte pieces per thread
+        const int64_t first = (int64_t)blockIdx.x * TOK_WG;
+        const int64_t nvec = min((int64_t)TOK_WG, dm.T - first) * (D / 8);
+        const u32x4* src = (const u32x4*)(v + first * D);
+        u32x4 vw[NV];
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int64_t i = threadIdx.x + 256 * j;
+            vw[j] = i < nvec ? src[i] : (u32x4){0u, 0u, 0u, 0u};
+        }
+        uint32_t m = 0;
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m = max(m, max(vw[j][e] & 0x7FFFu, (vw[j][e] >> 16) & 0x7FFFu));
+        for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+        if (lane == 0) wvmax[wave] = m;
+    }
     f16x8 xb[TOKF][KS];
     float xn2[TOKF];
 #pragma unroll
     for (int f = 0; f < TOKF; ++f) {
-        const int64_t tok = tok0 + f * 32 + (lane & 31);
-        u32x4 u[KS];
         uint32_t mb = 0;   // largest |x| as bf16 bits (integer order = float order)
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            u[s] = (u32x4){0u, 0u, 0u, 0u};
-            if (tok < dm.T) u[s] = ((const u32x4*)(qk + tok * D))[2 * s + (lane >> 5)];
+        for (int s = 0; s < KS; ++s)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) mb = max(mb, max(u[s][e] & 0x7FFFu, (u[s][e] >> 16) & 0x7FFFu));
-        }
+            for (int e = 0; e < 4; ++e) mb = max(mb, max(ux[f][s][e] & 0x7FFFu, (ux[f][s][e] >> 16) & 0x7FFFu));
         mb = max(mb, (uint32_t)__shfl_xor((int)mb, 32));
         const int xe = 15 - __builtin_amdgcn_frexp_expf(__uint_as_float(mb << 16));
         xn2[f] = 0.f;
@@ -311,8 +339,8 @@ __global__ __launch_bounds__(256) void hash_mfma_kernel(const uint16_t* __restri
             u32x4 h;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float a = ldexpf(__uint_as_float(u[s][e] << 16), xe);
-                const float b = ldexpf(__uint_as_float(u[s][e] & 0xFFFF0000u), xe);
+                const float a = ldexpf(__uint_as_float(ux[f][s][e] << 16), xe);
+                const float b = ldexpf(__uint_as_float(ux[f][s][e] & 0xFFFF0000u), xe);
                 xn2[f] = fmaf(a, a, fmaf(b, b, xn2[f]));
                 h[e] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
                        ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
@@ -332,21 +360,6 @@ __global__ __launch_bounds__(256) void hash_mfma_kernel(const uint16_t* __restri
         item0[f] = tok_live[f] ? (int32_t)(bh * dm.nh * dm.L + i) : 0;
     }
 
-    __shared__ uint32_t wvmax[4];
-    if (v) {
-        // this workgroup's tokens are one contiguous run of value rows
-        const int64_t first = (int64_t)blockIdx.x * TOK_WG;
-        const int64_t nvec = min((int64_t)TOK_WG, dm.T - first) * (D / 8);
-        const u32x4* src = (const u32x4*)(v + first * D);
-        uint32_t m = 0;
-        for (int64_t i = threadIdx.x; i < nvec; i += 256) {
-            const u32x4 w = src[i];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) m = max(m, max(w[e] & 0x7FFFu, (w[e] >> 16) & 0x7FFFu));
-        }
-        for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-        if (lane == 0) wvmax[wave] = m;
-    }
     for (int i = threadIdx.x; i < TILE_U4; i += 256) lds[0][i] = rfrag[i];
     __syncthreads();
     if (v && threadIdx.x == 0)
