@@ -25,38 +25,37 @@ sys.path.insert(0, ROOT)
 
 METRIC = "LSH-attention fwd tokens/s at L=64K, 8 heads, 8 hashes; % of MFMA/HBM roofline"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
-PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+PEAK_F16_TFLOPS = 2500.0       # MI355X dense fp16 / bf16 MFMA, TFLOP/s
 PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 (vector / matrix), TFLOP/s
 
 
 def algorithmic_work(w):
     """Per-launch algorithmic flops or HBM bytes of each kernel, by kernel name.
 
-    Returns {name: (bound, amount, unit)} with bound 'mfma' (amount in flops) or
-    'hbm' (amount in bytes)."""
+    Returns {name: (bound, amount, unit)} with bound 'mfma' (amount in flops),
+    'alu' (flops) or 'hbm' (amount in bytes)."""
     e = 2 if w.dtype == "bf16" else 4
     T = w.B * w.H * w.L                      # token-heads
     TR = T * w.n_hashes                      # token-rounds
     d, half = w.d, w.n_buckets // 2
     hash_flops = 2.0 * d * half * w.n_hashes * T
     return {
-        # projection x R for every round: one fp32-exact contraction, evaluated
-        # on bf16 matrix cores (two passes of the split R; counted once)
+        # projection x R for every round, one fp16 matrix-core pass (fp32
+        # accumulation); R prep and re-decision are separate entries
         "hash_fast_mfma": ("mfma", hash_flops, "flop"),
         "hash_fast_fp32": ("alu", hash_flops, "flop"),
-        # read buckets twice (count, scatter), write perm and inv
+        # read the buckets (count); read them again and write one packed key
+        # per slot (scatter, fused forward)
         "sort_count": ("hbm", 4.0 * TR, "B"),
-        "sort_scatter": ("hbm", 12.0 * TR, "B"),
-        # gather qk and v rows once per token-round, read perm and the bucket,
-        # write the round's output row and lse (fp16 rows on the bf16
+        "sort_scatter": ("hbm", 8.0 * TR, "B"),
+        # gather qk and v rows once per token-round, read the packed sorted
+        # key, write the round's output row and lse (fp16 rows on the bf16
         # matrix-core path, fp32 otherwise)
         "attend_fp32": ("hbm", TR * (2 * d * e + 8 + 4 * d + 4), "B"),
-        "attend_mfma": ("hbm", TR * (2 * d * e + 8 + 2 * d + 4), "B"),
+        "attend_mfma": ("hbm", TR * (2 * d * e + 4 + 2 * d + 4), "B"),
         # read every round's output row and lse of a token; write out
         "combine": ("hbm", T * (w.n_hashes * ((2 if w.dtype == "bf16" else 4) * d + 4) + d * e),
                     "B"),
-        # read v once
-        "vmax": ("hbm", T * d * e, "B"),
     }
 
 
@@ -177,7 +176,7 @@ def main() -> int:
         roof = {"bound": "hbm", "achieved": amount / secs / 1e9, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
     elif bound == "mfma":
-        roof = {"bound": "mfma", "achieved": amount / secs / 1e12, "peak": PEAK_BF16_TFLOPS,
+        roof = {"bound": "mfma", "achieved": amount / secs / 1e12, "peak": PEAK_F16_TFLOPS,
                 "unit": "TFLOP/s"}
     else:
         roof = {"bound": "alu", "achieved": amount / secs / 1e12, "peak": PEAK_FP32_TFLOPS,

@@ -60,6 +60,7 @@ static size_t rt_elems(const Dims& d) {
 size_t hash_workspace_bytes(const Dims& d) {
     size_t b = 256;                                              // counter
     b += align_up(sizeof(float) * 3 * d.nh, 256);                // rnorm, rnorm_s, resn_s
+    b += align_up(sizeof(float) * d.nh * hash_ntiles(d), 256);   // tmax
     b += align_up(sizeof(uint16_t) * rfrag_elems(d), 256);       // rfrag
     b += align_up(sizeof(float) * rt_elems(d), 256);             // rt
     b += align_up(sizeof(RefineItem) * (size_t)queue_tokens(d) * d.nh, 256);   // queue
@@ -80,6 +81,8 @@ HashWorkspace carve_hash_workspace(void* ws, const Dims& d) {
     w.rnorm_s = w.rnorm + d.nh;
     w.resn_s = w.rnorm + 2 * d.nh;
     p += align_up(sizeof(float) * 3 * d.nh, 256);
+    w.tmax = (float*)p;
+    p += align_up(sizeof(float) * d.nh * hash_ntiles(d), 256);
     w.rfrag = (uint16_t*)p;
     p += align_up(sizeof(uint16_t) * rfrag_elems(d), 256);
     w.rt = (float*)p;
@@ -97,15 +100,40 @@ HashWorkspace carve_hash_workspace(void* ws, const Dims& d) {
 }
 
 // ------------------------------------------------------------------ R prep
-__global__ void zero_counter_kernel(int32_t* counter, float* rnorm, int32_t* scount, int nh) {
-    if (threadIdx.x < 4) counter[threadIdx.x] = 0;   // re-decided count and max|v|
-    for (int r = threadIdx.x; r < 3 * nh; r += blockDim.x) rnorm[r] = 0.f;
-    for (int r = threadIdx.x; r < nh; r += blockDim.x) scount[r] = 0;
+// One workgroup per (32-column tile, round): max |R| over the tile, written to
+// tmax[round * ntiles + tile] (no atomics, so nothing to clear first).
+// Workgroup (0, 0) also clears the re-decision count, max|v| and the per-round
+// norms and list counts that later passes fold into.
+__global__ __launch_bounds__(256) void rmax_kernel(const float* __restrict__ R, int d, int half,
+                                                   int ntiles, float* __restrict__ tmax,
+                                                   int32_t* __restrict__ counter,
+                                                   float* __restrict__ rnorm,
+                                                   int32_t* __restrict__ scount) {
+    __shared__ float wmax[4];
+    const int t = blockIdx.x, r = blockIdx.y, nh = gridDim.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (t == 0 && r == 0) {
+        if (threadIdx.x < 4) counter[threadIdx.x] = 0;
+        for (int i = threadIdx.x; i < 3 * nh; i += 256) rnorm[i] = 0.f;
+        for (int i = threadIdx.x; i < nh; i += 256) scount[i] = 0;
+    }
+    const float* Rr = R + (int64_t)r * d * half;
+    const int col0 = t * kHashColTile;
+    float m = 0.f;
+#pragma unroll 8
+    for (int idx = threadIdx.x; idx < d * kHashColTile; idx += 256) {
+        const int k = idx / kHashColTile, c = idx % kHashColTile;
+        if (col0 + c < half) m = fmaxf(m, fabsf(Rr[(int64_t)k * half + col0 + c]));
+    }
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if (lane == 0) wmax[wave] = m;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        tmax[(int64_t)r * ntiles + t] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
 }
 
 // One workgroup per (round, 32-column tile) of R, staged through LDS:
-//  * e_r from max|R| of the round (every workgroup of the round reads the
-//    whole round and finds the same value);
+//  * e_r from max|R| of the round (the per-tile maxima of rmax_kernel);
 //  * rnorm / rnorm_s / resn_s: column norms (sums of squares in fp32, then
 //    rounded up), folded by an atomic max on the bits of non-negative floats,
 //    which is order independent;
@@ -116,38 +144,24 @@ __global__ void zero_counter_kernel(int32_t* counter, float* rnorm, int32_t* sco
 //            values, lane l holding column tile*32 + l%32 and
 //            k = kstep*16 + 8*(l/32) + e.
 __global__ __launch_bounds__(256) void rprep_kernel(const float* __restrict__ R, int d, int half,
-                                                    int ntiles, float* __restrict__ rnorm,
+                                                    int ntiles, const float* __restrict__ tmax,
+                                                    float* __restrict__ rnorm,
                                                     float* __restrict__ rt,
                                                     uint16_t* __restrict__ rfrag) {
-    typedef float f32x4 __attribute__((ext_vector_type(4)));
     __shared__ float tile[128][kHashColTile + 1];
-    __shared__ float wmax[4];
     const int t = blockIdx.x, r = blockIdx.y, nh = gridDim.y;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const float* Rr = R + (int64_t)r * d * half;
-    const int n = d * half;   // a multiple of 64
-    float m = 0.f;
-    if ((reinterpret_cast<uintptr_t>(Rr) & 15) == 0) {
-        const f32x4* R4 = (const f32x4*)Rr;
-#pragma unroll 8
-        for (int i = threadIdx.x; i < n / 4; i += 256) {
-            const f32x4 q = R4[i];
-            m = fmaxf(m, fmaxf(fmaxf(fabsf(q.x), fabsf(q.y)), fmaxf(fabsf(q.z), fabsf(q.w))));
-        }
-    } else {
-#pragma unroll 8
-        for (int i = threadIdx.x; i < n; i += 256) m = fmaxf(m, fabsf(Rr[i]));
-    }
-    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    if (lane == 0) wmax[wave] = m;
     const int col0 = t * kHashColTile;
 #pragma unroll 8
     for (int idx = threadIdx.x; idx < d * kHashColTile; idx += 256) {
         const int k = idx / kHashColTile, c = idx % kHashColTile;
         tile[k][c] = (col0 + c < half) ? Rr[(int64_t)k * half + col0 + c] : 0.f;
     }
+    // max |R| of the round from the per-tile maxima (every workgroup of the
+    // round reads the same values, so all agree on the scale)
+    float M = 0.f;
+    for (int i = 0; i < ntiles; ++i) M = fmaxf(M, tmax[(int64_t)r * ntiles + i]);
     __syncthreads();
-    const float M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
     const int e = 15 - __builtin_amdgcn_frexp_expf(M);   // M * 2^e in [2^14, 2^15)
 
     {   // 8 threads per column, d/8 rows each
@@ -166,13 +180,31 @@ __global__ __launch_bounds__(256) void rprep_kernel(const float* __restrict__ R,
             s1 += __shfl_xor(s1, off);
             s2 += __shfl_xor(s2, off);
         }
-        if (part == 0 && col0 + c < half) {
-            // fp32 sums of d squares: relative error below d * 2^-24; sqrt halves it
-            const float up = 1.0f + (float)(d + 4) * kTwoM24;
-            const float flush = sqrtf((float)d) * 1.0001f * 6.103515625e-05f;   // sqrt(d) 2^-14
-            atomicMax((int*)&rnorm[r], __float_as_int(sqrtf(s0) * up));
-            atomicMax((int*)&rnorm[nh + r], __float_as_int(sqrtf(s1) * up));
-            atomicMax((int*)&rnorm[2 * nh + r], __float_as_int(sqrtf(s2) * up + flush));
+        // fp32 sums of d squares: relative error below d * 2^-24; sqrt halves it
+        const float up = 1.0f + (float)(d + 4) * kTwoM24;
+        const float flush = sqrtf((float)d) * 1.0001f * 6.103515625e-05f;   // sqrt(d) 2^-14
+        const bool real = col0 + c < half;
+        float n0 = real ? sqrtf(s0) * up : 0.f;
+        float n1 = real ? sqrtf(s1) * up : 0.f;
+        float n2 = real ? sqrtf(s2) * up + flush : 0.f;
+        // the tile's largest, then one atomic max per workgroup and bound
+        for (int off = 8; off < 64; off <<= 1) {
+            n0 = fmaxf(n0, __shfl_xor(n0, off));
+            n1 = fmaxf(n1, __shfl_xor(n1, off));
+            n2 = fmaxf(n2, __shfl_xor(n2, off));
+        }
+        __shared__ float wn[3][4];
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        if (lane == 0) {
+            wn[0][wave] = n0;
+            wn[1][wave] = n1;
+            wn[2][wave] = n2;
+        }
+        __syncthreads();
+        if (threadIdx.x < 3) {
+            const float v = fmaxf(fmaxf(wn[threadIdx.x][0], wn[threadIdx.x][1]),
+                                  fmaxf(wn[threadIdx.x][2], wn[threadIdx.x][3]));
+            atomicMax((int*)&rnorm[threadIdx.x * nh + r], __float_as_int(v));
         }
     }
     float* dst = rt + ((int64_t)r * ntiles * kHashColTile + col0) * d;
@@ -770,9 +802,9 @@ hipError_t launch_hash(const void* qk, const float* R, const Dims& d, int32_t* b
     const int half = d.nb / 2;
     const int ntiles = hash_ntiles(d);
     hipError_t e;
-    zero_counter_kernel<<<1, 256, 0, st>>>(w.counter, w.rnorm, w.scount, d.nh);
-    rprep_kernel<<<dim3((unsigned)ntiles, (unsigned)d.nh), 256, 0, st>>>(R, d.d, half, ntiles,
-                                                                         w.rnorm, w.rt, w.rfrag);
+    const dim3 pgrid((unsigned)ntiles, (unsigned)d.nh);
+    rmax_kernel<<<pgrid, 256, 0, st>>>(R, d.d, half, ntiles, w.tmax, w.counter, w.rnorm, w.scount);
+    rprep_kernel<<<pgrid, 256, 0, st>>>(R, d.d, half, ntiles, w.tmax, w.rnorm, w.rt, w.rfrag);
     if ((e = mark(st, ev, nev, names, "hash_prep")) != hipSuccess) return e;
     if (d.dtype == LSH_BF16) {
 #ifndef LSH_HASH_TOKF

@@ -71,6 +71,7 @@ struct HashWorkspace {
     float* rnorm;
     float* rnorm_s;
     float* resn_s;
+    float* tmax;          // [nh][ntiles] max |R| per column tile
     uint16_t* rfrag;      // fp16(R_s) in matrix-core fragment order
     float* rt;            // R transposed to [nh][ntiles*32][d], fp32
     RefineItem* queue;    // [queue_tokens * nh]

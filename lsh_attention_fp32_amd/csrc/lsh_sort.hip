@@ -6,14 +6,14 @@
 // summary, section "・LSH Attention" (sort per bucket before chunking).
 //
 // Positions arrive in increasing order, so a stable counting sort on the
-// bucket alone yields the (bucket, position) order. Three kernels:
+// bucket alone yields the (bucket, position) order. Two kernels:
 //   count   per 4096-element tile: bucket histogram in LDS
-//   scan    per segment: exclusive scan of the histograms in (bucket, tile)
-//           order -> the first slot of every (tile, bucket) run
-//   scatter per tile: each wave walks its 1024 elements in order; lanes with
-//           equal buckets are grouped by a ballot match, so ranks are exact
-//           and the LDS counter of a hot bucket is bumped once per wave step
-//           (skewed buckets do not serialise on LDS atomics).
+//   scatter per tile: first the slot where each of its (tile, bucket) runs
+//           starts -- the segment's bucket totals, scanned, plus the counts
+//           of the earlier tiles -- then each wave walks its 1024 elements in
+//           order; lanes with equal buckets are grouped by a ballot match, so
+//           ranks are exact and the LDS counter of a hot bucket is bumped once
+//           per wave step (skewed buckets do not serialise on LDS atomics).
 #include "lsh_internal.h"
 
 namespace lsh {
@@ -68,49 +68,6 @@ __global__ __launch_bounds__(256) void sort_count_kernel(const int32_t* __restri
         counts[(seg * ntiles + tile) * dm.nb + b] = hist[b];
 }
 
-// One block per segment: turns the [tile][bucket] counts into the first slot of
-// every (tile, bucket) run, in (bucket, tile) order: a bucket's runs follow
-// each other tile by tile, and buckets follow each other in increasing order.
-// Thread b owns buckets b, b+1024, ...: a column sum, a block-wide exclusive
-// scan of the bucket totals, then a running sum down the column (all reads
-// and writes are coalesced across threads).
-__global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t* __restrict__ counts, int nb,
-                                                         int ntiles) {
-    constexpr int BPT = kMaxBuckets / 1024;   // buckets per thread
-    __shared__ int32_t wsum[16];
-    int32_t* c = counts + (int64_t)blockIdx.x * ntiles * nb;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int32_t tot[BPT];
-    int32_t mine = 0;
-#pragma unroll
-    for (int j = 0; j < BPT; ++j) {
-        const int b = threadIdx.x * BPT + j;
-        tot[j] = 0;
-        if (b < nb)
-            for (int t = 0; t < ntiles; ++t) tot[j] += c[(int64_t)t * nb + b];
-        mine += tot[j];
-    }
-    int32_t incl = mine;
-    for (int off = 1; off < 64; off <<= 1) {
-        const int32_t o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-    }
-    if (lane == 63) wsum[wave] = incl;
-    __syncthreads();
-    int32_t run = incl - mine;
-    for (int w = 0; w < wave; ++w) run += wsum[w];
-#pragma unroll
-    for (int j = 0; j < BPT; ++j) {
-        const int b = threadIdx.x * BPT + j;
-        if (b < nb)
-            for (int t = 0; t < ntiles; ++t) {
-                const int32_t cnt = c[(int64_t)t * nb + b];
-                c[(int64_t)t * nb + b] = run;
-                run += cnt;
-            }
-    }
-}
-
 // PACKED: perm[slot] = (bucket << kPackPosBits) | position and no inverse.
 template <bool PACKED>
 __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __restrict__ buckets,
@@ -118,12 +75,55 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __rest
                                                            Dims dm, int ntiles, int nbits,
                                                            int32_t* __restrict__ perm,
                                                            int32_t* __restrict__ inv) {
-    extern __shared__ int32_t sh[];   // [kSortWaves][nb]: counts, then running slots
+    extern __shared__ int32_t sh[];   // [kSortWaves][nb] counts, then running slots; [nb] run starts
+    __shared__ int32_t wsum[4];
     constexpr int SUB = kSortTile / kSortWaves;
     const int tile = blockIdx.x;
     const int64_t seg = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nb = dm.nb;
+    int32_t* start = sh + kSortWaves * nb;
+
+    // First slot of this tile's run of every bucket: exclusive scan over
+    // buckets of the segment totals, plus the counts of the earlier tiles.
+    // Totals (start[]) and earlier-tile counts (sh[0..nb)) are gathered with
+    // coalesced reads, then scanned in contiguous chunks of bpt buckets.
+    {
+        const int32_t* cnt = offs + seg * ntiles * nb;
+        for (int b = threadIdx.x; b < nb; b += 256) {
+            int32_t tot = 0, before = 0;
+#pragma unroll 16
+            for (int t = 0; t < ntiles; ++t) {
+                const int32_t c = cnt[(int64_t)t * nb + b];
+                tot += c;
+                before += t < tile ? c : 0;
+            }
+            start[b] = tot;
+            sh[b] = before;
+        }
+        __syncthreads();
+        const int bpt = (nb + 255) / 256;
+        const int b0 = threadIdx.x * bpt;
+        int32_t mine = 0;
+        for (int j = 0; j < bpt; ++j)
+            if (b0 + j < nb) mine += start[b0 + j];
+        int32_t incl = mine;
+        for (int off = 1; off < 64; off <<= 1) {
+            const int32_t o = __shfl_up(incl, off);
+            if (lane >= off) incl += o;
+        }
+        if (lane == 63) wsum[wave] = incl;
+        __syncthreads();
+        int32_t run = incl - mine;
+        for (int w = 0; w < wave; ++w) run += wsum[w];
+        for (int j = 0; j < bpt; ++j)
+            if (b0 + j < nb) {
+                const int32_t tot = start[b0 + j];
+                start[b0 + j] = run + sh[b0 + j];
+                run += tot;
+            }
+    }
+    __syncthreads();
     for (int k = threadIdx.x; k < kSortWaves * nb; k += 256) sh[k] = 0;
     __syncthreads();
     const int32_t* src = buckets + seg * dm.L;
@@ -141,11 +141,11 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __rest
     __syncthreads();
     // first slot of each (wave, bucket) run
     for (int b = threadIdx.x; b < nb; b += 256) {
-        int32_t run = offs[(seg * ntiles + tile) * nb + b];
+        int32_t run = start[b];
         for (int w = 0; w < kSortWaves; ++w) {
-            const int32_t cnt = sh[w * nb + b];
+            const int32_t c = sh[w * nb + b];
             sh[w * nb + b] = run;
-            run += cnt;
+            run += c;
         }
     }
     __syncthreads();
@@ -184,9 +184,7 @@ hipError_t launch_sort(const int32_t* buckets, const Dims& d, int32_t* perm, int
     hipError_t e;
     sort_count_kernel<<<grid, 256, sizeof(int32_t) * d.nb, st>>>(buckets, d, ntiles, nbits, counts);
     if ((e = mark(st, ev, nev, names, "sort_count")) != hipSuccess) return e;
-    sort_scan_kernel<<<(unsigned)d.segs, 1024, 0, st>>>(counts, d.nb, ntiles);
-    if ((e = mark(st, ev, nev, names, "sort_scan")) != hipSuccess) return e;
-    const size_t lds = sizeof(int32_t) * kSortWaves * d.nb;
+    const size_t lds = sizeof(int32_t) * (kSortWaves + 1) * d.nb;
     if (packed)
         sort_scatter_kernel<true><<<grid, 256, lds, st>>>(buckets, counts, d, ntiles, nbits, perm,
                                                           nullptr);
