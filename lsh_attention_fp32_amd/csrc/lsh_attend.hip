@@ -363,12 +363,32 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
         const int64_t orow_idx = HALF ? (bh * L + qpos) * dm.nh + (seg - bh * dm.nh) : slot;
         if constexpr (HALF) {
             const float inv = oscale / sumr;
-            _Float16* orow = (_Float16*)o_sorted + orow_idx * D;
+            // Lane (g, r16) holds features 16 dt + 4 g + i of its query. The
+            // four lanes of a query swap pieces so that lane g stores features
+            // 32 k + 8 g .. +7: each store then writes 64 contiguous bytes of
+            // the row (half as many memory requests as 8-byte pieces).
+            u32x2 hv[DT];
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 const f32x4 o = oacc[dt] * inv;
-                f16x4 h = {(_Float16)o.x, (_Float16)o.y, (_Float16)o.z, (_Float16)o.w};
-                *(f16x4*)(orow + dt * 16 + 4 * g) = h;
+                const f16x4 h = {(_Float16)o.x, (_Float16)o.y, (_Float16)o.z, (_Float16)o.w};
+                hv[dt] = __builtin_bit_cast(u32x2, h);
+            }
+            const int src_a = r16 + 32 * (g & 1);   // holds features 8 (g % 2) + 0..3
+            const bool upper = g >= 2;               // wants the odd feature tile of each pair
+            _Float16* orow = (_Float16*)o_sorted + orow_idx * D;
+#pragma unroll
+            for (int k = 0; k < DT / 2; ++k) {
+                uint32_t w[4];
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const uint32_t a = __shfl(hv[2 * k][h2], src_a + 16 * q);
+                        const uint32_t b = __shfl(hv[2 * k + 1][h2], src_a + 16 * q);
+                        w[2 * q + h2] = upper ? b : a;
+                    }
+                *(u32x4*)(orow + 32 * k + 8 * g) = (u32x4){w[0], w[1], w[2], w[3]};
             }
         } else {
             const float inv = 1.0f / sumr;
