@@ -401,10 +401,12 @@ __global__ __launch_bounds__(256) void hash_mfma_kernel(const uint16_t* __restri
 #pragma unroll
     for (int f = 0; f < TOKF; ++f) k1[f] = k2[f] = k3[f] = 0.f;
 
-    // Software pipeline: the MFMAs of tile g are issued before the epilogue of
-    // tile g-1, which reads the other accumulator set, so the wave's VALU work
-    // overlaps its own matrix-core work.
-    f32x16 accA[TOKF], accB[TOKF];
+    // One accumulator set: a step issues the MFMAs of tile g, parks the next
+    // tile in LDS and then runs the epilogue of tile g; with three waves per
+    // SIMD (164 VGPRs) the other waves' matrix-core and VALU work fill the
+    // wait. (A two-set software pipeline inside the wave measured no faster and
+    // holds occupancy at two.)
+    f32x16 accA[TOKF];
 
     auto mfma_tile = [&](int g, f32x16(&acc)[TOKF]) {
         const u32x4* cur = lds[g & 1];
@@ -474,10 +476,10 @@ __global__ __launch_bounds__(256) void hash_mfma_kernel(const uint16_t* __restri
         }
     };
 
-    // One pipeline step: start fetching tile g+2 from L2 into registers, MFMAs
-    // of tile g, epilogue of tile g-1, then park tile g+1 (fetched a step ago)
-    // in the LDS buffer tile g-1 used. Two register sets keep two tiles in
-    // flight, so L2 latency is hidden behind a whole step.
+    // One step: start fetching tile g+2 from L2 into registers, MFMAs of tile
+    // g, park tile g+1 (fetched a step ago) in the LDS buffer tile g-1 used,
+    // epilogue of tile g. Two register sets keep two tiles in flight, so L2
+    // latency is hidden behind a whole step.
     auto fetch = [&](int t, u32x4(&pre)[PRE]) {
         if (t < total) {
             const u32x4* src = rfrag + (int64_t)t * TILE_U4;
@@ -485,33 +487,26 @@ __global__ __launch_bounds__(256) void hash_mfma_kernel(const uint16_t* __restri
             for (int j = 0; j < PRE; ++j) pre[j] = src[threadIdx.x + j * 256];
         }
     };
-    auto step = [&](int g, f32x16(&acc_new)[TOKF], f32x16(&acc_old)[TOKF], u32x4(&pre_new)[PRE],
-                    u32x4(&pre_old)[PRE]) {
+    auto step = [&](int g, f32x16(&acc)[TOKF], u32x4(&pre_new)[PRE], u32x4(&pre_old)[PRE]) {
         fetch(g + 2, pre_new);
-        mfma_tile(g, acc_new);
-        if (g > 0) epilogue(g - 1, acc_old);
+        mfma_tile(g, acc);
         if (g + 1 < total) {
             u32x4* dst = lds[(g + 1) & 1];
 #pragma unroll
             for (int j = 0; j < PRE; ++j) dst[threadIdx.x + j * 256] = pre_old[j];
         }
+        epilogue(g, acc);
         __syncthreads();
     };
 
     u32x4 preA[PRE], preB[PRE];
     fetch(1, preA);
-    step(0, accA, accB, preB, preA);
-    int g = 1;
+    int g = 0;
     for (; g + 1 < total; g += 2) {
-        step(g, accB, accA, preA, preB);
-        step(g + 1, accA, accB, preB, preA);
+        step(g, accA, preB, preA);
+        step(g + 1, accA, preA, preB);
     }
-    if (g < total) {
-        step(g, accB, accA, preA, preB);
-        epilogue(g, accB);
-    } else {
-        epilogue(g - 1, accA);
-    }
+    if (g < total) step(g, accA, preB, preA);
     qw.finish(rcount, region, lane);
 }
 
