@@ -279,6 +279,83 @@ __device__ __forceinline__ int classify(float v1, float v2, float v3, float thr)
     return 1;                      // scan every column
 }
 
+// ------------------------------------------------------------------ re-decision, part 1
+// Run by each wave of a fast pass on its own queue region when its sweep is
+// done (it wrote the region itself, so no other wave is involved): the
+// two-candidate items are decided in fp64 from the fp32 transpose of R, 16 at
+// a time, 4 lanes per item (lane l4 takes elements 16 j + 4 l4 + e, so the
+// four lanes of an item read 64 contiguous bytes per load), the next items
+// fetched a pass ahead. Full-scan items are moved to their round's list for
+// the grouped scan (a per-round atomic ticket; such items are rare). The exact
+// rule: largest |p| = |x . R_b| over [p, -p], ties to the lowest index of the
+// concatenation (a p of either zero sign counts as "+").
+template <typename T>
+__device__ __forceinline__ void refine_region(const T* __restrict__ qk,
+                                              const float* __restrict__ rt, const Dims& dm,
+                                              const RefineItem* rq, int region_size, int n0,
+                                              int n1, int lane, int32_t* __restrict__ buckets,
+                                              int32_t* __restrict__ scount,
+                                              int32_t* __restrict__ slist,
+                                              uint64_t* __restrict__ sbest, int64_t cap) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const int half = dm.nb / 2;
+    const int hpad = ((half + kHashColTile - 1) / kHashColTile) * kHashColTile;
+    const int D = dm.d;
+    const int sub = lane >> 2, l4 = lane & 3, ksteps = D / 16;
+    // the region's entries were stored by this wave's lanes: make them visible
+    // to the other lanes before reading them back
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+    RefineItem nxt = sub < n0 ? rq[sub] : RefineItem{0, -1, -1, 0};
+    for (int q0 = 0; q0 < n0; q0 += 16) {
+        const bool ok = q0 + sub < n0;
+        const RefineItem it = nxt;
+        if (q0 + 16 + sub < n0) nxt = rq[q0 + 16 + sub];   // next pass's item, in flight
+        const bool va = it.a >= 0 && it.a < half, vb = it.b >= 0 && it.b < half && it.b != it.a;
+        double pa = 0.0, pb = 0.0;
+        if (ok) {
+            const int i = it.item % dm.L, rest = it.item / dm.L;
+            const int r = rest % dm.nh, bh = rest / dm.nh;
+            const T* x = qk + ((int64_t)bh * dm.L + i) * D + 4 * l4;
+            const float* Rr = rt + (int64_t)r * hpad * D;      // [column][k]
+            const float* ra = Rr + (int64_t)(va ? it.a : 0) * D + 4 * l4;
+            const float* rb = Rr + (int64_t)(vb ? it.b : 0) * D + 4 * l4;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (j < ksteps) {
+                    const f32x4 A = *(const f32x4*)(ra + 16 * j);
+                    const f32x4 B = *(const f32x4*)(rb + 16 * j);
+                    const f32x4 X = IO<T>::load4(x, 16 * j);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        pa += (double)X[e] * (double)A[e];
+                        pb += (double)X[e] * (double)B[e];
+                    }
+                }
+        }
+        for (int off = 2; off > 0; off >>= 1) {
+            pa += __shfl_xor(pa, off);
+            pb += __shfl_xor(pb, off);
+        }
+        if (ok && l4 == 0) {
+            const int ca = it.a + (pa < 0.0 ? half : 0), cb = it.b + (pb < 0.0 ? half : 0);
+            int pick;
+            if (!vb) pick = ca;
+            else if (!va) pick = cb;
+            else if (fabs(pa) > fabs(pb)) pick = ca;
+            else if (fabs(pb) > fabs(pa)) pick = cb;
+            else pick = min(ca, cb);
+            buckets[it.item] = pick;
+        }
+    }
+    for (int q = lane; q < n1; q += kWave) {
+        const int32_t item = rq[region_size - 1 - q].item;
+        const int r = (item / dm.L) % dm.nh;
+        const int slot = atomicAdd(&scount[r], 1);
+        slist[(int64_t)r * cap + slot] = item;
+        sbest[(int64_t)r * cap + slot] = 0ull;
+    }
+}
+
 // ------------------------------------------------------------------ fast pass (MFMA)
 // One workgroup = 4 waves; a wave owns 32*TOKF tokens (TOKF B-operand
 // fragments kept in registers for the whole kernel) and sweeps every column
@@ -289,14 +366,19 @@ __device__ __forceinline__ int classify(float v1, float v2, float v3, float thr)
 // of the fp16 per-round outputs of the fused forward comes for the price of a
 // read that overlaps the matrix-core work.
 template <int D, int TOKF>
-__global__ __launch_bounds__(256) void hash_mfma_kernel(const uint16_t* __restrict__ qk,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void hash_mfma_kernel(const uint16_t* __restrict__ qk,
                                                         const u32x4* __restrict__ rfrag,
                                                         const float* __restrict__ rnorm, Dims dm,
                                                         int32_t* __restrict__ buckets,
                                                         RefineItem* __restrict__ queue,
                                                         int32_t* __restrict__ rcount,
                                                         const uint16_t* __restrict__ v,
-                                                        uint32_t* __restrict__ vmax) {
+                                                        uint32_t* __restrict__ vmax,
+                                                        const float* __restrict__ rt,
+                                                        int32_t* __restrict__ scount,
+                                                        int32_t* __restrict__ slist,
+                                                        uint64_t* __restrict__ sbest,
+                                                        int64_t cap) {
     constexpr int KS = D / 16;
     constexpr int TILE_U4 = KS * kWave;         // 16-byte lane fragments per column tile
     constexpr int PRE = TILE_U4 / 256;          // fragments each thread stages
@@ -403,9 +485,9 @@ __global__ __launch_bounds__(256) void hash_mfma_kernel(const uint16_t* __restri
 
     // One accumulator set: a step issues the MFMAs of tile g, parks the next
     // tile in LDS and then runs the epilogue of tile g; with three waves per
-    // SIMD (164 VGPRs) the other waves' matrix-core and VALU work fill the
-    // wait. (A two-set software pipeline inside the wave measured no faster and
-    // holds occupancy at two.)
+    // SIMD (at most 168 VGPRs, asked for on the kernel) the other waves'
+    // matrix-core and VALU work fill the wait. (A two-set software pipeline
+    // inside the wave measured no faster and holds occupancy at two.)
     f32x16 accA[TOKF];
 
     auto mfma_tile = [&](int g, f32x16(&acc)[TOKF]) {
@@ -508,6 +590,8 @@ __global__ __launch_bounds__(256) void hash_mfma_kernel(const uint16_t* __restri
     }
     if (g < total) step(g, accA, preB, preA);
     qw.finish(rcount, region, lane);
+    refine_region(qk, rt, dm, qw.base, qw.size, qw.n0, qw.n1, lane, buckets, scount, slist, sbest,
+                  cap);
 }
 
 // ------------------------------------------------------------------ fast pass (fp32 FMA)
@@ -519,7 +603,12 @@ __global__ __launch_bounds__(256) void hash_valu_kernel(const T* __restrict__ qk
                                                         const float* __restrict__ rnorm, Dims dm,
                                                         int32_t* __restrict__ buckets,
                                                         RefineItem* __restrict__ queue,
-                                                        int32_t* __restrict__ rcount) {
+                                                        int32_t* __restrict__ rcount,
+                                                        const float* __restrict__ rt,
+                                                        int32_t* __restrict__ scount,
+                                                        int32_t* __restrict__ slist,
+                                                        uint64_t* __restrict__ sbest,
+                                                        int64_t cap) {
     constexpr float kCoef = (float)(2 * D + 8) * kTwoM24;
     const int lane = threadIdx.x & 63;
     const int r = blockIdx.y;
@@ -568,112 +657,12 @@ __global__ __launch_bounds__(256) void hash_valu_kernel(const T* __restrict__ qk
     RefineItem it{(int32_t)item, i1, i2, mode};
     qw.push(live && mode >= 0, it, lane);
     qw.finish(rcount, region, lane);
+    refine_region(qk, rt, dm, qw.base, qw.size, qw.n0, qw.n1, lane, buckets, scount, slist, sbest,
+                  cap);
 }
 
-// ------------------------------------------------------------------ re-decision in fp64
-// The exact rule: largest |p| = |x . R_b| over [p, -p], ties to the lowest
-// index of the concatenation (a p of either zero sign counts as "+").
-//
-// Pass 1 (one wave per queue region, no barriers): two-candidate items are
-// decided here, 16 at a time, 4 lanes per item (each lane a quarter of the
-// row for both columns), the next items' records fetched a pass ahead. Full-scan items are moved to their round's list
-// for pass 2 (a per-round atomic ticket; such items are rare). Workgroup 0
-// also sums the region counts into the public count.
-template <typename T>
-__global__ __launch_bounds__(256) void hash_refine_kernel(const T* __restrict__ qk,
-                                                          const float* __restrict__ rt, Dims dm,
-                                                          int32_t* __restrict__ counter,
-                                                          const RefineItem* __restrict__ queue,
-                                                          const int32_t* __restrict__ rcount,
-                                                          int64_t nregions, int region_size,
-                                                          int32_t* __restrict__ buckets,
-                                                          int32_t* __restrict__ scount,
-                                                          int32_t* __restrict__ slist,
-                                                          uint64_t* __restrict__ sbest,
-                                                          int64_t cap) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int half = dm.nb / 2;
-    const int hpad = ((half + kHashColTile - 1) / kHashColTile) * kHashColTile;
-    const int D = dm.d;
-
-    if (blockIdx.x == 0) {
-        __shared__ int32_t part_sum[4];
-        int32_t c = 0;
-#pragma unroll 16
-        for (int64_t i = threadIdx.x; i < 2 * nregions; i += 256) c += rcount[i];
-        for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
-        if (lane == 0) part_sum[wave] = c;
-        __syncthreads();
-        if (threadIdx.x == 0) counter[0] = part_sum[0] + part_sum[1] + part_sum[2] + part_sum[3];
-    }
-
-    typedef float f32x4 __attribute__((ext_vector_type(4)));
-    typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
-    // 16 items per pass, 4 lanes each; lane l4 takes elements 16 j + 4 l4 + e,
-    // so the four lanes of an item read 64 contiguous bytes per load
-    const int sub = lane >> 2, l4 = lane & 3, ksteps = D / 16;
-    const int64_t nwaves = (int64_t)gridDim.x * 4;
-    for (int64_t region = (int64_t)blockIdx.x * 4 + wave; region < nregions; region += nwaves) {
-        const RefineItem* rq = queue + region * region_size;
-        // the counts and the first items of both ends are loaded together (a
-        // region holds at least 64 entries, so the reads stay inside it; stale
-        // entries past the counts are never used)
-        const i32x2 cnt = *(const i32x2*)(rcount + 2 * region);
-        RefineItem nxt = rq[sub];
-        const int32_t back_item = rq[region_size - 1 - lane].item;
-        const int n0 = cnt.x, n1 = cnt.y;
-        for (int q0 = 0; q0 < n0; q0 += 16) {
-            const bool ok = q0 + sub < n0;
-            const RefineItem it = nxt;
-            if (q0 + 16 + sub < n0) nxt = rq[q0 + 16 + sub];   // next pass's item, in flight
-            const bool va = it.a >= 0 && it.a < half, vb = it.b >= 0 && it.b < half && it.b != it.a;
-            double pa = 0.0, pb = 0.0;
-            if (ok) {
-                const int i = it.item % dm.L, rest = it.item / dm.L;
-                const int r = rest % dm.nh, bh = rest / dm.nh;
-                const T* x = qk + ((int64_t)bh * dm.L + i) * D + 4 * l4;
-                const float* Rr = rt + (int64_t)r * hpad * D;      // [column][k]
-                const float* ra = Rr + (int64_t)(va ? it.a : 0) * D + 4 * l4;
-                const float* rb = Rr + (int64_t)(vb ? it.b : 0) * D + 4 * l4;
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    if (j < ksteps) {
-                        const f32x4 A = *(const f32x4*)(ra + 16 * j);
-                        const f32x4 B = *(const f32x4*)(rb + 16 * j);
-                        const f32x4 X = IO<T>::load4(x, 16 * j);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            pa += (double)X[e] * (double)A[e];
-                            pb += (double)X[e] * (double)B[e];
-                        }
-                    }
-            }
-            for (int off = 2; off > 0; off >>= 1) {
-                pa += __shfl_xor(pa, off);
-                pb += __shfl_xor(pb, off);
-            }
-            if (ok && l4 == 0) {
-                const int ca = it.a + (pa < 0.0 ? half : 0), cb = it.b + (pb < 0.0 ? half : 0);
-                int pick;
-                if (!vb) pick = ca;
-                else if (!va) pick = cb;
-                else if (fabs(pa) > fabs(pb)) pick = ca;
-                else if (fabs(pb) > fabs(pa)) pick = cb;
-                else pick = min(ca, cb);
-                buckets[it.item] = pick;
-            }
-        }
-        for (int q = lane; q < n1; q += kWave) {
-            const int32_t item = q < kWave ? back_item : rq[region_size - 1 - q].item;
-            const int r = (item / dm.L) % dm.nh;
-            const int slot = atomicAdd(&scount[r], 1);
-            slist[(int64_t)r * cap + slot] = item;
-            sbest[(int64_t)r * cap + slot] = 0ull;
-        }
-    }
-}
-
-// Pass 2: every column for the listed items of a round, grouped so that a
+// ------------------------------------------------------------------ re-decision, part 2
+// Every column for the listed items of a round, grouped so that a
 // workgroup reads one 32-column tile of R once for 64 items. Block (t, r, z)
 // takes groups z, z + Z, ... of round r's list. Each (item, column) product is
 // summed in fp64; the best of the tile goes into the item's key by a 64-bit
@@ -755,13 +744,31 @@ __global__ __launch_bounds__(256) void hash_scan_kernel(const T* __restrict__ qk
     }
 }
 
-// Pass 3: the listed items take the bucket of their best key.
+// The listed items take the bucket of their best key; the last row of
+// workgroups sums the region counts into the public count.
 __global__ __launch_bounds__(256) void hash_scan_finish_kernel(const int32_t* __restrict__ scount,
                                                                const int32_t* __restrict__ slist,
                                                                const uint64_t* __restrict__ sbest,
                                                                int64_t cap,
-                                                               int32_t* __restrict__ buckets) {
+                                                               int32_t* __restrict__ buckets,
+                                                               const int32_t* __restrict__ rcount,
+                                                               int64_t nregions,
+                                                               int32_t* __restrict__ counter) {
     const int r = blockIdx.y;
+    if (r == (int)gridDim.y - 1) {
+        // the public count: the queue regions' two counts, summed
+        if (blockIdx.x != 0) return;
+        __shared__ int32_t part[4];
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        int32_t c = 0;
+#pragma unroll 16
+        for (int64_t i = threadIdx.x; i < 2 * nregions; i += 256) c += rcount[i];
+        for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+        if (lane == 0) part[wave] = c;
+        __syncthreads();
+        if (threadIdx.x == 0) counter[0] = part[0] + part[1] + part[2] + part[3];
+        return;
+    }
     const int n = min(scount[r], (int)cap);
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
         buckets[slist[(int64_t)r * cap + i]] = 4095 - (int)(sbest[(int64_t)r * cap + i] & 0xFFFull);
@@ -769,16 +776,10 @@ __global__ __launch_bounds__(256) void hash_scan_finish_kernel(const int32_t* __
 
 // ------------------------------------------------------------------ launcher
 template <typename T>
-static hipError_t launch_refine(const T* qk, const Dims& d, int32_t* buckets,
-                                const HashWorkspace& w, int64_t nregions, int region_size,
-                                hipStream_t st, hipEvent_t* ev, int* nev, const char** names) {
+static hipError_t launch_scan(const T* qk, const Dims& d, int32_t* buckets, const HashWorkspace& w,
+                              int64_t nregions, hipStream_t st, hipEvent_t* ev, int* nev,
+                              const char** names) {
     const int64_t cap = queue_tokens(d);
-    const unsigned blocks = (unsigned)std::min<int64_t>(2048, (nregions + 3) / 4);
-    hash_refine_kernel<T><<<blocks, 256, 0, st>>>(qk, w.rt, d, w.counter, w.queue, w.rcount,
-                                                  nregions, region_size, buckets, w.scount,
-                                                  w.slist, w.sbest, cap);
-    hipError_t e = mark(st, ev, nev, names, "hash_refine_pairs");
-    if (e != hipSuccess) return e;
     // enough groups for a few thousand listed items per round; more loop
     const unsigned z = (unsigned)std::min<int64_t>(16, (cap + 63) / 64);
     const dim3 sgrid((unsigned)hash_ntiles(d), (unsigned)d.nh, z);
@@ -786,8 +787,8 @@ static hipError_t launch_refine(const T* qk, const Dims& d, int32_t* buckets,
         hash_scan_kernel<64, T><<<sgrid, 256, 0, st>>>(qk, w.rt, d, w.scount, w.slist, w.sbest, cap);
     else
         hash_scan_kernel<128, T><<<sgrid, 256, 0, st>>>(qk, w.rt, d, w.scount, w.slist, w.sbest, cap);
-    hash_scan_finish_kernel<<<dim3(4, (unsigned)d.nh), 256, 0, st>>>(w.scount, w.slist, w.sbest,
-                                                                    cap, buckets);
+    hash_scan_finish_kernel<<<dim3(4, (unsigned)d.nh + 1), 256, 0, st>>>(
+        w.scount, w.slist, w.sbest, cap, buckets, w.rcount, nregions, w.counter);
     return mark(st, ev, nev, names, "hash_refine_scan");
 }
 
@@ -811,29 +812,31 @@ hipError_t launch_hash(const void* qk, const float* R, const Dims& d, int32_t* b
         static_assert(per_wave >= kWave, "the re-decision pass reads 64 entries of a region ahead");
         const unsigned grid = (unsigned)((d.T + per_wg - 1) / per_wg);
         const uint16_t* x = (const uint16_t*)qk;
+        const int64_t cap = queue_tokens(d);
         if (d.d == 64)
-            hash_mfma_kernel<64, TOKF><<<grid, 256, 0, st>>>(x, (const u32x4*)w.rfrag, w.rnorm, d,
-                                                           buckets, w.queue, w.rcount,
-                                                           (const uint16_t*)v_for_max, w.vmax);
+            hash_mfma_kernel<64, TOKF><<<grid, 256, 0, st>>>(
+                x, (const u32x4*)w.rfrag, w.rnorm, d, buckets, w.queue, w.rcount,
+                (const uint16_t*)v_for_max, w.vmax, w.rt, w.scount, w.slist, w.sbest, cap);
         else
-            hash_mfma_kernel<128, TOKF><<<grid, 256, 0, st>>>(x, (const u32x4*)w.rfrag, w.rnorm, d,
-                                                            buckets, w.queue, w.rcount,
-                                                            (const uint16_t*)v_for_max, w.vmax);
+            hash_mfma_kernel<128, TOKF><<<grid, 256, 0, st>>>(
+                x, (const u32x4*)w.rfrag, w.rnorm, d, buckets, w.queue, w.rcount,
+                (const uint16_t*)v_for_max, w.vmax, w.rt, w.scount, w.slist, w.sbest, cap);
         if ((e = mark(st, ev, nev, names, "hash_fast_mfma")) != hipSuccess) return e;
-        return launch_refine(x, d, buckets, w, (int64_t)grid * 4, per_wave * d.nh, st, ev, nev,
-                             names);
+        return launch_scan(x, d, buckets, w, (int64_t)grid * 4, st, ev, nev, names);
     } else {
         const float* x = (const float*)qk;
         dim3 grid((unsigned)((d.T + 255) / 256), (unsigned)d.nh);
+        const int64_t cap = queue_tokens(d);
         if (d.d == 64)
             hash_valu_kernel<64, float><<<grid, 256, 0, st>>>(x, R, w.rnorm, d, buckets, w.queue,
-                                                              w.rcount);
+                                                              w.rcount, w.rt, w.scount, w.slist,
+                                                              w.sbest, cap);
         else
             hash_valu_kernel<128, float><<<grid, 256, 0, st>>>(x, R, w.rnorm, d, buckets, w.queue,
-                                                               w.rcount);
+                                                               w.rcount, w.rt, w.scount, w.slist,
+                                                               w.sbest, cap);
         if ((e = mark(st, ev, nev, names, "hash_fast_fp32")) != hipSuccess) return e;
-        return launch_refine(x, d, buckets, w, (int64_t)grid.x * 4 * d.nh, kWave, st, ev, nev,
-                             names);
+        return launch_scan(x, d, buckets, w, (int64_t)grid.x * 4 * d.nh, st, ev, nev, names);
     }
 }
 
