@@ -120,8 +120,11 @@ def test_hash_exact_ties_and_zero_rows(dtype):
     assert refined >= 2 * 17
 
 
+# the last three cases span many sort tiles (64K, 64K plus a ragged tail, 96K)
 SORT_CASES = [("uniform", 1024, 4096 + 192), ("uniform", 64, 4096 * 3), ("skewed", 256, 16384),
-              ("constant", 64, 5000 // 8 * 8), ("uniform", 4096, 8192), ("uniform", 2, 100)]
+              ("constant", 64, 5000 // 8 * 8), ("uniform", 4096, 8192), ("uniform", 2, 100),
+              ("uniform", 2048, 65536), ("uniform", 256, 65536 + 64 * 5),
+              ("skewed", 4096, 3 * 32768)]
 
 
 @pytest.mark.parametrize("kind,nb,L", SORT_CASES)
