@@ -38,6 +38,7 @@ def algorithmic_work(w):
     T = w.B * w.H * w.L                      # token-heads
     TR = T * w.n_hashes                      # token-rounds
     d, half = w.d, w.n_buckets // 2
+    compact = w.dtype == "bf16" and w.chunk_len == 64   # fp16 per-round rows
     hash_flops = 2.0 * d * half * w.n_hashes * T
     return {
         # projection x R for every round, one fp16 matrix-core pass (fp32
@@ -48,14 +49,15 @@ def algorithmic_work(w):
         # per slot (scatter, fused forward)
         "sort_count": ("hbm", 4.0 * TR, "B"),
         "sort_scatter": ("hbm", 8.0 * TR, "B"),
-        # gather qk and v rows once per token-round, read the packed sorted
-        # key, write the round's output row and lse (fp16 rows on the bf16
-        # matrix-core path, fp32 otherwise)
+        # gather qk and v rows once per token-round, read the sorted key (and
+        # bucket id), write the round's output row: fp32 plus a separate lse
+        # on the plain path, fp16 with the lse carried in the row on the bf16
+        # matrix-core path
         "attend_fp32": ("hbm", TR * (2 * d * e + 8 + 4 * d + 4), "B"),
-        "attend_mfma": ("hbm", TR * (2 * d * e + 4 + 2 * d + 4), "B"),
-        # read every round's output row and lse of a token; write out
-        "combine": ("hbm", T * (w.n_hashes * ((2 if w.dtype == "bf16" else 4) * d + 4) + d * e),
-                    "B"),
+        "attend_mfma": ("hbm", TR * (2 * d * e + 4 + 2 * d), "B"),
+        # read every round's output row of a token (fp16 rows carry their lse;
+        # fp32 rows come with an lse and an inverse-permutation entry); write out
+        "combine": ("hbm", T * (w.n_hashes * (2 * d if compact else 4 * d + 8) + d * e), "B"),
     }
 
 

@@ -79,12 +79,16 @@ FwdLayout fwd_layout(const Dims& d) {
     off += align_up(sizeof(int32_t) * n, 256);
     f.perm = off;
     off += align_up(sizeof(int32_t) * n, 256);
+    // The fp16 by-position rows carry their own lse and, with packed sort
+    // keys, need no inverse permutation: those regions are then empty.
+    const bool compact = compact_o_sorted(d);
+    const bool packed = compact && packed_sort_keys(d);
     f.inv = off;
-    off += align_up(sizeof(int32_t) * n, 256);
+    off += packed ? 0 : align_up(sizeof(int32_t) * n, 256);
     f.lse = off;
-    off += align_up(sizeof(float) * n, 256);
+    off += compact ? 0 : align_up(sizeof(float) * n, 256);
     f.o = off;
-    off += align_up((compact_o_sorted(d) ? 2 : sizeof(float)) * n * d.d, 256);
+    off += align_up((compact ? 2 : sizeof(float)) * n * d.d, 256);
     f.total = off;
     return f;
 }

@@ -367,6 +367,20 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
             // four lanes of a query swap pieces so that lane g stores features
             // 32 k + 8 g .. +7: each store then writes 64 contiguous bytes of
             // the row (half as many memory requests as 8-byte pieces).
+            //
+            // The row also carries the round's log-partition function (log2
+            // domain): every 64-byte group of 32 features holds its 32 bits in
+            // the lowest mantissa bit of each value -- word j of the group
+            // (features 2j, 2j+1) holds bit j in its low half and bit 16 + j
+            // in its high half. A separate lse array would be written 4 bytes
+            // at a time at scattered positions, each store a partial memory
+            // sector; this way the combine finds it in the row it reads
+            // anyway. The cost is at most one fp16 ulp on each value.
+            const uint32_t lb = __float_as_uint(mx + log2f(sum));
+            uint32_t pat[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                pat[i] = ((lb >> (4 * g + i)) & 1u) | (((lb >> (16 + 4 * g + i)) & 1u) << 16);
             u32x2 hv[DT];
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
@@ -388,15 +402,17 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
                         const uint32_t b = __shfl(hv[2 * k + 1][h2], src_a + 16 * q);
                         w[2 * q + h2] = upper ? b : a;
                     }
-                *(u32x4*)(orow + 32 * k + 8 * g) = (u32x4){w[0], w[1], w[2], w[3]};
+                *(u32x4*)(orow + 32 * k + 8 * g) =
+                    (u32x4){(w[0] & 0xFFFEFFFEu) | pat[0], (w[1] & 0xFFFEFFFEu) | pat[1],
+                            (w[2] & 0xFFFEFFFEu) | pat[2], (w[3] & 0xFFFEFFFEu) | pat[3]};
             }
         } else {
             const float inv = 1.0f / sumr;
             float* orow = (float*)o_sorted + slot * D;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) *(f32x4*)(orow + dt * 16 + 4 * g) = oacc[dt] * inv;
+            if (g == 0) lse_sorted[slot] = (mx + log2f(sum)) * 0.6931471805599453f;
         }
-        if (g == 0) lse_sorted[orow_idx] = (mx + log2f(sum)) * 0.6931471805599453f;
 
         if (c + kDepth + 1 < c1 && tid < kM) sm.nperm[(c + kDepth + 1) & 3][tid] = pf;
         __syncthreads();

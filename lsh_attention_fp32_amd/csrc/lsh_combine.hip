@@ -17,8 +17,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Stores 8 consecutive outputs with one vector store.
 __device__ __forceinline__ void store8(float* p, const f32x4& a, const f32x4& b) {
-    *(f32x4*)p = a;
-    *(f32x4*)(p + 4) = b;
+    __builtin_nontemporal_store(a, (f32x4*)p);
+    __builtin_nontemporal_store(b, (f32x4*)(p + 4));
 }
 __device__ __forceinline__ void store8(uint16_t* p, const f32x4& a, const f32x4& b) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -27,20 +27,22 @@ __device__ __forceinline__ void store8(uint16_t* p, const f32x4& a, const f32x4&
     w.y = (uint32_t)f32_to_bf16(a.z) | ((uint32_t)f32_to_bf16(a.w) << 16);
     w.z = (uint32_t)f32_to_bf16(b.x) | ((uint32_t)f32_to_bf16(b.y) << 16);
     w.w = (uint32_t)f32_to_bf16(b.z) | ((uint32_t)f32_to_bf16(b.w) << 16);
-    *(u32x4*)p = w;
+    __builtin_nontemporal_store(w, (u32x4*)p);
 }
 
-// 8 consecutive per-round outputs of one row, as two float4.
+// 8 consecutive per-round outputs of one row, as two float4. The rows are
+// read exactly once, and the outputs are not read again here, so both go
+// through the streaming (nontemporal) path and leave the caches alone.
 template <bool HALF>
 __device__ __forceinline__ void load8(const void* base, int64_t off, f32x4& a, f32x4& b) {
     if constexpr (HALF) {
         typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-        const f16x8 h = *(const f16x8*)((const _Float16*)base + off);
+        const f16x8 h = __builtin_nontemporal_load((const f16x8*)((const _Float16*)base + off));
         a = (f32x4){(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
         b = (f32x4){(float)h[4], (float)h[5], (float)h[6], (float)h[7]};
     } else {
-        a = *(const f32x4*)((const float*)base + off);
-        b = *(const f32x4*)((const float*)base + off + 4);
+        a = __builtin_nontemporal_load((const f32x4*)((const float*)base + off));
+        b = __builtin_nontemporal_load((const f32x4*)((const float*)base + off + 4));
     }
 }
 
@@ -103,51 +105,71 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 }
 
 // Fused form: the chunk kernel already stored every round's row of a token
-// next to each other ([token][round][d], scaled fp16; lse [token][round]), so
-// the un-sort is done and this pass reads one contiguous block per token.
+// next to each other ([token][round][d], scaled fp16), so the un-sort is done
+// and this pass reads one contiguous block per token. Each 64-byte group of
+// 32 features also carries the round's log2-domain lse in its values' lowest
+// mantissa bits: word j of the group holds bit j in its low half and bit
+// 16 + j in its high half. The thread owning 16-byte piece q of a row has
+// words j = 4 (q % 4) .. +3; the four threads of a quad together see one
+// whole group, so two DPP swaps assemble the value.
 template <int D, typename T>
 __global__ __launch_bounds__(256) void combine_bypos_kernel(const _Float16* __restrict__ o_pos,
                                                             const uint32_t* __restrict__ vmax,
-                                                            const float* __restrict__ lse,
                                                             Dims dm, T* __restrict__ out) {
-    constexpr int TPT = D / 8;
-    constexpr int G = 8;
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    constexpr int TPT = D / 8;   // threads per token, one 16-byte piece each
+    constexpr int G = 8;         // rounds whose loads are issued together
     // Blocks run from the last token back: the chunk pass finishes with the
     // last (batch, head) slices, whose rows are then still in the memory-side
     // cache when this pass starts.
     const int64_t gid = (int64_t)(gridDim.x - 1 - blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t tok = gid / TPT;
     const int q = (int)(gid - tok * TPT);
-    if (tok >= dm.T) return;
-    const int64_t row0 = tok * dm.nh;
+    if (tok >= dm.T) return;   // whole tokens, so whole quads, drop out together
+    const u32x4* rows = (const u32x4*)o_pos + tok * dm.nh * TPT + q;   // round r: rows[r * TPT]
+    const int sh = 4 * (q & 3);
     float mx = -INFINITY, sum = 0.f;
     f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
     for (int r0 = 0; r0 < dm.nh; r0 += G) {
         const int n = min(G, dm.nh - r0);
-        float l[G];
-        f32x4 o0[G], o1[G];
+        // past the last round the last row is read again and weighted 0
+        u32x4 w[G];
 #pragma unroll
         for (int k = 0; k < G; ++k)
-            if (k < n) {
-                l[k] = lse[row0 + r0 + k];
-                load8<true>(o_pos, (row0 + r0 + k) * D + 8 * q, o0[k], o1[k]);
-            }
+            w[k] = __builtin_nontemporal_load(rows + min(r0 + k, dm.nh - 1) * TPT);
+        float l[G];
         float gmx = mx;
 #pragma unroll
-        for (int k = 0; k < G; ++k)
-            if (k < n) gmx = fmaxf(gmx, l[k]);
-        const float rescale = expf(mx - gmx);
+        for (int k = 0; k < G; ++k) {
+            uint32_t b = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) b |= (w[k][i] & 0x10001u) << (sh + i);
+            b |= (uint32_t)__builtin_amdgcn_mov_dpp((int)b, 0xB1, 0xF, 0xF, false);   // quad [1,0,3,2]
+            b |= (uint32_t)__builtin_amdgcn_mov_dpp((int)b, 0x4E, 0xF, 0xF, false);   // quad [2,3,0,1]
+            l[k] = k < n ? __uint_as_float(b) : -INFINITY;
+            gmx = fmaxf(gmx, l[k]);
+        }
+        // exp2(l - running max), the running max kept unrounded (a round that
+        // saw only the query itself sits near -1e5 / ln 2)
+        const float rescale = __builtin_amdgcn_exp2f(mx - gmx);   // 0 on the first group
         sum *= rescale;
         a0 *= rescale;
         a1 *= rescale;
 #pragma unroll
-        for (int k = 0; k < G; ++k)
-            if (k < n) {
-                const float e = expf(l[k] - gmx);
-                sum += e;
-                a0 += e * o0[k];
-                a1 += e * o1[k];
-            }
+        for (int k = 0; k < G; ++k) {
+            const float e = __builtin_amdgcn_exp2f(l[k] - gmx);   // 0 past the last round
+            sum += e;
+            const f32x4 lo = {(float)__builtin_bit_cast(_Float16, (uint16_t)w[k][0]),
+                              (float)__builtin_bit_cast(_Float16, (uint16_t)(w[k][0] >> 16)),
+                              (float)__builtin_bit_cast(_Float16, (uint16_t)w[k][1]),
+                              (float)__builtin_bit_cast(_Float16, (uint16_t)(w[k][1] >> 16))};
+            const f32x4 hi = {(float)__builtin_bit_cast(_Float16, (uint16_t)w[k][2]),
+                              (float)__builtin_bit_cast(_Float16, (uint16_t)(w[k][2] >> 16)),
+                              (float)__builtin_bit_cast(_Float16, (uint16_t)w[k][3]),
+                              (float)__builtin_bit_cast(_Float16, (uint16_t)(w[k][3] >> 16))};
+            a0 += e * lo;
+            a1 += e * hi;
+        }
         mx = gmx;
     }
     // the rows carry the power-of-two scale chosen from max|v|
@@ -158,14 +180,13 @@ __global__ __launch_bounds__(256) void combine_bypos_kernel(const _Float16* __re
 template <typename T>
 static void launch_t(const OSorted& o, const float* lse, const int32_t* inv, const Dims& d, T* out,
                      hipStream_t st) {
-    const int64_t threads = d.T * (d.d / 8);
-    const unsigned grid = (unsigned)((threads + 255) / 256);
+    const unsigned grid = (unsigned)((d.T * (d.d / 8) + 255) / 256);
     if (o.half) {
         const _Float16* op = (const _Float16*)o.ptr;
         if (d.d == 64)
-            combine_bypos_kernel<64, T><<<grid, 256, 0, st>>>(op, o.vmax, lse, d, out);
+            combine_bypos_kernel<64, T><<<grid, 256, 0, st>>>(op, o.vmax, d, out);
         else
-            combine_bypos_kernel<128, T><<<grid, 256, 0, st>>>(op, o.vmax, lse, d, out);
+            combine_bypos_kernel<128, T><<<grid, 256, 0, st>>>(op, o.vmax, d, out);
     } else {
         const float* op = (const float*)o.ptr;
         if (d.d == 64)

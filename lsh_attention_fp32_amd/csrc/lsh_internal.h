@@ -117,7 +117,9 @@ hipError_t launch_sort(const int32_t* buckets, const Dims& d, int32_t* perm, int
 // [B,H,nh,L]) for the staged entry points; inside the fused forward on the
 // matrix-core path ("half"), fp16 multiplied by a power of two derived from
 // max|v| (o_scale), so no value can overflow, stored already un-sorted by
-// position ([B,H,L,nh,d], with lse [B,H,L,nh]).
+// position ([B,H,L,nh,d]); each 64-byte group of a row then carries that
+// round's lse (log2 domain) in its values' lowest mantissa bits and no lse
+// array is written.
 struct OSorted {
     void* ptr;                  // float* or _Float16*
     bool half;                  // fp16 by position

@@ -66,13 +66,16 @@ def test_workspace_size_rejects_bad_shapes(lib, kw, code):
 
 def test_workspace_sizes_are_consistent(lib):
     # the fused forward keeps per-round outputs in fp16 on the bf16 matrix-core
-    # path (chunk 64) and in fp32 otherwise
-    for dtype, m, o_bytes in ((lsh.LSH_BF16, 64, 2), (lsh.LSH_F32, 64, 4), (lsh.LSH_BF16, 32, 4)):
+    # path (chunk 64) and in fp32 otherwise; the fp16 rows carry their own lse
+    # and, with packed sort keys, need no inverse, so only buckets and perm
+    # remain of the four int32/fp32 per-slot arrays there
+    for dtype, m, o_bytes, per_slot in ((lsh.LSH_BF16, 64, 2, 2), (lsh.LSH_F32, 64, 4, 4),
+                                        (lsh.LSH_BF16, 32, 4, 4)):
         s = _shape(dtype=dtype, chunk_len=m)
         h, so, f = (lsh.lsh_workspace_size(k, s) for k in ("hash", "sort", "fwd"))
         n = s.B * s.H * s.n_hashes * s.L
         assert h > 0 and so > 0
-        assert f >= h + so + n * (4 * 4 + o_bytes * s.d)
+        assert f >= h + so + n * (4 * per_slot + o_bytes * s.d)
     s = _shape()
     with pytest.raises(lsh.LshError):
         lsh.lsh_workspace_size("nope", s)
