@@ -10,7 +10,7 @@
 //   count   per 4096-element tile: bucket histogram in LDS
 //   scatter per tile: first the slot where each of its (tile, bucket) runs
 //           starts -- the segment's bucket totals, scanned, plus the counts
-//           of the earlier tiles -- then each wave walks its 1024 elements in
+//           of the earlier tiles -- then each wave ranks its 1024 elements in
 //           order; lanes with equal buckets are grouped by a ballot match, so
 //           ranks are exact and the LDS counter of a hot bucket is bumped once
 //           per wave step (skewed buckets do not serialise on LDS atomics).
@@ -84,6 +84,19 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __rest
     const int nb = dm.nb;
     int32_t* start = sh + kSortWaves * nb;
 
+    // The wave's 1024 bucket ids are loaded first (all in flight while the
+    // run starts are computed) and stay in registers.
+    const int32_t* src = buckets + seg * dm.L;
+    const int64_t wbeg = (int64_t)tile * kSortTile + (int64_t)wave * SUB;
+    const int64_t wend = min(wbeg + (int64_t)SUB, (int64_t)dm.L);
+    constexpr int STEPS = SUB / kWave;
+    int kb[STEPS], rank[STEPS];
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+        const int64_t i = wbeg + s * kWave + lane;
+        kb[s] = i < wend ? clamp_bucket(src[i], nb) : 0;
+    }
+
     // First slot of this tile's run of every bucket: exclusive scan over
     // buckets of the segment totals, plus the counts of the earlier tiles.
     // Totals (start[]) and earlier-tile counts (sh[0..nb)) are gathered with
@@ -126,17 +139,19 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __rest
     __syncthreads();
     for (int k = threadIdx.x; k < kSortWaves * nb; k += 256) sh[k] = 0;
     __syncthreads();
-    const int32_t* src = buckets + seg * dm.L;
-    const int64_t wbeg = (int64_t)tile * kSortTile + (int64_t)wave * SUB;
-    const int64_t wend = min(wbeg + (int64_t)SUB, (int64_t)dm.L);
     int32_t* mine = sh + wave * nb;
-    // pass 1: this wave's count per bucket
-    for (int64_t i0 = wbeg; i0 < wend; i0 += kWave) {
-        const int64_t i = i0 + lane;
-        const bool active = i < wend;
-        const int b = active ? clamp_bucket(src[i], nb) : 0;
-        const uint64_t m = match_bucket(b, nbits, active);
-        if (active && (__ffsll((long long)m) - 1) == lane) mine[b] += __popcll(m);
+    // Pass 1 ranks every element among the wave's earlier elements of its
+    // bucket (ballot match, so exact and stable) while counting; pass 2 only
+    // adds the (wave, bucket) run start and stores.
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+        const bool active = wbeg + s * kWave + lane < wend;
+        const uint64_t m = match_bucket(kb[s], nbits, active);
+        rank[s] = mine[kb[s]] + __popcll(m & lanes_below_s(lane));
+        // every lane has read its bucket's count; leaders now advance them
+        __builtin_amdgcn_wave_barrier();
+        if (active && (__ffsll((long long)m) - 1) == lane) mine[kb[s]] += __popcll(m);
+        __builtin_amdgcn_wave_barrier();
     }
     __syncthreads();
     // first slot of each (wave, bucket) run
@@ -149,27 +164,21 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __rest
         }
     }
     __syncthreads();
-    // pass 2: ranks in position order
+    // pass 2: slots
     int32_t* P = perm + seg * dm.L;
     int32_t* I = PACKED ? nullptr : inv + seg * dm.L;
-    for (int64_t i0 = wbeg; i0 < wend; i0 += kWave) {
-        const int64_t i = i0 + lane;
-        const bool active = i < wend;
-        const int b = active ? clamp_bucket(src[i], nb) : 0;
-        const uint64_t m = match_bucket(b, nbits, active);
-        if (active) {
-            const int32_t slot = mine[b] + __popcll(m & lanes_below_s(lane));
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+        const int64_t i = wbeg + s * kWave + lane;
+        if (i < wend) {
+            const int32_t slot = mine[kb[s]] + rank[s];
             if constexpr (PACKED) {
-                P[slot] = (int32_t)(((uint32_t)b << kPackPosBits) | (uint32_t)i);
+                P[slot] = (int32_t)(((uint32_t)kb[s] << kPackPosBits) | (uint32_t)i);
             } else {
                 P[slot] = (int32_t)i;
                 I[i] = slot;
             }
         }
-        // every lane has read its run start; leaders now advance them
-        __builtin_amdgcn_wave_barrier();
-        if (active && (__ffsll((long long)m) - 1) == lane) mine[b] += __popcll(m);
-        __builtin_amdgcn_wave_barrier();
     }
 }
 
