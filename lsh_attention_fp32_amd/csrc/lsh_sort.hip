@@ -7,7 +7,7 @@
 //
 // Positions arrive in increasing order, so a stable counting sort on the
 // bucket alone yields the (bucket, position) order. Two kernels:
-//   count   per 4096-element tile: bucket histogram in LDS
+//   count   per 4096-element tile: bucket histogram in LDS (plain atomics)
 //   scatter per tile: first the slot where each of its (tile, bucket) runs
 //           starts -- the segment's bucket totals, scanned, plus the counts
 //           of the earlier tiles -- then each wave ranks its 1024 elements in
@@ -45,24 +45,28 @@ __device__ __forceinline__ uint64_t lanes_below_s(int lane) {
 
 // counts layout: [seg][tile][bucket] (each tile writes one contiguous row)
 __global__ __launch_bounds__(256) void sort_count_kernel(const int32_t* __restrict__ buckets,
-                                                         Dims dm, int ntiles, int nbits,
+                                                         Dims dm, int ntiles,
                                                          int32_t* __restrict__ counts) {
     extern __shared__ int32_t hist[];
     const int tile = blockIdx.x;
     const int64_t seg = blockIdx.y;
-    const int lane = threadIdx.x & 63;
     for (int b = threadIdx.x; b < dm.nb; b += 256) hist[b] = 0;
     __syncthreads();
     const int32_t* src = buckets + seg * dm.L;
     const int64_t beg = (int64_t)tile * kSortTile;
     const int64_t end = min(beg + (int64_t)kSortTile, (int64_t)dm.L);
-    for (int64_t i0 = beg + (threadIdx.x & ~63); i0 < end; i0 += 256) {
-        const int64_t i = i0 + lane;
-        const bool active = i < end;
-        const int b = active ? clamp_bucket(src[i], dm.nb) : 0;
-        const uint64_t m = match_bucket(b, nbits, active);
-        if (active && (__ffsll((long long)m) - 1) == lane) atomicAdd(&hist[b], __popcll(m));
+    // A count needs no order: plain LDS atomics (lanes of one instruction that
+    // hit the same bucket serialise, which only a heavily skewed tile feels).
+    constexpr int PER = kSortTile / 256;
+    int b[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int64_t i = beg + k * 256 + threadIdx.x;
+        b[k] = i < end ? clamp_bucket(src[i], dm.nb) : -1;
     }
+#pragma unroll
+    for (int k = 0; k < PER; ++k)
+        if (b[k] >= 0) atomicAdd(&hist[b[k]], 1);
     __syncthreads();
     for (int b = threadIdx.x; b < dm.nb; b += 256)
         counts[(seg * ntiles + tile) * dm.nb + b] = hist[b];
@@ -191,7 +195,7 @@ hipError_t launch_sort(const int32_t* buckets, const Dims& d, int32_t* perm, int
     int32_t* counts = (int32_t*)ws;
     dim3 grid((unsigned)ntiles, (unsigned)d.segs);
     hipError_t e;
-    sort_count_kernel<<<grid, 256, sizeof(int32_t) * d.nb, st>>>(buckets, d, ntiles, nbits, counts);
+    sort_count_kernel<<<grid, 256, sizeof(int32_t) * d.nb, st>>>(buckets, d, ntiles, counts);
     if ((e = mark(st, ev, nev, names, "sort_count")) != hipSuccess) return e;
     const size_t lds = sizeof(int32_t) * (kSortWaves + 1) * d.nb;
     if (packed)
