@@ -1,6 +1,7 @@
 """Benchmark of the LSH-attention forward on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+python bench.py --sweep [--dense]     one line per workload (length sweep and the rest)
 
 A step is one lsh_attention_fwd (hash -> sort -> chunk attention -> combine)
 over one batch of synthetic input already resident in HBM. The default
@@ -11,6 +12,13 @@ The per-kernel durations come from lsh_attention_fwd_timed (HIP events recorded
 after every kernel on the launch stream), averaged over the timed repeats; the
 roofline object reports the longest-running kernel against MI355X's published
 peak for the bound that limits it, with that kernel's algorithmic work.
+forward_roofline sums, over the method's four steps, the larger of (flops /
+peak, algorithmic bytes / HBM peak) and divides by the measured forward time.
+
+--dense adds, per sweep line, PyTorch's scaled_dot_product_attention (a
+third-party dense comparator, flash or memory-efficient backend only) at the
+same shape with is_causal matched, and the analytic dense-attention floor
+4 B H L^2 d / bf16 MFMA peak.
 """
 from __future__ import annotations
 
@@ -59,6 +67,103 @@ def algorithmic_work(w):
         # fp32 rows come with an lse and an inverse-permutation entry); write out
         "combine": ("hbm", T * (w.n_hashes * (2 * d if compact else 4 * d + 8) + d * e), "B"),
     }
+
+
+def forward_roofline(w, ms_per_step):
+    """Whole-forward floor: for each step of the method the larger of its
+    flops at the matching peak and its algorithmic HBM bytes at 8 TB/s
+    (hash: read qk, write the ids; sort: read ids, write keys; chunk pass:
+    gather rows, write per-round rows; combine: read them, write out)."""
+    e = 2 if w.dtype == "bf16" else 4
+    T = w.B * w.H * w.L
+    TR = T * w.n_hashes
+    d = w.d
+    compact = w.dtype == "bf16" and w.chunk_len == 64
+    hash_peak = PEAK_F16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    steps = {
+        "hash": (2.0 * d * (w.n_buckets // 2) * TR, hash_peak, T * (d * e + 4 * w.n_hashes)),
+        "sort": (0.0, 1.0, 12.0 * TR),
+        "chunk": (8.0 * w.chunk_len * d * TR, PEAK_F16_TFLOPS if compact else PEAK_FP32_TFLOPS,
+                  TR * (2 * d * e + 4 + (2 * d if compact else 4 * d + 4))),
+        "combine": (3.0 * w.n_hashes * d * T, PEAK_FP32_TFLOPS,
+                    T * (w.n_hashes * (2 * d if compact else 4 * d + 8) + d * e)),
+    }
+    per = {}
+    for k, (flops, peak, nbytes) in steps.items():
+        t_c = flops / (peak * 1e12) * 1e3
+        t_m = nbytes / (PEAK_HBM_GBS * 1e9) * 1e3
+        per[k] = {"roof_ms": max(t_c, t_m), "bound": "hbm" if t_m >= t_c else "compute"}
+    t_roof = sum(x["roof_ms"] for x in per.values())
+    return {"t_roof_ms": t_roof, "frac": t_roof / ms_per_step, "steps": per}
+
+
+def measure(lsh, torch, w, steps, warmup):
+    """Times `steps` back-to-back forwards on synthetic inputs resident in HBM,
+    then the per-kernel event intervals of a few more."""
+    import numpy as np
+    import workloads
+
+    dev = torch.device("cuda:0")
+    qk, v, R = workloads.make_inputs(w)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    qk_t = torch.from_numpy(qk).to(dev, dt)
+    v_t = torch.from_numpy(v).to(dev, dt)
+    R_t = torch.from_numpy(R).to(dev)
+    shape = lsh.shape_of(qk_t, w.n_buckets, w.n_hashes, w.chunk_len, w.causal)
+    ws = torch.empty(lsh.lsh_workspace_size("fwd", shape), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(qk_t)
+
+    for _ in range(warmup):
+        lsh.lsh_attention_fwd(qk_t, v_t, R_t, shape, out, ws)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        lsh.lsh_attention_fwd(qk_t, v_t, R_t, shape, out, ws)
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = start.elapsed_time(stop) / steps
+    refined = int(ws[:4].view(torch.int32).item())
+
+    # per-kernel durations, same launches with an event after each kernel
+    reps = max(3, min(steps, 10))
+    acc = {}
+    for _ in range(reps):
+        for kname, ms in lsh.lsh_attention_fwd_timed(qk_t, v_t, R_t, shape, out, ws):
+            acc.setdefault(kname, []).append(ms)
+    kernels = {k: float(np.mean(x)) for k, x in acc.items()}
+    return {"ms_per_step": ms_per_step, "wall": wall, "refined": refined, "kernels": kernels,
+            "inputs": (qk, v, R), "tensors": (qk_t, v_t)}
+
+
+def dense_comparator(torch, w, qk_t, v_t, steps=10):
+    """PyTorch SDPA at the same shape (queries = keys = qk), flash or
+    memory-efficient backend only; None when neither takes the shape."""
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    import torch.nn.functional as F
+
+    if w.dtype != "bf16":
+        return None
+    try:
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]):
+            for _ in range(2):
+                F.scaled_dot_product_attention(qk_t, qk_t, v_t, is_causal=bool(w.causal))
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(steps):
+                F.scaled_dot_product_attention(qk_t, qk_t, v_t, is_causal=bool(w.causal))
+            b.record()
+            torch.cuda.synchronize()
+    except RuntimeError as ex:
+        return {"ms": None, "note": str(ex).splitlines()[0][:120]}
+    ms = a.elapsed_time(b) / steps
+    floor = 4.0 * w.B * w.H * w.L * w.L * w.d / (PEAK_F16_TFLOPS * 1e12) * 1e3
+    return {"kind": "third-party: torch scaled_dot_product_attention", "ms": ms,
+            "tokens_per_s": w.B * w.L / (ms / 1e3), "analytic_dense_floor_ms": floor}
 
 
 def cpu_baseline(w, qk, v, R, target_s=12.0):
@@ -114,6 +219,10 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (to scale HBM byte counters)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="one JSON line per workload: the length sweep, then the others")
+    ap.add_argument("--dense", action="store_true",
+                    help="with --sweep: also time torch's dense SDPA at each shape")
     args = ap.parse_args()
     if args.copy_calibration:
         import torch
@@ -129,47 +238,34 @@ def main() -> int:
                                    "by (batch, head) with no communication, so --gpus must be 1"}))
         return 2
 
-    import numpy as np
     import torch
 
     import lsh_attention_fp32_amd as lsh
     import workloads
 
+    lsh.load_library()
+    if args.sweep:
+        names = [n for n in workloads.WORKLOADS if n.startswith("sweep_")]
+        names += [n for n in workloads.WORKLOADS if not n.startswith("sweep_")]
+        for n in names:
+            w = workloads.WORKLOADS[n]
+            r = measure(lsh, torch, w, min(args.steps, 10), args.warmup)
+            line = {"workload": n, "config": w.describe(), "ms_per_step": r["ms_per_step"],
+                    "tokens_per_s": w.B * w.L / (r["ms_per_step"] / 1e3),
+                    "kernels_ms": r["kernels"], "hash_redecided": r["refined"],
+                    "forward_roofline": forward_roofline(w, r["ms_per_step"])}
+            if args.dense:
+                line["dense"] = dense_comparator(torch, w, *r["tensors"])
+            del r
+            torch.cuda.empty_cache()
+            print(json.dumps(line), flush=True)
+        return 0
+
     name = args.workload or workloads.HEADLINE
     w = workloads.WORKLOADS[name]
-    dev = torch.device("cuda:0")
-    lsh.load_library()
-    qk, v, R = workloads.make_inputs(w)
-    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    qk_t = torch.from_numpy(qk).to(dev, dt)
-    v_t = torch.from_numpy(v).to(dev, dt)
-    R_t = torch.from_numpy(R).to(dev)
-    shape = lsh.shape_of(qk_t, w.n_buckets, w.n_hashes, w.chunk_len, w.causal)
-    ws = torch.empty(lsh.lsh_workspace_size("fwd", shape), dtype=torch.uint8, device=dev)
-    out = torch.empty_like(qk_t)
-
-    for _ in range(args.warmup):
-        lsh.lsh_attention_fwd(qk_t, v_t, R_t, shape, out, ws)
-    torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record()
-    for _ in range(args.steps):
-        lsh.lsh_attention_fwd(qk_t, v_t, R_t, shape, out, ws)
-    stop.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = start.elapsed_time(stop) / args.steps
-    refined = int(ws[:4].view(torch.int32).item())
-
-    # per-kernel durations, same launches with an event after each kernel
-    reps = max(3, min(args.steps, 10))
-    acc = {}
-    for _ in range(reps):
-        for kname, ms in lsh.lsh_attention_fwd_timed(qk_t, v_t, R_t, shape, out, ws):
-            acc.setdefault(kname, []).append(ms)
-    kernels = {k: float(np.mean(x)) for k, x in acc.items()}
+    r = measure(lsh, torch, w, args.steps, args.warmup)
+    ms_per_step, wall, refined, kernels = r["ms_per_step"], r["wall"], r["refined"], r["kernels"]
+    qk, v, R = r["inputs"]
     work = algorithmic_work(w)
     dominant = max((k for k in kernels if k in work), key=lambda k: kernels[k])
     bound, amount, _unit = work[dominant]
@@ -206,6 +302,7 @@ def main() -> int:
                    "n_buckets": w.n_buckets, "n_hashes": w.n_hashes, "chunk_len": w.chunk_len,
                    "causal": w.causal, "qk_dist": w.qk_dist},
         "roofline": roof,
+        "forward_roofline": forward_roofline(w, ms_per_step),
         "kernels_ms": kernels,
         "hash_redecided": refined,
         "wall_s_timed": wall,

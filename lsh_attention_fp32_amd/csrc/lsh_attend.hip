@@ -15,69 +15,124 @@
 
 namespace lsh {
 
-// Plain fp32 kernel: one thread per query slot, the window read through the
-// cache, two passes (max, then exp-sum and weighted sum of V). Used for fp32
-// inputs and any chunk length.
+// Plain fp32 kernel, for fp32 inputs and for any chunk length. A workgroup
+// takes 64 query slots of one chunk; the four lanes of a query each hold a
+// quarter of its features (dot products are summed across the quad). The
+// window's keys pass through LDS 32 at a time and a running (online) softmax
+// in the exp2 domain folds each block into the output.
 template <int D, typename T>
-__global__ __launch_bounds__(128) void attend_valu_kernel(const T* __restrict__ qk,
+__global__ __launch_bounds__(256) void attend_valu_kernel(const T* __restrict__ qk,
                                                           const T* __restrict__ v,
                                                           const int32_t* __restrict__ buckets,
                                                           const int32_t* __restrict__ perm,
-                                                          Dims dm, float* __restrict__ o_sorted,
+                                                          Dims dm, int nqb,
+                                                          float* __restrict__ o_sorted,
                                                           float* __restrict__ lse_sorted) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    constexpr int QD = D / 4;   // features per lane
+    constexpr int KB = 32;      // keys per LDS block
+    constexpr int KS = D + 4;   // padded LDS row (floats)
+    __shared__ __attribute__((aligned(16))) float ks[KB][KS];
+    __shared__ __attribute__((aligned(16))) float vs[KB][KS];
+    __shared__ int32_t kpos[KB], kbkt[KB];
     const int64_t seg = blockIdx.y;
-    const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (s >= dm.L) return;
-    const int64_t L = dm.L;
+    const int64_t c = blockIdx.x / nqb;
+    const int qb = (int)(blockIdx.x - c * nqb);
+    const int tid = threadIdx.x, ql = tid >> 2, part = tid & 3;
+    const int64_t L = dm.L, m = dm.m;
     const int64_t bh = seg / dm.nh;
     const int32_t* P = perm + seg * L;
     const int32_t* Bk = buckets + seg * L;
     const T* X = qk + bh * L * D;
     const T* V = v + bh * L * D;
-    const int64_t i = P[s];
-    const int bi = Bk[i];
-    const int64_t c = s / dm.m;
-    const int64_t t0 = c > 0 ? (c - 1) * dm.m : 0;
-    const int64_t t1 = (c + 1) * dm.m;
-    const float scale = 1.0f / sqrtf((float)D);
-    const T* xi = X + i * D;
-
-    float mx = -INFINITY;
-    for (int64_t t = t0; t < t1; ++t) {
-        const int64_t j = P[t];
-        if (Bk[j] != bi || (dm.causal && j > i)) continue;
-        const T* xj = X + j * D;
-        float dot = 0.f;
-#pragma unroll 8
-        for (int k = 0; k < D; ++k) dot = fmaf(IO<T>::load(xi, k), IO<T>::load(xj, k), dot);
-        float sc = dot * scale;
-        if (j == i) sc -= kSelfPenalty;
-        mx = fmaxf(mx, sc);
+    const int64_t qoff = (int64_t)qb * 64 + ql;   // query's place in its chunk
+    const bool qlive = qoff < m;
+    const int64_t s = c * m + (qlive ? qoff : 0); // its sorted slot (a real one when not live)
+    const int64_t qpos = P[s];
+    const int32_t qbkt = Bk[qpos];
+    float q[QD];
+#pragma unroll
+    for (int e = 0; e < QD; e += 4) {
+        const f32x4 a = IO<T>::load4(X, qpos * D + part * QD + e);
+        q[e] = a.x; q[e + 1] = a.y; q[e + 2] = a.z; q[e + 3] = a.w;
     }
-    float o[D];
+    const float c2 = 1.4426950408889634f / sqrtf((float)D);   // log2(e) / sqrt(d)
+    const float pen2 = kSelfPenalty * 1.4426950408889634f;
+    float mx = -INFINITY, l = 0.f, acc[QD];
 #pragma unroll
-    for (int k = 0; k < D; ++k) o[k] = 0.f;
-    float sum = 0.f;
-    for (int64_t t = t0; t < t1; ++t) {
-        const int64_t j = P[t];
-        if (Bk[j] != bi || (dm.causal && j > i)) continue;
-        const T* xj = X + j * D;
-        float dot = 0.f;
-#pragma unroll 8
-        for (int k = 0; k < D; ++k) dot = fmaf(IO<T>::load(xi, k), IO<T>::load(xj, k), dot);
-        float sc = dot * scale;
-        if (j == i) sc -= kSelfPenalty;
-        const float p = expf(sc - mx);
-        sum += p;
-        const T* vj = V + j * D;
+    for (int e = 0; e < QD; ++e) acc[e] = 0.f;
+    const int64_t t0 = c > 0 ? (c - 1) * m : 0, t1 = (c + 1) * m;
+    for (int64_t kb0 = t0; kb0 < t1; kb0 += KB) {
+        const int nk = (int)min((int64_t)KB, t1 - kb0);
+        __syncthreads();   // the previous block has been consumed
+        if (tid < KB) {
+            const int32_t p = tid < nk ? P[kb0 + tid] : -1;
+            kpos[tid] = p;
+            kbkt[tid] = p >= 0 ? Bk[p] : 0;
+        }
+        __syncthreads();
+        for (int i = tid; i < KB * (D / 4); i += 256) {
+            const int j = i / (D / 4), k = 4 * (i % (D / 4));
+            const int32_t p = kpos[j];
+            f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+            if (p >= 0) {
+                a = IO<T>::load4(X, (int64_t)p * D + k);
+                b = IO<T>::load4(V, (int64_t)p * D + k);
+            }
+            *(f32x4*)&ks[j][k] = a;
+            *(f32x4*)&vs[j][k] = b;
+        }
+        __syncthreads();
+        float sc[KB];
+        float bmx = mx;
 #pragma unroll
-        for (int k = 0; k < D; ++k) o[k] = fmaf(p, IO<T>::load(vj, k), o[k]);
+        for (int j = 0; j < KB; ++j) {
+            float dot = 0.f;
+#pragma unroll
+            for (int e = 0; e < QD; e += 4) {
+                const f32x4 kk = *(const f32x4*)&ks[j][part * QD + e];
+                dot = fmaf(q[e], kk.x, dot);
+                dot = fmaf(q[e + 1], kk.y, dot);
+                dot = fmaf(q[e + 2], kk.z, dot);
+                dot = fmaf(q[e + 3], kk.w, dot);
+            }
+            dot += __shfl_xor(dot, 1);
+            dot += __shfl_xor(dot, 2);
+            const int32_t kp = kpos[j];
+            const bool ok = j < nk && kbkt[j] == qbkt && (!dm.causal || kp <= qpos);
+            const float s2 = dot * c2 - (kp == qpos ? pen2 : 0.f);
+            sc[j] = ok ? s2 : -INFINITY;
+            bmx = fmaxf(bmx, sc[j]);
+        }
+        if (bmx == -INFINITY) continue;   // nothing valid yet (the same for a query's quad)
+        const float rs = __builtin_amdgcn_exp2f(mx - bmx);   // 0 while mx = -inf
+        l *= rs;
+#pragma unroll
+        for (int e = 0; e < QD; ++e) acc[e] *= rs;
+#pragma unroll
+        for (int j = 0; j < KB; ++j) {
+            const float p = __builtin_amdgcn_exp2f(sc[j] - bmx);   // 0 where masked
+            l += p;
+#pragma unroll
+            for (int e = 0; e < QD; e += 4) {
+                const f32x4 vv = *(const f32x4*)&vs[j][part * QD + e];
+                acc[e] = fmaf(p, vv.x, acc[e]);
+                acc[e + 1] = fmaf(p, vv.y, acc[e + 1]);
+                acc[e + 2] = fmaf(p, vv.z, acc[e + 2]);
+                acc[e + 3] = fmaf(p, vv.w, acc[e + 3]);
+            }
+        }
+        mx = bmx;
     }
-    const float inv_sum = 1.0f / sum;
-    float* os = o_sorted + (seg * L + s) * D;
+    if (!qlive) return;
+    // the query's own key is always in its window and valid, so l > 0
+    const float inv = 1.0f / l;
+    float* os = o_sorted + (seg * L + s) * D + part * QD;
 #pragma unroll
-    for (int k = 0; k < D; ++k) os[k] = o[k] * inv_sum;
-    lse_sorted[seg * L + s] = mx + logf(sum);
+    for (int e = 0; e < QD; e += 4)
+        *(f32x4*)(os + e) = (f32x4){acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv,
+                                    acc[e + 3] * inv};
+    if (part == 0) lse_sorted[seg * L + s] = (mx + log2f(l)) * 0.6931471805599453f;
 }
 
 // ---------------------------------------------------------------------------
@@ -428,11 +483,12 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
 template <typename T>
 static void launch_valu(const T* qk, const T* v, const int32_t* buckets, const int32_t* perm,
                         const Dims& d, float* o, float* lse, hipStream_t st) {
-    dim3 grid((unsigned)((d.L + 127) / 128), (unsigned)d.segs);
+    const int nqb = (d.m + 63) / 64;   // 64-query blocks per chunk
+    dim3 grid((unsigned)((int64_t)(d.L / d.m) * nqb), (unsigned)d.segs);
     if (d.d == 64)
-        attend_valu_kernel<64, T><<<grid, 128, 0, st>>>(qk, v, buckets, perm, d, o, lse);
+        attend_valu_kernel<64, T><<<grid, 256, 0, st>>>(qk, v, buckets, perm, d, nqb, o, lse);
     else
-        attend_valu_kernel<128, T><<<grid, 128, 0, st>>>(qk, v, buckets, perm, d, o, lse);
+        attend_valu_kernel<128, T><<<grid, 256, 0, st>>>(qk, v, buckets, perm, d, nqb, o, lse);
 }
 
 hipError_t launch_attend(const void* qk, const void* v, const int32_t* buckets,

@@ -160,6 +160,12 @@ STEP_CASES = [
     _wl("bf16", B=1, H=2, L=64 * 17, d=64, nb=16, nh=2, m=64, causal=False, seed=18),
     _wl("bf16", B=1, H=2, L=64 * 33, d=128, nb=64, nh=2, m=64, causal=True, seed=19,
         dist="clusters"),
+    # plain-kernel chunks that are not a multiple of its 64-query blocks or
+    # of its 32-key blocks (96: a partial second query block; 40: partial key
+    # blocks), and a long chunk with a 128-wide head
+    _wl("fp32", B=1, H=1, L=96 * 8, d=64, nb=8, nh=2, m=96, causal=True, seed=23),
+    _wl("fp32", B=1, H=2, L=40 * 9, d=64, nb=4, nh=2, m=40, causal=False, seed=24),
+    _wl("bf16", B=1, H=1, L=128 * 6, d=128, nb=8, nh=2, m=128, causal=True, seed=25),
 ]
 
 
