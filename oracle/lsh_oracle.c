@@ -31,7 +31,8 @@
  *   [SCHOLAR]   ai-scholar.tech summary, section "Transformerの問題点とは":
  *               scaled dot-product attention with the 1/sqrt(d_k) factor;
  *               section "・LSH Attention": Q = K, bucket, sort, equal chunks,
- *               attend own chunk and the preceding one.
+ *               attend own chunk and the preceding one; section
+ *               "Reformerを用いた結果": model width d_model 1024 with 8 heads.
  *
  * Readings where the pages are silent (each is listed with its reason in the
  * design notes):
@@ -335,5 +336,47 @@ int oracle_forward(const double *qk, const double *v, const double *R,
         free(os);
         if (rc) return rc;
     }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* P0 -- input projections ahead of the hash.                               */
+/* [GLOSSARY] "Atenção LSH": queries and keys come from one shared          */
+/* projection; [SCHOLAR] "Reformerを用いた結果": a model width of 1024       */
+/* split over 8 heads. Reading: two bias-free linear maps of the token      */
+/* vectors, one giving the shared query/key vectors and one the values,     */
+/* each with H*d outputs, head h taking outputs h*d .. h*d + d - 1; the     */
+/* weight of output n for input k is w[n * d_model + k].                    */
+/*   x            [B, L, d_model]                                           */
+/*   w_qk, w_v    [H * d, d_model]                                          */
+/*   qk, v (out)  [B, H, L, d]                                              */
+/*   qk[b,h,l,e] = sum_k x[b,l,k] * w_qk[h*d + e, k]   (likewise v with w_v) */
+/* ------------------------------------------------------------------------ */
+int oracle_project(const double *x, int B, int64_t L, int d_model,
+                   const double *w_qk, const double *w_v, int H, int d,
+                   double *qk, double *v)
+{
+    if (B < 0 || L < 0 || d_model < 1 || H < 1 || d < 1) return -1;
+#ifdef _OPENMP
+#pragma omp parallel for collapse(2) schedule(static)
+#endif
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < H; ++h)
+            for (int64_t l = 0; l < L; ++l) {
+                const double *xr = x + ((int64_t)b * L + l) * d_model;
+                double *qo = qk + (((int64_t)b * H + h) * L + l) * d;
+                double *vo = v + (((int64_t)b * H + h) * L + l) * d;
+                for (int e = 0; e < d; ++e) {
+                    const double *wq = w_qk + ((int64_t)h * d + e) * d_model;
+                    const double *wv = w_v + ((int64_t)h * d + e) * d_model;
+                    double sq = 0.0, sv = 0.0;
+                    for (int k = 0; k < d_model; ++k) {
+                        sq += xr[k] * wq[k];
+                        sv += xr[k] * wv[k];
+                    }
+                    qo[e] = sq;
+                    vo[e] = sv;
+                }
+            }
     return 0;
 }

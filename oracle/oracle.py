@@ -14,6 +14,8 @@ their sources are documented in ``lsh_oracle.c``:
               causal and self rules, softmax in double
   combine  -- O5, un-sort and logsumexp-weighted sum over rounds
   forward  -- O1..O5 over every (batch, head)
+  project  -- P0, the shared query/key and the value projections of the
+              token vectors, split into heads
 """
 from __future__ import annotations
 
@@ -63,10 +65,12 @@ def _load():
                                        ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                        ctypes.c_int, ctypes.c_int, _f64p, _i32p, _f64p, _i32p,
                                        _i32p, _f64p, _f64p]
+        lib.oracle_project.argtypes = [_f64p, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                       _f64p, _f64p, ctypes.c_int, ctypes.c_int, _f64p, _f64p]
         lib.oracle_threads.argtypes = []
         lib.oracle_threads.restype = ctypes.c_int
         for fn in (lib.oracle_hash, lib.oracle_sort, lib.oracle_attend, lib.oracle_combine,
-                   lib.oracle_forward):
+                   lib.oracle_forward, lib.oracle_project):
             fn.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -187,3 +191,22 @@ def forward(qk, v, R, n_buckets: int, chunk_len: int, causal: bool, return_all: 
                                   _p(g("perm"), _i32p), _p(g("inv"), _i32p),
                                   _p(g("o_sorted"), _f64p), _p(g("lse"), _f64p)), "forward")
     return (out, extra) if return_all else out
+
+
+def project(x, w_qk, w_v, n_heads: int):
+    """P0: qk, v [B, H, L, d] from token vectors x [B, L, d_model] and weights
+    w_qk, w_v [H * d, d_model] (output n of input k at w[n, k]); head h takes
+    outputs h*d .. h*d + d - 1."""
+    x = _f64(x)
+    w_qk = _f64(w_qk)
+    w_v = _f64(w_v)
+    B, L, dm = x.shape
+    n_out = w_qk.shape[0]
+    if w_qk.shape != (n_out, dm) or w_v.shape != (n_out, dm) or n_out % n_heads:
+        raise ValueError("weights must be [H * d, d_model] with d_model matching x")
+    d = n_out // n_heads
+    qk = np.zeros((B, n_heads, L, d))
+    v = np.zeros((B, n_heads, L, d))
+    _check(_load().oracle_project(_p(x, _f64p), B, L, dm, _p(w_qk, _f64p), _p(w_v, _f64p),
+                                  n_heads, d, _p(qk, _f64p), _p(v, _f64p)), "project")
+    return qk, v

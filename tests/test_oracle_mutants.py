@@ -46,6 +46,14 @@ MUTANTS = {
     "combine_wrong_round_slot": ("const int64_t s = inv[(int64_t)r * L + i];",
                                  "const int64_t s = inv[i];"),
     "lse_log2": ("const double l = mx + log(sum);", "const double l = mx + log2(sum);"),
+    # every index below stays inside the buffers for any shape
+    "project_weights_transposed": (
+        "sq += xr[k] * wq[k];",
+        "sq += xr[k] * w_qk[(int64_t)k * H * d + (int64_t)h * d + e];"),
+    "project_layout_bl_h": (
+        "double *qo = qk + (((int64_t)b * H + h) * L + l) * d;",
+        "double *qo = qk + (((int64_t)b * L + l) * H + h) * d;"),
+    "project_v_from_qk_weights": ("sv += xr[k] * wv[k];", "sv += xr[k] * wq[k];"),
 }
 
 

@@ -341,3 +341,48 @@ def test_forward_bf16_inputs_widen_exactly():
     a = np.random.default_rng(1).standard_normal(100000).astype(np.float32) * 7
     ref = torch.from_numpy(a).to(torch.bfloat16).to(torch.float32).numpy()
     assert np.array_equal(workloads.round_to_bf16(a), ref)
+
+
+# --------------------------------------------------------------------------- P0 projections
+
+def test_project_hand_example(oracle_mod):
+    """P0: a hand-computed example; it fixes the head split, the weight
+    orientation (output n of input k at w[n, k]) and which weights feed v."""
+    g = _golden("projection_hand_example.json")
+    qk, v = oracle_mod.project(np.array(g["x"], float), np.array(g["w_qk"], float),
+                               np.array(g["w_v"], float), g["heads"])
+    assert np.array_equal(qk, np.array(g["qk"], float))
+    assert np.array_equal(v, np.array(g["v"], float))
+
+
+def test_project_selection_weights_copy_features(oracle_mod):
+    """P0: one-hot weight rows copy input features, so every output is an
+    exact copy of a known input element (layout [B, H, L, d])."""
+    rng = np.random.default_rng(40)
+    B, L, dm, H, d = 2, 5, 12, 3, 4
+    x = rng.standard_normal((B, L, dm))
+    pick_q = rng.integers(0, dm, H * d)
+    pick_v = rng.permutation(dm)[: H * d] if H * d <= dm else rng.integers(0, dm, H * d)
+    w_qk = np.eye(dm)[pick_q]
+    w_v = -2.0 * np.eye(dm)[pick_v]
+    qk, v = oracle_mod.project(x, w_qk, w_v, H)
+    for b in range(B):
+        for h in range(H):
+            for l in range(L):
+                for e in range(d):
+                    assert qk[b, h, l, e] == x[b, l, pick_q[h * d + e]]
+                    assert v[b, h, l, e] == -2.0 * x[b, l, pick_v[h * d + e]]
+
+
+def test_project_matches_einsum(oracle_mod):
+    """P0: agrees with numpy's einsum (a library contraction) on random data."""
+    rng = np.random.default_rng(41)
+    B, L, dm, H, d = 2, 7, 24, 2, 8
+    x = rng.standard_normal((B, L, dm))
+    w_qk = rng.standard_normal((H * d, dm))
+    w_v = rng.standard_normal((H * d, dm))
+    qk, v = oracle_mod.project(x, w_qk, w_v, H)
+    ref_qk = np.einsum("blk,hek->bhle", x, w_qk.reshape(H, d, dm))
+    ref_v = np.einsum("blk,hek->bhle", x, w_v.reshape(H, d, dm))
+    assert np.allclose(qk, ref_qk, rtol=1e-12, atol=1e-12)
+    assert np.allclose(v, ref_v, rtol=1e-12, atol=1e-12)
