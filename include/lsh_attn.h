@@ -83,9 +83,9 @@ typedef struct lsh_shape {
     int32_t dtype;
 } lsh_shape_t;
 
-/* Bytes of workspace needed by `stage` ("hash", "sort" or "fwd") for `shape`,
- * written to *bytes (host). Returns LSH_ERR_ARG for an unknown stage or an
- * invalid shape. */
+/* Bytes of workspace needed by `stage` ("hash", "sort", "fwd" or "fwd_x")
+ * for `shape`, written to *bytes (host). Returns LSH_ERR_ARG for an unknown
+ * stage or an invalid shape. */
 int lsh_workspace_size(const char *stage, const lsh_shape_t *shape, size_t *bytes);
 
 /* Step 1 -- angular LSH over n_hashes rounds (glossary "Atenção LSH";
@@ -151,6 +151,32 @@ int lsh_attention_fwd_timed(const void *qk, const void *v, const float *R,
                             const lsh_shape_t *shape, void *out, void *ws, size_t ws_bytes,
                             void *stream, float *kernel_ms, const char **kernel_names,
                             int32_t max_kernels, int32_t *n_kernels);
+
+/* Input projections ahead of step 1 (glossary "Atenção LSH": queries and
+ * keys come from one shared projection; ai-scholar.tech summary, section
+ * "Reformerを用いた結果": model width 1024 split over 8 heads). Two bias-free
+ * linear maps of the token vectors, each with H*d outputs; head h takes
+ * outputs h*d .. h*d + d - 1:
+ *   qk[b,h,l,e] = sum_k x[b,l,k] * w_qk[h*d + e, k]     (v likewise, w_v)
+ *   x         [B, L, d_model]       shape->dtype
+ *   w_qk, w_v [H*d, d_model]        shape->dtype (a linear layer's weight:
+ *                                   row = output, column = input)
+ *   qk, v     [B, H, L, d]          shape->dtype (out)
+ * Accumulation in float32 (bf16: matrix cores), outputs rounded to nearest
+ * even. d_model must be a positive multiple of 8 (else LSH_ERR_ARG). Only
+ * B, H, L, d and dtype of `shape` are used, but the whole shape must be
+ * valid. No workspace. */
+int lsh_qkv_project(const void *x, const void *w_qk, const void *w_v, const lsh_shape_t *shape,
+                    int32_t d_model, void *qk, void *v, void *stream);
+
+/* lsh_qkv_project followed by lsh_attention_fwd, with qk and v kept in the
+ * workspace (at least lsh_workspace_size("fwd_x") bytes; its first int32 is
+ * the hash stage's re-decided count, as in lsh_hash).
+ *   x [B, L, d_model], w_qk, w_v [H*d, d_model], R as for lsh_hash,
+ *   out [B, H, L, d]. */
+int lsh_attention_fwd_x(const void *x, const void *w_qk, const void *w_v, const float *R,
+                        const lsh_shape_t *shape, int32_t d_model, void *out, void *ws,
+                        size_t ws_bytes, void *stream);
 
 /* Message for the last error on the calling thread ("" if none). */
 const char *lsh_last_error(void);

@@ -9,9 +9,10 @@ no other implementation to fall back to.
 Low-level functions keep the C names and argument order (tensors in place of
 pointers): ``lsh_workspace_size``, ``lsh_hash``, ``lsh_sort``,
 ``lsh_chunk_attend``, ``lsh_unsort_combine``, ``lsh_attention_fwd``,
-``lsh_attention_fwd_timed``. The allocating helpers ``hash``, ``sort``,
-``chunk_attend``, ``unsort_combine`` and ``attention_fwd`` create the outputs
-and workspaces with torch.
+``lsh_attention_fwd_timed``, ``lsh_qkv_project``, ``lsh_attention_fwd_x``.
+The allocating helpers ``hash``, ``sort``, ``chunk_attend``,
+``unsort_combine``, ``attention_fwd``, ``qkv_project`` and
+``attention_fwd_x`` create the outputs and workspaces with torch.
 """
 from ._binding import (  # noqa: F401
     LSH_BF16,
@@ -19,18 +20,22 @@ from ._binding import (  # noqa: F401
     LshError,
     Shape,
     attention_fwd,
+    attention_fwd_x,
     chunk_attend,
     hash,
     library_path,
     load_library,
     lsh_attention_fwd,
     lsh_attention_fwd_timed,
+    lsh_attention_fwd_x,
     lsh_chunk_attend,
     lsh_hash,
     lsh_last_error,
+    lsh_qkv_project,
     lsh_sort,
     lsh_unsort_combine,
     lsh_workspace_size,
+    qkv_project,
     shape_of,
     sort,
     unsort_combine,

@@ -57,8 +57,11 @@ def load_library():
                                             ctypes.POINTER(ctypes.c_float),
                                             ctypes.POINTER(ctypes.c_char_p), i32,
                                             ctypes.POINTER(i32)]
+    lib.lsh_qkv_project.argtypes = [vp, vp, vp, sp, i32, vp, vp, vp]
+    lib.lsh_attention_fwd_x.argtypes = [vp, vp, vp, vp, sp, i32, vp, vp, sz, vp]
     for name in ("lsh_workspace_size", "lsh_hash", "lsh_sort", "lsh_chunk_attend",
-                 "lsh_unsort_combine", "lsh_attention_fwd", "lsh_attention_fwd_timed"):
+                 "lsh_unsort_combine", "lsh_attention_fwd", "lsh_attention_fwd_timed",
+                 "lsh_qkv_project", "lsh_attention_fwd_x"):
         getattr(lib, name).restype = ctypes.c_int
     lib.lsh_last_error.argtypes = []
     lib.lsh_last_error.restype = ctypes.c_char_p
@@ -156,6 +159,20 @@ def lsh_attention_fwd_timed(qk, v, R, shape: Shape, out, ws, stream=None, max_ke
     return [(names[k].decode(), float(ms[k])) for k in range(n.value)]
 
 
+def lsh_qkv_project(x, w_qk, w_v, shape: Shape, d_model: int, qk, v, stream=None) -> None:
+    _check(load_library().lsh_qkv_project(_ptr(x), _ptr(w_qk), _ptr(w_v), ctypes.byref(shape),
+                                          int(d_model), _ptr(qk), _ptr(v), _stream(stream)),
+           "lsh_qkv_project")
+
+
+def lsh_attention_fwd_x(x, w_qk, w_v, R, shape: Shape, d_model: int, out, ws,
+                        stream=None) -> None:
+    _check(load_library().lsh_attention_fwd_x(
+        _ptr(x), _ptr(w_qk), _ptr(w_v), _ptr(R), ctypes.byref(shape), int(d_model), _ptr(out),
+        _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)),
+        "lsh_attention_fwd_x")
+
+
 # ---------------------------------------------------------------- allocating helpers
 
 def _workspace(stage: str, shape: Shape, device) -> torch.Tensor:
@@ -215,4 +232,41 @@ def attention_fwd(qk, v, R, n_buckets: int, chunk_len: int, causal: bool, ws=Non
     out = torch.empty_like(qk) if out is None else out
     ws = _workspace("fwd", shape, qk.device) if ws is None else ws
     lsh_attention_fwd(qk, v, R, shape, out, ws, stream)
+    return out
+
+
+def _x_shape(x, w_qk, w_v, n_heads: int, n_buckets: int, n_hashes: int, chunk_len: int,
+             causal: bool) -> Shape:
+    if x.dim() != 3:
+        raise ValueError(f"x must be [B, L, d_model], got {tuple(x.shape)}")
+    if x.dtype not in _DTYPES:
+        raise ValueError(f"x dtype must be float32 or bfloat16, got {x.dtype}")
+    B, L, dm = x.shape
+    n_out = w_qk.shape[0]
+    if (w_qk.shape != (n_out, dm) or w_v.shape != (n_out, dm) or n_out % n_heads
+            or w_qk.dtype != x.dtype or w_v.dtype != x.dtype):
+        raise ValueError("w_qk and w_v must be [H * d, d_model] in x's dtype")
+    return Shape(B, n_heads, L, n_out // n_heads, n_buckets, n_hashes, chunk_len,
+                 int(bool(causal)), _DTYPES[x.dtype])
+
+
+def qkv_project(x, w_qk, w_v, n_heads: int, stream=None):
+    """Returns (qk, v), both [B, H, L, d] in x's dtype, from x [B, L, d_model]
+    and weights [H * d, d_model]."""
+    shape = _x_shape(x, w_qk, w_v, n_heads, 2, 1, 1, False)
+    shape.chunk_len = max(1, shape.L)
+    qk = torch.empty((shape.B, shape.H, shape.L, shape.d), dtype=x.dtype, device=x.device)
+    v = torch.empty_like(qk)
+    lsh_qkv_project(x, w_qk, w_v, shape, x.shape[2], qk, v, stream)
+    return qk, v
+
+
+def attention_fwd_x(x, w_qk, w_v, R, n_heads: int, n_buckets: int, chunk_len: int, causal: bool,
+                    ws=None, out=None, stream=None):
+    """Projections, then the whole forward; returns out [B, H, L, d] in x's dtype."""
+    shape = _x_shape(x, w_qk, w_v, n_heads, n_buckets, R.shape[0], chunk_len, causal)
+    out = torch.empty((shape.B, shape.H, shape.L, shape.d), dtype=x.dtype,
+                      device=x.device) if out is None else out
+    ws = _workspace("fwd_x", shape, x.device) if ws is None else ws
+    lsh_attention_fwd_x(x, w_qk, w_v, R, shape, x.shape[2], out, ws, stream)
     return out

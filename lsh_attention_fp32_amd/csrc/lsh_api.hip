@@ -139,6 +139,19 @@ int run_fwd(const void* qk, const void* v, const float* R, const lsh_shape_t* sh
     return LSH_OK;
 }
 
+// One projected tensor ([B,H,L,d] in the I/O dtype), rounded up so the next
+// region stays 256-byte aligned.
+size_t projected_bytes(const Dims& d) {
+    return align_up((size_t)d.T * d.d * (d.dtype == LSH_BF16 ? 2 : 4), 256);
+}
+
+int check_dmodel(const char* fn, int32_t d_model) {
+    if (d_model < 8 || d_model % 8 != 0)
+        return fail(LSH_ERR_ARG, "%s: d_model must be a positive multiple of 8 (got %d)", fn,
+                    (int)d_model);
+    return LSH_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -154,7 +167,8 @@ int lsh_workspace_size(const char* stage, const lsh_shape_t* shape, size_t* byte
     if (!strcmp(stage, "hash")) *bytes = hash_workspace_bytes(d);
     else if (!strcmp(stage, "sort")) *bytes = sort_workspace_bytes(d);
     else if (!strcmp(stage, "fwd")) *bytes = fwd_layout(d).total;
-    else return fail(LSH_ERR_ARG, "unknown stage '%s' (hash, sort or fwd)", stage);
+    else if (!strcmp(stage, "fwd_x")) *bytes = 2 * projected_bytes(d) + fwd_layout(d).total;
+    else return fail(LSH_ERR_ARG, "unknown stage '%s' (hash, sort, fwd or fwd_x)", stage);
     return LSH_OK;
 }
 
@@ -239,6 +253,48 @@ int lsh_attention_fwd(const void* qk, const void* v, const float* R, const lsh_s
         return fail(LSH_ERR_ARG, "lsh_attention_fwd: tensor pointers must be 16-byte aligned");
     return run_fwd(qk, v, R, shape, out, ws, ws_bytes, (hipStream_t)stream, nullptr, nullptr,
                    nullptr);
+}
+
+int lsh_qkv_project(const void* x, const void* w_qk, const void* w_v, const lsh_shape_t* shape,
+                    int32_t d_model, void* qk, void* v, void* stream) {
+    g_err[0] = 0;
+    int rc = validate(shape);
+    if (rc) return rc;
+    if ((rc = check_dmodel("lsh_qkv_project", d_model))) return rc;
+    if (empty(shape)) return LSH_OK;
+    if (!x || !w_qk || !w_v || !qk || !v)
+        return fail(LSH_ERR_ARG, "lsh_qkv_project: NULL tensor pointer");
+    if (misaligned({x, w_qk, w_v, qk, v}))
+        return fail(LSH_ERR_ARG, "lsh_qkv_project: tensor pointers must be 16-byte aligned");
+    const Dims d = make_dims(*shape);
+    hipError_t e = launch_project(x, w_qk, w_v, d, d_model, qk, v, (hipStream_t)stream);
+    return e == hipSuccess ? LSH_OK : hip_fail(e, "lsh_qkv_project");
+}
+
+int lsh_attention_fwd_x(const void* x, const void* w_qk, const void* w_v, const float* R,
+                        const lsh_shape_t* shape, int32_t d_model, void* out, void* ws,
+                        size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    int rc = validate(shape);
+    if (rc) return rc;
+    if ((rc = check_dmodel("lsh_attention_fwd_x", d_model))) return rc;
+    if (empty(shape)) return LSH_OK;
+    if (!x || !w_qk || !w_v || !R || !out)
+        return fail(LSH_ERR_ARG, "lsh_attention_fwd_x: NULL tensor pointer");
+    if (misaligned({x, w_qk, w_v, R, out}))
+        return fail(LSH_ERR_ARG, "lsh_attention_fwd_x: tensor pointers must be 16-byte aligned");
+    const Dims d = make_dims(*shape);
+    const size_t pb = projected_bytes(d);
+    if ((rc = check_ws("lsh_attention_fwd_x", d, ws, ws_bytes, 2 * pb + fwd_layout(d).total)))
+        return rc;
+    // the forward's own workspace comes first, so its re-decided count stays
+    // the first int32 of ws; the projected tensors follow it
+    const size_t fb = fwd_layout(d).total;
+    char* qk = (char*)ws + fb;
+    char* v = qk + pb;
+    hipError_t e = launch_project(x, w_qk, w_v, d, d_model, qk, v, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "lsh_attention_fwd_x: projection");
+    return run_fwd(qk, v, R, shape, out, ws, fb, (hipStream_t)stream, nullptr, nullptr, nullptr);
 }
 
 int lsh_attention_fwd_timed(const void* qk, const void* v, const float* R,

@@ -141,6 +141,11 @@ hipError_t launch_combine(const OSorted& o, const float* lse_sorted, const int32
                           const Dims& d, void* out, hipStream_t st, hipEvent_t* ev, int* nev,
                           const char** names);
 
+// ----------------------------------------------------- input projections
+// qk, v [B,H,L,d] from x [B,L,d_model] and weights [H*d, d_model].
+hipError_t launch_project(const void* x, const void* w_qk, const void* w_v, const Dims& d,
+                          int d_model, void* qk, void* v, hipStream_t st);
+
 // Power of two s with max|v| * s <= 2^14: fp16 then holds every |o| <= max|v|.
 __device__ __forceinline__ float o_scale(uint32_t vmax_bf16) {
     const uint32_t bits = (vmax_bf16 & 0x7FFFu) << 16;

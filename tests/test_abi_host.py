@@ -35,7 +35,7 @@ def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("lsh_hash", "lsh_sort", "lsh_chunk_attend", "lsh_unsort_combine",
               "lsh_attention_fwd", "lsh_workspace_size", "lsh_last_error",
-              "lsh_attention_fwd_timed"):
+              "lsh_attention_fwd_timed", "lsh_qkv_project", "lsh_attention_fwd_x"):
         assert n in names
 
 
@@ -115,3 +115,30 @@ def test_empty_problems_enqueue_nothing(lib):
         s = _shape(**kw)
         assert lib.lsh_attention_fwd(None, None, None, ctypes.byref(s), None, None, 0, None) == 0
         assert lib.lsh_hash(None, None, ctypes.byref(s), None, None, 0, None) == 0
+
+
+@pytest.mark.parametrize("d_model", [0, -8, 12, 100])
+def test_projection_rejects_bad_d_model(lib, d_model):
+    # host-side check, before any pointer is looked at or anything is enqueued
+    s = ctypes.byref(_shape())
+    assert lib.lsh_qkv_project(None, None, None, s, d_model, None, None, None) == -1
+    assert "d_model" in lsh.lsh_last_error()
+    assert lib.lsh_attention_fwd_x(None, None, None, None, s, d_model, None, None, 0, None) == -1
+    assert "d_model" in lsh.lsh_last_error()
+
+
+def test_projection_rejects_null_and_misaligned_pointers(lib):
+    assert lib.lsh_qkv_project(None, None, None, ctypes.byref(_shape()), 64, None, None,
+                               None) == -1
+    assert "NULL" in lsh.lsh_last_error()
+    p = ctypes.c_void_p(0x1008)
+    rc = lib.lsh_qkv_project(p, p, p, ctypes.byref(_shape()), 64, p, p, None)
+    assert rc == -1 and "aligned" in lsh.lsh_last_error()
+
+
+def test_fwd_x_workspace_holds_the_projected_tensors(lib):
+    for dtype, e in ((lsh.LSH_BF16, 2), (lsh.LSH_F32, 4)):
+        s = _shape(dtype=dtype)
+        fwd = lsh.lsh_workspace_size("fwd", s)
+        fx = lsh.lsh_workspace_size("fwd_x", s)
+        assert fx >= fwd + 2 * s.B * s.H * s.L * s.d * e
