@@ -2,6 +2,7 @@
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 python bench.py --sweep [--dense]     one line per workload (length sweep and the rest)
+python bench.py --project             input projections (d_model 1024) and the forward from x
 
 A step is one lsh_attention_fwd (hash -> sort -> chunk attention -> combine)
 over one batch of synthetic input already resident in HBM. The default
@@ -139,6 +140,48 @@ def measure(lsh, torch, w, steps, warmup):
             "inputs": (qk, v, R), "tensors": (qk_t, v_t)}
 
 
+def measure_projection(lsh, torch, w, steps, warmup, d_model=1024):
+    """lsh_qkv_project and lsh_attention_fwd_x at the workload's shape with
+    model width d_model (synthetic bf16 token vectors and weights)."""
+    import numpy as np
+
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    g = torch.Generator(device="cpu").manual_seed(w.seed)
+    x = torch.randn((w.B, w.L, d_model), generator=g).to(dev, dt)
+    wq = (torch.randn((w.H * w.d, d_model), generator=g) / np.sqrt(d_model)).to(dev, dt)
+    wv = (torch.randn((w.H * w.d, d_model), generator=g) / np.sqrt(d_model)).to(dev, dt)
+    R = torch.randn((w.n_hashes, w.d, w.n_buckets // 2), generator=g).to(dev)
+    shape = lsh.Shape(w.B, w.H, w.L, w.d, w.n_buckets, w.n_hashes, w.chunk_len, int(w.causal),
+                      lsh.LSH_BF16 if w.dtype == "bf16" else lsh.LSH_F32)
+    qk = torch.empty((w.B, w.H, w.L, w.d), dtype=dt, device=dev)
+    v = torch.empty_like(qk)
+    out = torch.empty_like(qk)
+    ws = torch.empty(lsh.lsh_workspace_size("fwd_x", shape), dtype=torch.uint8, device=dev)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    p_ms = timed(lambda: lsh.lsh_qkv_project(x, wq, wv, shape, d_model, qk, v))
+    f_ms = timed(lambda: lsh.lsh_attention_fwd_x(x, wq, wv, R, shape, d_model, out, ws))
+    flops = 2.0 * w.B * w.L * d_model * 2 * w.H * w.d
+    peak = PEAK_F16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    return {"workload": f"{w.name}_dmodel{d_model}", "project_ms": p_ms,
+            "project_tflops": flops / p_ms / 1e9, "project_frac": flops / p_ms / 1e9 / peak,
+            "project_bytes": (w.B * w.L * d_model + 2 * w.H * w.d * d_model
+                              + 2 * w.B * w.H * w.L * w.d) * (2 if w.dtype == "bf16" else 4),
+            "fwd_x_ms": f_ms, "fwd_x_tokens_per_s": w.B * w.L / (f_ms / 1e3)}
+
+
 def dense_comparator(torch, w, qk_t, v_t, steps=10):
     """PyTorch SDPA at the same shape (queries = keys = qk), flash or
     memory-efficient backend only; None when neither takes the shape."""
@@ -223,6 +266,8 @@ def main() -> int:
                     help="one JSON line per workload: the length sweep, then the others")
     ap.add_argument("--dense", action="store_true",
                     help="with --sweep: also time torch's dense SDPA at each shape")
+    ap.add_argument("--project", action="store_true",
+                    help="time the input projections and the forward that starts from x")
     args = ap.parse_args()
     if args.copy_calibration:
         import torch
@@ -259,6 +304,11 @@ def main() -> int:
             del r
             torch.cuda.empty_cache()
             print(json.dumps(line), flush=True)
+        return 0
+
+    if args.project:
+        print(json.dumps(measure_projection(lsh, torch, workloads.WORKLOADS[
+            args.workload or workloads.HEADLINE], args.steps, args.warmup)), flush=True)
         return 0
 
     name = args.workload or workloads.HEADLINE

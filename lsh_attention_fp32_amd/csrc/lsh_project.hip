@@ -30,6 +30,7 @@ constexpr int kPN = 256;        // outputs (n) per workgroup
 constexpr int kPM = 128;        // tokens (m) per workgroup
 constexpr int kPK = 32;         // k per LDS stage
 constexpr int kPRow = kPK + 8;  // padded LDS row (bf16): 80 bytes, rows 20 banks apart
+constexpr int kXcds = 8;        // L2 domains the dispatcher deals workgroups over
 
 struct ProjectLds {
     uint16_t a[2][kPN][kPRow];   // weight rows
@@ -61,12 +62,29 @@ struct OutMap {
 __global__ __launch_bounds__(256) void project_mfma_kernel(const uint16_t* __restrict__ x,
                                                            const uint16_t* __restrict__ wqk,
                                                            const uint16_t* __restrict__ wv,
-                                                           int64_t M, int N, int K, OutMap out) {
+                                                           int64_t M, int N, int K, int ntn,
+                                                           int64_t ntm, OutMap out) {
     __shared__ ProjectLds sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wn = wave & 1, wm = wave >> 1;
-    const int n0 = blockIdx.x * kPN;
-    const int64_t m0 = (int64_t)blockIdx.y * kPM;
+    // Workgroups are dealt round-robin over the L2 domains, so the linear id
+    // is remapped: the ids that share a domain take one token tile through
+    // every output tile in turn, and its token rows come from HBM once.
+    int64_t tn, tm;
+    {
+        const int64_t id = blockIdx.x, total = (int64_t)ntn * ntm;
+        const int64_t full = total / ((int64_t)kXcds * ntn) * ((int64_t)kXcds * ntn);
+        if (id < full) {
+            const int64_t xcd = id % kXcds, j = id / kXcds;
+            tn = j % ntn;
+            tm = (j / ntn) * kXcds + xcd;
+        } else {   // the tail that does not fill every domain: plain order
+            tn = (id - full) % ntn;
+            tm = full / ntn + (id - full) / ntn;
+        }
+    }
+    const int n0 = (int)tn * kPN;
+    const int64_t m0 = tm * kPM;
     const int hd = N / 2;
 
     // global -> register staging: row r = tid / 4 + 64 j, piece tid % 4
@@ -133,25 +151,42 @@ __global__ __launch_bounds__(256) void project_mfma_kernel(const uint16_t* __res
         __syncthreads();
     }
 
-    // D register r of lane l: output 8 (r / 4) + 4 (l / 32) + r % 4 of the
-    // block, token l % 32
+    // The results go out through LDS, one half of the tokens at a time: the
+    // waves that own tokens 64 p .. 64 p + 63 write them as bf16 rows
+    // [token][output] (D register r of lane l is output 8 (r / 4) + 4 (l / 32)
+    // + r % 4 of its block, token l % 32), then every thread stores 16-byte
+    // pieces of whole rows, each piece 8 consecutive features of one head.
+    constexpr int ORow = kPN + 8;   // padded row (bf16): 528 bytes, 16-byte aligned
+    static_assert(64 * ORow * 2 <= (int)sizeof(ProjectLds), "output staging fits the stage buffers");
+    uint16_t* ot = (uint16_t*)&sm;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int64_t m = m0 + wm * 64 + 32 * j + (lane & 31);
-        if (m >= M) continue;
+    for (int p = 0; p < 2; ++p) {
+        if (wm == p) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * 128 + 32 * i + 8 * g + 4 * (lane >> 5);
-                if (n >= N) continue;
-                const f32x16& a = acc[i][j];
-                const u32x2 w = {(uint32_t)f32_to_bf16(a[4 * g]) |
-                                     ((uint32_t)f32_to_bf16(a[4 * g + 1]) << 16),
-                                 (uint32_t)f32_to_bf16(a[4 * g + 2]) |
-                                     ((uint32_t)f32_to_bf16(a[4 * g + 3]) << 16)};
-                *(u32x2*)out.at(m, n) = w;
-            }
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int ml = 32 * j + (lane & 31);
+                        const int nl = wn * 128 + 32 * i + 8 * g + 4 * (lane >> 5);
+                        const f32x16& a = acc[i][j];
+                        *(u32x2*)&ot[ml * ORow + nl] =
+                            (u32x2){(uint32_t)f32_to_bf16(a[4 * g]) |
+                                        ((uint32_t)f32_to_bf16(a[4 * g + 1]) << 16),
+                                    (uint32_t)f32_to_bf16(a[4 * g + 2]) |
+                                        ((uint32_t)f32_to_bf16(a[4 * g + 3]) << 16)};
+                    }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = tid; q < 64 * (kPN / 8); q += 256) {
+            const int ml = q / (kPN / 8), pc = q % (kPN / 8);
+            const int64_t m = m0 + 64 * p + ml;
+            const int n = n0 + 8 * pc;
+            if (m < M && n < N) *(u32x4*)out.at(m, n) = *(const u32x4*)&ot[ml * ORow + 8 * pc];
+        }
+        __syncthreads();
     }
 }
 
@@ -224,10 +259,12 @@ hipError_t launch_project(const void* x, const void* w_qk, const void* w_v, cons
     const int N = 2 * d.H * d.d;
     if (M == 0) return hipSuccess;
     if (d.dtype == LSH_BF16) {
-        const dim3 grid((unsigned)((N + kPN - 1) / kPN), (unsigned)((M + kPM - 1) / kPM));
+        const int ntn = (N + kPN - 1) / kPN;
+        const int64_t ntm = (M + kPM - 1) / kPM;
         const OutMap om{(uint16_t*)qk, (uint16_t*)v, d.L, d.H, d.d, d.H * d.d};
-        project_mfma_kernel<<<grid, 256, 0, st>>>((const uint16_t*)x, (const uint16_t*)w_qk,
-                                                  (const uint16_t*)w_v, M, N, d_model, om);
+        project_mfma_kernel<<<(unsigned)(ntn * ntm), 256, 0, st>>>(
+            (const uint16_t*)x, (const uint16_t*)w_qk, (const uint16_t*)w_v, M, N, d_model, ntn,
+            ntm, om);
     } else {
         const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
         project_f32_kernel<<<grid, 256, 0, st>>>((const float*)x, (const float*)w_qk,
