@@ -340,6 +340,127 @@ int oracle_forward(const double *qk, const double *v, const double *R,
 }
 
 /* ------------------------------------------------------------------------ */
+/* G1 -- backward of the whole forward for one (batch, head) and beyond.    */
+/* The hash and the sort are piecewise constant, so only the attention       */
+/* carries a gradient. By O4/O5 the output of position i is one softmax over */
+/* every (round, key) hit: out_i = sum_{r,j} P_i(r,j) v_j with               */
+/* P_i(r,j) = exp(s_ij - Z_i), s_ij the masked, penalised score of key j in  */
+/* round r's window of i, and Z_i = log sum_r exp(lse_r(i)). For a loss with */
+/* gradient g_i = dL/dout_i this gives, with D_i = g_i . out_i:              */
+/*   dv_j     += P_i(r,j) g_i                                                */
+/*   dS_i(r,j) = P_i(r,j) (g_i . v_j - D_i)                                  */
+/*   dq_i     += dS_i(r,j) x_j / sqrt(d)     (x_i as the query)              */
+/*   dk_j     += dS_i(r,j) x_i / sqrt(d)     (x_j as the key)                */
+/* and, queries and keys being the same vectors, dqk = dq + dk. The penalty  */
+/* on the self score is a constant and has no derivative of its own.         */
+/*                                                                           */
+/*   qk, v, dout  [B, H, L, d]                                               */
+/*   R            [n_hashes, d, n_buckets/2]                                 */
+/*   dqk, dv      [B, H, L, d]  out                                          */
+/* ------------------------------------------------------------------------ */
+int oracle_backward(const double *qk, const double *v, const double *R, const double *dout,
+                    int B, int H, int64_t L, int d, int n_buckets, int n_hashes,
+                    int chunk_len, int causal, double *dqk, double *dv)
+{
+    if (B < 0 || H < 0 || L < 0 || d < 1 || n_hashes < 1 || chunk_len < 1 ||
+        n_buckets < 2 || (n_buckets % 2) != 0 || (L % chunk_len) != 0)
+        return -1;
+    const int64_t seg = (int64_t)n_hashes * L;
+    const int64_t m = chunk_len;
+    const double scale = 1.0 / sqrt((double)d);
+    for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
+        const double *x = qk + bh * L * d;
+        const double *vv = v + bh * L * d;
+        const double *g = dout + bh * L * d;
+        double *gx = dqk + bh * L * d;
+        double *gv = dv + bh * L * d;
+        const size_t n1 = (size_t)(seg ? seg : 1), nl = (size_t)(L ? L : 1);
+        int32_t *bk = (int32_t *)malloc(sizeof(int32_t) * n1);
+        int32_t *pm = (int32_t *)malloc(sizeof(int32_t) * n1);
+        int32_t *iv = (int32_t *)malloc(sizeof(int32_t) * n1);
+        double *mg = (double *)malloc(sizeof(double) * n1);
+        double *ls = (double *)malloc(sizeof(double) * n1);
+        double *os = (double *)malloc(sizeof(double) * n1 * (size_t)d);
+        double *out = (double *)malloc(sizeof(double) * nl * (size_t)d);
+        double *z = (double *)malloc(sizeof(double) * nl);
+        double *dd = (double *)malloc(sizeof(double) * nl);
+        int rc = (bk && pm && iv && mg && ls && os && out && z && dd) ? 0 : -2;
+        /* the forward's own steps */
+        if (!rc) rc = oracle_hash(x, L, d, R, n_hashes, n_buckets, bk, mg);
+        for (int r = 0; !rc && r < n_hashes; ++r)
+            rc = oracle_sort(bk + r * L, L, pm + r * L, iv + r * L);
+        for (int r = 0; !rc && r < n_hashes; ++r)
+            rc = oracle_attend(x, vv, L, d, bk + r * L, pm + r * L, chunk_len, causal, NULL, 0,
+                               os + r * L * d, ls + r * L);
+        if (!rc) rc = oracle_combine(os, ls, iv, n_hashes, L, d, NULL, 0, out);
+        if (!rc) {
+            /* Z_i (log of the total partition function) and D_i */
+            for (int64_t i = 0; i < L; ++i) {
+                double mx = -INFINITY;
+                for (int r = 0; r < n_hashes; ++r) {
+                    const double l = ls[(int64_t)r * L + iv[(int64_t)r * L + i]];
+                    if (l > mx) mx = l;
+                }
+                double sum = 0.0;
+                for (int r = 0; r < n_hashes; ++r)
+                    sum += exp(ls[(int64_t)r * L + iv[(int64_t)r * L + i]] - mx);
+                z[i] = mx + log(sum);
+                double dot = 0.0;
+                for (int k = 0; k < d; ++k) dot += g[i * d + k] * out[i * d + k];
+                dd[i] = dot;
+            }
+            for (int64_t e = 0; e < L * d; ++e) {
+                gx[e] = 0.0;
+                gv[e] = 0.0;
+            }
+            /* every (round, query slot, window key): serial, so the sums into
+               the keys' gradients need no care */
+            for (int r = 0; r < n_hashes; ++r) {
+                const int32_t *bucket = bk + (int64_t)r * L;
+                const int32_t *perm = pm + (int64_t)r * L;
+                for (int64_t s = 0; s < L; ++s) {
+                    const int64_t i = perm[s];
+                    const int64_t c = s / m;
+                    const int64_t t0 = (c > 0) ? (c - 1) * m : 0;
+                    const int64_t t1 = (c + 1) * m;
+                    const double *xi = x + i * d, *gi = g + i * d;
+                    for (int64_t t = t0; t < t1; ++t) {
+                        const int64_t j = perm[t];
+                        if (!((bucket[j] == bucket[i]) && (!causal || j <= i))) continue;
+                        const double *xj = x + j * d, *vj = vv + j * d;
+                        double dot = 0.0, gdv = 0.0;
+                        for (int k = 0; k < d; ++k) {
+                            dot += xi[k] * xj[k];
+                            gdv += gi[k] * vj[k];
+                        }
+                        double sc = dot * scale;
+                        if (j == i) sc -= ORACLE_SELF_PENALTY;
+                        const double p = exp(sc - z[i]);
+                        const double ds = p * (gdv - dd[i]);
+                        for (int k = 0; k < d; ++k) {
+                            gv[j * d + k] += p * gi[k];
+                            gx[i * d + k] += ds * scale * xj[k];
+                            gx[j * d + k] += ds * scale * xi[k];
+                        }
+                    }
+                }
+            }
+        }
+        free(bk);
+        free(pm);
+        free(iv);
+        free(mg);
+        free(ls);
+        free(os);
+        free(out);
+        free(z);
+        free(dd);
+        if (rc) return rc;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* P0 -- input projections ahead of the hash.                               */
 /* [GLOSSARY] "Atenção LSH": queries and keys come from one shared          */
 /* projection; [SCHOLAR] "Reformerを用いた結果": a model width of 1024       */

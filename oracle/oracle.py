@@ -16,6 +16,7 @@ their sources are documented in ``lsh_oracle.c``:
   forward  -- O1..O5 over every (batch, head)
   project  -- P0, the shared query/key and the value projections of the
               token vectors, split into heads
+  backward -- G1, gradients of the forward for a given output gradient
 """
 from __future__ import annotations
 
@@ -67,10 +68,13 @@ def _load():
                                        _i32p, _f64p, _f64p]
         lib.oracle_project.argtypes = [_f64p, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
                                        _f64p, _f64p, ctypes.c_int, ctypes.c_int, _f64p, _f64p]
+        lib.oracle_backward.argtypes = [_f64p, _f64p, _f64p, _f64p, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_int, _f64p, _f64p]
         lib.oracle_threads.argtypes = []
         lib.oracle_threads.restype = ctypes.c_int
         for fn in (lib.oracle_hash, lib.oracle_sort, lib.oracle_attend, lib.oracle_combine,
-                   lib.oracle_forward, lib.oracle_project):
+                   lib.oracle_forward, lib.oracle_project, lib.oracle_backward):
             fn.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -210,3 +214,20 @@ def project(x, w_qk, w_v, n_heads: int):
     _check(_load().oracle_project(_p(x, _f64p), B, L, dm, _p(w_qk, _f64p), _p(w_v, _f64p),
                                   n_heads, d, _p(qk, _f64p), _p(v, _f64p)), "project")
     return qk, v
+
+
+def backward(qk, v, R, dout, n_buckets: int, chunk_len: int, causal: bool):
+    """G1: (dqk, dv), both [B, H, L, d], for a loss whose gradient with
+    respect to the forward's output is dout [B, H, L, d]."""
+    qk = _f64(qk)
+    v = _f64(v)
+    R = _f64(R)
+    dout = _f64(dout)
+    B, H, L, d = qk.shape
+    nh = R.shape[0]
+    dqk = np.zeros((B, H, L, d))
+    dv = np.zeros((B, H, L, d))
+    _check(_load().oracle_backward(_p(qk, _f64p), _p(v, _f64p), _p(R, _f64p), _p(dout, _f64p),
+                                   B, H, L, d, n_buckets, nh, chunk_len, int(bool(causal)),
+                                   _p(dqk, _f64p), _p(dv, _f64p)), "backward")
+    return dqk, dv

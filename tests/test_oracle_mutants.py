@@ -54,6 +54,11 @@ MUTANTS = {
         "double *qo = qk + (((int64_t)b * H + h) * L + l) * d;",
         "double *qo = qk + (((int64_t)b * L + l) * H + h) * d;"),
     "project_v_from_qk_weights": ("sv += xr[k] * wv[k];", "sv += xr[k] * wq[k];"),
+    "backward_no_key_gradient": ("gx[j * d + k] += ds * scale * xi[k];", "(void)0;"),
+    "backward_round_lse_as_normaliser": ("const double p = exp(sc - z[i]);",
+                                         "const double p = exp(sc - ls[(int64_t)r * L + s]);"),
+    "backward_no_D_term": ("const double ds = p * (gdv - dd[i]);", "const double ds = p * gdv;"),
+    "backward_dv_to_query": ("gv[j * d + k] += p * gi[k];", "gv[i * d + k] += p * gi[k];"),
 }
 
 

@@ -386,3 +386,80 @@ def test_project_matches_einsum(oracle_mod):
     ref_v = np.einsum("blk,hek->bhle", x, w_v.reshape(H, d, dm))
     assert np.allclose(qk, ref_qk, rtol=1e-12, atol=1e-12)
     assert np.allclose(v, ref_v, rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- G1 backward
+
+def _fd_case(rng, B, H, L, d, nh, nb):
+    qk = rng.standard_normal((B, H, L, d))
+    v = rng.standard_normal((B, H, L, d))
+    R = rng.standard_normal((nh, d, nb // 2))
+    g = rng.standard_normal((B, H, L, d))
+    return qk, v, R, g
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_matches_finite_differences(oracle_mod, causal):
+    """G1: the gradient of sum(dout * forward) by central differences of the
+    oracle's own forward (the hash is piecewise constant: perturbations that
+    move a bucket are skipped and counted)."""
+    rng = np.random.default_rng(60 + causal)
+    B, H, L, d, nh, nb, m = 1, 2, 16, 6, 3, 4, 4
+    qk, v, R, g = _fd_case(rng, B, H, L, d, nh, nb)
+    dqk, dv = oracle_mod.backward(qk, v, R, g, nb, m, causal)
+    base_b = oracle_mod.forward(qk, v, R, nb, m, causal, return_all=True)[1]["buckets"]
+    eps = 1e-6
+    skipped = 0
+    for which, arr, grad in (("qk", qk, dqk), ("v", v, dv)):
+        for idx in np.ndindex(arr.shape):
+            vals = []
+            for sgn in (1.0, -1.0):
+                a = arr.copy()
+                a[idx] += sgn * eps
+                args = (a, v) if which == "qk" else (qk, a)
+                out, extra = oracle_mod.forward(*args, R, nb, m, causal, return_all=True)
+                vals.append((float((g * out).sum()), np.array_equal(extra["buckets"], base_b)))
+            if not (vals[0][1] and vals[1][1]):
+                skipped += 1
+                continue
+            num = (vals[0][0] - vals[1][0]) / (2 * eps)
+            assert abs(num - grad[idx]) <= 1e-6 * (1.0 + abs(grad[idx])), (which, idx)
+    assert skipped <= 4
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_one_bucket_matches_torch_autograd(oracle_mod, causal):
+    """G1: all tokens in one bucket and one chunk: the gradients of plain
+    softmax attention with queries = keys, from torch's autograd in float64."""
+    rng = np.random.default_rng(62 + causal)
+    L, d = 24, 8
+    x = rng.standard_normal((L, d))
+    x[:, 0] = np.abs(x[:, 0]) + 0.1
+    v = rng.standard_normal((L, d))
+    g = rng.standard_normal((L, d))
+    R = np.zeros((1, d, 1))
+    R[0, 0, 0] = 1.0
+    dqk, dv = oracle_mod.backward(x[None, None], v[None, None], R, g[None, None], 2, L, causal)
+    xt = torch.from_numpy(x).requires_grad_(True)
+    vt = torch.from_numpy(v).requires_grad_(True)
+    mask = torch.zeros(L, L, dtype=torch.float64)
+    mask.fill_diagonal_(-brute.SELF_PENALTY)
+    if causal:
+        mask.masked_fill_(torch.ones(L, L, dtype=torch.bool).triu(1), float("-inf"))
+    s = xt @ xt.T / math.sqrt(d) + mask
+    out = torch.softmax(s, dim=1) @ vt
+    (out * torch.from_numpy(g)).sum().backward()
+    np.testing.assert_allclose(dqk[0, 0], xt.grad.numpy(), rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(dv[0, 0], vt.grad.numpy(), rtol=1e-9, atol=1e-11)
+
+
+def test_backward_duplicated_round(oracle_mod):
+    """G1: a round repeated ([R0, R0]) doubles every multiplicity uniformly, so
+    the gradients equal those of [R0] alone."""
+    rng = np.random.default_rng(64)
+    qk, v, R, g = _fd_case(rng, 1, 2, 32, 8, 1, 8)
+    a = oracle_mod.backward(qk, v, R, g, 8, 8, True)
+    b = oracle_mod.backward(qk, v, np.concatenate([R, R]), g, 8, 8, True)
+    # equal up to double rounding of sums taken in a different order
+    np.testing.assert_allclose(a[0], b[0], rtol=1e-9, atol=1e-9)
+    np.testing.assert_allclose(a[1], b[1], rtol=1e-9, atol=1e-9)
