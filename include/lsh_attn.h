@@ -83,9 +83,10 @@ typedef struct lsh_shape {
     int32_t dtype;
 } lsh_shape_t;
 
-/* Bytes of workspace needed by `stage` ("hash", "sort", "fwd" or "fwd_x")
- * for `shape`, written to *bytes (host). Returns LSH_ERR_ARG for an unknown
- * stage or an invalid shape. */
+/* Bytes of workspace needed by `stage` ("hash", "sort", "fwd", "fwd_x",
+ * "state" or "bwd") for `shape`, written to *bytes (host). "state" is the
+ * size of the buffer lsh_attention_fwd_train fills for lsh_attention_bwd.
+ * Returns LSH_ERR_ARG for an unknown stage or an invalid shape. */
 int lsh_workspace_size(const char *stage, const lsh_shape_t *shape, size_t *bytes);
 
 /* Step 1 -- angular LSH over n_hashes rounds (glossary "Atenção LSH";
@@ -177,6 +178,33 @@ int lsh_qkv_project(const void *x, const void *w_qk, const void *w_v, const lsh_
 int lsh_attention_fwd_x(const void *x, const void *w_qk, const void *w_v, const float *R,
                         const lsh_shape_t *shape, int32_t d_model, void *out, void *ws,
                         size_t ws_bytes, void *stream);
+
+/* Forward for training: lsh_attention_fwd, and the sort it used plus the
+ * log of each position's total partition function are written to `state`
+ * (device memory of at least lsh_workspace_size("state") bytes, owned by
+ * the caller, read by lsh_attention_bwd; its layout is internal to the
+ * library). `ws` is as for lsh_attention_fwd. */
+int lsh_attention_fwd_train(const void *qk, const void *v, const float *R,
+                            const lsh_shape_t *shape, void *out, void *state,
+                            size_t state_bytes, void *ws, size_t ws_bytes, void *stream);
+
+/* Backward of lsh_attention_fwd_train. The hash and the sort are piecewise
+ * constant and carry no gradient; the attention of each position is one
+ * softmax over every (round, key) hit of its rounds' windows (walkthrough
+ * "1 LSH Attention": the union of the rounds' sets), so with P the weight of
+ * a hit, D_i = dout_i . out_i and s = x_i . x_j / sqrt(d):
+ *   dv_j += P dout_i,  dS = P (dout_i . v_j - D_i),
+ *   dqk_i += dS x_j / sqrt(d),  dqk_j += dS x_i / sqrt(d)
+ * (queries and keys are the same vectors, so both terms land in dqk).
+ *   qk, v, out, dout [B,H,L,d] shape->dtype (out as returned by the training
+ *                    forward, dout the gradient of the loss with respect to it)
+ *   state            as filled by lsh_attention_fwd_train for these inputs
+ *   dqk, dv          [B,H,L,d] shape->dtype (out)
+ *   ws               at least lsh_workspace_size("bwd") bytes
+ * Accumulation in float32; deterministic (no atomics). */
+int lsh_attention_bwd(const void *qk, const void *v, const void *out, const void *dout,
+                      const void *state, size_t state_bytes, const lsh_shape_t *shape, void *dqk,
+                      void *dv, void *ws, size_t ws_bytes, void *stream);
 
 /* Message for the last error on the calling thread ("" if none). */
 const char *lsh_last_error(void);

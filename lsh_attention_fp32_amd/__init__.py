@@ -9,17 +9,23 @@ no other implementation to fall back to.
 Low-level functions keep the C names and argument order (tensors in place of
 pointers): ``lsh_workspace_size``, ``lsh_hash``, ``lsh_sort``,
 ``lsh_chunk_attend``, ``lsh_unsort_combine``, ``lsh_attention_fwd``,
-``lsh_attention_fwd_timed``, ``lsh_qkv_project``, ``lsh_attention_fwd_x``.
-The allocating helpers ``hash``, ``sort``, ``chunk_attend``,
-``unsort_combine``, ``attention_fwd``, ``qkv_project`` and
-``attention_fwd_x`` create the outputs and workspaces with torch.
+``lsh_attention_fwd_timed``, ``lsh_qkv_project``, ``lsh_attention_fwd_x``,
+``lsh_attention_fwd_train``, ``lsh_attention_bwd``. The allocating helpers
+``hash``, ``sort``, ``chunk_attend``, ``unsort_combine``, ``attention_fwd``,
+``qkv_project``, ``attention_fwd_x``, ``attention_fwd_train`` and
+``attention_bwd`` create the outputs and workspaces with torch;
+``LSHAttention`` is a torch.autograd.Function over the training forward and
+the backward.
 """
 from ._binding import (  # noqa: F401
     LSH_BF16,
     LSH_F32,
+    LSHAttention,
     LshError,
     Shape,
+    attention_bwd,
     attention_fwd,
+    attention_fwd_train,
     attention_fwd_x,
     chunk_attend,
     hash,
@@ -27,6 +33,8 @@ from ._binding import (  # noqa: F401
     load_library,
     lsh_attention_fwd,
     lsh_attention_fwd_timed,
+    lsh_attention_bwd,
+    lsh_attention_fwd_train,
     lsh_attention_fwd_x,
     lsh_chunk_attend,
     lsh_hash,

@@ -59,9 +59,12 @@ def load_library():
                                             ctypes.POINTER(i32)]
     lib.lsh_qkv_project.argtypes = [vp, vp, vp, sp, i32, vp, vp, vp]
     lib.lsh_attention_fwd_x.argtypes = [vp, vp, vp, vp, sp, i32, vp, vp, sz, vp]
+    lib.lsh_attention_fwd_train.argtypes = [vp, vp, vp, sp, vp, vp, sz, vp, sz, vp]
+    lib.lsh_attention_bwd.argtypes = [vp, vp, vp, vp, vp, sz, sp, vp, vp, vp, sz, vp]
     for name in ("lsh_workspace_size", "lsh_hash", "lsh_sort", "lsh_chunk_attend",
                  "lsh_unsort_combine", "lsh_attention_fwd", "lsh_attention_fwd_timed",
-                 "lsh_qkv_project", "lsh_attention_fwd_x"):
+                 "lsh_qkv_project", "lsh_attention_fwd_x", "lsh_attention_fwd_train",
+                 "lsh_attention_bwd"):
         getattr(lib, name).restype = ctypes.c_int
     lib.lsh_last_error.argtypes = []
     lib.lsh_last_error.restype = ctypes.c_char_p
@@ -173,6 +176,23 @@ def lsh_attention_fwd_x(x, w_qk, w_v, R, shape: Shape, d_model: int, out, ws,
         "lsh_attention_fwd_x")
 
 
+def _nbytes(t):
+    return t.numel() * t.element_size() if t is not None else 0
+
+
+def lsh_attention_fwd_train(qk, v, R, shape: Shape, out, state, ws, stream=None) -> None:
+    _check(load_library().lsh_attention_fwd_train(
+        _ptr(qk), _ptr(v), _ptr(R), ctypes.byref(shape), _ptr(out), _ptr(state), _nbytes(state),
+        _ptr(ws), _nbytes(ws), _stream(stream)), "lsh_attention_fwd_train")
+
+
+def lsh_attention_bwd(qk, v, out, dout, state, shape: Shape, dqk, dv, ws, stream=None) -> None:
+    _check(load_library().lsh_attention_bwd(
+        _ptr(qk), _ptr(v), _ptr(out), _ptr(dout), _ptr(state), _nbytes(state),
+        ctypes.byref(shape), _ptr(dqk), _ptr(dv), _ptr(ws), _nbytes(ws), _stream(stream)),
+        "lsh_attention_bwd")
+
+
 # ---------------------------------------------------------------- allocating helpers
 
 def _workspace(stage: str, shape: Shape, device) -> torch.Tensor:
@@ -270,3 +290,48 @@ def attention_fwd_x(x, w_qk, w_v, R, n_heads: int, n_buckets: int, chunk_len: in
     ws = _workspace("fwd_x", shape, x.device) if ws is None else ws
     lsh_attention_fwd_x(x, w_qk, w_v, R, shape, x.shape[2], out, ws, stream)
     return out
+
+
+def attention_fwd_train(qk, v, R, n_buckets: int, chunk_len: int, causal: bool, stream=None):
+    """Training forward; returns (out [B,H,L,d], state) for attention_bwd."""
+    shape = shape_of(qk, n_buckets, R.shape[0], chunk_len, causal)
+    if v.shape != qk.shape or v.dtype != qk.dtype:
+        raise ValueError("v must match qk in shape and dtype")
+    out = torch.empty_like(qk)
+    state = _workspace("state", shape, qk.device)
+    ws = _workspace("fwd", shape, qk.device)
+    lsh_attention_fwd_train(qk, v, R, shape, out, state, ws, stream)
+    return out, state
+
+
+def attention_bwd(qk, v, out, dout, state, n_buckets: int, n_hashes: int, chunk_len: int,
+                  causal: bool, stream=None):
+    """Returns (dqk, dv) for the output gradient dout (contiguous, qk's dtype)."""
+    shape = shape_of(qk, n_buckets, n_hashes, chunk_len, causal)
+    dout = dout.to(qk.dtype).contiguous()
+    dqk = torch.empty_like(qk)
+    dv = torch.empty_like(v)
+    ws = _workspace("bwd", shape, qk.device)
+    lsh_attention_bwd(qk, v, out, dout, state, shape, dqk, dv, ws, stream)
+    return dqk, dv
+
+
+class LSHAttention(torch.autograd.Function):
+    """out = LSH attention of (qk, v) with rotations R; differentiable in qk
+    and v (the hash and the sort carry no gradient; R gets none).
+    Use: ``LSHAttention.apply(qk, v, R, n_buckets, chunk_len, causal)``."""
+
+    @staticmethod
+    def forward(ctx, qk, v, R, n_buckets, chunk_len, causal):
+        qk = qk.contiguous()
+        v = v.contiguous()
+        out, state = attention_fwd_train(qk, v, R.contiguous(), n_buckets, chunk_len, causal)
+        ctx.save_for_backward(qk, v, out, state)
+        ctx.cfg = (n_buckets, R.shape[0], chunk_len, causal)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        qk, v, out, state = ctx.saved_tensors
+        dqk, dv = attention_bwd(qk, v, out, dout, state, *ctx.cfg)
+        return dqk, dv, None, None, None, None

@@ -103,9 +103,42 @@ int check_ws(const char* stage, const Dims& d, void* ws, size_t ws_bytes, size_t
     return LSH_OK;
 }
 
+// The state a training forward leaves for the backward: bucket ids by
+// position, the sorted keys (packed when the fused path packs them) and Z.
+struct StateLayout {
+    size_t buckets, perm, z, total;
+};
+
+StateLayout state_layout(const Dims& d) {
+    StateLayout s;
+    const size_t n = (size_t)d.segs * d.L;
+    s.buckets = 0;
+    s.perm = align_up(sizeof(int32_t) * n, 256);
+    s.z = s.perm + align_up(sizeof(int32_t) * n, 256);
+    s.total = s.z + align_up(sizeof(float) * (size_t)d.T, 256);
+    return s;
+}
+
+bool fused_packed(const Dims& d) { return compact_o_sorted(d) && packed_sort_keys(d); }
+
+struct BwdLayout {
+    size_t dvec, dx, dv, total;
+};
+
+BwdLayout bwd_layout(const Dims& d) {
+    BwdLayout b;
+    const size_t rows = (size_t)d.T * d.nh * d.d;
+    b.dvec = 0;
+    b.dx = align_up(sizeof(float) * (size_t)d.T, 256);
+    b.dv = b.dx + align_up(sizeof(float) * rows, 256);
+    b.total = b.dv + align_up(sizeof(float) * rows, 256);
+    return b;
+}
+
+// state (or null): where the sort and Z go for a later backward.
 int run_fwd(const void* qk, const void* v, const float* R, const lsh_shape_t* shape, void* out,
             void* ws, size_t ws_bytes, hipStream_t st, hipEvent_t* ev, int* nev,
-            const char** names) {
+            const char** names, void* state = nullptr) {
     const Dims d = make_dims(*shape);
     const FwdLayout f = fwd_layout(d);
     int rc = check_ws("lsh_attention_fwd", d, ws, ws_bytes, f.total);
@@ -113,6 +146,13 @@ int run_fwd(const void* qk, const void* v, const float* R, const lsh_shape_t* sh
     char* base = (char*)ws;
     int32_t* buckets = (int32_t*)(base + f.buckets);
     int32_t* perm = (int32_t*)(base + f.perm);
+    float* z = nullptr;
+    if (state) {
+        const StateLayout sl = state_layout(d);
+        buckets = (int32_t*)((char*)state + sl.buckets);
+        perm = (int32_t*)((char*)state + sl.perm);
+        z = (float*)((char*)state + sl.z);
+    }
     int32_t* inv = (int32_t*)(base + f.inv);
     float* lse = (float*)(base + f.lse);
     const HashWorkspace hw = carve_hash_workspace(base + f.hash, d);
@@ -133,7 +173,7 @@ int run_fwd(const void* qk, const void* v, const float* R, const lsh_shape_t* sh
     if ((e = launch_attend(qk, v, buckets, perm, d, o, lse, st, ev, nev, names, packed)) !=
         hipSuccess)
         return hip_fail(e, "chunk_attend");
-    if ((e = launch_combine(o, lse, inv, d, out, st, ev, nev, names)) != hipSuccess)
+    if ((e = launch_combine(o, lse, inv, d, out, st, ev, nev, names, z)) != hipSuccess)
         return hip_fail(e, "unsort_combine");
     if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "launch");
     return LSH_OK;
@@ -168,7 +208,11 @@ int lsh_workspace_size(const char* stage, const lsh_shape_t* shape, size_t* byte
     else if (!strcmp(stage, "sort")) *bytes = sort_workspace_bytes(d);
     else if (!strcmp(stage, "fwd")) *bytes = fwd_layout(d).total;
     else if (!strcmp(stage, "fwd_x")) *bytes = 2 * projected_bytes(d) + fwd_layout(d).total;
-    else return fail(LSH_ERR_ARG, "unknown stage '%s' (hash, sort, fwd or fwd_x)", stage);
+    else if (!strcmp(stage, "state")) *bytes = state_layout(d).total;
+    else if (!strcmp(stage, "bwd")) *bytes = bwd_layout(d).total;
+    else
+        return fail(LSH_ERR_ARG, "unknown stage '%s' (hash, sort, fwd, fwd_x, state or bwd)",
+                    stage);
     return LSH_OK;
 }
 
@@ -295,6 +339,52 @@ int lsh_attention_fwd_x(const void* x, const void* w_qk, const void* w_v, const 
     hipError_t e = launch_project(x, w_qk, w_v, d, d_model, qk, v, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "lsh_attention_fwd_x: projection");
     return run_fwd(qk, v, R, shape, out, ws, fb, (hipStream_t)stream, nullptr, nullptr, nullptr);
+}
+
+int lsh_attention_fwd_train(const void* qk, const void* v, const float* R,
+                            const lsh_shape_t* shape, void* out, void* state,
+                            size_t state_bytes, void* ws, size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    int rc = validate(shape);
+    if (rc) return rc;
+    if (empty(shape)) return LSH_OK;
+    if (!qk || !v || !R || !out)
+        return fail(LSH_ERR_ARG, "lsh_attention_fwd_train: NULL tensor pointer");
+    if (misaligned({qk, v, R, out}))
+        return fail(LSH_ERR_ARG, "lsh_attention_fwd_train: tensor pointers must be 16-byte aligned");
+    const Dims d = make_dims(*shape);
+    if ((rc = check_ws("lsh_attention_fwd_train (state)", d, state, state_bytes,
+                       state_layout(d).total)))
+        return rc;
+    return run_fwd(qk, v, R, shape, out, ws, ws_bytes, (hipStream_t)stream, nullptr, nullptr,
+                   nullptr, state);
+}
+
+int lsh_attention_bwd(const void* qk, const void* v, const void* out, const void* dout,
+                      const void* state, size_t state_bytes, const lsh_shape_t* shape, void* dqk,
+                      void* dv, void* ws, size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    int rc = validate(shape);
+    if (rc) return rc;
+    if (empty(shape)) return LSH_OK;
+    if (!qk || !v || !out || !dout || !dqk || !dv)
+        return fail(LSH_ERR_ARG, "lsh_attention_bwd: NULL tensor pointer");
+    if (misaligned({qk, v, out, dout, dqk, dv}))
+        return fail(LSH_ERR_ARG, "lsh_attention_bwd: tensor pointers must be 16-byte aligned");
+    const Dims d = make_dims(*shape);
+    const StateLayout sl = state_layout(d);
+    if ((rc = check_ws("lsh_attention_bwd (state)", d, (void*)state, state_bytes, sl.total)))
+        return rc;
+    const BwdLayout bl = bwd_layout(d);
+    if ((rc = check_ws("lsh_attention_bwd", d, ws, ws_bytes, bl.total))) return rc;
+    const char* sb = (const char*)state;
+    char* wb = (char*)ws;
+    BwdArgs a{qk, v, out, dout,
+              (const int32_t*)(sb + sl.perm), (const int32_t*)(sb + sl.buckets),
+              (const float*)(sb + sl.z), (float*)(wb + bl.dvec), (float*)(wb + bl.dx),
+              (float*)(wb + bl.dv), dqk, dv};
+    hipError_t e = launch_backward(a, d, fused_packed(d), (hipStream_t)stream);
+    return e == hipSuccess ? LSH_OK : hip_fail(e, "lsh_attention_bwd");
 }
 
 int lsh_attention_fwd_timed(const void* qk, const void* v, const float* R,

@@ -51,7 +51,7 @@ template <int D, typename T>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o_sorted,
                                                       const float* __restrict__ lse,
                                                       const int32_t* __restrict__ inv, Dims dm,
-                                                      T* __restrict__ out) {
+                                                      T* __restrict__ out, float* __restrict__ z) {
     constexpr int TPT = D / 8;   // threads per token, 8 features each
     constexpr int G = 8;         // rounds whose loads are issued together
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -102,6 +102,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     }
     const float inv_sum = 1.0f / sum;
     store8(out + tok * D + 8 * q, a0 * inv_sum, a1 * inv_sum);
+    if (z && q == 0) z[tok] = mx + logf(sum);
 }
 
 // Fused form: the chunk kernel already stored every round's row of a token
@@ -115,7 +116,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 template <int D, typename T>
 __global__ __launch_bounds__(256) void combine_bypos_kernel(const _Float16* __restrict__ o_pos,
                                                             const uint32_t* __restrict__ vmax,
-                                                            Dims dm, T* __restrict__ out) {
+                                                            Dims dm, T* __restrict__ out,
+                                                            float* __restrict__ z) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     constexpr int TPT = D / 8;   // threads per token, one 16-byte piece each
     constexpr int G = 8;         // rounds whose loads are issued together
@@ -175,34 +177,35 @@ __global__ __launch_bounds__(256) void combine_bypos_kernel(const _Float16* __re
     // the rows carry the power-of-two scale chosen from max|v|
     const float inv_sum = 1.0f / (o_scale(*vmax) * sum);
     store8(out + tok * D + 8 * q, a0 * inv_sum, a1 * inv_sum);
+    if (z && q == 0) z[tok] = (mx + log2f(sum)) * 0.6931471805599453f;   // natural log
 }
 
 template <typename T>
 static void launch_t(const OSorted& o, const float* lse, const int32_t* inv, const Dims& d, T* out,
-                     hipStream_t st) {
+                     float* z, hipStream_t st) {
     const unsigned grid = (unsigned)((d.T * (d.d / 8) + 255) / 256);
     if (o.half) {
         const _Float16* op = (const _Float16*)o.ptr;
         if (d.d == 64)
-            combine_bypos_kernel<64, T><<<grid, 256, 0, st>>>(op, o.vmax, d, out);
+            combine_bypos_kernel<64, T><<<grid, 256, 0, st>>>(op, o.vmax, d, out, z);
         else
-            combine_bypos_kernel<128, T><<<grid, 256, 0, st>>>(op, o.vmax, d, out);
+            combine_bypos_kernel<128, T><<<grid, 256, 0, st>>>(op, o.vmax, d, out, z);
     } else {
         const float* op = (const float*)o.ptr;
         if (d.d == 64)
-            combine_kernel<64, T><<<grid, 256, 0, st>>>(op, lse, inv, d, out);
+            combine_kernel<64, T><<<grid, 256, 0, st>>>(op, lse, inv, d, out, z);
         else
-            combine_kernel<128, T><<<grid, 256, 0, st>>>(op, lse, inv, d, out);
+            combine_kernel<128, T><<<grid, 256, 0, st>>>(op, lse, inv, d, out, z);
     }
 }
 
 hipError_t launch_combine(const OSorted& o, const float* lse_sorted, const int32_t* inv,
                           const Dims& d, void* out, hipStream_t st, hipEvent_t* ev, int* nev,
-                          const char** names) {
+                          const char** names, float* z) {
     if (d.dtype == LSH_BF16)
-        launch_t<uint16_t>(o, lse_sorted, inv, d, (uint16_t*)out, st);
+        launch_t<uint16_t>(o, lse_sorted, inv, d, (uint16_t*)out, z, st);
     else
-        launch_t<float>(o, lse_sorted, inv, d, (float*)out, st);
+        launch_t<float>(o, lse_sorted, inv, d, (float*)out, z, st);
     return mark(st, ev, nev, names, "combine");
 }
 

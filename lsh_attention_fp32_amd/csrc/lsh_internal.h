@@ -137,14 +137,35 @@ hipError_t launch_attend(const void* qk, const void* v, const int32_t* buckets,
                          bool packed = false);
 
 // ----------------------------------------------------------- combine stage
+// z (or null): per token [B,H,L], the natural-log partition function over
+// every round, logsumexp_r lse_r -- what the backward needs besides the sort.
 hipError_t launch_combine(const OSorted& o, const float* lse_sorted, const int32_t* inv,
                           const Dims& d, void* out, hipStream_t st, hipEvent_t* ev, int* nev,
-                          const char** names);
+                          const char** names, float* z = nullptr);
 
 // ----------------------------------------------------- input projections
 // qk, v [B,H,L,d] from x [B,L,d_model] and weights [H*d, d_model].
 hipError_t launch_project(const void* x, const void* w_qk, const void* w_v, const Dims& d,
                           int d_model, void* qk, void* v, hipStream_t st);
+
+// --------------------------------------------------------------- backward
+// Gradients from the saved sort (perm: packed keys when `packed`, else
+// positions with bucket ids by position in `buckets`) and Z per token.
+struct BwdArgs {
+    const void* qk;
+    const void* v;
+    const void* out;
+    const void* dout;
+    const int32_t* perm;      // [B,H,nh,L]
+    const int32_t* buckets;   // [B,H,nh,L] by position
+    const float* z;           // [B,H,L] natural-log total partition function
+    float* Dv;                // [B,H,L] scratch: dout . out
+    float* dx_r;              // [B,H,L,nh,d] scratch: per-round dq + dk
+    float* dv_r;              // [B,H,L,nh,d] scratch: per-round dv
+    void* dqk;                // [B,H,L,d] out
+    void* dv;                 // [B,H,L,d] out
+};
+hipError_t launch_backward(const BwdArgs& a, const Dims& d, bool packed, hipStream_t st);
 
 // Power of two s with max|v| * s <= 2^14: fp16 then holds every |o| <= max|v|.
 __device__ __forceinline__ float o_scale(uint32_t vmax_bf16) {

@@ -35,7 +35,8 @@ def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("lsh_hash", "lsh_sort", "lsh_chunk_attend", "lsh_unsort_combine",
               "lsh_attention_fwd", "lsh_workspace_size", "lsh_last_error",
-              "lsh_attention_fwd_timed", "lsh_qkv_project", "lsh_attention_fwd_x"):
+              "lsh_attention_fwd_timed", "lsh_qkv_project", "lsh_attention_fwd_x",
+              "lsh_attention_fwd_train", "lsh_attention_bwd"):
         assert n in names
 
 
@@ -142,3 +143,17 @@ def test_fwd_x_workspace_holds_the_projected_tensors(lib):
         fwd = lsh.lsh_workspace_size("fwd", s)
         fx = lsh.lsh_workspace_size("fwd_x", s)
         assert fx >= fwd + 2 * s.B * s.H * s.L * s.d * e
+
+
+def test_training_state_and_backward_workspace_sizes(lib):
+    s = _shape()
+    n = s.B * s.H * s.n_hashes * s.L
+    assert lsh.lsh_workspace_size("state", s) >= 8 * n + 4 * s.B * s.H * s.L
+    assert lsh.lsh_workspace_size("bwd", s) >= 2 * 4 * n * s.d + 4 * s.B * s.H * s.L
+
+
+def test_backward_rejects_small_state(lib):
+    s = ctypes.byref(_shape())
+    p = ctypes.c_void_p(0x1000)
+    rc = lib.lsh_attention_bwd(p, p, p, p, p, 16, s, p, p, p, 1 << 40, None)
+    assert rc == -2 and "state" in lsh.lsh_last_error()
