@@ -3,6 +3,7 @@
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 python bench.py --sweep [--dense]     one line per workload (length sweep and the rest)
 python bench.py --project             input projections (d_model 1024) and the forward from x
+python bench.py --train               training forward and backward
 
 A step is one lsh_attention_fwd (hash -> sort -> chunk attention -> combine)
 over one batch of synthetic input already resident in HBM. The default
@@ -182,6 +183,50 @@ def measure_projection(lsh, torch, w, steps, warmup, d_model=1024):
             "fwd_x_ms": f_ms, "fwd_x_tokens_per_s": w.B * w.L / (f_ms / 1e3)}
 
 
+def measure_training(lsh, torch, w, steps, warmup):
+    """lsh_attention_fwd_train and lsh_attention_bwd at the workload's shape;
+    the backward's work is counted per (query, window key) pair: the score
+    and g . v recomputed, then dq, dk and dv, 10 d flops."""
+    import workloads
+
+    dev = torch.device("cuda:0")
+    qk, v, R = workloads.make_inputs(w)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    qk_t = torch.from_numpy(qk).to(dev, dt)
+    v_t = torch.from_numpy(v).to(dev, dt)
+    R_t = torch.from_numpy(R).to(dev)
+    g_t = torch.randn(qk_t.shape, generator=torch.Generator().manual_seed(w.seed)).to(dev, dt)
+    shape = lsh.shape_of(qk_t, w.n_buckets, w.n_hashes, w.chunk_len, w.causal)
+    out = torch.empty_like(qk_t)
+    state = torch.empty(lsh.lsh_workspace_size("state", shape), dtype=torch.uint8, device=dev)
+    ws = torch.empty(lsh.lsh_workspace_size("fwd", shape), dtype=torch.uint8, device=dev)
+    bws = torch.empty(lsh.lsh_workspace_size("bwd", shape), dtype=torch.uint8, device=dev)
+    dqk = torch.empty_like(qk_t)
+    dv = torch.empty_like(v_t)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    f_ms = timed(lambda: lsh.lsh_attention_fwd_train(qk_t, v_t, R_t, shape, out, state, ws))
+    b_ms = timed(lambda: lsh.lsh_attention_bwd(qk_t, v_t, out, g_t, state, shape, dqk, dv, bws))
+    T = w.B * w.H * w.L
+    pairs = T * w.n_hashes * (2 * w.chunk_len - w.chunk_len * w.chunk_len / w.L)
+    flops = 10.0 * w.d * pairs
+    return {"workload": w.name, "fwd_train_ms": f_ms, "bwd_ms": b_ms,
+            "train_step_tokens_per_s": w.B * w.L / ((f_ms + b_ms) / 1e3),
+            "bwd_pair_flops": flops, "bwd_tflops": flops / b_ms / 1e9,
+            "bwd_frac_fp32_vector": flops / b_ms / 1e9 / PEAK_FP32_TFLOPS}
+
+
 def dense_comparator(torch, w, qk_t, v_t, steps=10):
     """PyTorch SDPA at the same shape (queries = keys = qk), flash or
     memory-efficient backend only; None when neither takes the shape."""
@@ -268,6 +313,8 @@ def main() -> int:
                     help="with --sweep: also time torch's dense SDPA at each shape")
     ap.add_argument("--project", action="store_true",
                     help="time the input projections and the forward that starts from x")
+    ap.add_argument("--train", action="store_true",
+                    help="time the training forward and the backward")
     args = ap.parse_args()
     if args.copy_calibration:
         import torch
@@ -304,6 +351,11 @@ def main() -> int:
             del r
             torch.cuda.empty_cache()
             print(json.dumps(line), flush=True)
+        return 0
+
+    if args.train:
+        print(json.dumps(measure_training(lsh, torch, workloads.WORKLOADS[
+            args.workload or workloads.HEADLINE], min(args.steps, 10), args.warmup)), flush=True)
         return 0
 
     if args.project:

@@ -23,6 +23,8 @@
 //               (each row is owned by one quad of lanes), dv is written to a
 //               second set of rows;
 //   bwd_reduce  sums each position's rows over the rounds into dqk and dv.
+// With bf16 I/O and chunk 64 one matrix-core kernel (bwd_mfma) replaces the
+// two middle passes and writes bf16 rows.
 // Four lanes share a query (or key), each holding a quarter of its features;
 // dot products are summed across the quad.
 //
@@ -314,10 +316,19 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(const T* __restrict__ qk,
     }
 }
 
-// dqk_i = sum_r dx_r[i], dv_i = sum_r dv_r[i]; one thread per (token, 4 features).
-template <int D, typename T>
-__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict__ dx_r,
-                                                         const float* __restrict__ dv_r, Dims dm,
+// Four consecutive values of a per-round row, as float32.
+__device__ __forceinline__ f32x4 load_row4(const float* p) { return *(const f32x4*)p; }
+__device__ __forceinline__ f32x4 load_row4(const uint16_t* p) {
+    const uint2 w = *(const uint2*)p;
+    return (f32x4){__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                   __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
+}
+
+// dqk_i = sum_r dx_r[i], dv_i = sum_r dv_r[i]; one thread per (token, 4
+// features). Rows are float32 (plain passes) or bf16 (matrix-core pass).
+template <int D, typename T, typename RowT>
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const RowT* __restrict__ dx_r,
+                                                         const RowT* __restrict__ dv_r, Dims dm,
                                                          T* __restrict__ dqk, T* __restrict__ dv) {
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t tok = gid / (D / 4);
@@ -326,13 +337,316 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict
     f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
     for (int r = 0; r < dm.nh; ++r) {
         const int64_t row = (tok * dm.nh + r) * D + e;
-        a += *(const f32x4*)(dx_r + row);
-        b += *(const f32x4*)(dv_r + row);
+        a += load_row4(dx_r + row);
+        b += load_row4(dv_r + row);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         IO<T>::store(dqk, tok * D + e + i, a[i]);
         IO<T>::store(dv, tok * D + e + i, b[i]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core passes (bf16 I/O, chunk 64), v_mfma_f32_16x16x32_bf16 with fp32
+// accumulation. Lane layout: A[m][k] in lane m%16 + 16*(k/8), element k%8;
+// B[k][n] in lane n + 16*(k/8); D[m][n] in lane n + 16*(m/4), register m%4.
+// A 16 x 16 score tile whose rows are the "other side" (keys in the query
+// pass, queries in the key pass) takes row m from item
+// 32 kb + 8 (m / 4) + 4 h + m % 4 of a 32-item block kb (h = 0, 1 the two
+// tiles of the block): a lane then holds 8 consecutive items of the block,
+// exactly the B-operand layout of the next product, so weights go from the
+// score registers into the next matrix instruction without leaving the lane.
+// The weights and dS are rounded to bf16 for those products.
+constexpr int kBM = 64;   // chunk length of the matrix-core passes
+
+template <int D>
+struct BwdRows {
+    static constexpr int RS = D + 8;     // padded row (bf16): rows 4 banks apart
+    static constexpr int TS = kBM + 8;   // padded transposed row (bf16)
+};
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Gathers the 64 rows of sorted slots [t0, t0 + 64) of one segment: row-major
+// into `rm` ([64][RS]) and, when `tr` is given, transposed into `tr` ([D][TS]);
+// positions and bucket ids into pos / bkt (when given). Rows past the segment
+// (no chunk) are zero with bucket -1.
+template <int D, bool PACKED>
+__device__ __forceinline__ void stage_rows(const uint16_t* __restrict__ src,
+                                           const int32_t* __restrict__ P,
+                                           const int32_t* __restrict__ Bk, int64_t t0, bool exists,
+                                           uint16_t (*rm)[BwdRows<D>::RS],
+                                           uint16_t (*tr)[BwdRows<D>::TS], int32_t* pos,
+                                           int32_t* bkt, int32_t* spos) {
+    const int tid = threadIdx.x;
+    if (tid < kBM) {
+        int32_t p = 0, b = -1;
+        if (exists) read_key<PACKED>(P, Bk, t0 + tid, p, b);
+        spos[tid] = exists ? p : -1;
+        if (pos) pos[tid] = p;
+        if (bkt) bkt[tid] = b;
+    }
+    __syncthreads();
+    // row-major: 64 rows x D/8 pieces of 16 bytes
+    for (int i = tid; i < kBM * (D / 8); i += 256) {
+        const int row = i / (D / 8), pc = i % (D / 8);
+        const int32_t p = spos[row];
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (p >= 0) w = *(const u32x4*)(src + (int64_t)p * D + pc * 8);
+        *(u32x4*)&rm[row][pc * 8] = w;
+    }
+    if (tr) {
+        // transposed: a thread takes rows 2 pr, 2 pr + 1 and 8 features
+        for (int i = tid; i < (kBM / 2) * (D / 8); i += 256) {
+            const int pr = i % (kBM / 2), fg = i / (kBM / 2);
+            const int32_t p0 = spos[2 * pr], p1 = spos[2 * pr + 1];
+            u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+            if (p0 >= 0) a = *(const u32x4*)(src + (int64_t)p0 * D + fg * 8);
+            if (p1 >= 0) b = *(const u32x4*)(src + (int64_t)p1 * D + fg * 8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t lo = (a[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                const uint32_t hi = (b[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                *(uint32_t*)&tr[fg * 8 + e][2 * pr] = lo | (hi << 16);
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const bf16x2 w = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, w);
+}
+
+// Transposes the 64 rows of `rm` into `tr` ([D][TS]) inside LDS: a thread
+// takes two rows and 8 features and writes them as 8 words of two values.
+template <int D>
+__device__ __forceinline__ void transpose_rows(const uint16_t (*rm)[BwdRows<D>::RS],
+                                               uint16_t (*tr)[BwdRows<D>::TS]) {
+    for (int i = threadIdx.x; i < (kBM / 2) * (D / 8); i += 256) {
+        const int pr = i % (kBM / 2), fg = i / (kBM / 2);
+        const u32x4 a = *(const u32x4*)&rm[2 * pr][fg * 8];
+        const u32x4 b = *(const u32x4*)&rm[2 * pr + 1][fg * 8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t lo = (a[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+            const uint32_t hi = (b[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+            *(uint32_t*)&tr[fg * 8 + e][2 * pr] = lo | (hi << 16);
+        }
+    }
+}
+
+template <int D>
+struct BwdLds {
+    uint16_t ra[kBM][BwdRows<D>::RS];   // rows of the other side: qk
+    uint16_t rb[kBM][BwdRows<D>::RS];   // its values (query pass) or output gradients (key pass)
+    uint16_t ta[D][BwdRows<D>::TS];     // ra transposed
+    uint16_t tb[D][BwdRows<D>::TS];     // rb transposed
+    int32_t apos[kBM], abkt[kBM], spos[kBM];
+    float az[kBM], ad[kBM];             // Z and D of ra's rows (as queries)
+};
+
+// One workgroup per (round, chunk c): the chunk's 64 slots are at once the
+// queries of the pairs (c, c - 1), (c, c) and the keys of the pairs (c, c),
+// (c + 1, c), so it produces dq, dk and dv of those slots. Wave w owns slots
+// 16 w .. 16 w + 15; their qk, v and dout fragments stay in registers. Query
+// side (the chunk's slots as queries, keys of chunk kc on rows):
+//   S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ^T += K^T dS^T;
+// key side (the chunk's slots as keys, queries of chunk qc on rows):
+//   S = Q K^T, dP = dO V^T, dS = P (dP - D), dK^T += Q^T dS, dV^T += dO^T P.
+// A slot's dq and dk land in the same lane and register, so dq + dk and dv
+// are written once to the per-round rows.
+template <int D, bool PACKED>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_mfma_kernel(const uint16_t* __restrict__ qk,
+                                                       const uint16_t* __restrict__ v,
+                                                       const uint16_t* __restrict__ g,
+                                                       const int32_t* __restrict__ perm,
+                                                       const int32_t* __restrict__ buckets,
+                                                       const float* __restrict__ z,
+                                                       const float* __restrict__ Dv, Dims dm,
+                                                       uint16_t* __restrict__ dx_r,
+                                                       uint16_t* __restrict__ dv_r) {
+    constexpr int KSTEPS = D / 32, DT = D / 16;
+    __shared__ BwdLds<D> sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int gq = lane >> 4, r16 = lane & 15;
+    const int64_t seg = blockIdx.y;
+    const int c = blockIdx.x;
+    const int nchunks = dm.L / kBM;
+    const int64_t L = dm.L;
+    const int64_t bh = seg / dm.nh;
+    const int r = (int)(seg - bh * dm.nh);
+    const int32_t* P = perm + seg * L;
+    const int32_t* Bk = buckets + seg * L;
+    const uint16_t* X = qk + bh * L * D;
+    const uint16_t* V = v + bh * L * D;
+    const uint16_t* G = g + bh * L * D;
+    const float c2 = kLog2e / sqrtf((float)D);
+    const float pen2 = kSelfPenalty * kLog2e;
+    const float inv_nh = 1.0f / (float)dm.nh;
+
+    // rows of chunk ch into ra (with positions, buckets, Z and D) and the
+    // rows of `second` into rb; ra (and rb) transposed when asked
+    auto stage = [&](int ch, const uint16_t* second, bool trb) {
+        __syncthreads();   // every wave is done with the buffers
+        stage_rows<D, PACKED>(X, P, Bk, (int64_t)ch * kBM, true, sm.ra, nullptr, sm.apos,
+                              sm.abkt, sm.spos);
+        if (tid < kBM) {
+            const int32_t p = sm.spos[tid];
+            sm.az[tid] = z[bh * L + p];
+            sm.ad[tid] = Dv[bh * L + p];
+        }
+        __syncthreads();
+        stage_rows<D, PACKED>(second, P, Bk, (int64_t)ch * kBM, true, sm.rb, nullptr, nullptr,
+                              nullptr, sm.spos);
+        __syncthreads();
+        transpose_rows<D>(sm.ra, sm.ta);
+        if (trb) transpose_rows<D>(sm.rb, sm.tb);
+        __syncthreads();
+    };
+
+    // ---- the chunk itself: qk into ra, v into rb
+    stage(c, V, false);
+    const int me = 16 * wave + r16;   // this lane's slot within the chunk
+    const int32_t mpos = sm.apos[me], mbkt = sm.abkt[me];
+    const float mz = sm.az[me], mz2 = mz * kLog2e, mD = sm.ad[me];
+    const bool mself_only = mz < -0.5f * kSelfPenalty;
+    bf16x8 xf[KSTEPS], vf[KSTEPS], gf[KSTEPS];
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+        xf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.ra[me][32 * s + 8 * gq]);
+        vf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.rb[me][32 * s + 8 * gq]);
+        gf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(G + (int64_t)mpos * D + 32 * s + 8 * gq));
+    }
+    f32x4 dq[DT], dk[DT], dvv[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) dq[dt] = dk[dt] = dvv[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    // query side against the keys in ra (values in rb, keys transposed in ta)
+    auto query_side = [&]() {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            u32x4 dsfrag;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int kw = 32 * kb + 8 * (r16 >> 2) + 4 * h + (r16 & 3);
+                f32x4 sacc = {0.f, 0.f, 0.f, 0.f}, pacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < KSTEPS; ++s) {
+                    const bf16x8 ka = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.ra[kw][32 * s + 8 * gq]);
+                    const bf16x8 va = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.rb[kw][32 * s + 8 * gq]);
+                    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, xf[s], sacc, 0, 0, 0);
+                    pacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, gf[s], pacc, 0, 0, 0);
+                }
+                float ds[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {   // key 32 kb + 8 gq + 4 h + i
+                    const int key = 32 * kb + 8 * gq + 4 * h + i;
+                    const int32_t kp = sm.apos[key];
+                    const bool ok = sm.abkt[key] == mbkt && (!dm.causal || kp <= mpos);
+                    const float s2 = sacc[i] * c2 - (kp == mpos ? pen2 : 0.f);
+                    const float pw = pair_weight(ok, kp == mpos, s2, mz2, mself_only, inv_nh);
+                    ds[i] = pw * (pacc[i] - mD);
+                }
+                dsfrag[2 * h] = pack_bf16x2(ds[0], ds[1]);
+                dsfrag[2 * h + 1] = pack_bf16x2(ds[2], ds[3]);
+            }
+            const bf16x8 bd = __builtin_bit_cast(bf16x8, dsfrag);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const bf16x8 af = __builtin_bit_cast(
+                    bf16x8, *(const u32x4*)&sm.ta[dt * 16 + r16][32 * kb + 8 * gq]);
+                dq[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bd, dq[dt], 0, 0, 0);
+            }
+        }
+    };
+    // key side against the queries in ra (output gradients in rb, both
+    // transposed in ta, tb)
+    auto key_side = [&]() {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            u32x4 pfrag, dsfrag;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int qw = 32 * qb + 8 * (r16 >> 2) + 4 * h + (r16 & 3);
+                f32x4 sacc = {0.f, 0.f, 0.f, 0.f}, pacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < KSTEPS; ++s) {
+                    const bf16x8 qa = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.ra[qw][32 * s + 8 * gq]);
+                    const bf16x8 ga = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.rb[qw][32 * s + 8 * gq]);
+                    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, xf[s], sacc, 0, 0, 0);
+                    pacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga, vf[s], pacc, 0, 0, 0);
+                }
+                float pw[4], ds[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {   // query 32 qb + 8 gq + 4 h + i
+                    const int q = 32 * qb + 8 * gq + 4 * h + i;
+                    const int32_t qp = sm.apos[q];
+                    const float zq = sm.az[q];
+                    const bool ok = sm.abkt[q] == mbkt && (!dm.causal || mpos <= qp);
+                    const float s2 = sacc[i] * c2 - (mpos == qp ? pen2 : 0.f);
+                    pw[i] = pair_weight(ok, mpos == qp, s2, zq * kLog2e,
+                                        zq < -0.5f * kSelfPenalty, inv_nh);
+                    ds[i] = pw[i] * (pacc[i] - sm.ad[q]);
+                }
+                pfrag[2 * h] = pack_bf16x2(pw[0], pw[1]);
+                pfrag[2 * h + 1] = pack_bf16x2(pw[2], pw[3]);
+                dsfrag[2 * h] = pack_bf16x2(ds[0], ds[1]);
+                dsfrag[2 * h + 1] = pack_bf16x2(ds[2], ds[3]);
+            }
+            const bf16x8 bp = __builtin_bit_cast(bf16x8, pfrag);
+            const bf16x8 bd = __builtin_bit_cast(bf16x8, dsfrag);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const bf16x8 aq = __builtin_bit_cast(
+                    bf16x8, *(const u32x4*)&sm.ta[dt * 16 + r16][32 * qb + 8 * gq]);
+                const bf16x8 ag = __builtin_bit_cast(
+                    bf16x8, *(const u32x4*)&sm.tb[dt * 16 + r16][32 * qb + 8 * gq]);
+                dk[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, bd, dk[dt], 0, 0, 0);
+                dvv[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag, bp, dvv[dt], 0, 0, 0);
+            }
+        }
+    };
+
+    // pair (c, c), query side: keys = the chunk (ra), values (rb)
+    __syncthreads();
+    transpose_rows<D>(sm.ra, sm.ta);
+    __syncthreads();
+    query_side();
+    // pair (c, c), key side: queries = the chunk (ra), output gradients into rb
+    __syncthreads();
+    stage_rows<D, PACKED>(G, P, Bk, (int64_t)c * kBM, true, sm.rb, nullptr, nullptr, nullptr,
+                          sm.spos);
+    __syncthreads();
+    transpose_rows<D>(sm.rb, sm.tb);
+    __syncthreads();
+    key_side();
+    // pair (c, c - 1): the previous chunk's keys and values
+    if (c > 0) {
+        stage(c - 1, V, false);
+        query_side();
+    }
+    // pair (c + 1, c): the next chunk's queries and output gradients
+    if (c + 1 < nchunks) {
+        stage(c + 1, G, true);
+        key_side();
+    }
+    // lane (slot me, group gq) holds features 16 dt + 4 gq + i of dq, dk, dv;
+    // the per-round rows are bf16 (one rounding, 2^-9 relative, before the
+    // float32 sum over rounds)
+    const float scale = 1.0f / sqrtf((float)D);
+    const int64_t row = ((bh * L + mpos) * dm.nh + r) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+        const f32x4 x = (dq[dt] + dk[dt]) * scale;
+        const f32x4 y = dvv[dt];
+        *(uint2*)(dx_r + row + 16 * dt + 4 * gq) =
+            make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
+        *(uint2*)(dv_r + row + 16 * dt + 4 * gq) =
+            make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
     }
 }
 
@@ -343,6 +657,19 @@ hipError_t launch_bwd_t(const BwdArgs& a, const Dims& d, hipStream_t st) {
     const T* g = (const T*)a.dout;
     const unsigned gq = (unsigned)((d.T * 4 + 255) / 256);
     bwd_dot_kernel<D, T><<<gq, 256, 0, st>>>(g, (const T*)a.out, d, a.Dv);
+    if constexpr (sizeof(T) == 2) {
+        if (d.m == kBM) {   // matrix-core passes
+            const dim3 grid((unsigned)(d.L / kBM), (unsigned)d.segs);
+            uint16_t* hx = (uint16_t*)a.dx_r;
+            uint16_t* hv = (uint16_t*)a.dv_r;
+            bwd_mfma_kernel<D, PACKED><<<grid, 256, 0, st>>>(qk, v, g, a.perm, a.buckets, a.z,
+                                                             a.Dv, d, hx, hv);
+            const unsigned gr = (unsigned)((d.T * (D / 4) + 255) / 256);
+            bwd_reduce_kernel<D, T, uint16_t><<<gr, 256, 0, st>>>(hx, hv, d, (T*)a.dqk,
+                                                                  (T*)a.dv);
+            return hipGetLastError();
+        }
+    }
     const int nqb = (d.m + 63) / 64;
     const dim3 grid((unsigned)((int64_t)(d.L / d.m) * nqb), (unsigned)d.segs);
     bwd_dq_kernel<D, T, PACKED><<<grid, 256, 0, st>>>(qk, v, g, a.perm, a.buckets, a.z, a.Dv, d,
@@ -350,7 +677,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, const Dims& d, hipStream_t st) {
     bwd_dkv_kernel<D, T, PACKED><<<grid, 256, 0, st>>>(qk, v, g, a.perm, a.buckets, a.z, a.Dv, d,
                                                        nqb, a.dx_r, a.dv_r);
     const unsigned gr = (unsigned)((d.T * (D / 4) + 255) / 256);
-    bwd_reduce_kernel<D, T><<<gr, 256, 0, st>>>(a.dx_r, a.dv_r, d, (T*)a.dqk, (T*)a.dv);
+    bwd_reduce_kernel<D, T, float><<<gr, 256, 0, st>>>(a.dx_r, a.dv_r, d, (T*)a.dqk, (T*)a.dv);
     return hipGetLastError();
 }
 
