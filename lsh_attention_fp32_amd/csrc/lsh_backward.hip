@@ -363,12 +363,25 @@ constexpr int kBM = 64;   // chunk length of the matrix-core passes
 template <int D>
 struct BwdRows {
     static constexpr int RS = D + 8;     // padded row (bf16): rows 4 banks apart
-    static constexpr int TS = kBM + 8;   // padded transposed row (bf16)
+#ifndef LSH_BWD_TS
+#define LSH_BWD_TS (kBM + 8)
+#endif
+    static constexpr int TS = LSH_BWD_TS;   // padded transposed row (bf16)
 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// LDS row of item j (of a 64-item chunk) in the row-major buffers of the
+// fused kernel. A score tile (block kb, half h) reads item
+// 32 kb + 8 a + 4 h + b in lane 4 a + b; storing that item at row
+// 32 kb + 16 h + 4 a + b makes the 16 lanes of a tile read 16 consecutive
+// rows (rows 4 banks apart), where the item order would put rows 8 items
+// apart on the same banks.
+__device__ __forceinline__ int phys_row(int j) {
+    return (j & ~31) | (((j >> 3) & 3) << 2) | (((j >> 2) & 1) << 4) | (j & 3);
+}
 
 // Gathers the 64 rows of sorted slots [t0, t0 + 64) of one segment: row-major
 // into `rm` ([64][RS]) and, when `tr` is given, transposed into `tr` ([D][TS]);
@@ -421,32 +434,32 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, w);
 }
 
-// Transposes the 64 rows of `rm` into `tr` ([D][TS]) inside LDS: a thread
-// takes two rows and 8 features and writes them as 8 words of two values.
+// Transposes the 64 rows of `rm` (stored at phys_row(item)) into `tr`
+// ([D][TS], item order) inside LDS. The 64 lanes of a wave take the 64 items
+// at one 8-feature piece: the 16-byte reads land on distinct banks and each
+// of the 8 two-byte writes covers 128 contiguous bytes of a transposed row.
 template <int D>
-__device__ __forceinline__ void transpose_rows(const uint16_t (*rm)[BwdRows<D>::RS],
-                                               uint16_t (*tr)[BwdRows<D>::TS]) {
-    for (int i = threadIdx.x; i < (kBM / 2) * (D / 8); i += 256) {
-        const int pr = i % (kBM / 2), fg = i / (kBM / 2);
-        const u32x4 a = *(const u32x4*)&rm[2 * pr][fg * 8];
-        const u32x4 b = *(const u32x4*)&rm[2 * pr + 1][fg * 8];
+__device__ __forceinline__ void transpose_items(const uint16_t (*rm)[BwdRows<D>::RS],
+                                                uint16_t (*tr)[BwdRows<D>::TS]) {
+    const int item = threadIdx.x & (kBM - 1);
+    const int row = phys_row(item);
+    for (int pc = threadIdx.x >> 6; pc < D / 8; pc += 256 / kBM) {
+        const u32x4 a = *(const u32x4*)&rm[row][pc * 8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t lo = (a[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-            const uint32_t hi = (b[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-            *(uint32_t*)&tr[fg * 8 + e][2 * pr] = lo | (hi << 16);
-        }
+        for (int e = 0; e < 8; ++e)
+            tr[pc * 8 + e][item] = (uint16_t)((a[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
     }
 }
 
 template <int D>
 struct BwdLds {
     uint16_t ra[kBM][BwdRows<D>::RS];   // rows of the other side: qk
-    uint16_t rb[kBM][BwdRows<D>::RS];   // its values (query pass) or output gradients (key pass)
+    uint16_t rb[kBM][BwdRows<D>::RS];   // its values (query side) or output gradients (key side)
     uint16_t ta[D][BwdRows<D>::TS];     // ra transposed
     uint16_t tb[D][BwdRows<D>::TS];     // rb transposed
-    int32_t apos[kBM], abkt[kBM], spos[kBM];
-    float az[kBM], ad[kBM];             // Z and D of ra's rows (as queries)
+    // chunks c - 1, c, c + 1: position, bucket id, Z and D of each slot
+    int32_t pos[3][kBM], bkt[3][kBM];
+    float zz[3][kBM], dd[3][kBM];
 };
 
 // One workgroup per (round, chunk c): the chunk's 64 slots are at once the
@@ -458,7 +471,9 @@ struct BwdLds {
 // key side (the chunk's slots as keys, queries of chunk qc on rows):
 //   S = Q K^T, dP = dO V^T, dS = P (dP - D), dK^T += Q^T dS, dV^T += dO^T P.
 // A slot's dq and dk land in the same lane and register, so dq + dk and dv
-// are written once to the per-round rows.
+// are written once to the per-round rows. The sorted keys, Z and D of the
+// three chunks are read in one go at the start, and each stage issues its two
+// row gathers together, so a workgroup waits on memory five times in a row.
 template <int D, bool PACKED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_mfma_kernel(const uint16_t* __restrict__ qk,
                                                        const uint16_t* __restrict__ v,
@@ -470,6 +485,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
                                                        uint16_t* __restrict__ dx_r,
                                                        uint16_t* __restrict__ dv_r) {
     constexpr int KSTEPS = D / 32, DT = D / 16;
+    constexpr int PER = kBM * (D / 8) / 256;   // 16-byte pieces per thread and source
     __shared__ BwdLds<D> sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int gq = lane >> 4, r16 = lane & 15;
@@ -488,51 +504,79 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     const float pen2 = kSelfPenalty * kLog2e;
     const float inv_nh = 1.0f / (float)dm.nh;
 
-    // rows of chunk ch into ra (with positions, buckets, Z and D) and the
-    // rows of `second` into rb; ra (and rb) transposed when asked
-    auto stage = [&](int ch, const uint16_t* second, bool trb) {
+    // sorted keys of chunks c - 1, c, c + 1 (index 0, 1, 2); their Z and D
+    // are read together with the first row gather
+    int32_t zpos = -1;
+    if (tid < 3 * kBM) {
+        const int w3 = tid >> 6, j = tid & (kBM - 1);
+        const int ch = c - 1 + w3;
+        int32_t b = -1;
+        if (ch >= 0 && ch < nchunks) read_key<PACKED>(P, Bk, (int64_t)ch * kBM + j, zpos, b);
+        sm.pos[w3][j] = zpos;
+        sm.bkt[w3][j] = b;
+    }
+    __syncthreads();
+
+    // rows of chunk index w3 from sa into ra (unless sa is null: ra keeps
+    // its rows) and from sb into rb, all loads issued before any store, then
+    // the transposes asked for
+    auto stage = [&](int w3, const uint16_t* sa, const uint16_t* sb, bool tra, bool trb) {
+        u32x4 wa[PER], wb[PER];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int i = tid + 256 * k, row = i / (D / 8), pc = i % (D / 8);
+            const int64_t off = (int64_t)sm.pos[w3][row] * D + pc * 8;
+            if (sa) wa[k] = *(const u32x4*)(sa + off);
+            wb[k] = *(const u32x4*)(sb + off);
+        }
         __syncthreads();   // every wave is done with the buffers
-        stage_rows<D, PACKED>(X, P, Bk, (int64_t)ch * kBM, true, sm.ra, nullptr, sm.apos,
-                              sm.abkt, sm.spos);
-        if (tid < kBM) {
-            const int32_t p = sm.spos[tid];
-            sm.az[tid] = z[bh * L + p];
-            sm.ad[tid] = Dv[bh * L + p];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int i = tid + 256 * k, row = phys_row(i / (D / 8)), pc = i % (D / 8);
+            if (sa) *(u32x4*)&sm.ra[row][pc * 8] = wa[k];
+            *(u32x4*)&sm.rb[row][pc * 8] = wb[k];
         }
         __syncthreads();
-        stage_rows<D, PACKED>(second, P, Bk, (int64_t)ch * kBM, true, sm.rb, nullptr, nullptr,
-                              nullptr, sm.spos);
-        __syncthreads();
-        transpose_rows<D>(sm.ra, sm.ta);
-        if (trb) transpose_rows<D>(sm.rb, sm.tb);
-        __syncthreads();
+        if (tra) transpose_items<D>(sm.ra, sm.ta);
+        if (trb) transpose_items<D>(sm.rb, sm.tb);
+        if (tra || trb) __syncthreads();
     };
 
-    // ---- the chunk itself: qk into ra, v into rb
-    stage(c, V, false);
     const int me = 16 * wave + r16;   // this lane's slot within the chunk
-    const int32_t mpos = sm.apos[me], mbkt = sm.abkt[me];
-    const float mz = sm.az[me], mz2 = mz * kLog2e, mD = sm.ad[me];
-    const bool mself_only = mz < -0.5f * kSelfPenalty;
+    const int32_t mpos = sm.pos[1][me], mbkt = sm.bkt[1][me];
     bf16x8 xf[KSTEPS], vf[KSTEPS], gf[KSTEPS];
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-        xf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.ra[me][32 * s + 8 * gq]);
-        vf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.rb[me][32 * s + 8 * gq]);
+    for (int s = 0; s < KSTEPS; ++s)
         gf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(G + (int64_t)mpos * D + 32 * s + 8 * gq));
+    if (tid < 3 * kBM) {
+        const int w3 = tid >> 6, j = tid & (kBM - 1);
+        sm.zz[w3][j] = zpos >= 0 ? z[bh * L + zpos] : 0.f;
+        sm.dd[w3][j] = zpos >= 0 ? Dv[bh * L + zpos] : 0.f;
+    }
+    // ---- the chunk itself: qk into ra (transposed too), v into rb (the
+    // stage's barriers also publish Z and D)
+    stage(1, X, V, true, false);
+    const float mz = sm.zz[1][me], mz2 = mz * kLog2e, mD = sm.dd[1][me];
+    const bool mself_only = mz < -0.5f * kSelfPenalty;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+        xf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.ra[phys_row(me)][32 * s + 8 * gq]);
+        vf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.rb[phys_row(me)][32 * s + 8 * gq]);
     }
     f32x4 dq[DT], dk[DT], dvv[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) dq[dt] = dk[dt] = dvv[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    // query side against the keys in ra (values in rb, keys transposed in ta)
-    auto query_side = [&]() {
+    // query side against the keys of chunk index w3 in ra (values in rb,
+    // keys transposed in ta)
+    auto query_side = [&](int w3) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             u32x4 dsfrag;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const int kw = 32 * kb + 8 * (r16 >> 2) + 4 * h + (r16 & 3);
+                // tile row r16 is item 32 kb + 8 (r16 / 4) + 4 h + r16 % 4
+                const int kw = 32 * kb + 16 * h + r16;   // its LDS row
                 f32x4 sacc = {0.f, 0.f, 0.f, 0.f}, pacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < KSTEPS; ++s) {
@@ -545,8 +589,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {   // key 32 kb + 8 gq + 4 h + i
                     const int key = 32 * kb + 8 * gq + 4 * h + i;
-                    const int32_t kp = sm.apos[key];
-                    const bool ok = sm.abkt[key] == mbkt && (!dm.causal || kp <= mpos);
+                    const int32_t kp = sm.pos[w3][key];
+                    const bool ok = sm.bkt[w3][key] == mbkt && (!dm.causal || kp <= mpos);
                     const float s2 = sacc[i] * c2 - (kp == mpos ? pen2 : 0.f);
                     const float pw = pair_weight(ok, kp == mpos, s2, mz2, mself_only, inv_nh);
                     ds[i] = pw * (pacc[i] - mD);
@@ -563,15 +607,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
             }
         }
     };
-    // key side against the queries in ra (output gradients in rb, both
-    // transposed in ta, tb)
-    auto key_side = [&]() {
+    // key side against the queries of chunk index w3 in ra (output gradients
+    // in rb, both transposed in ta, tb)
+    auto key_side = [&](int w3) {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             u32x4 pfrag, dsfrag;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const int qw = 32 * qb + 8 * (r16 >> 2) + 4 * h + (r16 & 3);
+                // tile row r16 is item 32 qb + 8 (r16 / 4) + 4 h + r16 % 4
+                const int qw = 32 * qb + 16 * h + r16;   // its LDS row
                 f32x4 sacc = {0.f, 0.f, 0.f, 0.f}, pacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < KSTEPS; ++s) {
@@ -584,13 +629,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {   // query 32 qb + 8 gq + 4 h + i
                     const int q = 32 * qb + 8 * gq + 4 * h + i;
-                    const int32_t qp = sm.apos[q];
-                    const float zq = sm.az[q];
-                    const bool ok = sm.abkt[q] == mbkt && (!dm.causal || mpos <= qp);
+                    const int32_t qp = sm.pos[w3][q];
+                    const float zq = sm.zz[w3][q];
+                    const bool ok = sm.bkt[w3][q] == mbkt && (!dm.causal || mpos <= qp);
                     const float s2 = sacc[i] * c2 - (mpos == qp ? pen2 : 0.f);
                     pw[i] = pair_weight(ok, mpos == qp, s2, zq * kLog2e,
                                         zq < -0.5f * kSelfPenalty, inv_nh);
-                    ds[i] = pw[i] * (pacc[i] - sm.ad[q]);
+                    ds[i] = pw[i] * (pacc[i] - sm.dd[w3][q]);
                 }
                 pfrag[2 * h] = pack_bf16x2(pw[0], pw[1]);
                 pfrag[2 * h + 1] = pack_bf16x2(pw[2], pw[3]);
@@ -611,28 +656,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
         }
     };
 
-    // pair (c, c), query side: keys = the chunk (ra), values (rb)
-    __syncthreads();
-    transpose_rows<D>(sm.ra, sm.ta);
-    __syncthreads();
-    query_side();
-    // pair (c, c), key side: queries = the chunk (ra), output gradients into rb
-    __syncthreads();
-    stage_rows<D, PACKED>(G, P, Bk, (int64_t)c * kBM, true, sm.rb, nullptr, nullptr, nullptr,
-                          sm.spos);
-    __syncthreads();
-    transpose_rows<D>(sm.rb, sm.tb);
-    __syncthreads();
-    key_side();
+    // pair (c, c), query side: keys = the chunk (ra, ta), values (rb)
+    query_side(1);
+    // pair (c, c), key side: queries = the chunk (still in ra, ta), output
+    // gradients into rb, tb
+    stage(1, nullptr, G, false, true);
+    key_side(1);
     // pair (c, c - 1): the previous chunk's keys and values
     if (c > 0) {
-        stage(c - 1, V, false);
-        query_side();
+        stage(0, X, V, true, false);
+        query_side(0);
     }
     // pair (c + 1, c): the next chunk's queries and output gradients
     if (c + 1 < nchunks) {
-        stage(c + 1, G, true);
-        key_side();
+        stage(2, X, G, true, true);
+        key_side(2);
     }
     // lane (slot me, group gq) holds features 16 dt + 4 gq + i of dq, dk, dv;
     // the per-round rows are bf16 (one rounding, 2^-9 relative, before the
