@@ -221,10 +221,14 @@ def measure_training(lsh, torch, w, steps, warmup):
     T = w.B * w.H * w.L
     pairs = T * w.n_hashes * (2 * w.chunk_len - w.chunk_len * w.chunk_len / w.L)
     flops = 10.0 * w.d * pairs
+    # bf16 with chunk 64 runs on the matrix cores (bf16 products), else fp32 vector
+    mfma = w.dtype == "bf16" and w.chunk_len == 64
+    peak = PEAK_F16_TFLOPS if mfma else PEAK_FP32_TFLOPS
     return {"workload": w.name, "fwd_train_ms": f_ms, "bwd_ms": b_ms,
             "train_step_tokens_per_s": w.B * w.L / ((f_ms + b_ms) / 1e3),
             "bwd_pair_flops": flops, "bwd_tflops": flops / b_ms / 1e9,
-            "bwd_frac_fp32_vector": flops / b_ms / 1e9 / PEAK_FP32_TFLOPS}
+            "bwd_peak": "bf16 mfma" if mfma else "fp32 vector",
+            "bwd_frac": flops / b_ms / 1e9 / peak}
 
 
 def dense_comparator(torch, w, qk_t, v_t, steps=10):
