@@ -45,6 +45,11 @@
  *   - rounds are combined with weights exp(lse_r - logsumexp_r lse_r), with
  *     no de-duplication of keys seen in several rounds;
  *   - ties in the argmax go to the first (lowest) index, as torch's argmax.
+ * Variant (key_norm = 1): the key side of a score uses the unit vector
+ * x_j / |x_j| ([WALKTHRU] "1 LSH Attention": the formula, stripped on the
+ * page, that makes a key share its query's bucket); queries stay as they are
+ * and the hash is unchanged (it is invariant to positive scaling). A zero
+ * vector keeps a zero key.
  */
 #include <math.h>
 #include <stdint.h>
@@ -179,9 +184,18 @@ int oracle_sort(const int32_t *bucket, int64_t L, int32_t *perm, int32_t *inv)
 /*   o       [L, d]  out, by sorted slot: softmax-weighted sum of v           */
 /*   lse     [L]     out, by sorted slot: natural-log partition function     */
 /* ------------------------------------------------------------------------ */
+/* 1 / |x| (0 for the zero vector): the key scale of the key_norm variant */
+static double inv_norm(const double *x, int d)
+{
+    double s = 0.0;
+    for (int k = 0; k < d; ++k) s += x[k] * x[k];
+    return s > 0.0 ? 1.0 / sqrt(s) : 0.0;
+}
+
 int oracle_attend(const double *x, const double *v, int64_t L, int d,
                   const int32_t *bucket, const int32_t *perm, int m, int causal,
-                  const int64_t *slots, int64_t n_slots, double *o, double *lse)
+                  const int64_t *slots, int64_t n_slots, double *o, double *lse,
+                  int key_norm)
 {
     if (L < 0 || d < 1 || m < 1 || (L % m) != 0) return -1;
     const int64_t n_q = slots ? n_slots : L;
@@ -214,6 +228,7 @@ int oracle_attend(const double *x, const double *v, int64_t L, int d,
                 double dot = 0.0;
                 for (int k = 0; k < d; ++k) dot += xi[k] * xj[k];
                 double sc = dot * scale;
+                if (key_norm) sc *= inv_norm(xj, d);
                 if (j == i) sc -= ORACLE_SELF_PENALTY;
                 score[t - t0] = sc;
                 if (sc > mx) mx = sc;
@@ -295,7 +310,7 @@ int oracle_forward(const double *qk, const double *v, const double *R,
                    int B, int H, int64_t L, int d, int n_buckets, int n_hashes,
                    int chunk_len, int causal, double *out, int32_t *buckets_out,
                    double *margin_out, int32_t *perm_out, int32_t *inv_out,
-                   double *o_sorted_out, double *lse_out)
+                   double *o_sorted_out, double *lse_out, int key_norm)
 {
     if (B < 0 || H < 0 || L < 0 || d < 1 || n_hashes < 1 || chunk_len < 1 ||
         n_buckets < 2 || (n_buckets % 2) != 0 || (L % chunk_len) != 0)
@@ -316,7 +331,7 @@ int oracle_forward(const double *qk, const double *v, const double *R,
             rc = oracle_sort(bk + r * L, L, pm + r * L, iv + r * L);
         for (int r = 0; !rc && r < n_hashes; ++r)
             rc = oracle_attend(x, vv, L, d, bk + r * L, pm + r * L, chunk_len,
-                               causal, NULL, 0, os + r * L * d, ls + r * L);
+                               causal, NULL, 0, os + r * L * d, ls + r * L, key_norm);
         if (!rc)
             rc = oracle_combine(os, ls, iv, n_hashes, L, d, NULL, 0, out + bh * L * d);
         if (!rc) {
@@ -360,7 +375,7 @@ int oracle_forward(const double *qk, const double *v, const double *R,
 /* ------------------------------------------------------------------------ */
 int oracle_backward(const double *qk, const double *v, const double *R, const double *dout,
                     int B, int H, int64_t L, int d, int n_buckets, int n_hashes,
-                    int chunk_len, int causal, double *dqk, double *dv)
+                    int chunk_len, int causal, double *dqk, double *dv, int key_norm)
 {
     if (B < 0 || H < 0 || L < 0 || d < 1 || n_hashes < 1 || chunk_len < 1 ||
         n_buckets < 2 || (n_buckets % 2) != 0 || (L % chunk_len) != 0)
@@ -391,7 +406,7 @@ int oracle_backward(const double *qk, const double *v, const double *R, const do
             rc = oracle_sort(bk + r * L, L, pm + r * L, iv + r * L);
         for (int r = 0; !rc && r < n_hashes; ++r)
             rc = oracle_attend(x, vv, L, d, bk + r * L, pm + r * L, chunk_len, causal, NULL, 0,
-                               os + r * L * d, ls + r * L);
+                               os + r * L * d, ls + r * L, key_norm);
         if (!rc) rc = oracle_combine(os, ls, iv, n_hashes, L, d, NULL, 0, out);
         if (!rc) {
             /* Z_i (log of the total partition function) and D_i */
@@ -433,14 +448,20 @@ int oracle_backward(const double *qk, const double *v, const double *R, const do
                             dot += xi[k] * xj[k];
                             gdv += gi[k] * vj[k];
                         }
-                        double sc = dot * scale;
+                        /* key_norm: s = x_i . x_j rn / sqrt(d), rn = 1 / |x_j|; its
+                           derivative in x_j is rn (x_i - (x_i . x_j) rn^2 x_j) / sqrt(d) */
+                        const double rn = key_norm ? inv_norm(xj, d) : 1.0;
+                        double sc = dot * scale * rn;
                         if (j == i) sc -= ORACLE_SELF_PENALTY;
                         const double p = exp(sc - z[i]);
                         const double ds = p * (gdv - dd[i]);
                         for (int k = 0; k < d; ++k) {
                             gv[j * d + k] += p * gi[k];
-                            gx[i * d + k] += ds * scale * xj[k];
-                            gx[j * d + k] += ds * scale * xi[k];
+                            gx[i * d + k] += ds * scale * rn * xj[k];
+                            if (key_norm)
+                                gx[j * d + k] += ds * scale * rn * (xi[k] - dot * rn * rn * xj[k]);
+                            else
+                                gx[j * d + k] += ds * scale * xi[k];
                         }
                     }
                 }

@@ -59,18 +59,18 @@ def _load():
         lib.oracle_sort.argtypes = [_i32p, ctypes.c_int64, _i32p, _i32p]
         lib.oracle_attend.argtypes = [_f64p, _f64p, ctypes.c_int64, ctypes.c_int, _i32p, _i32p,
                                       ctypes.c_int, ctypes.c_int, _i64p, ctypes.c_int64, _f64p,
-                                      _f64p]
+                                      _f64p, ctypes.c_int]
         lib.oracle_combine.argtypes = [_f64p, _f64p, _i32p, ctypes.c_int, ctypes.c_int64,
                                        ctypes.c_int, _i64p, ctypes.c_int64, _f64p]
         lib.oracle_forward.argtypes = [_f64p, _f64p, _f64p, ctypes.c_int, ctypes.c_int,
                                        ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                        ctypes.c_int, ctypes.c_int, _f64p, _i32p, _f64p, _i32p,
-                                       _i32p, _f64p, _f64p]
+                                       _i32p, _f64p, _f64p, ctypes.c_int]
         lib.oracle_project.argtypes = [_f64p, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
                                        _f64p, _f64p, ctypes.c_int, ctypes.c_int, _f64p, _f64p]
         lib.oracle_backward.argtypes = [_f64p, _f64p, _f64p, _f64p, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                        ctypes.c_int, ctypes.c_int, _f64p, _f64p]
+                                        ctypes.c_int, ctypes.c_int, _f64p, _f64p, ctypes.c_int]
         lib.oracle_threads.argtypes = []
         lib.oracle_threads.restype = ctypes.c_int
         for fn in (lib.oracle_hash, lib.oracle_sort, lib.oracle_attend, lib.oracle_combine,
@@ -130,11 +130,12 @@ def sort(bucket):
     return perm, inv
 
 
-def attend(x, v, bucket, perm, chunk_len: int, causal: bool, slots=None):
+def attend(x, v, bucket, perm, chunk_len: int, causal: bool, slots=None, key_norm=False):
     """O3/O4 for one round. x, v: [L, d]; bucket, perm: [L].
 
     Returns (o [L, d], lse [L]) indexed by sorted slot. With ``slots`` only
-    those query slots are computed; the other rows are NaN.
+    those query slots are computed; the other rows are NaN. ``key_norm``:
+    the key side of each score uses x_j / |x_j|.
     """
     x = _f64(x)
     v = _f64(v)
@@ -146,7 +147,8 @@ def attend(x, v, bucket, perm, chunk_len: int, causal: bool, slots=None):
     sl = None if slots is None else np.ascontiguousarray(np.asarray(slots, dtype=np.int64))
     _check(_load().oracle_attend(_p(x, _f64p), _p(v, _f64p), L, d, _p(bucket, _i32p),
                                  _p(perm, _i32p), chunk_len, int(bool(causal)), _p(sl, _i64p),
-                                 0 if sl is None else sl.shape[0], _p(o, _f64p), _p(lse, _f64p)),
+                                 0 if sl is None else sl.shape[0], _p(o, _f64p), _p(lse, _f64p),
+                                 int(bool(key_norm))),
            "attend")
     return o, lse
 
@@ -168,8 +170,10 @@ def combine(o, lse, inv, tokens=None):
     return out
 
 
-def forward(qk, v, R, n_buckets: int, chunk_len: int, causal: bool, return_all: bool = False):
-    """O1..O5 over every (batch, head). qk, v: [B, H, L, d]; R: [nh, d, nb/2].
+def forward(qk, v, R, n_buckets: int, chunk_len: int, causal: bool, return_all: bool = False,
+            key_norm: bool = False):
+    """O1..O5 over every (batch, head). qk, v: [B, H, L, d]; R: [nh, d, nb/2];
+    ``key_norm``: the key side of each score uses x_j / |x_j|.
 
     Returns out [B, H, L, d]; with ``return_all`` also a dict of the
     intermediate results (buckets, margin, perm, inv, lse, o_sorted).
@@ -193,7 +197,8 @@ def forward(qk, v, R, n_buckets: int, chunk_len: int, causal: bool, return_all: 
                                   n_buckets, nh, chunk_len, int(bool(causal)), _p(out, _f64p),
                                   _p(g("buckets"), _i32p), _p(g("margin"), _f64p),
                                   _p(g("perm"), _i32p), _p(g("inv"), _i32p),
-                                  _p(g("o_sorted"), _f64p), _p(g("lse"), _f64p)), "forward")
+                                  _p(g("o_sorted"), _f64p), _p(g("lse"), _f64p),
+                                  int(bool(key_norm))), "forward")
     return (out, extra) if return_all else out
 
 
@@ -216,7 +221,8 @@ def project(x, w_qk, w_v, n_heads: int):
     return qk, v
 
 
-def backward(qk, v, R, dout, n_buckets: int, chunk_len: int, causal: bool):
+def backward(qk, v, R, dout, n_buckets: int, chunk_len: int, causal: bool,
+             key_norm: bool = False):
     """G1: (dqk, dv), both [B, H, L, d], for a loss whose gradient with
     respect to the forward's output is dout [B, H, L, d]."""
     qk = _f64(qk)
@@ -229,5 +235,6 @@ def backward(qk, v, R, dout, n_buckets: int, chunk_len: int, causal: bool):
     dv = np.zeros((B, H, L, d))
     _check(_load().oracle_backward(_p(qk, _f64p), _p(v, _f64p), _p(R, _f64p), _p(dout, _f64p),
                                    B, H, L, d, n_buckets, nh, chunk_len, int(bool(causal)),
-                                   _p(dqk, _f64p), _p(dv, _f64p)), "backward")
+                                   _p(dqk, _f64p), _p(dv, _f64p), int(bool(key_norm))),
+           "backward")
     return dqk, dv

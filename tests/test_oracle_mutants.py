@@ -59,6 +59,9 @@ MUTANTS = {
                                          "const double p = exp(sc - ls[(int64_t)r * L + s]);"),
     "backward_no_D_term": ("const double ds = p * (gdv - dd[i]);", "const double ds = p * gdv;"),
     "backward_dv_to_query": ("gv[j * d + k] += p * gi[k];", "gv[i * d + k] += p * gi[k];"),
+    "key_norm_on_the_query": ("if (key_norm) sc *= inv_norm(xj, d);",
+                              "if (key_norm) sc *= inv_norm(xi, d);"),
+    "key_norm_backward_no_projection": ("(xi[k] - dot * rn * rn * xj[k])", "(xi[k])"),
 }
 
 
@@ -73,8 +76,10 @@ def _pin_calls():
         grid = [{}]
         for mark in getattr(fn, "pytestmark", []):
             if mark.name == "parametrize":
-                argname, values = mark.args
-                grid = [dict(g, **{argname: v}) for g in grid for v in values]
+                argnames, values = mark.args
+                names = [a.strip() for a in argnames.split(",")]
+                rows = [v if len(names) > 1 else (v,) for v in values]
+                grid = [dict(g, **dict(zip(names, row))) for g in grid for row in rows]
         for kw in grid:
             calls.append((name, fn, kw))
     return calls

@@ -398,15 +398,15 @@ def _fd_case(rng, B, H, L, d, nh, nb):
     return qk, v, R, g
 
 
-@pytest.mark.parametrize("causal", [False, True])
-def test_backward_matches_finite_differences(oracle_mod, causal):
+@pytest.mark.parametrize("causal,key_norm", [(False, False), (True, False), (True, True)])
+def test_backward_matches_finite_differences(oracle_mod, causal, key_norm):
     """G1: the gradient of sum(dout * forward) by central differences of the
     oracle's own forward (the hash is piecewise constant: perturbations that
-    move a bucket are skipped and counted)."""
+    move a bucket are skipped and counted); also with normalised keys."""
     rng = np.random.default_rng(60 + causal)
     B, H, L, d, nh, nb, m = 1, 2, 16, 6, 3, 4, 4
     qk, v, R, g = _fd_case(rng, B, H, L, d, nh, nb)
-    dqk, dv = oracle_mod.backward(qk, v, R, g, nb, m, causal)
+    dqk, dv = oracle_mod.backward(qk, v, R, g, nb, m, causal, key_norm=key_norm)
     base_b = oracle_mod.forward(qk, v, R, nb, m, causal, return_all=True)[1]["buckets"]
     eps = 1e-6
     skipped = 0
@@ -417,7 +417,8 @@ def test_backward_matches_finite_differences(oracle_mod, causal):
                 a = arr.copy()
                 a[idx] += sgn * eps
                 args = (a, v) if which == "qk" else (qk, a)
-                out, extra = oracle_mod.forward(*args, R, nb, m, causal, return_all=True)
+                out, extra = oracle_mod.forward(*args, R, nb, m, causal, return_all=True,
+                                                key_norm=key_norm)
                 vals.append((float((g * out).sum()), np.array_equal(extra["buckets"], base_b)))
             if not (vals[0][1] and vals[1][1]):
                 skipped += 1
@@ -463,3 +464,41 @@ def test_backward_duplicated_round(oracle_mod):
     # equal up to double rounding of sums taken in a different order
     np.testing.assert_allclose(a[0], b[0], rtol=1e-9, atol=1e-9)
     np.testing.assert_allclose(a[1], b[1], rtol=1e-9, atol=1e-9)
+
+
+# --------------------------------------------------------------------------- key normalisation
+
+def test_key_norm_unit_rows_equal_plain(oracle_mod):
+    """Variant: with rows of unit length, normalising the keys changes nothing."""
+    rng = np.random.default_rng(70)
+    qk = rng.standard_normal((1, 2, 64, 8))
+    qk /= np.linalg.norm(qk, axis=-1, keepdims=True)
+    v = rng.standard_normal((1, 2, 64, 8))
+    R = rng.standard_normal((2, 8, 4))
+    a = oracle_mod.forward(qk, v, R, 8, 16, True)
+    b = oracle_mod.forward(qk, v, R, 8, 16, True, key_norm=True)
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_norm_single_bucket_matches_torch_sdpa(oracle_mod, causal):
+    """Variant: all tokens in one bucket and one chunk: softmax attention of the
+    queries against unit-length keys, from torch's scaled_dot_product_attention
+    with an additive mask."""
+    rng = np.random.default_rng(71)
+    L, d = 40, 16
+    x = rng.standard_normal((L, d)) * rng.uniform(0.5, 3.0, (L, 1))
+    x[:, 0] = np.abs(x[:, 0]) + 0.1
+    v = rng.standard_normal((L, d))
+    R = np.zeros((1, d, 1))
+    R[0, 0, 0] = 1.0
+    out = oracle_mod.forward(x[None, None], v[None, None], R, 2, L, causal, key_norm=True)
+    mask = torch.zeros(L, L, dtype=torch.float64)
+    mask.fill_diagonal_(-brute.SELF_PENALTY)
+    if causal:
+        mask.masked_fill_(torch.ones(L, L, dtype=torch.bool).triu(1), float("-inf"))
+    xt = torch.from_numpy(x)
+    kt = xt / xt.norm(dim=1, keepdim=True)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        xt[None, None], kt[None, None], torch.from_numpy(v)[None, None], attn_mask=mask)[0, 0]
+    np.testing.assert_allclose(out[0, 0], ref.numpy(), rtol=1e-10, atol=1e-12)
