@@ -99,7 +99,7 @@ def forward_roofline(w, ms_per_step):
     return {"t_roof_ms": t_roof, "frac": t_roof / ms_per_step, "steps": per}
 
 
-def measure(lsh, torch, w, steps, warmup):
+def measure(lsh, torch, w, steps, warmup, key_norm=False):
     """Times `steps` back-to-back forwards on synthetic inputs resident in HBM,
     then the per-kernel event intervals of a few more."""
     import numpy as np
@@ -111,7 +111,7 @@ def measure(lsh, torch, w, steps, warmup):
     qk_t = torch.from_numpy(qk).to(dev, dt)
     v_t = torch.from_numpy(v).to(dev, dt)
     R_t = torch.from_numpy(R).to(dev)
-    shape = lsh.shape_of(qk_t, w.n_buckets, w.n_hashes, w.chunk_len, w.causal)
+    shape = lsh.shape_of(qk_t, w.n_buckets, w.n_hashes, w.chunk_len, w.causal, key_norm)
     ws = torch.empty(lsh.lsh_workspace_size("fwd", shape), dtype=torch.uint8, device=dev)
     out = torch.empty_like(qk_t)
 
@@ -183,7 +183,7 @@ def measure_projection(lsh, torch, w, steps, warmup, d_model=1024):
             "fwd_x_ms": f_ms, "fwd_x_tokens_per_s": w.B * w.L / (f_ms / 1e3)}
 
 
-def measure_training(lsh, torch, w, steps, warmup):
+def measure_training(lsh, torch, w, steps, warmup, key_norm=False):
     """lsh_attention_fwd_train and lsh_attention_bwd at the workload's shape;
     the backward's work is counted per (query, window key) pair: the score
     and g . v recomputed, then dq, dk and dv, 10 d flops."""
@@ -196,7 +196,7 @@ def measure_training(lsh, torch, w, steps, warmup):
     v_t = torch.from_numpy(v).to(dev, dt)
     R_t = torch.from_numpy(R).to(dev)
     g_t = torch.randn(qk_t.shape, generator=torch.Generator().manual_seed(w.seed)).to(dev, dt)
-    shape = lsh.shape_of(qk_t, w.n_buckets, w.n_hashes, w.chunk_len, w.causal)
+    shape = lsh.shape_of(qk_t, w.n_buckets, w.n_hashes, w.chunk_len, w.causal, key_norm)
     out = torch.empty_like(qk_t)
     state = torch.empty(lsh.lsh_workspace_size("state", shape), dtype=torch.uint8, device=dev)
     ws = torch.empty(lsh.lsh_workspace_size("fwd", shape), dtype=torch.uint8, device=dev)
@@ -224,7 +224,7 @@ def measure_training(lsh, torch, w, steps, warmup):
     # bf16 with chunk 64 runs on the matrix cores (bf16 products), else fp32 vector
     mfma = w.dtype == "bf16" and w.chunk_len == 64
     peak = PEAK_F16_TFLOPS if mfma else PEAK_FP32_TFLOPS
-    return {"workload": w.name, "fwd_train_ms": f_ms, "bwd_ms": b_ms,
+    return {"workload": w.name, "key_norm": bool(key_norm), "fwd_train_ms": f_ms, "bwd_ms": b_ms,
             "train_step_tokens_per_s": w.B * w.L / ((f_ms + b_ms) / 1e3),
             "bwd_pair_flops": flops, "bwd_tflops": flops / b_ms / 1e9,
             "bwd_peak": "bf16 mfma" if mfma else "fp32 vector",
@@ -319,6 +319,9 @@ def main() -> int:
                     help="time the input projections and the forward that starts from x")
     ap.add_argument("--train", action="store_true",
                     help="time the training forward and the backward")
+    ap.add_argument("--key-norm", action="store_true",
+                    help="time the key-normalisation variant (forward, or with --train both "
+                         "passes) instead of the headline line")
     args = ap.parse_args()
     if args.copy_calibration:
         import torch
@@ -359,7 +362,20 @@ def main() -> int:
 
     if args.train:
         print(json.dumps(measure_training(lsh, torch, workloads.WORKLOADS[
-            args.workload or workloads.HEADLINE], min(args.steps, 10), args.warmup)), flush=True)
+            args.workload or workloads.HEADLINE], min(args.steps, 10), args.warmup,
+            key_norm=args.key_norm)), flush=True)
+        return 0
+
+    if args.key_norm:
+        name = args.workload or workloads.HEADLINE
+        w = workloads.WORKLOADS[name]
+        r = measure(lsh, torch, w, args.steps, args.warmup, key_norm=True)
+        print(json.dumps({"variant": "key_norm", "workload": name, "config": w.describe(),
+                          "ms_per_step": r["ms_per_step"],
+                          "tokens_per_s": w.B * w.L / (r["ms_per_step"] / 1e3),
+                          "kernels_ms": r["kernels"],
+                          "forward_roofline": forward_roofline(w, r["ms_per_step"])}),
+              flush=True)
         return 0
 
     if args.project:

@@ -59,6 +59,16 @@ extern "C" {
 
 enum { LSH_F32 = 0, LSH_BF16 = 1 };
 
+/* Bits of lsh_shape_t.flags. */
+enum {
+    /* The key side of every attention score uses the unit vector x_j / |x_j|
+     * (walkthrough "1 LSH Attention": its stripped formula is where the
+     * method normalises keys); queries keep their length and the hash is
+     * unchanged. A zero vector gives a zero key. The backward differentiates
+     * through the norm. */
+    LSH_KEY_NORM = 1
+};
+
 enum {
     LSH_OK = 0,
     LSH_ERR_ARG = -1,         /* an argument breaks the method's constraints    */
@@ -76,16 +86,19 @@ enum {
  *                into equal chunks).
  *   causal       0 or 1: key position must not exceed the query position.
  *   dtype        LSH_F32 or LSH_BF16 for qk, v and out.
+ *   flags        0 or LSH_KEY_NORM (other bits: LSH_ERR_ARG).
  * Also required: B*H*n_hashes*L < 2^31. */
 typedef struct lsh_shape {
     int32_t B, H, L, d;
     int32_t n_buckets, n_hashes, chunk_len, causal;
     int32_t dtype;
+    int32_t flags;
 } lsh_shape_t;
 
 /* Bytes of workspace needed by `stage` ("hash", "sort", "fwd", "fwd_x",
  * "state" or "bwd") for `shape`, written to *bytes (host). "state" is the
  * size of the buffer lsh_attention_fwd_train fills for lsh_attention_bwd.
+ * LSH_KEY_NORM adds 4 bytes per token (B*H*L) to "fwd", "fwd_x" and "bwd".
  * Returns LSH_ERR_ARG for an unknown stage or an invalid shape. */
 int lsh_workspace_size(const char *stage, const lsh_shape_t *shape, size_t *bytes);
 
@@ -119,8 +132,9 @@ int lsh_sort(const int32_t *buckets, const lsh_shape_t *shape, int32_t *perm, in
  * with chunk c = s / m, the candidate keys are the slots of chunks c-1 and c
  * of the same round (chunk 0 has no look-back). Key position j is valid for
  * query position i when bucket(j) == bucket(i) and, if causal, j <= i. The
- * score is (x_i . x_j) / sqrt(d), lowered by 1e5 when j == i, so a query
- * attends to itself only when no other key is valid. Softmax in float32.
+ * score is (x_i . x_j) / sqrt(d) (with LSH_KEY_NORM, also divided by |x_j|),
+ * lowered by 1e5 when j == i, so a query attends to itself only when no
+ * other key is valid. Softmax in float32.
  *   qk, v     [B,H,L,d] shape->dtype
  *   buckets   [B,H,n_hashes,L] int32     perm [B,H,n_hashes,L] int32
  *   o_sorted  [B,H,n_hashes,L,d] f32 (out)

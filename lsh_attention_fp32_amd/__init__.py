@@ -20,6 +20,7 @@ the backward.
 from ._binding import (  # noqa: F401
     LSH_BF16,
     LSH_F32,
+    LSH_KEY_NORM,
     LSHAttention,
     LshError,
     Shape,

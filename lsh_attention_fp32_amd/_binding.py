@@ -8,6 +8,7 @@ import torch
 
 LSH_F32 = 0
 LSH_BF16 = 1
+LSH_KEY_NORM = 1   # lsh_shape_t.flags bit: keys as unit vectors in the scores
 _DTYPES = {torch.float32: LSH_F32, torch.bfloat16: LSH_BF16}
 _ERRORS = {-1: "LSH_ERR_ARG", -2: "LSH_ERR_WORKSPACE", -3: "LSH_ERR_HIP", -4: "LSH_ERR_UNSUPPORTED"}
 
@@ -27,7 +28,8 @@ class Shape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("L", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("n_buckets", ctypes.c_int32),
                 ("n_hashes", ctypes.c_int32), ("chunk_len", ctypes.c_int32),
-                ("causal", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("causal", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("flags", ctypes.c_int32)]
 
     def __repr__(self):
         return "Shape(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
@@ -99,14 +101,15 @@ def _stream(stream):
 
 
 def shape_of(qk: torch.Tensor, n_buckets: int, n_hashes: int, chunk_len: int,
-             causal: bool) -> Shape:
+             causal: bool, key_norm: bool = False) -> Shape:
     """Shape for qk of shape [B, H, L, d] (float32 or bfloat16)."""
     if qk.dim() != 4:
         raise ValueError(f"qk must be [B, H, L, d], got {tuple(qk.shape)}")
     if qk.dtype not in _DTYPES:
         raise ValueError(f"qk dtype must be float32 or bfloat16, got {qk.dtype}")
     B, H, L, d = qk.shape
-    return Shape(B, H, L, d, n_buckets, n_hashes, chunk_len, int(bool(causal)), _DTYPES[qk.dtype])
+    return Shape(B, H, L, d, n_buckets, n_hashes, chunk_len, int(bool(causal)), _DTYPES[qk.dtype],
+                 LSH_KEY_NORM if key_norm else 0)
 
 
 # ---------------------------------------------------------------- C-named calls
@@ -225,9 +228,10 @@ def sort(buckets, n_buckets: int, stream=None):
     return perm, inv
 
 
-def chunk_attend(qk, v, buckets, perm, n_buckets: int, chunk_len: int, causal: bool, stream=None):
+def chunk_attend(qk, v, buckets, perm, n_buckets: int, chunk_len: int, causal: bool, stream=None,
+                 key_norm: bool = False):
     """Returns (o_sorted [B,H,n_hashes,L,d] f32, lse_sorted [B,H,n_hashes,L] f32)."""
-    shape = shape_of(qk, n_buckets, buckets.shape[2], chunk_len, causal)
+    shape = shape_of(qk, n_buckets, buckets.shape[2], chunk_len, causal, key_norm)
     o = torch.empty(_rounds_shape(shape) + (shape.d,), dtype=torch.float32, device=qk.device)
     lse = torch.empty(_rounds_shape(shape), dtype=torch.float32, device=qk.device)
     lsh_chunk_attend(qk, v, buckets, perm, shape, o, lse, stream)
@@ -244,9 +248,9 @@ def unsort_combine(o_sorted, lse_sorted, inv, dtype=torch.bfloat16, stream=None)
 
 
 def attention_fwd(qk, v, R, n_buckets: int, chunk_len: int, causal: bool, ws=None, out=None,
-                  stream=None):
+                  stream=None, key_norm: bool = False):
     """Whole forward; returns out [B,H,L,d] in qk's dtype."""
-    shape = shape_of(qk, n_buckets, R.shape[0], chunk_len, causal)
+    shape = shape_of(qk, n_buckets, R.shape[0], chunk_len, causal, key_norm)
     if v.shape != qk.shape or v.dtype != qk.dtype:
         raise ValueError("v must match qk in shape and dtype")
     out = torch.empty_like(qk) if out is None else out
@@ -256,7 +260,7 @@ def attention_fwd(qk, v, R, n_buckets: int, chunk_len: int, causal: bool, ws=Non
 
 
 def _x_shape(x, w_qk, w_v, n_heads: int, n_buckets: int, n_hashes: int, chunk_len: int,
-             causal: bool) -> Shape:
+             causal: bool, key_norm: bool = False) -> Shape:
     if x.dim() != 3:
         raise ValueError(f"x must be [B, L, d_model], got {tuple(x.shape)}")
     if x.dtype not in _DTYPES:
@@ -267,7 +271,7 @@ def _x_shape(x, w_qk, w_v, n_heads: int, n_buckets: int, n_hashes: int, chunk_le
             or w_qk.dtype != x.dtype or w_v.dtype != x.dtype):
         raise ValueError("w_qk and w_v must be [H * d, d_model] in x's dtype")
     return Shape(B, n_heads, L, n_out // n_heads, n_buckets, n_hashes, chunk_len,
-                 int(bool(causal)), _DTYPES[x.dtype])
+                 int(bool(causal)), _DTYPES[x.dtype], LSH_KEY_NORM if key_norm else 0)
 
 
 def qkv_project(x, w_qk, w_v, n_heads: int, stream=None):
@@ -282,9 +286,9 @@ def qkv_project(x, w_qk, w_v, n_heads: int, stream=None):
 
 
 def attention_fwd_x(x, w_qk, w_v, R, n_heads: int, n_buckets: int, chunk_len: int, causal: bool,
-                    ws=None, out=None, stream=None):
+                    ws=None, out=None, stream=None, key_norm: bool = False):
     """Projections, then the whole forward; returns out [B, H, L, d] in x's dtype."""
-    shape = _x_shape(x, w_qk, w_v, n_heads, n_buckets, R.shape[0], chunk_len, causal)
+    shape = _x_shape(x, w_qk, w_v, n_heads, n_buckets, R.shape[0], chunk_len, causal, key_norm)
     out = torch.empty((shape.B, shape.H, shape.L, shape.d), dtype=x.dtype,
                       device=x.device) if out is None else out
     ws = _workspace("fwd_x", shape, x.device) if ws is None else ws
@@ -292,9 +296,10 @@ def attention_fwd_x(x, w_qk, w_v, R, n_heads: int, n_buckets: int, chunk_len: in
     return out
 
 
-def attention_fwd_train(qk, v, R, n_buckets: int, chunk_len: int, causal: bool, stream=None):
+def attention_fwd_train(qk, v, R, n_buckets: int, chunk_len: int, causal: bool, stream=None,
+                        key_norm: bool = False):
     """Training forward; returns (out [B,H,L,d], state) for attention_bwd."""
-    shape = shape_of(qk, n_buckets, R.shape[0], chunk_len, causal)
+    shape = shape_of(qk, n_buckets, R.shape[0], chunk_len, causal, key_norm)
     if v.shape != qk.shape or v.dtype != qk.dtype:
         raise ValueError("v must match qk in shape and dtype")
     out = torch.empty_like(qk)
@@ -305,9 +310,10 @@ def attention_fwd_train(qk, v, R, n_buckets: int, chunk_len: int, causal: bool, 
 
 
 def attention_bwd(qk, v, out, dout, state, n_buckets: int, n_hashes: int, chunk_len: int,
-                  causal: bool, stream=None):
-    """Returns (dqk, dv) for the output gradient dout (contiguous, qk's dtype)."""
-    shape = shape_of(qk, n_buckets, n_hashes, chunk_len, causal)
+                  causal: bool, stream=None, key_norm: bool = False):
+    """Returns (dqk, dv) for the output gradient dout (contiguous, qk's dtype);
+    ``key_norm`` must match the training forward that wrote ``state``."""
+    shape = shape_of(qk, n_buckets, n_hashes, chunk_len, causal, key_norm)
     dout = dout.to(qk.dtype).contiguous()
     dqk = torch.empty_like(qk)
     dv = torch.empty_like(v)
@@ -319,19 +325,21 @@ def attention_bwd(qk, v, out, dout, state, n_buckets: int, n_hashes: int, chunk_
 class LSHAttention(torch.autograd.Function):
     """out = LSH attention of (qk, v) with rotations R; differentiable in qk
     and v (the hash and the sort carry no gradient; R gets none).
-    Use: ``LSHAttention.apply(qk, v, R, n_buckets, chunk_len, causal)``."""
+    Use: ``LSHAttention.apply(qk, v, R, n_buckets, chunk_len, causal[, key_norm])``."""
 
     @staticmethod
-    def forward(ctx, qk, v, R, n_buckets, chunk_len, causal):
+    def forward(ctx, qk, v, R, n_buckets, chunk_len, causal, key_norm=False):
         qk = qk.contiguous()
         v = v.contiguous()
-        out, state = attention_fwd_train(qk, v, R.contiguous(), n_buckets, chunk_len, causal)
+        out, state = attention_fwd_train(qk, v, R.contiguous(), n_buckets, chunk_len, causal,
+                                         key_norm=key_norm)
         ctx.save_for_backward(qk, v, out, state)
         ctx.cfg = (n_buckets, R.shape[0], chunk_len, causal)
+        ctx.key_norm = key_norm
         return out
 
     @staticmethod
     def backward(ctx, dout):
         qk, v, out, state = ctx.saved_tensors
-        dqk, dv = attention_bwd(qk, v, out, dout, state, *ctx.cfg)
-        return dqk, dv, None, None, None, None
+        dqk, dv = attention_bwd(qk, v, out, dout, state, *ctx.cfg, key_norm=ctx.key_norm)
+        return dqk, dv, None, None, None, None, None

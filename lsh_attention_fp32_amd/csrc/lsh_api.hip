@@ -47,6 +47,8 @@ int validate(const lsh_shape_t* s) {
         return fail(LSH_ERR_ARG, "causal must be 0 or 1 (got %d)", s->causal);
     if (s->dtype != LSH_F32 && s->dtype != LSH_BF16)
         return fail(LSH_ERR_ARG, "dtype must be LSH_F32 or LSH_BF16 (got %d)", s->dtype);
+    if (s->flags & ~LSH_KEY_NORM)
+        return fail(LSH_ERR_ARG, "unknown flags 0x%x (only LSH_KEY_NORM)", (unsigned)s->flags);
     if ((int64_t)s->B * s->H * s->n_hashes * s->L >= ((int64_t)1 << 31))
         return fail(LSH_ERR_ARG, "B*H*n_hashes*L must stay below 2^31");
     if (s->d != 64 && s->d != 128)
@@ -64,7 +66,7 @@ int misaligned(std::initializer_list<const void*> ptrs) {
 }
 
 struct FwdLayout {
-    size_t hash, sort, buckets, perm, inv, lse, o, total;
+    size_t hash, sort, buckets, perm, inv, lse, o, rn, total;
 };
 
 FwdLayout fwd_layout(const Dims& d) {
@@ -89,6 +91,9 @@ FwdLayout fwd_layout(const Dims& d) {
     off += compact ? 0 : align_up(sizeof(float) * n, 256);
     f.o = off;
     off += align_up((compact ? 2 : sizeof(float)) * n * d.d, 256);
+    // key normalisation: 1 / |qk| per token, computed once per call
+    f.rn = off;
+    off += d.key_norm ? align_up(sizeof(float) * (size_t)d.T, 256) : 0;
     f.total = off;
     return f;
 }
@@ -122,7 +127,7 @@ StateLayout state_layout(const Dims& d) {
 bool fused_packed(const Dims& d) { return compact_o_sorted(d) && packed_sort_keys(d); }
 
 struct BwdLayout {
-    size_t dvec, dx, dv, total;
+    size_t dvec, dx, dv, rn, total;
 };
 
 BwdLayout bwd_layout(const Dims& d) {
@@ -131,7 +136,8 @@ BwdLayout bwd_layout(const Dims& d) {
     b.dvec = 0;
     b.dx = align_up(sizeof(float) * (size_t)d.T, 256);
     b.dv = b.dx + align_up(sizeof(float) * rows, 256);
-    b.total = b.dv + align_up(sizeof(float) * rows, 256);
+    b.rn = b.dv + align_up(sizeof(float) * rows, 256);
+    b.total = b.rn + (d.key_norm ? align_up(sizeof(float) * (size_t)d.T, 256) : 0);
     return b;
 }
 
@@ -170,7 +176,14 @@ int run_fwd(const void* qk, const void* v, const float* R, const lsh_shape_t* sh
     if ((e = launch_sort(buckets, d, perm, inv, base + f.sort, st, ev, nev, names, packed)) !=
         hipSuccess)
         return hip_fail(e, "sort");
-    if ((e = launch_attend(qk, v, buckets, perm, d, o, lse, st, ev, nev, names, packed)) !=
+    float* rn = nullptr;
+    if (d.key_norm) {
+        rn = (float*)(base + f.rn);
+        if ((e = launch_key_rnorm(qk, d, rn, st)) != hipSuccess ||
+            (e = mark(st, ev, nev, names, "key_rnorm")) != hipSuccess)
+            return hip_fail(e, "key_rnorm");
+    }
+    if ((e = launch_attend(qk, v, buckets, perm, d, o, lse, st, ev, nev, names, packed, rn)) !=
         hipSuccess)
         return hip_fail(e, "chunk_attend");
     if ((e = launch_combine(o, lse, inv, d, out, st, ev, nev, names, z)) != hipSuccess)
@@ -379,11 +392,14 @@ int lsh_attention_bwd(const void* qk, const void* v, const void* out, const void
     if ((rc = check_ws("lsh_attention_bwd", d, ws, ws_bytes, bl.total))) return rc;
     const char* sb = (const char*)state;
     char* wb = (char*)ws;
+    float* rn = d.key_norm ? (float*)(wb + bl.rn) : nullptr;
     BwdArgs a{qk, v, out, dout,
               (const int32_t*)(sb + sl.perm), (const int32_t*)(sb + sl.buckets),
-              (const float*)(sb + sl.z), (float*)(wb + bl.dvec), (float*)(wb + bl.dx),
+              (const float*)(sb + sl.z), (float*)(wb + bl.dvec), rn, (float*)(wb + bl.dx),
               (float*)(wb + bl.dv), dqk, dv};
-    hipError_t e = launch_backward(a, d, fused_packed(d), (hipStream_t)stream);
+    hipError_t e = hipSuccess;
+    if (rn) e = launch_key_rnorm(qk, d, rn, (hipStream_t)stream);
+    if (e == hipSuccess) e = launch_backward(a, d, fused_packed(d), (hipStream_t)stream);
     return e == hipSuccess ? LSH_OK : hip_fail(e, "lsh_attention_bwd");
 }
 

@@ -35,6 +35,7 @@ __global__ __launch_bounds__(256) void attend_valu_kernel(const T* __restrict__ 
     __shared__ __attribute__((aligned(16))) float ks[KB][KS];
     __shared__ __attribute__((aligned(16))) float vs[KB][KS];
     __shared__ int32_t kpos[KB], kbkt[KB];
+    __shared__ float krn[KB];   // key scale: 1 / |x_j| with key normalisation, else 1
     const int64_t seg = blockIdx.y;
     const int64_t c = blockIdx.x / nqb;
     const int qb = (int)(blockIdx.x - c * nqb);
@@ -69,6 +70,7 @@ __global__ __launch_bounds__(256) void attend_valu_kernel(const T* __restrict__ 
             const int32_t p = tid < nk ? P[kb0 + tid] : -1;
             kpos[tid] = p;
             kbkt[tid] = p >= 0 ? Bk[p] : 0;
+            krn[tid] = 1.f;
         }
         __syncthreads();
         for (int i = tid; i < KB * (D / 4); i += 256) {
@@ -81,6 +83,13 @@ __global__ __launch_bounds__(256) void attend_valu_kernel(const T* __restrict__ 
             }
             *(f32x4*)&ks[j][k] = a;
             *(f32x4*)&vs[j][k] = b;
+            if (dm.key_norm) {
+                // the D/4 lanes of row j are consecutive and aligned in the wave
+                float ss = a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+#pragma unroll
+                for (int o = 1; o < D / 4; o <<= 1) ss += __shfl_xor(ss, o);
+                if (k == 0) krn[j] = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
+            }
         }
         __syncthreads();
         float sc[KB];
@@ -100,7 +109,7 @@ __global__ __launch_bounds__(256) void attend_valu_kernel(const T* __restrict__ 
             dot += __shfl_xor(dot, 2);
             const int32_t kp = kpos[j];
             const bool ok = j < nk && kbkt[j] == qbkt && (!dm.causal || kp <= qpos);
-            const float s2 = dot * c2 - (kp == qpos ? pen2 : 0.f);
+            const float s2 = dot * krn[j] * c2 - (kp == qpos ? pen2 : 0.f);
             sc[j] = ok ? s2 : -INFINITY;
             bmx = fmaxf(bmx, sc[j]);
         }
@@ -183,10 +192,13 @@ struct alignas(16) AttendLds {
     uint16_t vt[D][VS];
     int32_t pos[kWin];
     int32_t bkt[kWin];
+    float rn[kWin];         // key scale (key normalisation): 1 / |x_j|
     int32_t nperm[4][kM];   // sorted keys of chunks waiting to be gathered
 };
 
-template <int D, bool HALF, bool PACKED>
+// KN (key normalisation): 0 off; 1 each key's 1 / |x| read from rn next to
+// its position; 2 summed here from the pieces of the row being stored.
+template <int D, bool HALF, bool PACKED, int KN>
 __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __restrict__ qk,
                                                           const uint16_t* __restrict__ v,
                                                           const int32_t* __restrict__ buckets,
@@ -194,7 +206,8 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
                                                           Dims dm, int nruns,
                                                           void* __restrict__ o_sorted,
                                                           const uint32_t* __restrict__ vmax,
-                                                          float* __restrict__ lse_sorted) {
+                                                          float* __restrict__ lse_sorted,
+                                                          const float* __restrict__ rn) {
     constexpr int PIECES = D / 8;              // 16-byte pieces per row
     constexpr int QPT = kM * PIECES / 256;     // qk pieces per thread
     constexpr int QROWS = 256 / PIECES;        // rows covered per pass
@@ -230,6 +243,7 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
         u32x4 q[QPT];
         u32x4 v[VPT][2];
         int32_t pos, bkt;   // position and bucket of row tid (threads < 64)
+        float rn;           // and its 1 / |x| (KN == 1)
     };
     auto issue_rows = [&](Rows& rw, const int32_t* kl) {
 #pragma unroll
@@ -247,14 +261,28 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
             const int32_t k = kl[tid];
             rw.pos = key_pos(k);
             rw.bkt = PACKED ? (int32_t)((uint32_t)k >> kPackPosBits) : Bk[k];
+            if constexpr (KN == 1) rw.rn = rn[bh * L + rw.pos];
         }
     };
-    // registers -> ring slot
+    // registers -> ring slot; with KN == 2 each row's 1 / |x| is summed from
+    // the pieces its PIECES consecutive lanes hold
     auto store_rows = [&](const Rows& rw, int slot) {
 #pragma unroll
         for (int j = 0; j < QPT; ++j) {
             const int row = tid / PIECES + QROWS * j;
             *(u32x4*)&sm.k[slot][row][(tid % PIECES) * 8] = rw.q[j];
+            if constexpr (KN == 2) {
+                float ss = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float lo = __uint_as_float(rw.q[j][e] << 16);
+                    const float hi = __uint_as_float(rw.q[j][e] & 0xFFFF0000u);
+                    ss = fmaf(lo, lo, fmaf(hi, hi, ss));
+                }
+#pragma unroll
+                for (int o = 1; o < PIECES; o <<= 1) ss += __shfl_xor(ss, o);
+                if (tid % PIECES == 0) sm.rn[slot * kM + row] = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
+            }
         }
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
@@ -269,6 +297,7 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
         if (tid < kM) {
             sm.pos[slot * kM + tid] = rw.pos;
             sm.bkt[slot * kM + tid] = rw.bkt;
+            if constexpr (KN == 1) sm.rn[slot * kM + tid] = rw.rn;
         }
     };
 
@@ -290,6 +319,7 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
             if (tid < kM) {
                 sm.pos[slot * kM + tid] = 0;
                 sm.bkt[slot * kM + tid] = -1;   // never equal to a bucket id
+                sm.rn[slot * kM + tid] = 0.f;
             }
         }
         if (tid < kM)
@@ -356,9 +386,11 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
             // mask (exp2 domain); register i is key 32*kb + 8*g + 4*h + i
             const i32x4 kbk = *(const i32x4*)&sm.bkt[32 * kb + 8 * g + 4 * h];
             const i32x4 kps = *(const i32x4*)&sm.pos[32 * kb + 8 * g + 4 * h];
+            f32x4 krn = {1.f, 1.f, 1.f, 1.f};
+            if constexpr (KN != 0) krn = *(const f32x4*)&sm.rn[32 * kb + 8 * g + 4 * h];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float s2 = acc[i] * c_log2 - (kps[i] == qpos ? pen2 : 0.f);
+                float s2 = acc[i] * krn[i] * c_log2 - (kps[i] == qpos ? pen2 : 0.f);
                 const bool ok = kbk[i] == qb && (!dm.causal || kps[i] <= qpos);
                 s2 = ok ? s2 : -INFINITY;
                 st[kt][i] = s2;
@@ -494,7 +526,7 @@ static void launch_valu(const T* qk, const T* v, const int32_t* buckets, const i
 hipError_t launch_attend(const void* qk, const void* v, const int32_t* buckets,
                          const int32_t* perm, const Dims& d, const OSorted& o, float* lse_sorted,
                          hipStream_t st, hipEvent_t* ev, int* nev, const char** names,
-                         bool packed) {
+                         bool packed, const float* rn) {
     if (packed && !(o.half && d.dtype == LSH_BF16 && d.m == kM)) return hipErrorInvalidValue;
     if (d.dtype == LSH_BF16 && d.m == kM) {
         const int nchunks = d.L / kM;
@@ -502,9 +534,13 @@ hipError_t launch_attend(const void* qk, const void* v, const int32_t* buckets,
         const unsigned grid = (unsigned)(d.segs * nruns);
         const uint16_t* x = (const uint16_t*)qk;
         const uint16_t* vv = (const uint16_t*)v;
-#define LSH_ATTEND_LAUNCH(DD, HH, PP, VM)                                                       \
-    attend_mfma_kernel<DD, HH, PP><<<grid, 256, 0, st>>>(x, vv, buckets, perm, d, nruns, o.ptr, \
-                                                         VM, lse_sorted)
+#define LSH_ATTEND_LAUNCH(DD, HH, PP, VM)                                                      \
+    (!d.key_norm ? attend_mfma_kernel<DD, HH, PP, 0><<<grid, 256, 0, st>>>(                    \
+                       x, vv, buckets, perm, d, nruns, o.ptr, VM, lse_sorted, nullptr)        \
+     : rn ? attend_mfma_kernel<DD, HH, PP, 1><<<grid, 256, 0, st>>>(                           \
+                x, vv, buckets, perm, d, nruns, o.ptr, VM, lse_sorted, rn)                    \
+          : attend_mfma_kernel<DD, HH, PP, 2><<<grid, 256, 0, st>>>(                           \
+                x, vv, buckets, perm, d, nruns, o.ptr, VM, lse_sorted, nullptr))
         if (o.half && packed) {
             if (d.d == 64) LSH_ATTEND_LAUNCH(64, true, true, o.vmax);
             else LSH_ATTEND_LAUNCH(128, true, true, o.vmax);

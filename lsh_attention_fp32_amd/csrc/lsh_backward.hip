@@ -8,7 +8,10 @@
 // D_i = g_i . out_i and the scale 1/sqrt(d) (scholar "Transformerの問題点とは"):
 //   dv_j += P g_i,   dS = P (g_i . v_j - D_i),
 //   dq_i += dS x_j / sqrt(d),   dk_j += dS x_i / sqrt(d),   dqk = dq + dk
-// (queries and keys are the same vectors). The hash and the sort are
+// (queries and keys are the same vectors). With key normalisation the score
+// is s = (x_i . x_j) rn_j / sqrt(d), rn_j = 1 / |x_j|, so dq_i takes
+// dS rn_j x_j and dk_j takes rn_j (dS x_i - rn_j^2 dS (x_i . x_j) x_j), both
+// over sqrt(d); rn comes from a per-token pass before the kernels. The hash and the sort are
 // piecewise constant and carry no gradient; the backward re-reads the sorted
 // order and bucket ids the forward saved, and Z.
 //
@@ -113,12 +116,14 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const T* __restrict__ qk,
                                                      const int32_t* __restrict__ perm,
                                                      const int32_t* __restrict__ buckets,
                                                      const float* __restrict__ z,
-                                                     const float* __restrict__ Dv, Dims dm,
+                                                     const float* __restrict__ Dv,
+                                                     const float* __restrict__ rn, Dims dm,
                                                      int nqb, float* __restrict__ dx_r) {
     constexpr int QD = D / 4, KB = 32, KS = D + 4;
     __shared__ __attribute__((aligned(16))) float ks[KB][KS];
     __shared__ __attribute__((aligned(16))) float vs[KB][KS];
     __shared__ int32_t kpos[KB], kbkt[KB];
+    __shared__ float krn[KB];   // 1 / |x_j| with key normalisation, else 1
     const int64_t seg = blockIdx.y;
     const int64_t c = blockIdx.x / nqb;
     const int qb = (int)(blockIdx.x - c * nqb);
@@ -157,6 +162,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const T* __restrict__ qk,
             if (tid < nk) read_key<PACKED>(P, Bk, kb0 + tid, p, b);
             kpos[tid] = p;
             kbkt[tid] = b;
+            krn[tid] = (rn && p >= 0) ? rn[bh * L + p] : 1.f;
         }
         __syncthreads();
         for (int i = tid; i < KB * (D / 4); i += 256) {
@@ -184,9 +190,9 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const T* __restrict__ qk,
             gv = quad_sum(gv);
             const int32_t kp = kpos[j];
             const bool ok = kbkt[j] == qbkt && (!dm.causal || kp <= qpos);
-            const float s2 = dot * c2 - (kp == qpos ? pen2 : 0.f);
+            const float s2 = dot * krn[j] * c2 - (kp == qpos ? pen2 : 0.f);
             const float p = pair_weight(ok, kp == qpos, s2, z2, self_only, inv_nh);
-            const float ds = p * (gv - Di);
+            const float ds = p * (gv - Di) * krn[j];
 #pragma unroll
             for (int e = 0; e < QD; e += 4) {
                 const f32x4 kk = *(const f32x4*)&ks[j][part * QD + e];
@@ -212,7 +218,8 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(const T* __restrict__ qk,
                                                       const int32_t* __restrict__ perm,
                                                       const int32_t* __restrict__ buckets,
                                                       const float* __restrict__ z,
-                                                      const float* __restrict__ Dv, Dims dm,
+                                                      const float* __restrict__ Dv,
+                                                      const float* __restrict__ rn, Dims dm,
                                                       int nkb, float* __restrict__ dx_r,
                                                       float* __restrict__ dv_r) {
     constexpr int QD = D / 4, QB = 32, QS = D + 4;
@@ -242,6 +249,9 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(const T* __restrict__ qk,
     load_quarter<QD>(V + (int64_t)kpos * D, part, vk);
 #pragma unroll
     for (int e = 0; e < QD; ++e) dk[e] = dv[e] = 0.f;
+    // the key's 1 / |x| and its sum of dS (x_i . x_j)
+    const float krn = rn ? rn[bh * L + kpos] : 1.f;
+    float sdd = 0.f;
     const float c2 = kLog2e / sqrtf((float)D);
     const float pen2 = kSelfPenalty * kLog2e;
     const float inv_nh = 1.0f / (float)dm.nh;
@@ -285,11 +295,12 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(const T* __restrict__ qk,
             const int32_t qp = qposs[j];
             // the key counts for this query: same bucket and, if causal, not later
             const bool ok = qbkts[j] == kbkt && (!dm.causal || kpos <= qp);
-            const float s2 = dot * c2 - (kpos == qp ? pen2 : 0.f);
+            const float s2 = dot * krn * c2 - (kpos == qp ? pen2 : 0.f);
             const float zq = qz[j];
             const float p = pair_weight(ok, kpos == qp, s2, zq * kLog2e,
                                         zq < -0.5f * kSelfPenalty, inv_nh);
             const float ds = p * (gv - qD[j]);
+            sdd = fmaf(ds, dot, sdd);
 #pragma unroll
             for (int e = 0; e < QD; e += 4) {
                 const f32x4 qq = *(const f32x4*)&qs[j][part * QD + e];
@@ -306,6 +317,11 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(const T* __restrict__ qk,
         }
     }
     if (!klive) return;
+    if (rn) {
+        const float pr = krn * krn * sdd;
+#pragma unroll
+        for (int e = 0; e < QD; ++e) dk[e] = krn * fmaf(-pr, k[e], dk[e]);
+    }
     const float scale = 1.0f / sqrtf((float)D);
     const int64_t row = ((bh * L + kpos) * dm.nh + r) * D + part * QD;
 #pragma unroll
@@ -460,6 +476,7 @@ struct BwdLds {
     // chunks c - 1, c, c + 1: position, bucket id, Z and D of each slot
     int32_t pos[3][kBM], bkt[3][kBM];
     float zz[3][kBM], dd[3][kBM];
+    float rn[3][kBM];   // 1 / |x| of each slot (key normalisation)
 };
 
 // One workgroup per (round, chunk c): the chunk's 64 slots are at once the
@@ -474,14 +491,15 @@ struct BwdLds {
 // are written once to the per-round rows. The sorted keys, Z and D of the
 // three chunks are read in one go at the start, and each stage issues its two
 // row gathers together, so a workgroup waits on memory five times in a row.
-template <int D, bool PACKED>
+template <int D, bool PACKED, bool KN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_mfma_kernel(const uint16_t* __restrict__ qk,
                                                        const uint16_t* __restrict__ v,
                                                        const uint16_t* __restrict__ g,
                                                        const int32_t* __restrict__ perm,
                                                        const int32_t* __restrict__ buckets,
                                                        const float* __restrict__ z,
-                                                       const float* __restrict__ Dv, Dims dm,
+                                                       const float* __restrict__ Dv,
+                                                       const float* __restrict__ rn, Dims dm,
                                                        uint16_t* __restrict__ dx_r,
                                                        uint16_t* __restrict__ dv_r) {
     constexpr int KSTEPS = D / 32, DT = D / 16;
@@ -552,12 +570,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
         const int w3 = tid >> 6, j = tid & (kBM - 1);
         sm.zz[w3][j] = zpos >= 0 ? z[bh * L + zpos] : 0.f;
         sm.dd[w3][j] = zpos >= 0 ? Dv[bh * L + zpos] : 0.f;
+        if constexpr (KN) sm.rn[w3][j] = zpos >= 0 ? rn[bh * L + zpos] : 0.f;
     }
     // ---- the chunk itself: qk into ra (transposed too), v into rb (the
-    // stage's barriers also publish Z and D)
+    // stage's barriers also publish Z, D and the key scales)
     stage(1, X, V, true, false);
     const float mz = sm.zz[1][me], mz2 = mz * kLog2e, mD = sm.dd[1][me];
     const bool mself_only = mz < -0.5f * kSelfPenalty;
+    const float mrn = KN ? sm.rn[1][me] : 1.f;   // this slot's 1 / |x| as a key
+    float msdd = 0.f;   // its sum of dS (x_i . x_j) over the key-side pairs
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
         xf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.ra[phys_row(me)][32 * s + 8 * gq]);
@@ -591,9 +612,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
                     const int key = 32 * kb + 8 * gq + 4 * h + i;
                     const int32_t kp = sm.pos[w3][key];
                     const bool ok = sm.bkt[w3][key] == mbkt && (!dm.causal || kp <= mpos);
-                    const float s2 = sacc[i] * c2 - (kp == mpos ? pen2 : 0.f);
+                    const float krn = KN ? sm.rn[w3][key] : 1.f;
+                    const float s2 = sacc[i] * krn * c2 - (kp == mpos ? pen2 : 0.f);
                     const float pw = pair_weight(ok, kp == mpos, s2, mz2, mself_only, inv_nh);
-                    ds[i] = pw * (pacc[i] - mD);
+                    ds[i] = pw * (pacc[i] - mD) * krn;
                 }
                 dsfrag[2 * h] = pack_bf16x2(ds[0], ds[1]);
                 dsfrag[2 * h + 1] = pack_bf16x2(ds[2], ds[3]);
@@ -632,10 +654,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
                     const int32_t qp = sm.pos[w3][q];
                     const float zq = sm.zz[w3][q];
                     const bool ok = sm.bkt[w3][q] == mbkt && (!dm.causal || mpos <= qp);
-                    const float s2 = sacc[i] * c2 - (mpos == qp ? pen2 : 0.f);
+                    const float s2 = sacc[i] * mrn * c2 - (mpos == qp ? pen2 : 0.f);
                     pw[i] = pair_weight(ok, mpos == qp, s2, zq * kLog2e,
                                         zq < -0.5f * kSelfPenalty, inv_nh);
                     ds[i] = pw[i] * (pacc[i] - sm.dd[w3][q]);
+                    if constexpr (KN) msdd = fmaf(ds[i], sacc[i], msdd);
                 }
                 pfrag[2 * h] = pack_bf16x2(pw[0], pw[1]);
                 pfrag[2 * h + 1] = pack_bf16x2(pw[2], pw[3]);
@@ -677,6 +700,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     // float32 sum over rounds)
     const float scale = 1.0f / sqrtf((float)D);
     const int64_t row = ((bh * L + mpos) * dm.nh + r) * D;
+    if constexpr (KN) {
+        // dk = rn (sum dS x_i - rn^2 (sum dS x_i . x_j) x_j); the lanes of a
+        // slot hold disjoint query sets, so their sums are added first
+        msdd += __shfl_xor(msdd, 16);
+        msdd += __shfl_xor(msdd, 32);
+        const float pr = mrn * mrn * msdd;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const uint2 w = *(const uint2*)(X + (int64_t)mpos * D + 16 * dt + 4 * gq);
+            const f32x4 xm = {__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                              __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
+            dk[dt] = (dk[dt] - pr * xm) * mrn;
+        }
+    }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
         const f32x4 x = (dq[dt] + dk[dt]) * scale;
@@ -700,8 +737,12 @@ hipError_t launch_bwd_t(const BwdArgs& a, const Dims& d, hipStream_t st) {
             const dim3 grid((unsigned)(d.L / kBM), (unsigned)d.segs);
             uint16_t* hx = (uint16_t*)a.dx_r;
             uint16_t* hv = (uint16_t*)a.dv_r;
-            bwd_mfma_kernel<D, PACKED><<<grid, 256, 0, st>>>(qk, v, g, a.perm, a.buckets, a.z,
-                                                             a.Dv, d, hx, hv);
+            if (a.rn)
+                bwd_mfma_kernel<D, PACKED, true><<<grid, 256, 0, st>>>(
+                    qk, v, g, a.perm, a.buckets, a.z, a.Dv, a.rn, d, hx, hv);
+            else
+                bwd_mfma_kernel<D, PACKED, false><<<grid, 256, 0, st>>>(
+                    qk, v, g, a.perm, a.buckets, a.z, a.Dv, nullptr, d, hx, hv);
             const unsigned gr = (unsigned)((d.T * (D / 4) + 255) / 256);
             bwd_reduce_kernel<D, T, uint16_t><<<gr, 256, 0, st>>>(hx, hv, d, (T*)a.dqk,
                                                                   (T*)a.dv);
@@ -710,10 +751,10 @@ hipError_t launch_bwd_t(const BwdArgs& a, const Dims& d, hipStream_t st) {
     }
     const int nqb = (d.m + 63) / 64;
     const dim3 grid((unsigned)((int64_t)(d.L / d.m) * nqb), (unsigned)d.segs);
-    bwd_dq_kernel<D, T, PACKED><<<grid, 256, 0, st>>>(qk, v, g, a.perm, a.buckets, a.z, a.Dv, d,
-                                                      nqb, a.dx_r);
-    bwd_dkv_kernel<D, T, PACKED><<<grid, 256, 0, st>>>(qk, v, g, a.perm, a.buckets, a.z, a.Dv, d,
-                                                       nqb, a.dx_r, a.dv_r);
+    bwd_dq_kernel<D, T, PACKED><<<grid, 256, 0, st>>>(qk, v, g, a.perm, a.buckets, a.z, a.Dv,
+                                                      a.rn, d, nqb, a.dx_r);
+    bwd_dkv_kernel<D, T, PACKED><<<grid, 256, 0, st>>>(qk, v, g, a.perm, a.buckets, a.z, a.Dv,
+                                                       a.rn, d, nqb, a.dx_r, a.dv_r);
     const unsigned gr = (unsigned)((d.T * (D / 4) + 255) / 256);
     bwd_reduce_kernel<D, T, float><<<gr, 256, 0, st>>>(a.dx_r, a.dv_r, d, (T*)a.dqk, (T*)a.dv);
     return hipGetLastError();
@@ -728,6 +769,7 @@ hipError_t launch_bwd_d(const BwdArgs& a, const Dims& d, hipStream_t st) {
 
 hipError_t launch_backward(const BwdArgs& a, const Dims& d, bool packed, hipStream_t st) {
     if (d.T == 0) return hipSuccess;
+    if (d.key_norm != (a.rn != nullptr)) return hipErrorInvalidValue;
     if (d.dtype == LSH_BF16)
         return packed ? launch_bwd_d<uint16_t, true>(a, d, st) : launch_bwd_d<uint16_t, false>(a, d, st);
     return packed ? launch_bwd_d<float, true>(a, d, st) : launch_bwd_d<float, false>(a, d, st);

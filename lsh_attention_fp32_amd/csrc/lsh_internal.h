@@ -20,6 +20,7 @@ struct Dims {
     int32_t B, H, L, d;
     int32_t nb, nh, m, causal;
     int32_t dtype;
+    int32_t key_norm;   // keys as unit vectors in the scores (LSH_KEY_NORM)
     int64_t T;        // B*H*L token-heads
     int64_t segs;     // B*H*nh (batch, head, round) segments
 };
@@ -29,6 +30,7 @@ inline Dims make_dims(const lsh_shape_t& s) {
     d.B = s.B; d.H = s.H; d.L = s.L; d.d = s.d;
     d.nb = s.n_buckets; d.nh = s.n_hashes; d.m = s.chunk_len; d.causal = s.causal;
     d.dtype = s.dtype;
+    d.key_norm = (s.flags & LSH_KEY_NORM) ? 1 : 0;
     d.T = (int64_t)s.B * s.H * s.L;
     d.segs = (int64_t)s.B * s.H * s.n_hashes;
     return d;
@@ -131,10 +133,16 @@ inline bool compact_o_sorted(const Dims& d) { return d.dtype == LSH_BF16 && d.m 
 
 // packed: perm holds packed sorted keys (buckets is then not read); only
 // the fp16 by-position form takes them.
+// With d.key_norm, rn holds 1 / |qk| per token (launch_key_rnorm); when it is
+// null the kernels sum each staged row's squares themselves.
 hipError_t launch_attend(const void* qk, const void* v, const int32_t* buckets,
                          const int32_t* perm, const Dims& d, const OSorted& o, float* lse_sorted,
                          hipStream_t st, hipEvent_t* ev, int* nev, const char** names,
-                         bool packed = false);
+                         bool packed = false, const float* rn = nullptr);
+
+// ----------------------------------------------------- key normalisation
+// rn[t] = 1 / |qk[t]| (0 for the zero vector), float32, one per token-head.
+hipError_t launch_key_rnorm(const void* qk, const Dims& d, float* rn, hipStream_t st);
 
 // ----------------------------------------------------------- combine stage
 // z (or null): per token [B,H,L], the natural-log partition function over
@@ -160,6 +168,7 @@ struct BwdArgs {
     const int32_t* buckets;   // [B,H,nh,L] by position
     const float* z;           // [B,H,L] natural-log total partition function
     float* Dv;                // [B,H,L] scratch: dout . out
+    const float* rn;          // [B,H,L] 1 / |qk| (key normalisation), else null
     float* dx_r;              // [B,H,L,nh,d] scratch: per-round dq + dk
     float* dv_r;              // [B,H,L,nh,d] scratch: per-round dv
     void* dqk;                // [B,H,L,d] out

@@ -57,6 +57,7 @@ def _shape(**kw):
     (dict(chunk_len=0), -1), (dict(L=100, chunk_len=64), -1), (dict(causal=2), -1),
     (dict(dtype=7), -1), (dict(B=-1), -1), (dict(d=96), -4), (dict(n_buckets=8192), -4),
     (dict(B=64, H=64, L=65536, n_hashes=8, chunk_len=64), -1),
+    (dict(flags=2), -1), (dict(flags=-1), -1),
 ])
 def test_workspace_size_rejects_bad_shapes(lib, kw, code):
     with pytest.raises(lsh.LshError) as ei:
@@ -157,3 +158,16 @@ def test_backward_rejects_small_state(lib):
     p = ctypes.c_void_p(0x1000)
     rc = lib.lsh_attention_bwd(p, p, p, p, p, 16, s, p, p, p, 1 << 40, None)
     assert rc == -2 and "state" in lsh.lsh_last_error()
+
+
+def test_key_norm_workspace_holds_one_float_per_token(lib):
+    """LSH_KEY_NORM adds 1 / |qk| per token (256-byte aligned) to the forward
+    and backward workspaces; the other stages and the training state keep
+    their size."""
+    base, kn = _shape(), _shape(flags=lsh.LSH_KEY_NORM)
+    tokens = base.B * base.H * base.L
+    extra = -(-4 * tokens // 256) * 256
+    for stage in ("hash", "sort", "state"):
+        assert lsh.lsh_workspace_size(stage, kn) == lsh.lsh_workspace_size(stage, base)
+    for stage in ("fwd", "fwd_x", "bwd"):
+        assert lsh.lsh_workspace_size(stage, kn) == lsh.lsh_workspace_size(stage, base) + extra
