@@ -296,11 +296,23 @@ int oracle_combine(const double *o, const double *lse, const int32_t *inv,
     return 0;
 }
 
+/* Rotations used by (batch, head) bh: the shared R, or head (bh mod H)'s own */
+/* block of n_hashes rounds when each head has its rotations.               */
+static const double *head_rotations(const double *R, int64_t bh, int H, int n_hashes, int d,
+                                    int n_buckets, int per_head_r)
+{
+    if (!per_head_r) return R;
+    const int64_t per_head = (int64_t)n_hashes * d * (n_buckets / 2);
+    return R + (bh % H) * per_head;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Whole forward over [B, H]: O1 -> O2 -> O3/O4 -> O5 for every (b, h).      */
 /*                                                                           */
 /*   qk, v  [B, H, L, d]                                                     */
-/*   R      [n_hashes, d, n_buckets/2] shared by every batch and head        */
+/*   R      [n_hashes, d, n_buckets/2] shared by every batch and head, or,   */
+/*          with per_head_r, [H, n_hashes, d, n_buckets/2]: head h hashes     */
+/*          with its own rotations R[h] in every batch                       */
 /*   out    [B, H, L, d]                                                     */
 /*   optional outputs (each may be NULL):                                    */
 /*     buckets, perm, inv [B, H, n_hashes, L]; margin, lse [B, H, n_hashes, L]*/
@@ -310,7 +322,7 @@ int oracle_forward(const double *qk, const double *v, const double *R,
                    int B, int H, int64_t L, int d, int n_buckets, int n_hashes,
                    int chunk_len, int causal, double *out, int32_t *buckets_out,
                    double *margin_out, int32_t *perm_out, int32_t *inv_out,
-                   double *o_sorted_out, double *lse_out, int key_norm)
+                   double *o_sorted_out, double *lse_out, int key_norm, int per_head_r)
 {
     if (B < 0 || H < 0 || L < 0 || d < 1 || n_hashes < 1 || chunk_len < 1 ||
         n_buckets < 2 || (n_buckets % 2) != 0 || (L % chunk_len) != 0)
@@ -326,7 +338,8 @@ int oracle_forward(const double *qk, const double *v, const double *R,
         double *ls = (double *)malloc(sizeof(double) * (size_t)(seg ? seg : 1));
         double *os = (double *)malloc(sizeof(double) * (size_t)(seg ? seg * d : 1));
         int rc = (bk && pm && iv && mg && ls && os) ? 0 : -2;
-        if (!rc) rc = oracle_hash(x, L, d, R, n_hashes, n_buckets, bk, mg);
+        const double *Rh = head_rotations(R, bh, H, n_hashes, d, n_buckets, per_head_r);
+        if (!rc) rc = oracle_hash(x, L, d, Rh, n_hashes, n_buckets, bk, mg);
         for (int r = 0; !rc && r < n_hashes; ++r)
             rc = oracle_sort(bk + r * L, L, pm + r * L, iv + r * L);
         for (int r = 0; !rc && r < n_hashes; ++r)
@@ -370,12 +383,14 @@ int oracle_forward(const double *qk, const double *v, const double *R,
 /* on the self score is a constant and has no derivative of its own.         */
 /*                                                                           */
 /*   qk, v, dout  [B, H, L, d]                                               */
-/*   R            [n_hashes, d, n_buckets/2]                                 */
+/*   R            [n_hashes, d, n_buckets/2], or [H, n_hashes, d, nb/2] with */
+/*                per_head_r (as in oracle_forward)                          */
 /*   dqk, dv      [B, H, L, d]  out                                          */
 /* ------------------------------------------------------------------------ */
 int oracle_backward(const double *qk, const double *v, const double *R, const double *dout,
                     int B, int H, int64_t L, int d, int n_buckets, int n_hashes,
-                    int chunk_len, int causal, double *dqk, double *dv, int key_norm)
+                    int chunk_len, int causal, double *dqk, double *dv, int key_norm,
+                    int per_head_r)
 {
     if (B < 0 || H < 0 || L < 0 || d < 1 || n_hashes < 1 || chunk_len < 1 ||
         n_buckets < 2 || (n_buckets % 2) != 0 || (L % chunk_len) != 0)
@@ -401,7 +416,8 @@ int oracle_backward(const double *qk, const double *v, const double *R, const do
         double *dd = (double *)malloc(sizeof(double) * nl);
         int rc = (bk && pm && iv && mg && ls && os && out && z && dd) ? 0 : -2;
         /* the forward's own steps */
-        if (!rc) rc = oracle_hash(x, L, d, R, n_hashes, n_buckets, bk, mg);
+        const double *Rh = head_rotations(R, bh, H, n_hashes, d, n_buckets, per_head_r);
+        if (!rc) rc = oracle_hash(x, L, d, Rh, n_hashes, n_buckets, bk, mg);
         for (int r = 0; !rc && r < n_hashes; ++r)
             rc = oracle_sort(bk + r * L, L, pm + r * L, iv + r * L);
         for (int r = 0; !rc && r < n_hashes; ++r)

@@ -65,12 +65,13 @@ def _load():
         lib.oracle_forward.argtypes = [_f64p, _f64p, _f64p, ctypes.c_int, ctypes.c_int,
                                        ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                        ctypes.c_int, ctypes.c_int, _f64p, _i32p, _f64p, _i32p,
-                                       _i32p, _f64p, _f64p, ctypes.c_int]
+                                       _i32p, _f64p, _f64p, ctypes.c_int, ctypes.c_int]
         lib.oracle_project.argtypes = [_f64p, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
                                        _f64p, _f64p, ctypes.c_int, ctypes.c_int, _f64p, _f64p]
         lib.oracle_backward.argtypes = [_f64p, _f64p, _f64p, _f64p, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                        ctypes.c_int, ctypes.c_int, _f64p, _f64p, ctypes.c_int]
+                                        ctypes.c_int, ctypes.c_int, _f64p, _f64p, ctypes.c_int,
+                                        ctypes.c_int]
         lib.oracle_threads.argtypes = []
         lib.oracle_threads.restype = ctypes.c_int
         for fn in (lib.oracle_hash, lib.oracle_sort, lib.oracle_attend, lib.oracle_combine,
@@ -170,9 +171,24 @@ def combine(o, lse, inv, tokens=None):
     return out
 
 
+def _rotations(R, H: int, d: int, n_buckets: int):
+    """R as float64 and (n_hashes, per_head): [nh, d, nb/2] is shared by every
+    head, [H, nh, d, nb/2] gives each head its own rotations."""
+    R = _f64(R)
+    if R.ndim == 4:
+        if R.shape[0] != H or R.shape[2:] != (d, n_buckets // 2):
+            raise ValueError(f"per-head R has shape {R.shape}, expected (H={H}, nh, {d}, "
+                             f"{n_buckets // 2})")
+        return R, R.shape[1], 1
+    if R.ndim != 3 or R.shape[1:] != (d, n_buckets // 2):
+        raise ValueError(f"R has shape {R.shape}, expected (nh, {d}, {n_buckets // 2})")
+    return R, R.shape[0], 0
+
+
 def forward(qk, v, R, n_buckets: int, chunk_len: int, causal: bool, return_all: bool = False,
             key_norm: bool = False):
-    """O1..O5 over every (batch, head). qk, v: [B, H, L, d]; R: [nh, d, nb/2];
+    """O1..O5 over every (batch, head). qk, v: [B, H, L, d]; R: [nh, d, nb/2]
+    shared by every head, or [H, nh, d, nb/2] (each head its own rotations);
     ``key_norm``: the key side of each score uses x_j / |x_j|.
 
     Returns out [B, H, L, d]; with ``return_all`` also a dict of the
@@ -180,9 +196,8 @@ def forward(qk, v, R, n_buckets: int, chunk_len: int, causal: bool, return_all: 
     """
     qk = _f64(qk)
     v = _f64(v)
-    R = _f64(R)
     B, H, L, d = qk.shape
-    nh = R.shape[0]
+    R, nh, per_head = _rotations(R, H, d, n_buckets)
     out = np.empty((B, H, L, d))
     extra = {}
     if return_all:
@@ -198,7 +213,7 @@ def forward(qk, v, R, n_buckets: int, chunk_len: int, causal: bool, return_all: 
                                   _p(g("buckets"), _i32p), _p(g("margin"), _f64p),
                                   _p(g("perm"), _i32p), _p(g("inv"), _i32p),
                                   _p(g("o_sorted"), _f64p), _p(g("lse"), _f64p),
-                                  int(bool(key_norm))), "forward")
+                                  int(bool(key_norm)), per_head), "forward")
     return (out, extra) if return_all else out
 
 
@@ -224,17 +239,16 @@ def project(x, w_qk, w_v, n_heads: int):
 def backward(qk, v, R, dout, n_buckets: int, chunk_len: int, causal: bool,
              key_norm: bool = False):
     """G1: (dqk, dv), both [B, H, L, d], for a loss whose gradient with
-    respect to the forward's output is dout [B, H, L, d]."""
+    respect to the forward's output is dout [B, H, L, d]; R as in forward."""
     qk = _f64(qk)
     v = _f64(v)
-    R = _f64(R)
     dout = _f64(dout)
     B, H, L, d = qk.shape
-    nh = R.shape[0]
+    R, nh, per_head = _rotations(R, H, d, n_buckets)
     dqk = np.zeros((B, H, L, d))
     dv = np.zeros((B, H, L, d))
     _check(_load().oracle_backward(_p(qk, _f64p), _p(v, _f64p), _p(R, _f64p), _p(dout, _f64p),
                                    B, H, L, d, n_buckets, nh, chunk_len, int(bool(causal)),
-                                   _p(dqk, _f64p), _p(dv, _f64p), int(bool(key_norm))),
+                                   _p(dqk, _f64p), _p(dv, _f64p), int(bool(key_norm)), per_head),
            "backward")
     return dqk, dv

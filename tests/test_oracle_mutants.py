@@ -61,6 +61,10 @@ MUTANTS = {
     "backward_dv_to_query": ("gv[j * d + k] += p * gi[k];", "gv[i * d + k] += p * gi[k];"),
     "key_norm_on_the_query": ("if (key_norm) sc *= inv_norm(xj, d);",
                               "if (key_norm) sc *= inv_norm(xi, d);"),
+    # both stay inside R for any shape
+    "per_head_rotations_of_the_batch": ("return R + (bh % H) * per_head;",
+                                        "return R + ((bh / H) % H) * per_head;"),
+    "per_head_rotations_ignored": ("if (!per_head_r) return R;", "return R;"),
     "key_norm_backward_no_projection": ("(xi[k] - dot * rn * rn * xj[k])", "(xi[k])"),
 }
 

@@ -502,3 +502,41 @@ def test_key_norm_single_bucket_matches_torch_sdpa(oracle_mod, causal):
     ref = torch.nn.functional.scaled_dot_product_attention(
         xt[None, None], kt[None, None], torch.from_numpy(v)[None, None], attn_mask=mask)[0, 0]
     np.testing.assert_allclose(out[0, 0], ref.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_per_head_rotations_equal_heads_equal_shared(oracle_mod):
+    """Variant: per-head rotations that are all the same matrix give the
+    shared-R method exactly."""
+    rng = np.random.default_rng(80)
+    qk = rng.standard_normal((2, 3, 64, 8))
+    v = rng.standard_normal((2, 3, 64, 8))
+    R = rng.standard_normal((2, 8, 4))
+    a = oracle_mod.forward(qk, v, R, 8, 16, True)
+    b = oracle_mod.forward(qk, v, np.stack([R] * 3), 8, 16, True)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_per_head_rotations_are_each_heads_own(oracle_mod):
+    """Variant: with R [H, nh, d, nb/2], slice (b, h) hashes with R[h] in every
+    batch: its buckets are the plain hash of that slice by R[h], and its output
+    and gradients equal the one-head method run on the slice alone with R[h]."""
+    rng = np.random.default_rng(81)
+    B, H, L, d, nb = 2, 3, 64, 8, 8
+    qk = rng.standard_normal((B, H, L, d))
+    v = rng.standard_normal((B, H, L, d))
+    g = rng.standard_normal((B, H, L, d))
+    R4 = rng.standard_normal((H, 2, d, nb // 2))
+    out, extra = oracle_mod.forward(qk, v, R4, nb, 16, True, return_all=True)
+    dqk, dv = oracle_mod.backward(qk, v, R4, g, nb, 16, True)
+    shared = oracle_mod.forward(qk, v, R4[0], nb, 16, True)
+    assert np.abs(out - shared).max() > 1e-3      # the heads' rotations matter
+    for b in range(B):
+        for h in range(H):
+            bk, _ = oracle_mod.hash(qk[b, h], R4[h], nb)
+            np.testing.assert_array_equal(extra["buckets"][b, h], bk)
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            one = oracle_mod.forward(qk[sl], v[sl], R4[h], nb, 16, True)
+            np.testing.assert_array_equal(out[b, h], one[0, 0])
+            gq, gv = oracle_mod.backward(qk[sl], v[sl], R4[h], g[sl], nb, 16, True)
+            np.testing.assert_array_equal(dqk[b, h], gq[0, 0])
+            np.testing.assert_array_equal(dv[b, h], gv[0, 0])
