@@ -99,7 +99,18 @@ def forward_roofline(w, ms_per_step):
     return {"t_roof_ms": t_roof, "frac": t_roof / ms_per_step, "steps": per}
 
 
-def measure(lsh, torch, w, steps, warmup, key_norm=False):
+def _rotations(w, per_head_r):
+    """The workload's R, or with per-head rotations R [H, nh, d, nb/2] drawn
+    from a generator seeded with the workload's seed + 1."""
+    import numpy as np
+    import workloads
+    if not per_head_r:
+        return workloads.make_inputs(w)[2]
+    rng = np.random.default_rng(w.seed + 1)
+    return rng.standard_normal((w.H, w.n_hashes, w.d, w.n_buckets // 2), dtype=np.float32)
+
+
+def measure(lsh, torch, w, steps, warmup, key_norm=False, per_head_r=False):
     """Times `steps` back-to-back forwards on synthetic inputs resident in HBM,
     then the per-kernel event intervals of a few more."""
     import numpy as np
@@ -110,8 +121,11 @@ def measure(lsh, torch, w, steps, warmup, key_norm=False):
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     qk_t = torch.from_numpy(qk).to(dev, dt)
     v_t = torch.from_numpy(v).to(dev, dt)
+    if per_head_r:
+        R = _rotations(w, True)
     R_t = torch.from_numpy(R).to(dev)
-    shape = lsh.shape_of(qk_t, w.n_buckets, w.n_hashes, w.chunk_len, w.causal, key_norm)
+    shape = lsh.shape_of(qk_t, w.n_buckets, w.n_hashes, w.chunk_len, w.causal, key_norm,
+                         per_head_r)
     ws = torch.empty(lsh.lsh_workspace_size("fwd", shape), dtype=torch.uint8, device=dev)
     out = torch.empty_like(qk_t)
 
@@ -183,7 +197,7 @@ def measure_projection(lsh, torch, w, steps, warmup, d_model=1024):
             "fwd_x_ms": f_ms, "fwd_x_tokens_per_s": w.B * w.L / (f_ms / 1e3)}
 
 
-def measure_training(lsh, torch, w, steps, warmup, key_norm=False):
+def measure_training(lsh, torch, w, steps, warmup, key_norm=False, per_head_r=False):
     """lsh_attention_fwd_train and lsh_attention_bwd at the workload's shape;
     the backward's work is counted per (query, window key) pair: the score
     and g . v recomputed, then dq, dk and dv, 10 d flops."""
@@ -194,9 +208,10 @@ def measure_training(lsh, torch, w, steps, warmup, key_norm=False):
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     qk_t = torch.from_numpy(qk).to(dev, dt)
     v_t = torch.from_numpy(v).to(dev, dt)
-    R_t = torch.from_numpy(R).to(dev)
+    R_t = torch.from_numpy(_rotations(w, True) if per_head_r else R).to(dev)
     g_t = torch.randn(qk_t.shape, generator=torch.Generator().manual_seed(w.seed)).to(dev, dt)
-    shape = lsh.shape_of(qk_t, w.n_buckets, w.n_hashes, w.chunk_len, w.causal, key_norm)
+    shape = lsh.shape_of(qk_t, w.n_buckets, w.n_hashes, w.chunk_len, w.causal, key_norm,
+                         per_head_r)
     out = torch.empty_like(qk_t)
     state = torch.empty(lsh.lsh_workspace_size("state", shape), dtype=torch.uint8, device=dev)
     ws = torch.empty(lsh.lsh_workspace_size("fwd", shape), dtype=torch.uint8, device=dev)
@@ -224,7 +239,8 @@ def measure_training(lsh, torch, w, steps, warmup, key_norm=False):
     # bf16 with chunk 64 runs on the matrix cores (bf16 products), else fp32 vector
     mfma = w.dtype == "bf16" and w.chunk_len == 64
     peak = PEAK_F16_TFLOPS if mfma else PEAK_FP32_TFLOPS
-    return {"workload": w.name, "key_norm": bool(key_norm), "fwd_train_ms": f_ms, "bwd_ms": b_ms,
+    return {"workload": w.name, "key_norm": bool(key_norm), "per_head_r": bool(per_head_r),
+            "fwd_train_ms": f_ms, "bwd_ms": b_ms,
             "train_step_tokens_per_s": w.B * w.L / ((f_ms + b_ms) / 1e3),
             "bwd_pair_flops": flops, "bwd_tflops": flops / b_ms / 1e9,
             "bwd_peak": "bf16 mfma" if mfma else "fp32 vector",
@@ -322,6 +338,9 @@ def main() -> int:
     ap.add_argument("--key-norm", action="store_true",
                     help="time the key-normalisation variant (forward, or with --train both "
                          "passes) instead of the headline line")
+    ap.add_argument("--per-head-r", action="store_true",
+                    help="time the per-head rotations variant (R [H, nh, d, nb/2]); combines "
+                         "with --key-norm and --train")
     args = ap.parse_args()
     if args.copy_calibration:
         import torch
@@ -363,14 +382,17 @@ def main() -> int:
     if args.train:
         print(json.dumps(measure_training(lsh, torch, workloads.WORKLOADS[
             args.workload or workloads.HEADLINE], min(args.steps, 10), args.warmup,
-            key_norm=args.key_norm)), flush=True)
+            key_norm=args.key_norm, per_head_r=args.per_head_r)), flush=True)
         return 0
 
-    if args.key_norm:
+    if args.key_norm or args.per_head_r:
         name = args.workload or workloads.HEADLINE
         w = workloads.WORKLOADS[name]
-        r = measure(lsh, torch, w, args.steps, args.warmup, key_norm=True)
-        print(json.dumps({"variant": "key_norm", "workload": name, "config": w.describe(),
+        r = measure(lsh, torch, w, args.steps, args.warmup, key_norm=args.key_norm,
+                    per_head_r=args.per_head_r)
+        variant = "+".join(n for n, on in (("key_norm", args.key_norm),
+                                           ("per_head_r", args.per_head_r)) if on)
+        print(json.dumps({"variant": variant, "workload": name, "config": w.describe(),
                           "ms_per_step": r["ms_per_step"],
                           "tokens_per_s": w.B * w.L / (r["ms_per_step"] / 1e3),
                           "kernels_ms": r["kernels"],

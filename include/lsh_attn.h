@@ -28,7 +28,9 @@
  *  - Tensors are dense row-major with these shapes (T = B*H):
  *      qk, v, out      [B, H, L, d]            dtype = shape->dtype
  *      R               [n_hashes, d, n_buckets/2]   float32, shared by all
- *                                              batches and heads
+ *                                              batches and heads; with
+ *                                              LSH_PER_HEAD_R [H, n_hashes,
+ *                                              d, n_buckets/2]
  *      buckets         [B, H, n_hashes, L]     int32, by original position
  *      perm            [B, H, n_hashes, L]     int32, perm[s] = position in
  *                                              sorted slot s of that round
@@ -66,7 +68,12 @@ enum {
      * method normalises keys); queries keep their length and the hash is
      * unchanged. A zero vector gives a zero key. The backward differentiates
      * through the norm. */
-    LSH_KEY_NORM = 1
+    LSH_KEY_NORM = 1,
+    /* R is [H, n_hashes, d, n_buckets/2]: head h hashes with its own
+     * rotations R[h] in every batch, instead of one R shared by all heads (the
+     * glossary's R has no head axis; this is the alternative of giving each
+     * head independent random rotations). Only the hash reads R. */
+    LSH_PER_HEAD_R = 2
 };
 
 enum {
@@ -86,7 +93,8 @@ enum {
  *                into equal chunks).
  *   causal       0 or 1: key position must not exceed the query position.
  *   dtype        LSH_F32 or LSH_BF16 for qk, v and out.
- *   flags        0 or LSH_KEY_NORM (other bits: LSH_ERR_ARG).
+ *   flags        0, or LSH_KEY_NORM and/or LSH_PER_HEAD_R (other bits:
+ *                LSH_ERR_ARG).
  * Also required: B*H*n_hashes*L < 2^31. */
 typedef struct lsh_shape {
     int32_t B, H, L, d;

@@ -21,6 +21,7 @@ from ._binding import (  # noqa: F401
     LSH_BF16,
     LSH_F32,
     LSH_KEY_NORM,
+    LSH_PER_HEAD_R,
     LSHAttention,
     LshError,
     Shape,
@@ -32,6 +33,7 @@ from ._binding import (  # noqa: F401
     hash,
     library_path,
     load_library,
+    rounds_of,
     lsh_attention_fwd,
     lsh_attention_fwd_timed,
     lsh_attention_bwd,

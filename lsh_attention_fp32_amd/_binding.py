@@ -9,6 +9,7 @@ import torch
 LSH_F32 = 0
 LSH_BF16 = 1
 LSH_KEY_NORM = 1   # lsh_shape_t.flags bit: keys as unit vectors in the scores
+LSH_PER_HEAD_R = 2  # lsh_shape_t.flags bit: R is [H, n_hashes, d, n_buckets/2]
 _DTYPES = {torch.float32: LSH_F32, torch.bfloat16: LSH_BF16}
 _ERRORS = {-1: "LSH_ERR_ARG", -2: "LSH_ERR_WORKSPACE", -3: "LSH_ERR_HIP", -4: "LSH_ERR_UNSUPPORTED"}
 
@@ -101,7 +102,7 @@ def _stream(stream):
 
 
 def shape_of(qk: torch.Tensor, n_buckets: int, n_hashes: int, chunk_len: int,
-             causal: bool, key_norm: bool = False) -> Shape:
+             causal: bool, key_norm: bool = False, per_head_r: bool = False) -> Shape:
     """Shape for qk of shape [B, H, L, d] (float32 or bfloat16)."""
     if qk.dim() != 4:
         raise ValueError(f"qk must be [B, H, L, d], got {tuple(qk.shape)}")
@@ -109,7 +110,18 @@ def shape_of(qk: torch.Tensor, n_buckets: int, n_hashes: int, chunk_len: int,
         raise ValueError(f"qk dtype must be float32 or bfloat16, got {qk.dtype}")
     B, H, L, d = qk.shape
     return Shape(B, H, L, d, n_buckets, n_hashes, chunk_len, int(bool(causal)), _DTYPES[qk.dtype],
-                 LSH_KEY_NORM if key_norm else 0)
+                 (LSH_KEY_NORM if key_norm else 0) | (LSH_PER_HEAD_R if per_head_r else 0))
+
+
+def rounds_of(R) -> tuple[int, bool]:
+    """(n_hashes, per-head): R [n_hashes, d, nb/2] is shared by every head,
+    R [H, n_hashes, d, nb/2] gives each head its own rotations."""
+    if R.dim() == 4:
+        return R.shape[1], True
+    if R.dim() != 3:
+        raise ValueError(f"R must be [n_hashes, d, nb/2] or [H, n_hashes, d, nb/2], "
+                         f"got {tuple(R.shape)}")
+    return R.shape[0], False
 
 
 # ---------------------------------------------------------------- C-named calls
@@ -208,7 +220,8 @@ def _rounds_shape(shape: Shape):
 
 def hash(qk, R, n_buckets: int, ws=None, stream=None):
     """Returns (buckets [B,H,n_hashes,L] int32, number of token-rounds re-decided in fp64)."""
-    shape = shape_of(qk, n_buckets, R.shape[0], 1, False)
+    nh, per_head = rounds_of(R)
+    shape = shape_of(qk, n_buckets, nh, 1, False, per_head_r=per_head)
     shape.chunk_len = max(1, shape.L)  # any divisor of L: the hash does not use it
     buckets = torch.empty(_rounds_shape(shape), dtype=torch.int32, device=qk.device)
     ws = _workspace("hash", shape, qk.device) if ws is None else ws
@@ -250,7 +263,8 @@ def unsort_combine(o_sorted, lse_sorted, inv, dtype=torch.bfloat16, stream=None)
 def attention_fwd(qk, v, R, n_buckets: int, chunk_len: int, causal: bool, ws=None, out=None,
                   stream=None, key_norm: bool = False):
     """Whole forward; returns out [B,H,L,d] in qk's dtype."""
-    shape = shape_of(qk, n_buckets, R.shape[0], chunk_len, causal, key_norm)
+    nh, per_head = rounds_of(R)
+    shape = shape_of(qk, n_buckets, nh, chunk_len, causal, key_norm, per_head)
     if v.shape != qk.shape or v.dtype != qk.dtype:
         raise ValueError("v must match qk in shape and dtype")
     out = torch.empty_like(qk) if out is None else out
@@ -260,7 +274,7 @@ def attention_fwd(qk, v, R, n_buckets: int, chunk_len: int, causal: bool, ws=Non
 
 
 def _x_shape(x, w_qk, w_v, n_heads: int, n_buckets: int, n_hashes: int, chunk_len: int,
-             causal: bool, key_norm: bool = False) -> Shape:
+             causal: bool, key_norm: bool = False, per_head_r: bool = False) -> Shape:
     if x.dim() != 3:
         raise ValueError(f"x must be [B, L, d_model], got {tuple(x.shape)}")
     if x.dtype not in _DTYPES:
@@ -271,7 +285,8 @@ def _x_shape(x, w_qk, w_v, n_heads: int, n_buckets: int, n_hashes: int, chunk_le
             or w_qk.dtype != x.dtype or w_v.dtype != x.dtype):
         raise ValueError("w_qk and w_v must be [H * d, d_model] in x's dtype")
     return Shape(B, n_heads, L, n_out // n_heads, n_buckets, n_hashes, chunk_len,
-                 int(bool(causal)), _DTYPES[x.dtype], LSH_KEY_NORM if key_norm else 0)
+                 int(bool(causal)), _DTYPES[x.dtype],
+                 (LSH_KEY_NORM if key_norm else 0) | (LSH_PER_HEAD_R if per_head_r else 0))
 
 
 def qkv_project(x, w_qk, w_v, n_heads: int, stream=None):
@@ -288,7 +303,8 @@ def qkv_project(x, w_qk, w_v, n_heads: int, stream=None):
 def attention_fwd_x(x, w_qk, w_v, R, n_heads: int, n_buckets: int, chunk_len: int, causal: bool,
                     ws=None, out=None, stream=None, key_norm: bool = False):
     """Projections, then the whole forward; returns out [B, H, L, d] in x's dtype."""
-    shape = _x_shape(x, w_qk, w_v, n_heads, n_buckets, R.shape[0], chunk_len, causal, key_norm)
+    nh, per_head = rounds_of(R)
+    shape = _x_shape(x, w_qk, w_v, n_heads, n_buckets, nh, chunk_len, causal, key_norm, per_head)
     out = torch.empty((shape.B, shape.H, shape.L, shape.d), dtype=x.dtype,
                       device=x.device) if out is None else out
     ws = _workspace("fwd_x", shape, x.device) if ws is None else ws
@@ -299,7 +315,8 @@ def attention_fwd_x(x, w_qk, w_v, R, n_heads: int, n_buckets: int, chunk_len: in
 def attention_fwd_train(qk, v, R, n_buckets: int, chunk_len: int, causal: bool, stream=None,
                         key_norm: bool = False):
     """Training forward; returns (out [B,H,L,d], state) for attention_bwd."""
-    shape = shape_of(qk, n_buckets, R.shape[0], chunk_len, causal, key_norm)
+    nh, per_head = rounds_of(R)
+    shape = shape_of(qk, n_buckets, nh, chunk_len, causal, key_norm, per_head)
     if v.shape != qk.shape or v.dtype != qk.dtype:
         raise ValueError("v must match qk in shape and dtype")
     out = torch.empty_like(qk)
@@ -334,7 +351,7 @@ class LSHAttention(torch.autograd.Function):
         out, state = attention_fwd_train(qk, v, R.contiguous(), n_buckets, chunk_len, causal,
                                          key_norm=key_norm)
         ctx.save_for_backward(qk, v, out, state)
-        ctx.cfg = (n_buckets, R.shape[0], chunk_len, causal)
+        ctx.cfg = (n_buckets, rounds_of(R)[0], chunk_len, causal)
         ctx.key_norm = key_norm
         return out
 

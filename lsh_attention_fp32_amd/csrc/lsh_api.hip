@@ -47,8 +47,9 @@ int validate(const lsh_shape_t* s) {
         return fail(LSH_ERR_ARG, "causal must be 0 or 1 (got %d)", s->causal);
     if (s->dtype != LSH_F32 && s->dtype != LSH_BF16)
         return fail(LSH_ERR_ARG, "dtype must be LSH_F32 or LSH_BF16 (got %d)", s->dtype);
-    if (s->flags & ~LSH_KEY_NORM)
-        return fail(LSH_ERR_ARG, "unknown flags 0x%x (only LSH_KEY_NORM)", (unsigned)s->flags);
+    if (s->flags & ~(LSH_KEY_NORM | LSH_PER_HEAD_R))
+        return fail(LSH_ERR_ARG, "unknown flags 0x%x (only LSH_KEY_NORM, LSH_PER_HEAD_R)",
+                    (unsigned)s->flags);
     if ((int64_t)s->B * s->H * s->n_hashes * s->L >= ((int64_t)1 << 31))
         return fail(LSH_ERR_ARG, "B*H*n_hashes*L must stay below 2^31");
     if (s->d != 64 && s->d != 128)

@@ -48,26 +48,26 @@ static constexpr float kTwoM24 = 5.9604644775390625e-8f;   // 2^-24
 
 // ------------------------------------------------------------------ workspace
 static size_t rfrag_elems(const Dims& d) {
-    // [nh][ntiles][d/16 k-steps][64 lanes][8] fp16
-    return (size_t)d.nh * hash_ntiles(d) * kHashColTile * d.d;
+    // [nr][ntiles][d/16 k-steps][64 lanes][8] fp16
+    return (size_t)d.nr * hash_ntiles(d) * kHashColTile * d.d;
 }
 
 static size_t rt_elems(const Dims& d) {
-    // [nh][ntiles * 32 columns][d] float32
-    return (size_t)d.nh * hash_ntiles(d) * kHashColTile * d.d;
+    // [nr][ntiles * 32 columns][d] float32
+    return (size_t)d.nr * hash_ntiles(d) * kHashColTile * d.d;
 }
 
 size_t hash_workspace_bytes(const Dims& d) {
     size_t b = 256;                                              // counter
-    b += align_up(sizeof(float) * 3 * d.nh, 256);                // rnorm, rnorm_s, resn_s
-    b += align_up(sizeof(float) * d.nh * hash_ntiles(d), 256);   // tmax
+    b += align_up(sizeof(float) * 3 * d.nr, 256);                // rnorm, rnorm_s, resn_s
+    b += align_up(sizeof(float) * d.nr * hash_ntiles(d), 256);   // tmax
     b += align_up(sizeof(uint16_t) * rfrag_elems(d), 256);       // rfrag
     b += align_up(sizeof(float) * rt_elems(d), 256);             // rt
     b += align_up(sizeof(RefineItem) * (size_t)queue_tokens(d) * d.nh, 256);   // queue
     b += align_up(sizeof(int32_t) * 2 * (size_t)queue_tokens(d) / kWave * d.nh, 256);   // rcount
-    b += align_up(sizeof(int32_t) * d.nh, 256);                                          // scount
-    b += align_up(sizeof(int32_t) * (size_t)queue_tokens(d) * d.nh, 256);                // slist
-    b += align_up(sizeof(uint64_t) * (size_t)queue_tokens(d) * d.nh, 256);               // sbest
+    b += align_up(sizeof(int32_t) * d.nr, 256);                                          // scount
+    b += align_up(sizeof(int32_t) * (size_t)queue_tokens(d) * d.nr, 256);                // slist
+    b += align_up(sizeof(uint64_t) * (size_t)queue_tokens(d) * d.nr, 256);               // sbest
     return b;
 }
 
@@ -78,11 +78,11 @@ HashWorkspace carve_hash_workspace(void* ws, const Dims& d) {
     w.vmax = (uint32_t*)(p + 3 * sizeof(int32_t));
     p += 256;
     w.rnorm = (float*)p;
-    w.rnorm_s = w.rnorm + d.nh;
-    w.resn_s = w.rnorm + 2 * d.nh;
-    p += align_up(sizeof(float) * 3 * d.nh, 256);
+    w.rnorm_s = w.rnorm + d.nr;
+    w.resn_s = w.rnorm + 2 * d.nr;
+    p += align_up(sizeof(float) * 3 * d.nr, 256);
     w.tmax = (float*)p;
-    p += align_up(sizeof(float) * d.nh * hash_ntiles(d), 256);
+    p += align_up(sizeof(float) * d.nr * hash_ntiles(d), 256);
     w.rfrag = (uint16_t*)p;
     p += align_up(sizeof(uint16_t) * rfrag_elems(d), 256);
     w.rt = (float*)p;
@@ -92,9 +92,9 @@ HashWorkspace carve_hash_workspace(void* ws, const Dims& d) {
     w.rcount = (int32_t*)p;
     p += align_up(sizeof(int32_t) * 2 * (size_t)queue_tokens(d) / kWave * d.nh, 256);
     w.scount = (int32_t*)p;
-    p += align_up(sizeof(int32_t) * d.nh, 256);
+    p += align_up(sizeof(int32_t) * d.nr, 256);
     w.slist = (int32_t*)p;
-    p += align_up(sizeof(int32_t) * (size_t)queue_tokens(d) * d.nh, 256);
+    p += align_up(sizeof(int32_t) * (size_t)queue_tokens(d) * d.nr, 256);
     w.sbest = (uint64_t*)p;
     return w;
 }
@@ -316,7 +316,7 @@ __device__ __forceinline__ void refine_region(const T* __restrict__ qk,
             const int i = it.item % dm.L, rest = it.item / dm.L;
             const int r = rest % dm.nh, bh = rest / dm.nh;
             const T* x = qk + ((int64_t)bh * dm.L + i) * D + 4 * l4;
-            const float* Rr = rt + (int64_t)r * hpad * D;      // [column][k]
+            const float* Rr = rt + (int64_t)r_round(dm, bh, r) * hpad * D;   // [column][k]
             const float* ra = Rr + (int64_t)(va ? it.a : 0) * D + 4 * l4;
             const float* rb = Rr + (int64_t)(vb ? it.b : 0) * D + 4 * l4;
 #pragma unroll
@@ -349,7 +349,8 @@ __device__ __forceinline__ void refine_region(const T* __restrict__ qk,
     }
     for (int q = lane; q < n1; q += kWave) {
         const int32_t item = rq[region_size - 1 - q].item;
-        const int r = (item / dm.L) % dm.nh;
+        const int rest = item / dm.L;
+        const int r = r_round(dm, rest / dm.nh, rest % dm.nh);   // lists are per R round
         const int slot = atomicAdd(&scount[r], 1);
         slist[(int64_t)r * cap + slot] = item;
         sbest[(int64_t)r * cap + slot] = 0ull;
@@ -393,7 +394,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void h
     const int half = dm.nb / 2;
     const int ntiles = (half + kHashColTile - 1) / kHashColTile;
     const int total = dm.nh * ntiles;
-    const int64_t tok0 = (int64_t)blockIdx.x * TOK_WG + (int64_t)wave * TOK_WAVE;
+    // The workgroup's tokens: TOK_WG consecutive token-heads. With per-head
+    // rotations they stay inside one (batch, head), whose R rounds start at vr0.
+    int64_t wg_first = (int64_t)blockIdx.x * TOK_WG, wg_end = dm.T;
+    int vr0 = 0;
+    if (dm.per_head_r) {
+        const int nblk = (dm.L + TOK_WG - 1) / TOK_WG;
+        const int64_t bh = blockIdx.x / nblk;
+        wg_first = bh * dm.L + (int64_t)(blockIdx.x - bh * nblk) * TOK_WG;
+        wg_end = (bh + 1) * dm.L;
+        vr0 = r_round(dm, bh, 0);
+    }
+    const int64_t tok0 = wg_first + (int64_t)wave * TOK_WAVE;
+    const u32x4* rf = rfrag + (int64_t)vr0 * ntiles * TILE_U4;   // this head's R tiles
     // this wave's queue region: its tokens, every round
     const int64_t region = (int64_t)blockIdx.x * 4 + wave;
     RegionWriter qw{queue + region * TOK_WAVE * dm.nh, TOK_WAVE * dm.nh, 0, 0};
@@ -412,15 +425,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void h
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             ux[f][s] = (u32x4){0u, 0u, 0u, 0u};
-            if (tok < dm.T) ux[f][s] = ((const u32x4*)(qk + tok * D))[2 * s + (lane >> 5)];
+            if (tok < wg_end) ux[f][s] = ((const u32x4*)(qk + tok * D))[2 * s + (lane >> 5)];
         }
     }
     __shared__ uint32_t wvmax[4];
     if (v) {
         // this workgroup's tokens are one contiguous run of value rows
         constexpr int NV = TOK_WG * (D / 8) / 256;   // 16-byte pieces per thread
-        const int64_t first = (int64_t)blockIdx.x * TOK_WG;
-        const int64_t nvec = min((int64_t)TOK_WG, dm.T - first) * (D / 8);
+        const int64_t first = wg_first;
+        const int64_t nvec = min((int64_t)TOK_WG, wg_end - first) * (D / 8);
         const u32x4* src = (const u32x4*)(v + first * D);
         u32x4 vw[NV];
 #pragma unroll
@@ -469,12 +482,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void h
 #pragma unroll
     for (int f = 0; f < TOKF; ++f) {
         const int64_t tok = tok0 + f * 32 + (lane & 31);
-        tok_live[f] = tok < dm.T;
+        tok_live[f] = tok < wg_end;
         const int64_t bh = tok / dm.L, i = tok - bh * dm.L;
         item0[f] = tok_live[f] ? (int32_t)(bh * dm.nh * dm.L + i) : 0;
     }
 
-    for (int i = threadIdx.x; i < TILE_U4; i += 256) lds[0][i] = rfrag[i];
+    for (int i = threadIdx.x; i < TILE_U4; i += 256) lds[0][i] = rf[i];
     __syncthreads();
     if (v && threadIdx.x == 0)
         atomicMax(vmax, max(max(wvmax[0], wvmax[1]), max(wvmax[2], wvmax[3])));
@@ -524,7 +537,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void h
             }
         }
         if (t != ntiles - 1) return;
-        const float rn_s = rnorm[dm.nh + r], res_s = rnorm[2 * dm.nh + r];
+        const float rn_s = rnorm[dm.nr + vr0 + r], res_s = rnorm[2 * dm.nr + vr0 + r];
         const float Ea = 2.f * (res_s + kAcc * rn_s), Eb = 2.f * kFlushX * rn_s;
 #pragma unroll
         for (int f = 0; f < TOKF; ++f) {
@@ -564,7 +577,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void h
     // latency is hidden behind a whole step.
     auto fetch = [&](int t, u32x4(&pre)[PRE]) {
         if (t < total) {
-            const u32x4* src = rfrag + (int64_t)t * TILE_U4;
+            const u32x4* src = rf + (int64_t)t * TILE_U4;
 #pragma unroll
             for (int j = 0; j < PRE; ++j) pre[j] = src[threadIdx.x + j * 256];
         }
@@ -596,8 +609,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void h
 
 // ------------------------------------------------------------------ fast pass (fp32 FMA)
 // One thread per (token, round); the block's round is uniform so R reads are
-// scalar. Used for fp32 inputs (and any dtype when requested).
-template <int D, typename T>
+// scalar (with per-head rotations, PH, each lane reads its own head's R).
+// Used for fp32 inputs (and any dtype when requested).
+template <int D, typename T, bool PH>
 __global__ __launch_bounds__(256) void hash_valu_kernel(const T* __restrict__ qk,
                                                         const float* __restrict__ R,
                                                         const float* __restrict__ rnorm, Dims dm,
@@ -625,7 +639,8 @@ __global__ __launch_bounds__(256) void hash_valu_kernel(const T* __restrict__ qk
         x[k] = live ? IO<T>::load(qk, tok * D + k) : 0.f;
         xn2 = fmaf(x[k], x[k], xn2);
     }
-    const float* Rr = R + (int64_t)r * D * half;
+    const int rr = (PH && live) ? r_round(dm, tok / dm.L, r) : r;   // R round
+    const float* Rr = R + (int64_t)rr * D * half;
     float v1 = -1.f, v2 = -1.f, v3 = -1.f;
     int i1 = 0, i2 = 0;
     bool neg1 = false;
@@ -645,7 +660,7 @@ __global__ __launch_bounds__(256) void hash_valu_kernel(const T* __restrict__ qk
     if (half == 1) { v2 = 0.f; v3 = 0.f; i2 = 0; }     // a single column: compare with -p only
     if (half == 2) v3 = 0.f;
     const float xn = sqrtf(xn2) * (1.0f + (float)(D + 4) * kTwoM24);
-    const float thr = 2.f * kCoef * xn * rnorm[r] + v1 * 9.5367431640625e-7f + 1e-30f;
+    const float thr = 2.f * kCoef * xn * rnorm[rr] + v1 * 9.5367431640625e-7f + 1e-30f;
     int mode = classify(v1, v2, v3, thr);
     if (half == 1) mode = (v1 > thr) ? -1 : 1;
     int64_t item = 0;
@@ -662,9 +677,9 @@ __global__ __launch_bounds__(256) void hash_valu_kernel(const T* __restrict__ qk
 }
 
 // ------------------------------------------------------------------ re-decision, part 2
-// Every column for the listed items of a round, grouped so that a
+// Every column for the listed items of an R round, grouped so that a
 // workgroup reads one 32-column tile of R once for 64 items. Block (t, r, z)
-// takes groups z, z + Z, ... of round r's list. Each (item, column) product is
+// takes groups z, z + Z, ... of R round r's list. Each (item, column) product is
 // summed in fp64; the best of the tile goes into the item's key by a 64-bit
 // atomic max. Key = bits of |p| (a non-negative double, so integer order is
 // float order) with the low 12 bits replaced by 4095 - bucket: equal |p| then
@@ -782,12 +797,12 @@ static hipError_t launch_scan(const T* qk, const Dims& d, int32_t* buckets, cons
     const int64_t cap = queue_tokens(d);
     // enough groups for a few thousand listed items per round; more loop
     const unsigned z = (unsigned)std::min<int64_t>(16, (cap + 63) / 64);
-    const dim3 sgrid((unsigned)hash_ntiles(d), (unsigned)d.nh, z);
+    const dim3 sgrid((unsigned)hash_ntiles(d), (unsigned)d.nr, z);
     if (d.d == 64)
         hash_scan_kernel<64, T><<<sgrid, 256, 0, st>>>(qk, w.rt, d, w.scount, w.slist, w.sbest, cap);
     else
         hash_scan_kernel<128, T><<<sgrid, 256, 0, st>>>(qk, w.rt, d, w.scount, w.slist, w.sbest, cap);
-    hash_scan_finish_kernel<<<dim3(4, (unsigned)d.nh + 1), 256, 0, st>>>(
+    hash_scan_finish_kernel<<<dim3(4, (unsigned)d.nr + 1), 256, 0, st>>>(
         w.scount, w.slist, w.sbest, cap, buckets, w.rcount, nregions, w.counter);
     return mark(st, ev, nev, names, "hash_refine_scan");
 }
@@ -798,7 +813,7 @@ hipError_t launch_hash(const void* qk, const float* R, const Dims& d, int32_t* b
     const int half = d.nb / 2;
     const int ntiles = hash_ntiles(d);
     hipError_t e;
-    const dim3 pgrid((unsigned)ntiles, (unsigned)d.nh);
+    const dim3 pgrid((unsigned)ntiles, (unsigned)d.nr);   // every R round
     rmax_kernel<<<pgrid, 256, 0, st>>>(R, d.d, half, ntiles, w.tmax, w.counter, w.rnorm, w.scount);
     rprep_kernel<<<pgrid, 256, 0, st>>>(R, d.d, half, ntiles, w.tmax, w.rnorm, w.rt, w.rfrag);
     if ((e = mark(st, ev, nev, names, "hash_prep")) != hipSuccess) return e;
@@ -808,9 +823,13 @@ hipError_t launch_hash(const void* qk, const float* R, const Dims& d, int32_t* b
 #endif
         constexpr int TOKF = LSH_HASH_TOKF;
         constexpr int per_wave = 32 * TOKF, per_wg = 4 * per_wave;
-        static_assert(per_wg <= kQueuePad, "queue regions must fit the padded capacity");
+        static_assert(per_wg <= kQueuePad && kQueuePad % per_wg == 0,
+                      "queue regions must fit the padded capacity");
         static_assert(per_wave >= kWave, "the re-decision pass reads 64 entries of a region ahead");
-        const unsigned grid = (unsigned)((d.T + per_wg - 1) / per_wg);
+        // with per-head rotations each (batch, head) starts a new workgroup
+        const unsigned grid = d.per_head_r
+                                  ? (unsigned)((int64_t)d.B * d.H * ((d.L + per_wg - 1) / per_wg))
+                                  : (unsigned)((d.T + per_wg - 1) / per_wg);
         const uint16_t* x = (const uint16_t*)qk;
         const int64_t cap = queue_tokens(d);
         if (d.d == 64)
@@ -827,14 +846,18 @@ hipError_t launch_hash(const void* qk, const float* R, const Dims& d, int32_t* b
         const float* x = (const float*)qk;
         dim3 grid((unsigned)((d.T + 255) / 256), (unsigned)d.nh);
         const int64_t cap = queue_tokens(d);
-        if (d.d == 64)
-            hash_valu_kernel<64, float><<<grid, 256, 0, st>>>(x, R, w.rnorm, d, buckets, w.queue,
-                                                              w.rcount, w.rt, w.scount, w.slist,
-                                                              w.sbest, cap);
-        else
-            hash_valu_kernel<128, float><<<grid, 256, 0, st>>>(x, R, w.rnorm, d, buckets, w.queue,
-                                                               w.rcount, w.rt, w.scount, w.slist,
-                                                               w.sbest, cap);
+#define LSH_HASH_VALU(DD, PH)                                                                  \
+    hash_valu_kernel<DD, float, PH><<<grid, 256, 0, st>>>(x, R, w.rnorm, d, buckets, w.queue,   \
+                                                          w.rcount, w.rt, w.scount, w.slist,   \
+                                                          w.sbest, cap)
+        if (d.d == 64) {
+            if (d.per_head_r) LSH_HASH_VALU(64, true);
+            else LSH_HASH_VALU(64, false);
+        } else {
+            if (d.per_head_r) LSH_HASH_VALU(128, true);
+            else LSH_HASH_VALU(128, false);
+        }
+#undef LSH_HASH_VALU
         if ((e = mark(st, ev, nev, names, "hash_fast_fp32")) != hipSuccess) return e;
         return launch_scan(x, d, buckets, w, (int64_t)grid.x * 4 * d.nh, st, ev, nev, names);
     }

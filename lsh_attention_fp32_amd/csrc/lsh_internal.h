@@ -21,6 +21,9 @@ struct Dims {
     int32_t nb, nh, m, causal;
     int32_t dtype;
     int32_t key_norm;   // keys as unit vectors in the scores (LSH_KEY_NORM)
+    int32_t per_head_r; // R is [H, nh, d, nb/2]: each head its own rotations
+    int32_t nr;         // rounds of R: nh, or H*nh with per-head rotations; head h's
+                        // round r is R round h*nh + r (a "virtual round")
     int64_t T;        // B*H*L token-heads
     int64_t segs;     // B*H*nh (batch, head, round) segments
 };
@@ -31,6 +34,8 @@ inline Dims make_dims(const lsh_shape_t& s) {
     d.nb = s.n_buckets; d.nh = s.n_hashes; d.m = s.chunk_len; d.causal = s.causal;
     d.dtype = s.dtype;
     d.key_norm = (s.flags & LSH_KEY_NORM) ? 1 : 0;
+    d.per_head_r = (s.flags & LSH_PER_HEAD_R) ? 1 : 0;
+    d.nr = d.per_head_r ? s.H * s.n_hashes : s.n_hashes;
     d.T = (int64_t)s.B * s.H * s.L;
     d.segs = (int64_t)s.B * s.H * s.n_hashes;
     return d;
@@ -56,14 +61,24 @@ struct RefineItem {
 // wave appends without any atomic: two-candidate items fill its region from
 // the front, full scans from the back, and the wave stores the two counts
 // (rcount[2 * region], rcount[2 * region + 1]) when it ends. Capacity covers
-// T rounded up to kQueuePad tokens, every round.
+// T rounded up to kQueuePad tokens, every round -- with per-head rotations,
+// where a workgroup's tokens stay inside one (batch, head), every L is
+// rounded up (a sum of round-ups is at least the round-up of the sum).
 constexpr int kQueuePad = 256;
-inline int64_t queue_tokens(const Dims& d) { return (d.T + kQueuePad - 1) / kQueuePad * kQueuePad; }
+inline int64_t queue_tokens(const Dims& d) {
+    if (d.per_head_r) return (int64_t)d.B * d.H * ((d.L + kQueuePad - 1) / kQueuePad * kQueuePad);
+    return (d.T + kQueuePad - 1) / kQueuePad * kQueuePad;
+}
+
+// R round used by round r of (batch, head) bh.
+__host__ __device__ inline int r_round(const Dims& d, int64_t bh, int r) {
+    return d.per_head_r ? (int)(bh % d.H) * d.nh + r : r;
+}
 
 struct HashWorkspace {
     int32_t* counter;     // [0]: items re-decided (the public count)
     uint32_t* vmax;       // max|v| (bf16 bits) when the fast pass is asked to fold it in
-    // Per-round bounds, each [nh] and contiguous, rounded up (atomic max over
+    // Per R-round bounds, each [nr] and contiguous, rounded up (atomic max over
     // column tiles). With R_s = R * 2^e_r, e_r the power of two that brings
     // max|R| of round r into [2^14, 2^15):
     //   rnorm   max column 2-norm of R
@@ -73,17 +88,17 @@ struct HashWorkspace {
     float* rnorm;
     float* rnorm_s;
     float* resn_s;
-    float* tmax;          // [nh][ntiles] max |R| per column tile
+    float* tmax;          // [nr][ntiles] max |R| per column tile
     uint16_t* rfrag;      // fp16(R_s) in matrix-core fragment order
-    float* rt;            // R transposed to [nh][ntiles*32][d], fp32
+    float* rt;            // R transposed to [nr][ntiles*32][d], fp32
     RefineItem* queue;    // [queue_tokens * nh]
     int32_t* rcount;      // [2 * queue_tokens * nh / 64]: per-region counts
-    // Full-scan items regrouped by round for the scan pass: per round r,
+    // Full-scan items regrouped by R round for the scan pass: per R round r,
     // scount[r] items, slist[r * queue_tokens + i] their flat bucket index and
     // sbest[r * queue_tokens + i] the best packed key found so far.
-    int32_t* scount;      // [nh]
-    int32_t* slist;       // [nh * queue_tokens]
-    uint64_t* sbest;      // [nh * queue_tokens]
+    int32_t* scount;      // [nr]
+    int32_t* slist;       // [nr * queue_tokens]
+    uint64_t* sbest;      // [nr * queue_tokens]
 };
 size_t hash_workspace_bytes(const Dims& d);
 HashWorkspace carve_hash_workspace(void* ws, const Dims& d);

@@ -57,7 +57,7 @@ def _shape(**kw):
     (dict(chunk_len=0), -1), (dict(L=100, chunk_len=64), -1), (dict(causal=2), -1),
     (dict(dtype=7), -1), (dict(B=-1), -1), (dict(d=96), -4), (dict(n_buckets=8192), -4),
     (dict(B=64, H=64, L=65536, n_hashes=8, chunk_len=64), -1),
-    (dict(flags=2), -1), (dict(flags=-1), -1),
+    (dict(flags=4), -1), (dict(flags=-1), -1),
 ])
 def test_workspace_size_rejects_bad_shapes(lib, kw, code):
     with pytest.raises(lsh.LshError) as ei:
@@ -171,3 +171,27 @@ def test_key_norm_workspace_holds_one_float_per_token(lib):
         assert lsh.lsh_workspace_size(stage, kn) == lsh.lsh_workspace_size(stage, base)
     for stage in ("fwd", "fwd_x", "bwd"):
         assert lsh.lsh_workspace_size(stage, kn) == lsh.lsh_workspace_size(stage, base) + extra
+
+
+def test_per_head_rotations_workspace(lib):
+    """LSH_PER_HEAD_R keeps R-derived tables per (head, round): the hash
+    workspace grows with H, and with one head it is the shared-R size."""
+    one = _shape(H=1)
+    assert lsh.lsh_workspace_size("hash", _shape(H=1, flags=lsh.LSH_PER_HEAD_R)) == \
+        lsh.lsh_workspace_size("hash", one)
+    assert lsh.lsh_workspace_size("hash", _shape(H=4, flags=lsh.LSH_PER_HEAD_R)) > \
+        lsh.lsh_workspace_size("hash", _shape(H=4))
+    both = lsh.LSH_PER_HEAD_R | lsh.LSH_KEY_NORM
+    assert lsh.lsh_workspace_size("fwd", _shape(flags=both)) >= \
+        lsh.lsh_workspace_size("fwd", _shape(flags=lsh.LSH_KEY_NORM))
+    # the per-head queue rounds each (batch, head) up: L = 300 pads to 512 tokens
+    assert lsh.lsh_workspace_size("hash", _shape(L=300, chunk_len=300, flags=lsh.LSH_PER_HEAD_R)) > \
+        lsh.lsh_workspace_size("hash", _shape(L=300, chunk_len=300))
+
+
+def test_rounds_of_reads_the_rotation_layout():
+    import torch
+    assert lsh.rounds_of(torch.empty(3, 64, 8)) == (3, False)
+    assert lsh.rounds_of(torch.empty(2, 3, 64, 8)) == (3, True)
+    with pytest.raises(ValueError):
+        lsh.rounds_of(torch.empty(64, 8))
