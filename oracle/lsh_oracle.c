@@ -46,10 +46,16 @@
  *     no de-duplication of keys seen in several rounds;
  *   - ties in the argmax go to the first (lowest) index, as torch's argmax.
  * Variant (key_norm = 1): the key side of a score uses the unit vector
- * x_j / |x_j| ([WALKTHRU] "1 LSH Attention": the formula, stripped on the
- * page, that makes a key share its query's bucket); queries stay as they are
- * and the hash is unchanged (it is invariant to positive scaling). A zero
- * vector keeps a zero key.
+ * x_j / |x_j| ([WALKTHRU] "1 LSH Attention": its stripped formula is where
+ * the method normalises keys); queries stay as they are and the hash is
+ * unchanged (it is invariant to positive scaling). A zero vector keeps a zero
+ * key.
+ * Variant (per_head_r = 1): R is [H, n_hashes, d, n_buckets/2] and head h
+ * hashes with R[h] in every batch.
+ * F1, the chunked feed-forward ([WALKTHRU] "3 分塊"; [SCHOLAR] "Reformerを
+ * 用いた結果" for d_model 1024 and d_ff 4096): reading -- the Transformer's
+ * position-wise feed-forward relu(x W1^T + b1) W2^T + b2, rows processed a
+ * chunk at a time.
  */
 #include <math.h>
 #include <stdint.h>
@@ -536,5 +542,58 @@ int oracle_project(const double *x, int B, int64_t L, int d_model,
                     vo[e] = sv;
                 }
             }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* F1 -- chunked feed-forward.                                              */
+/* [WALKTHRU] "3 分塊": the feed-forward's inner width exceeds the model     */
+/* width, and since positions are computed independently the sequence is    */
+/* split into chunks processed one after another; [SCHOLAR] "Reformerを用い */
+/* た結果": d_model 1024, d_ff 4096. Reading (the pages give no formula):   */
+/* the Transformer's feed-forward, a ReLU between two linear maps with a    */
+/* bias after each (NULL = zero), weights output-major (w[n * in + k]).     */
+/*   x, out  [rows, d_model]   w1 [d_ff, d_model]   b1 [d_ff]               */
+/*   w2 [d_model, d_ff]        b2 [d_model]                                 */
+/* For each chunk of `chunk` rows: h = relu(x W1^T + b1) for the chunk,     */
+/* then out = h W2^T + b2.                                                  */
+/* ------------------------------------------------------------------------ */
+int oracle_ffn(const double *x, int64_t rows, int d_model, const double *w1, const double *b1,
+               const double *w2, const double *b2, int d_ff, int64_t chunk, double *out)
+{
+    if (rows < 0 || d_model < 1 || d_ff < 1 || chunk < 1) return -1;
+    const int64_t cap = rows < chunk ? rows : chunk;
+    double *h = (double *)malloc(sizeof(double) * (size_t)(cap > 0 ? cap : 1) * (size_t)d_ff);
+    if (!h) return -2;
+    for (int64_t r0 = 0; r0 < rows; r0 += chunk) {
+        const int64_t n = (rows - r0) < chunk ? (rows - r0) : chunk;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+        for (int64_t i = 0; i < n; ++i) {
+            const double *xr = x + (r0 + i) * d_model;
+            for (int f = 0; f < d_ff; ++f) {
+                const double *w = w1 + (int64_t)f * d_model;
+                double s = 0.0;
+                for (int k = 0; k < d_model; ++k) s += xr[k] * w[k];
+                if (b1) s += b1[f];
+                h[i * d_ff + f] = s > 0.0 ? s : 0.0;
+            }
+        }
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+        for (int64_t i = 0; i < n; ++i) {
+            const double *hr = h + i * d_ff;
+            for (int o = 0; o < d_model; ++o) {
+                const double *w = w2 + (int64_t)o * d_ff;
+                double s = 0.0;
+                for (int f = 0; f < d_ff; ++f) s += hr[f] * w[f];
+                if (b2) s += b2[o];
+                out[(r0 + i) * d_model + o] = s;
+            }
+        }
+    }
+    free(h);
     return 0;
 }

@@ -17,6 +17,7 @@ their sources are documented in ``lsh_oracle.c``:
   project  -- P0, the shared query/key and the value projections of the
               token vectors, split into heads
   backward -- G1, gradients of the forward for a given output gradient
+  ffn      -- F1, the chunked feed-forward relu(x W1^T + b1) W2^T + b2
 """
 from __future__ import annotations
 
@@ -72,10 +73,13 @@ def _load():
                                         ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_int, ctypes.c_int, _f64p, _f64p, ctypes.c_int,
                                         ctypes.c_int]
+        lib.oracle_ffn.argtypes = [_f64p, ctypes.c_int64, ctypes.c_int, _f64p, _f64p, _f64p,
+                                   _f64p, ctypes.c_int, ctypes.c_int64, _f64p]
         lib.oracle_threads.argtypes = []
         lib.oracle_threads.restype = ctypes.c_int
         for fn in (lib.oracle_hash, lib.oracle_sort, lib.oracle_attend, lib.oracle_combine,
-                   lib.oracle_forward, lib.oracle_project, lib.oracle_backward):
+                   lib.oracle_forward, lib.oracle_project, lib.oracle_backward,
+                   lib.oracle_ffn):
             fn.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -252,3 +256,22 @@ def backward(qk, v, R, dout, n_buckets: int, chunk_len: int, causal: bool,
                                    _p(dqk, _f64p), _p(dv, _f64p), int(bool(key_norm)), per_head),
            "backward")
     return dqk, dv
+
+
+def ffn(x, w1, b1, w2, b2, chunk: int):
+    """F1: out [rows, d_model] = relu(x W1^T + b1) W2^T + b2, ``chunk`` rows at
+    a time. x [rows, d_model]; w1 [d_ff, d_model]; w2 [d_model, d_ff]; b1, b2
+    vectors or None (zero)."""
+    x = _f64(x)
+    w1 = _f64(w1)
+    w2 = _f64(w2)
+    rows, dm = x.shape
+    dff = w1.shape[0]
+    if w1.shape != (dff, dm) or w2.shape != (dm, dff):
+        raise ValueError("w1 must be [d_ff, d_model] and w2 [d_model, d_ff]")
+    b1 = None if b1 is None else _f64(b1).reshape(dff)
+    b2 = None if b2 is None else _f64(b2).reshape(dm)
+    out = np.empty((rows, dm))
+    _check(_load().oracle_ffn(_p(x, _f64p), rows, dm, _p(w1, _f64p), _p(b1, _f64p),
+                              _p(w2, _f64p), _p(b2, _f64p), dff, chunk, _p(out, _f64p)), "ffn")
+    return out

@@ -65,6 +65,17 @@ MUTANTS = {
     "per_head_rotations_of_the_batch": ("return R + (bh % H) * per_head;",
                                         "return R + ((bh / H) % H) * per_head;"),
     "per_head_rotations_ignored": ("if (!per_head_r) return R;", "return R;"),
+    # w1[k * d_ff + f] stays inside w1's d_ff * d_model elements
+    "ffn_w1_transposed": ("const double *w = w1 + (int64_t)f * d_model;\n"
+                          "                double s = 0.0;\n"
+                          "                for (int k = 0; k < d_model; ++k) s += xr[k] * w[k];",
+                          "double s = 0.0;\n"
+                          "                for (int k = 0; k < d_model; ++k) "
+                          "s += xr[k] * w1[(int64_t)k * d_ff + f];"),
+    "ffn_no_relu": ("h[i * d_ff + f] = s > 0.0 ? s : 0.0;", "h[i * d_ff + f] = s;"),
+    "ffn_no_second_bias": ("if (b2) s += b2[o];", "(void)b2;"),
+    "ffn_chunk_restarts_rows": ("const double *xr = x + (r0 + i) * d_model;",
+                                "const double *xr = x + i * d_model;"),
     "key_norm_backward_no_projection": ("(xi[k] - dot * rn * rn * xj[k])", "(xi[k])"),
 }
 

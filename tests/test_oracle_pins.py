@@ -540,3 +540,60 @@ def test_per_head_rotations_are_each_heads_own(oracle_mod):
             gq, gv = oracle_mod.backward(qk[sl], v[sl], R4[h], g[sl], nb, 16, True)
             np.testing.assert_array_equal(dqk[b, h], gq[0, 0])
             np.testing.assert_array_equal(dv[b, h], gv[0, 0])
+
+
+def test_ffn_hand_example(oracle_mod):
+    """F1: a hand-computed example; it fixes the weight orientation, where each
+    bias is added and that the ReLU acts between the two maps."""
+    g = _golden("ffn_hand_example.json")
+    a = [np.array(g[k], float) for k in ("x", "w1", "b1", "w2", "b2")]
+    for chunk in (1, 2, 5):
+        assert np.array_equal(oracle_mod.ffn(*a, chunk), np.array(g["out"], float))
+
+
+def test_ffn_matches_torch_linear_relu(oracle_mod):
+    """F1 against torch's linear and relu in float64 on random inputs, with
+    and without biases."""
+    rng = np.random.default_rng(90)
+    rows, dm, dff = 37, 24, 40
+    x = rng.standard_normal((rows, dm))
+    w1 = rng.standard_normal((dff, dm))
+    w2 = rng.standard_normal((dm, dff))
+    b1 = rng.standard_normal(dff)
+    b2 = rng.standard_normal(dm)
+    F = torch.nn.functional
+    t = lambda a: torch.from_numpy(a)
+    for bias in (True, False):
+        ref = F.linear(F.relu(F.linear(t(x), t(w1), t(b1) if bias else None)), t(w2),
+                       t(b2) if bias else None).numpy()
+        got = oracle_mod.ffn(x, w1, b1 if bias else None, w2, b2 if bias else None, 8)
+        np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_ffn_chunk_size_changes_nothing(oracle_mod):
+    """F1: rows are independent, so every chunk size gives the same bits."""
+    rng = np.random.default_rng(91)
+    x = rng.standard_normal((23, 16))
+    w1 = rng.standard_normal((32, 16))
+    w2 = rng.standard_normal((16, 32))
+    b1 = rng.standard_normal(32)
+    b2 = rng.standard_normal(16)
+    ref = oracle_mod.ffn(x, w1, b1, w2, b2, 23)
+    for chunk in (1, 2, 5, 22, 100):
+        assert np.array_equal(oracle_mod.ffn(x, w1, b1, w2, b2, chunk), ref)
+
+
+def test_ffn_relu_regions(oracle_mod):
+    """F1: a very negative b1 switches every hidden unit off (out = b2
+    exactly); non-negative x, W1, b1 keep them all on, where the map is the
+    affine closed form x (W2 W1)^T + W2 b1 + b2 (numpy products)."""
+    rng = np.random.default_rng(92)
+    x = rng.standard_normal((9, 8))
+    w1 = rng.standard_normal((12, 8))
+    w2 = rng.standard_normal((8, 12))
+    b2 = rng.standard_normal(8)
+    off = oracle_mod.ffn(x, w1, np.full(12, -1e6), w2, b2, 4)
+    assert np.array_equal(off, np.broadcast_to(b2, off.shape))
+    xp, w1p, b1p = np.abs(x), np.abs(w1), np.abs(rng.standard_normal(12))
+    on = oracle_mod.ffn(xp, w1p, b1p, w2, b2, 4)
+    np.testing.assert_allclose(on, xp @ (w2 @ w1p).T + w2 @ b1p + b2, rtol=1e-12, atol=1e-12)
