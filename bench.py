@@ -247,6 +247,39 @@ def measure_training(lsh, torch, w, steps, warmup, key_norm=False, per_head_r=Fa
             "bwd_frac": flops / b_ms / 1e9 / peak}
 
 
+def measure_ffn(lsh, torch, steps, warmup, rows=65536, d_model=1024, d_ff=4096, chunk=16384):
+    """The chunked feed-forward at the pages' widths (d_model 1024, d_ff 4096)
+    over 64K token rows in bf16, synthetic inputs resident in HBM. Work:
+    2 products of 2 * rows * d_model * d_ff flops each."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(1006)
+    mk = lambda *sh, sc=1.0: (torch.randn(*sh, generator=g) * sc).to(dev, torch.bfloat16)
+    x = mk(rows, d_model)
+    w1, b1 = mk(d_ff, d_model, sc=d_model ** -0.5), mk(d_ff, sc=0.1)
+    w2, b2 = mk(d_model, d_ff, sc=d_ff ** -0.5), mk(d_model, sc=0.1)
+    out = torch.empty_like(x)
+    ws = torch.empty(lsh.lsh_ffn_workspace_size(rows, d_ff, chunk, lsh.LSH_BF16),
+                     dtype=torch.uint8, device=dev)
+    run = lambda: lsh.ffn(x, w1, b1, w2, b2, chunk, ws=ws, out=out)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    flops = 4.0 * rows * d_model * d_ff
+    launches = 2 * ((rows + chunk - 1) // chunk)
+    return {"workload": "ffn_rows64k_dmodel1024_dff4096", "rows": rows, "d_model": d_model,
+            "d_ff": d_ff, "chunk_rows": chunk, "dtype": "bf16", "ms": ms,
+            "tokens_per_s": rows / (ms / 1e3), "tflops": flops / ms / 1e9,
+            "peak_tflops": PEAK_F16_TFLOPS, "frac": flops / ms / 1e9 / PEAK_F16_TFLOPS,
+            "launches": launches, "ms_per_launch": ms / launches}
+
+
 def dense_comparator(torch, w, qk_t, v_t, steps=10):
     """PyTorch SDPA at the same shape (queries = keys = qk), flash or
     memory-efficient backend only; None when neither takes the shape."""
@@ -338,6 +371,10 @@ def main() -> int:
     ap.add_argument("--key-norm", action="store_true",
                     help="time the key-normalisation variant (forward, or with --train both "
                          "passes) instead of the headline line")
+    ap.add_argument("--ffn", action="store_true",
+                    help="time the chunked feed-forward (64K rows, 1024 -> 4096 -> 1024, bf16)")
+    ap.add_argument("--ffn-chunk", type=int, default=16384,
+                    help="rows per chunk of the feed-forward (with --ffn)")
     ap.add_argument("--per-head-r", action="store_true",
                     help="time the per-head rotations variant (R [H, nh, d, nb/2]); combines "
                          "with --key-norm and --train")
@@ -383,6 +420,11 @@ def main() -> int:
         print(json.dumps(measure_training(lsh, torch, workloads.WORKLOADS[
             args.workload or workloads.HEADLINE], min(args.steps, 10), args.warmup,
             key_norm=args.key_norm, per_head_r=args.per_head_r)), flush=True)
+        return 0
+
+    if args.ffn:
+        print(json.dumps(measure_ffn(lsh, torch, min(args.steps, 10), args.warmup,
+                                     chunk=args.ffn_chunk)), flush=True)
         return 0
 
     if args.key_norm or args.per_head_r:

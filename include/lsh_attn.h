@@ -228,6 +228,30 @@ int lsh_attention_bwd(const void *qk, const void *v, const void *out, const void
                       const void *state, size_t state_bytes, const lsh_shape_t *shape, void *dqk,
                       void *dv, void *ws, size_t ws_bytes, void *stream);
 
+/* Chunked feed-forward (walkthrough "3 分塊": positions are independent, so
+ * the rows are processed a chunk at a time to bound the wide intermediate;
+ * scholar "Reformerを用いた結果" for d_model 1024, d_ff 4096). For every row m:
+ *     out[m] = relu(x[m] W1^T + b1) W2^T + b2
+ * (the Transformer's position-wise feed-forward; the pages name neither the
+ * activation nor the biases, so a NULL bias is zero).
+ *   x, out   [rows, d_model] dtype             d_model, d_ff: multiples of 8
+ *   w1       [d_ff, d_model] dtype (output-major, as a linear layer stores it)
+ *   b1       [d_ff] dtype or NULL
+ *   w2       [d_model, d_ff] dtype             b2 [d_model] dtype or NULL
+ *   ws       lsh_ffn_workspace_size bytes: one chunk's intermediate,
+ *            min(chunk_rows, rows) * d_ff elements of dtype, caller-owned
+ * The result does not depend on chunk_rows (rows are independent; bit-equal
+ * across chunk sizes). bf16: matrix cores, fp32 accumulation, the
+ * intermediate rounded to bf16 after bias and ReLU; fp32: fp32 throughout.
+ * Errors: LSH_ERR_ARG for sizes, dtype, NULL or misaligned tensors;
+ * LSH_ERR_WORKSPACE for a missing or small workspace. */
+int lsh_ffn_workspace_size(int64_t rows, int32_t d_ff, int32_t chunk_rows, int32_t dtype,
+                           size_t *bytes);
+int lsh_ffn_chunked(const void *x, const void *w1, const void *b1, const void *w2,
+                    const void *b2, int64_t rows, int32_t d_model, int32_t d_ff,
+                    int32_t chunk_rows, int32_t dtype, void *out, void *ws, size_t ws_bytes,
+                    void *stream);
+
 /* Message for the last error on the calling thread ("" if none). */
 const char *lsh_last_error(void);
 

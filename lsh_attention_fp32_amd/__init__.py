@@ -30,6 +30,7 @@ from ._binding import (  # noqa: F401
     attention_fwd_train,
     attention_fwd_x,
     chunk_attend,
+    ffn,
     hash,
     library_path,
     load_library,
@@ -40,6 +41,8 @@ from ._binding import (  # noqa: F401
     lsh_attention_fwd_train,
     lsh_attention_fwd_x,
     lsh_chunk_attend,
+    lsh_ffn_chunked,
+    lsh_ffn_workspace_size,
     lsh_hash,
     lsh_last_error,
     lsh_qkv_project,

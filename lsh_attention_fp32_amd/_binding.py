@@ -64,7 +64,10 @@ def load_library():
     lib.lsh_attention_fwd_x.argtypes = [vp, vp, vp, vp, sp, i32, vp, vp, sz, vp]
     lib.lsh_attention_fwd_train.argtypes = [vp, vp, vp, sp, vp, vp, sz, vp, sz, vp]
     lib.lsh_attention_bwd.argtypes = [vp, vp, vp, vp, vp, sz, sp, vp, vp, vp, sz, vp]
-    for name in ("lsh_workspace_size", "lsh_hash", "lsh_sort", "lsh_chunk_attend",
+    i64 = ctypes.c_int64
+    lib.lsh_ffn_workspace_size.argtypes = [i64, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.lsh_ffn_chunked.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp, sz, vp]
+    for name in ("lsh_ffn_workspace_size", "lsh_ffn_chunked", "lsh_workspace_size", "lsh_hash", "lsh_sort", "lsh_chunk_attend",
                  "lsh_unsort_combine", "lsh_attention_fwd", "lsh_attention_fwd_timed",
                  "lsh_qkv_project", "lsh_attention_fwd_x", "lsh_attention_fwd_train",
                  "lsh_attention_bwd"):
@@ -175,6 +178,49 @@ def lsh_attention_fwd_timed(qk, v, R, shape: Shape, out, ws, stream=None, max_ke
         ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream), ms, names,
         max_kernels, ctypes.byref(n)), "lsh_attention_fwd_timed")
     return [(names[k].decode(), float(ms[k])) for k in range(n.value)]
+
+
+def lsh_ffn_workspace_size(rows: int, d_ff: int, chunk_rows: int, dtype: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().lsh_ffn_workspace_size(int(rows), int(d_ff), int(chunk_rows),
+                                                 int(dtype), ctypes.byref(n)),
+           "lsh_ffn_workspace_size")
+    return n.value
+
+
+def lsh_ffn_chunked(x, w1, b1, w2, b2, rows: int, d_model: int, d_ff: int, chunk_rows: int,
+                    dtype: int, out, ws, stream=None) -> None:
+    _check(load_library().lsh_ffn_chunked(_ptr(x), _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2),
+                                          int(rows), int(d_model), int(d_ff), int(chunk_rows),
+                                          int(dtype), _ptr(out), _ptr(ws), _nbytes(ws),
+                                          _stream(stream)),
+           "lsh_ffn_chunked")
+
+
+def ffn(x, w1, b1, w2, b2, chunk_rows: int, ws=None, out=None, stream=None):
+    """Chunked feed-forward relu(x W1^T + b1) W2^T + b2 over the rows of x
+    [..., d_model]; w1 [d_ff, d_model], w2 [d_model, d_ff], biases [d_ff],
+    [d_model] or None, all in x's dtype. Returns out shaped like x."""
+    if x.dtype not in _DTYPES:
+        raise ValueError(f"x dtype must be float32 or bfloat16, got {x.dtype}")
+    dm = x.shape[-1]
+    dff = w1.shape[0]
+    if w1.shape != (dff, dm) or w2.shape != (dm, dff):
+        raise ValueError("w1 must be [d_ff, d_model] and w2 [d_model, d_ff]")
+    for t, n in ((b1, dff), (b2, dm)):
+        if t is not None and t.shape != (n,):
+            raise ValueError("biases must be [d_ff] and [d_model]")
+    for t in (w1, w2, b1, b2):
+        if t is not None and t.dtype != x.dtype:
+            raise ValueError("weights and biases must be in x's dtype")
+    rows = x.numel() // dm if dm else 0
+    dtype = _DTYPES[x.dtype]
+    out = torch.empty_like(x) if out is None else out
+    if ws is None:
+        ws = torch.empty(max(1, lsh_ffn_workspace_size(rows, dff, chunk_rows, dtype)),
+                         dtype=torch.uint8, device=x.device)
+    lsh_ffn_chunked(x, w1, b1, w2, b2, rows, dm, dff, chunk_rows, dtype, out, ws, stream)
+    return out
 
 
 def lsh_qkv_project(x, w_qk, w_v, shape: Shape, d_model: int, qk, v, stream=None) -> None:

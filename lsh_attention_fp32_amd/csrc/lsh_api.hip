@@ -329,6 +329,46 @@ int lsh_qkv_project(const void* x, const void* w_qk, const void* w_v, const lsh_
     return e == hipSuccess ? LSH_OK : hip_fail(e, "lsh_qkv_project");
 }
 
+int lsh_ffn_workspace_size(int64_t rows, int32_t d_ff, int32_t chunk_rows, int32_t dtype,
+                           size_t* bytes) {
+    g_err[0] = 0;
+    if (!bytes) return fail(LSH_ERR_ARG, "lsh_ffn_workspace_size: bytes must not be NULL");
+    if (rows < 0 || d_ff < 8 || d_ff % 8 != 0 || chunk_rows < 1 ||
+        (dtype != LSH_F32 && dtype != LSH_BF16))
+        return fail(LSH_ERR_ARG,
+                    "lsh_ffn_workspace_size: rows >= 0, d_ff a positive multiple of 8, "
+                    "chunk_rows >= 1 and a known dtype required");
+    const int64_t n = rows < chunk_rows ? rows : chunk_rows;
+    *bytes = (size_t)n * d_ff * (dtype == LSH_BF16 ? 2 : 4);
+    return LSH_OK;
+}
+
+int lsh_ffn_chunked(const void* x, const void* w1, const void* b1, const void* w2,
+                    const void* b2, int64_t rows, int32_t d_model, int32_t d_ff,
+                    int32_t chunk_rows, int32_t dtype, void* out, void* ws, size_t ws_bytes,
+                    void* stream) {
+    g_err[0] = 0;
+    if (d_model < 8 || d_model % 8 != 0)
+        return fail(LSH_ERR_ARG, "lsh_ffn_chunked: d_model must be a positive multiple of 8 "
+                                 "(got %d)", (int)d_model);
+    size_t need = 0;
+    int rc = lsh_ffn_workspace_size(rows, d_ff, chunk_rows, dtype, &need);
+    if (rc) return rc;
+    if (rows == 0) return LSH_OK;
+    if (!x || !w1 || !w2 || !out)
+        return fail(LSH_ERR_ARG, "lsh_ffn_chunked: NULL tensor pointer");
+    if (misaligned({x, w1, w2, out}))
+        return fail(LSH_ERR_ARG, "lsh_ffn_chunked: tensor pointers must be 16-byte aligned");
+    if (!ws) return fail(LSH_ERR_WORKSPACE, "lsh_ffn_chunked: workspace is NULL");
+    if (misaligned({ws})) return fail(LSH_ERR_ARG, "lsh_ffn_chunked: workspace must be 16-byte aligned");
+    if (ws_bytes < need)
+        return fail(LSH_ERR_WORKSPACE, "lsh_ffn_chunked: workspace has %zu bytes, needs %zu",
+                    ws_bytes, need);
+    hipError_t e = launch_ffn(x, w1, b1, w2, b2, rows, d_model, d_ff, chunk_rows,
+                              dtype == LSH_BF16, out, ws, (hipStream_t)stream);
+    return e == hipSuccess ? LSH_OK : hip_fail(e, "lsh_ffn_chunked");
+}
+
 int lsh_attention_fwd_x(const void* x, const void* w_qk, const void* w_v, const float* R,
                         const lsh_shape_t* shape, int32_t d_model, void* out, void* ws,
                         size_t ws_bytes, void* stream) {

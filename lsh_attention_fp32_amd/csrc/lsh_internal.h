@@ -155,6 +155,13 @@ hipError_t launch_attend(const void* qk, const void* v, const int32_t* buckets,
                          hipStream_t st, hipEvent_t* ev, int* nev, const char** names,
                          bool packed = false, const float* rn = nullptr);
 
+// ----------------------------------------------------- feed-forward
+// out = relu(x W1^T + b1) W2^T + b2 over `rows` rows, chunk_rows at a time;
+// inter holds one chunk's intermediate (min(chunk_rows, rows) * d_ff elements).
+hipError_t launch_ffn(const void* x, const void* w1, const void* b1, const void* w2,
+                      const void* b2, int64_t rows, int d_model, int d_ff, int chunk_rows,
+                      bool bf16, void* out, void* inter, hipStream_t st);
+
 // ----------------------------------------------------- key normalisation
 // rn[t] = 1 / |qk[t]| (0 for the zero vector), float32, one per token-head.
 hipError_t launch_key_rnorm(const void* qk, const Dims& d, float* rn, hipStream_t st);
@@ -217,11 +224,9 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
 }
 
 // float -> bf16, round to nearest even (finite inputs; NaN stays NaN)
+// Round to nearest even (the hardware conversion, v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 template <typename T>

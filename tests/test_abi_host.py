@@ -36,7 +36,8 @@ def test_header_declares_the_entry_points():
     for n in ("lsh_hash", "lsh_sort", "lsh_chunk_attend", "lsh_unsort_combine",
               "lsh_attention_fwd", "lsh_workspace_size", "lsh_last_error",
               "lsh_attention_fwd_timed", "lsh_qkv_project", "lsh_attention_fwd_x",
-              "lsh_attention_fwd_train", "lsh_attention_bwd"):
+              "lsh_attention_fwd_train", "lsh_attention_bwd", "lsh_ffn_chunked",
+              "lsh_ffn_workspace_size"):
         assert n in names
 
 
@@ -195,3 +196,37 @@ def test_rounds_of_reads_the_rotation_layout():
     assert lsh.rounds_of(torch.empty(2, 3, 64, 8)) == (3, True)
     with pytest.raises(ValueError):
         lsh.rounds_of(torch.empty(64, 8))
+
+
+def test_ffn_workspace_is_one_chunk_of_the_intermediate(lib):
+    assert lsh.lsh_ffn_workspace_size(65536, 4096, 8192, lsh.LSH_BF16) == 8192 * 4096 * 2
+    assert lsh.lsh_ffn_workspace_size(100, 4096, 8192, lsh.LSH_F32) == 100 * 4096 * 4
+    assert lsh.lsh_ffn_workspace_size(0, 64, 16, lsh.LSH_BF16) == 0
+    for args in ((10, 12, 4, lsh.LSH_BF16), (10, 64, 0, lsh.LSH_BF16), (-1, 64, 4, lsh.LSH_F32),
+                 (10, 64, 4, 9)):
+        with pytest.raises(lsh.LshError) as ei:
+            lsh.lsh_ffn_workspace_size(*args)
+        assert ei.value.code == -1
+
+
+def test_ffn_rejects_on_host(lib):
+    import ctypes
+    call = lib.lsh_ffn_chunked
+    fake = ctypes.c_void_p(1 << 20)   # never dereferenced: every case fails on the host
+    # d_model not a multiple of 8
+    assert call(fake, fake, None, fake, None, 4, 12, 64, 4, lsh.LSH_BF16, fake, fake, 1 << 20,
+                None) == -1
+    # NULL x
+    assert call(None, fake, None, fake, None, 4, 16, 64, 4, lsh.LSH_BF16, fake, fake, 1 << 20,
+                None) == -1
+    # misaligned weight
+    assert call(fake, ctypes.c_void_p((1 << 20) + 2), None, fake, None, 4, 16, 64, 4,
+                lsh.LSH_BF16, fake, fake, 1 << 20, None) == -1
+    # workspace too small (needs 4 * 64 * 2 bytes), and missing
+    assert call(fake, fake, None, fake, None, 4, 16, 64, 4, lsh.LSH_BF16, fake, fake, 511,
+                None) == -2
+    assert call(fake, fake, None, fake, None, 4, 16, 64, 4, lsh.LSH_BF16, fake, None, 1 << 20,
+                None) == -2
+    # no rows: nothing to do, no pointer is needed
+    assert call(None, None, None, None, None, 0, 16, 64, 4, lsh.LSH_BF16, None, None, 0,
+                None) == 0
