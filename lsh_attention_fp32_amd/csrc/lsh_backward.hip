@@ -26,7 +26,7 @@
 //               (each row is owned by one quad of lanes), dv is written to a
 //               second set of rows;
 //   bwd_reduce  sums each position's rows over the rounds into dqk and dv.
-// With bf16 I/O and chunk 64 one matrix-core kernel (bwd_mfma) replaces the
+// With bf16 I/O and chunk 64 one matrix-core kernel (bwd_run) replaces the
 // two middle passes and writes bf16 rows.
 // Four lanes share a query (or key), each holding a quarter of its features;
 // dot products are summed across the quad.
@@ -379,10 +379,7 @@ constexpr int kBM = 64;   // chunk length of the matrix-core passes
 template <int D>
 struct BwdRows {
     static constexpr int RS = D + 8;     // padded row (bf16): rows 4 banks apart
-#ifndef LSH_BWD_TS
-#define LSH_BWD_TS (kBM + 8)
-#endif
-    static constexpr int TS = LSH_BWD_TS;   // padded transposed row (bf16)
+    static constexpr int TS = kBM + 8;   // padded transposed row (bf16)
 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -397,52 +394,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // apart on the same banks.
 __device__ __forceinline__ int phys_row(int j) {
     return (j & ~31) | (((j >> 3) & 3) << 2) | (((j >> 2) & 1) << 4) | (j & 3);
-}
-
-// Gathers the 64 rows of sorted slots [t0, t0 + 64) of one segment: row-major
-// into `rm` ([64][RS]) and, when `tr` is given, transposed into `tr` ([D][TS]);
-// positions and bucket ids into pos / bkt (when given). Rows past the segment
-// (no chunk) are zero with bucket -1.
-template <int D, bool PACKED>
-__device__ __forceinline__ void stage_rows(const uint16_t* __restrict__ src,
-                                           const int32_t* __restrict__ P,
-                                           const int32_t* __restrict__ Bk, int64_t t0, bool exists,
-                                           uint16_t (*rm)[BwdRows<D>::RS],
-                                           uint16_t (*tr)[BwdRows<D>::TS], int32_t* pos,
-                                           int32_t* bkt, int32_t* spos) {
-    const int tid = threadIdx.x;
-    if (tid < kBM) {
-        int32_t p = 0, b = -1;
-        if (exists) read_key<PACKED>(P, Bk, t0 + tid, p, b);
-        spos[tid] = exists ? p : -1;
-        if (pos) pos[tid] = p;
-        if (bkt) bkt[tid] = b;
-    }
-    __syncthreads();
-    // row-major: 64 rows x D/8 pieces of 16 bytes
-    for (int i = tid; i < kBM * (D / 8); i += 256) {
-        const int row = i / (D / 8), pc = i % (D / 8);
-        const int32_t p = spos[row];
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (p >= 0) w = *(const u32x4*)(src + (int64_t)p * D + pc * 8);
-        *(u32x4*)&rm[row][pc * 8] = w;
-    }
-    if (tr) {
-        // transposed: a thread takes rows 2 pr, 2 pr + 1 and 8 features
-        for (int i = tid; i < (kBM / 2) * (D / 8); i += 256) {
-            const int pr = i % (kBM / 2), fg = i / (kBM / 2);
-            const int32_t p0 = spos[2 * pr], p1 = spos[2 * pr + 1];
-            u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-            if (p0 >= 0) a = *(const u32x4*)(src + (int64_t)p0 * D + fg * 8);
-            if (p1 >= 0) b = *(const u32x4*)(src + (int64_t)p1 * D + fg * 8);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t lo = (a[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-                const uint32_t hi = (b[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-                *(uint32_t*)&tr[fg * 8 + e][2 * pr] = lo | (hi << 16);
-            }
-        }
-    }
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -467,49 +418,60 @@ __device__ __forceinline__ void transpose_items(const uint16_t (*rm)[BwdRows<D>:
     }
 }
 
+// ---------------------------------------------------------------------------
+// Run-based matrix-core pass. A workgroup walks a run of kBwdRun consecutive
+// chunks of one (batch, head, round) segment. Chunk c's slots are the queries
+// of the pairs (c, c - 1), (c, c) and the keys of the pairs (c, c), (c + 1, c);
+// at step c the workgroup
+//   1. finishes chunk c - 1 as keys: the key side of pair (c, c - 1), the
+//      queries being chunk c; then writes chunk c - 1's rows (dq + dk, dv);
+//   2. takes chunk c as queries against the keys of chunks c - 1 and c (dq);
+//   3. takes chunk c as keys against its own queries (dk, dv so far).
+// LDS holds the rows of chunks c - 1 and c (qk and v row-major, qk
+// transposed, one slot per chunk parity) and chunk c's output gradients.
+// Chunk c + 1's rows are gathered into registers at the top of step c and
+// parked in the slot chunk c - 1 leaves, so every chunk's rows come from HBM
+// once per run and a gather has a whole step of matrix work to arrive. The
+// last chunk of a run is finished by a partial step (1 only) on the next
+// chunk, whose run repeats that pair for its own queries.
+constexpr int kBwdRun = 16;   // chunks per workgroup
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
 template <int D>
-struct BwdLds {
-    uint16_t ra[kBM][BwdRows<D>::RS];   // rows of the other side: qk
-    uint16_t rb[kBM][BwdRows<D>::RS];   // its values (query side) or output gradients (key side)
-    uint16_t ta[D][BwdRows<D>::TS];     // ra transposed
-    uint16_t tb[D][BwdRows<D>::TS];     // rb transposed
-    // chunks c - 1, c, c + 1: position, bucket id, Z and D of each slot
-    int32_t pos[3][kBM], bkt[3][kBM];
-    float zz[3][kBM], dd[3][kBM];
-    float rn[3][kBM];   // 1 / |x| of each slot (key normalisation)
+struct alignas(16) BwdRunLds {
+    static constexpr int RS = BwdRows<D>::RS, TS = BwdRows<D>::TS;
+    uint16_t xr[2][kBM][RS];   // qk rows of the chunk of each parity (phys_row order)
+    uint16_t vr[2][kBM][RS];   // v rows
+    uint16_t gr[kBM][RS];      // output-gradient rows of the current chunk
+    uint16_t xt[2][D][TS];     // qk transposed (item order)
+    uint16_t gt[D][TS];        // output gradients transposed
+    int32_t pos[3][kBM], bkt[3][kBM];          // chunk t in slot t % 3
+    float zz[2][kBM], dd[2][kBM], rn[2][kBM];   // chunk t in slot t & 1
 };
 
-// One workgroup per (round, chunk c): the chunk's 64 slots are at once the
-// queries of the pairs (c, c - 1), (c, c) and the keys of the pairs (c, c),
-// (c + 1, c), so it produces dq, dk and dv of those slots. Wave w owns slots
-// 16 w .. 16 w + 15; their qk, v and dout fragments stay in registers. Query
-// side (the chunk's slots as queries, keys of chunk kc on rows):
-//   S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ^T += K^T dS^T;
-// key side (the chunk's slots as keys, queries of chunk qc on rows):
-//   S = Q K^T, dP = dO V^T, dS = P (dP - D), dK^T += Q^T dS, dV^T += dO^T P.
-// A slot's dq and dk land in the same lane and register, so dq + dk and dv
-// are written once to the per-round rows. The sorted keys, Z and D of the
-// three chunks are read in one go at the start, and each stage issues its two
-// row gathers together, so a workgroup waits on memory five times in a row.
 template <int D, bool PACKED, bool KN>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void bwd_mfma_kernel(const uint16_t* __restrict__ qk,
-                                                       const uint16_t* __restrict__ v,
-                                                       const uint16_t* __restrict__ g,
-                                                       const int32_t* __restrict__ perm,
-                                                       const int32_t* __restrict__ buckets,
-                                                       const float* __restrict__ z,
-                                                       const float* __restrict__ Dv,
-                                                       const float* __restrict__ rn, Dims dm,
-                                                       uint16_t* __restrict__ dx_r,
-                                                       uint16_t* __restrict__ dv_r) {
+__global__ __launch_bounds__(256) void bwd_run_kernel(const uint16_t* __restrict__ qk,
+                                                      const uint16_t* __restrict__ v,
+                                                      const uint16_t* __restrict__ g,
+                                                      const int32_t* __restrict__ perm,
+                                                      const int32_t* __restrict__ buckets,
+                                                      const float* __restrict__ z,
+                                                      const float* __restrict__ Dv,
+                                                      const float* __restrict__ rn, Dims dm,
+                                                      int nruns, uint16_t* __restrict__ dx_r,
+                                                      uint16_t* __restrict__ dv_r) {
     constexpr int KSTEPS = D / 32, DT = D / 16;
     constexpr int PER = kBM * (D / 8) / 256;   // 16-byte pieces per thread and source
-    __shared__ BwdLds<D> sm;
+    __shared__ BwdRunLds<D> sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int gq = lane >> 4, r16 = lane & 15;
-    const int64_t seg = blockIdx.y;
-    const int c = blockIdx.x;
+    const int64_t seg = blockIdx.x / nruns;
+    const int run = blockIdx.x - (int)(seg * nruns);
     const int nchunks = dm.L / kBM;
+    const int c0 = run * kBwdRun;
+    const int c1 = min(c0 + kBwdRun, nchunks);
+    const int clast = min(c1, nchunks - 1);   // step c1 (when it exists) runs part 1 only
     const int64_t L = dm.L;
     const int64_t bh = seg / dm.nh;
     const int r = (int)(seg - bh * dm.nh);
@@ -521,78 +483,72 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     const float c2 = kLog2e / sqrtf((float)D);
     const float pen2 = kSelfPenalty * kLog2e;
     const float inv_nh = 1.0f / (float)dm.nh;
+    const float scale = 1.0f / sqrtf((float)D);
+    const int me = 16 * wave + r16;   // this lane's slot within a chunk
+    const int prow = phys_row(me);
 
-    // sorted keys of chunks c - 1, c, c + 1 (index 0, 1, 2); their Z and D
-    // are read together with the first row gather
-    int32_t zpos = -1;
-    if (tid < 3 * kBM) {
-        const int w3 = tid >> 6, j = tid & (kBM - 1);
-        const int ch = c - 1 + w3;
-        int32_t b = -1;
-        if (ch >= 0 && ch < nchunks) read_key<PACKED>(P, Bk, (int64_t)ch * kBM + j, zpos, b);
-        sm.pos[w3][j] = zpos;
-        sm.bkt[w3][j] = b;
-    }
-    __syncthreads();
-
-    // rows of chunk index w3 from sa into ra (unless sa is null: ra keeps
-    // its rows) and from sb into rb, all loads issued before any store, then
-    // the transposes asked for
-    auto stage = [&](int w3, const uint16_t* sa, const uint16_t* sb, bool tra, bool trb) {
-        u32x4 wa[PER], wb[PER];
+    // rows of chunk t (positions in its pos slot) into registers, then LDS
+    struct Pre {
+        u32x4 x[PER], v[PER], g[PER];
+        float z, d, rn;
+    };
+    auto gather = [&](int t, Pre& pf) {
+        const int s3 = t % 3;
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
             const int i = tid + 256 * k, row = i / (D / 8), pc = i % (D / 8);
-            const int64_t off = (int64_t)sm.pos[w3][row] * D + pc * 8;
-            if (sa) wa[k] = *(const u32x4*)(sa + off);
-            wb[k] = *(const u32x4*)(sb + off);
+            const int64_t off = (int64_t)sm.pos[s3][row] * D + pc * 8;
+            pf.x[k] = *(const u32x4*)(X + off);
+            pf.v[k] = *(const u32x4*)(V + off);
+            pf.g[k] = *(const u32x4*)(G + off);
         }
-        __syncthreads();   // every wave is done with the buffers
+        if (tid < kBM) {
+            const int64_t p = bh * L + sm.pos[s3][tid];
+            pf.z = z[p];
+            pf.d = Dv[p];
+            pf.rn = KN ? rn[p] : 1.f;
+        }
+    };
+    auto park = [&](int t, const Pre& pf) {
+        const int par = t & 1;
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
             const int i = tid + 256 * k, row = phys_row(i / (D / 8)), pc = i % (D / 8);
-            if (sa) *(u32x4*)&sm.ra[row][pc * 8] = wa[k];
-            *(u32x4*)&sm.rb[row][pc * 8] = wb[k];
+            *(u32x4*)&sm.xr[par][row][pc * 8] = pf.x[k];
+            *(u32x4*)&sm.vr[par][row][pc * 8] = pf.v[k];
+            *(u32x4*)&sm.gr[row][pc * 8] = pf.g[k];
         }
-        __syncthreads();
-        if (tra) transpose_items<D>(sm.ra, sm.ta);
-        if (trb) transpose_items<D>(sm.rb, sm.tb);
-        if (tra || trb) __syncthreads();
+        if (tid < kBM) {
+            sm.zz[par][tid] = pf.z;
+            sm.dd[par][tid] = pf.d;
+            sm.rn[par][tid] = pf.rn;
+        }
+    };
+    auto load_keys = [&](int t) {   // sorted keys of chunk t into its slot (threads < 64)
+        int32_t p, b;
+        read_key<PACKED>(P, Bk, (int64_t)t * kBM + tid, p, b);
+        sm.pos[t % 3][tid] = p;
+        sm.bkt[t % 3][tid] = b;
     };
 
-    const int me = 16 * wave + r16;   // this lane's slot within the chunk
-    const int32_t mpos = sm.pos[1][me], mbkt = sm.bkt[1][me];
-    bf16x8 xf[KSTEPS], vf[KSTEPS], gf[KSTEPS];
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s)
-        gf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(G + (int64_t)mpos * D + 32 * s + 8 * gq));
-    if (tid < 3 * kBM) {
-        const int w3 = tid >> 6, j = tid & (kBM - 1);
-        sm.zz[w3][j] = zpos >= 0 ? z[bh * L + zpos] : 0.f;
-        sm.dd[w3][j] = zpos >= 0 ? Dv[bh * L + zpos] : 0.f;
-        if constexpr (KN) sm.rn[w3][j] = zpos >= 0 ? rn[bh * L + zpos] : 0.f;
-    }
-    // ---- the chunk itself: qk into ra (transposed too), v into rb (the
-    // stage's barriers also publish Z, D and the key scales)
-    stage(1, X, V, true, false);
-    const float mz = sm.zz[1][me], mz2 = mz * kLog2e, mD = sm.dd[1][me];
-    const bool mself_only = mz < -0.5f * kSelfPenalty;
-    const float mrn = KN ? sm.rn[1][me] : 1.f;   // this slot's 1 / |x| as a key
-    float msdd = 0.f;   // its sum of dS (x_i . x_j) over the key-side pairs
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-        xf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.ra[phys_row(me)][32 * s + 8 * gq]);
-        vf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.rb[phys_row(me)][32 * s + 8 * gq]);
-    }
-    f32x4 dq[DT], dk[DT], dvv[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) dq[dt] = dk[dt] = dvv[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
-    // query side against the keys of chunk index w3 in ra (values in rb,
-    // keys transposed in ta)
-    auto query_side = [&](int w3) {
+    // chunk c's queries (fragments xf, gf) against the keys of chunk t (LDS)
+    // A 32-item block takes part only if its bucket range meets the wave's
+    // (chunks are sorted by bucket) and, within one chunk under causality,
+    // only if it is not wholly on the wrong side: a key slot after every
+    // query slot of the same bucket has a later position. Wave-uniform.
+    auto active = [&](int lo, int hi, int mlo, int mhi, bool skip) -> bool {
+        const bool a = lo <= mhi && hi >= mlo && !skip;
+        return __builtin_amdgcn_readfirstlane((int)a) != 0;
+    };
+    auto query_pass = [&](int t, bool own, const bf16x8(&xf)[KSTEPS], const bf16x8(&gf)[KSTEPS],
+                          int32_t mpos, int32_t mbkt, float mz2, float mD, bool mself_only,
+                          int mlo, int mhi, f32x4(&dq)[DT]) {
+        const int par = t & 1, s3 = t % 3;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
+            if (!active(sm.bkt[s3][32 * kb], sm.bkt[s3][32 * kb + 31], mlo, mhi,
+                        own && dm.causal && 32 * kb > 16 * wave + 15))
+                continue;
             u32x4 dsfrag;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -601,21 +557,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
                 f32x4 sacc = {0.f, 0.f, 0.f, 0.f}, pacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < KSTEPS; ++s) {
-                    const bf16x8 ka = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.ra[kw][32 * s + 8 * gq]);
-                    const bf16x8 va = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.rb[kw][32 * s + 8 * gq]);
+                    const bf16x8 ka = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.xr[par][kw][32 * s + 8 * gq]);
+                    const bf16x8 va = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.vr[par][kw][32 * s + 8 * gq]);
                     sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, xf[s], sacc, 0, 0, 0);
                     pacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, gf[s], pacc, 0, 0, 0);
                 }
                 float ds[4];
+                const int kbase = 32 * kb + 8 * gq + 4 * h;   // register i is key kbase + i
+                const i32x4 kps = *(const i32x4*)&sm.pos[s3][kbase];
+                const i32x4 kbk = *(const i32x4*)&sm.bkt[s3][kbase];
+                f32x4 krn = {1.f, 1.f, 1.f, 1.f};
+                if constexpr (KN) krn = *(const f32x4*)&sm.rn[par][kbase];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {   // key 32 kb + 8 gq + 4 h + i
-                    const int key = 32 * kb + 8 * gq + 4 * h + i;
-                    const int32_t kp = sm.pos[w3][key];
-                    const bool ok = sm.bkt[w3][key] == mbkt && (!dm.causal || kp <= mpos);
-                    const float krn = KN ? sm.rn[w3][key] : 1.f;
-                    const float s2 = sacc[i] * krn * c2 - (kp == mpos ? pen2 : 0.f);
-                    const float pw = pair_weight(ok, kp == mpos, s2, mz2, mself_only, inv_nh);
-                    ds[i] = pw * (pacc[i] - mD) * krn;
+                for (int i = 0; i < 4; ++i) {
+                    const bool ok = kbk[i] == mbkt && (!dm.causal || kps[i] <= mpos);
+                    const float s2 = sacc[i] * krn[i] * c2 - (kps[i] == mpos ? pen2 : 0.f);
+                    const float pw = pair_weight(ok, kps[i] == mpos, s2, mz2, mself_only, inv_nh);
+                    ds[i] = pw * (pacc[i] - mD) * krn[i];
                 }
                 dsfrag[2 * h] = pack_bf16x2(ds[0], ds[1]);
                 dsfrag[2 * h + 1] = pack_bf16x2(ds[2], ds[3]);
@@ -624,40 +582,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 const bf16x8 af = __builtin_bit_cast(
-                    bf16x8, *(const u32x4*)&sm.ta[dt * 16 + r16][32 * kb + 8 * gq]);
+                    bf16x8, *(const u32x4*)&sm.xt[par][dt * 16 + r16][32 * kb + 8 * gq]);
                 dq[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bd, dq[dt], 0, 0, 0);
             }
         }
     };
-    // key side against the queries of chunk index w3 in ra (output gradients
-    // in rb, both transposed in ta, tb)
-    auto key_side = [&](int w3) {
+    // keys in fragments (xf, vf) against the queries of chunk t (LDS, with
+    // its output gradients in gr / gt)
+    auto key_pass = [&](int t, bool own, const bf16x8(&xf)[KSTEPS], const bf16x8(&vf)[KSTEPS],
+                        int32_t mpos, int32_t mbkt, float mrn, int mlo, int mhi,
+                        f32x4(&dk)[DT], f32x4(&dvv)[DT], float& msdd) {
+        const int par = t & 1, s3 = t % 3;
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
+            if (!active(sm.bkt[s3][32 * qb], sm.bkt[s3][32 * qb + 31], mlo, mhi,
+                        own && dm.causal && 32 * qb + 31 < 16 * wave))
+                continue;
             u32x4 pfrag, dsfrag;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                // tile row r16 is item 32 qb + 8 (r16 / 4) + 4 h + r16 % 4
-                const int qw = 32 * qb + 16 * h + r16;   // its LDS row
+                const int qw = 32 * qb + 16 * h + r16;
                 f32x4 sacc = {0.f, 0.f, 0.f, 0.f}, pacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < KSTEPS; ++s) {
-                    const bf16x8 qa = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.ra[qw][32 * s + 8 * gq]);
-                    const bf16x8 ga = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.rb[qw][32 * s + 8 * gq]);
+                    const bf16x8 qa = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.xr[par][qw][32 * s + 8 * gq]);
+                    const bf16x8 ga = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.gr[qw][32 * s + 8 * gq]);
                     sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, xf[s], sacc, 0, 0, 0);
                     pacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga, vf[s], pacc, 0, 0, 0);
                 }
                 float pw[4], ds[4];
+                const int qbase = 32 * qb + 8 * gq + 4 * h;   // register i is query qbase + i
+                const i32x4 qps = *(const i32x4*)&sm.pos[s3][qbase];
+                const i32x4 qbk = *(const i32x4*)&sm.bkt[s3][qbase];
+                const f32x4 zq = *(const f32x4*)&sm.zz[par][qbase];
+                const f32x4 dq4 = *(const f32x4*)&sm.dd[par][qbase];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {   // query 32 qb + 8 gq + 4 h + i
-                    const int q = 32 * qb + 8 * gq + 4 * h + i;
-                    const int32_t qp = sm.pos[w3][q];
-                    const float zq = sm.zz[w3][q];
-                    const bool ok = sm.bkt[w3][q] == mbkt && (!dm.causal || mpos <= qp);
-                    const float s2 = sacc[i] * mrn * c2 - (mpos == qp ? pen2 : 0.f);
-                    pw[i] = pair_weight(ok, mpos == qp, s2, zq * kLog2e,
-                                        zq < -0.5f * kSelfPenalty, inv_nh);
-                    ds[i] = pw[i] * (pacc[i] - sm.dd[w3][q]);
+                for (int i = 0; i < 4; ++i) {
+                    const bool ok = qbk[i] == mbkt && (!dm.causal || mpos <= qps[i]);
+                    const float s2 = sacc[i] * mrn * c2 - (mpos == qps[i] ? pen2 : 0.f);
+                    pw[i] = pair_weight(ok, mpos == qps[i], s2, zq[i] * kLog2e,
+                                        zq[i] < -0.5f * kSelfPenalty, inv_nh);
+                    ds[i] = pw[i] * (pacc[i] - dq4[i]);
                     if constexpr (KN) msdd = fmaf(ds[i], sacc[i], msdd);
                 }
                 pfrag[2 * h] = pack_bf16x2(pw[0], pw[1]);
@@ -670,59 +635,120 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 const bf16x8 aq = __builtin_bit_cast(
-                    bf16x8, *(const u32x4*)&sm.ta[dt * 16 + r16][32 * qb + 8 * gq]);
+                    bf16x8, *(const u32x4*)&sm.xt[par][dt * 16 + r16][32 * qb + 8 * gq]);
                 const bf16x8 ag = __builtin_bit_cast(
-                    bf16x8, *(const u32x4*)&sm.tb[dt * 16 + r16][32 * qb + 8 * gq]);
+                    bf16x8, *(const u32x4*)&sm.gt[dt * 16 + r16][32 * qb + 8 * gq]);
                 dk[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, bd, dk[dt], 0, 0, 0);
                 dvv[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag, bp, dvv[dt], 0, 0, 0);
             }
         }
     };
-
-    // pair (c, c), query side: keys = the chunk (ra, ta), values (rb)
-    query_side(1);
-    // pair (c, c), key side: queries = the chunk (still in ra, ta), output
-    // gradients into rb, tb
-    stage(1, nullptr, G, false, true);
-    key_side(1);
-    // pair (c, c - 1): the previous chunk's keys and values
-    if (c > 0) {
-        stage(0, X, V, true, false);
-        query_side(0);
-    }
-    // pair (c + 1, c): the next chunk's queries and output gradients
-    if (c + 1 < nchunks) {
-        stage(2, X, G, true, true);
-        key_side(2);
-    }
-    // lane (slot me, group gq) holds features 16 dt + 4 gq + i of dq, dk, dv;
-    // the per-round rows are bf16 (one rounding, 2^-9 relative, before the
-    // float32 sum over rounds)
-    const float scale = 1.0f / sqrtf((float)D);
-    const int64_t row = ((bh * L + mpos) * dm.nh + r) * D;
-    if constexpr (KN) {
-        // dk = rn (sum dS x_i - rn^2 (sum dS x_i . x_j) x_j); the lanes of a
-        // slot hold disjoint query sets, so their sums are added first
-        msdd += __shfl_xor(msdd, 16);
-        msdd += __shfl_xor(msdd, 32);
-        const float pr = mrn * mrn * msdd;
+    // rows (dq + dk) * scale and dv of one slot; lane (slot, gq) holds
+    // features 16 dt + 4 gq + i
+    auto write_out = [&](int32_t mpos, float mrn, float msdd, f32x4(&dq)[DT], f32x4(&dk)[DT],
+                         f32x4(&dvv)[DT]) {
+        const int64_t row = ((bh * L + mpos) * dm.nh + r) * D;
+        if constexpr (KN) {
+            // dk = rn (sum dS x_i - rn^2 (sum dS x_i . x_j) x_j); the lanes of a
+            // slot hold disjoint query sets, so their sums are added first
+            msdd += __shfl_xor(msdd, 16);
+            msdd += __shfl_xor(msdd, 32);
+            const float pr = mrn * mrn * msdd;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const uint2 w = *(const uint2*)(X + (int64_t)mpos * D + 16 * dt + 4 * gq);
+                const f32x4 xm = {__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                                  __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
+                dk[dt] = (dk[dt] - pr * xm) * mrn;
+            }
+        }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            const uint2 w = *(const uint2*)(X + (int64_t)mpos * D + 16 * dt + 4 * gq);
-            const f32x4 xm = {__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
-                              __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
-            dk[dt] = (dk[dt] - pr * xm) * mrn;
+            const f32x4 a = (dq[dt] + dk[dt]) * scale;
+            const f32x4 b = dvv[dt];
+            *(uint2*)(dx_r + row + 16 * dt + 4 * gq) =
+                make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+            *(uint2*)(dv_r + row + 16 * dt + 4 * gq) =
+                make_uint2(pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3]));
+        }
+    };
+
+    // ---- prologue: sorted keys of chunks c0 - 1 .. c0 + 1, rows of chunks
+    // c0 - 1 and c0 (and their transposes)
+    if (tid < kBM)
+        for (int t = max(c0 - 1, 0); t <= min(c0 + 1, clast); ++t) load_keys(t);
+    __syncthreads();
+    Pre pf;
+    if (c0 > 0) {
+        gather(c0 - 1, pf);
+        park(c0 - 1, pf);
+    }
+    gather(c0, pf);
+    park(c0, pf);   // the same thread overwrites the output-gradient rows
+    __syncthreads();
+    if (c0 > 0) transpose_items<D>(sm.xr[(c0 - 1) & 1], sm.xt[(c0 - 1) & 1]);
+    transpose_items<D>(sm.xr[c0 & 1], sm.xt[c0 & 1]);
+    transpose_items<D>(sm.gr, sm.gt);
+    __syncthreads();
+
+    bf16x8 xf[KSTEPS], vf[KSTEPS], gf[KSTEPS];
+    f32x4 dq[DT], dk[DT], dvv[DT];
+    int32_t mpos = 0, mbkt = -1;
+    float mrn = 1.f, msdd = 0.f;
+    for (int c = c0; c <= clast; ++c) {
+        const bool mine = c < c1;          // chunk c belongs to this run
+        const bool nxt = c + 1 <= clast;   // chunk c + 1 is stepped by this run
+        // sorted keys of chunk c + 2 and rows of chunk c + 1 start travelling
+        int32_t kp2 = 0, kb2 = -1;
+        if (tid < kBM && c + 2 <= clast) read_key<PACKED>(P, Bk, (int64_t)(c + 2) * kBM + tid, kp2, kb2);
+        if (nxt) gather(c + 1, pf);
+        // 1. chunk c - 1 as keys against chunk c's queries, then its rows out
+        if (c > c0) {
+            const int s3p = (c - 1) % 3;   // chunk c - 1's keys: this wave's bucket range
+            key_pass(c, false, xf, vf, mpos, mbkt, mrn, sm.bkt[s3p][16 * wave],
+                     sm.bkt[s3p][16 * wave + 15], dk, dvv, msdd);
+            write_out(mpos, mrn, msdd, dq, dk, dvv);
+        }
+        if (mine) {
+            const int par = c & 1;
+#pragma unroll
+            for (int s = 0; s < KSTEPS; ++s) {
+                xf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.xr[par][prow][32 * s + 8 * gq]);
+                vf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.vr[par][prow][32 * s + 8 * gq]);
+                gf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.gr[prow][32 * s + 8 * gq]);
+            }
+            mpos = sm.pos[c % 3][me];
+            mbkt = sm.bkt[c % 3][me];
+            const float mz = sm.zz[par][me], mD = sm.dd[par][me];
+            mrn = KN ? sm.rn[par][me] : 1.f;
+            msdd = 0.f;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) dq[dt] = dk[dt] = dvv[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            const bool self_only = mz < -0.5f * kSelfPenalty;
+            const int mlo = sm.bkt[c % 3][16 * wave], mhi = sm.bkt[c % 3][16 * wave + 15];
+            // 2. chunk c as queries against chunks c - 1 and c
+            if (c > 0)
+                query_pass(c - 1, false, xf, gf, mpos, mbkt, mz * kLog2e, mD, self_only, mlo, mhi, dq);
+            query_pass(c, true, xf, gf, mpos, mbkt, mz * kLog2e, mD, self_only, mlo, mhi, dq);
+            // 3. chunk c as keys against its own queries
+            key_pass(c, true, xf, vf, mpos, mbkt, mrn, mlo, mhi, dk, dvv, msdd);
+        }
+        if (nxt) {
+            __syncthreads();   // every wave is done with chunk c - 1's slot and chunk c's gradients
+            park(c + 1, pf);
+            if (tid < kBM && c + 2 <= clast) {
+                sm.pos[(c + 2) % 3][tid] = kp2;
+                sm.bkt[(c + 2) % 3][tid] = kb2;
+            }
+            __syncthreads();
+            transpose_items<D>(sm.xr[(c + 1) & 1], sm.xt[(c + 1) & 1]);
+            transpose_items<D>(sm.gr, sm.gt);
+            __syncthreads();
         }
     }
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-        const f32x4 x = (dq[dt] + dk[dt]) * scale;
-        const f32x4 y = dvv[dt];
-        *(uint2*)(dx_r + row + 16 * dt + 4 * gq) =
-            make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
-        *(uint2*)(dv_r + row + 16 * dt + 4 * gq) =
-            make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
-    }
+    // a run that ends its segment finishes its last chunk here: there is no
+    // pair (c1, c1 - 1)
+    if (c1 == nchunks) write_out(mpos, mrn, msdd, dq, dk, dvv);
 }
 
 template <int D, typename T, bool PACKED>
@@ -734,15 +760,17 @@ hipError_t launch_bwd_t(const BwdArgs& a, const Dims& d, hipStream_t st) {
     bwd_dot_kernel<D, T><<<gq, 256, 0, st>>>(g, (const T*)a.out, d, a.Dv);
     if constexpr (sizeof(T) == 2) {
         if (d.m == kBM) {   // matrix-core passes
-            const dim3 grid((unsigned)(d.L / kBM), (unsigned)d.segs);
             uint16_t* hx = (uint16_t*)a.dx_r;
             uint16_t* hv = (uint16_t*)a.dv_r;
+            const int nchunks = d.L / kBM;
+            const int nruns = (nchunks + kBwdRun - 1) / kBwdRun;
+            const unsigned grid = (unsigned)(d.segs * nruns);
             if (a.rn)
-                bwd_mfma_kernel<D, PACKED, true><<<grid, 256, 0, st>>>(
-                    qk, v, g, a.perm, a.buckets, a.z, a.Dv, a.rn, d, hx, hv);
+                bwd_run_kernel<D, PACKED, true><<<grid, 256, 0, st>>>(
+                    qk, v, g, a.perm, a.buckets, a.z, a.Dv, a.rn, d, nruns, hx, hv);
             else
-                bwd_mfma_kernel<D, PACKED, false><<<grid, 256, 0, st>>>(
-                    qk, v, g, a.perm, a.buckets, a.z, a.Dv, nullptr, d, hx, hv);
+                bwd_run_kernel<D, PACKED, false><<<grid, 256, 0, st>>>(
+                    qk, v, g, a.perm, a.buckets, a.z, a.Dv, nullptr, d, nruns, hx, hv);
             const unsigned gr = (unsigned)((d.T * (D / 4) + 255) / 256);
             bwd_reduce_kernel<D, T, uint16_t><<<gr, 256, 0, st>>>(hx, hv, d, (T*)a.dqk,
                                                                   (T*)a.dv);

@@ -43,6 +43,11 @@ CASES = [
     _wl("bf16", 1, 2, 2048, 128, 128, 3, 64, True, 42),
     _wl("fp32", 1, 2, 768, 128, 8, 2, 32, True, 43),        # plain permutation
     _wl("bf16", 1, 1, 768, 64, 8, 2, 128, False, 44),       # chunk 128: fp32 rows
+    # runs of 16 chunks per workgroup: one chunk; a last run of one chunk;
+    # a last run of four
+    _wl("bf16", 1, 2, 64, 128, 8, 3, 64, True, 45),
+    _wl("bf16", 1, 2, 64 * 17, 64, 16, 2, 64, True, 46),
+    _wl("bf16", 2, 1, 64 * 20, 128, 32, 2, 64, False, 47),
 ]
 
 
