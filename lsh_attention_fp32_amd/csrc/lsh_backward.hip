@@ -332,16 +332,11 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(const T* __restrict__ qk,
     }
 }
 
-// Four consecutive values of a per-round row, as float32.
+// Four consecutive values of a float32 per-round row.
 __device__ __forceinline__ f32x4 load_row4(const float* p) { return *(const f32x4*)p; }
-__device__ __forceinline__ f32x4 load_row4(const uint16_t* p) {
-    const uint2 w = *(const uint2*)p;
-    return (f32x4){__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
-                   __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
-}
 
 // dqk_i = sum_r dx_r[i], dv_i = sum_r dv_r[i]; one thread per (token, 4
-// features). Rows are float32 (plain passes) or bf16 (matrix-core pass).
+// features), float32 rows of the plain passes.
 template <int D, typename T, typename RowT>
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(const RowT* __restrict__ dx_r,
                                                          const RowT* __restrict__ dv_r, Dims dm,
@@ -361,6 +356,50 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const RowT* __restrict_
         IO<T>::store(dqk, tok * D + e + i, a[i]);
         IO<T>::store(dv, tok * D + e + i, b[i]);
     }
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const bf16x2 w = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, w);
+}
+
+// The same sum for the bf16 rows of the matrix-core pass and bf16 outputs:
+// one thread per (token, 8 features), 16-byte nontemporal loads (the rows are
+// read once), fp32 sums.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_reduce_bf16_kernel(const uint16_t* __restrict__ dx_r,
+                                                              const uint16_t* __restrict__ dv_r,
+                                                              Dims dm, uint16_t* __restrict__ dqk,
+                                                              uint16_t* __restrict__ dv) {
+    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t tok = gid / (D / 8);
+    const int e = 8 * (int)(gid - tok * (D / 8));
+    if (tok >= dm.T) return;
+    float a[8] = {}, b[8] = {};
+#pragma unroll 4
+    for (int r = 0; r < dm.nh; ++r) {
+        const int64_t row = (tok * dm.nh + r) * D + e;
+        const u32x4v wa = __builtin_nontemporal_load((const u32x4v*)(dx_r + row));
+        const u32x4v wb = __builtin_nontemporal_load((const u32x4v*)(dv_r + row));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            a[2 * k] += __uint_as_float(wa[k] << 16);
+            a[2 * k + 1] += __uint_as_float(wa[k] & 0xFFFF0000u);
+            b[2 * k] += __uint_as_float(wb[k] << 16);
+            b[2 * k + 1] += __uint_as_float(wb[k] & 0xFFFF0000u);
+        }
+    }
+    u32x4v oa, ob;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        oa[k] = pack_bf16x2(a[2 * k], a[2 * k + 1]);
+        ob[k] = pack_bf16x2(b[2 * k], b[2 * k + 1]);
+    }
+    *(u32x4v*)(dqk + tok * D + e) = oa;
+    *(u32x4v*)(dv + tok * D + e) = ob;
 }
 
 // ---------------------------------------------------------------------------
@@ -384,7 +423,6 @@ struct BwdRows {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // LDS row of item j (of a 64-item chunk) in the row-major buffers of the
 // fused kernel. A score tile (block kb, half h) reads item
@@ -394,11 +432,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // apart on the same banks.
 __device__ __forceinline__ int phys_row(int j) {
     return (j & ~31) | (((j >> 3) & 3) << 2) | (((j >> 2) & 1) << 4) | (j & 3);
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    const bf16x2 w = {(__bf16)a, (__bf16)b};
-    return __builtin_bit_cast(uint32_t, w);
 }
 
 // Transposes the 64 rows of `rm` (stored at phys_row(item)) into `tr`
@@ -771,9 +804,9 @@ hipError_t launch_bwd_t(const BwdArgs& a, const Dims& d, hipStream_t st) {
             else
                 bwd_run_kernel<D, PACKED, false><<<grid, 256, 0, st>>>(
                     qk, v, g, a.perm, a.buckets, a.z, a.Dv, nullptr, d, nruns, hx, hv);
-            const unsigned gr = (unsigned)((d.T * (D / 4) + 255) / 256);
-            bwd_reduce_kernel<D, T, uint16_t><<<gr, 256, 0, st>>>(hx, hv, d, (T*)a.dqk,
-                                                                  (T*)a.dv);
+            const unsigned gr = (unsigned)((d.T * (D / 8) + 255) / 256);
+            bwd_reduce_bf16_kernel<D><<<gr, 256, 0, st>>>(hx, hv, d, (uint16_t*)a.dqk,
+                                                          (uint16_t*)a.dv);
             return hipGetLastError();
         }
     }
