@@ -438,12 +438,12 @@ __device__ __forceinline__ int phys_row(int j) {
 // ([D][TS], item order) inside LDS. The 64 lanes of a wave take the 64 items
 // at one 8-feature piece: the 16-byte reads land on distinct banks and each
 // of the 8 two-byte writes covers 128 contiguous bytes of a transposed row.
-template <int D>
+template <int D, int NT>
 __device__ __forceinline__ void transpose_items(const uint16_t (*rm)[BwdRows<D>::RS],
                                                 uint16_t (*tr)[BwdRows<D>::TS]) {
     const int item = threadIdx.x & (kBM - 1);
     const int row = phys_row(item);
-    for (int pc = threadIdx.x >> 6; pc < D / 8; pc += 256 / kBM) {
+    for (int pc = threadIdx.x >> 6; pc < D / 8; pc += NT / kBM) {
         const u32x4 a = *(const u32x4*)&rm[row][pc * 8];
 #pragma unroll
         for (int e = 0; e < 8; ++e)
@@ -454,20 +454,25 @@ __device__ __forceinline__ void transpose_items(const uint16_t (*rm)[BwdRows<D>:
 // ---------------------------------------------------------------------------
 // Run-based matrix-core pass. A workgroup walks a run of kBwdRun consecutive
 // chunks of one (batch, head, round) segment. Chunk c's slots are the queries
-// of the pairs (c, c - 1), (c, c) and the keys of the pairs (c, c), (c + 1, c);
-// at step c the workgroup
-//   1. finishes chunk c - 1 as keys: the key side of pair (c, c - 1), the
-//      queries being chunk c; then writes chunk c - 1's rows (dq + dk, dv);
-//   2. takes chunk c as queries against the keys of chunks c - 1 and c (dq);
-//   3. takes chunk c as keys against its own queries (dk, dv so far).
+// of the pairs (c, c - 1), (c, c) and the keys of the pairs (c, c), (c + 1, c).
+// Eight waves: waves 0-3 take the query side, waves 4-7 the key side, so each
+// SIMD runs one of each and the matrix work of one overlaps the other's
+// vector work. At step c
+//   query waves: chunk c as queries against the keys of chunks c - 1 and c
+//                (dq), handed to the key waves through LDS (bf16);
+//   key waves:   chunk c - 1 as keys against chunk c's queries (the key side
+//                of pair (c, c - 1)), then chunk c - 1's rows out
+//                ((dq + dk) scaled, dv); chunk c as keys against its own
+//                queries (dk, dv so far).
 // LDS holds the rows of chunks c - 1 and c (qk and v row-major, qk
 // transposed, one slot per chunk parity) and chunk c's output gradients.
 // Chunk c + 1's rows are gathered into registers at the top of step c and
 // parked in the slot chunk c - 1 leaves, so every chunk's rows come from HBM
 // once per run and a gather has a whole step of matrix work to arrive. The
-// last chunk of a run is finished by a partial step (1 only) on the next
-// chunk, whose run repeats that pair for its own queries.
-constexpr int kBwdRun = 16;   // chunks per workgroup
+// last chunk of a run is finished by a partial step on the next chunk (its
+// key side only), whose run repeats that pair for its own queries.
+constexpr int kBwdRun = 16;    // chunks per workgroup
+constexpr int kBwdThreads = 512;
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
@@ -479,32 +484,36 @@ struct alignas(16) BwdRunLds {
     uint16_t gr[kBM][RS];      // output-gradient rows of the current chunk
     uint16_t xt[2][D][TS];     // qk transposed (item order)
     uint16_t gt[D][TS];        // output gradients transposed
+    uint16_t xq[kBM][RS];      // dq of the current chunk (bf16), query waves -> key waves
     int32_t pos[3][kBM], bkt[3][kBM];          // chunk t in slot t % 3
     float zz[2][kBM], dd[2][kBM], rn[2][kBM];   // chunk t in slot t & 1
 };
 
 template <int D, bool PACKED, bool KN>
-__global__ __launch_bounds__(256) void bwd_run_kernel(const uint16_t* __restrict__ qk,
-                                                      const uint16_t* __restrict__ v,
-                                                      const uint16_t* __restrict__ g,
-                                                      const int32_t* __restrict__ perm,
-                                                      const int32_t* __restrict__ buckets,
-                                                      const float* __restrict__ z,
-                                                      const float* __restrict__ Dv,
-                                                      const float* __restrict__ rn, Dims dm,
-                                                      int nruns, uint16_t* __restrict__ dx_r,
-                                                      uint16_t* __restrict__ dv_r) {
+__global__ __launch_bounds__(kBwdThreads) void bwd_run_kernel(const uint16_t* __restrict__ qk,
+                                                              const uint16_t* __restrict__ v,
+                                                              const uint16_t* __restrict__ g,
+                                                              const int32_t* __restrict__ perm,
+                                                              const int32_t* __restrict__ buckets,
+                                                              const float* __restrict__ z,
+                                                              const float* __restrict__ Dv,
+                                                              const float* __restrict__ rn, Dims dm,
+                                                              int nruns, uint16_t* __restrict__ dx_r,
+                                                              uint16_t* __restrict__ dv_r) {
     constexpr int KSTEPS = D / 32, DT = D / 16;
-    constexpr int PER = kBM * (D / 8) / 256;   // 16-byte pieces per thread and source
+    constexpr int PER = kBM * (D / 8) / kBwdThreads;   // 16-byte pieces per thread and source
+    static_assert(PER >= 1, "every thread moves a piece of each row set");
     __shared__ BwdRunLds<D> sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool qside = wave < 4;   // waves 0-3: query side; 4-7: key side
+    const int wg = wave & 3;       // the wave's 16 slots in a chunk
     const int gq = lane >> 4, r16 = lane & 15;
     const int64_t seg = blockIdx.x / nruns;
     const int run = blockIdx.x - (int)(seg * nruns);
     const int nchunks = dm.L / kBM;
     const int c0 = run * kBwdRun;
     const int c1 = min(c0 + kBwdRun, nchunks);
-    const int clast = min(c1, nchunks - 1);   // step c1 (when it exists) runs part 1 only
+    const int clast = min(c1, nchunks - 1);   // step c1 (when it exists) is key side only
     const int64_t L = dm.L;
     const int64_t bh = seg / dm.nh;
     const int r = (int)(seg - bh * dm.nh);
@@ -517,7 +526,7 @@ __global__ __launch_bounds__(256) void bwd_run_kernel(const uint16_t* __restrict
     const float pen2 = kSelfPenalty * kLog2e;
     const float inv_nh = 1.0f / (float)dm.nh;
     const float scale = 1.0f / sqrtf((float)D);
-    const int me = 16 * wave + r16;   // this lane's slot within a chunk
+    const int me = 16 * wg + r16;   // this lane's slot within a chunk
     const int prow = phys_row(me);
 
     // rows of chunk t (positions in its pos slot) into registers, then LDS
@@ -529,7 +538,7 @@ __global__ __launch_bounds__(256) void bwd_run_kernel(const uint16_t* __restrict
         const int s3 = t % 3;
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
-            const int i = tid + 256 * k, row = i / (D / 8), pc = i % (D / 8);
+            const int i = tid + kBwdThreads * k, row = i / (D / 8), pc = i % (D / 8);
             const int64_t off = (int64_t)sm.pos[s3][row] * D + pc * 8;
             pf.x[k] = *(const u32x4*)(X + off);
             pf.v[k] = *(const u32x4*)(V + off);
@@ -546,7 +555,7 @@ __global__ __launch_bounds__(256) void bwd_run_kernel(const uint16_t* __restrict
         const int par = t & 1;
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
-            const int i = tid + 256 * k, row = phys_row(i / (D / 8)), pc = i % (D / 8);
+            const int i = tid + kBwdThreads * k, row = phys_row(i / (D / 8)), pc = i % (D / 8);
             *(u32x4*)&sm.xr[par][row][pc * 8] = pf.x[k];
             *(u32x4*)&sm.vr[par][row][pc * 8] = pf.v[k];
             *(u32x4*)&sm.gr[row][pc * 8] = pf.g[k];
@@ -564,7 +573,6 @@ __global__ __launch_bounds__(256) void bwd_run_kernel(const uint16_t* __restrict
         sm.bkt[t % 3][tid] = b;
     };
 
-    // chunk c's queries (fragments xf, gf) against the keys of chunk t (LDS)
     // A 32-item block takes part only if its bucket range meets the wave's
     // (chunks are sorted by bucket) and, within one chunk under causality,
     // only if it is not wholly on the wrong side: a key slot after every
@@ -573,6 +581,7 @@ __global__ __launch_bounds__(256) void bwd_run_kernel(const uint16_t* __restrict
         const bool a = lo <= mhi && hi >= mlo && !skip;
         return __builtin_amdgcn_readfirstlane((int)a) != 0;
     };
+    // chunk c's queries (fragments xf, gf) against the keys of chunk t (LDS)
     auto query_pass = [&](int t, bool own, const bf16x8(&xf)[KSTEPS], const bf16x8(&gf)[KSTEPS],
                           int32_t mpos, int32_t mbkt, float mz2, float mD, bool mself_only,
                           int mlo, int mhi, f32x4(&dq)[DT]) {
@@ -580,7 +589,7 @@ __global__ __launch_bounds__(256) void bwd_run_kernel(const uint16_t* __restrict
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             if (!active(sm.bkt[s3][32 * kb], sm.bkt[s3][32 * kb + 31], mlo, mhi,
-                        own && dm.causal && 32 * kb > 16 * wave + 15))
+                        own && dm.causal && 32 * kb > 16 * wg + 15))
                 continue;
             u32x4 dsfrag;
 #pragma unroll
@@ -629,7 +638,7 @@ __global__ __launch_bounds__(256) void bwd_run_kernel(const uint16_t* __restrict
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             if (!active(sm.bkt[s3][32 * qb], sm.bkt[s3][32 * qb + 31], mlo, mhi,
-                        own && dm.causal && 32 * qb + 31 < 16 * wave))
+                        own && dm.causal && 32 * qb + 31 < 16 * wg))
                 continue;
             u32x4 pfrag, dsfrag;
 #pragma unroll
@@ -719,69 +728,103 @@ __global__ __launch_bounds__(256) void bwd_run_kernel(const uint16_t* __restrict
     gather(c0, pf);
     park(c0, pf);   // the same thread overwrites the output-gradient rows
     __syncthreads();
-    if (c0 > 0) transpose_items<D>(sm.xr[(c0 - 1) & 1], sm.xt[(c0 - 1) & 1]);
-    transpose_items<D>(sm.xr[c0 & 1], sm.xt[c0 & 1]);
-    transpose_items<D>(sm.gr, sm.gt);
+    if (c0 > 0) transpose_items<D, kBwdThreads>(sm.xr[(c0 - 1) & 1], sm.xt[(c0 - 1) & 1]);
+    transpose_items<D, kBwdThreads>(sm.xr[c0 & 1], sm.xt[c0 & 1]);
+    transpose_items<D, kBwdThreads>(sm.gr, sm.gt);
     __syncthreads();
 
-    bf16x8 xf[KSTEPS], vf[KSTEPS], gf[KSTEPS];
-    f32x4 dq[DT], dk[DT], dvv[DT];
+    // One set of variables, two roles: query waves keep chunk c's qk and
+    // output-gradient fragments (fa, fb) and dq (acc); key waves keep their
+    // key chunk's qk and v fragments (fa, fb), dk (acc), dv (acc2) and the dq
+    // handed over (acc3), carried into the next step, where the key side of
+    // pair (c + 1, c) finishes them.
+    bf16x8 fa[KSTEPS], fb[KSTEPS];
+    f32x4 acc[DT], acc2[DT], acc3[DT];
     int32_t mpos = 0, mbkt = -1;
     float mrn = 1.f, msdd = 0.f;
     for (int c = c0; c <= clast; ++c) {
         const bool mine = c < c1;          // chunk c belongs to this run
         const bool nxt = c + 1 <= clast;   // chunk c + 1 is stepped by this run
+        const int par = c & 1, s3 = c % 3;
         // sorted keys of chunk c + 2 and rows of chunk c + 1 start travelling
         int32_t kp2 = 0, kb2 = -1;
         if (tid < kBM && c + 2 <= clast) read_key<PACKED>(P, Bk, (int64_t)(c + 2) * kBM + tid, kp2, kb2);
         if (nxt) gather(c + 1, pf);
-        // 1. chunk c - 1 as keys against chunk c's queries, then its rows out
-        if (c > c0) {
-            const int s3p = (c - 1) % 3;   // chunk c - 1's keys: this wave's bucket range
-            key_pass(c, false, xf, vf, mpos, mbkt, mrn, sm.bkt[s3p][16 * wave],
-                     sm.bkt[s3p][16 * wave + 15], dk, dvv, msdd);
-            write_out(mpos, mrn, msdd, dq, dk, dvv);
-        }
-        if (mine) {
-            const int par = c & 1;
+        const int mlo = sm.bkt[s3][16 * wg], mhi = sm.bkt[s3][16 * wg + 15];
+        if (qside) {
+            if (mine) {
+                // chunk c as queries against chunks c - 1 and c
 #pragma unroll
-            for (int s = 0; s < KSTEPS; ++s) {
-                xf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.xr[par][prow][32 * s + 8 * gq]);
-                vf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.vr[par][prow][32 * s + 8 * gq]);
-                gf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.gr[prow][32 * s + 8 * gq]);
+                for (int s = 0; s < KSTEPS; ++s) {
+                    fa[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.xr[par][prow][32 * s + 8 * gq]);
+                    fb[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.gr[prow][32 * s + 8 * gq]);
+                }
+                mpos = sm.pos[s3][me];
+                mbkt = sm.bkt[s3][me];
+                const float mz = sm.zz[par][me], mD = sm.dd[par][me];
+                const bool self_only = mz < -0.5f * kSelfPenalty;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) acc[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+                if (c > 0)
+                    query_pass(c - 1, false, fa, fb, mpos, mbkt, mz * kLog2e, mD, self_only, mlo, mhi, acc);
+                query_pass(c, true, fa, fb, mpos, mbkt, mz * kLog2e, mD, self_only, mlo, mhi, acc);
             }
-            mpos = sm.pos[c % 3][me];
-            mbkt = sm.bkt[c % 3][me];
-            const float mz = sm.zz[par][me], mD = sm.dd[par][me];
-            mrn = KN ? sm.rn[par][me] : 1.f;
-            msdd = 0.f;
+        } else {
+            // chunk c - 1 as keys against chunk c's queries, then its rows out
+            if (c > c0) {
+                const int s3p = (c - 1) % 3;   // chunk c - 1's keys: this wave's bucket range
+                key_pass(c, false, fa, fb, mpos, mbkt, mrn, sm.bkt[s3p][16 * wg],
+                         sm.bkt[s3p][16 * wg + 15], acc, acc2, msdd);
+                write_out(mpos, mrn, msdd, acc3, acc, acc2);
+            }
+            if (mine) {
+                // chunk c as keys against its own queries
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) dq[dt] = dk[dt] = dvv[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-            const bool self_only = mz < -0.5f * kSelfPenalty;
-            const int mlo = sm.bkt[c % 3][16 * wave], mhi = sm.bkt[c % 3][16 * wave + 15];
-            // 2. chunk c as queries against chunks c - 1 and c
-            if (c > 0)
-                query_pass(c - 1, false, xf, gf, mpos, mbkt, mz * kLog2e, mD, self_only, mlo, mhi, dq);
-            query_pass(c, true, xf, gf, mpos, mbkt, mz * kLog2e, mD, self_only, mlo, mhi, dq);
-            // 3. chunk c as keys against its own queries
-            key_pass(c, true, xf, vf, mpos, mbkt, mrn, mlo, mhi, dk, dvv, msdd);
+                for (int s = 0; s < KSTEPS; ++s) {
+                    fa[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.xr[par][prow][32 * s + 8 * gq]);
+                    fb[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.vr[par][prow][32 * s + 8 * gq]);
+                }
+                mpos = sm.pos[s3][me];
+                mbkt = sm.bkt[s3][me];
+                mrn = KN ? sm.rn[par][me] : 1.f;
+                msdd = 0.f;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) acc[dt] = acc2[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+                key_pass(c, true, fa, fb, mpos, mbkt, mrn, mlo, mhi, acc, acc2, msdd);
+            }
+        }
+        __syncthreads();   // chunk c - 1's slot, chunk c's gradients and xq are free
+        if (qside && mine) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                *(uint2*)&sm.xq[me][16 * dt + 4 * gq] =
+                    make_uint2(pack_bf16x2(acc[dt][0], acc[dt][1]), pack_bf16x2(acc[dt][2], acc[dt][3]));
         }
         if (nxt) {
-            __syncthreads();   // every wave is done with chunk c - 1's slot and chunk c's gradients
             park(c + 1, pf);
             if (tid < kBM && c + 2 <= clast) {
                 sm.pos[(c + 2) % 3][tid] = kp2;
                 sm.bkt[(c + 2) % 3][tid] = kb2;
             }
-            __syncthreads();
-            transpose_items<D>(sm.xr[(c + 1) & 1], sm.xt[(c + 1) & 1]);
-            transpose_items<D>(sm.gr, sm.gt);
-            __syncthreads();
         }
+        __syncthreads();
+        if (!qside && mine) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const uint2 w = *(const uint2*)&sm.xq[me][16 * dt + 4 * gq];
+                acc3[dt] = (f32x4){__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                                   __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
+            }
+        }
+        if (nxt) {
+            transpose_items<D, kBwdThreads>(sm.xr[(c + 1) & 1], sm.xt[(c + 1) & 1]);
+            transpose_items<D, kBwdThreads>(sm.gr, sm.gt);
+        }
+        __syncthreads();
     }
     // a run that ends its segment finishes its last chunk here: there is no
     // pair (c1, c1 - 1)
-    if (c1 == nchunks) write_out(mpos, mrn, msdd, dq, dk, dvv);
+    if (!qside && c1 == nchunks) write_out(mpos, mrn, msdd, acc3, acc, acc2);
 }
 
 template <int D, typename T, bool PACKED>
@@ -799,10 +842,10 @@ hipError_t launch_bwd_t(const BwdArgs& a, const Dims& d, hipStream_t st) {
             const int nruns = (nchunks + kBwdRun - 1) / kBwdRun;
             const unsigned grid = (unsigned)(d.segs * nruns);
             if (a.rn)
-                bwd_run_kernel<D, PACKED, true><<<grid, 256, 0, st>>>(
+                bwd_run_kernel<D, PACKED, true><<<grid, kBwdThreads, 0, st>>>(
                     qk, v, g, a.perm, a.buckets, a.z, a.Dv, a.rn, d, nruns, hx, hv);
             else
-                bwd_run_kernel<D, PACKED, false><<<grid, 256, 0, st>>>(
+                bwd_run_kernel<D, PACKED, false><<<grid, kBwdThreads, 0, st>>>(
                     qk, v, g, a.perm, a.buckets, a.z, a.Dv, nullptr, d, nruns, hx, hv);
             const unsigned gr = (unsigned)((d.T * (D / 8) + 255) / 256);
             bwd_reduce_bf16_kernel<D><<<gr, 256, 0, st>>>(hx, hv, d, (uint16_t*)a.dqk,
