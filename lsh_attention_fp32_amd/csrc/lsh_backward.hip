@@ -686,9 +686,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_run_kernel(const uint16_t* __
         }
     };
     // rows (dq + dk) * scale and dv of one slot; lane (slot, gq) holds
-    // features 16 dt + 4 gq + i
-    auto write_out = [&](int32_t mpos, float mrn, float msdd, f32x4(&dq)[DT], f32x4(&dk)[DT],
-                         f32x4(&dvv)[DT]) {
+    // features 16 dt + 4 gq + i of dk and dv, and dq waits in xq (the query
+    // waves write the next chunk's only after the barrier that ends this pass)
+    auto write_out = [&](int32_t mpos, float mrn, float msdd, f32x4(&dk)[DT], f32x4(&dvv)[DT]) {
         const int64_t row = ((bh * L + mpos) * dm.nh + r) * D;
         if constexpr (KN) {
             // dk = rn (sum dS x_i - rn^2 (sum dS x_i . x_j) x_j); the lanes of a
@@ -706,7 +706,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_run_kernel(const uint16_t* __
         }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            const f32x4 a = (dq[dt] + dk[dt]) * scale;
+            const uint2 w = *(const uint2*)&sm.xq[me][16 * dt + 4 * gq];
+            const f32x4 dq = {__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                              __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
+            const f32x4 a = (dq + dk[dt]) * scale;
             const f32x4 b = dvv[dt];
             *(uint2*)(dx_r + row + 16 * dt + 4 * gq) =
                 make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
@@ -735,11 +738,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_run_kernel(const uint16_t* __
 
     // One set of variables, two roles: query waves keep chunk c's qk and
     // output-gradient fragments (fa, fb) and dq (acc); key waves keep their
-    // key chunk's qk and v fragments (fa, fb), dk (acc), dv (acc2) and the dq
-    // handed over (acc3), carried into the next step, where the key side of
-    // pair (c + 1, c) finishes them.
+    // key chunk's qk and v fragments (fa, fb), dk (acc) and dv (acc2),
+    // carried into the next step, where the key side of pair (c + 1, c)
+    // finishes them.
     bf16x8 fa[KSTEPS], fb[KSTEPS];
-    f32x4 acc[DT], acc2[DT], acc3[DT];
+    f32x4 acc[DT], acc2[DT];
     int32_t mpos = 0, mbkt = -1;
     float mrn = 1.f, msdd = 0.f;
     for (int c = c0; c <= clast; ++c) {
@@ -775,7 +778,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_run_kernel(const uint16_t* __
                 const int s3p = (c - 1) % 3;   // chunk c - 1's keys: this wave's bucket range
                 key_pass(c, false, fa, fb, mpos, mbkt, mrn, sm.bkt[s3p][16 * wg],
                          sm.bkt[s3p][16 * wg + 15], acc, acc2, msdd);
-                write_out(mpos, mrn, msdd, acc3, acc, acc2);
+                write_out(mpos, mrn, msdd, acc, acc2);
             }
             if (mine) {
                 // chunk c as keys against its own queries
@@ -793,7 +796,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_run_kernel(const uint16_t* __
                 key_pass(c, true, fa, fb, mpos, mbkt, mrn, mlo, mhi, acc, acc2, msdd);
             }
         }
-        __syncthreads();   // chunk c - 1's slot, chunk c's gradients and xq are free
+        __syncthreads();   // chunk c - 1's slot, chunk c's gradients and xq (read by the write-out) are free
         if (qside && mine) {
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
@@ -808,14 +811,6 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_run_kernel(const uint16_t* __
             }
         }
         __syncthreads();
-        if (!qside && mine) {
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const uint2 w = *(const uint2*)&sm.xq[me][16 * dt + 4 * gq];
-                acc3[dt] = (f32x4){__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
-                                   __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
-            }
-        }
         if (nxt) {
             transpose_items<D, kBwdThreads>(sm.xr[(c + 1) & 1], sm.xt[(c + 1) & 1]);
             transpose_items<D, kBwdThreads>(sm.gr, sm.gt);
@@ -824,7 +819,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_run_kernel(const uint16_t* __
     }
     // a run that ends its segment finishes its last chunk here: there is no
     // pair (c1, c1 - 1)
-    if (!qside && c1 == nchunks) write_out(mpos, mrn, msdd, acc3, acc, acc2);
+    if (!qside && c1 == nchunks) write_out(mpos, mrn, msdd, acc, acc2);
 }
 
 template <int D, typename T, bool PACKED>
