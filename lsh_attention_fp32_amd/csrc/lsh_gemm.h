@@ -23,14 +23,17 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kPN = 256;        // outputs (n) per workgroup
 constexpr int kPM = 128;        // tokens (m) per workgroup
-constexpr int kPK = 32;         // k per LDS stage
-constexpr int kPRow = kPK + 8;  // padded LDS row (bf16): 80 bytes, rows 20 banks apart
+constexpr int kPK = 32;         // k per LDS stage: a 64-byte row of four 16-byte pieces
 constexpr int kXcds = 8;        // L2 domains the dispatcher deals workgroups over
 
+// LDS rows are unpadded; piece q of row r sits at piece q ^ swz(r). A
+// fragment read takes one piece of 16 consecutive rows, which then cover all
+// 64 banks; a stage store writes 4 whole rows (256 contiguous bytes).
 struct Lds {
-    uint16_t a[2][kPN][kPRow];   // weight rows
-    uint16_t b[2][kPM][kPRow];   // token rows
+    uint16_t a[2][kPN][kPK];   // weight rows
+    uint16_t b[2][kPM][kPK];   // token rows
 };
+__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
 // Weight rows n < nsplit come from w0, the others from w1 (row n - nsplit):
 // two weight tensors act as one concatenated W.
@@ -121,9 +124,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LSH_GEMM_WA
     };
     auto store_stage = [&](int buf) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) *(u32x4*)&sm.a[buf][pr + 64 * j][pc] = ra[j];
+        for (int j = 0; j < 4; ++j)
+            *(u32x4*)&sm.a[buf][pr + 64 * j][8 * ((pc >> 3) ^ swz(pr + 64 * j))] = ra[j];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) *(u32x4*)&sm.b[buf][pr + 64 * j][pc] = rb[j];
+        for (int j = 0; j < 2; ++j)
+            *(u32x4*)&sm.b[buf][pr + 64 * j][8 * ((pc >> 3) ^ swz(pr + 64 * j))] = rb[j];
     };
 
     f32x16 acc[4][2];
@@ -143,15 +148,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LSH_GEMM_WA
         if (s + 1 < nstages) load_stage((s + 1) * kPK);
 #pragma unroll
         for (int kk = 0; kk < kPK; kk += 16) {
+            const int q = (kk + fk) >> 3;   // logical piece of the fragment
             bf16x8 af[4], bfr[2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                af[i] = __builtin_bit_cast(
-                    bf16x8, *(const u32x4*)&sm.a[buf][wn * 128 + 32 * i + fr][kk + fk]);
+            for (int i = 0; i < 4; ++i) {
+                const int row = wn * 128 + 32 * i + fr;
+                af[i] = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.a[buf][row][8 * (q ^ swz(row))]);
+            }
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                bfr[j] = __builtin_bit_cast(
-                    bf16x8, *(const u32x4*)&sm.b[buf][wm * 64 + 32 * j + fr][kk + fk]);
+            for (int j = 0; j < 2; ++j) {
+                const int row = wm * 64 + 32 * j + fr;
+                bfr[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.b[buf][row][8 * (q ^ swz(row))]);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
