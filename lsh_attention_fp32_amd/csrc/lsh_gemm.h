@@ -35,6 +35,19 @@ struct Lds {
 };
 __device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
+// Waves per workgroup: 8 (a 4 x 2 grid of waves, 64 outputs x 64 tokens
+// each) or 4 (2 x 2, 128 x 64 each).
+#ifndef LSH_GEMM_WAVES
+#define LSH_GEMM_WAVES 8
+#endif
+constexpr int kGW = LSH_GEMM_WAVES;
+constexpr int kGT = 64 * kGW;            // threads per workgroup
+constexpr int kWN = kGW / 2;             // waves along the outputs
+constexpr int kNB = kPN / (32 * kWN);    // 32 x 32 blocks per wave along the outputs
+constexpr int kMB = kPM / (32 * 2);      // and along the tokens
+constexpr int kRows = kGT / 4;           // rows a staging pass covers (4 pieces each)
+constexpr int kAL = kPN / kRows, kBL = kPM / kRows;   // weight / token loads per thread
+
 // Weight rows n < nsplit come from w0, the others from w1 (row n - nsplit):
 // two weight tensors act as one concatenated W.
 struct Weights {
@@ -79,12 +92,12 @@ inline int64_t mfma_grid(int ntn, int64_t ntm) {
 // matrix work and stored after it). K and N must be multiples of 8; KTAIL:
 // K is not a multiple of kPK, so the last stage masks its missing pieces.
 template <class Out, bool KTAIL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LSH_GEMM_WAVES_PER_EU))) void mfma_kernel(const uint16_t* __restrict__ x, Weights wt,
+__global__ __launch_bounds__(kGT) __attribute__((amdgpu_waves_per_eu(LSH_GEMM_WAVES_PER_EU))) void mfma_kernel(const uint16_t* __restrict__ x, Weights wt,
                                                    int64_t M, int N, int K, int ntn, int64_t ntm,
                                                    Out out) {
     __shared__ Lds sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wn = wave & 1, wm = wave >> 1;
+    const int wn = wave % kWN, wm = wave / kWN;
     // this workgroup's tiles: group (block) b of its domain, place w in it;
     // places outside the tile grid end here, before any barrier
     int64_t tn, tm;
@@ -101,41 +114,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LSH_GEMM_WA
     const int n0 = (int)tn * kPN;
     const int64_t m0 = tm * kPM;
 
-    // global -> register staging: row r = tid / 4 + 64 j, piece tid % 4.
+    // global -> register staging: row r = tid / 4 + kRows j, piece tid % 4.
     // Each thread's six row pointers are fixed for the whole k loop; rows
     // past M or N read the last row instead (their results are never
     // stored), so a stage's loads are plain pointer + k, no bounds test.
     const int pr = tid >> 2, pc = (tid & 3) * 8;
-    const uint16_t* wp[4];
-    const uint16_t* xp[2];
+    const uint16_t* wp[kAL];
+    const uint16_t* xp[kBL];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) wp[j] = wt.row<uint16_t>(min(n0 + pr + 64 * j, N - 1), K) + pc;
+    for (int j = 0; j < kAL; ++j) wp[j] = wt.row<uint16_t>(min(n0 + pr + kRows * j, N - 1), K) + pc;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) xp[j] = x + min(m0 + pr + 64 * j, M - 1) * K + pc;
-    u32x4 ra[4], rb[2];
+    for (int j = 0; j < kBL; ++j) xp[j] = x + min(m0 + pr + kRows * j, M - 1) * K + pc;
+    u32x4 ra[kAL], rb[kBL];
     auto load_stage = [&](int k0) {
         const bool ok = !KTAIL || k0 + pc < K;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < kAL; ++j)
             ra[j] = ok ? *(const u32x4*)(wp[j] + k0) : (u32x4){0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < kBL; ++j)
             rb[j] = ok ? *(const u32x4*)(xp[j] + k0) : (u32x4){0u, 0u, 0u, 0u};
     };
     auto store_stage = [&](int buf) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            *(u32x4*)&sm.a[buf][pr + 64 * j][8 * ((pc >> 3) ^ swz(pr + 64 * j))] = ra[j];
+        for (int j = 0; j < kAL; ++j)
+            *(u32x4*)&sm.a[buf][pr + kRows * j][8 * ((pc >> 3) ^ swz(pr + kRows * j))] = ra[j];
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            *(u32x4*)&sm.b[buf][pr + 64 * j][8 * ((pc >> 3) ^ swz(pr + 64 * j))] = rb[j];
+        for (int j = 0; j < kBL; ++j)
+            *(u32x4*)&sm.b[buf][pr + kRows * j][8 * ((pc >> 3) ^ swz(pr + kRows * j))] = rb[j];
     };
 
-    f32x16 acc[4][2];
+    f32x16 acc[kNB][kMB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kNB; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = (f32x16){};
+        for (int j = 0; j < kMB; ++j) acc[i][j] = (f32x16){};
 
     // the next stage's rows travel into registers while this stage computes
     const int nstages = (K + kPK - 1) / kPK;
@@ -149,21 +162,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LSH_GEMM_WA
 #pragma unroll
         for (int kk = 0; kk < kPK; kk += 16) {
             const int q = (kk + fk) >> 3;   // logical piece of the fragment
-            bf16x8 af[4], bfr[2];
+            bf16x8 af[kNB], bfr[kMB];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = wn * 128 + 32 * i + fr;
+            for (int i = 0; i < kNB; ++i) {
+                const int row = wn * (32 * kNB) + 32 * i + fr;
                 af[i] = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.a[buf][row][8 * (q ^ swz(row))]);
             }
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < kMB; ++j) {
                 const int row = wm * 64 + 32 * j + fr;
                 bfr[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.b[buf][row][8 * (q ^ swz(row))]);
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < kNB; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < kMB; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j],
                                                                         0, 0, 0);
         }
@@ -183,13 +196,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LSH_GEMM_WA
     for (int p = 0; p < 2; ++p) {
         if (wm == p) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < kMB; ++j)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < kNB; ++i)
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
                         const int ml = 32 * j + (lane & 31);
-                        const int nl = wn * 128 + 32 * i + 8 * g + 4 * (lane >> 5);
+                        const int nl = wn * (32 * kNB) + 32 * i + 8 * g + 4 * (lane >> 5);
                         const int n = n0 + nl;
                         const f32x16& a = acc[i][j];
                         float f[4];
@@ -203,7 +216,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LSH_GEMM_WA
         }
         __syncthreads();
 #pragma unroll
-        for (int q = tid; q < 64 * (kPN / 8); q += 256) {
+        for (int q = tid; q < 64 * (kPN / 8); q += kGT) {
             const int ml = q / (kPN / 8), pc2 = q % (kPN / 8);
             const int64_t m = m0 + 64 * p + ml;
             const int n = n0 + 8 * pc2;
@@ -269,10 +282,10 @@ inline hipError_t launch(bool bf16, const void* x, Weights wt, int64_t M, int N,
         const int64_t ntm = (M + kPM - 1) / kPM;
         const unsigned grid = (unsigned)mfma_grid(ntn, ntm);
         if (K % kPK)
-            mfma_kernel<OutB, true><<<grid, 256, 0, st>>>((const uint16_t*)x, wt, M, N, K, ntn,
+            mfma_kernel<OutB, true><<<grid, kGT, 0, st>>>((const uint16_t*)x, wt, M, N, K, ntn,
                                                           ntm, ob);
         else
-            mfma_kernel<OutB, false><<<grid, 256, 0, st>>>((const uint16_t*)x, wt, M, N, K, ntn,
+            mfma_kernel<OutB, false><<<grid, kGT, 0, st>>>((const uint16_t*)x, wt, M, N, K, ntn,
                                                            ntm, ob);
     } else {
         const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
