@@ -66,13 +66,6 @@ struct Weights {
 //                                       n % 8 == 0 the 8 outputs n .. n+7
 //                                       are contiguous (bf16 path)
 
-// Waves per SIMD the register budget is cut for (the accumulators take 128
-// registers of a wave; one wave per SIMD lets the compiler keep them apart in
-// AGPRs, two make it fit everything in 256).
-#ifndef LSH_GEMM_WAVES_PER_EU
-#define LSH_GEMM_WAVES_PER_EU 1
-#endif
-
 // Workgroups are dealt round-robin over the L2 domains (id % kXcds). Each
 // domain takes groups of kGM token tiles x kGN output tiles, so the
 // workgroups it runs together share 8 token panels and 4 weight panels
@@ -86,13 +79,14 @@ inline int64_t mfma_grid(int ntn, int64_t ntm) {
     return (nblocks + kXcds - 1) / kXcds * kXcds * kGM * kGN;
 }
 
-// Waves 2 (n) x 2 (m); each wave owns 128 outputs x 64 tokens = 4 x 2 blocks
-// of 32 x 32 accumulators. A stage moves 256 + 128 rows of 64 bytes from HBM
-// into LDS (six 16-byte loads per thread, issued before the current stage's
-// matrix work and stored after it). K and N must be multiples of 8; KTAIL:
-// K is not a multiple of kPK, so the last stage masks its missing pieces.
+// Waves kWN (n) x 2 (m); each wave owns 32 kNB outputs x 64 tokens (kNB x 2
+// blocks of 32 x 32 accumulators). A stage moves 256 + 128 rows of 64 bytes
+// from HBM into LDS (kAL + kBL 16-byte loads per thread, issued before the
+// current stage's matrix work and stored after it). K and N must be
+// multiples of 8; KTAIL: K is not a multiple of kPK, so the last stage masks
+// its missing pieces.
 template <class Out, bool KTAIL>
-__global__ __launch_bounds__(kGT) __attribute__((amdgpu_waves_per_eu(LSH_GEMM_WAVES_PER_EU))) void mfma_kernel(const uint16_t* __restrict__ x, Weights wt,
+__global__ __launch_bounds__(kGT) void mfma_kernel(const uint16_t* __restrict__ x, Weights wt,
                                                    int64_t M, int N, int K, int ntn, int64_t ntm,
                                                    Out out) {
     __shared__ Lds sm;
