@@ -504,6 +504,166 @@ int oracle_backward(const double *qk, const double *v, const double *R, const do
 }
 
 /* ------------------------------------------------------------------------ */
+/* G1 at chosen positions of one (batch, head): the rows dqk[p] and dv[p]   */
+/* of G1 for each position p in toks, by the same sums restricted to the    */
+/* terms that land in those rows. A position's rows receive terms only from */
+/* query slots in its own chunk (as query and as key) and in the next chunk */
+/* (queries that look back at it), in every round; those queries' Z_i and   */
+/* D_i need their forward at every round's slot. So the forward runs at     */
+/* exactly those slots and tokens, and the (round, slot, key) loop visits   */
+/* the same terms in the same order as G1 does, skipping the ones that land */
+/* in rows outside toks: each chosen row comes out as G1 computes it. Meant */
+/* for sequences where G1 over every position is too slow.                  */
+/*                                                                           */
+/*   x, v, dout  [L, d]  one (batch, head) by original position             */
+/*   R           [n_hashes, d, n_buckets/2]  this head's rotations          */
+/*   toks        n_toks distinct positions                                  */
+/*   dqk, dv     [n_toks, d]  out, row q for position toks[q]                */
+/* ------------------------------------------------------------------------ */
+int oracle_backward_rows(const double *x, const double *v, const double *R,
+                         const double *dout, int64_t L, int d, int n_buckets, int n_hashes,
+                         int chunk_len, int causal, int key_norm, const int64_t *toks,
+                         int64_t n_toks, double *dqk, double *dv)
+{
+    if (L < 1 || d < 1 || n_hashes < 1 || chunk_len < 1 || n_buckets < 2 ||
+        (n_buckets % 2) != 0 || (L % chunk_len) != 0 || n_toks < 0)
+        return -1;
+    const int64_t seg = (int64_t)n_hashes * L;
+    const int64_t m = chunk_len, n_chunks = L / chunk_len;
+    const double scale = 1.0 / sqrt((double)d);
+    int32_t *bk = (int32_t *)malloc(sizeof(int32_t) * (size_t)seg);
+    int32_t *pm = (int32_t *)malloc(sizeof(int32_t) * (size_t)seg);
+    int32_t *iv = (int32_t *)malloc(sizeof(int32_t) * (size_t)seg);
+    double *mg = (double *)malloc(sizeof(double) * (size_t)seg);
+    double *ls = (double *)malloc(sizeof(double) * (size_t)seg);
+    double *os = (double *)malloc(sizeof(double) * (size_t)seg * (size_t)d);
+    double *out = (double *)malloc(sizeof(double) * (size_t)L * (size_t)d);
+    double *z = (double *)malloc(sizeof(double) * (size_t)L);
+    double *dd = (double *)malloc(sizeof(double) * (size_t)L);
+    int64_t *row = (int64_t *)malloc(sizeof(int64_t) * (size_t)L);     /* position -> q, or -1 */
+    char *qchunk = (char *)calloc((size_t)(n_hashes * n_chunks), 1);  /* query chunks visited */
+    char *need = (char *)calloc((size_t)seg, 1);                      /* slots to attend */
+    char *qtok = (char *)calloc((size_t)L, 1);                        /* queries visited */
+    int64_t *list = (int64_t *)malloc(sizeof(int64_t) * (size_t)(seg > L ? seg : L));
+    int rc = (bk && pm && iv && mg && ls && os && out && z && dd && row && qchunk && need &&
+              qtok && list) ? 0 : -2;
+    if (!rc) rc = oracle_hash(x, L, d, R, n_hashes, n_buckets, bk, mg);
+    for (int r = 0; !rc && r < n_hashes; ++r)
+        rc = oracle_sort(bk + r * L, L, pm + r * L, iv + r * L);
+    for (int64_t p = 0; !rc && p < L; ++p) row[p] = -1;
+    for (int64_t q = 0; !rc && q < n_toks; ++q) {
+        const int64_t p = toks[q];
+        if (p < 0 || p >= L || row[p] >= 0) rc = -1;   /* out of range or repeated */
+        else row[p] = q;
+    }
+    if (!rc) {
+        /* query chunks whose terms reach a chosen row: its own and the next */
+        for (int64_t q = 0; q < n_toks; ++q)
+            for (int r = 0; r < n_hashes; ++r) {
+                const int64_t c = iv[(int64_t)r * L + toks[q]] / m;
+                qchunk[r * n_chunks + c] = 1;
+                if (c + 1 < n_chunks) qchunk[r * n_chunks + c + 1] = 1;
+            }
+        /* their queries, and each of those queries' slots in every round */
+        for (int r = 0; r < n_hashes; ++r)
+            for (int64_t s = 0; s < L; ++s)
+                if (qchunk[r * n_chunks + s / m]) qtok[pm[(int64_t)r * L + s]] = 1;
+        for (int64_t i = 0; i < L; ++i)
+            if (qtok[i])
+                for (int r = 0; r < n_hashes; ++r) need[(int64_t)r * L + iv[(int64_t)r * L + i]] = 1;
+        for (int r = 0; !rc && r < n_hashes; ++r) {
+            int64_t n = 0;
+            for (int64_t s = 0; s < L; ++s)
+                if (need[(int64_t)r * L + s]) list[n++] = s;
+            rc = oracle_attend(x, v, L, d, bk + r * L, pm + r * L, chunk_len, causal, list, n,
+                               os + r * L * d, ls + r * L, key_norm);
+        }
+        int64_t n_q = 0;
+        for (int64_t i = 0; i < L; ++i)
+            if (qtok[i]) list[n_q++] = i;
+        if (!rc) rc = oracle_combine(os, ls, iv, n_hashes, L, d, list, n_q, out);
+    }
+    if (!rc) {
+        /* Z_i and D_i as G1 forms them, for the visited queries */
+        for (int64_t i = 0; i < L; ++i) {
+            if (!qtok[i]) continue;
+            double mx = -INFINITY;
+            for (int r = 0; r < n_hashes; ++r) {
+                const double l = ls[(int64_t)r * L + iv[(int64_t)r * L + i]];
+                if (l > mx) mx = l;
+            }
+            double sum = 0.0;
+            for (int r = 0; r < n_hashes; ++r)
+                sum += exp(ls[(int64_t)r * L + iv[(int64_t)r * L + i]] - mx);
+            z[i] = mx + log(sum);
+            double dot = 0.0;
+            for (int k = 0; k < d; ++k) dot += dout[i * d + k] * out[i * d + k];
+            dd[i] = dot;
+        }
+        for (int64_t e = 0; e < n_toks * d; ++e) {
+            dqk[e] = 0.0;
+            dv[e] = 0.0;
+        }
+        for (int r = 0; r < n_hashes; ++r) {
+            const int32_t *bucket = bk + (int64_t)r * L;
+            const int32_t *perm = pm + (int64_t)r * L;
+            for (int64_t s = 0; s < L; ++s) {
+                const int64_t c = s / m;
+                if (!qchunk[r * n_chunks + c]) continue;
+                const int64_t i = perm[s];
+                const int64_t t0 = (c > 0) ? (c - 1) * m : 0;
+                const int64_t t1 = (c + 1) * m;
+                const double *xi = x + i * d, *gi = dout + i * d;
+                for (int64_t t = t0; t < t1; ++t) {
+                    const int64_t j = perm[t];
+                    if (row[i] < 0 && row[j] < 0) continue;
+                    if (!((bucket[j] == bucket[i]) && (!causal || j <= i))) continue;
+                    const double *xj = x + j * d, *vj = v + j * d;
+                    double dot = 0.0, gdv = 0.0;
+                    for (int k = 0; k < d; ++k) {
+                        dot += xi[k] * xj[k];
+                        gdv += gi[k] * vj[k];
+                    }
+                    const double rn = key_norm ? inv_norm(xj, d) : 1.0;
+                    double sc = dot * scale * rn;
+                    if (j == i) sc -= ORACLE_SELF_PENALTY;
+                    const double p = exp(sc - z[i]);
+                    const double ds = p * (gdv - dd[i]);
+                    double *qi = row[i] >= 0 ? dqk + row[i] * d : NULL;
+                    double *kj = row[j] >= 0 ? dqk + row[j] * d : NULL;
+                    double *vo = row[j] >= 0 ? dv + row[j] * d : NULL;
+                    for (int k = 0; k < d; ++k) {
+                        if (vo) vo[k] += p * gi[k];
+                        if (qi) qi[k] += ds * scale * rn * xj[k];
+                        if (kj) {
+                            if (key_norm)
+                                kj[k] += ds * scale * rn * (xi[k] - dot * rn * rn * xj[k]);
+                            else
+                                kj[k] += ds * scale * xi[k];
+                        }
+                    }
+                }
+            }
+        }
+    }
+    free(bk);
+    free(pm);
+    free(iv);
+    free(mg);
+    free(ls);
+    free(os);
+    free(out);
+    free(z);
+    free(dd);
+    free(row);
+    free(qchunk);
+    free(need);
+    free(qtok);
+    free(list);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
 /* P0 -- input projections ahead of the hash.                               */
 /* [GLOSSARY] "Atenção LSH": queries and keys come from one shared          */
 /* projection; [SCHOLAR] "Reformerを用いた結果": a model width of 1024       */

@@ -73,13 +73,17 @@ def _load():
                                         ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_int, ctypes.c_int, _f64p, _f64p, ctypes.c_int,
                                         ctypes.c_int]
+        lib.oracle_backward_rows.argtypes = [_f64p, _f64p, _f64p, _f64p, ctypes.c_int64,
+                                             ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_int, ctypes.c_int, _i64p,
+                                             ctypes.c_int64, _f64p, _f64p]
         lib.oracle_ffn.argtypes = [_f64p, ctypes.c_int64, ctypes.c_int, _f64p, _f64p, _f64p,
                                    _f64p, ctypes.c_int, ctypes.c_int64, _f64p]
         lib.oracle_threads.argtypes = []
         lib.oracle_threads.restype = ctypes.c_int
         for fn in (lib.oracle_hash, lib.oracle_sort, lib.oracle_attend, lib.oracle_combine,
                    lib.oracle_forward, lib.oracle_project, lib.oracle_backward,
-                   lib.oracle_ffn):
+                   lib.oracle_backward_rows, lib.oracle_ffn):
             fn.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -255,6 +259,31 @@ def backward(qk, v, R, dout, n_buckets: int, chunk_len: int, causal: bool,
                                    B, H, L, d, n_buckets, nh, chunk_len, int(bool(causal)),
                                    _p(dqk, _f64p), _p(dv, _f64p), int(bool(key_norm)), per_head),
            "backward")
+    return dqk, dv
+
+
+def backward_rows(x, v, R, dout, tokens, n_buckets: int, chunk_len: int, causal: bool,
+                  key_norm: bool = False):
+    """G1 at chosen positions of one (batch, head): rows (dqk[p], dv[p]) for
+    each p in ``tokens`` (distinct), each as ``backward`` computes it, with
+    the forward run only where those rows need it. x, v, dout: [L, d];
+    R: this head's rotations [nh, d, nb/2]. Returns two [len(tokens), d]."""
+    x = _f64(x)
+    v = _f64(v)
+    dout = _f64(dout)
+    R = _f64(R)
+    L, d = x.shape
+    nh = R.shape[0]
+    if R.shape != (nh, d, n_buckets // 2) or v.shape != x.shape or dout.shape != x.shape:
+        raise ValueError("x, v, dout must be [L, d] and R [nh, d, n_buckets/2]")
+    tk = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))
+    dqk = np.empty((tk.shape[0], d))
+    dv = np.empty((tk.shape[0], d))
+    _check(_load().oracle_backward_rows(_p(x, _f64p), _p(v, _f64p), _p(R, _f64p),
+                                        _p(dout, _f64p), L, d, n_buckets, nh, chunk_len,
+                                        int(bool(causal)), int(bool(key_norm)), _p(tk, _i64p),
+                                        tk.shape[0], _p(dqk, _f64p), _p(dv, _f64p)),
+           "backward_rows")
     return dqk, dv
 
 

@@ -124,3 +124,31 @@ def test_fwd_x_matches_oracle(dtype, B, L, dm, H, d, nb, nh, m, causal):
             compared += 1
             assert np.abs(got[b, h] - ref[b, h]).max() <= TOL[dtype]
     assert compared >= 1
+
+
+def test_projection_fullsize_sampled_rows():
+    """The benchmark's shape (65536 tokens, d_model 1024 -> 8 heads x 128):
+    the whole projection on the GPU, sampled token rows against the oracle
+    (each output row depends only on its own token vector), with the bound
+    of the small cases; and lsh_attention_fwd_x bit-equal to the projection
+    followed by lsh_attention_fwd at that size."""
+    B, L, dm, H, d, nb, nh, m = 1, 65536, 1024, 8, 128, 1024, 8, 64
+    rng = np.random.default_rng(800)
+    x = workloads.round_to_bf16(rng.standard_normal((B, L, dm), dtype=np.float32))
+    w_qk = workloads.round_to_bf16(rng.standard_normal((H * d, dm), dtype=np.float32) / 32)
+    w_v = workloads.round_to_bf16(rng.standard_normal((H * d, dm), dtype=np.float32) / 32)
+    xt, wq, wv = _dev(x, "bf16"), _dev(w_qk, "bf16"), _dev(w_v, "bf16")
+    qk_t, v_t = lsh.qkv_project(xt, wq, wv, H)
+    toks = np.sort(np.concatenate([[0, L - 1], rng.choice(np.arange(1, L - 1), 62,
+                                                          replace=False)]))
+    ref_qk, ref_v = oracle.project(x[:, toks], w_qk, w_v, H)
+    mag_qk, mag_v = oracle.project(np.abs(x[:, toks]), np.abs(w_qk), np.abs(w_v), H)
+    for got_t, ref, mag in ((qk_t, ref_qk, mag_qk), (v_t, ref_v, mag_v)):
+        got = got_t.float().cpu().numpy()
+        assert np.isfinite(got).all()
+        got = got[:, :, toks]
+        assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 2.0 ** -16 * mag)
+    R = torch.from_numpy(rng.standard_normal((nh, d, nb // 2), dtype=np.float32)).to(DEV)
+    out = lsh.attention_fwd_x(xt, wq, wv, R, H, nb, m, True)
+    ref_out = lsh.attention_fwd(qk_t, v_t, R, nb, m, True)
+    assert torch.equal(out, ref_out)

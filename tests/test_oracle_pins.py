@@ -466,6 +466,40 @@ def test_backward_duplicated_round(oracle_mod):
     np.testing.assert_allclose(a[1], b[1], rtol=1e-9, atol=1e-9)
 
 
+@pytest.mark.parametrize("L,d,nb,nh,m,causal,key_norm", [
+    (256, 16, 8, 3, 16, True, False),
+    (512, 32, 16, 2, 32, False, True),
+    (192, 8, 4, 4, 64, True, True),
+    (64, 8, 4, 2, 64, False, False),        # one chunk
+])
+def test_backward_rows_equal_full_backward(oracle_mod, L, d, nb, nh, m, causal, key_norm):
+    """G1 at chosen positions: every chosen row is the full backward's row,
+    bit for bit (the same terms summed in the same order), including the
+    positions in the first and last sorted chunk of every round."""
+    rng = np.random.default_rng(66 + L + d)
+    qk, v, R, g = _fd_case(rng, 1, 1, L, d, nh, nb)
+    dqk, dv = oracle_mod.backward(qk, v, R, g, nb, m, causal, key_norm=key_norm)
+    _, extra = oracle_mod.forward(qk, v, R, nb, m, causal, return_all=True)
+    edge = {int(p) for r in range(nh) for p in (extra["perm"][0, 0, r, 0],
+                                                 extra["perm"][0, 0, r, L - 1])}
+    toks = np.array(sorted(edge | set(rng.choice(L, size=12, replace=False).tolist())))
+    rq, rv = oracle_mod.backward_rows(qk[0, 0], v[0, 0], R, g[0, 0], toks, nb, m, causal,
+                                      key_norm=key_norm)
+    assert np.array_equal(rq, dqk[0, 0, toks]) and np.array_equal(rv, dv[0, 0, toks])
+    # one position alone gives its row too (nothing depends on the other rows)
+    q1, v1 = oracle_mod.backward_rows(qk[0, 0], v[0, 0], R, g[0, 0], toks[:1], nb, m, causal,
+                                      key_norm=key_norm)
+    assert np.array_equal(q1[0], dqk[0, 0, toks[0]]) and np.array_equal(v1[0], dv[0, 0, toks[0]])
+
+
+def test_backward_rows_rejects_bad_positions(oracle_mod):
+    rng = np.random.default_rng(67)
+    qk, v, R, g = _fd_case(rng, 1, 1, 64, 8, 2, 4)
+    for toks in ([3, 3], [64], [-1]):
+        with pytest.raises(ValueError):
+            oracle_mod.backward_rows(qk[0, 0], v[0, 0], R, g[0, 0], toks, 4, 16, True)
+
+
 # --------------------------------------------------------------------------- key normalisation
 
 def test_key_norm_unit_rows_equal_plain(oracle_mod):
