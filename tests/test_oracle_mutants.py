@@ -77,6 +77,12 @@ MUTANTS = {
     "ffn_chunk_restarts_rows": ("const double *xr = x + (r0 + i) * d_model;",
                                 "const double *xr = x + i * d_model;"),
     "key_norm_backward_no_projection": ("(xi[k] - dot * rn * rn * xj[k])", "(xi[k])"),
+    # the chosen-rows backward: queries of the next chunk (which look back at
+    # a chosen key) left out; terms landing only in a chosen key row skipped
+    "backward_rows_no_next_chunk": ("if (c + 1 < n_chunks) qchunk[r * n_chunks + c + 1] = 1;",
+                                    "(void)0;"),
+    "backward_rows_query_side_only": ("if (row[i] < 0 && row[j] < 0) continue;",
+                                      "if (row[i] < 0) continue;"),
 }
 
 
