@@ -28,9 +28,15 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 TOL = {"fp32": 1e-4, "bf16": 2e-2}
 
+# 500 chunks of 64 per (head, round): the backward's workgroups take runs of
+# 32 chunks there, the last one ragged (20 chunks); 64 at 64K tokens
+EXTRA = {"l32000_h8_d128_nh8": workloads.Workload("l32000_h8_d128_nh8", 1, 8, 32000, 128,
+                                                  "bf16", 1000, 8, 64, True, 1017)}
+
 # (workload, key_norm, per-head rotations)
 CASES = [
     ("l64k_h8_d128_nh8", False, False),
+    ("l32000_h8_d128_nh8", False, False),
     ("l64k_h8_d128_nh8", True, False),
     ("l64k_h8_d128_nh8", False, True),
     ("b8_h8_l4k_nh4", False, False),
@@ -49,7 +55,7 @@ def _gpu():
                          ids=[f"{n}{'_keynorm' if k else ''}{'_perhead' if p else ''}"
                               for n, k, p in CASES])
 def test_fullsize_backward_sampled_rows(name, key_norm, per_head):
-    w = workloads.WORKLOADS[name]
+    w = EXTRA[name] if name in EXTRA else workloads.WORKLOADS[name]
     qk, v, R = workloads.make_inputs(w)
     if per_head:
         R = np.random.default_rng(w.seed + 1).standard_normal(
