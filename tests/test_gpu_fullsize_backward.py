@@ -30,13 +30,17 @@ TOL = {"fp32": 1e-4, "bf16": 2e-2}
 
 # 500 chunks of 64 per (head, round): the backward's workgroups take runs of
 # 32 chunks there, the last one ragged (20 chunks); 64 at 64K tokens
+# 520 chunks, 128 segments: runs of 64 chunks with a ragged last run (8)
 EXTRA = {"l32000_h8_d128_nh8": workloads.Workload("l32000_h8_d128_nh8", 1, 8, 32000, 128,
-                                                  "bf16", 1000, 8, 64, True, 1017)}
+                                                  "bf16", 1000, 8, 64, True, 1017),
+         "l33280_h16_d64_nh8": workloads.Workload("l33280_h16_d64_nh8", 1, 16, 33280, 64,
+                                                  "bf16", 1040, 8, 64, True, 1018)}
 
 # (workload, key_norm, per-head rotations)
 CASES = [
     ("l64k_h8_d128_nh8", False, False),
     ("l32000_h8_d128_nh8", False, False),
+    ("l33280_h16_d64_nh8", False, False),
     ("l64k_h8_d128_nh8", True, False),
     ("l64k_h8_d128_nh8", False, True),
     ("b8_h8_l4k_nh4", False, False),
