@@ -109,6 +109,32 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(const T* __restrict__ g,
     if (part == 0) Dv[tok] = s;
 }
 
+// The same dot for bf16 rows: D/8 lanes per token, one 16-byte nontemporal
+// load of each row per lane (a wave's load covers whole rows, contiguous),
+// fp32 products summed across the token's lanes.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dot_bf16_kernel(const uint16_t* __restrict__ g,
+                                                           const uint16_t* __restrict__ out,
+                                                           Dims dm, float* __restrict__ Dv) {
+    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+    constexpr int TPT = D / 8;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t tok = gid / TPT;
+    const int q = (int)(gid % TPT);
+    if (tok >= dm.T) return;   // whole tokens drop out together
+    const u32x4v a = __builtin_nontemporal_load((const u32x4v*)(g + tok * D) + q);
+    const u32x4v b = __builtin_nontemporal_load((const u32x4v*)(out + tok * D) + q);
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        s = fmaf(__uint_as_float(a[i] << 16), __uint_as_float(b[i] << 16), s);
+        s = fmaf(__uint_as_float(a[i] & 0xFFFF0000u), __uint_as_float(b[i] & 0xFFFF0000u), s);
+    }
+#pragma unroll
+    for (int off = TPT / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    if (q == 0) Dv[tok] = s;
+}
+
 template <int D, typename T, bool PACKED>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(const T* __restrict__ qk,
                                                      const T* __restrict__ v,
@@ -838,8 +864,13 @@ hipError_t launch_bwd_t(const BwdArgs& a, const Dims& d, hipStream_t st) {
     const T* qk = (const T*)a.qk;
     const T* v = (const T*)a.v;
     const T* g = (const T*)a.dout;
-    const unsigned gq = (unsigned)((d.T * 4 + 255) / 256);
-    bwd_dot_kernel<D, T><<<gq, 256, 0, st>>>(g, (const T*)a.out, d, a.Dv);
+    if constexpr (sizeof(T) == 2) {
+        const unsigned gq = (unsigned)((d.T * (D / 8) + 255) / 256);
+        bwd_dot_bf16_kernel<D><<<gq, 256, 0, st>>>(g, (const T*)a.out, d, a.Dv);
+    } else {
+        const unsigned gq = (unsigned)((d.T * 4 + 255) / 256);
+        bwd_dot_kernel<D, T><<<gq, 256, 0, st>>>(g, (const T*)a.out, d, a.Dv);
+    }
     if constexpr (sizeof(T) == 2) {
         if (d.m == kBM) {   // matrix-core passes
             uint16_t* hx = (uint16_t*)a.dx_r;
