@@ -31,11 +31,19 @@ DEV = "cuda:0"
 TOL = {"fp32": 1e-4, "bf16": 2e-2}
 
 FULL = ["b8_h8_l4k_nh4", "l64k_h8_d128_nh8", "skewed_l16k_nh8", "sweep_b64_l1k_nh8",
-        "sweep_b16_l4k_nh2", "sweep_b4_l16k_nh4", "sweep_b1_l64k_nh8", "l33280_h16_d64_nh8"]
+        "sweep_b16_l4k_nh2", "sweep_b4_l16k_nh4", "sweep_b1_l64k_nh8", "l33280_h16_d64_nh8",
+        "l1m_h1_d64_nh2", "l16k_h2_d64_nh2_fp32"]
 # 520 chunks of 64 per (head, round), 128 segments: the chunk pass takes runs
 # of 32 chunks there with a ragged last run (8 chunks)
+# 2^20 + 64 positions: past the 20-bit position field of the packed sort keys,
+# so the fused path takes the plain permutation and its inverse; and an fp32
+# case over many tiles of the vector kernels
 EXTRA = {"l33280_h16_d64_nh8": workloads.Workload("l33280_h16_d64_nh8", 1, 16, 33280, 64,
-                                                  "bf16", 1040, 8, 64, True, 1018)}
+                                                  "bf16", 1040, 8, 64, True, 1018),
+         "l1m_h1_d64_nh2": workloads.Workload("l1m_h1_d64_nh2", 1, 1, (1 << 20) + 64, 64,
+                                              "bf16", 64, 2, 64, True, 1019),
+         "l16k_h2_d64_nh2_fp32": workloads.Workload("l16k_h2_d64_nh2_fp32", 1, 2, 16384, 64,
+                                                    "fp32", 128, 2, 64, False, 1020)}
 
 
 @pytest.fixture(scope="module", autouse=True)

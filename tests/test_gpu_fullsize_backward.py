@@ -34,13 +34,17 @@ TOL = {"fp32": 1e-4, "bf16": 2e-2}
 EXTRA = {"l32000_h8_d128_nh8": workloads.Workload("l32000_h8_d128_nh8", 1, 8, 32000, 128,
                                                   "bf16", 1000, 8, 64, True, 1017),
          "l33280_h16_d64_nh8": workloads.Workload("l33280_h16_d64_nh8", 1, 16, 33280, 64,
-                                                  "bf16", 1040, 8, 64, True, 1018)}
+                                                  "bf16", 1040, 8, 64, True, 1018),
+         # past the packed keys' 20-bit position field: plain permutation
+         "l1m_h1_d64_nh2": workloads.Workload("l1m_h1_d64_nh2", 1, 1, (1 << 20) + 64, 64,
+                                              "bf16", 64, 2, 64, True, 1019)}
 
 # (workload, key_norm, per-head rotations)
 CASES = [
     ("l64k_h8_d128_nh8", False, False),
     ("l32000_h8_d128_nh8", False, False),
     ("l33280_h16_d64_nh8", False, False),
+    ("l1m_h1_d64_nh2", False, False),
     ("l64k_h8_d128_nh8", True, False),
     ("l64k_h8_d128_nh8", False, True),
     ("b8_h8_l4k_nh4", False, False),
