@@ -20,7 +20,8 @@ peak, algorithmic bytes / HBM peak) and divides by the measured forward time.
 --dense adds, per sweep line, PyTorch's scaled_dot_product_attention (a
 third-party dense comparator, flash or memory-efficient backend only) at the
 same shape with is_causal matched, and the analytic dense-attention floor
-4 B H L^2 d / bf16 MFMA peak.
+4 B H L^2 d / bf16 MFMA peak; with --ffn or --project it adds PyTorch's
+linear (hipBLASLt) at the same shapes.
 """
 from __future__ import annotations
 
@@ -155,7 +156,7 @@ def measure(lsh, torch, w, steps, warmup, key_norm=False, per_head_r=False):
             "inputs": (qk, v, R), "tensors": (qk_t, v_t)}
 
 
-def measure_projection(lsh, torch, w, steps, warmup, d_model=1024):
+def measure_projection(lsh, torch, w, steps, warmup, d_model=1024, dense=False):
     """lsh_qkv_project and lsh_attention_fwd_x at the workload's shape with
     model width d_model (synthetic bf16 token vectors and weights)."""
     import numpy as np
@@ -190,11 +191,20 @@ def measure_projection(lsh, torch, w, steps, warmup, d_model=1024):
     f_ms = timed(lambda: lsh.lsh_attention_fwd_x(x, wq, wv, R, shape, d_model, out, ws))
     flops = 2.0 * w.B * w.L * d_model * 2 * w.H * w.d
     peak = PEAK_F16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
-    return {"workload": f"{w.name}_dmodel{d_model}", "project_ms": p_ms,
+    line = {"workload": f"{w.name}_dmodel{d_model}", "project_ms": p_ms,
             "project_tflops": flops / p_ms / 1e9, "project_frac": flops / p_ms / 1e9 / peak,
             "project_bytes": (w.B * w.L * d_model + 2 * w.H * w.d * d_model
                               + 2 * w.B * w.H * w.L * w.d) * (2 if w.dtype == "bf16" else 4),
             "fwd_x_ms": f_ms, "fwd_x_tokens_per_s": w.B * w.L / (f_ms / 1e3)}
+    if dense:
+        import torch.nn.functional as F
+        wcat = torch.cat([wq, wv])
+        x2 = x.view(-1, d_model)
+        t_ms = timed(lambda: F.linear(x2, wcat))
+        line["torch_linear"] = {"ms": t_ms, "tflops": flops / t_ms / 1e9,
+                                "note": "one torch.nn.functional.linear of x by [W_qk; W_v] "
+                                        "(hipBLASLt) into [B L, 2 H d], no head split"}
+    return line
 
 
 def measure_training(lsh, torch, w, steps, warmup, key_norm=False, per_head_r=False):
@@ -247,10 +257,13 @@ def measure_training(lsh, torch, w, steps, warmup, key_norm=False, per_head_r=Fa
             "bwd_frac": flops / b_ms / 1e9 / peak}
 
 
-def measure_ffn(lsh, torch, steps, warmup, rows=65536, d_model=1024, d_ff=4096, chunk=16384):
+def measure_ffn(lsh, torch, steps, warmup, rows=65536, d_model=1024, d_ff=4096, chunk=16384,
+                dense=False):
     """The chunked feed-forward at the pages' widths (d_model 1024, d_ff 4096)
     over 64K token rows in bf16, synthetic inputs resident in HBM. Work:
-    2 products of 2 * rows * d_model * d_ff flops each."""
+    2 products of 2 * rows * d_model * d_ff flops each. ``dense``: also time
+    PyTorch's linear (hipBLASLt) + relu over the same chunks, a third-party
+    comparator."""
     dev = torch.device("cuda:0")
     g = torch.Generator(device="cpu").manual_seed(1006)
     mk = lambda *sh, sc=1.0: (torch.randn(*sh, generator=g) * sc).to(dev, torch.bfloat16)
@@ -273,11 +286,34 @@ def measure_ffn(lsh, torch, steps, warmup, rows=65536, d_model=1024, d_ff=4096, 
     ms = a.elapsed_time(b) / steps
     flops = 4.0 * rows * d_model * d_ff
     launches = 2 * ((rows + chunk - 1) // chunk)
-    return {"workload": "ffn_rows64k_dmodel1024_dff4096", "rows": rows, "d_model": d_model,
+    line = {"workload": "ffn_rows64k_dmodel1024_dff4096", "rows": rows, "d_model": d_model,
             "d_ff": d_ff, "chunk_rows": chunk, "dtype": "bf16", "ms": ms,
             "tokens_per_s": rows / (ms / 1e3), "tflops": flops / ms / 1e9,
             "peak_tflops": PEAK_F16_TFLOPS, "frac": flops / ms / 1e9 / PEAK_F16_TFLOPS,
             "launches": launches, "ms_per_launch": ms / launches}
+    if dense:
+        import torch.nn.functional as F
+
+        def ref():
+            for c in range(0, rows, chunk):
+                F.linear(torch.relu(F.linear(x[c:c + chunk], w1, b1)), w2, b2)
+        t_ms = _timed_ms(torch, ref, steps, warmup)
+        line["torch_linear"] = {"ms": t_ms, "tflops": flops / t_ms / 1e9,
+                                "note": "torch.nn.functional.linear (hipBLASLt) + relu, same chunks"}
+    return line
+
+
+def _timed_ms(torch, fn, steps, warmup):
+    for _ in range(max(1, warmup)):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
 
 
 def dense_comparator(torch, w, qk_t, v_t, steps=10):
@@ -363,7 +399,9 @@ def main() -> int:
     ap.add_argument("--sweep", action="store_true",
                     help="one JSON line per workload: the length sweep, then the others")
     ap.add_argument("--dense", action="store_true",
-                    help="with --sweep: also time torch's dense SDPA at each shape")
+                    help="with --sweep: also time torch's dense SDPA at each shape; with "
+                         "--ffn or --project: also time torch's linear (hipBLASLt) at the "
+                         "same shapes")
     ap.add_argument("--project", action="store_true",
                     help="time the input projections and the forward that starts from x")
     ap.add_argument("--train", action="store_true",
@@ -424,7 +462,7 @@ def main() -> int:
 
     if args.ffn:
         print(json.dumps(measure_ffn(lsh, torch, min(args.steps, 10), args.warmup,
-                                     chunk=args.ffn_chunk)), flush=True)
+                                     chunk=args.ffn_chunk, dense=args.dense)), flush=True)
         return 0
 
     if args.key_norm or args.per_head_r:
@@ -444,7 +482,8 @@ def main() -> int:
 
     if args.project:
         print(json.dumps(measure_projection(lsh, torch, workloads.WORKLOADS[
-            args.workload or workloads.HEADLINE], args.steps, args.warmup)), flush=True)
+            args.workload or workloads.HEADLINE], args.steps, args.warmup,
+            dense=args.dense)), flush=True)
         return 0
 
     name = args.workload or workloads.HEADLINE
