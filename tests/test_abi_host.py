@@ -230,3 +230,17 @@ def test_ffn_rejects_on_host(lib):
     # no rows: nothing to do, no pointer is needed
     assert call(None, None, None, None, None, 0, 16, 64, 4, lsh.LSH_BF16, None, None, 0,
                 None) == 0
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus 2 exits with status 2 and a JSON
+    error line before touching a device."""
+    import json
+    import pathlib
+    import subprocess
+    import sys
+    root = pathlib.Path(__file__).resolve().parent.parent
+    res = subprocess.run([sys.executable, str(root / "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120, cwd=root)
+    assert res.returncode == 2
+    assert "error" in json.loads(res.stdout.strip().splitlines()[-1])
