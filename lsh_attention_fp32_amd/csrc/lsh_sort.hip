@@ -72,6 +72,8 @@ __global__ __launch_bounds__(256) void sort_count_kernel(const int32_t* __restri
         counts[(seg * ntiles + tile) * dm.nb + b] = hist[b];
 }
 
+constexpr int kScatterXcds = 8;   // L2 domains of the chip
+
 // PACKED: perm[slot] = (bucket << kPackPosBits) | position and no inverse.
 template <bool PACKED>
 __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __restrict__ buckets,
@@ -82,8 +84,13 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __rest
     extern __shared__ int32_t sh[];   // [kSortWaves][nb] counts, then running slots; [nb] run starts
     __shared__ int32_t wsum[4];
     constexpr int SUB = kSortTile / kSortWaves;
-    const int tile = blockIdx.x;
-    const int64_t seg = blockIdx.y;
+    // Workgroups are dealt round-robin over the L2 domains (id % kScatterXcds):
+    // every tile of a segment gets the same residue, so one L2 collects the
+    // segment's scattered 4-byte writes and hands whole lines to memory.
+    const int64_t id = blockIdx.x, k = id / kScatterXcds;
+    const int64_t seg = (k / ntiles) * kScatterXcds + id % kScatterXcds;
+    const int tile = (int)(k % ntiles);
+    if (seg >= dm.segs) return;   // the grid is rounded up to whole domain groups
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nb = dm.nb;
     int32_t* start = sh + kSortWaves * nb;
@@ -198,12 +205,14 @@ hipError_t launch_sort(const int32_t* buckets, const Dims& d, int32_t* perm, int
     sort_count_kernel<<<grid, 256, sizeof(int32_t) * d.nb, st>>>(buckets, d, ntiles, counts);
     if ((e = mark(st, ev, nev, names, "sort_count")) != hipSuccess) return e;
     const size_t lds = sizeof(int32_t) * (kSortWaves + 1) * d.nb;
+    const int64_t sgroups = (d.segs + kScatterXcds - 1) / kScatterXcds;
+    const unsigned sgrid = (unsigned)(sgroups * kScatterXcds * ntiles);
     if (packed)
-        sort_scatter_kernel<true><<<grid, 256, lds, st>>>(buckets, counts, d, ntiles, nbits, perm,
-                                                          nullptr);
+        sort_scatter_kernel<true><<<sgrid, 256, lds, st>>>(buckets, counts, d, ntiles, nbits,
+                                                           perm, nullptr);
     else
-        sort_scatter_kernel<false><<<grid, 256, lds, st>>>(buckets, counts, d, ntiles, nbits,
-                                                           perm, inv);
+        sort_scatter_kernel<false><<<sgrid, 256, lds, st>>>(buckets, counts, d, ntiles, nbits,
+                                                            perm, inv);
     return mark(st, ev, nev, names, "sort_scatter");
 }
 
