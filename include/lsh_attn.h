@@ -19,8 +19,8 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Every pointer argument is caller-owned DEVICE memory (hipMalloc'd or a
- *    torch CUDA tensor), except `shape`, which is a host struct, and the host
- *    outputs of lsh_workspace_size / lsh_attention_fwd_timed. The library
+ *    torch CUDA tensor), except `shape` and `stage`, which are host values,
+ *    and the host outputs of lsh_attention_fwd_timed. The library
  *    never allocates or frees device memory and keeps no pointer after a call.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Work is enqueued asynchronously on it; inputs must stay valid and
@@ -78,15 +78,16 @@ enum {
 
 enum {
     LSH_OK = 0,
-    LSH_ERR_ARG = -1,         /* an argument breaks the method's constraints    */
+    LSH_ERR_ARG = -1,         /* an argument breaks a constraint listed below   */
     LSH_ERR_WORKSPACE = -2,   /* workspace pointer NULL or smaller than needed  */
-    LSH_ERR_HIP = -3,         /* a HIP launch or runtime call failed            */
-    LSH_ERR_UNSUPPORTED = -4  /* valid for the method but not built (e.g. d)    */
+    LSH_ERR_HIP = -3          /* a HIP launch or runtime call failed            */
 };
 
-/* Problem description (host struct, read during the call only).
- *   B, H, L, d   batch, heads, sequence length, head dimension. d must be 64
- *                or 128 (others: LSH_ERR_UNSUPPORTED).
+/* Problem description (host struct, read during the call only). Every
+ * constraint below is checked on the host; a shape that breaks one is
+ * rejected with LSH_ERR_ARG.
+ *   B, H, L, d   batch, heads, sequence length, head dimension; B, H, L >= 0
+ *                and d in {64, 128} (the head sizes the kernels are built for).
  *   n_buckets    even, 2 <= n_buckets <= 4096.
  *   n_hashes     hash rounds, 1 <= n_hashes <= 4096.
  *   chunk_len    m >= 1 with L % m == 0 (the pages cut the sorted sequence
@@ -95,7 +96,9 @@ enum {
  *   dtype        LSH_F32 or LSH_BF16 for qk, v and out.
  *   flags        0, or LSH_KEY_NORM and/or LSH_PER_HEAD_R (other bits:
  *                LSH_ERR_ARG).
- * Also required: B*H*n_hashes*L < 2^31. */
+ * Also required: B*H*n_hashes*L < 2^31 (every per-slot array is indexed
+ * with 32-bit integers; this replaces a bound on a packed 32-bit
+ * (round, bucket, position) sort key, which the sort does not use). */
 typedef struct lsh_shape {
     int32_t B, H, L, d;
     int32_t n_buckets, n_hashes, chunk_len, causal;
@@ -104,11 +107,13 @@ typedef struct lsh_shape {
 } lsh_shape_t;
 
 /* Bytes of workspace needed by `stage` ("hash", "sort", "fwd", "fwd_x",
- * "state" or "bwd") for `shape`, written to *bytes (host). "state" is the
- * size of the buffer lsh_attention_fwd_train fills for lsh_attention_bwd.
- * LSH_KEY_NORM adds 4 bytes per token (B*H*L) to "fwd", "fwd_x" and "bwd".
- * Returns LSH_ERR_ARG for an unknown stage or an invalid shape. */
-int lsh_workspace_size(const char *stage, const lsh_shape_t *shape, size_t *bytes);
+ * "state" or "bwd") for `shape`. "state" is the size of the buffer
+ * lsh_attention_fwd_train fills for lsh_attention_bwd. LSH_KEY_NORM adds
+ * 4 bytes per token (B*H*L) to "fwd", "fwd_x" and "bwd".
+ * Errors: an unknown or NULL stage, or an invalid shape, returns 0 and sets
+ * lsh_last_error(); after a successful call lsh_last_error() is "" (a valid
+ * empty problem may need 0 bytes, so test the message, not the size). */
+size_t lsh_workspace_size(const char *stage, const lsh_shape_t *shape);
 
 /* Step 1 -- angular LSH over n_hashes rounds (glossary "Atenção LSH";
  * walkthrough "1 LSH Attention" for one hash function per round).
@@ -239,14 +244,15 @@ int lsh_attention_bwd(const void *qk, const void *v, const void *out, const void
  *   b1       [d_ff] dtype or NULL
  *   w2       [d_model, d_ff] dtype             b2 [d_model] dtype or NULL
  *   ws       lsh_ffn_workspace_size bytes: one chunk's intermediate,
- *            min(chunk_rows, rows) * d_ff elements of dtype, caller-owned
+ *            min(chunk_rows, rows) * d_ff elements of dtype, caller-owned;
+ *            lsh_ffn_workspace_size returns 0 and sets lsh_last_error() for
+ *            invalid sizes (rows = 0 validly needs 0 bytes)
  * The result does not depend on chunk_rows (rows are independent; bit-equal
  * across chunk sizes). bf16: matrix cores, fp32 accumulation, the
  * intermediate rounded to bf16 after bias and ReLU; fp32: fp32 throughout.
  * Errors: LSH_ERR_ARG for sizes, dtype, NULL or misaligned tensors;
  * LSH_ERR_WORKSPACE for a missing or small workspace. */
-int lsh_ffn_workspace_size(int64_t rows, int32_t d_ff, int32_t chunk_rows, int32_t dtype,
-                           size_t *bytes);
+size_t lsh_ffn_workspace_size(int64_t rows, int32_t d_ff, int32_t chunk_rows, int32_t dtype);
 int lsh_ffn_chunked(const void *x, const void *w1, const void *b1, const void *w2,
                     const void *b2, int64_t rows, int32_t d_model, int32_t d_ff,
                     int32_t chunk_rows, int32_t dtype, void *out, void *ws, size_t ws_bytes,

@@ -11,7 +11,7 @@ LSH_BF16 = 1
 LSH_KEY_NORM = 1   # lsh_shape_t.flags bit: keys as unit vectors in the scores
 LSH_PER_HEAD_R = 2  # lsh_shape_t.flags bit: R is [H, n_hashes, d, n_buckets/2]
 _DTYPES = {torch.float32: LSH_F32, torch.bfloat16: LSH_BF16}
-_ERRORS = {-1: "LSH_ERR_ARG", -2: "LSH_ERR_WORKSPACE", -3: "LSH_ERR_HIP", -4: "LSH_ERR_UNSUPPORTED"}
+_ERRORS = {-1: "LSH_ERR_ARG", -2: "LSH_ERR_WORKSPACE", -3: "LSH_ERR_HIP"}
 
 _PKG = pathlib.Path(__file__).resolve().parent
 _LIB_PATH = _PKG / "liblsh_attn.so"
@@ -50,7 +50,8 @@ def load_library():
                            "(python -m lsh_attention_fp32_amd.build or __graft_entry__.build())")
     lib = ctypes.CDLL(str(_LIB_PATH))
     vp, sz, i32, sp = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.POINTER(Shape)
-    lib.lsh_workspace_size.argtypes = [ctypes.c_char_p, sp, ctypes.POINTER(sz)]
+    lib.lsh_workspace_size.argtypes = [ctypes.c_char_p, sp]
+    lib.lsh_workspace_size.restype = sz
     lib.lsh_hash.argtypes = [vp, vp, sp, vp, vp, sz, vp]
     lib.lsh_sort.argtypes = [vp, sp, vp, vp, vp, sz, vp]
     lib.lsh_chunk_attend.argtypes = [vp, vp, vp, vp, sp, vp, vp, vp]
@@ -65,9 +66,10 @@ def load_library():
     lib.lsh_attention_fwd_train.argtypes = [vp, vp, vp, sp, vp, vp, sz, vp, sz, vp]
     lib.lsh_attention_bwd.argtypes = [vp, vp, vp, vp, vp, sz, sp, vp, vp, vp, sz, vp]
     i64 = ctypes.c_int64
-    lib.lsh_ffn_workspace_size.argtypes = [i64, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.lsh_ffn_workspace_size.argtypes = [i64, i32, i32, i32]
+    lib.lsh_ffn_workspace_size.restype = sz
     lib.lsh_ffn_chunked.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp, sz, vp]
-    for name in ("lsh_ffn_workspace_size", "lsh_ffn_chunked", "lsh_workspace_size", "lsh_hash", "lsh_sort", "lsh_chunk_attend",
+    for name in ("lsh_ffn_chunked", "lsh_hash", "lsh_sort", "lsh_chunk_attend",
                  "lsh_unsort_combine", "lsh_attention_fwd", "lsh_attention_fwd_timed",
                  "lsh_qkv_project", "lsh_attention_fwd_x", "lsh_attention_fwd_train",
                  "lsh_attention_bwd"):
@@ -127,74 +129,173 @@ def rounds_of(R) -> tuple[int, bool]:
     return R.shape[0], False
 
 
+def check_rotations(R, qk, n_buckets: int) -> tuple[int, bool]:
+    """Validates R against qk [B, H, L, d] and n_buckets: a contiguous float32
+    tensor on qk's device, [n_hashes, d, nb/2] or [H, n_hashes, d, nb/2].
+    Returns (n_hashes, per-head)."""
+    if not isinstance(R, torch.Tensor):
+        raise TypeError("R must be a torch tensor")
+    nh, per_head = rounds_of(R)
+    B, H, L, d = qk.shape
+    want = ((H,) if per_head else ()) + (nh, d, n_buckets // 2)
+    if tuple(R.shape) != want or nh < 1:
+        raise ValueError(f"R must be [{'H, ' if per_head else ''}n_hashes, d, n_buckets/2] = "
+                         f"{want} for qk {tuple(qk.shape)} and n_buckets {n_buckets}, "
+                         f"got {tuple(R.shape)}")
+    if R.dtype != torch.float32:
+        raise ValueError(f"R must be float32, got {R.dtype}")
+    if R.device != qk.device or not R.is_contiguous():
+        raise ValueError("R must be contiguous and on qk's device")
+    return nh, per_head
+
+
+def check_like(t, ref, what: str) -> None:
+    """``t`` must match ``ref`` in shape, dtype and device, and be contiguous."""
+    if (not isinstance(t, torch.Tensor) or t.shape != ref.shape or t.dtype != ref.dtype
+            or t.device != ref.device or not t.is_contiguous()):
+        raise ValueError(f"{what} must be a contiguous {ref.dtype} tensor of shape "
+                         f"{tuple(ref.shape)} on {ref.device}")
+
+
 # ---------------------------------------------------------------- C-named calls
 
+def _size_query(n: int, fn: str) -> int:
+    """A size_t result of the C ABI: 0 with a message means an error (always
+    LSH_ERR_ARG for the size queries)."""
+    msg = lsh_last_error()
+    if msg:
+        raise LshError(-1, fn, msg)
+    return int(n)
+
+
 def lsh_workspace_size(stage: str, shape: Shape) -> int:
-    n = ctypes.c_size_t(0)
-    _check(load_library().lsh_workspace_size(stage.encode(), ctypes.byref(shape), ctypes.byref(n)),
-           "lsh_workspace_size")
-    return n.value
+    return _size_query(load_library().lsh_workspace_size(stage.encode(), ctypes.byref(shape)),
+                       "lsh_workspace_size")
+
+
+_TORCH_DTYPE = {LSH_F32: torch.float32, LSH_BF16: torch.bfloat16}
+
+
+def _need(fn: str, what: str, t, dtype, numel: int, optional: bool = False) -> None:
+    """Host check before a call: ``t`` holds at least ``numel`` elements of
+    ``dtype`` (the library takes plain pointers, so it cannot see a short or
+    mistyped buffer; this keeps every kernel inside its buffers)."""
+    if t is None:
+        if optional or numel == 0:
+            return
+        raise ValueError(f"{fn}: {what} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{fn}: {what} must be a torch tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{fn}: {what} must be {dtype}, got {t.dtype}")
+    if t.numel() < numel:
+        raise ValueError(f"{fn}: {what} holds {t.numel()} elements, needs {numel}")
+
+
+def _io(shape: Shape):
+    return _TORCH_DTYPE.get(shape.dtype, torch.float32)
+
+
+def _sizes(shape: Shape):
+    """(token rows B*H*L*d, per-slot entries B*H*nh*L, R elements) of a shape."""
+    rows = shape.B * shape.H * shape.L * shape.d
+    slots = shape.B * shape.H * shape.n_hashes * shape.L
+    heads = shape.H if shape.flags & LSH_PER_HEAD_R else 1
+    r = heads * shape.n_hashes * shape.d * (shape.n_buckets // 2)
+    return rows, slots, r
+
+
+def _need_qkvr(fn: str, shape: Shape, qk=None, v=None, R=None, out=None, with_r=True,
+               with_v=True, with_out=True) -> None:
+    rows, _, r = _sizes(shape)
+    io = _io(shape)
+    _need(fn, "qk", qk, io, rows)
+    if with_v:
+        _need(fn, "v", v, io, rows)
+    if with_r:
+        _need(fn, "R", R, torch.float32, r)
+    if with_out:
+        _need(fn, "out", out, io, rows)
 
 
 def lsh_hash(qk, R, shape: Shape, buckets, ws, stream=None) -> None:
+    _need_qkvr("lsh_hash", shape, qk, R=R, with_v=False, with_out=False)
+    _need("lsh_hash", "buckets", buckets, torch.int32, _sizes(shape)[1])
     _check(load_library().lsh_hash(_ptr(qk), _ptr(R), ctypes.byref(shape), _ptr(buckets), _ptr(ws),
-                                   ws.numel() * ws.element_size() if ws is not None else 0,
-                                   _stream(stream)), "lsh_hash")
+                                   _nbytes(ws), _stream(stream)), "lsh_hash")
 
 
 def lsh_sort(buckets, shape: Shape, perm, inv, ws, stream=None) -> None:
+    n = _sizes(shape)[1]
+    for what, t in (("buckets", buckets), ("perm", perm), ("inv", inv)):
+        _need("lsh_sort", what, t, torch.int32, n)
     _check(load_library().lsh_sort(_ptr(buckets), ctypes.byref(shape), _ptr(perm), _ptr(inv),
-                                   _ptr(ws),
-                                   ws.numel() * ws.element_size() if ws is not None else 0,
-                                   _stream(stream)), "lsh_sort")
+                                   _ptr(ws), _nbytes(ws), _stream(stream)), "lsh_sort")
 
 
 def lsh_chunk_attend(qk, v, buckets, perm, shape: Shape, o_sorted, lse_sorted, stream=None) -> None:
+    fn = "lsh_chunk_attend"
+    _need_qkvr(fn, shape, qk, v, with_r=False, with_out=False)
+    n = _sizes(shape)[1]
+    _need(fn, "buckets", buckets, torch.int32, n)
+    _need(fn, "perm", perm, torch.int32, n)
+    _need(fn, "o_sorted", o_sorted, torch.float32, n * shape.d)
+    _need(fn, "lse_sorted", lse_sorted, torch.float32, n)
     _check(load_library().lsh_chunk_attend(_ptr(qk), _ptr(v), _ptr(buckets), _ptr(perm),
                                            ctypes.byref(shape), _ptr(o_sorted), _ptr(lse_sorted),
-                                           _stream(stream)), "lsh_chunk_attend")
+                                           _stream(stream)), fn)
 
 
 def lsh_unsort_combine(o_sorted, lse_sorted, inv, shape: Shape, out, stream=None) -> None:
+    fn = "lsh_unsort_combine"
+    n = _sizes(shape)[1]
+    _need(fn, "o_sorted", o_sorted, torch.float32, n * shape.d)
+    _need(fn, "lse_sorted", lse_sorted, torch.float32, n)
+    _need(fn, "inv", inv, torch.int32, n)
+    _need(fn, "out", out, _io(shape), _sizes(shape)[0])
     _check(load_library().lsh_unsort_combine(_ptr(o_sorted), _ptr(lse_sorted), _ptr(inv),
-                                             ctypes.byref(shape), _ptr(out), _stream(stream)),
-           "lsh_unsort_combine")
+                                             ctypes.byref(shape), _ptr(out), _stream(stream)), fn)
 
 
 def lsh_attention_fwd(qk, v, R, shape: Shape, out, ws, stream=None) -> None:
+    _need_qkvr("lsh_attention_fwd", shape, qk, v, R, out)
     _check(load_library().lsh_attention_fwd(_ptr(qk), _ptr(v), _ptr(R), ctypes.byref(shape),
-                                            _ptr(out), _ptr(ws),
-                                            ws.numel() * ws.element_size() if ws is not None else 0,
-                                            _stream(stream)), "lsh_attention_fwd")
+                                            _ptr(out), _ptr(ws), _nbytes(ws), _stream(stream)),
+           "lsh_attention_fwd")
 
 
 def lsh_attention_fwd_timed(qk, v, R, shape: Shape, out, ws, stream=None, max_kernels: int = 16):
     """Runs the forward and returns [(kernel name, milliseconds), ...] (waits for the GPU)."""
+    _need_qkvr("lsh_attention_fwd_timed", shape, qk, v, R, out)
     ms = (ctypes.c_float * max_kernels)()
     names = (ctypes.c_char_p * max_kernels)()
     n = ctypes.c_int32(0)
     _check(load_library().lsh_attention_fwd_timed(
-        _ptr(qk), _ptr(v), _ptr(R), ctypes.byref(shape), _ptr(out), _ptr(ws),
-        ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream), ms, names,
-        max_kernels, ctypes.byref(n)), "lsh_attention_fwd_timed")
+        _ptr(qk), _ptr(v), _ptr(R), ctypes.byref(shape), _ptr(out), _ptr(ws), _nbytes(ws),
+        _stream(stream), ms, names, max_kernels, ctypes.byref(n)), "lsh_attention_fwd_timed")
     return [(names[k].decode(), float(ms[k])) for k in range(n.value)]
 
 
 def lsh_ffn_workspace_size(rows: int, d_ff: int, chunk_rows: int, dtype: int) -> int:
-    n = ctypes.c_size_t(0)
-    _check(load_library().lsh_ffn_workspace_size(int(rows), int(d_ff), int(chunk_rows),
-                                                 int(dtype), ctypes.byref(n)),
-           "lsh_ffn_workspace_size")
-    return n.value
+    return _size_query(load_library().lsh_ffn_workspace_size(int(rows), int(d_ff),
+                                                             int(chunk_rows), int(dtype)),
+                       "lsh_ffn_workspace_size")
 
 
 def lsh_ffn_chunked(x, w1, b1, w2, b2, rows: int, d_model: int, d_ff: int, chunk_rows: int,
                     dtype: int, out, ws, stream=None) -> None:
+    fn = "lsh_ffn_chunked"
+    io = _TORCH_DTYPE.get(dtype, torch.float32)
+    _need(fn, "x", x, io, rows * d_model)
+    _need(fn, "w1", w1, io, d_ff * d_model)
+    _need(fn, "b1", b1, io, d_ff, optional=True)
+    _need(fn, "w2", w2, io, d_model * d_ff)
+    _need(fn, "b2", b2, io, d_model, optional=True)
+    _need(fn, "out", out, io, rows * d_model)
     _check(load_library().lsh_ffn_chunked(_ptr(x), _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2),
                                           int(rows), int(d_model), int(d_ff), int(chunk_rows),
                                           int(dtype), _ptr(out), _ptr(ws), _nbytes(ws),
-                                          _stream(stream)),
-           "lsh_ffn_chunked")
+                                          _stream(stream)), fn)
 
 
 def ffn(x, w1, b1, w2, b2, chunk_rows: int, ws=None, out=None, stream=None):
@@ -215,6 +316,8 @@ def ffn(x, w1, b1, w2, b2, chunk_rows: int, ws=None, out=None, stream=None):
             raise ValueError("weights and biases must be in x's dtype")
     rows = x.numel() // dm if dm else 0
     dtype = _DTYPES[x.dtype]
+    if out is not None and (out.shape != x.shape or out.dtype != x.dtype):
+        raise ValueError("out must match x in shape and dtype")
     out = torch.empty_like(x) if out is None else out
     if ws is None:
         ws = torch.empty(max(1, lsh_ffn_workspace_size(rows, dff, chunk_rows, dtype)),
@@ -224,17 +327,29 @@ def ffn(x, w1, b1, w2, b2, chunk_rows: int, ws=None, out=None, stream=None):
 
 
 def lsh_qkv_project(x, w_qk, w_v, shape: Shape, d_model: int, qk, v, stream=None) -> None:
+    fn = "lsh_qkv_project"
+    io = _io(shape)
+    _need(fn, "x", x, io, shape.B * shape.L * d_model)
+    _need(fn, "w_qk", w_qk, io, shape.H * shape.d * d_model)
+    _need(fn, "w_v", w_v, io, shape.H * shape.d * d_model)
+    _need_qkvr(fn, shape, qk, v, with_r=False, with_out=False)
     _check(load_library().lsh_qkv_project(_ptr(x), _ptr(w_qk), _ptr(w_v), ctypes.byref(shape),
-                                          int(d_model), _ptr(qk), _ptr(v), _stream(stream)),
-           "lsh_qkv_project")
+                                          int(d_model), _ptr(qk), _ptr(v), _stream(stream)), fn)
 
 
 def lsh_attention_fwd_x(x, w_qk, w_v, R, shape: Shape, d_model: int, out, ws,
                         stream=None) -> None:
+    fn = "lsh_attention_fwd_x"
+    io = _io(shape)
+    _need(fn, "x", x, io, shape.B * shape.L * d_model)
+    _need(fn, "w_qk", w_qk, io, shape.H * shape.d * d_model)
+    _need(fn, "w_v", w_v, io, shape.H * shape.d * d_model)
+    rows, _, r = _sizes(shape)
+    _need(fn, "R", R, torch.float32, r)
+    _need(fn, "out", out, io, rows)
     _check(load_library().lsh_attention_fwd_x(
         _ptr(x), _ptr(w_qk), _ptr(w_v), _ptr(R), ctypes.byref(shape), int(d_model), _ptr(out),
-        _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)),
-        "lsh_attention_fwd_x")
+        _ptr(ws), _nbytes(ws), _stream(stream)), fn)
 
 
 def _nbytes(t):
@@ -242,16 +357,21 @@ def _nbytes(t):
 
 
 def lsh_attention_fwd_train(qk, v, R, shape: Shape, out, state, ws, stream=None) -> None:
+    _need_qkvr("lsh_attention_fwd_train", shape, qk, v, R, out)
     _check(load_library().lsh_attention_fwd_train(
         _ptr(qk), _ptr(v), _ptr(R), ctypes.byref(shape), _ptr(out), _ptr(state), _nbytes(state),
         _ptr(ws), _nbytes(ws), _stream(stream)), "lsh_attention_fwd_train")
 
 
 def lsh_attention_bwd(qk, v, out, dout, state, shape: Shape, dqk, dv, ws, stream=None) -> None:
+    fn = "lsh_attention_bwd"
+    _need_qkvr(fn, shape, qk, v, out=out, with_r=False)
+    rows = _sizes(shape)[0]
+    for what, t in (("dout", dout), ("dqk", dqk), ("dv", dv)):
+        _need(fn, what, t, _io(shape), rows)
     _check(load_library().lsh_attention_bwd(
         _ptr(qk), _ptr(v), _ptr(out), _ptr(dout), _ptr(state), _nbytes(state),
-        ctypes.byref(shape), _ptr(dqk), _ptr(dv), _ptr(ws), _nbytes(ws), _stream(stream)),
-        "lsh_attention_bwd")
+        ctypes.byref(shape), _ptr(dqk), _ptr(dv), _ptr(ws), _nbytes(ws), _stream(stream)), fn)
 
 
 # ---------------------------------------------------------------- allocating helpers
@@ -266,7 +386,7 @@ def _rounds_shape(shape: Shape):
 
 def hash(qk, R, n_buckets: int, ws=None, stream=None):
     """Returns (buckets [B,H,n_hashes,L] int32, number of token-rounds re-decided in fp64)."""
-    nh, per_head = rounds_of(R)
+    nh, per_head = check_rotations(R, qk, n_buckets)
     shape = shape_of(qk, n_buckets, nh, 1, False, per_head_r=per_head)
     shape.chunk_len = max(1, shape.L)  # any divisor of L: the hash does not use it
     buckets = torch.empty(_rounds_shape(shape), dtype=torch.int32, device=qk.device)
@@ -309,10 +429,11 @@ def unsort_combine(o_sorted, lse_sorted, inv, dtype=torch.bfloat16, stream=None)
 def attention_fwd(qk, v, R, n_buckets: int, chunk_len: int, causal: bool, ws=None, out=None,
                   stream=None, key_norm: bool = False):
     """Whole forward; returns out [B,H,L,d] in qk's dtype."""
-    nh, per_head = rounds_of(R)
+    nh, per_head = check_rotations(R, qk, n_buckets)
     shape = shape_of(qk, n_buckets, nh, chunk_len, causal, key_norm, per_head)
-    if v.shape != qk.shape or v.dtype != qk.dtype:
-        raise ValueError("v must match qk in shape and dtype")
+    check_like(v, qk, "v")
+    if out is not None:
+        check_like(out, qk, "out")
     out = torch.empty_like(qk) if out is None else out
     ws = _workspace("fwd", shape, qk.device) if ws is None else ws
     lsh_attention_fwd(qk, v, R, shape, out, ws, stream)
@@ -351,8 +472,11 @@ def attention_fwd_x(x, w_qk, w_v, R, n_heads: int, n_buckets: int, chunk_len: in
     """Projections, then the whole forward; returns out [B, H, L, d] in x's dtype."""
     nh, per_head = rounds_of(R)
     shape = _x_shape(x, w_qk, w_v, n_heads, n_buckets, nh, chunk_len, causal, key_norm, per_head)
-    out = torch.empty((shape.B, shape.H, shape.L, shape.d), dtype=x.dtype,
-                      device=x.device) if out is None else out
+    ref = torch.empty((shape.B, shape.H, shape.L, shape.d), dtype=x.dtype, device=x.device)
+    check_rotations(R, ref, n_buckets)
+    if out is not None:
+        check_like(out, ref, "out")
+    out = ref if out is None else out
     ws = _workspace("fwd_x", shape, x.device) if ws is None else ws
     lsh_attention_fwd_x(x, w_qk, w_v, R, shape, x.shape[2], out, ws, stream)
     return out
@@ -361,10 +485,9 @@ def attention_fwd_x(x, w_qk, w_v, R, n_heads: int, n_buckets: int, chunk_len: in
 def attention_fwd_train(qk, v, R, n_buckets: int, chunk_len: int, causal: bool, stream=None,
                         key_norm: bool = False):
     """Training forward; returns (out [B,H,L,d], state) for attention_bwd."""
-    nh, per_head = rounds_of(R)
+    nh, per_head = check_rotations(R, qk, n_buckets)
     shape = shape_of(qk, n_buckets, nh, chunk_len, causal, key_norm, per_head)
-    if v.shape != qk.shape or v.dtype != qk.dtype:
-        raise ValueError("v must match qk in shape and dtype")
+    check_like(v, qk, "v")
     out = torch.empty_like(qk)
     state = _workspace("state", shape, qk.device)
     ws = _workspace("fwd", shape, qk.device)

@@ -36,7 +36,7 @@ int validate(const lsh_shape_t* s) {
     if (s->n_buckets < 2 || (s->n_buckets % 2) != 0)
         return fail(LSH_ERR_ARG, "n_buckets must be even and >= 2 (got %d)", s->n_buckets);
     if (s->n_buckets > kMaxBuckets)
-        return fail(LSH_ERR_UNSUPPORTED, "n_buckets above %d is not built (got %d)", kMaxBuckets,
+        return fail(LSH_ERR_ARG, "n_buckets must be at most %d (got %d)", kMaxBuckets,
                     s->n_buckets);
     if (s->n_hashes < 1 || s->n_hashes > kMaxHashes)
         return fail(LSH_ERR_ARG, "n_hashes must be in [1, %d] (got %d)", kMaxHashes, s->n_hashes);
@@ -53,7 +53,7 @@ int validate(const lsh_shape_t* s) {
     if ((int64_t)s->B * s->H * s->n_hashes * s->L >= ((int64_t)1 << 31))
         return fail(LSH_ERR_ARG, "B*H*n_hashes*L must stay below 2^31");
     if (s->d != 64 && s->d != 128)
-        return fail(LSH_ERR_UNSUPPORTED, "head size d=%d is not built (64 or 128)", s->d);
+        return fail(LSH_ERR_ARG, "head size d must be 64 or 128 (got %d)", s->d);
     return LSH_OK;
 }
 
@@ -199,6 +199,18 @@ size_t projected_bytes(const Dims& d) {
     return align_up((size_t)d.T * d.d * (d.dtype == LSH_BF16 ? 2 : 4), 256);
 }
 
+// Bytes of one chunk's intermediate of the chunked feed-forward.
+int ffn_workspace(int64_t rows, int32_t d_ff, int32_t chunk_rows, int32_t dtype, size_t* bytes) {
+    if (rows < 0 || d_ff < 8 || d_ff % 8 != 0 || chunk_rows < 1 ||
+        (dtype != LSH_F32 && dtype != LSH_BF16))
+        return fail(LSH_ERR_ARG,
+                    "lsh_ffn: rows >= 0, d_ff a positive multiple of 8, chunk_rows >= 1 and a "
+                    "known dtype required");
+    const int64_t n = rows < chunk_rows ? rows : chunk_rows;
+    *bytes = (size_t)n * d_ff * (dtype == LSH_BF16 ? 2 : 4);
+    return LSH_OK;
+}
+
 int check_dmodel(const char* fn, int32_t d_model) {
     if (d_model < 8 || d_model % 8 != 0)
         return fail(LSH_ERR_ARG, "%s: d_model must be a positive multiple of 8 (got %d)", fn,
@@ -212,22 +224,19 @@ extern "C" {
 
 const char* lsh_last_error(void) { return g_err; }
 
-int lsh_workspace_size(const char* stage, const lsh_shape_t* shape, size_t* bytes) {
+size_t lsh_workspace_size(const char* stage, const lsh_shape_t* shape) {
     g_err[0] = 0;
-    if (!stage || !bytes) return fail(LSH_ERR_ARG, "stage and bytes must not be NULL");
-    int rc = validate(shape);
-    if (rc) return rc;
+    if (!stage) return fail(LSH_ERR_ARG, "lsh_workspace_size: stage must not be NULL"), 0;
+    if (validate(shape)) return 0;
     const Dims d = make_dims(*shape);
-    if (!strcmp(stage, "hash")) *bytes = hash_workspace_bytes(d);
-    else if (!strcmp(stage, "sort")) *bytes = sort_workspace_bytes(d);
-    else if (!strcmp(stage, "fwd")) *bytes = fwd_layout(d).total;
-    else if (!strcmp(stage, "fwd_x")) *bytes = 2 * projected_bytes(d) + fwd_layout(d).total;
-    else if (!strcmp(stage, "state")) *bytes = state_layout(d).total;
-    else if (!strcmp(stage, "bwd")) *bytes = bwd_layout(d).total;
-    else
-        return fail(LSH_ERR_ARG, "unknown stage '%s' (hash, sort, fwd, fwd_x, state or bwd)",
-                    stage);
-    return LSH_OK;
+    if (!strcmp(stage, "hash")) return hash_workspace_bytes(d);
+    if (!strcmp(stage, "sort")) return sort_workspace_bytes(d);
+    if (!strcmp(stage, "fwd")) return fwd_layout(d).total;
+    if (!strcmp(stage, "fwd_x")) return 2 * projected_bytes(d) + fwd_layout(d).total;
+    if (!strcmp(stage, "state")) return state_layout(d).total;
+    if (!strcmp(stage, "bwd")) return bwd_layout(d).total;
+    fail(LSH_ERR_ARG, "unknown stage '%s' (hash, sort, fwd, fwd_x, state or bwd)", stage);
+    return 0;
 }
 
 int lsh_hash(const void* qk, const float* R, const lsh_shape_t* shape, int32_t* buckets,
@@ -329,18 +338,10 @@ int lsh_qkv_project(const void* x, const void* w_qk, const void* w_v, const lsh_
     return e == hipSuccess ? LSH_OK : hip_fail(e, "lsh_qkv_project");
 }
 
-int lsh_ffn_workspace_size(int64_t rows, int32_t d_ff, int32_t chunk_rows, int32_t dtype,
-                           size_t* bytes) {
+size_t lsh_ffn_workspace_size(int64_t rows, int32_t d_ff, int32_t chunk_rows, int32_t dtype) {
     g_err[0] = 0;
-    if (!bytes) return fail(LSH_ERR_ARG, "lsh_ffn_workspace_size: bytes must not be NULL");
-    if (rows < 0 || d_ff < 8 || d_ff % 8 != 0 || chunk_rows < 1 ||
-        (dtype != LSH_F32 && dtype != LSH_BF16))
-        return fail(LSH_ERR_ARG,
-                    "lsh_ffn_workspace_size: rows >= 0, d_ff a positive multiple of 8, "
-                    "chunk_rows >= 1 and a known dtype required");
-    const int64_t n = rows < chunk_rows ? rows : chunk_rows;
-    *bytes = (size_t)n * d_ff * (dtype == LSH_BF16 ? 2 : 4);
-    return LSH_OK;
+    size_t bytes = 0;
+    return ffn_workspace(rows, d_ff, chunk_rows, dtype, &bytes) ? 0 : bytes;
 }
 
 int lsh_ffn_chunked(const void* x, const void* w1, const void* b1, const void* w2,
@@ -352,7 +353,7 @@ int lsh_ffn_chunked(const void* x, const void* w1, const void* b1, const void* w
         return fail(LSH_ERR_ARG, "lsh_ffn_chunked: d_model must be a positive multiple of 8 "
                                  "(got %d)", (int)d_model);
     size_t need = 0;
-    int rc = lsh_ffn_workspace_size(rows, d_ff, chunk_rows, dtype, &need);
+    int rc = ffn_workspace(rows, d_ff, chunk_rows, dtype, &need);
     if (rc) return rc;
     if (rows == 0) return LSH_OK;
     if (!x || !w1 || !w2 || !out)

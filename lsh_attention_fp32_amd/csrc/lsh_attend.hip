@@ -183,10 +183,9 @@ constexpr int kWin = 2 * kM;      // keys in a window
 inline int attend_run_len(int64_t segs, int nchunks) {
     return segs * ((nchunks + 31) / 32) >= 8 * 256 ? 32 : 16;
 }
-#ifndef LSH_ATTEND_DEPTH
-#define LSH_ATTEND_DEPTH 1
-#endif
-constexpr int kDepth = LSH_ATTEND_DEPTH;   // chunks whose gathers are in flight (1..3)
+// Chunks whose gathers are in flight behind the one computing: one measures
+// as fast as two or three at 64K tokens and holds the fewest registers.
+constexpr int kDepth = 1;
 static_assert(kDepth >= 1 && kDepth <= 3, "key buffers hold four chunks");
 
 template <int D>

@@ -35,12 +35,10 @@ struct Lds {
 };
 __device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
-// Waves per workgroup: 8 (a 4 x 2 grid of waves, 64 outputs x 64 tokens
-// each) or 4 (2 x 2, 128 x 64 each).
-#ifndef LSH_GEMM_WAVES
-#define LSH_GEMM_WAVES 8
-#endif
-constexpr int kGW = LSH_GEMM_WAVES;
+// Waves per workgroup: 8, a 4 x 2 grid of waves with 64 outputs x 64 tokens
+// each (four waves per SIMD hide more of the fragment-read stalls than four
+// waves of 128 x 64).
+constexpr int kGW = 8;
 constexpr int kGT = 64 * kGW;            // threads per workgroup
 constexpr int kWN = kGW / 2;             // waves along the outputs
 constexpr int kNB = kPN / (32 * kWN);    // 32 x 32 blocks per wave along the outputs

@@ -818,10 +818,9 @@ hipError_t launch_hash(const void* qk, const float* R, const Dims& d, int32_t* b
     rprep_kernel<<<pgrid, 256, 0, st>>>(R, d.d, half, ntiles, w.tmax, w.rnorm, w.rt, w.rfrag);
     if ((e = mark(st, ev, nev, names, "hash_prep")) != hipSuccess) return e;
     if (d.dtype == LSH_BF16) {
-#ifndef LSH_HASH_TOKF
-#define LSH_HASH_TOKF 2
-#endif
-        constexpr int TOKF = LSH_HASH_TOKF;
+        // two 32-token fragments per wave (32 and 128 tokens per wave measured
+        // slower)
+        constexpr int TOKF = 2;
         constexpr int per_wave = 32 * TOKF, per_wg = 4 * per_wave;
         static_assert(per_wg <= kQueuePad && kQueuePad % per_wg == 0,
                       "queue regions must fit the padded capacity");

@@ -56,7 +56,7 @@ def _shape(**kw):
 @pytest.mark.parametrize("kw, code", [
     (dict(n_buckets=15), -1), (dict(n_buckets=0), -1), (dict(n_hashes=0), -1),
     (dict(chunk_len=0), -1), (dict(L=100, chunk_len=64), -1), (dict(causal=2), -1),
-    (dict(dtype=7), -1), (dict(B=-1), -1), (dict(d=96), -4), (dict(n_buckets=8192), -4),
+    (dict(dtype=7), -1), (dict(B=-1), -1), (dict(d=96), -1), (dict(n_buckets=8192), -1),
     (dict(B=64, H=64, L=65536, n_hashes=8, chunk_len=64), -1),
     (dict(flags=4), -1), (dict(flags=-1), -1),
 ])
@@ -65,6 +65,30 @@ def test_workspace_size_rejects_bad_shapes(lib, kw, code):
         lsh.lsh_workspace_size("fwd", _shape(**kw))
     assert ei.value.code == code
     assert lsh.lsh_last_error()
+
+
+def test_workspace_size_is_a_size_t_with_zero_on_error(lib):
+    """size_t lsh_workspace_size(stage, shape): the size, with an empty
+    message; 0 and a message for an unknown or NULL stage or a bad shape."""
+    s = _shape()
+    n = lib.lsh_workspace_size(b"fwd", ctypes.byref(s))
+    assert n > 0 and lsh.lsh_last_error() == ""
+    assert lib.lsh_workspace_size(b"nope", ctypes.byref(s)) == 0
+    assert "unknown stage" in lsh.lsh_last_error()
+    assert lib.lsh_workspace_size(None, ctypes.byref(s)) == 0
+    assert "stage" in lsh.lsh_last_error()
+    bad = _shape(d=96)
+    assert lib.lsh_workspace_size(b"fwd", ctypes.byref(bad)) == 0
+    assert "d must be 64 or 128" in lsh.lsh_last_error()
+    assert lib.lsh_workspace_size(b"fwd", None) == 0
+    # the message is cleared by the next successful call
+    assert lib.lsh_workspace_size(b"sort", ctypes.byref(s)) > 0 and lsh.lsh_last_error() == ""
+    # a valid empty problem can need no sort workspace at all: size 0, no message
+    assert lib.lsh_workspace_size(b"sort", ctypes.byref(_shape(B=0))) == 0
+    assert lsh.lsh_last_error() == ""
+    assert lib.lsh_ffn_workspace_size(10, 12, 4, lsh.LSH_BF16) == 0 and lsh.lsh_last_error()
+    assert lib.lsh_ffn_workspace_size(0, 64, 4, lsh.LSH_BF16) == 0
+    assert lsh.lsh_last_error() == ""
 
 
 def test_workspace_sizes_are_consistent(lib):
@@ -87,7 +111,7 @@ def test_workspace_sizes_are_consistent(lib):
 def test_entry_points_reject_on_host(lib):
     s = _shape(d=96)
     vp = ctypes.c_void_p
-    assert lib.lsh_attention_fwd(None, None, None, ctypes.byref(s), None, None, 0, None) == -4
+    assert lib.lsh_attention_fwd(None, None, None, ctypes.byref(s), None, None, 0, None) == -1
     s = _shape()
     # NULL tensors are refused before anything reaches the device
     assert lib.lsh_hash(None, None, ctypes.byref(s), None, None, 0, None) == -1
@@ -244,3 +268,67 @@ def test_bench_refuses_more_than_one_gpu():
                          capture_output=True, text=True, timeout=120, cwd=root)
     assert res.returncode == 2
     assert "error" in json.loads(res.stdout.strip().splitlines()[-1])
+
+
+def _cpu_qk(B=1, H=2, L=256, d=64, dtype=None):
+    import torch
+    return torch.zeros(B, H, L, d, dtype=dtype or torch.bfloat16)
+
+
+@pytest.mark.parametrize("rshape, rdtype, msg", [
+    ((2, 64, 8), "bfloat16", "float32"),      # bf16 R (natural next to bf16 qk)
+    ((2, 64, 4), "float32", "n_buckets/2"),   # R for 8 buckets, called with 16
+    ((2, 32, 8), "float32", "n_buckets/2"),   # wrong head size
+    ((3, 2, 64, 8), "float32", "n_buckets/2"),  # per-head R for 3 heads, qk has 2
+    ((0, 64, 8), "float32", "n_buckets/2"),   # no rounds
+])
+def test_helpers_validate_R_before_any_launch(rshape, rdtype, msg):
+    """R is read by kernels sized from qk and n_buckets: a mismatched or
+    mistyped R is refused on the host (CPU tensors here, so nothing could be
+    launched even if the check were missing: the device check comes later)."""
+    import torch
+    qk = _cpu_qk()
+    R = torch.zeros(rshape, dtype=getattr(torch, rdtype))
+    for call in (lambda: lsh.hash(qk, R, 16),
+                 lambda: lsh.attention_fwd(qk, qk, R, 16, 64, True),
+                 lambda: lsh.attention_fwd_train(qk, qk, R, 16, 64, True)):
+        with pytest.raises(ValueError, match=msg):
+            call()
+
+
+def test_helpers_validate_out_and_v():
+    import torch
+    qk = _cpu_qk()
+    R = torch.zeros(2, 64, 8)
+    with pytest.raises(ValueError, match="out"):
+        lsh.attention_fwd(qk, qk, R, 16, 64, True, out=torch.zeros(1, 2, 256, 64))
+    with pytest.raises(ValueError, match="out"):
+        lsh.attention_fwd(qk, qk, R, 16, 64, True, out=_cpu_qk(L=128))
+    with pytest.raises(ValueError, match="v"):
+        lsh.attention_fwd(qk, _cpu_qk(d=128), R, 16, 64, True)
+
+
+def test_c_named_wrappers_check_buffer_sizes_and_dtypes():
+    """The C-named Python calls check every tensor against the shape before the
+    call (a short or mistyped buffer would be read past its end on the GPU)."""
+    import torch
+    s = _shape()
+    qk = _cpu_qk()
+    R = torch.zeros(2, 64, 8)
+    n = s.B * s.H * s.n_hashes * s.L
+    with pytest.raises(ValueError, match="buckets"):
+        lsh.lsh_hash(qk, R, s, torch.zeros(n - 1, dtype=torch.int32), None)
+    with pytest.raises(ValueError, match="R"):
+        lsh.lsh_hash(qk, torch.zeros(2, 64, 8, dtype=torch.bfloat16), s,
+                     torch.zeros(n, dtype=torch.int32), None)
+    with pytest.raises(ValueError, match="qk"):
+        lsh.lsh_attention_fwd(qk.float(), qk, R, s, qk, None)
+    with pytest.raises(ValueError, match="inv"):
+        lsh.lsh_sort(torch.zeros(n, dtype=torch.int32), s, torch.zeros(n, dtype=torch.int32),
+                     torch.zeros(n, dtype=torch.int64), None)
+    with pytest.raises(ValueError, match="o_sorted"):
+        lsh.lsh_chunk_attend(qk, qk, torch.zeros(n, dtype=torch.int32),
+                             torch.zeros(n, dtype=torch.int32), s,
+                             torch.zeros(n, dtype=torch.float32), torch.zeros(n), None)
+    with pytest.raises(ValueError, match="dv"):
+        lsh.lsh_attention_bwd(qk, qk, qk, qk, None, s, qk, None, None)
