@@ -59,6 +59,10 @@ def algorithmic_work(w):
         # read the buckets (count); read them again and write one packed key
         # per slot (scatter, fused forward)
         "sort_count": ("hbm", 4.0 * TR, "B"),
+        # per (segment, tile, bucket) count read and prefix written back, plus
+        # the segment totals: not per token-round work (tiny next to the keys)
+        "sort_prefix": ("hbm", 4.0 * w.B * w.H * w.n_hashes * w.n_buckets
+                        * (2 * -(-w.L // 4096) + 1), "B"),
         "sort_scatter": ("hbm", 8.0 * TR, "B"),
         # gather qk and v rows once per token-round, read the sorted key (and
         # bucket id), write the round's output row: fp32 plus a separate lse
@@ -343,6 +347,17 @@ def dense_comparator(torch, w, qk_t, v_t, steps=10):
             "tokens_per_s": w.B * w.L / (ms / 1e3), "analytic_dense_floor_ms": floor}
 
 
+def _cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo ("unknown" elsewhere)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, qk, v, R, target_s=12.0):
     """Times the oracle (as it is) on a bounded sample of the workload: whole
     (batch, head) slices with every round, as many heads of batch row 0 as fit
@@ -364,6 +379,7 @@ def cpu_baseline(w, qk, v, R, target_s=12.0):
             break
         L //= 2
     return {"value": L * heads / w.H / dt, "unit": "tokens/s", "cores": oracle.threads(),
+            "threads": oracle.threads(), "nproc": os.cpu_count(), "cpu_model": _cpu_model(),
             "kind": "oracle",
             "sample": f"batch row 0, {heads} of {w.H} heads, first {L} positions, all "
                       f"{w.n_hashes} rounds: {dt:.1f} s; rate scaled by {heads}/{w.H} heads"}

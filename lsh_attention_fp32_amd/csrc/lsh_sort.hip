@@ -6,20 +6,27 @@
 // summary, section "・LSH Attention" (sort per bucket before chunking).
 //
 // Positions arrive in increasing order, so a stable counting sort on the
-// bucket alone yields the (bucket, position) order. Two kernels:
-//   count   per 4096-element tile: bucket histogram in LDS (plain atomics)
-//   scatter per tile: first the slot where each of its (tile, bucket) runs
-//           starts -- the segment's bucket totals, scanned, plus the counts
-//           of the earlier tiles -- then each wave ranks its 1024 elements in
-//           order; lanes with equal buckets are grouped by a ballot match, so
-//           ranks are exact and the LDS counter of a hot bucket is bumped once
-//           per wave step (skewed buckets do not serialise on LDS atomics).
+// bucket alone yields the (bucket, position) order. Three kernels:
+//   count   per 4096-element tile: bucket histogram in LDS (plain atomics),
+//           written to counts[seg][tile][bucket]
+//   prefix  per (segment, 256 buckets): each bucket's counts become the
+//           number of that bucket in the segment's earlier tiles (in place),
+//           and its total goes to totals[seg][bucket]
+//   scatter per tile: the slot where each of its (tile, bucket) runs starts
+//           is the exclusive scan of the segment's totals plus the tile's
+//           prefix -- 2 nb values read per tile, whatever the number of
+//           tiles -- then each wave ranks its 1024 elements in order; lanes
+//           with equal buckets are grouped by a ballot match, so ranks are
+//           exact and the LDS counter of a hot bucket is bumped once per wave
+//           step (skewed buckets do not serialise on LDS atomics).
 #include "lsh_internal.h"
 
 namespace lsh {
 
 size_t sort_workspace_bytes(const Dims& d) {
-    return align_up(sizeof(int32_t) * (size_t)d.segs * d.nb * (size_t)sort_ntiles(d), 256);
+    // counts (then earlier-tile prefixes) [seg][tile][nb], totals [seg][nb]
+    return align_up(sizeof(int32_t) * (size_t)d.segs * d.nb * (size_t)sort_ntiles(d), 256) +
+           align_up(sizeof(int32_t) * (size_t)d.segs * d.nb, 256);
 }
 
 // Mask of the lanes whose bucket equals this lane's (0 for inactive lanes).
@@ -72,21 +79,86 @@ __global__ __launch_bounds__(256) void sort_count_kernel(const int32_t* __restri
         counts[(seg * ntiles + tile) * dm.nb + b] = hist[b];
 }
 
+// counts[seg][t][b] -> number of b in tiles 0 .. t-1 of the segment (in
+// place); totals[seg][b] = number of b in the segment. One thread per bucket,
+// so every tile's row is read and written with coalesced accesses; the loads
+// of kBatch tiles are issued before any is used.
+__global__ __launch_bounds__(256) void sort_prefix_kernel(int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ totals, int nb,
+                                                          int ntiles) {
+    constexpr int kBatch = 8;
+    const int b = blockIdx.x * 256 + threadIdx.x;
+    const int64_t seg = blockIdx.y;
+    if (b >= nb) return;
+    int32_t* c = counts + seg * ntiles * nb + b;
+    int32_t run = 0;
+    for (int t0 = 0; t0 < ntiles; t0 += kBatch) {
+        int32_t x[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) x[k] = t0 + k < ntiles ? c[(int64_t)(t0 + k) * nb] : 0;
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k)
+            if (t0 + k < ntiles) {
+                c[(int64_t)(t0 + k) * nb] = run;
+                run += x[k];
+            }
+    }
+    totals[seg * nb + b] = run;
+}
+
 constexpr int kScatterXcds = 8;   // L2 domains of the chip
 
+// Exclusive scan of a[0..n) in LDS by the 256 threads of the workgroup (each
+// takes a contiguous chunk, then a wave scan and the earlier waves' sums).
+// Ends with a barrier; a[] is read and written only between barriers.
+__device__ __forceinline__ void block_exclusive_scan(int32_t* a, int n, int32_t* wsum) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int per = (n + 255) / 256;
+    const int b0 = threadIdx.x * per;
+    int32_t mine = 0;
+    for (int j = 0; j < per; ++j)
+        if (b0 + j < n) mine += a[b0 + j];
+    int32_t incl = mine;
+    for (int off = 1; off < 64; off <<= 1) {
+        const int32_t o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int32_t run = incl - mine;
+    for (int w = 0; w < wave; ++w) run += wsum[w];
+    for (int j = 0; j < per; ++j)
+        if (b0 + j < n) {
+            const int32_t c = a[b0 + j];
+            a[b0 + j] = run;
+            run += c;
+        }
+    __syncthreads();
+}
+
 // PACKED: perm[slot] = (bucket << kPackPosBits) | position and no inverse.
-template <bool PACKED>
+// STAGED (positions below 2^kPackPosBits): the tile's elements are first put
+// in their sorted order in LDS, then written out with consecutive threads on
+// consecutive slots, so each (tile, bucket) run leaves as one contiguous
+// piece instead of one 4-byte store per element at scattered slots.
+template <bool PACKED, bool STAGED>
 __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __restrict__ buckets,
-                                                           const int32_t* __restrict__ offs,
+                                                           const int32_t* __restrict__ prefix,
+                                                           const int32_t* __restrict__ totals,
                                                            Dims dm, int ntiles, int nbits,
                                                            int32_t* __restrict__ perm,
                                                            int32_t* __restrict__ inv) {
-    extern __shared__ int32_t sh[];   // [kSortWaves][nb] counts, then running slots; [nb] run starts
+    // LDS: [kSortWaves][nb] per-wave counts, then run starts; [nb] the tile's
+    // first slot of each bucket (later: slot minus tile-local index); STAGED:
+    // [kSortTile] the tile's keys in sorted order, whose first nb entries
+    // hold the tile-local bucket starts before the keys are written
+    extern __shared__ int32_t sh[];
     __shared__ int32_t wsum[4];
+    static_assert(!PACKED || STAGED, "packed keys are staged");
     constexpr int SUB = kSortTile / kSortWaves;
     // Workgroups are dealt round-robin over the L2 domains (id % kScatterXcds):
     // every tile of a segment gets the same residue, so one L2 collects the
-    // segment's scattered 4-byte writes and hands whole lines to memory.
+    // segment's writes and hands whole lines to memory.
     const int64_t id = blockIdx.x, k = id / kScatterXcds;
     const int64_t seg = (k / ntiles) * kScatterXcds + id % kScatterXcds;
     const int tile = (int)(k % ntiles);
@@ -94,11 +166,13 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __rest
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nb = dm.nb;
     int32_t* start = sh + kSortWaves * nb;
+    int32_t* lkeys = start + nb;
 
     // The wave's 1024 bucket ids are loaded first (all in flight while the
     // run starts are computed) and stay in registers.
     const int32_t* src = buckets + seg * dm.L;
-    const int64_t wbeg = (int64_t)tile * kSortTile + (int64_t)wave * SUB;
+    const int64_t tbeg = (int64_t)tile * kSortTile;
+    const int64_t wbeg = tbeg + (int64_t)wave * SUB;
     const int64_t wend = min(wbeg + (int64_t)SUB, (int64_t)dm.L);
     constexpr int STEPS = SUB / kWave;
     int kb[STEPS], rank[STEPS];
@@ -109,43 +183,18 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __rest
     }
 
     // First slot of this tile's run of every bucket: exclusive scan over
-    // buckets of the segment totals, plus the counts of the earlier tiles.
-    // Totals (start[]) and earlier-tile counts (sh[0..nb)) are gathered with
-    // coalesced reads, then scanned in contiguous chunks of bpt buckets.
+    // buckets of the segment totals, plus this bucket's count in the earlier
+    // tiles (both read with coalesced loads).
     {
-        const int32_t* cnt = offs + seg * ntiles * nb;
+        const int32_t* tot = totals + seg * nb;
+        const int32_t* pre = prefix + (seg * ntiles + tile) * nb;
         for (int b = threadIdx.x; b < nb; b += 256) {
-            int32_t tot = 0, before = 0;
-#pragma unroll 16
-            for (int t = 0; t < ntiles; ++t) {
-                const int32_t c = cnt[(int64_t)t * nb + b];
-                tot += c;
-                before += t < tile ? c : 0;
-            }
-            start[b] = tot;
-            sh[b] = before;
+            start[b] = tot[b];
+            sh[b] = pre[b];
         }
         __syncthreads();
-        const int bpt = (nb + 255) / 256;
-        const int b0 = threadIdx.x * bpt;
-        int32_t mine = 0;
-        for (int j = 0; j < bpt; ++j)
-            if (b0 + j < nb) mine += start[b0 + j];
-        int32_t incl = mine;
-        for (int off = 1; off < 64; off <<= 1) {
-            const int32_t o = __shfl_up(incl, off);
-            if (lane >= off) incl += o;
-        }
-        if (lane == 63) wsum[wave] = incl;
-        __syncthreads();
-        int32_t run = incl - mine;
-        for (int w = 0; w < wave; ++w) run += wsum[w];
-        for (int j = 0; j < bpt; ++j)
-            if (b0 + j < nb) {
-                const int32_t tot = start[b0 + j];
-                start[b0 + j] = run + sh[b0 + j];
-                run += tot;
-            }
+        block_exclusive_scan(start, nb, wsum);
+        for (int b = threadIdx.x; b < nb; b += 256) start[b] += sh[b];
     }
     __syncthreads();
     for (int k = threadIdx.x; k < kSortWaves * nb; k += 256) sh[k] = 0;
@@ -165,27 +214,64 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __rest
         __builtin_amdgcn_wave_barrier();
     }
     __syncthreads();
-    // first slot of each (wave, bucket) run
-    for (int b = threadIdx.x; b < nb; b += 256) {
-        int32_t run = start[b];
-        for (int w = 0; w < kSortWaves; ++w) {
-            const int32_t c = sh[w * nb + b];
-            sh[w * nb + b] = run;
-            run += c;
+    if constexpr (STAGED) {
+        // tile-local start of every bucket (scan of the tile's counts), then
+        // each (wave, bucket) run's local start; start[] becomes slot - local
+        int32_t* lstart = lkeys;
+        for (int b = threadIdx.x; b < nb; b += 256) {
+            int32_t c = 0;
+            for (int w = 0; w < kSortWaves; ++w) c += sh[w * nb + b];
+            lstart[b] = c;
         }
-    }
-    __syncthreads();
-    // pass 2: slots
-    int32_t* P = perm + seg * dm.L;
-    int32_t* I = PACKED ? nullptr : inv + seg * dm.L;
+        __syncthreads();
+        block_exclusive_scan(lstart, nb, wsum);
+        for (int b = threadIdx.x; b < nb; b += 256) {
+            int32_t run = lstart[b];
+            start[b] -= run;
+            for (int w = 0; w < kSortWaves; ++w) {
+                const int32_t c = sh[w * nb + b];
+                sh[w * nb + b] = run;
+                run += c;
+            }
+        }
+        __syncthreads();   // lstart is dead from here on: its space takes the keys
+        int32_t* I = PACKED ? nullptr : inv + seg * dm.L;
 #pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
-        const int64_t i = wbeg + s * kWave + lane;
-        if (i < wend) {
-            const int32_t slot = mine[kb[s]] + rank[s];
-            if constexpr (PACKED) {
-                P[slot] = (int32_t)(((uint32_t)kb[s] << kPackPosBits) | (uint32_t)i);
-            } else {
+        for (int s = 0; s < STEPS; ++s) {
+            const int64_t i = wbeg + s * kWave + lane;
+            if (i < wend) {
+                const int32_t local = mine[kb[s]] + rank[s];
+                lkeys[local] = (int32_t)(((uint32_t)kb[s] << kPackPosBits) | (uint32_t)i);
+                if constexpr (!PACKED) I[i] = local + start[kb[s]];
+            }
+        }
+        __syncthreads();
+        int32_t* P = perm + seg * dm.L;
+        const int n = (int)min((int64_t)kSortTile, (int64_t)dm.L - tbeg);
+        for (int i = threadIdx.x; i < n; i += 256) {
+            const uint32_t key = (uint32_t)lkeys[i];
+            const int32_t slot = i + start[key >> kPackPosBits];
+            P[slot] = PACKED ? (int32_t)key : (int32_t)(key & kPackPosMask);
+        }
+    } else {
+        // first slot of each (wave, bucket) run
+        for (int b = threadIdx.x; b < nb; b += 256) {
+            int32_t run = start[b];
+            for (int w = 0; w < kSortWaves; ++w) {
+                const int32_t c = sh[w * nb + b];
+                sh[w * nb + b] = run;
+                run += c;
+            }
+        }
+        __syncthreads();
+        // pass 2: every element straight to its slot
+        int32_t* P = perm + seg * dm.L;
+        int32_t* I = inv + seg * dm.L;
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s) {
+            const int64_t i = wbeg + s * kWave + lane;
+            if (i < wend) {
+                const int32_t slot = mine[kb[s]] + rank[s];
                 P[slot] = (int32_t)i;
                 I[i] = slot;
             }
@@ -200,19 +286,31 @@ hipError_t launch_sort(const int32_t* buckets, const Dims& d, int32_t* perm, int
     int nbits = 0;
     while ((1 << nbits) < d.nb) ++nbits;
     int32_t* counts = (int32_t*)ws;
+    int32_t* totals =
+        (int32_t*)((char*)ws + align_up(sizeof(int32_t) * (size_t)d.segs * d.nb * ntiles, 256));
     dim3 grid((unsigned)ntiles, (unsigned)d.segs);
     hipError_t e;
     sort_count_kernel<<<grid, 256, sizeof(int32_t) * d.nb, st>>>(buckets, d, ntiles, counts);
     if ((e = mark(st, ev, nev, names, "sort_count")) != hipSuccess) return e;
-    const size_t lds = sizeof(int32_t) * (kSortWaves + 1) * d.nb;
+    sort_prefix_kernel<<<dim3((unsigned)((d.nb + 255) / 256), (unsigned)d.segs), 256, 0, st>>>(
+        counts, totals, d.nb, ntiles);
+    if ((e = mark(st, ev, nev, names, "sort_prefix")) != hipSuccess) return e;
+    // staged needs positions below 2^kPackPosBits (a packed key per element)
+    const bool staged = packed_sort_keys(d);
+    if (packed && !staged) return hipErrorInvalidValue;
+    static_assert(kSortTile >= kMaxBuckets, "the staged keys' space first holds nb starts");
+    const size_t lds = sizeof(int32_t) * ((kSortWaves + 1) * d.nb + (staged ? kSortTile : 0));
     const int64_t sgroups = (d.segs + kScatterXcds - 1) / kScatterXcds;
     const unsigned sgrid = (unsigned)(sgroups * kScatterXcds * ntiles);
     if (packed)
-        sort_scatter_kernel<true><<<sgrid, 256, lds, st>>>(buckets, counts, d, ntiles, nbits,
-                                                           perm, nullptr);
+        sort_scatter_kernel<true, true><<<sgrid, 256, lds, st>>>(buckets, counts, totals, d,
+                                                                 ntiles, nbits, perm, nullptr);
+    else if (staged)
+        sort_scatter_kernel<false, true><<<sgrid, 256, lds, st>>>(buckets, counts, totals, d,
+                                                                  ntiles, nbits, perm, inv);
     else
-        sort_scatter_kernel<false><<<sgrid, 256, lds, st>>>(buckets, counts, d, ntiles, nbits,
-                                                            perm, inv);
+        sort_scatter_kernel<false, false><<<sgrid, 256, lds, st>>>(buckets, counts, totals, d,
+                                                                   ntiles, nbits, perm, inv);
     return mark(st, ev, nev, names, "sort_scatter");
 }
 

@@ -125,12 +125,17 @@ SORT_CASES = [("uniform", 1024, 4096 + 192), ("uniform", 64, 4096 * 3), ("skewed
               ("constant", 64, 5000 // 8 * 8), ("uniform", 4096, 8192), ("uniform", 2, 100),
               ("uniform", 2048, 65536), ("uniform", 256, 65536 + 64 * 5),
               ("skewed", 4096, 3 * 32768)]
+# 12 segments (B 1, H 3, 4 rounds): the scatter deals segments to the eight L2
+# domains in groups of eight, so the second group is partial, over four
+# tiles with a ragged last one
+SORT_CASES_12 = [("uniform", 512, 3 * 4096 + 64), ("skewed", 1024, 3 * 4096 + 64)]
 
 
-@pytest.mark.parametrize("kind,nb,L", SORT_CASES)
-def test_sort_matches_oracle(kind, nb, L):
+@pytest.mark.parametrize("kind,nb,L,bhn", [c + ((1, 2, 3),) for c in SORT_CASES] +
+                         [c + ((1, 3, 4),) for c in SORT_CASES_12])
+def test_sort_matches_oracle(kind, nb, L, bhn):
     rng = np.random.default_rng(nb + L)
-    B, H, nh = 1, 2, 3
+    B, H, nh = bhn
     if kind == "uniform":
         b = rng.integers(0, nb, (B, H, nh, L))
     elif kind == "skewed":
@@ -166,6 +171,9 @@ STEP_CASES = [
     _wl("fp32", B=1, H=1, L=96 * 8, d=64, nb=8, nh=2, m=96, causal=True, seed=23),
     _wl("fp32", B=1, H=2, L=40 * 9, d=64, nb=4, nh=2, m=40, causal=False, seed=24),
     _wl("bf16", B=1, H=1, L=128 * 6, d=128, nb=8, nh=2, m=128, causal=True, seed=25),
+    # 12 segments over four sort tiles (ragged last tile): the fused forward's
+    # packed scatter with a partial group of L2 domains
+    _wl("bf16", B=1, H=3, L=3 * 4096 + 64, d=64, nb=256, nh=4, m=64, causal=True, seed=26),
 ]
 
 
@@ -195,6 +203,17 @@ def _oracle_pipeline(qk, v, R, w):
                     qk[b, h], v[b, h], bk, ref["perm"][b, h, r], w.chunk_len, w.causal)
             ref["out"][b, h] = oracle.combine(ref["o"][b, h], ref["lse"][b, h], ref["inv"][b, h])
     return ref
+
+
+def _round_magnitude(ref):
+    """sum_r w_r |o_r| per (batch, head, position, feature) from the oracle's
+    per-round results, w_r = exp(lse_r - logsumexp over rounds)."""
+    inv = ref["inv"].astype(np.int64)                     # [B, H, nh, L]
+    lse = np.take_along_axis(ref["lse"], inv, axis=3)     # by position
+    w = np.exp(lse - lse.max(axis=2, keepdims=True))
+    w /= w.sum(axis=2, keepdims=True)
+    o = np.take_along_axis(np.abs(ref["o"]), inv[..., None], axis=3)
+    return (w[..., None] * o).sum(axis=2)
 
 
 def _dev(a, dtype=None):
@@ -249,10 +268,23 @@ def test_steps_match_oracle(w):
     assert worst_l <= (1e-5 if w.dtype == "fp32" else 1e-3)
     assert worst_f <= tol
     assert skipped < w.B * w.H
-    # the fused forward keeps per-round outputs in scaled fp16 on the bf16
-    # matrix-core path (relative error 2^-12) instead of the staged fp32
+    # The fused forward keeps per-round outputs in scaled fp16 on the bf16
+    # matrix-core path instead of the staged fp32, with one value bit given to
+    # the carried lse: each stored value is within 1.5 fp16 ulps (2^-10
+    # relative) of the fp32 one, so before the output's rounding the two paths
+    # differ by at most 1.5 2^-10 sum_r w_r |o_r| -- relative to the rounds'
+    # magnitudes, not to the output, which cancellation can make small. Each
+    # output is then rounded to bf16 (one ulp apart at most, 2^-7 relative).
     if w.dtype == "bf16" and w.chunk_len == 64:
-        assert np.all(np.abs(fwd - staged) <= 2.0 ** -7 * np.abs(staged) + 1e-3)
+        mag = _round_magnitude(ref)
+        bar = 2.0 ** -7 * 1.01 * np.abs(staged) + 2.0 ** -9 * mag + 1e-6
+        excess = np.abs(fwd - staged) - bar
+        # slices whose bucket ids match the oracle's (the magnitudes are the
+        # oracle's rounds)
+        same = np.array([[np.array_equal(gb[b, h], ref["buckets"][b, h]) for h in range(w.H)]
+                         for b in range(w.B)])
+        worst = float(excess[same].max())
+        assert worst <= 0, f"fused vs staged beyond the fp16 bound by {worst:.3g}"
     else:
         assert np.array_equal(staged, fwd), "fused forward differs from the staged calls"
 
