@@ -140,6 +140,21 @@ int lsh_hash(const void *qk, const float *R, const lsh_shape_t *shape, int32_t *
 int lsh_sort(const int32_t *buckets, const lsh_shape_t *shape, int32_t *perm, int32_t *inv,
              void *ws, size_t ws_bytes, void *stream);
 
+/* lsh_sort without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops, harnesses that
+ * forbid allocation). Same kernels and result as lsh_sort; the sort's
+ * per-tile counts live in a static device array of 16 MiB that the library
+ * holds on each GPU it runs on until the process ends (its address is looked
+ * up on the first call on a device). It calls no allocating routine.
+ *   buckets, perm, inv   as for lsh_sort
+ *   stream               must belong to the current device (else LSH_ERR_ARG)
+ * Errors: LSH_ERR_WORKSPACE when lsh_workspace_size("sort") exceeds 16 MiB
+ * (e.g. B*H*n_hashes * ceil(L/4096) * n_buckets * 4 bytes past it); the
+ * other checks as for lsh_sort. Calls that overlap on one GPU (several
+ * streams or host threads) share the array and race: serialise them. */
+int lsh_sort_noalloc(const int32_t *buckets, const lsh_shape_t *shape, int32_t *perm,
+                     int32_t *inv, void *stream);
+
 /* Steps 3+4 -- gather into sorted order and chunked attention (walkthrough
  * "1 LSH Attention"; glossary "Atenção LSH"). For sorted slot s of a round,
  * with chunk c = s / m, the candidate keys are the slots of chunks c-1 and c

@@ -7,7 +7,7 @@ current HIP stream. It raises if the library has not been built -- there is
 no other implementation to fall back to.
 
 Low-level functions keep the C names and argument order (tensors in place of
-pointers): ``lsh_workspace_size``, ``lsh_hash``, ``lsh_sort``,
+pointers): ``lsh_workspace_size``, ``lsh_hash``, ``lsh_sort``, ``lsh_sort_noalloc``,
 ``lsh_chunk_attend``, ``lsh_unsort_combine``, ``lsh_attention_fwd``,
 ``lsh_attention_fwd_timed``, ``lsh_qkv_project``, ``lsh_attention_fwd_x``,
 ``lsh_attention_fwd_train``, ``lsh_attention_bwd``. The allocating helpers
@@ -47,6 +47,7 @@ from ._binding import (  # noqa: F401
     lsh_last_error,
     lsh_qkv_project,
     lsh_sort,
+    lsh_sort_noalloc,
     lsh_unsort_combine,
     lsh_workspace_size,
     qkv_project,

@@ -54,6 +54,7 @@ def load_library():
     lib.lsh_workspace_size.restype = sz
     lib.lsh_hash.argtypes = [vp, vp, sp, vp, vp, sz, vp]
     lib.lsh_sort.argtypes = [vp, sp, vp, vp, vp, sz, vp]
+    lib.lsh_sort_noalloc.argtypes = [vp, sp, vp, vp, vp]
     lib.lsh_chunk_attend.argtypes = [vp, vp, vp, vp, sp, vp, vp, vp]
     lib.lsh_unsort_combine.argtypes = [vp, vp, vp, sp, vp, vp]
     lib.lsh_attention_fwd.argtypes = [vp, vp, vp, sp, vp, vp, sz, vp]
@@ -69,7 +70,7 @@ def load_library():
     lib.lsh_ffn_workspace_size.argtypes = [i64, i32, i32, i32]
     lib.lsh_ffn_workspace_size.restype = sz
     lib.lsh_ffn_chunked.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp, sz, vp]
-    for name in ("lsh_ffn_chunked", "lsh_hash", "lsh_sort", "lsh_chunk_attend",
+    for name in ("lsh_ffn_chunked", "lsh_hash", "lsh_sort", "lsh_sort_noalloc", "lsh_chunk_attend",
                  "lsh_unsort_combine", "lsh_attention_fwd", "lsh_attention_fwd_timed",
                  "lsh_qkv_project", "lsh_attention_fwd_x", "lsh_attention_fwd_train",
                  "lsh_attention_bwd"):
@@ -231,6 +232,14 @@ def lsh_sort(buckets, shape: Shape, perm, inv, ws, stream=None) -> None:
         _need("lsh_sort", what, t, torch.int32, n)
     _check(load_library().lsh_sort(_ptr(buckets), ctypes.byref(shape), _ptr(perm), _ptr(inv),
                                    _ptr(ws), _nbytes(ws), _stream(stream)), "lsh_sort")
+
+
+def lsh_sort_noalloc(buckets, shape: Shape, perm, inv, stream=None) -> None:
+    n = _sizes(shape)[1]
+    for what, t in (("buckets", buckets), ("perm", perm), ("inv", inv)):
+        _need("lsh_sort_noalloc", what, t, torch.int32, n)
+    _check(load_library().lsh_sort_noalloc(_ptr(buckets), ctypes.byref(shape), _ptr(perm),
+                                           _ptr(inv), _stream(stream)), "lsh_sort_noalloc")
 
 
 def lsh_chunk_attend(qk, v, buckets, perm, shape: Shape, o_sorted, lse_sorted, stream=None) -> None:

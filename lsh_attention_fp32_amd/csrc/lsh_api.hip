@@ -273,6 +273,41 @@ int lsh_sort(const int32_t* buckets, const lsh_shape_t* shape, int32_t* perm, in
     return e == hipSuccess ? LSH_OK : hip_fail(e, "lsh_sort");
 }
 
+int lsh_sort_noalloc(const int32_t* buckets, const lsh_shape_t* shape, int32_t* perm, int32_t* inv,
+                     void* stream) {
+    g_err[0] = 0;
+    int rc = validate(shape);
+    if (rc) return rc;
+    if (empty(shape)) return LSH_OK;
+    if (!buckets || !perm || !inv)
+        return fail(LSH_ERR_ARG, "lsh_sort_noalloc: NULL tensor pointer");
+    if (misaligned({buckets, perm, inv}))
+        return fail(LSH_ERR_ARG, "lsh_sort_noalloc: tensor pointers must be 16-byte aligned");
+    const Dims d = make_dims(*shape);
+    const size_t need = sort_workspace_bytes(d);
+    if (need > kSortScratchBytes)
+        return fail(LSH_ERR_WORKSPACE,
+                    "lsh_sort_noalloc: the shape needs %zu bytes of scratch, the static scratch "
+                    "holds %zu (use lsh_sort with a workspace)",
+                    need, kSortScratchBytes);
+    hipStream_t st = (hipStream_t)stream;
+    if (st) {
+        int cur = 0, sdev = 0;
+        hipError_t e = hipGetDevice(&cur);
+        if (e == hipSuccess) e = hipStreamGetDevice(st, &sdev);
+        if (e != hipSuccess) return hip_fail(e, "lsh_sort_noalloc: device of the stream");
+        if (sdev != cur)
+            return fail(LSH_ERR_ARG, "lsh_sort_noalloc: the stream belongs to device %d, the "
+                                     "current device is %d", sdev, cur);
+    }
+    void* ws = nullptr;
+    hipError_t e = sort_scratch(&ws);
+    if (e != hipSuccess) return hip_fail(e, "lsh_sort_noalloc: scratch address");
+    e = launch_sort(buckets, d, perm, inv, ws, st, nullptr, nullptr, nullptr);
+    if (e == hipSuccess) e = hipGetLastError();
+    return e == hipSuccess ? LSH_OK : hip_fail(e, "lsh_sort_noalloc");
+}
+
 int lsh_chunk_attend(const void* qk, const void* v, const int32_t* buckets, const int32_t* perm,
                      const lsh_shape_t* shape, float* o_sorted, float* lse_sorted, void* stream) {
     g_err[0] = 0;

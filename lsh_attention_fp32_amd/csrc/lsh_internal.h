@@ -118,6 +118,11 @@ constexpr int kMaxHashes = 4096;
 inline int64_t sort_ntiles(const Dims& d) { return (d.L + kSortTile - 1) / kSortTile; }
 size_t sort_workspace_bytes(const Dims& d);
 
+// Size of the static scratch behind lsh_sort_noalloc, and its device address
+// on the current device (looked up once per device).
+constexpr size_t kSortScratchBytes = (size_t)16 << 20;
+hipError_t sort_scratch(void** ptr);
+
 // Packed sorted keys: inside the fused forward the sort can store, per slot,
 // (bucket << kPackPosBits) | position instead of the plain position, so the
 // chunk pass reads both from one coalesced word; no inverse is written then.

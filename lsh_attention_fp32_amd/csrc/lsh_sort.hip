@@ -19,9 +19,38 @@
 //           with equal buckets are grouped by a ballot match, so ranks are
 //           exact and the LDS counter of a hot bucket is bumped once per wave
 //           step (skewed buckets do not serialise on LDS atomics).
+#include <mutex>
+
 #include "lsh_internal.h"
 
 namespace lsh {
+
+// Static scratch of lsh_sort_noalloc: the sort's counts, prefixes and totals
+// for callers that cannot allocate. Each GPU the library runs on holds its own
+// copy until the process ends. In host code `scratch` names a host-side
+// stand-in, never the device memory: only the address hipGetSymbolAddress
+// returns (sort_scratch below) may reach a kernel or a copy.
+static __device__ __align__(256) int32_t scratch[kSortScratchBytes / sizeof(int32_t)];
+
+hipError_t sort_scratch(void** ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        // once per device, with that device current
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 size_t sort_workspace_bytes(const Dims& d) {
     // counts (then earlier-tile prefixes) [seg][tile][nb], totals [seg][nb]

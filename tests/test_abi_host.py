@@ -332,3 +332,17 @@ def test_c_named_wrappers_check_buffer_sizes_and_dtypes():
                              torch.zeros(n, dtype=torch.float32), torch.zeros(n), None)
     with pytest.raises(ValueError, match="dv"):
         lsh.lsh_attention_bwd(qk, qk, qk, qk, None, s, qk, None, None)
+
+
+def test_sort_noalloc_refuses_on_host(lib):
+    """lsh_sort_noalloc checks the shape, the pointers and its 16 MiB static
+    scratch's limit on the host, before any HIP call."""
+    fake = ctypes.c_void_p(0x1000)
+    big = _shape(B=1, H=1, n_hashes=8, L=1 << 20, chunk_len=64, n_buckets=4096)
+    assert lib.lsh_sort_noalloc(fake, ctypes.byref(big), fake, fake, None) == -2
+    assert "static scratch" in lsh.lsh_last_error()
+    s = _shape()
+    assert lib.lsh_sort_noalloc(None, ctypes.byref(s), fake, fake, None) == -1
+    assert lib.lsh_sort_noalloc(fake, ctypes.byref(s), ctypes.c_void_p(0x1008), fake, None) == -1
+    assert lib.lsh_sort_noalloc(fake, ctypes.byref(_shape(d=96)), fake, fake, None) == -1
+    assert lib.lsh_sort_noalloc(None, ctypes.byref(_shape(L=0)), None, None, None) == 0
