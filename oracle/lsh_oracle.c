@@ -52,6 +52,17 @@
  * key.
  * Variant (per_head_r = 1): R is [H, n_hashes, d, n_buckets/2] and head h
  * hashes with R[h] in every batch.
+ * Ablation Q1 (separate queries and keys): [WALKTHRU] "1 LSH Attention"
+ * describes the bucket-sorted attention matrix before Q = K -- queries and
+ * keys each hashed and sorted by bucket, so a bucket's query and key counts
+ * need not match and a bucket may hold queries but no keys. Reading: round r
+ * hashes queries and keys with the same R_r; queries and keys are sorted
+ * separately by (bucket, position); query chunk c sees the keys of key
+ * chunks c-1 and c; a key counts when its bucket equals the query's (and,
+ * causal, its position is not later); no self penalty (it exists only
+ * because a shared vector would attend to itself); a window with no such key
+ * gives that round lse = -inf and a zero output, so the round takes no
+ * weight, and a query with no key in any round outputs zero.
  * F1, the chunked feed-forward ([WALKTHRU] "3 分塊"; [SCHOLAR] "Reformerを
  * 用いた結果" for d_model 1024 and d_ff 4096): reading -- the Transformer's
  * position-wise feed-forward relu(x W1^T + b1) W2^T + b2, rows processed a
@@ -271,6 +282,8 @@ int oracle_attend(const double *x, const double *v, int64_t L, int d,
 /*   inv  [n_hashes, L]     per-round slot of each position                  */
 /*   toks list of positions to compute (NULL: all L)                         */
 /*   out  [L, d]            out, by original position                        */
+/* A round whose lse is -inf (no key, separate queries and keys only) takes  */
+/* weight 0; with no round left the output row is zero.                      */
 /* ------------------------------------------------------------------------ */
 int oracle_combine(const double *o, const double *lse, const int32_t *inv,
                    int n_hashes, int64_t L, int d, const int64_t *toks,
@@ -286,11 +299,17 @@ int oracle_combine(const double *o, const double *lse, const int32_t *inv,
             const double l = lse[(int64_t)r * L + inv[(int64_t)r * L + i]];
             if (l > mx) mx = l;
         }
+        double *oi = out + i * d;
+        if (mx == -INFINITY) {
+            /* no round has a key (only with separate queries and keys): an
+               empty softmax, read as a zero output */
+            for (int k = 0; k < d; ++k) oi[k] = 0.0;
+            continue;
+        }
         double sum = 0.0;
         for (int r = 0; r < n_hashes; ++r)
             sum += exp(lse[(int64_t)r * L + inv[(int64_t)r * L + i]] - mx);
         const double z = mx + log(sum);
-        double *oi = out + i * d;
         for (int k = 0; k < d; ++k) oi[k] = 0.0;
         for (int r = 0; r < n_hashes; ++r) {
             const int64_t s = inv[(int64_t)r * L + i];
@@ -368,6 +387,152 @@ int oracle_forward(const double *qk, const double *v, const double *R,
         free(mg);
         free(ls);
         free(os);
+        if (rc) return rc;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Q1 (ablation). Chunked attention of one segment with separate queries     */
+/* and keys ([WALKTHRU] "1 LSH Attention": the bucket-sorted matrix before   */
+/* Q = K, where a bucket may hold queries but no keys).                      */
+/*                                                                           */
+/*   q, k, v      [L, d] by original position                                */
+/*   bucket_q/_k  [L]    this round's bucket of each query / key position    */
+/*   perm_q/_k    [L]    the queries' / keys' sorted order (from O2)          */
+/*   slots        query slots to compute (NULL: all L)                       */
+/*   o   [L, d]   out, by query slot; lse [L] out, by query slot (-inf and a */
+/*                zero row when no key of the window counts)                 */
+/* ------------------------------------------------------------------------ */
+int oracle_attend_qk(const double *q, const double *k, const double *v, int64_t L, int d,
+                     const int32_t *bucket_q, const int32_t *bucket_k,
+                     const int32_t *perm_q, const int32_t *perm_k, int m, int causal,
+                     const int64_t *slots, int64_t n_slots, double *o, double *lse)
+{
+    if (L < 0 || d < 1 || m < 1 || (L % m) != 0) return -1;
+    const int64_t n_q = slots ? n_slots : L;
+    const double scale = 1.0 / sqrt((double)d);
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *score = (double *)malloc(sizeof(double) * 2 * (size_t)m);
+        int *valid = (int *)malloc(sizeof(int) * 2 * (size_t)m);
+        if (!score || !valid) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 64)
+        for (int64_t qi = 0; qi < n_q; ++qi) {
+            if (!score || !valid) continue;
+            const int64_t s = slots ? slots[qi] : qi;
+            const int64_t i = perm_q[s];
+            const int64_t c = s / m;
+            /* the same chunk and the previous one, in the keys' sorted order */
+            const int64_t t0 = (c > 0) ? (c - 1) * m : 0;
+            const int64_t t1 = (c + 1) * m;
+            const double *qv = q + i * d;
+            double mx = -INFINITY;
+            int any = 0;
+            for (int64_t t = t0; t < t1; ++t) {
+                const int64_t j = perm_k[t];
+                const int ok = (bucket_k[j] == bucket_q[i]) && (!causal || j <= i);
+                valid[t - t0] = ok;
+                if (!ok) continue;
+                const double *kv = k + j * d;
+                double dot = 0.0;
+                for (int e = 0; e < d; ++e) dot += qv[e] * kv[e];
+                const double sc = dot * scale;
+                score[t - t0] = sc;
+                if (!any || sc > mx) mx = sc;
+                any = 1;
+            }
+            double *os = o + s * d;
+            for (int e = 0; e < d; ++e) os[e] = 0.0;
+            if (!any) {
+                lse[s] = -INFINITY;
+                continue;
+            }
+            double sum = 0.0;
+            for (int64_t t = t0; t < t1; ++t)
+                if (valid[t - t0]) sum += exp(score[t - t0] - mx);
+            const double l = mx + log(sum);
+            lse[s] = l;
+            for (int64_t t = t0; t < t1; ++t) {
+                if (!valid[t - t0]) continue;
+                const double w = exp(score[t - t0] - l);
+                const double *vj = v + (int64_t)perm_k[t] * d;
+                for (int e = 0; e < d; ++e) os[e] += w * vj[e];
+            }
+        }
+        free(score);
+        free(valid);
+    }
+    return failed ? -2 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Q1 forward over [B, H]: O1 on the queries and on the keys (the same R),    */
+/* O2 on each, chunked attention with separate queries and keys, O5 through  */
+/* the queries' inverse order.                                               */
+/*                                                                           */
+/*   q, k, v  [B, H, L, d];  R as in oracle_forward;  out [B, H, L, d]        */
+/*   optional outputs (each may be NULL), [B, H, n_hashes, L]: buckets_q,    */
+/*   buckets_k, margin_q, margin_k, perm_q, perm_k, inv_q, lse (by query      */
+/*   slot); o_sorted [B, H, n_hashes, L, d] by query slot                    */
+/* ------------------------------------------------------------------------ */
+int oracle_forward_qk(const double *q, const double *k, const double *v, const double *R,
+                      int B, int H, int64_t L, int d, int n_buckets, int n_hashes,
+                      int chunk_len, int causal, double *out, int32_t *bq_out,
+                      int32_t *bk_out, double *mq_out, double *mk_out, int32_t *pq_out,
+                      int32_t *pk_out, int32_t *iq_out, double *o_sorted_out,
+                      double *lse_out, int per_head_r)
+{
+    if (B < 0 || H < 0 || L < 0 || d < 1 || n_hashes < 1 || chunk_len < 1 ||
+        n_buckets < 2 || (n_buckets % 2) != 0 || (L % chunk_len) != 0)
+        return -1;
+    const int64_t seg = (int64_t)n_hashes * L;
+    const size_t n1 = (size_t)(seg ? seg : 1);
+    for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
+        const double *qq = q + bh * L * d;
+        const double *kk = k + bh * L * d;
+        const double *vv = v + bh * L * d;
+        int32_t *bq = (int32_t *)malloc(sizeof(int32_t) * n1);
+        int32_t *bk = (int32_t *)malloc(sizeof(int32_t) * n1);
+        double *mq = (double *)malloc(sizeof(double) * n1);
+        double *mk = (double *)malloc(sizeof(double) * n1);
+        int32_t *pq = (int32_t *)malloc(sizeof(int32_t) * n1);
+        int32_t *iq = (int32_t *)malloc(sizeof(int32_t) * n1);
+        int32_t *pk = (int32_t *)malloc(sizeof(int32_t) * n1);
+        int32_t *ik = (int32_t *)malloc(sizeof(int32_t) * n1);
+        double *ls = (double *)malloc(sizeof(double) * n1);
+        double *os = (double *)malloc(sizeof(double) * (size_t)(seg ? seg * d : 1));
+        int rc = (bq && bk && mq && mk && pq && iq && pk && ik && ls && os) ? 0 : -2;
+        const double *Rh = head_rotations(R, bh, H, n_hashes, d, n_buckets, per_head_r);
+        if (!rc) rc = oracle_hash(qq, L, d, Rh, n_hashes, n_buckets, bq, mq);
+        if (!rc) rc = oracle_hash(kk, L, d, Rh, n_hashes, n_buckets, bk, mk);
+        for (int r = 0; !rc && r < n_hashes; ++r) {
+            rc = oracle_sort(bq + r * L, L, pq + r * L, iq + r * L);
+            if (!rc) rc = oracle_sort(bk + r * L, L, pk + r * L, ik + r * L);
+        }
+        for (int r = 0; !rc && r < n_hashes; ++r)
+            rc = oracle_attend_qk(qq, kk, vv, L, d, bq + r * L, bk + r * L, pq + r * L,
+                                  pk + r * L, chunk_len, causal, NULL, 0, os + r * L * d,
+                                  ls + r * L);
+        if (!rc) rc = oracle_combine(os, ls, iq, n_hashes, L, d, NULL, 0, out + bh * L * d);
+        if (!rc) {
+            const size_t ni = sizeof(int32_t) * (size_t)seg, nd = sizeof(double) * (size_t)seg;
+            if (bq_out) memcpy(bq_out + bh * seg, bq, ni);
+            if (bk_out) memcpy(bk_out + bh * seg, bk, ni);
+            if (mq_out) memcpy(mq_out + bh * seg, mq, nd);
+            if (mk_out) memcpy(mk_out + bh * seg, mk, nd);
+            if (pq_out) memcpy(pq_out + bh * seg, pq, ni);
+            if (pk_out) memcpy(pk_out + bh * seg, pk, ni);
+            if (iq_out) memcpy(iq_out + bh * seg, iq, ni);
+            if (lse_out) memcpy(lse_out + bh * seg, ls, nd);
+            if (o_sorted_out) memcpy(o_sorted_out + bh * seg * d, os, nd * (size_t)d);
+        }
+        free(bq); free(bk); free(mq); free(mk); free(pq); free(iq); free(pk); free(ik);
+        free(ls); free(os);
         if (rc) return rc;
     }
     return 0;

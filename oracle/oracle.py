@@ -18,6 +18,7 @@ their sources are documented in ``lsh_oracle.c``:
               token vectors, split into heads
   backward -- G1, gradients of the forward for a given output gradient
   ffn      -- F1, the chunked feed-forward relu(x W1^T + b1) W2^T + b2
+  attend_qk, forward_qk -- Q1, the ablation with separate queries and keys
 """
 from __future__ import annotations
 
@@ -79,11 +80,20 @@ def _load():
                                              ctypes.c_int64, _f64p, _f64p]
         lib.oracle_ffn.argtypes = [_f64p, ctypes.c_int64, ctypes.c_int, _f64p, _f64p, _f64p,
                                    _f64p, ctypes.c_int, ctypes.c_int64, _f64p]
+        lib.oracle_attend_qk.argtypes = [_f64p, _f64p, _f64p, ctypes.c_int64, ctypes.c_int,
+                                         _i32p, _i32p, _i32p, _i32p, ctypes.c_int, ctypes.c_int,
+                                         _i64p, ctypes.c_int64, _f64p, _f64p]
+        lib.oracle_forward_qk.argtypes = [_f64p, _f64p, _f64p, _f64p, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_int, _f64p,
+                                          _i32p, _i32p, _f64p, _f64p, _i32p, _i32p, _i32p,
+                                          _f64p, _f64p, ctypes.c_int]
         lib.oracle_threads.argtypes = []
         lib.oracle_threads.restype = ctypes.c_int
         for fn in (lib.oracle_hash, lib.oracle_sort, lib.oracle_attend, lib.oracle_combine,
                    lib.oracle_forward, lib.oracle_project, lib.oracle_backward,
-                   lib.oracle_backward_rows, lib.oracle_ffn):
+                   lib.oracle_backward_rows, lib.oracle_ffn, lib.oracle_attend_qk,
+                   lib.oracle_forward_qk):
             fn.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -304,3 +314,54 @@ def ffn(x, w1, b1, w2, b2, chunk: int):
     _check(_load().oracle_ffn(_p(x, _f64p), rows, dm, _p(w1, _f64p), _p(b1, _f64p),
                               _p(w2, _f64p), _p(b2, _f64p), dff, chunk, _p(out, _f64p)), "ffn")
     return out
+
+
+def attend_qk(q, k, v, bucket_q, bucket_k, perm_q, perm_k, chunk_len: int, causal: bool,
+              slots=None):
+    """Q1 for one round with separate queries and keys. q, k, v: [L, d];
+    bucket_q/_k, perm_q/_k: [L]. Returns (o [L, d], lse [L]) by query slot; a
+    query whose window holds no key of its bucket gets lse -inf and a zero row."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    L, d = q.shape
+    o = np.full((L, d), np.nan)
+    lse = np.full(L, np.nan)
+    sl = None if slots is None else np.ascontiguousarray(np.asarray(slots, dtype=np.int64))
+    _check(_load().oracle_attend_qk(_p(q, _f64p), _p(k, _f64p), _p(v, _f64p), L, d,
+                                    _p(_i32(bucket_q), _i32p), _p(_i32(bucket_k), _i32p),
+                                    _p(_i32(perm_q), _i32p), _p(_i32(perm_k), _i32p),
+                                    chunk_len, int(bool(causal)), _p(sl, _i64p),
+                                    0 if sl is None else sl.shape[0], _p(o, _f64p),
+                                    _p(lse, _f64p)), "attend_qk")
+    return o, lse
+
+
+def forward_qk(q, k, v, R, n_buckets: int, chunk_len: int, causal: bool,
+               return_all: bool = False):
+    """Q1 over every (batch, head): queries and keys hashed with the same R,
+    sorted separately, chunked attention, combine. q, k, v: [B, H, L, d];
+    R as in forward. Returns out [B, H, L, d]; with ``return_all`` also a dict
+    (buckets_q, buckets_k, margin_q, margin_k, perm_q, perm_k, inv_q,
+    o_sorted and lse by query slot)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, L, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k and v must have the same shape")
+    R, nh, per_head = _rotations(R, H, d, n_buckets)
+    out = np.empty((B, H, L, d))
+    extra = {}
+    if return_all:
+        i32 = lambda: np.empty((B, H, nh, L), np.int32)
+        f64 = lambda: np.empty((B, H, nh, L))
+        extra = dict(buckets_q=i32(), buckets_k=i32(), margin_q=f64(), margin_k=f64(),
+                     perm_q=i32(), perm_k=i32(), inv_q=i32(), lse=f64(),
+                     o_sorted=np.empty((B, H, nh, L, d)))
+    g = extra.get
+    _check(_load().oracle_forward_qk(_p(q, _f64p), _p(k, _f64p), _p(v, _f64p), _p(R, _f64p),
+                                     B, H, L, d, n_buckets, nh, chunk_len, int(bool(causal)),
+                                     _p(out, _f64p), _p(g("buckets_q"), _i32p),
+                                     _p(g("buckets_k"), _i32p), _p(g("margin_q"), _f64p),
+                                     _p(g("margin_k"), _f64p), _p(g("perm_q"), _i32p),
+                                     _p(g("perm_k"), _i32p), _p(g("inv_q"), _i32p),
+                                     _p(g("o_sorted"), _f64p), _p(g("lse"), _f64p), per_head),
+           "forward_qk")
+    return (out, extra) if return_all else out

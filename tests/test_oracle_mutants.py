@@ -83,6 +83,17 @@ MUTANTS = {
                                     "(void)0;"),
     "backward_rows_query_side_only": ("if (row[i] < 0 && row[j] < 0) continue;",
                                       "if (row[i] < 0) continue;"),
+    # separate queries and keys
+    "qk_keys_in_query_order": ("const int64_t j = perm_k[t];", "const int64_t j = perm_q[t];"),
+    "qk_self_penalty": ("const double sc = dot * scale;\n                score[t - t0] = sc;",
+                        "const double sc = dot * scale - (j == i ? ORACLE_SELF_PENALTY : 0.0);\n"
+                        "                score[t - t0] = sc;"),
+    "qk_query_buckets_for_keys": ("(bucket_k[j] == bucket_q[i])", "(bucket_q[j] == bucket_q[i])"),
+    "qk_empty_round_lse_zero": ("lse[s] = -INFINITY;", "lse[s] = 0.0;"),
+    "qk_keys_hashed_as_queries": ("rc = oracle_hash(kk, L, d, Rh, n_hashes, n_buckets, bk, mk);",
+                                  "rc = oracle_hash(qq, L, d, Rh, n_hashes, n_buckets, bk, mk);"),
+    "qk_combined_through_key_order": ("oracle_combine(os, ls, iq,", "oracle_combine(os, ls, ik,"),
+    "combine_empty_row_not_zero": ("if (mx == -INFINITY) {", "if (0) {"),
 }
 
 

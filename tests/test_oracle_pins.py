@@ -631,3 +631,86 @@ def test_ffn_relu_regions(oracle_mod):
     xp, w1p, b1p = np.abs(x), np.abs(w1), np.abs(rng.standard_normal(12))
     on = oracle_mod.ffn(xp, w1p, b1p, w2, b2, 4)
     np.testing.assert_allclose(on, xp @ (w2 @ w1p).T + w2 @ b1p + b2, rtol=1e-12, atol=1e-12)
+
+
+
+# --------------------------------------------------------------------------- Q1 separate Q/K
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_separate_qk_hand_built_windows(oracle_mod, causal):
+    """Separate queries and keys on a hand-derived 8-token case: each side
+    sorted on its own, query chunk c against key chunks c-1 and c, bucket and
+    causal masks, no self penalty, and a window without a key of the query's
+    bucket (position 0, causal) giving a zero row and lse -inf."""
+    g = _golden("separate_qk_window_cases.json")
+    bq, bk = np.array(g["bucket_q"]), np.array(g["bucket_k"])
+    q = np.zeros((8, 8))
+    k = np.zeros((8, 8))
+    q[:, 0] = np.where(bq == 0, 1.0, -1.0)
+    k[:, 0] = np.where(bk == 0, 1.0, -1.0)
+    R = np.zeros((1, 8, 1))
+    R[0, 0, 0] = 1.0
+    v = np.eye(8)
+    out, ex = oracle_mod.forward_qk(q[None, None], k[None, None], v[None, None], R, 2, 2,
+                                    causal, return_all=True)
+    assert ex["buckets_q"][0, 0, 0].tolist() == g["bucket_q"]
+    assert ex["buckets_k"][0, 0, 0].tolist() == g["bucket_k"]
+    assert ex["perm_q"][0, 0, 0].tolist() == g["perm_q"]
+    assert ex["perm_k"][0, 0, 0].tolist() == g["perm_k"]
+    keys = g["keys"]["causal" if causal else "non_causal"]
+    for pos, ks in keys.items():
+        want = np.zeros(8)
+        want[ks] = 1.0 / len(ks) if ks else 0.0
+        np.testing.assert_allclose(out[0, 0, int(pos)], want, rtol=1e-12, atol=1e-12)
+        slot = ex["inv_q"][0, 0, 0, int(pos)]
+        assert np.isneginf(ex["lse"][0, 0, 0, slot]) == (not ks)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("m", [4, 8, 32])
+def test_separate_qk_matches_multiset_closed_form(oracle_mod, causal, m):
+    """Separate queries and keys against a brute force that takes the buckets
+    from numpy's argmax and enumerates every (query, key) pair's windows from
+    numpy's stable argsort of each side; m = 32 is one chunk, i.e. dense
+    attention over same-bucket pairs."""
+    rng = np.random.default_rng(61 + m)
+    L, d, nb, nh = 32, 8, 4, 3
+    q = rng.standard_normal((L, d))
+    k = rng.standard_normal((L, d))
+    v = rng.standard_normal((L, d))
+    R = rng.standard_normal((nh, d, nb // 2))
+    out = oracle_mod.forward_qk(q[None, None], k[None, None], v[None, None], R, nb, m, causal)
+    bq, bk = brute.angular_buckets(q, R), brute.angular_buckets(k, R)
+    ref = brute.multiset_closed_form_qk(q, k, v, bq, bk, m, causal)
+    np.testing.assert_allclose(out[0, 0], ref, rtol=1e-11, atol=1e-12)
+    # the case must exercise queries that find no key in any round
+    if causal and m == 4:
+        assert (np.abs(ref).sum(1) == 0).any()
+
+
+def test_separate_qk_invariants(oracle_mod):
+    """Rows with a hit are convex combinations of V, rows without are zero;
+    duplicating every round changes nothing; the causal first position sees
+    its own key exactly when the buckets agree in some round."""
+    rng = np.random.default_rng(64)
+    B, H, L, d, nb, nh, m = 1, 2, 64, 8, 8, 3, 8
+    q = rng.standard_normal((B, H, L, d))
+    k = rng.standard_normal((B, H, L, d))
+    v = rng.standard_normal((B, H, L, d))
+    R = rng.standard_normal((nh, d, nb // 2))
+    out, ex = oracle_mod.forward_qk(q, k, v, R, nb, m, True, return_all=True)
+    lse_by_pos = np.take_along_axis(ex["lse"], ex["inv_q"].astype(np.int64), axis=3)
+    empty = np.isneginf(lse_by_pos).all(axis=2)
+    assert empty.any() and not empty.all()
+    assert np.all(out[empty] == 0)
+    lo = v.min(axis=2, keepdims=True)
+    hi = v.max(axis=2, keepdims=True)
+    inside = (out >= lo - 1e-10) & (out <= hi + 1e-10)
+    assert inside[~empty].all()
+    dup = oracle_mod.forward_qk(q, k, v, np.concatenate([R, R]), nb, m, True)
+    np.testing.assert_allclose(dup, out, rtol=1e-10, atol=1e-12)
+    same0 = (ex["buckets_q"][:, :, :, 0] == ex["buckets_k"][:, :, :, 0]).any(axis=2)
+    for b in range(B):
+        for h in range(H):
+            want = v[b, h, 0] if same0[b, h] else np.zeros(d)
+            np.testing.assert_allclose(out[b, h, 0], want, rtol=1e-12, atol=1e-14)
