@@ -4,6 +4,7 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-
 python bench.py --sweep [--dense]     one line per workload (length sweep and the rest)
 python bench.py --project             input projections (d_model 1024) and the forward from x
 python bench.py --train               training forward and backward
+python bench.py --separate-qk         the separate-queries-and-keys ablation
 
 A step is one lsh_attention_fwd (hash -> sort -> chunk attention -> combine)
 over one batch of synthetic input already resident in HBM. The default
@@ -158,6 +159,29 @@ def measure(lsh, torch, w, steps, warmup, key_norm=False, per_head_r=False):
     kernels = {k: float(np.mean(x)) for k, x in acc.items()}
     return {"ms_per_step": ms_per_step, "wall": wall, "refined": refined, "kernels": kernels,
             "inputs": (qk, v, R), "tensors": (qk_t, v_t)}
+
+
+def measure_separate(lsh, torch, w, steps, warmup):
+    """lsh_attention_fwd_qk (queries and keys hashed and sorted separately) at
+    the workload's shape, next to the shared forward on the same q as qk."""
+    import workloads
+
+    dev = torch.device("cuda:0")
+    q, k, v, R = workloads.make_separate_inputs(w)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q_t, k_t, v_t = (torch.from_numpy(a).to(dev, dt) for a in (q, k, v))
+    R_t = torch.from_numpy(R).to(dev)
+    shape = lsh.shape_of(q_t, w.n_buckets, w.n_hashes, w.chunk_len, w.causal)
+    out = torch.empty_like(q_t)
+    ws = torch.empty(lsh.lsh_workspace_size("fwd_qk", shape), dtype=torch.uint8, device=dev)
+    sep_ms = _timed_ms(torch, lambda: lsh.lsh_attention_fwd_qk(q_t, k_t, v_t, R_t, shape, out,
+                                                               ws), steps, warmup)
+    ws2 = torch.empty(lsh.lsh_workspace_size("fwd", shape), dtype=torch.uint8, device=dev)
+    shared_ms = _timed_ms(torch, lambda: lsh.lsh_attention_fwd(q_t, v_t, R_t, shape, out, ws2),
+                          steps, warmup)
+    return {"variant": "separate_qk", "workload": w.name, "config": w.describe(),
+            "ms_per_step": sep_ms, "tokens_per_s": w.B * w.L / (sep_ms / 1e3),
+            "shared_qk_ms": shared_ms}
 
 
 def measure_projection(lsh, torch, w, steps, warmup, d_model=1024, dense=False):
@@ -429,6 +453,9 @@ def main() -> int:
                     help="time the chunked feed-forward (64K rows, 1024 -> 4096 -> 1024, bf16)")
     ap.add_argument("--ffn-chunk", type=int, default=16384,
                     help="rows per chunk of the feed-forward (with --ffn)")
+    ap.add_argument("--separate-qk", action="store_true",
+                    help="time the separate-queries-and-keys ablation (lsh_attention_fwd_qk) "
+                         "at the workload's shape")
     ap.add_argument("--per-head-r", action="store_true",
                     help="time the per-head rotations variant (R [H, nh, d, nb/2]); combines "
                          "with --key-norm and --train")
@@ -479,6 +506,11 @@ def main() -> int:
     if args.ffn:
         print(json.dumps(measure_ffn(lsh, torch, min(args.steps, 10), args.warmup,
                                      chunk=args.ffn_chunk, dense=args.dense)), flush=True)
+        return 0
+
+    if args.separate_qk:
+        print(json.dumps(measure_separate(lsh, torch, workloads.WORKLOADS[
+            args.workload or workloads.HEADLINE], args.steps, args.warmup)), flush=True)
         return 0
 
     if args.key_norm or args.per_head_r:

@@ -106,8 +106,8 @@ typedef struct lsh_shape {
     int32_t flags;
 } lsh_shape_t;
 
-/* Bytes of workspace needed by `stage` ("hash", "sort", "fwd", "fwd_x",
- * "state" or "bwd") for `shape`. "state" is the size of the buffer
+/* Bytes of workspace needed by `stage` ("hash", "sort", "fwd", "fwd_qk",
+ * "fwd_x", "state" or "bwd") for `shape`. "state" is the size of the buffer
  * lsh_attention_fwd_train fills for lsh_attention_bwd. LSH_KEY_NORM adds
  * 4 bytes per token (B*H*L) to "fwd", "fwd_x" and "bwd".
  * Errors: an unknown or NULL stage, or an invalid shape, returns 0 and sets
@@ -170,12 +170,33 @@ int lsh_sort_noalloc(const int32_t *buckets, const lsh_shape_t *shape, int32_t *
 int lsh_chunk_attend(const void *qk, const void *v, const int32_t *buckets, const int32_t *perm,
                      const lsh_shape_t *shape, float *o_sorted, float *lse_sorted, void *stream);
 
+/* Steps 3+4 with separate queries and keys (an ablation). The walkthrough's
+ * "1 LSH Attention" shows the bucket-sorted attention matrix before it sets
+ * Q = K: queries and keys each hashed and sorted by bucket, so a bucket's
+ * query and key counts need not match and a bucket may hold queries but no
+ * keys. Here query slot s (chunk c = s / m of the queries' order perm_q)
+ * sees the key slots of chunks c-1 and c of the keys' order perm_k; key
+ * position j counts for query position i when buckets_k(j) == buckets_q(i)
+ * and, if causal, j <= i; the score is (q_i . k_j) / sqrt(d) with no self
+ * penalty. A query with no key that counts gets a zero row and lse -inf.
+ *   q, k, v                [B,H,L,d] shape->dtype
+ *   buckets_q, buckets_k   [B,H,n_hashes,L] int32 (lsh_hash of q and of k)
+ *   perm_q, perm_k         [B,H,n_hashes,L] int32 (lsh_sort of each)
+ *   o_sorted, lse_sorted   by query slot, as for lsh_chunk_attend
+ * LSH_KEY_NORM is refused (LSH_ERR_ARG): it belongs to shared vectors. */
+int lsh_chunk_attend_qk(const void *q, const void *k, const void *v, const int32_t *buckets_q,
+                        const int32_t *buckets_k, const int32_t *perm_q, const int32_t *perm_k,
+                        const lsh_shape_t *shape, float *o_sorted, float *lse_sorted,
+                        void *stream);
+
 /* Step 5 -- un-sort and combine the rounds (walkthrough "1 LSH Attention":
  * multi-round hashing attends to the union of the rounds' sets). For each
  * position i: l_r = lse_sorted[r, inv_r[i]], Z = logsumexp_r l_r,
  * out_i = sum_r exp(l_r - Z) * o_sorted[r, inv_r[i]].
  *   o_sorted [B,H,n_hashes,L,d] f32   lse_sorted [B,H,n_hashes,L] f32
- *   inv      [B,H,n_hashes,L] int32   out [B,H,L,d] shape->dtype (out) */
+ *   inv      [B,H,n_hashes,L] int32   out [B,H,L,d] shape->dtype (out)
+ * A round whose lse is -inf (no key, separate queries and keys only) takes
+ * weight 0; a position with no other round gets a zero row. */
 int lsh_unsort_combine(const float *o_sorted, const float *lse_sorted, const int32_t *inv,
                        const lsh_shape_t *shape, void *out, void *stream);
 
@@ -184,6 +205,17 @@ int lsh_unsort_combine(const float *o_sorted, const float *lse_sorted, const int
  * hash stage's re-decided count, as in lsh_hash). */
 int lsh_attention_fwd(const void *qk, const void *v, const float *R, const lsh_shape_t *shape,
                       void *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Whole forward with separate queries and keys (the ablation of
+ * lsh_chunk_attend_qk): q and k are hashed with the same R and sorted on
+ * their own, then attended and combined through the queries' order. out
+ * rows of queries that find no key in any round are zero.
+ *   q, k, v [B,H,L,d] shape->dtype; R as for lsh_hash; out [B,H,L,d]
+ *   ws      at least lsh_workspace_size("fwd_qk") bytes
+ * LSH_KEY_NORM is refused (LSH_ERR_ARG). */
+int lsh_attention_fwd_qk(const void *q, const void *k, const void *v, const float *R,
+                         const lsh_shape_t *shape, void *out, void *ws, size_t ws_bytes,
+                         void *stream);
 
 /* Diagnostic twin of lsh_attention_fwd: the same launches, with a HIP event
  * recorded after each kernel. It waits for the stream, then writes each

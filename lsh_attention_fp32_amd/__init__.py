@@ -8,7 +8,8 @@ no other implementation to fall back to.
 
 Low-level functions keep the C names and argument order (tensors in place of
 pointers): ``lsh_workspace_size``, ``lsh_hash``, ``lsh_sort``, ``lsh_sort_noalloc``,
-``lsh_chunk_attend``, ``lsh_unsort_combine``, ``lsh_attention_fwd``,
+``lsh_chunk_attend``, ``lsh_chunk_attend_qk``, ``lsh_unsort_combine``,
+``lsh_attention_fwd``, ``lsh_attention_fwd_qk``,
 ``lsh_attention_fwd_timed``, ``lsh_qkv_project``, ``lsh_attention_fwd_x``,
 ``lsh_attention_fwd_train``, ``lsh_attention_bwd``. The allocating helpers
 ``hash``, ``sort``, ``chunk_attend``, ``unsort_combine``, ``attention_fwd``,
@@ -27,9 +28,11 @@ from ._binding import (  # noqa: F401
     Shape,
     attention_bwd,
     attention_fwd,
+    attention_fwd_qk,
     attention_fwd_train,
     attention_fwd_x,
     chunk_attend,
+    chunk_attend_qk,
     ffn,
     hash,
     library_path,
@@ -40,7 +43,9 @@ from ._binding import (  # noqa: F401
     lsh_attention_bwd,
     lsh_attention_fwd_train,
     lsh_attention_fwd_x,
+    lsh_attention_fwd_qk,
     lsh_chunk_attend,
+    lsh_chunk_attend_qk,
     lsh_ffn_chunked,
     lsh_ffn_workspace_size,
     lsh_hash,

@@ -56,6 +56,8 @@ def load_library():
     lib.lsh_sort.argtypes = [vp, sp, vp, vp, vp, sz, vp]
     lib.lsh_sort_noalloc.argtypes = [vp, sp, vp, vp, vp]
     lib.lsh_chunk_attend.argtypes = [vp, vp, vp, vp, sp, vp, vp, vp]
+    lib.lsh_chunk_attend_qk.argtypes = [vp, vp, vp, vp, vp, vp, vp, sp, vp, vp, vp]
+    lib.lsh_attention_fwd_qk.argtypes = [vp, vp, vp, vp, sp, vp, vp, sz, vp]
     lib.lsh_unsort_combine.argtypes = [vp, vp, vp, sp, vp, vp]
     lib.lsh_attention_fwd.argtypes = [vp, vp, vp, sp, vp, vp, sz, vp]
     lib.lsh_attention_fwd_timed.argtypes = [vp, vp, vp, sp, vp, vp, sz, vp,
@@ -71,6 +73,7 @@ def load_library():
     lib.lsh_ffn_workspace_size.restype = sz
     lib.lsh_ffn_chunked.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp, vp, sz, vp]
     for name in ("lsh_ffn_chunked", "lsh_hash", "lsh_sort", "lsh_sort_noalloc", "lsh_chunk_attend",
+                 "lsh_chunk_attend_qk", "lsh_attention_fwd_qk",
                  "lsh_unsort_combine", "lsh_attention_fwd", "lsh_attention_fwd_timed",
                  "lsh_qkv_project", "lsh_attention_fwd_x", "lsh_attention_fwd_train",
                  "lsh_attention_bwd"):
@@ -255,6 +258,31 @@ def lsh_chunk_attend(qk, v, buckets, perm, shape: Shape, o_sorted, lse_sorted, s
                                            _stream(stream)), fn)
 
 
+def lsh_chunk_attend_qk(q, k, v, buckets_q, buckets_k, perm_q, perm_k, shape: Shape, o_sorted,
+                        lse_sorted, stream=None) -> None:
+    fn = "lsh_chunk_attend_qk"
+    _need_qkvr(fn, shape, q, v, with_r=False, with_out=False)
+    _need(fn, "k", k, _io(shape), _sizes(shape)[0])
+    n = _sizes(shape)[1]
+    for what, t in (("buckets_q", buckets_q), ("buckets_k", buckets_k), ("perm_q", perm_q),
+                    ("perm_k", perm_k)):
+        _need(fn, what, t, torch.int32, n)
+    _need(fn, "o_sorted", o_sorted, torch.float32, n * shape.d)
+    _need(fn, "lse_sorted", lse_sorted, torch.float32, n)
+    _check(load_library().lsh_chunk_attend_qk(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(buckets_q), _ptr(buckets_k), _ptr(perm_q), _ptr(perm_k),
+        ctypes.byref(shape), _ptr(o_sorted), _ptr(lse_sorted), _stream(stream)), fn)
+
+
+def lsh_attention_fwd_qk(q, k, v, R, shape: Shape, out, ws, stream=None) -> None:
+    fn = "lsh_attention_fwd_qk"
+    _need_qkvr(fn, shape, q, v, R, out)
+    _need(fn, "k", k, _io(shape), _sizes(shape)[0])
+    _check(load_library().lsh_attention_fwd_qk(_ptr(q), _ptr(k), _ptr(v), _ptr(R),
+                                               ctypes.byref(shape), _ptr(out), _ptr(ws),
+                                               _nbytes(ws), _stream(stream)), fn)
+
+
 def lsh_unsort_combine(o_sorted, lse_sorted, inv, shape: Shape, out, stream=None) -> None:
     fn = "lsh_unsort_combine"
     n = _sizes(shape)[1]
@@ -424,6 +452,36 @@ def chunk_attend(qk, v, buckets, perm, n_buckets: int, chunk_len: int, causal: b
     lse = torch.empty(_rounds_shape(shape), dtype=torch.float32, device=qk.device)
     lsh_chunk_attend(qk, v, buckets, perm, shape, o, lse, stream)
     return o, lse
+
+
+def chunk_attend_qk(q, k, v, buckets_q, buckets_k, perm_q, perm_k, n_buckets: int,
+                    chunk_len: int, causal: bool, stream=None):
+    """Separate queries and keys: returns (o_sorted, lse_sorted) by query slot,
+    [B,H,n_hashes,L,d] and [B,H,n_hashes,L] float32 (lse -inf and a zero row
+    for a query whose window holds no key of its bucket)."""
+    check_like(k, q, "k")
+    check_like(v, q, "v")
+    shape = shape_of(q, n_buckets, buckets_q.shape[2], chunk_len, causal)
+    o = torch.empty(_rounds_shape(shape) + (shape.d,), dtype=torch.float32, device=q.device)
+    lse = torch.empty(_rounds_shape(shape), dtype=torch.float32, device=q.device)
+    lsh_chunk_attend_qk(q, k, v, buckets_q, buckets_k, perm_q, perm_k, shape, o, lse, stream)
+    return o, lse
+
+
+def attention_fwd_qk(q, k, v, R, n_buckets: int, chunk_len: int, causal: bool, ws=None,
+                     out=None, stream=None):
+    """Whole forward with separate queries and keys (the ablation); returns out
+    [B,H,L,d] in q's dtype (zero rows for queries that find no key)."""
+    nh, per_head = check_rotations(R, q, n_buckets)
+    shape = shape_of(q, n_buckets, nh, chunk_len, causal, per_head_r=per_head)
+    check_like(k, q, "k")
+    check_like(v, q, "v")
+    if out is not None:
+        check_like(out, q, "out")
+    out = torch.empty_like(q) if out is None else out
+    ws = _workspace("fwd_qk", shape, q.device) if ws is None else ws
+    lsh_attention_fwd_qk(q, k, v, R, shape, out, ws, stream)
+    return out
 
 
 def unsort_combine(o_sorted, lse_sorted, inv, dtype=torch.bfloat16, stream=None):

@@ -67,10 +67,12 @@ int misaligned(std::initializer_list<const void*> ptrs) {
 }
 
 struct FwdLayout {
-    size_t hash, sort, buckets, perm, inv, lse, o, rn, total;
+    size_t hash, sort, buckets, perm, inv, lse, o, rn, bk, pk, ik, total;
 };
 
-FwdLayout fwd_layout(const Dims& d) {
+// sep: separate queries and keys -- the keys' bucket ids and sorted order
+// follow (and their inverse when the sort cannot pack its keys).
+FwdLayout fwd_layout(const Dims& d, bool sep = false) {
     FwdLayout f;
     const size_t n = (size_t)d.segs * d.L;
     size_t off = 0;
@@ -95,6 +97,12 @@ FwdLayout fwd_layout(const Dims& d) {
     // key normalisation: 1 / |qk| per token, computed once per call
     f.rn = off;
     off += d.key_norm ? align_up(sizeof(float) * (size_t)d.T, 256) : 0;
+    f.bk = off;
+    off += sep ? align_up(sizeof(int32_t) * n, 256) : 0;
+    f.pk = off;
+    off += sep ? align_up(sizeof(int32_t) * n, 256) : 0;
+    f.ik = off;
+    off += sep && !packed ? align_up(sizeof(int32_t) * n, 256) : 0;
     f.total = off;
     return f;
 }
@@ -193,6 +201,48 @@ int run_fwd(const void* qk, const void* v, const float* R, const lsh_shape_t* sh
     return LSH_OK;
 }
 
+// Separate queries and keys: both hashed with the same R and sorted on their
+// own, then the chunk pass with the keys' order in the ring and the queries'
+// order on the query side, then the combine through the queries' order.
+int run_fwd_qk(const void* q, const void* k, const void* v, const float* R,
+               const lsh_shape_t* shape, void* out, void* ws, size_t ws_bytes, hipStream_t st) {
+    const Dims d = make_dims(*shape);
+    const FwdLayout f = fwd_layout(d, true);
+    int rc = check_ws("lsh_attention_fwd_qk", d, ws, ws_bytes, f.total);
+    if (rc) return rc;
+    char* base = (char*)ws;
+    int32_t* bq = (int32_t*)(base + f.buckets);
+    int32_t* pq = (int32_t*)(base + f.perm);
+    int32_t* iq = (int32_t*)(base + f.inv);
+    int32_t* bk = (int32_t*)(base + f.bk);
+    int32_t* pk = (int32_t*)(base + f.pk);
+    int32_t* ik = (int32_t*)(base + f.ik);
+    float* lse = (float*)(base + f.lse);
+    const HashWorkspace hw = carve_hash_workspace(base + f.hash, d);
+    const bool compact = compact_o_sorted(d);
+    const bool packed = compact && packed_sort_keys(d);
+    const OSorted o{base + f.o, compact, hw.vmax};
+    hipError_t e;
+    // the keys' pass folds max|v| (each hash pass clears it first)
+    if ((e = launch_hash(q, R, d, bq, hw, st, nullptr, nullptr, nullptr)) != hipSuccess ||
+        (e = launch_hash(k, R, d, bk, hw, st, nullptr, nullptr, nullptr,
+                         compact ? v : nullptr)) != hipSuccess)
+        return hip_fail(e, "hash");
+    if ((e = launch_sort(bq, d, pq, iq, base + f.sort, st, nullptr, nullptr, nullptr, packed)) !=
+            hipSuccess ||
+        (e = launch_sort(bk, d, pk, ik, base + f.sort, st, nullptr, nullptr, nullptr, packed)) !=
+            hipSuccess)
+        return hip_fail(e, "sort");
+    const SepQK sep{q, bq, pq};
+    if ((e = launch_attend(k, v, bk, pk, d, o, lse, st, nullptr, nullptr, nullptr, packed,
+                           nullptr, &sep)) != hipSuccess)
+        return hip_fail(e, "chunk_attend");
+    if ((e = launch_combine(o, lse, iq, d, out, st, nullptr, nullptr, nullptr)) != hipSuccess)
+        return hip_fail(e, "unsort_combine");
+    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "launch");
+    return LSH_OK;
+}
+
 // One projected tensor ([B,H,L,d] in the I/O dtype), rounded up so the next
 // region stays 256-byte aligned.
 size_t projected_bytes(const Dims& d) {
@@ -232,10 +282,12 @@ size_t lsh_workspace_size(const char* stage, const lsh_shape_t* shape) {
     if (!strcmp(stage, "hash")) return hash_workspace_bytes(d);
     if (!strcmp(stage, "sort")) return sort_workspace_bytes(d);
     if (!strcmp(stage, "fwd")) return fwd_layout(d).total;
+    if (!strcmp(stage, "fwd_qk")) return fwd_layout(d, true).total;
     if (!strcmp(stage, "fwd_x")) return 2 * projected_bytes(d) + fwd_layout(d).total;
     if (!strcmp(stage, "state")) return state_layout(d).total;
     if (!strcmp(stage, "bwd")) return bwd_layout(d).total;
-    fail(LSH_ERR_ARG, "unknown stage '%s' (hash, sort, fwd, fwd_x, state or bwd)", stage);
+    fail(LSH_ERR_ARG, "unknown stage '%s' (hash, sort, fwd, fwd_qk, fwd_x, state or bwd)",
+         stage);
     return 0;
 }
 
@@ -326,6 +378,31 @@ int lsh_chunk_attend(const void* qk, const void* v, const int32_t* buckets, cons
     return e == hipSuccess ? LSH_OK : hip_fail(e, "lsh_chunk_attend");
 }
 
+int lsh_chunk_attend_qk(const void* q, const void* k, const void* v, const int32_t* buckets_q,
+                        const int32_t* buckets_k, const int32_t* perm_q, const int32_t* perm_k,
+                        const lsh_shape_t* shape, float* o_sorted, float* lse_sorted,
+                        void* stream) {
+    g_err[0] = 0;
+    int rc = validate(shape);
+    if (rc) return rc;
+    if (shape->flags & LSH_KEY_NORM)
+        return fail(LSH_ERR_ARG, "lsh_chunk_attend_qk: LSH_KEY_NORM belongs to shared queries "
+                                 "and keys");
+    if (empty(shape)) return LSH_OK;
+    if (!q || !k || !v || !buckets_q || !buckets_k || !perm_q || !perm_k || !o_sorted ||
+        !lse_sorted)
+        return fail(LSH_ERR_ARG, "lsh_chunk_attend_qk: NULL tensor pointer");
+    if (misaligned({q, k, v, buckets_q, buckets_k, perm_q, perm_k, o_sorted, lse_sorted}))
+        return fail(LSH_ERR_ARG, "lsh_chunk_attend_qk: tensor pointers must be 16-byte aligned");
+    const Dims d = make_dims(*shape);
+    const OSorted o{o_sorted, false, nullptr};
+    const SepQK sep{q, buckets_q, perm_q};
+    hipError_t e = launch_attend(k, v, buckets_k, perm_k, d, o, lse_sorted, (hipStream_t)stream,
+                                 nullptr, nullptr, nullptr, false, nullptr, &sep);
+    if (e == hipSuccess) e = hipGetLastError();
+    return e == hipSuccess ? LSH_OK : hip_fail(e, "lsh_chunk_attend_qk");
+}
+
 int lsh_unsort_combine(const float* o_sorted, const float* lse_sorted, const int32_t* inv,
                        const lsh_shape_t* shape, void* out, void* stream) {
     g_err[0] = 0;
@@ -355,6 +432,23 @@ int lsh_attention_fwd(const void* qk, const void* v, const float* R, const lsh_s
         return fail(LSH_ERR_ARG, "lsh_attention_fwd: tensor pointers must be 16-byte aligned");
     return run_fwd(qk, v, R, shape, out, ws, ws_bytes, (hipStream_t)stream, nullptr, nullptr,
                    nullptr);
+}
+
+int lsh_attention_fwd_qk(const void* q, const void* k, const void* v, const float* R,
+                         const lsh_shape_t* shape, void* out, void* ws, size_t ws_bytes,
+                         void* stream) {
+    g_err[0] = 0;
+    int rc = validate(shape);
+    if (rc) return rc;
+    if (shape->flags & LSH_KEY_NORM)
+        return fail(LSH_ERR_ARG, "lsh_attention_fwd_qk: LSH_KEY_NORM belongs to shared queries "
+                                 "and keys");
+    if (empty(shape)) return LSH_OK;
+    if (!q || !k || !v || !R || !out)
+        return fail(LSH_ERR_ARG, "lsh_attention_fwd_qk: NULL tensor pointer");
+    if (misaligned({q, k, v, R, out}))
+        return fail(LSH_ERR_ARG, "lsh_attention_fwd_qk: tensor pointers must be 16-byte aligned");
+    return run_fwd_qk(q, k, v, R, shape, out, ws, ws_bytes, (hipStream_t)stream);
 }
 
 int lsh_qkv_project(const void* x, const void* w_qk, const void* w_v, const lsh_shape_t* shape,

@@ -20,11 +20,20 @@ namespace lsh {
 // quarter of its features (dot products are summed across the quad). The
 // window's keys pass through LDS 32 at a time and a running (online) softmax
 // in the exp2 domain folds each block into the output.
-template <int D, typename T>
-__global__ __launch_bounds__(256) void attend_valu_kernel(const T* __restrict__ qk,
+//
+// With separate queries and keys (SEP) the query of slot s comes from q
+// through the queries' order (perm_q, buckets_q) and the window's keys and
+// values from k and v through the keys' order; there is no self penalty, and
+// a query whose window holds no key of its bucket gets a zero row and lse
+// -inf. In the shared form q = k and the two orders are one.
+template <int D, typename T, bool SEP>
+__global__ __launch_bounds__(256) void attend_valu_kernel(const T* __restrict__ qsrc,
+                                                          const T* __restrict__ ksrc,
                                                           const T* __restrict__ v,
-                                                          const int32_t* __restrict__ buckets,
-                                                          const int32_t* __restrict__ perm,
+                                                          const int32_t* __restrict__ buckets_q,
+                                                          const int32_t* __restrict__ perm_q,
+                                                          const int32_t* __restrict__ buckets_k,
+                                                          const int32_t* __restrict__ perm_k,
                                                           Dims dm, int nqb,
                                                           float* __restrict__ o_sorted,
                                                           float* __restrict__ lse_sorted) {
@@ -42,19 +51,19 @@ __global__ __launch_bounds__(256) void attend_valu_kernel(const T* __restrict__ 
     const int tid = threadIdx.x, ql = tid >> 2, part = tid & 3;
     const int64_t L = dm.L, m = dm.m;
     const int64_t bh = seg / dm.nh;
-    const int32_t* P = perm + seg * L;
-    const int32_t* Bk = buckets + seg * L;
-    const T* X = qk + bh * L * D;
+    const int32_t* P = perm_k + seg * L;
+    const int32_t* Bk = buckets_k + seg * L;
+    const T* X = ksrc + bh * L * D;
     const T* V = v + bh * L * D;
     const int64_t qoff = (int64_t)qb * 64 + ql;   // query's place in its chunk
     const bool qlive = qoff < m;
     const int64_t s = c * m + (qlive ? qoff : 0); // its sorted slot (a real one when not live)
-    const int64_t qpos = P[s];
-    const int32_t qbkt = Bk[qpos];
+    const int64_t qpos = perm_q[seg * L + s];
+    const int32_t qbkt = buckets_q[seg * L + qpos];
     float q[QD];
 #pragma unroll
     for (int e = 0; e < QD; e += 4) {
-        const f32x4 a = IO<T>::load4(X, qpos * D + part * QD + e);
+        const f32x4 a = IO<T>::load4(qsrc + bh * L * D, qpos * D + part * QD + e);
         q[e] = a.x; q[e + 1] = a.y; q[e + 2] = a.z; q[e + 3] = a.w;
     }
     const float c2 = 1.4426950408889634f / sqrtf((float)D);   // log2(e) / sqrt(d)
@@ -109,7 +118,7 @@ __global__ __launch_bounds__(256) void attend_valu_kernel(const T* __restrict__ 
             dot += __shfl_xor(dot, 2);
             const int32_t kp = kpos[j];
             const bool ok = j < nk && kbkt[j] == qbkt && (!dm.causal || kp <= qpos);
-            const float s2 = dot * krn[j] * c2 - (kp == qpos ? pen2 : 0.f);
+            const float s2 = dot * krn[j] * c2 - (!SEP && kp == qpos ? pen2 : 0.f);
             sc[j] = ok ? s2 : -INFINITY;
             bmx = fmaxf(bmx, sc[j]);
         }
@@ -134,14 +143,16 @@ __global__ __launch_bounds__(256) void attend_valu_kernel(const T* __restrict__ 
         mx = bmx;
     }
     if (!qlive) return;
-    // the query's own key is always in its window and valid, so l > 0
-    const float inv = 1.0f / l;
+    // shared form: the query's own key is always in its window and valid, so
+    // l > 0; separate queries and keys: l = 0 when no key counts
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
     float* os = o_sorted + (seg * L + s) * D + part * QD;
 #pragma unroll
     for (int e = 0; e < QD; e += 4)
         *(f32x4*)(os + e) = (f32x4){acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv,
                                     acc[e + 3] * inv};
-    if (part == 0) lse_sorted[seg * L + s] = (mx + log2f(l)) * 0.6931471805599453f;
+    if (part == 0)
+        lse_sorted[seg * L + s] = l > 0.f ? (mx + log2f(l)) * 0.6931471805599453f : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -202,7 +213,12 @@ struct alignas(16) AttendLds {
 
 // KN (key normalisation): 0 off; 1 each key's 1 / |x| read from rn next to
 // its position; 2 summed here from the pieces of the row being stored.
-template <int D, bool HALF, bool PACKED, int KN>
+// SEP (separate queries and keys): the ring holds key rows from k through the
+// keys' order (perm, buckets); each lane gathers its query row from q through
+// the queries' order (perm_q, buckets_q) straight into its fragments, one
+// chunk ahead; no self penalty, no causal block skip (the two orders differ),
+// and a query without a key of its bucket gets a zero row and lse -inf.
+template <int D, bool HALF, bool PACKED, int KN, bool SEP>
 __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __restrict__ qk,
                                                           const uint16_t* __restrict__ v,
                                                           const int32_t* __restrict__ buckets,
@@ -211,7 +227,10 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
                                                           void* __restrict__ o_sorted,
                                                           const uint32_t* __restrict__ vmax,
                                                           float* __restrict__ lse_sorted,
-                                                          const float* __restrict__ rn) {
+                                                          const float* __restrict__ rn,
+                                                          const uint16_t* __restrict__ qsep,
+                                                          const int32_t* __restrict__ buckets_q,
+                                                          const int32_t* __restrict__ perm_q) {
     constexpr int PIECES = D / 8;              // 16-byte pieces per row
     constexpr int QPT = kM * PIECES / 256;     // qk pieces per thread
     constexpr int QROWS = 256 / PIECES;        // rows covered per pass
@@ -305,6 +324,33 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
         }
     };
 
+    // ---- separate queries: lane (g, r16) of wave w owns query row 16 w + r16
+    // of each chunk; its fragments come from q, a chunk ahead, and the sorted
+    // key of the row after that is fetched a further chunk ahead, so a row's
+    // address never waits on a load issued in the same step.
+    struct QRow {
+        u32x4 f[KSTEPS];
+        int32_t pos, bkt;
+    };
+    const int qrow_l = 16 * wave + r16;
+    auto q_key = [&](int c) -> int32_t {
+        return SEP ? perm_q[seg * L + (int64_t)c * kM + qrow_l] : 0;
+    };
+    auto issue_q = [&](QRow& qr, int32_t key) {
+        qr.pos = key_pos(key);
+        qr.bkt = PACKED ? (int32_t)((uint32_t)key >> kPackPosBits)
+                        : buckets_q[seg * L + qr.pos];
+        const uint16_t* row = qsep + (bh * L + qr.pos) * D + 8 * g;
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) qr.f[s] = *(const u32x4*)(row + 32 * s);
+    };
+    QRow qcur, qnext;
+    int32_t qkey_next = 0;
+    if constexpr (SEP) {
+        issue_q(qcur, q_key(c0));
+        if (c0 + 1 < c1) qkey_next = q_key(c0 + 1);
+    }
+
     // ---- prologue: the look-back chunk c0-1 (or an empty slot) parked in its
     // ring slot; chunks c0 .. c0+DEPTH-1 in flight; the keys of c0+DEPTH in LDS.
     // Key buffers rotate over four slots (chunk & 3).
@@ -344,6 +390,10 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
         int32_t pf = 0;
         if (c + kDepth < c1) issue_rows(rows, sm.nperm[(c + kDepth) & 3]);
         if (c + kDepth + 1 < c1 && tid < kM) pf = P[(int64_t)(c + kDepth + 1) * kM + tid];
+        if constexpr (SEP) {
+            if (c + 1 < c1) issue_q(qnext, qkey_next);
+            if (c + 2 < c1) qkey_next = q_key(c + 2);
+        }
 
         // ---- which 32-key blocks can hold a valid key for any of this wave's
         // queries (wave-uniform): the block's bucket range must meet the
@@ -351,14 +401,18 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
         // own-chunk block that starts after the last query holds only later
         // positions of the same buckets.
         const int qrow = 16 * wave + r16;
-        const int qb_lo = sm.bkt[cs * kM + 16 * wave];
-        const int qb_hi = sm.bkt[cs * kM + 16 * wave + 15];
+        // lanes 0 and 15 hold the wave's first and last query rows
+        const int qb_lo = SEP ? __builtin_amdgcn_readlane(qcur.bkt, 0)
+                              : sm.bkt[cs * kM + 16 * wave];
+        const int qb_hi = SEP ? __builtin_amdgcn_readlane(qcur.bkt, 15)
+                              : sm.bkt[cs * kM + 16 * wave + 15];
         bool act[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             const int first = sm.bkt[32 * kb], last = sm.bkt[32 * kb + 31];
             bool a = first <= qb_hi && last >= qb_lo;
-            if (dm.causal && (kb >> 1) == cs && 32 * (kb & 1) > 16 * wave + 15) a = false;
+            if (!SEP && dm.causal && (kb >> 1) == cs && 32 * (kb & 1) > 16 * wave + 15)
+                a = false;
             act[kb] = __builtin_amdgcn_readfirstlane((int)a) != 0;
         }
 
@@ -369,9 +423,10 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
         bf16x8 qf[KSTEPS];
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s)
-            qf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.k[cs][qrow][32 * s + 8 * g]);
-        const int qpos = sm.pos[cs * kM + qrow];
-        const int qb = sm.bkt[cs * kM + qrow];
+            qf[s] = __builtin_bit_cast(
+                bf16x8, SEP ? qcur.f[s] : *(const u32x4*)&sm.k[cs][qrow][32 * s + 8 * g]);
+        const int qpos = SEP ? qcur.pos : sm.pos[cs * kM + qrow];
+        const int qb = SEP ? qcur.bkt : sm.bkt[cs * kM + qrow];
         f32x4 st[8];
         float mx = -INFINITY;
 #pragma unroll
@@ -394,7 +449,7 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
             if constexpr (KN != 0) krn = *(const f32x4*)&sm.rn[32 * kb + 8 * g + 4 * h];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float s2 = acc[i] * krn[i] * c_log2 - (kps[i] == qpos ? pen2 : 0.f);
+                float s2 = acc[i] * krn[i] * c_log2 - (!SEP && kps[i] == qpos ? pen2 : 0.f);
                 const bool ok = kbk[i] == qb && (!dm.causal || kps[i] <= qpos);
                 s2 = ok ? s2 : -INFINITY;
                 st[kt][i] = s2;
@@ -403,6 +458,9 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
         }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
+        // separate queries: a query without a key of its bucket keeps mx = -inf;
+        // its exponentials are then taken against 0 (all of them are 0)
+        const float mref = (SEP && mx == -INFINITY) ? 0.f : mx;
 
         // ---- P = exp2(s - max) as bf16; the P-weight sum that normalises O is
         // taken on the matrix cores from the same bf16 values (ones x P^T)
@@ -416,7 +474,7 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
                 float pr[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    pr[i] = __builtin_amdgcn_exp2f(st[2 * kb + h][i] - mx);
+                    pr[i] = __builtin_amdgcn_exp2f(st[2 * kb + h][i] - mref);
                     sum += pr[i];
                 }
                 const bf16x2 w0 = {(__bf16)pr[0], (__bf16)pr[1]};
@@ -453,7 +511,8 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
         // row (b, h, position, round) in scaled fp16, so the combine streams
         const int64_t orow_idx = HALF ? (bh * L + qpos) * dm.nh + (seg - bh * dm.nh) : slot;
         if constexpr (HALF) {
-            const float inv = oscale / sumr;
+            // (sumr = 0 only for a separate-keys query that found no key)
+            const float inv = sumr > 0.f ? oscale / sumr : 0.f;
             // Lane (g, r16) holds features 16 dt + 4 g + i of its query. The
             // four lanes of a query swap pieces so that lane g stores features
             // 32 k + 8 g .. +7: each store then writes 64 contiguous bytes of
@@ -498,14 +557,15 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
                             (w[2] & 0xFFFEFFFEu) | pat[2], (w[3] & 0xFFFEFFFEu) | pat[3]};
             }
         } else {
-            const float inv = 1.0f / sumr;
+            const float inv = sumr > 0.f ? 1.0f / sumr : 0.f;
             float* orow = (float*)o_sorted + slot * D;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) *(f32x4*)(orow + dt * 16 + 4 * g) = oacc[dt] * inv;
-            if (g == 0) lse_sorted[slot] = (mx + log2f(sum)) * 0.6931471805599453f;
+            if (g == 0) lse_sorted[slot] = (mx + log2f(sum)) * 0.6931471805599453f;   // -inf if empty
         }
 
         if (c + kDepth + 1 < c1 && tid < kM) sm.nperm[(c + kDepth + 1) & 3][tid] = pf;
+        if constexpr (SEP) qcur = qnext;
         __syncthreads();
     };
 
@@ -516,22 +576,38 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
     }
 }
 
-template <typename T>
-static void launch_valu(const T* qk, const T* v, const int32_t* buckets, const int32_t* perm,
-                        const Dims& d, float* o, float* lse, hipStream_t st) {
+template <typename T, bool SEP>
+static void launch_valu(const T* qsrc, const T* ksrc, const T* v, const int32_t* bq,
+                        const int32_t* pq, const int32_t* bk, const int32_t* pk, const Dims& d,
+                        float* o, float* lse, hipStream_t st) {
     const int nqb = (d.m + 63) / 64;   // 64-query blocks per chunk
     dim3 grid((unsigned)((int64_t)(d.L / d.m) * nqb), (unsigned)d.segs);
     if (d.d == 64)
-        attend_valu_kernel<64, T><<<grid, 256, 0, st>>>(qk, v, buckets, perm, d, nqb, o, lse);
+        attend_valu_kernel<64, T, SEP><<<grid, 256, 0, st>>>(qsrc, ksrc, v, bq, pq, bk, pk, d,
+                                                             nqb, o, lse);
     else
-        attend_valu_kernel<128, T><<<grid, 256, 0, st>>>(qk, v, buckets, perm, d, nqb, o, lse);
+        attend_valu_kernel<128, T, SEP><<<grid, 256, 0, st>>>(qsrc, ksrc, v, bq, pq, bk, pk, d,
+                                                              nqb, o, lse);
+}
+
+template <typename T>
+static void launch_valu_any(const void* qk, const void* v, const int32_t* buckets,
+                            const int32_t* perm, const SepQK* sep, const Dims& d, float* o,
+                            float* lse, hipStream_t st) {
+    const T* k = (const T*)qk;
+    if (sep)
+        launch_valu<T, true>((const T*)sep->q, k, (const T*)v, sep->buckets_q, sep->perm_q,
+                             buckets, perm, d, o, lse, st);
+    else
+        launch_valu<T, false>(k, k, (const T*)v, buckets, perm, buckets, perm, d, o, lse, st);
 }
 
 hipError_t launch_attend(const void* qk, const void* v, const int32_t* buckets,
                          const int32_t* perm, const Dims& d, const OSorted& o, float* lse_sorted,
                          hipStream_t st, hipEvent_t* ev, int* nev, const char** names,
-                         bool packed, const float* rn) {
+                         bool packed, const float* rn, const SepQK* sep) {
     if (packed && !(o.half && d.dtype == LSH_BF16 && d.m == kM)) return hipErrorInvalidValue;
+    if (sep && d.key_norm) return hipErrorInvalidValue;
     if (d.dtype == LSH_BF16 && d.m == kM) {
         const int nchunks = d.L / kM;
         const int run_len = attend_run_len(d.segs, nchunks);
@@ -539,13 +615,20 @@ hipError_t launch_attend(const void* qk, const void* v, const int32_t* buckets,
         const unsigned grid = (unsigned)(d.segs * nruns);
         const uint16_t* x = (const uint16_t*)qk;
         const uint16_t* vv = (const uint16_t*)v;
+        const uint16_t* qs = sep ? (const uint16_t*)sep->q : nullptr;
+        const int32_t* bq = sep ? sep->buckets_q : nullptr;
+        const int32_t* pq = sep ? sep->perm_q : nullptr;
+#define LSH_ATTEND_ARGS(VM, RN) \
+    x, vv, buckets, perm, d, nruns, run_len, o.ptr, VM, lse_sorted, RN, qs, bq, pq
 #define LSH_ATTEND_LAUNCH(DD, HH, PP, VM)                                                      \
-    (!d.key_norm ? attend_mfma_kernel<DD, HH, PP, 0><<<grid, 256, 0, st>>>(                    \
-                       x, vv, buckets, perm, d, nruns, run_len, o.ptr, VM, lse_sorted, nullptr)        \
-     : rn ? attend_mfma_kernel<DD, HH, PP, 1><<<grid, 256, 0, st>>>(                           \
-                x, vv, buckets, perm, d, nruns, run_len, o.ptr, VM, lse_sorted, rn)                    \
-          : attend_mfma_kernel<DD, HH, PP, 2><<<grid, 256, 0, st>>>(                           \
-                x, vv, buckets, perm, d, nruns, run_len, o.ptr, VM, lse_sorted, nullptr))
+    (sep ? attend_mfma_kernel<DD, HH, PP, 0, true><<<grid, 256, 0, st>>>(                      \
+               LSH_ATTEND_ARGS(VM, nullptr))                                                   \
+     : !d.key_norm ? attend_mfma_kernel<DD, HH, PP, 0, false><<<grid, 256, 0, st>>>(           \
+                         LSH_ATTEND_ARGS(VM, nullptr))                                         \
+     : rn ? attend_mfma_kernel<DD, HH, PP, 1, false><<<grid, 256, 0, st>>>(                    \
+                LSH_ATTEND_ARGS(VM, rn))                                                       \
+          : attend_mfma_kernel<DD, HH, PP, 2, false><<<grid, 256, 0, st>>>(                    \
+                LSH_ATTEND_ARGS(VM, nullptr)))
         if (o.half && packed) {
             if (d.d == 64) LSH_ATTEND_LAUNCH(64, true, true, o.vmax);
             else LSH_ATTEND_LAUNCH(128, true, true, o.vmax);
@@ -557,13 +640,14 @@ hipError_t launch_attend(const void* qk, const void* v, const int32_t* buckets,
             else LSH_ATTEND_LAUNCH(128, false, false, nullptr);
         }
 #undef LSH_ATTEND_LAUNCH
+#undef LSH_ATTEND_ARGS
         return mark(st, ev, nev, names, "attend_mfma");
     }
     float* of = (float*)o.ptr;
     if (d.dtype == LSH_BF16)
-        launch_valu((const uint16_t*)qk, (const uint16_t*)v, buckets, perm, d, of, lse_sorted, st);
+        launch_valu_any<uint16_t>(qk, v, buckets, perm, sep, d, of, lse_sorted, st);
     else
-        launch_valu((const float*)qk, (const float*)v, buckets, perm, d, of, lse_sorted, st);
+        launch_valu_any<float>(qk, v, buckets, perm, sep, d, of, lse_sorted, st);
     return mark(st, ev, nev, names, "attend_fp32");
 }
 

@@ -86,23 +86,28 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 #pragma unroll
         for (int k = 0; k < G; ++k)
             if (k < n) gmx = fmaxf(gmx, l[k]);
-        const float rescale = expf(mx - gmx);   // 0 on the first group (mx = -inf)
+        // a round with lse -inf (no key: separate queries and keys only)
+        // weighs 0; while every round so far is such, take exponentials
+        // against 0 instead of -inf
+        const float gref = gmx == -INFINITY ? 0.f : gmx;
+        const float rescale = expf(mx - gref);   // 0 on the first group (mx = -inf)
         sum *= rescale;
         a0 *= rescale;
         a1 *= rescale;
 #pragma unroll
         for (int k = 0; k < G; ++k)
             if (k < n) {
-                const float e = expf(l[k] - gmx);
+                const float e = expf(l[k] - gref);
                 sum += e;
                 a0 += e * o0[k];
                 a1 += e * o1[k];
             }
         mx = gmx;
     }
-    const float inv_sum = 1.0f / sum;
+    // sum = 0: no round has a key, the output row is zero
+    const float inv_sum = sum > 0.f ? 1.0f / sum : 0.f;
     store8(out + tok * D + 8 * q, a0 * inv_sum, a1 * inv_sum);
-    if (z && q == 0) z[tok] = mx + logf(sum);
+    if (z && q == 0) z[tok] = sum > 0.f ? mx + logf(sum) : -INFINITY;
 }
 
 // Fused form: the chunk kernel already stored every round's row of a token
@@ -152,14 +157,17 @@ __global__ __launch_bounds__(256) void combine_bypos_kernel(const _Float16* __re
             gmx = fmaxf(gmx, l[k]);
         }
         // exp2(l - running max), the running max kept unrounded (a round that
-        // saw only the query itself sits near -1e5 / ln 2)
-        const float rescale = __builtin_amdgcn_exp2f(mx - gmx);   // 0 on the first group
+        // saw only the query itself sits near -1e5 / ln 2); rounds with lse
+        // -inf (no key: separate queries and keys only) weigh 0, and while
+        // every round so far is such the reference is 0 instead of -inf
+        const float gref = gmx == -INFINITY ? 0.f : gmx;
+        const float rescale = __builtin_amdgcn_exp2f(mx - gref);   // 0 on the first group
         sum *= rescale;
         a0 *= rescale;
         a1 *= rescale;
 #pragma unroll
         for (int k = 0; k < G; ++k) {
-            const float e = __builtin_amdgcn_exp2f(l[k] - gmx);   // 0 past the last round
+            const float e = __builtin_amdgcn_exp2f(l[k] - gref);   // 0 past the last round
             sum += e;
             const f32x4 lo = {(float)__builtin_bit_cast(_Float16, (uint16_t)w[k][0]),
                               (float)__builtin_bit_cast(_Float16, (uint16_t)(w[k][0] >> 16)),
@@ -174,10 +182,12 @@ __global__ __launch_bounds__(256) void combine_bypos_kernel(const _Float16* __re
         }
         mx = gmx;
     }
-    // the rows carry the power-of-two scale chosen from max|v|
-    const float inv_sum = 1.0f / (o_scale(*vmax) * sum);
+    // the rows carry the power-of-two scale chosen from max|v|; sum = 0: no
+    // round has a key, the output row is zero
+    const float inv_sum = sum > 0.f ? 1.0f / (o_scale(*vmax) * sum) : 0.f;
     store8(out + tok * D + 8 * q, a0 * inv_sum, a1 * inv_sum);
-    if (z && q == 0) z[tok] = (mx + log2f(sum)) * 0.6931471805599453f;   // natural log
+    if (z && q == 0)
+        z[tok] = sum > 0.f ? (mx + log2f(sum)) * 0.6931471805599453f : -INFINITY;   // natural log
 }
 
 template <typename T>

@@ -151,14 +151,25 @@ struct OSorted {
 // True when the fused forward can keep o_sorted in scaled fp16.
 inline bool compact_o_sorted(const Dims& d) { return d.dtype == LSH_BF16 && d.m == 64; }
 
+// Separate queries and keys: the queries' tensor and sorted order. The
+// attend launcher's qk / buckets / perm then describe the keys.
+struct SepQK {
+    const void* q;
+    const int32_t* buckets_q;   // [B,H,nh,L] by position (read when keys are not packed)
+    const int32_t* perm_q;      // [B,H,nh,L] sorted (packed like perm when packed)
+};
+
 // packed: perm holds packed sorted keys (buckets is then not read); only
 // the fp16 by-position form takes them.
 // With d.key_norm, rn holds 1 / |qk| per token (launch_key_rnorm); when it is
 // null the kernels sum each staged row's squares themselves.
+// sep (or null): separate queries and keys -- qk, buckets and perm are the
+// keys', sep the queries'; outputs by query slot (or query position).
 hipError_t launch_attend(const void* qk, const void* v, const int32_t* buckets,
                          const int32_t* perm, const Dims& d, const OSorted& o, float* lse_sorted,
                          hipStream_t st, hipEvent_t* ev, int* nev, const char** names,
-                         bool packed = false, const float* rn = nullptr);
+                         bool packed = false, const float* rn = nullptr,
+                         const SepQK* sep = nullptr);
 
 // ----------------------------------------------------- feed-forward
 // out = relu(x W1^T + b1) W2^T + b2 over `rows` rows, chunk_rows at a time;

@@ -20,7 +20,9 @@ Recipe (identical for every workload):
   * the "clusters" distribution (skewed buckets): 64 centres c_k ~ N(0, I_d),
     weights p_k proportional to k^-1.1 (Zipf 1.1 truncated to 64 ranks), per
     (batch, head, position) a centre k ~ p and x = c_k + 0.1 * N(0, I_d). The
-    centres, then the centre choices, then the noise are drawn before v and R.
+    centres, then the centre choices, then the noise are drawn before v and R;
+  * separate queries and keys (make_separate_inputs): q, k, v, R in that
+    order from the seed + 7919, each of q and k drawn as qk would be.
 """
 from __future__ import annotations
 
@@ -118,6 +120,36 @@ def make_inputs(w: Workload, seed: int | None = None):
     elif w.dtype != "fp32":
         raise ValueError(f"unknown dtype {w.dtype!r}")
     return qk, v, R
+
+
+def make_separate_inputs(w: Workload, seed: int | None = None):
+    """Inputs for separate queries and keys: (q, k, v [B,H,L,d], R [n_hashes,
+    d, n_buckets/2]) as float32. Same recipe as make_inputs with the draw
+    order q, k, v, R (q and k from the workload's distribution; with
+    clusters, q and k are drawn around the same centres)."""
+    rng = np.random.default_rng(w.seed + 7919 if seed is None else seed)
+    shape = (w.B, w.H, w.L, w.d)
+    if w.qk_dist == "normal":
+        q = rng.standard_normal(shape, dtype=np.float32)
+        k = rng.standard_normal(shape, dtype=np.float32)
+    elif w.qk_dist == "clusters":
+        n_centres = 64
+        centres = rng.standard_normal((n_centres, w.d), dtype=np.float32)
+        p = np.arange(1, n_centres + 1, dtype=np.float64) ** -1.1
+        p /= p.sum()
+        q = centres[rng.choice(n_centres, size=shape[:3], p=p)] + np.float32(0.1) * \
+            rng.standard_normal(shape, dtype=np.float32)
+        k = centres[rng.choice(n_centres, size=shape[:3], p=p)] + np.float32(0.1) * \
+            rng.standard_normal(shape, dtype=np.float32)
+    else:
+        raise ValueError(f"unknown qk distribution {w.qk_dist!r}")
+    v = rng.standard_normal(shape, dtype=np.float32)
+    R = rng.standard_normal((w.n_hashes, w.d, w.n_buckets // 2), dtype=np.float32)
+    if w.dtype == "bf16":
+        q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
+    elif w.dtype != "fp32":
+        raise ValueError(f"unknown dtype {w.dtype!r}")
+    return q, k, v, R
 
 
 def scaled(w: Workload, **changes) -> Workload:
