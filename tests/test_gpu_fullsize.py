@@ -30,9 +30,12 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 TOL = {"fp32": 1e-4, "bf16": 2e-2}
 
-FULL = ["b8_h8_l4k_nh4", "l64k_h8_d128_nh8", "skewed_l16k_nh8", "sweep_b64_l1k_nh8",
-        "sweep_b16_l4k_nh2", "sweep_b4_l16k_nh4", "sweep_b1_l64k_nh8", "l33280_h16_d64_nh8",
-        "l1m_h1_d64_nh2", "l16k_h2_d64_nh2_fp32"]
+# every workload: the four fixed ones, all sixteen points of the length sweep
+# (64K tokens per launch: B x L in {64 x 1K, 16 x 4K, 4 x 16K, 1 x 64K} with
+# 1, 2, 4 and 8 rounds), and three cases of their own
+FULL = (["b8_h8_l4k_nh4", "l64k_h8_d128_nh8", "skewed_l16k_nh8", "single_head_l1k_fp32"]
+        + [n for n in workloads.WORKLOADS if n.startswith("sweep_")]
+        + ["l33280_h16_d64_nh8", "l1m_h1_d64_nh2", "l16k_h2_d64_nh2_fp32"])
 # 520 chunks of 64 per (head, round), 128 segments: the chunk pass takes runs
 # of 32 chunks there with a ragged last run (8 chunks)
 # 2^20 + 64 positions: past the 20-bit position field of the packed sort keys,
@@ -112,8 +115,9 @@ def test_fullsize_sampled_parity(name):
         ref = oracle.combine(os_, ls_, inv, tokens=toks)[toks]
         worst = max(worst, float(np.abs(out[b, h][toks] - ref).max()))
         compared += 1
-    print(f"{name}: sampled {n_bh} slices ({compared} compared) x 48 tokens, "
-          f"max |out - oracle| = {worst:.3e}, near-ties {near}")
+    print(f"{name}: sampled {n_bh} slices ({compared} compared) x 48 tokens = "
+          f"{compared * min(L, 48)} rows compared, max |out - oracle| = {worst:.3e}, "
+          f"near-ties {near}")
     assert compared >= 1
     assert worst <= TOL[w.dtype]
 
@@ -126,3 +130,72 @@ def test_fullsize_fp32_workload_exact_oracle():
     ref, extra = oracle.forward(qk, v, R, w.n_buckets, w.chunk_len, w.causal, return_all=True)
     assert np.array_equal(buckets, extra["buckets"])
     assert np.abs(out - ref).max() <= TOL["fp32"]
+
+
+def test_headline_whole_slice():
+    """The 64K-token, 8-head, 8-round workload: every one of a (batch, head)
+    slice's 65,536 output rows against the oracle's whole forward on that
+    slice (the first slice whose GPU bucket ids all equal the oracle's)."""
+    w = workloads.WORKLOADS["l64k_h8_d128_nh8"]
+    qk, v, R, out, deterministic, buckets = _run(w)
+    assert deterministic and np.isfinite(out).all()
+    rows = 0
+    for h in (3, 6):
+        x = np.ascontiguousarray(qk[0, h], dtype=np.float64)
+        vv = np.ascontiguousarray(v[0, h], dtype=np.float64)
+        ref, extra = oracle.forward(x[None, None], vv[None, None], R, w.n_buckets, w.chunk_len,
+                                    w.causal, return_all=True)
+        differ = buckets[0, h] != extra["buckets"][0, 0]
+        assert not np.any(differ & (extra["margin"][0, 0] >= 1e-5))
+        if differ.any():
+            continue
+        err = np.abs(out[0, h] - ref[0, 0])
+        rows = w.L
+        print(f"l64k_h8_d128_nh8 head {h}: {rows} rows compared, max |out - oracle| = "
+              f"{err.max():.3e}, mean {err.mean():.3e}")
+        assert err.max() <= TOL["bf16"]
+        break
+    assert rows == w.L
+
+
+def test_headline_round_full_length():
+    """One round of one slice of the 64K-token workload, all 65,536 sorted
+    slots: the chunk pass (staged entry point, fp32 rows) on the oracle's
+    bucket ids and order against the oracle's per-round outputs and lse."""
+    w = workloads.WORKLOADS["l64k_h8_d128_nh8"]
+    qk, v, R = workloads.make_inputs(w)
+    h, r = 5, 2
+    x = np.ascontiguousarray(qk[0, h], dtype=np.float64)
+    vv = np.ascontiguousarray(v[0, h], dtype=np.float64)
+    bk, _ = oracle.hash(x, R[r:r + 1], w.n_buckets)
+    perm, inv = oracle.sort(bk[0])
+    o_ref, lse_ref = oracle.attend(x, vv, bk[0], perm, w.chunk_len, w.causal)
+    dev = lambda a, dt=None: torch.from_numpy(np.ascontiguousarray(a)).to(DEV, dt)
+    o, lse = lsh.chunk_attend(dev(qk[:, h:h + 1], torch.bfloat16), dev(v[:, h:h + 1], torch.bfloat16),
+                              dev(bk[None, None]), dev(perm[None, None, None]), w.n_buckets,
+                              w.chunk_len, w.causal)
+    o = o.cpu().numpy()[0, 0, 0]
+    lse = lse.cpu().numpy()[0, 0, 0]
+    err_o = np.abs(o - o_ref).max()
+    err_l = (np.abs(lse - lse_ref) / np.maximum(1.0, np.abs(lse_ref))).max()
+    print(f"l64k round {r} of head {h}: {w.L} slots compared, max |o - oracle| = {err_o:.3e}, "
+          f"max lse error {err_l:.3e}")
+    assert err_o <= TOL["bf16"] and err_l <= 1e-3
+
+
+def test_b8_h8_l4k_every_slice():
+    """Batch 8 x 8 heads x 4K tokens x 4 rounds: every slice's every output row
+    against the oracle's whole forward (slices whose bucket ids all match)."""
+    w = workloads.WORKLOADS["b8_h8_l4k_nh4"]
+    qk, v, R, out, deterministic, buckets = _run(w)
+    assert deterministic and np.isfinite(out).all()
+    ref, extra = oracle.forward(qk, v, R, w.n_buckets, w.chunk_len, w.causal, return_all=True)
+    differ = buckets != extra["buckets"]
+    assert not np.any(differ & (extra["margin"] >= 1e-5))
+    match = ~differ.any(axis=(2, 3))
+    err = np.abs(out - ref).max(axis=(2, 3))
+    rows = int(match.sum()) * w.L
+    print(f"b8_h8_l4k_nh4: {int(match.sum())} of {w.B * w.H} slices, {rows} rows compared, "
+          f"max |out - oracle| = {err[match].max():.3e}")
+    assert match.sum() >= w.B * w.H - 2
+    assert err[match].max() <= TOL["bf16"]
