@@ -308,6 +308,17 @@ int lsh_ffn_chunked(const void *x, const void *w1, const void *b1, const void *w
 /* Message for the last error on the calling thread ("" if none). */
 const char *lsh_last_error(void);
 
+/* Test hook for the LSH_ERR_HIP path. After lsh_debug_fail_launch(n) with
+ * n >= 1, the n-th launcher status checked by the forward entry points
+ * (lsh_attention_fwd, _fwd_x, _fwd_train, _fwd_qk; counted from 1, on the
+ * calling thread) is reported as a HIP launch failure: the call returns
+ * LSH_ERR_HIP naming the step, as if the runtime had refused that launch.
+ * The kernels themselves run normally and nothing on the device fails; the
+ * outputs of that call are unspecified, as after any error. n = 0 turns the
+ * hook off (it is off by default and after it has fired); n < 0 is
+ * LSH_ERR_ARG. */
+int lsh_debug_fail_launch(int32_t n);
+
 #ifdef __cplusplus
 }
 #endif

@@ -78,6 +78,8 @@ def load_library():
                  "lsh_qkv_project", "lsh_attention_fwd_x", "lsh_attention_fwd_train",
                  "lsh_attention_bwd"):
         getattr(lib, name).restype = ctypes.c_int
+    lib.lsh_debug_fail_launch.argtypes = [i32]
+    lib.lsh_debug_fail_launch.restype = ctypes.c_int
     lib.lsh_last_error.argtypes = []
     lib.lsh_last_error.restype = ctypes.c_char_p
     _lib = lib

@@ -24,8 +24,24 @@ int fail(int code, const char* fmt, ...) {
     return code;
 }
 
+// Test hook (lsh_debug_fail_launch): launcher statuses left before one is
+// reported as failed; 0 = off. The launches themselves are never touched.
+thread_local int g_fail_in = 0;
+thread_local bool g_injected = false;
+
+hipError_t checked(hipError_t e) {
+    if (e == hipSuccess && g_fail_in > 0 && --g_fail_in == 0) {
+        g_injected = true;
+        return hipErrorLaunchFailure;
+    }
+    return e;
+}
+
 int hip_fail(hipError_t e, const char* where) {
-    return fail(LSH_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+    const bool inj = g_injected;
+    g_injected = false;
+    return fail(LSH_ERR_HIP, "%s: %s%s", where, hipGetErrorString(e),
+                inj ? " (injected by lsh_debug_fail_launch)" : "");
 }
 
 int validate(const lsh_shape_t* s) {
@@ -176,26 +192,26 @@ int run_fwd(const void* qk, const void* v, const float* R, const lsh_shape_t* sh
     const bool compact = compact_o_sorted(d);
     const OSorted o{base + f.o, compact, hw.vmax};
     hipError_t e;
-    if ((e = launch_hash(qk, R, d, buckets, hw, st, ev, nev, names, compact ? v : nullptr)) !=
-        hipSuccess)
+    if ((e = checked(launch_hash(qk, R, d, buckets, hw, st, ev, nev, names,
+                                 compact ? v : nullptr))) != hipSuccess)
         return hip_fail(e, "hash");
     // the fp16 by-position form un-sorts in the chunk pass, so the sort can
     // hand it packed keys and skip the inverse permutation
     const bool packed = compact && packed_sort_keys(d);
-    if ((e = launch_sort(buckets, d, perm, inv, base + f.sort, st, ev, nev, names, packed)) !=
-        hipSuccess)
+    if ((e = checked(launch_sort(buckets, d, perm, inv, base + f.sort, st, ev, nev, names,
+                                 packed))) != hipSuccess)
         return hip_fail(e, "sort");
     float* rn = nullptr;
     if (d.key_norm) {
         rn = (float*)(base + f.rn);
-        if ((e = launch_key_rnorm(qk, d, rn, st)) != hipSuccess ||
+        if ((e = checked(launch_key_rnorm(qk, d, rn, st))) != hipSuccess ||
             (e = mark(st, ev, nev, names, "key_rnorm")) != hipSuccess)
             return hip_fail(e, "key_rnorm");
     }
-    if ((e = launch_attend(qk, v, buckets, perm, d, o, lse, st, ev, nev, names, packed, rn)) !=
-        hipSuccess)
+    if ((e = checked(launch_attend(qk, v, buckets, perm, d, o, lse, st, ev, nev, names, packed,
+                                   rn))) != hipSuccess)
         return hip_fail(e, "chunk_attend");
-    if ((e = launch_combine(o, lse, inv, d, out, st, ev, nev, names, z)) != hipSuccess)
+    if ((e = checked(launch_combine(o, lse, inv, d, out, st, ev, nev, names, z))) != hipSuccess)
         return hip_fail(e, "unsort_combine");
     if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "launch");
     return LSH_OK;
@@ -224,20 +240,22 @@ int run_fwd_qk(const void* q, const void* k, const void* v, const float* R,
     const OSorted o{base + f.o, compact, hw.vmax};
     hipError_t e;
     // the keys' pass folds max|v| (each hash pass clears it first)
-    if ((e = launch_hash(q, R, d, bq, hw, st, nullptr, nullptr, nullptr)) != hipSuccess ||
-        (e = launch_hash(k, R, d, bk, hw, st, nullptr, nullptr, nullptr,
-                         compact ? v : nullptr)) != hipSuccess)
-        return hip_fail(e, "hash");
-    if ((e = launch_sort(bq, d, pq, iq, base + f.sort, st, nullptr, nullptr, nullptr, packed)) !=
+    if ((e = checked(launch_hash(q, R, d, bq, hw, st, nullptr, nullptr, nullptr))) !=
             hipSuccess ||
-        (e = launch_sort(bk, d, pk, ik, base + f.sort, st, nullptr, nullptr, nullptr, packed)) !=
-            hipSuccess)
+        (e = checked(launch_hash(k, R, d, bk, hw, st, nullptr, nullptr, nullptr,
+                                 compact ? v : nullptr))) != hipSuccess)
+        return hip_fail(e, "hash");
+    if ((e = checked(launch_sort(bq, d, pq, iq, base + f.sort, st, nullptr, nullptr, nullptr,
+                                 packed))) != hipSuccess ||
+        (e = checked(launch_sort(bk, d, pk, ik, base + f.sort, st, nullptr, nullptr, nullptr,
+                                 packed))) != hipSuccess)
         return hip_fail(e, "sort");
     const SepQK sep{q, bq, pq};
-    if ((e = launch_attend(k, v, bk, pk, d, o, lse, st, nullptr, nullptr, nullptr, packed,
-                           nullptr, &sep)) != hipSuccess)
+    if ((e = checked(launch_attend(k, v, bk, pk, d, o, lse, st, nullptr, nullptr, nullptr,
+                                   packed, nullptr, &sep))) != hipSuccess)
         return hip_fail(e, "chunk_attend");
-    if ((e = launch_combine(o, lse, iq, d, out, st, nullptr, nullptr, nullptr)) != hipSuccess)
+    if ((e = checked(launch_combine(o, lse, iq, d, out, st, nullptr, nullptr, nullptr))) !=
+        hipSuccess)
         return hip_fail(e, "unsort_combine");
     if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "launch");
     return LSH_OK;
@@ -273,6 +291,14 @@ int check_dmodel(const char* fn, int32_t d_model) {
 extern "C" {
 
 const char* lsh_last_error(void) { return g_err; }
+
+int lsh_debug_fail_launch(int32_t n) {
+    g_err[0] = 0;
+    if (n < 0) return fail(LSH_ERR_ARG, "lsh_debug_fail_launch: n must be >= 0 (got %d)", n);
+    g_fail_in = n;
+    g_injected = false;
+    return LSH_OK;
+}
 
 size_t lsh_workspace_size(const char* stage, const lsh_shape_t* shape) {
     g_err[0] = 0;

@@ -45,7 +45,8 @@ __global__ __launch_bounds__(256) void attend_valu_kernel(const T* __restrict__ 
     __shared__ __attribute__((aligned(16))) float vs[KB][KS];
     __shared__ int32_t kpos[KB], kbkt[KB];
     __shared__ float krn[KB];   // key scale: 1 / |x_j| with key normalisation, else 1
-    const int64_t seg = blockIdx.y;
+    const int64_t seg = block_y();
+    if (seg >= dm.segs) return;
     const int64_t c = blockIdx.x / nqb;
     const int qb = (int)(blockIdx.x - c * nqb);
     const int tid = threadIdx.x, ql = tid >> 2, part = tid & 3;
@@ -581,7 +582,7 @@ static void launch_valu(const T* qsrc, const T* ksrc, const T* v, const int32_t*
                         const int32_t* pq, const int32_t* bk, const int32_t* pk, const Dims& d,
                         float* o, float* lse, hipStream_t st) {
     const int nqb = (d.m + 63) / 64;   // 64-query blocks per chunk
-    dim3 grid((unsigned)((int64_t)(d.L / d.m) * nqb), (unsigned)d.segs);
+    const dim3 grid = grid_split((unsigned)((int64_t)(d.L / d.m) * nqb), d.segs);
     if (d.d == 64)
         attend_valu_kernel<64, T, SEP><<<grid, 256, 0, st>>>(qsrc, ksrc, v, bq, pq, bk, pk, d,
                                                              nqb, o, lse);

@@ -150,7 +150,8 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const T* __restrict__ qk,
     __shared__ __attribute__((aligned(16))) float vs[KB][KS];
     __shared__ int32_t kpos[KB], kbkt[KB];
     __shared__ float krn[KB];   // 1 / |x_j| with key normalisation, else 1
-    const int64_t seg = blockIdx.y;
+    const int64_t seg = block_y();
+    if (seg >= dm.segs) return;
     const int64_t c = blockIdx.x / nqb;
     const int qb = (int)(blockIdx.x - c * nqb);
     const int tid = threadIdx.x, ql = tid >> 2, part = tid & 3;
@@ -253,7 +254,8 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(const T* __restrict__ qk,
     __shared__ __attribute__((aligned(16))) float gs[QB][QS];
     __shared__ int32_t qposs[QB], qbkts[QB];
     __shared__ float qz[QB], qD[QB];
-    const int64_t seg = blockIdx.y;
+    const int64_t seg = block_y();
+    if (seg >= dm.segs) return;
     const int64_t c = blockIdx.x / nkb;
     const int kb = (int)(blockIdx.x - c * nkb);
     const int tid = threadIdx.x, kl = tid >> 2, part = tid & 3;
@@ -892,7 +894,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, const Dims& d, hipStream_t st) {
         }
     }
     const int nqb = (d.m + 63) / 64;
-    const dim3 grid((unsigned)((int64_t)(d.L / d.m) * nqb), (unsigned)d.segs);
+    const dim3 grid = grid_split((unsigned)((int64_t)(d.L / d.m) * nqb), d.segs);
     bwd_dq_kernel<D, T, PACKED><<<grid, 256, 0, st>>>(qk, v, g, a.perm, a.buckets, a.z, a.Dv,
                                                       a.rn, d, nqb, a.dx_r);
     bwd_dkv_kernel<D, T, PACKED><<<grid, 256, 0, st>>>(qk, v, g, a.perm, a.buckets, a.z, a.Dv,

@@ -226,7 +226,8 @@ __global__ __launch_bounds__(256) void f32_kernel(const float* __restrict__ x, W
     __shared__ float xs[KT][T + 1];   // [k][m]
     __shared__ float ws[KT][T + 1];   // [k][n]
     const int tid = threadIdx.x, tm = tid & 15, tn = tid >> 4;
-    const int64_t m0 = (int64_t)blockIdx.y * T;
+    const int64_t m0 = block_y() * T;
+    if (m0 >= M) return;
     const int n0 = blockIdx.x * T;
     float acc[4][4] = {};
     for (int k0 = 0; k0 < K; k0 += KT) {
@@ -280,7 +281,7 @@ inline hipError_t launch(bool bf16, const void* x, Weights wt, int64_t M, int N,
             mfma_kernel<OutB, false><<<grid, kGT, 0, st>>>((const uint16_t*)x, wt, M, N, K, ntn,
                                                            ntm, ob);
     } else {
-        const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
+        const dim3 grid = grid_split((unsigned)((N + 63) / 64), (M + 63) / 64);
         f32_kernel<OutF><<<grid, 256, 0, st>>>((const float*)x, wt, M, N, K, of);
     }
     return hipGetLastError();

@@ -105,12 +105,14 @@ HashWorkspace carve_hash_workspace(void* ws, const Dims& d) {
 // Workgroup (0, 0) also clears the re-decision count, max|v| and the per-round
 // norms and list counts that later passes fold into.
 __global__ __launch_bounds__(256) void rmax_kernel(const float* __restrict__ R, int d, int half,
-                                                   int ntiles, float* __restrict__ tmax,
+                                                   int ntiles, int nh, float* __restrict__ tmax,
                                                    int32_t* __restrict__ counter,
                                                    float* __restrict__ rnorm,
                                                    int32_t* __restrict__ scount) {
     __shared__ float wmax[4];
-    const int t = blockIdx.x, r = blockIdx.y, nh = gridDim.y;
+    const int t = blockIdx.x;
+    const int r = (int)block_y();   // R round, of nh
+    if (r >= nh) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (t == 0 && r == 0) {
         if (threadIdx.x < 4) counter[threadIdx.x] = 0;
@@ -144,12 +146,15 @@ __global__ __launch_bounds__(256) void rmax_kernel(const float* __restrict__ R, 
 //            values, lane l holding column tile*32 + l%32 and
 //            k = kstep*16 + 8*(l/32) + e.
 __global__ __launch_bounds__(256) void rprep_kernel(const float* __restrict__ R, int d, int half,
-                                                    int ntiles, const float* __restrict__ tmax,
+                                                    int ntiles, int nh,
+                                                    const float* __restrict__ tmax,
                                                     float* __restrict__ rnorm,
                                                     float* __restrict__ rt,
                                                     uint16_t* __restrict__ rfrag) {
     __shared__ float tile[128][kHashColTile + 1];
-    const int t = blockIdx.x, r = blockIdx.y, nh = gridDim.y;
+    const int t = blockIdx.x;
+    const int r = (int)block_y();   // R round, of nh
+    if (r >= nh) return;
     const float* Rr = R + (int64_t)r * d * half;
     const int col0 = t * kHashColTile;
 #pragma unroll 8
@@ -698,11 +703,15 @@ __global__ __launch_bounds__(256) void hash_scan_kernel(const T* __restrict__ qk
     __shared__ __attribute__((aligned(16))) float rtile[kHashColTile][S];
     __shared__ __attribute__((aligned(16))) float xs[G][S];
     __shared__ int64_t xrow[G];   // element offset of each item's row of x
-    const int t = blockIdx.x, r = blockIdx.y;
+    // x: (column tile, group stride); y/z: R round
+    const int ntiles = (dm.nb / 2 + kHashColTile - 1) / kHashColTile;
+    const int t = blockIdx.x % ntiles, zg = blockIdx.x / ntiles, Z = gridDim.x / ntiles;
+    const int r = (int)block_y();
+    if (r >= dm.nr) return;
     const int half = dm.nb / 2;
     const int hpad = ((half + kHashColTile - 1) / kHashColTile) * kHashColTile;
     const int n = min(scount[r], (int)cap);
-    const int64_t first = (int64_t)blockIdx.z * G;
+    const int64_t first = (int64_t)zg * G;
     if (first >= n) return;
     const float* Rt = rt + ((int64_t)r * hpad + (int64_t)t * kHashColTile) * D;
 #pragma unroll 4
@@ -711,7 +720,7 @@ __global__ __launch_bounds__(256) void hash_scan_kernel(const T* __restrict__ qk
         *(f32x4*)&rtile[c][k] = *(const f32x4*)(Rt + (int64_t)c * D + k);
     }
     const int it = threadIdx.x >> 2, cq = threadIdx.x & 3;   // item, column quarter
-    for (int64_t g0 = first; g0 < n; g0 += (int64_t)gridDim.z * G) {
+    for (int64_t g0 = first; g0 < n; g0 += (int64_t)Z * G) {
         const int gn = (int)min((int64_t)G, n - g0);
         __syncthreads();
         if (threadIdx.x < G) {
@@ -767,10 +776,11 @@ __global__ __launch_bounds__(256) void hash_scan_finish_kernel(const int32_t* __
                                                                int64_t cap,
                                                                int32_t* __restrict__ buckets,
                                                                const int32_t* __restrict__ rcount,
-                                                               int64_t nregions,
+                                                               int64_t nregions, int nr,
                                                                int32_t* __restrict__ counter) {
-    const int r = blockIdx.y;
-    if (r == (int)gridDim.y - 1) {
+    const int r = (int)block_y();   // R rounds 0 .. nr-1, then the count
+    if (r > nr) return;
+    if (r == nr) {
         // the public count: the queue regions' two counts, summed
         if (blockIdx.x != 0) return;
         __shared__ int32_t part[4];
@@ -797,13 +807,13 @@ static hipError_t launch_scan(const T* qk, const Dims& d, int32_t* buckets, cons
     const int64_t cap = queue_tokens(d);
     // enough groups for a few thousand listed items per round; more loop
     const unsigned z = (unsigned)std::min<int64_t>(16, (cap + 63) / 64);
-    const dim3 sgrid((unsigned)hash_ntiles(d), (unsigned)d.nr, z);
+    const dim3 sgrid = grid_split((unsigned)hash_ntiles(d) * z, d.nr);
     if (d.d == 64)
         hash_scan_kernel<64, T><<<sgrid, 256, 0, st>>>(qk, w.rt, d, w.scount, w.slist, w.sbest, cap);
     else
         hash_scan_kernel<128, T><<<sgrid, 256, 0, st>>>(qk, w.rt, d, w.scount, w.slist, w.sbest, cap);
-    hash_scan_finish_kernel<<<dim3(4, (unsigned)d.nr + 1), 256, 0, st>>>(
-        w.scount, w.slist, w.sbest, cap, buckets, w.rcount, nregions, w.counter);
+    hash_scan_finish_kernel<<<grid_split(4, (int64_t)d.nr + 1), 256, 0, st>>>(
+        w.scount, w.slist, w.sbest, cap, buckets, w.rcount, nregions, d.nr, w.counter);
     return mark(st, ev, nev, names, "hash_refine_scan");
 }
 
@@ -813,9 +823,11 @@ hipError_t launch_hash(const void* qk, const float* R, const Dims& d, int32_t* b
     const int half = d.nb / 2;
     const int ntiles = hash_ntiles(d);
     hipError_t e;
-    const dim3 pgrid((unsigned)ntiles, (unsigned)d.nr);   // every R round
-    rmax_kernel<<<pgrid, 256, 0, st>>>(R, d.d, half, ntiles, w.tmax, w.counter, w.rnorm, w.scount);
-    rprep_kernel<<<pgrid, 256, 0, st>>>(R, d.d, half, ntiles, w.tmax, w.rnorm, w.rt, w.rfrag);
+    const dim3 pgrid = grid_split((unsigned)ntiles, d.nr);   // every R round
+    rmax_kernel<<<pgrid, 256, 0, st>>>(R, d.d, half, ntiles, d.nr, w.tmax, w.counter, w.rnorm,
+                                       w.scount);
+    rprep_kernel<<<pgrid, 256, 0, st>>>(R, d.d, half, ntiles, d.nr, w.tmax, w.rnorm, w.rt,
+                                        w.rfrag);
     if ((e = mark(st, ev, nev, names, "hash_prep")) != hipSuccess) return e;
     if (d.dtype == LSH_BF16) {
         // two 32-token fragments per wave (32 and 128 tokens per wave measured

@@ -43,6 +43,19 @@ inline Dims make_dims(const lsh_shape_t& s) {
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Grids of nx x ny workgroups whose second count can pass the 65535 a grid
+// dimension holds (segments B*H*n_hashes, rotation rounds, row tiles): ny is
+// split over y and z, block_y() recovers the index, and the few blocks past
+// ny return before doing anything.
+constexpr int64_t kGridYZ = 65535;
+inline dim3 grid_split(unsigned nx, int64_t ny) {
+    const int64_t y = ny < kGridYZ ? (ny > 0 ? ny : 1) : kGridYZ;
+    return dim3(nx, (unsigned)y, (unsigned)((ny + y - 1) / y));
+}
+__device__ __forceinline__ int64_t block_y() {
+    return (int64_t)blockIdx.z * gridDim.y + blockIdx.y;
+}
+
 // ---------------------------------------------------------------- hash stage
 // Column tile of the matrix-core hash pass: 32 projection columns.
 constexpr int kHashColTile = 32;

@@ -85,7 +85,8 @@ __global__ __launch_bounds__(256) void sort_count_kernel(const int32_t* __restri
                                                          int32_t* __restrict__ counts) {
     extern __shared__ int32_t hist[];
     const int tile = blockIdx.x;
-    const int64_t seg = blockIdx.y;
+    const int64_t seg = block_y();
+    if (seg >= dm.segs) return;
     for (int b = threadIdx.x; b < dm.nb; b += 256) hist[b] = 0;
     __syncthreads();
     const int32_t* src = buckets + seg * dm.L;
@@ -114,11 +115,11 @@ __global__ __launch_bounds__(256) void sort_count_kernel(const int32_t* __restri
 // of kBatch tiles are issued before any is used.
 __global__ __launch_bounds__(256) void sort_prefix_kernel(int32_t* __restrict__ counts,
                                                           int32_t* __restrict__ totals, int nb,
-                                                          int ntiles) {
+                                                          int ntiles, int64_t segs) {
     constexpr int kBatch = 8;
     const int b = blockIdx.x * 256 + threadIdx.x;
-    const int64_t seg = blockIdx.y;
-    if (b >= nb) return;
+    const int64_t seg = block_y();
+    if (b >= nb || seg >= segs) return;
     int32_t* c = counts + seg * ntiles * nb + b;
     int32_t run = 0;
     for (int t0 = 0; t0 < ntiles; t0 += kBatch) {
@@ -317,12 +318,12 @@ hipError_t launch_sort(const int32_t* buckets, const Dims& d, int32_t* perm, int
     int32_t* counts = (int32_t*)ws;
     int32_t* totals =
         (int32_t*)((char*)ws + align_up(sizeof(int32_t) * (size_t)d.segs * d.nb * ntiles, 256));
-    dim3 grid((unsigned)ntiles, (unsigned)d.segs);
+    const dim3 grid = grid_split((unsigned)ntiles, d.segs);
     hipError_t e;
     sort_count_kernel<<<grid, 256, sizeof(int32_t) * d.nb, st>>>(buckets, d, ntiles, counts);
     if ((e = mark(st, ev, nev, names, "sort_count")) != hipSuccess) return e;
-    sort_prefix_kernel<<<dim3((unsigned)((d.nb + 255) / 256), (unsigned)d.segs), 256, 0, st>>>(
-        counts, totals, d.nb, ntiles);
+    sort_prefix_kernel<<<grid_split((unsigned)((d.nb + 255) / 256), d.segs), 256, 0, st>>>(
+        counts, totals, d.nb, ntiles, d.segs);
     if ((e = mark(st, ev, nev, names, "sort_prefix")) != hipSuccess) return e;
     // staged needs positions below 2^kPackPosBits (a packed key per element)
     const bool staged = packed_sort_keys(d);

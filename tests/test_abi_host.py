@@ -346,3 +346,8 @@ def test_sort_noalloc_refuses_on_host(lib):
     assert lib.lsh_sort_noalloc(fake, ctypes.byref(s), ctypes.c_void_p(0x1008), fake, None) == -1
     assert lib.lsh_sort_noalloc(fake, ctypes.byref(_shape(d=96)), fake, fake, None) == -1
     assert lib.lsh_sort_noalloc(None, ctypes.byref(_shape(L=0)), None, None, None) == 0
+
+
+def test_debug_fail_launch_rejects_negative(lib):
+    assert lib.lsh_debug_fail_launch(-1) == -1 and "n must be" in lsh.lsh_last_error()
+    assert lib.lsh_debug_fail_launch(0) == 0

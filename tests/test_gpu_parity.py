@@ -332,3 +332,23 @@ def test_empty_problem_is_a_no_op():
     R = torch.randn(2, 64, 8, device=DEV)
     out = lsh.attention_fwd(qk, qk, R, 16, 64, True)
     assert out.shape == (1, 2, 0, 64)
+
+
+def test_hip_errors_propagate_as_lsh_err_hip():
+    """LSH_ERR_HIP from each step of the fused forward: the test hook reports
+    the n-th launcher status as a HIP failure (every kernel still runs
+    normally); the call returns -3 naming that step, the hook is then spent,
+    and the next call succeeds with the usual result."""
+    w = _wl("bf16", B=1, H=2, L=1024, d=64, nb=16, nh=2, m=64, causal=True, seed=41)
+    qk, v, R, qk_t, v_t, R_t = _tensors(w)
+    lib = lsh.load_library()
+    want = lsh.attention_fwd(qk_t, v_t, R_t, w.n_buckets, w.chunk_len, w.causal)
+    for n, step in ((1, "hash"), (2, "sort"), (3, "chunk_attend"), (4, "unsort_combine")):
+        assert lib.lsh_debug_fail_launch(n) == 0
+        with pytest.raises(lsh.LshError) as ei:
+            lsh.attention_fwd(qk_t, v_t, R_t, w.n_buckets, w.chunk_len, w.causal)
+        torch.cuda.synchronize()
+        assert ei.value.code == -3
+        assert str(ei.value).count(step) and "injected" in str(ei.value)
+        got = lsh.attention_fwd(qk_t, v_t, R_t, w.n_buckets, w.chunk_len, w.causal)
+        assert torch.equal(got, want)
