@@ -59,13 +59,18 @@ size_t sort_workspace_bytes(const Dims& d) {
 }
 
 // Mask of the lanes whose bucket equals this lane's (0 for inactive lanes).
+// For bit k, the ballot s of the lanes with the bit set, xor'ed with this
+// lane's bit spread over a word (0 or all ones), is the set of lanes that
+// differ from it in bit k; the lanes that differ in no bit match.
 __device__ __forceinline__ uint64_t match_bucket(int b, int nbits, bool active) {
-    uint64_t m = __ballot(active);
+    uint32_t miss_lo = 0, miss_hi = 0;
     for (int k = 0; k < nbits; ++k) {
-        const bool bit = (b >> k) & 1;
-        const uint64_t s = __ballot(active && bit);
-        m &= bit ? s : ~s;
+        const int32_t spread = __builtin_amdgcn_sbfe((int32_t)b, k, 1);   // 0 or -1
+        const uint64_t s = __ballot(spread != 0);
+        miss_lo |= (uint32_t)s ^ (uint32_t)spread;
+        miss_hi |= (uint32_t)(s >> 32) ^ (uint32_t)spread;
     }
+    const uint64_t m = __ballot(active) & ~(((uint64_t)miss_hi << 32) | miss_lo);
     return active ? m : 0ull;
 }
 
