@@ -415,7 +415,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void h
     // this wave's queue region: its tokens, every round
     const int64_t region = (int64_t)blockIdx.x * 4 + wave;
     RegionWriter qw{queue + region * TOK_WAVE * dm.nh, TOK_WAVE * dm.nh, 0, 0};
-    const int bits = 32 - __clz(2 * ntiles * kHashColTile - 1);
+    // key = |p| with its low `bits` mantissa bits replaced by the column
+    const int bits = 32 - __clz(ntiles * kHashColTile - 1);
     const uint32_t keymask = 0x7FFFFFFFu & ~((1u << bits) - 1u);
     const float qerr = __uint_as_float((uint32_t)(127 + bits - 22) << 23) + 9.5367431640625e-7f;
 
@@ -498,8 +499,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void h
         atomicMax(vmax, max(max(wvmax[0], wvmax[1]), max(wvmax[2], wvmax[3])));
 
     float k1[TOKF], k2[TOKF], k3[TOKF];
+    // the round's largest projection of the lane's token as a signed integer
+    // (the float bits: positive floats keep their order and lie above every
+    // negative one), enough to tell whether the winner is positive
+    int32_t pmax[TOKF];
 #pragma unroll
-    for (int f = 0; f < TOKF; ++f) k1[f] = k2[f] = k3[f] = 0.f;
+    for (int f = 0; f < TOKF; ++f) {
+        k1[f] = k2[f] = k3[f] = 0.f;
+        pmax[f] = INT32_MIN;
+    }
+    // the key mask in a vector register, so one v_and_or builds a key from
+    // the accumulator, the mask and the column (a scalar)
+    uint32_t vmask;
+    asm("v_mov_b32 %0, %1" : "=v"(vmask) : "s"(keymask));
 
     // One accumulator set: a step issues the MFMAs of tile g, parks the next
     // tile in LDS and then runs the epilogue of tile g; with three waves per
@@ -522,11 +534,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void h
 
     // D layout: register j of lane l is row (column of R) 8*(j/4) + 4*(l/32) + j%4,
     // column (token) l%32. Key = |p| with the low mantissa bits replaced by
-    // (column << 1 | sign): alignbit builds the index, and_or merges it.
-    // The key's column omits the half-wave offset 4*(l/32), which is added to the
-    // three surviving keys once per round; the rest of the column, tile*32 +
-    // 8*(j/4) + j%4, is wave-uniform and lives in scalar registers.
-    const float half_off = __uint_as_float((uint32_t)(8 * (lane >> 5)));   // +4 columns
+    // the column, one v_and_or: the sign is not in the key. The winner's sign
+    // comes from pmax, the largest signed p of the token in the round (one
+    // v_max3_i32 per two values): a certified winner beats every other |p| by
+    // more than the key quantisation, so p > 0 exactly when pmax >= its key.
+    // The key's column omits the half-wave offset 4*(l/32), which is added
+    // to the three surviving keys once per round; the rest of the column,
+    // tile*32 + 8*(j/4) + j%4, is wave-uniform and lives in scalar registers.
+    const uint32_t half_off = (uint32_t)(4 * (lane >> 5));   // +4 columns
     auto epilogue = [&](int g, f32x16(&acc)[TOKF]) {
         const int r = __builtin_amdgcn_readfirstlane(g / ntiles);
         const int t = __builtin_amdgcn_readfirstlane(g - r * ntiles);
@@ -536,9 +551,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void h
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 const uint32_t u = __float_as_uint(acc[f][j]);
-                const uint32_t idx =
-                    __builtin_amdgcn_alignbit(cb + (uint32_t)(8 * (j / 4) + (j % 4)), u, 31);
-                top3_insert(k1[f], k2[f], k3[f], __uint_as_float((u & keymask) | idx));
+                const uint32_t col = cb + (uint32_t)(8 * (j / 4) + (j % 4));
+                top3_insert(k1[f], k2[f], k3[f], __uint_as_float((u & vmask) | col));
+                if (j & 1)
+                    pmax[f] = max(max(pmax[f], __float_as_int(acc[f][j - 1])), (int32_t)u);
             }
         }
         if (t != ntiles - 1) return;
@@ -548,15 +564,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void h
         for (int f = 0; f < TOKF; ++f) {
             // keys are non-negative floats whose bit patterns stay below the
             // masked float part, so an integer add moves the column by 4
-            k1[f] = __uint_as_float(__float_as_uint(k1[f]) + __float_as_uint(half_off));
-            k2[f] = __uint_as_float(__float_as_uint(k2[f]) + __float_as_uint(half_off));
-            k3[f] = __uint_as_float(__float_as_uint(k3[f]) + __float_as_uint(half_off));
+            k1[f] = __uint_as_float(__float_as_uint(k1[f]) + half_off);
+            k2[f] = __uint_as_float(__float_as_uint(k2[f]) + half_off);
+            k3[f] = __uint_as_float(__float_as_uint(k3[f]) + half_off);
             const float p1 = __shfl_xor(k1[f], 32);
             const float p2 = __shfl_xor(k2[f], 32);
             const float p3 = __shfl_xor(k3[f], 32);
             top3_insert(k1[f], k2[f], k3[f], p1);
             top3_insert(k1[f], k2[f], k3[f], p2);
             top3_insert(k1[f], k2[f], k3[f], p3);
+            const float pm = __int_as_float(max(pmax[f], __shfl_xor(pmax[f], 32)));
             const bool mine = lane < 32 && tok_live[f];
             const uint32_t b1 = __float_as_uint(k1[f]), b2 = __float_as_uint(k2[f]);
             const float v1 = __uint_as_float(b1 & keymask);
@@ -565,14 +582,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void h
             const float xn = sqrtf(xn2[f]) * (1.0f + (float)(D + 4) * kTwoM24);
             const float thr = Ea * xn + Eb + v1 * qerr + 1e-30f;
             const int mode = classify(v1, v2, v3, thr);
-            const uint32_t i1 = b1 & ~keymask & 0x7FFFFFFFu, i2 = b2 & ~keymask & 0x7FFFFFFFu;
-            const int c1 = (int)(i1 >> 1), c2 = (int)(i2 >> 1);
-            const int bucket = c1 < half ? c1 + ((i1 & 1u) ? half : 0) : 0;
+            const int c1 = (int)(b1 & ~keymask), c2 = (int)(b2 & ~keymask);
+            const int bucket = c1 < half ? c1 + (pm >= v1 ? 0 : half) : 0;
             const int32_t item = item0[f] + r * dm.L;
             if (mine) buckets[item] = bucket;
             RefineItem it{item, c1, c2, mode};
             qw.push(mine && mode >= 0, it, lane);
             k1[f] = k2[f] = k3[f] = 0.f;
+            pmax[f] = INT32_MIN;
         }
     };
 
