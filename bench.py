@@ -409,13 +409,15 @@ def cpu_baseline(w, qk, v, R, target_s=12.0):
                       f"{w.n_hashes} rounds: {dt:.1f} s; rate scaled by {heads}/{w.H} heads"}
 
 
-def measured_traffic(name, kernel):
-    """HBM-side bytes per launch of `kernel` from the committed counter run
-    (FETCH_SIZE and WRITE_SIZE scaled by a plain copy's readings), or None
-    when the kernel's source has changed since the counters were taken."""
+def profile_record(name, kernel):
+    """The committed rocprofv3 record of `kernel` at workload `name`
+    (profiles/kernels_<name>.json: the kernel-trace average duration and, when
+    counters were taken, HBM-side bytes from FETCH_SIZE / WRITE_SIZE scaled by a
+    plain copy's readings and the matrix pipe's busy share), or None when the
+    kernel's source has changed since it was measured."""
     import hashlib
 
-    path = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    path = os.path.join(ROOT, "profiles", f"kernels_{name}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path)).get("kernels", {}).get(kernel)
@@ -424,7 +426,40 @@ def measured_traffic(name, kernel):
     src = os.path.join(ROOT, "lsh_attention_fp32_amd", "csrc", rec["source"])
     if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
         return None
-    return rec["read_bytes"] + rec["write_bytes"]
+    return rec
+
+
+def kernel_rooflines(w, name, kernels):
+    """Per kernel: event-timed ms, its algorithmic work against the peak of the
+    roof that binds it, and (from the committed profile, when current) the
+    rocprofv3 average, counted HBM traffic and matrix-pipe busy share."""
+    work = algorithmic_work(w)
+    out = {}
+    for k, ms in kernels.items():
+        e = {"ms": ms}
+        if k in work:
+            bound, amount, _ = work[k]
+            secs = ms / 1e3
+            if bound == "hbm":
+                e.update(bound="hbm", achieved=amount / secs / 1e9, unit="GB/s", peak=PEAK_HBM_GBS)
+            elif bound == "mfma":
+                e.update(bound="mfma", achieved=amount / secs / 1e12, unit="TFLOP/s",
+                         peak=PEAK_F16_TFLOPS)
+            else:
+                e.update(bound="alu", achieved=amount / secs / 1e12, unit="TFLOP/s",
+                         peak=PEAK_FP32_TFLOPS)
+            e["frac"] = e["achieved"] / e["peak"]
+        rec = profile_record(name, k)
+        if rec:
+            e["rocprof_ms"] = rec.get("avg_us", 0.0) / 1e3 or None
+            tb = rec.get("read_bytes")
+            if tb is not None:
+                e["traffic_bytes"] = tb + rec["write_bytes"]
+                e["hbm_gbs_counted"] = e["traffic_bytes"] / (ms / 1e3) / 1e9
+            if rec.get("mfma_busy") is not None:
+                e["mfma_busy"] = rec["mfma_busy"]
+        out[k] = e
+    return out
 
 
 def main() -> int:
@@ -488,7 +523,8 @@ def main() -> int:
             r = measure(lsh, torch, w, min(args.steps, 10), args.warmup)
             line = {"workload": n, "config": w.describe(), "ms_per_step": r["ms_per_step"],
                     "tokens_per_s": w.B * w.L / (r["ms_per_step"] / 1e3),
-                    "kernels_ms": r["kernels"], "hash_redecided": r["refined"],
+                    "kernels_ms": r["kernels"], "kernels": kernel_rooflines(w, n, r["kernels"]),
+                    "hash_redecided": r["refined"],
                     "forward_roofline": forward_roofline(w, r["ms_per_step"])}
             if args.dense:
                 line["dense"] = dense_comparator(torch, w, *r["tensors"])
@@ -553,9 +589,15 @@ def main() -> int:
         roof = {"bound": "alu", "achieved": amount / secs / 1e12, "peak": PEAK_FP32_TFLOPS,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(name, dominant)
+    rec = profile_record(name, dominant)
+    roof["traffic"] = (rec["read_bytes"] + rec["write_bytes"]) if rec and "read_bytes" in rec \
+        else None
     roof["kernel"] = dominant
     roof["kernel_ms"] = kernels[dominant]
+    # the same fraction from the committed rocprofv3 kernel-trace average
+    if rec and rec.get("avg_us"):
+        roof["kernel_ms_rocprof"] = rec["avg_us"] / 1e3
+        roof["frac_rocprof"] = roof["frac"] * kernels[dominant] / roof["kernel_ms_rocprof"]
 
     tokens = w.B * w.L
     line = {
@@ -577,9 +619,12 @@ def main() -> int:
         "roofline": roof,
         "forward_roofline": forward_roofline(w, ms_per_step),
         "kernels_ms": kernels,
+        "kernels": kernel_rooflines(w, name, kernels),
         "hash_redecided": refined,
         "wall_s_timed": wall,
     }
+    if args.dense:
+        line["dense"] = dense_comparator(torch, w, *r["tensors"])
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, qk, v, R)
     print(json.dumps(line), flush=True)
