@@ -411,16 +411,16 @@ def cpu_baseline(w, qk, v, R, target_s=12.0):
 
 def profile_record(name, kernel):
     """The committed rocprofv3 record of `kernel` at workload `name`
-    (profiles/kernels_<name>.json: the kernel-trace average duration and, when
+    (profiles/kernels.json: the kernel-trace average duration and, when
     counters were taken, HBM-side bytes from FETCH_SIZE / WRITE_SIZE scaled by a
     plain copy's readings and the matrix pipe's busy share), or None when the
     kernel's source has changed since it was measured."""
     import hashlib
 
-    path = os.path.join(ROOT, "profiles", f"kernels_{name}.json")
+    path = os.path.join(ROOT, "profiles", "kernels.json")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path)).get("kernels", {}).get(kernel)
+    rec = json.load(open(path)).get("workloads", {}).get(name, {}).get("kernels", {}).get(kernel)
     if not rec:
         return None
     src = os.path.join(ROOT, "lsh_attention_fp32_amd", "csrc", rec["source"])
