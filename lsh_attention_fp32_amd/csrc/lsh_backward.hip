@@ -76,11 +76,14 @@ __device__ __forceinline__ void load_quarter(const T* row, int part, float (&r)[
 
 // Weight of a valid (query, key) pair: exp(s - Z) in the exp2 domain, or
 // 1 / n_hashes for the self pair of a position that sees only itself.
+// Every operand is formed and the result selected, without branches: the
+// pairs of a wave take different cases, and a branch per pair would
+// serialise them.
 __device__ __forceinline__ float pair_weight(bool ok, bool self, float s2, float z2,
                                              bool self_only, float inv_nh) {
-    if (!ok) return 0.f;
-    if (self_only) return self ? inv_nh : 0.f;
-    return __builtin_amdgcn_exp2f(s2 - z2);
+    const float e = __builtin_amdgcn_exp2f(s2 - z2);
+    const float w = self_only ? (self ? inv_nh : 0.f) : e;
+    return ok ? w : 0.f;
 }
 
 __device__ __forceinline__ float quad_sum(float x) {
@@ -481,30 +484,34 @@ __device__ __forceinline__ void transpose_items(const uint16_t (*rm)[BwdRows<D>:
 
 // ---------------------------------------------------------------------------
 // Run-based matrix-core pass. A workgroup walks a run of run_len consecutive
-// chunks of one (batch, head, round) segment. Chunk c's slots are the queries
-// of the pairs (c, c - 1), (c, c) and the keys of the pairs (c, c), (c + 1, c).
-// Eight waves: waves 0-3 take the query side, waves 4-7 the key side, so each
-// SIMD runs one of each and the matrix work of one overlaps the other's
-// vector work. At step c
-//   query waves: chunk c as queries against the keys of chunks c - 1 and c
-//                (dq), handed to the key waves through LDS (bf16);
-//   key waves:   chunk c - 1 as keys against chunk c's queries (the key side
-//                of pair (c, c - 1)), then chunk c - 1's rows out
-//                ((dq + dk) scaled, dv); chunk c as keys against its own
-//                queries (dk, dv so far).
-// LDS holds the rows of chunks c - 1 and c (qk and v row-major, qk
-// transposed, one slot per chunk parity) and chunk c's output gradients.
-// Chunk c + 1's rows are gathered into registers at the top of step c and
-// parked in the slot chunk c - 1 leaves, so every chunk's rows come from HBM
-// once per run and a gather has a whole step of matrix work to arrive. The
-// last chunk of a run is finished by a partial step on the next chunk (its
-// key side only), whose run repeats that pair for its own queries.
+// chunks of one (batch, head, round) segment. The keys of chunk t meet the
+// queries of chunks t (own pair) and t + 1 (look-back pair), so eight waves
+// split into two sets of four that take turns: at step c one set owns the 64
+// keys of chunk c, the other those of chunk c - 1, each wave 16 of them, with
+// their qk and v fragments and their dk, dv accumulators in registers for
+// both of the chunk's steps. At step c every wave
+//   A: scores its 16 keys against chunk c's 64 queries (S and dP tiles with
+//      the queries' rows from LDS), forms the pair weights P and dS in the
+//      lanes of its keys, adds dk += dS^T x_q and dv += P^T g_q (the queries'
+//      transposed rows from LDS), and writes its dS (times the key's 1/|x|
+//      under key normalisation) into a [query][key] LDS buffer;
+//   B: the set owning chunk c - 1 writes that chunk's rows out ((dq + dk)
+//      scaled, and dv), its dq waiting in LDS since step c - 1; every wave
+//      then computes its share of dq for chunk c = dS x_k over the 128 keys
+//      (the keys' transposed rows and the dS buffer from LDS);
+//   C: dq of chunk c goes to LDS; chunk c + 1's rows, gathered into
+//      registers since the top of the step, are parked in LDS;
+//   D: chunk c + 1's rows are transposed, and the set that just wrote chunk
+//      c - 1 out takes chunk c + 1's keys.
+// Every score is computed once. The first step of a run scores the look-back
+// pair for dq only (the run before finishes that chunk's dk, dv); a run that
+// does not end its segment closes with a partial step on the next chunk
+// (look-back keys only, no dq), whose run repeats those scores for its dq.
 constexpr int kBwdThreads = 512;
 
 // Chunks per workgroup: longer runs repeat the partial step on the next chunk
-// and the first gather's wait less often (64 chunks: 3 % less backward time
-// than 16 at 64K tokens x 8 heads x 8 rounds), as long as the grid keeps at
-// least four workgroups per compute unit; never fewer than 16.
+// and the first gather's wait less often, as long as the grid keeps at least
+// four workgroups per compute unit; never fewer than 16.
 inline int bwd_run_len(int64_t segs, int nchunks) {
     constexpr int64_t kMinGrid = 4 * 256;
     int run = 64;
@@ -514,17 +521,28 @@ inline int bwd_run_len(int64_t segs, int nchunks) {
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
+// The dS buffer holds, for each of the 64 queries of a step, the 128 keys
+// (chunk c - 1 then chunk c) as 16 units of 8 keys (16 bytes). Rows are 272
+// bytes apart, with 32 more bytes after every 16 rows, so unit u of query q
+// starts on bank 4 ((u + q + 2 (q / 16)) mod 16) of 64: the 16 lanes of a
+// 16-byte read (16 consecutive queries at one unit) cover every bank once,
+// and a dS write's 64 lanes (4 queries 8 apart, two units each) take 32
+// distinct banks.
+constexpr int kDsRow = 136;   // bf16 elements per row: 16 units and one unit of padding
+constexpr int kDsGap = 16;    // bf16 elements after every 16 rows
+
 template <int D>
 struct alignas(16) BwdRunLds {
     static constexpr int RS = BwdRows<D>::RS, TS = BwdRows<D>::TS;
-    uint16_t xr[2][kBM][RS];   // qk rows of the chunk of each parity (phys_row order)
-    uint16_t vr[2][kBM][RS];   // v rows
-    uint16_t gr[kBM][RS];      // output-gradient rows of the current chunk
-    uint16_t xt[2][D][TS];     // qk transposed (item order)
-    uint16_t gt[D][TS];        // output gradients transposed
-    uint16_t xq[kBM][RS];      // dq of the current chunk (bf16), query waves -> key waves
-    int32_t pos[3][kBM], bkt[3][kBM];          // chunk t in slot t % 3
-    float zz[2][kBM], dd[2][kBM], rn[2][kBM];   // chunk t in slot t & 1
+    uint16_t xr[kBM][RS];      // qk rows of chunk c (phys_row order)
+    uint16_t vr[kBM][RS];      // v rows of chunk c (phys_row order)
+    uint16_t gr[kBM][RS];      // output-gradient rows of chunk c (phys_row order)
+    uint16_t xt[2][D][TS];     // qk transposed (item order), chunk t in slot t & 1
+    uint16_t gt[D][TS];        // output gradients of chunk c transposed
+    uint16_t ds[kBM * kDsRow + (kBM / 16) * kDsGap];   // dS of step c by [query][key]
+    uint16_t xq[kBM][RS];      // dq of the chunk whose keys finish next (bf16, item order)
+    int32_t pos[3][kBM], bkt[3][kBM];   // chunk t in slot t % 3
+    float zz[kBM], dd[kBM], rn[kBM];    // chunk c's Z, D and 1 / |x|
 };
 
 template <int D, bool PACKED, bool KN>
@@ -541,18 +559,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_run_kernel(const uint16_t* __
                                                               uint16_t* __restrict__ dv_r) {
     constexpr int KSTEPS = D / 32, DT = D / 16;
     constexpr int PER = kBM * (D / 8) / kBwdThreads;   // 16-byte pieces per thread and source
+    constexpr int TPW = DT / 2;                        // dq tiles (16 features x 16 queries) per wave
     static_assert(PER >= 1, "every thread moves a piece of each row set");
     __shared__ BwdRunLds<D> sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const bool qside = wave < 4;   // waves 0-3: query side; 4-7: key side
-    const int wg = wave & 3;       // the wave's 16 slots in a chunk
+    const int wset = wave >> 2;    // the set: owns chunks t with t & 1 == wset
+    const int wg = wave & 3;       // the wave's 16 keys in a chunk
     const int gq = lane >> 4, r16 = lane & 15;
     const int64_t seg = blockIdx.x / nruns;
     const int run = blockIdx.x - (int)(seg * nruns);
     const int nchunks = dm.L / kBM;
     const int c0 = run * run_len;
     const int c1 = min(c0 + run_len, nchunks);
-    const int clast = min(c1, nchunks - 1);   // step c1 (when it exists) is key side only
+    const int clast = min(c1, nchunks - 1);   // step c1 (when it exists) is a partial step
     const int64_t L = dm.L;
     const int64_t bh = seg / dm.nh;
     const int r = (int)(seg - bh * dm.nh);
@@ -565,8 +584,22 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_run_kernel(const uint16_t* __
     const float pen2 = kSelfPenalty * kLog2e;
     const float inv_nh = 1.0f / (float)dm.nh;
     const float scale = 1.0f / sqrtf((float)D);
-    const int me = 16 * wg + r16;   // this lane's slot within a chunk
+    const int me = 16 * wg + r16;   // this lane's key within its chunk
     const int prow = phys_row(me);
+    // dq tiles of this wave: feature tile dq_dt, query tiles dq_qt .. + TPW - 1
+    const int dq_dt = wave % DT, dq_qt = (wave / DT) * TPW;   // dq_qt is even
+    // Per-lane LDS addresses; every tile below is a constant offset from one
+    // of them (row r16, column 8 gq of the row-major and transposed buffers).
+    constexpr int RS = BwdRows<D>::RS, TS = BwdRows<D>::TS;
+    const uint16_t* const xr_l = &sm.xr[r16][8 * gq];
+    const uint16_t* const gr_l = &sm.gr[r16][8 * gq];
+    const uint16_t* const xt_l = &sm.xt[0][r16][8 * gq];
+    const uint16_t* const gt_l = &sm.gt[r16][8 * gq];
+    const uint16_t* const xtq_l = xt_l + 16 * dq_dt * TS;
+    // dS writes: query 32 qb + 8 gq + e, key me (+ 64 for chunk c's keys)
+    uint16_t* const dsw_l = &sm.ds[8 * gq * kDsRow + (gq >> 1) * kDsGap + me];
+    // dS reads: query 16 qt + r16 (qt = dq_qt + j), keys 32 kb + 8 gq .. + 7
+    const uint16_t* const dsr_l = &sm.ds[(16 * dq_qt + r16) * kDsRow + dq_qt * kDsGap + 8 * gq];
 
     // rows of chunk t (positions in its pos slot) into registers, then LDS
     struct Pre {
@@ -590,19 +623,18 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_run_kernel(const uint16_t* __
             pf.rn = KN ? rn[p] : 1.f;
         }
     };
-    auto park = [&](int t, const Pre& pf) {
-        const int par = t & 1;
+    auto park = [&](const Pre& pf) {
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
             const int i = tid + kBwdThreads * k, row = phys_row(i / (D / 8)), pc = i % (D / 8);
-            *(u32x4*)&sm.xr[par][row][pc * 8] = pf.x[k];
-            *(u32x4*)&sm.vr[par][row][pc * 8] = pf.v[k];
+            *(u32x4*)&sm.xr[row][pc * 8] = pf.x[k];
+            *(u32x4*)&sm.vr[row][pc * 8] = pf.v[k];
             *(u32x4*)&sm.gr[row][pc * 8] = pf.g[k];
         }
         if (tid < kBM) {
-            sm.zz[par][tid] = pf.z;
-            sm.dd[par][tid] = pf.d;
-            sm.rn[par][tid] = pf.rn;
+            sm.zz[tid] = pf.z;
+            sm.dd[tid] = pf.d;
+            sm.rn[tid] = pf.rn;
         }
     };
     auto load_keys = [&](int t) {   // sorted keys of chunk t into its slot (threads < 64)
@@ -612,129 +644,178 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_run_kernel(const uint16_t* __
         sm.bkt[t % 3][tid] = b;
     };
 
-    // A 32-item block takes part only if its bucket range meets the wave's
-    // (chunks are sorted by bucket) and, within one chunk under causality,
-    // only if it is not wholly on the wrong side: a key slot after every
-    // query slot of the same bucket has a later position. Wave-uniform.
-    auto active = [&](int lo, int hi, int mlo, int mhi, bool skip) -> bool {
-        const bool a = lo <= mhi && hi >= mlo && !skip;
-        return __builtin_amdgcn_readfirstlane((int)a) != 0;
-    };
-    // chunk c's queries (fragments xf, gf) against the keys of chunk t (LDS)
-    auto query_pass = [&](int t, bool own, const bf16x8(&xf)[KSTEPS], const bf16x8(&gf)[KSTEPS],
-                          int32_t mpos, int32_t mbkt, float mz2, float mD, bool mself_only,
-                          int mlo, int mhi, f32x4(&dq)[DT]) {
-        const int par = t & 1, s3 = t % 3;
+    // the wave's keys: fragments, position, bucket, 1 / |x|, accumulators
+    bf16x8 kf[KSTEPS], vf[KSTEPS];
+    f32x4 dk[DT], dvv[DT];
+    int32_t mpos = 0, mbkt = -1;
+    float mrn = 1.f, msdd = 0.f;
+    // take the keys of chunk t (its rows parked in xr, vr; its keys in slot t % 3)
+    auto take_keys = [&](int t) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            if (!active(sm.bkt[s3][32 * kb], sm.bkt[s3][32 * kb + 31], mlo, mhi,
-                        own && dm.causal && 32 * kb > 16 * wg + 15))
-                continue;
-            u32x4 dsfrag;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                // tile row r16 is item 32 kb + 8 (r16 / 4) + 4 h + r16 % 4
-                const int kw = 32 * kb + 16 * h + r16;   // its LDS row
-                f32x4 sacc = {0.f, 0.f, 0.f, 0.f}, pacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < KSTEPS; ++s) {
-                    const bf16x8 ka = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.xr[par][kw][32 * s + 8 * gq]);
-                    const bf16x8 va = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.vr[par][kw][32 * s + 8 * gq]);
-                    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, xf[s], sacc, 0, 0, 0);
-                    pacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, gf[s], pacc, 0, 0, 0);
-                }
-                float ds[4];
-                const int kbase = 32 * kb + 8 * gq + 4 * h;   // register i is key kbase + i
-                const i32x4 kps = *(const i32x4*)&sm.pos[s3][kbase];
-                const i32x4 kbk = *(const i32x4*)&sm.bkt[s3][kbase];
-                f32x4 krn = {1.f, 1.f, 1.f, 1.f};
-                if constexpr (KN) krn = *(const f32x4*)&sm.rn[par][kbase];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const bool ok = kbk[i] == mbkt && (!dm.causal || kps[i] <= mpos);
-                    const float s2 = sacc[i] * krn[i] * c2 - (kps[i] == mpos ? pen2 : 0.f);
-                    const float pw = pair_weight(ok, kps[i] == mpos, s2, mz2, mself_only, inv_nh);
-                    ds[i] = pw * (pacc[i] - mD) * krn[i];
-                }
-                dsfrag[2 * h] = pack_bf16x2(ds[0], ds[1]);
-                dsfrag[2 * h + 1] = pack_bf16x2(ds[2], ds[3]);
-            }
-            const bf16x8 bd = __builtin_bit_cast(bf16x8, dsfrag);
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const bf16x8 af = __builtin_bit_cast(
-                    bf16x8, *(const u32x4*)&sm.xt[par][dt * 16 + r16][32 * kb + 8 * gq]);
-                dq[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bd, dq[dt], 0, 0, 0);
-            }
+        for (int s = 0; s < KSTEPS; ++s) {
+            kf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(&sm.xr[prow][8 * gq] + 32 * s));
+            vf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(&sm.vr[prow][8 * gq] + 32 * s));
         }
+        mpos = sm.pos[t % 3][me];
+        mbkt = sm.bkt[t % 3][me];
+        mrn = KN ? sm.rn[me] : 1.f;
+        msdd = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) dk[dt] = dvv[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
     };
-    // keys in fragments (xf, vf) against the queries of chunk t (LDS, with
-    // its output gradients in gr / gt)
-    auto key_pass = [&](int t, bool own, const bf16x8(&xf)[KSTEPS], const bf16x8(&vf)[KSTEPS],
-                        int32_t mpos, int32_t mbkt, float mrn, int mlo, int mhi,
-                        f32x4(&dk)[DT], f32x4(&dvv)[DT], float& msdd) {
-        const int par = t & 1, s3 = t % 3;
+
+    // Phase A for this wave's keys (of chunk c when own, else c - 1) against
+    // chunk c's queries. Tile rows are queries: A-row m of block qb, half h
+    // is query 32 qb + 8 (m / 4) + 4 h + m % 4 (LDS row 32 qb + 16 h + m), so
+    // after both halves lane (r16, gq) holds its key's P and dS for queries
+    // 32 qb + 8 gq + e, e < 8: the B operand of the dk and dv products.
+    auto key_step = [&](int c, bool own, bool do_dkv, bool do_ds) {
+        const int s3 = c % 3, par = c & 1;
+        const int klo = __builtin_amdgcn_readlane(mbkt, 0);
+        const int khi = __builtin_amdgcn_readlane(mbkt, 15);
+        const uint16_t* const xtc = xt_l + par * D * TS;   // chunk c's transposed qk
+        uint16_t* const dsw = dsw_l + (own ? kBM : 0);      // chunk c's keys: columns 64..127
+        // both query blocks' bucket bounds first, then one wave-uniform mask
+        // (non-short-circuit & and |: the loads are all issued before any test)
+        int lo[2], hi[2];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-            if (!active(sm.bkt[s3][32 * qb], sm.bkt[s3][32 * qb + 31], mlo, mhi,
-                        own && dm.causal && 32 * qb + 31 < 16 * wg))
-                continue;
-            u32x4 pfrag, dsfrag;
+            lo[qb] = sm.bkt[s3][32 * qb];
+            hi[qb] = sm.bkt[s3][32 * qb + 31];
+        }
+        uint32_t act = 0;
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int qw = 32 * qb + 16 * h + r16;
-                f32x4 sacc = {0.f, 0.f, 0.f, 0.f}, pacc = {0.f, 0.f, 0.f, 0.f};
+        for (int qb = 0; qb < 2; ++qb) {
+            const bool a = (lo[qb] <= khi) & (hi[qb] >= klo) &
+                           !(own && dm.causal && 16 * wg > 32 * qb + 31);
+            act |= (uint32_t)a << qb;
+        }
+        act = __builtin_amdgcn_readfirstlane(act);
 #pragma unroll
-                for (int s = 0; s < KSTEPS; ++s) {
-                    const bf16x8 qa = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.xr[par][qw][32 * s + 8 * gq]);
-                    const bf16x8 ga = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.gr[qw][32 * s + 8 * gq]);
-                    sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, xf[s], sacc, 0, 0, 0);
-                    pacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga, vf[s], pacc, 0, 0, 0);
+        for (int qb = 0; qb < 2; ++qb) {
+            u32x4 pfrag = {0u, 0u, 0u, 0u}, dsfrag = {0u, 0u, 0u, 0u}, dqfrag = {0u, 0u, 0u, 0u};
+            if ((act >> qb) & 1) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    f32x4 sacc = {0.f, 0.f, 0.f, 0.f}, pacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < KSTEPS; ++s) {
+                        // A row r16 of the tile: LDS row 32 qb + 16 h + r16
+                        const int off = (32 * qb + 16 * h) * RS + 32 * s;
+                        const bf16x8 qa = __builtin_bit_cast(bf16x8, *(const u32x4*)(xr_l + off));
+                        const bf16x8 ga = __builtin_bit_cast(bf16x8, *(const u32x4*)(gr_l + off));
+                        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[s], sacc, 0, 0, 0);
+                        pacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga, vf[s], pacc, 0, 0, 0);
+                    }
+                    float pw[4], ds[4];
+                    const int qbase = 32 * qb + 8 * gq + 4 * h;   // register i is query qbase + i
+                    const i32x4 qps = *(const i32x4*)&sm.pos[s3][qbase];
+                    const i32x4 qbk = *(const i32x4*)&sm.bkt[s3][qbase];
+                    const f32x4 zq = *(const f32x4*)&sm.zz[qbase];
+                    const f32x4 dq4 = *(const f32x4*)&sm.dd[qbase];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const bool ok = (qbk[i] == mbkt) & (!dm.causal | (mpos <= qps[i]));
+                        const float s2 = sacc[i] * mrn * c2 - (mpos == qps[i] ? pen2 : 0.f);
+                        pw[i] = pair_weight(ok, mpos == qps[i], s2, zq[i] * kLog2e,
+                                            zq[i] < -0.5f * kSelfPenalty, inv_nh);
+                        ds[i] = pw[i] * (pacc[i] - dq4[i]);
+                        if constexpr (KN) msdd = fmaf(ds[i], sacc[i], msdd);
+                    }
+                    pfrag[2 * h] = pack_bf16x2(pw[0], pw[1]);
+                    pfrag[2 * h + 1] = pack_bf16x2(pw[2], pw[3]);
+                    dsfrag[2 * h] = pack_bf16x2(ds[0], ds[1]);
+                    dsfrag[2 * h + 1] = pack_bf16x2(ds[2], ds[3]);
+                    if constexpr (KN) {   // dq takes dS times the key's 1 / |x|
+                        dqfrag[2 * h] = pack_bf16x2(ds[0] * mrn, ds[1] * mrn);
+                        dqfrag[2 * h + 1] = pack_bf16x2(ds[2] * mrn, ds[3] * mrn);
+                    }
                 }
-                float pw[4], ds[4];
-                const int qbase = 32 * qb + 8 * gq + 4 * h;   // register i is query qbase + i
-                const i32x4 qps = *(const i32x4*)&sm.pos[s3][qbase];
-                const i32x4 qbk = *(const i32x4*)&sm.bkt[s3][qbase];
-                const f32x4 zq = *(const f32x4*)&sm.zz[par][qbase];
-                const f32x4 dq4 = *(const f32x4*)&sm.dd[par][qbase];
+                if (do_dkv) {
+                    const bf16x8 bp = __builtin_bit_cast(bf16x8, pfrag);
+                    const bf16x8 bd = __builtin_bit_cast(bf16x8, dsfrag);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const bool ok = qbk[i] == mbkt && (!dm.causal || mpos <= qps[i]);
-                    const float s2 = sacc[i] * mrn * c2 - (mpos == qps[i] ? pen2 : 0.f);
-                    pw[i] = pair_weight(ok, mpos == qps[i], s2, zq[i] * kLog2e,
-                                        zq[i] < -0.5f * kSelfPenalty, inv_nh);
-                    ds[i] = pw[i] * (pacc[i] - dq4[i]);
-                    if constexpr (KN) msdd = fmaf(ds[i], sacc[i], msdd);
+                    for (int dt = 0; dt < DT; ++dt) {
+                        const int off = 16 * dt * TS + 32 * qb;
+                        const bf16x8 aq = __builtin_bit_cast(bf16x8, *(const u32x4*)(xtc + off));
+                        const bf16x8 ag = __builtin_bit_cast(bf16x8, *(const u32x4*)(gt_l + off));
+                        dk[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, bd, dk[dt], 0, 0, 0);
+                        dvv[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag, bp, dvv[dt], 0, 0, 0);
+                    }
                 }
-                pfrag[2 * h] = pack_bf16x2(pw[0], pw[1]);
-                pfrag[2 * h + 1] = pack_bf16x2(pw[2], pw[3]);
-                dsfrag[2 * h] = pack_bf16x2(ds[0], ds[1]);
-                dsfrag[2 * h + 1] = pack_bf16x2(ds[2], ds[3]);
             }
-            const bf16x8 bp = __builtin_bit_cast(bf16x8, pfrag);
-            const bf16x8 bd = __builtin_bit_cast(bf16x8, dsfrag);
+            if (do_ds) {   // zeros for a skipped block: the dq pass reads every key block it keeps
+                if constexpr (!KN) dqfrag = dsfrag;
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const bf16x8 aq = __builtin_bit_cast(
-                    bf16x8, *(const u32x4*)&sm.xt[par][dt * 16 + r16][32 * qb + 8 * gq]);
-                const bf16x8 ag = __builtin_bit_cast(
-                    bf16x8, *(const u32x4*)&sm.gt[dt * 16 + r16][32 * qb + 8 * gq]);
-                dk[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, bd, dk[dt], 0, 0, 0);
-                dvv[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag, bp, dvv[dt], 0, 0, 0);
+                for (int e = 0; e < 8; ++e)
+                    dsw[qb * (32 * kDsRow + 2 * kDsGap) + e * kDsRow] =
+                        (uint16_t)(dqfrag[e >> 1] >> (16 * (e & 1)));
             }
         }
     };
-    // rows (dq + dk) * scale and dv of one slot; lane (slot, gq) holds
-    // features 16 dt + 4 gq + i of dk and dv, and dq waits in xq (the query
-    // waves write the next chunk's only after the barrier that ends this pass)
-    auto write_out = [&](int32_t mpos, float mrn, float msdd, f32x4(&dk)[DT], f32x4(&dvv)[DT]) {
-        const int64_t row = ((bh * L + mpos) * dm.nh + r) * D;
+
+    // Phase B: dq^T tiles (16 features x 16 queries) of chunk c over the keys
+    // of chunks c - 1 (blocks 0, 1) and c (blocks 2, 3). A: the keys'
+    // transposed rows; B: lane (r16, gq) reads keys 32 kb + 8 gq .. + 7 of
+    // query 16 qt + r16 from the dS buffer. Lane (r16, gq) of tile j ends
+    // with features 16 dq_dt + 4 gq + i of query 16 (dq_qt + j) + r16. The
+    // blocks' bucket bounds are read together and turned into one mask, so
+    // the pass waits on LDS once for them.
+    auto dq_pass = [&](int c, f32x4(&dqa)[TPW]) {
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) dqa[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        const int s3 = c % 3, sp3 = (c + 2) % 3;   // slots of chunks c and c - 1
+        int qlo[TPW], qhi[TPW], klo[4], khi[4];
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            qlo[j] = sm.bkt[s3][16 * (dq_qt + j)];
+            qhi[j] = sm.bkt[s3][16 * (dq_qt + j) + 15];
+        }
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            klo[kb] = sm.bkt[kb < 2 ? sp3 : s3][32 * (kb & 1)];
+            khi[kb] = sm.bkt[kb < 2 ? sp3 : s3][32 * (kb & 1) + 31];
+        }
+        uint32_t act = 0;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int j = 0; j < TPW; ++j) {
+                const bool a = (kb >= 2 || c > 0) & (klo[kb] <= qhi[j]) & (khi[kb] >= qlo[j]) &
+                               !(kb >= 2 && dm.causal && 32 * (kb & 1) > 16 * (dq_qt + j) + 15);
+                act |= (uint32_t)a << (kb * TPW + j);
+            }
+        act = __builtin_amdgcn_readfirstlane(act);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            if (((act >> (kb * TPW)) & ((1u << TPW) - 1)) == 0) continue;
+            const int tk = kb < 2 ? c - 1 : c;
+            const bf16x8 ak = __builtin_bit_cast(
+                bf16x8, *(const u32x4*)(xtq_l + (tk & 1) * D * TS + 32 * (kb & 1)));
+#pragma unroll
+            for (int j = 0; j < TPW; ++j) {
+                if (!((act >> (kb * TPW + j)) & 1)) continue;
+                const bf16x8 bd = __builtin_bit_cast(
+                    bf16x8, *(const u32x4*)(dsr_l + j * (16 * kDsRow + kDsGap) + 32 * kb));
+                dqa[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bd, dqa[j], 0, 0, 0);
+            }
+        }
+    };
+
+    // Rows (dq + dk) * scale and dv of this wave's 16 keys (chunk t). Lane
+    // (key, gq) holds features 16 dt + 4 gq + i of dk and dv, and dq waits in
+    // xq. The finished rows are staged in LDS (dx over dq in xq, dv in vr,
+    // which is parked again only after the next barrier) and stored 16 bytes
+    // per lane with D / 8 lanes per row, so each store writes whole rows
+    // instead of 32-byte pieces of 16 rows.
+    auto write_out = [&](int t) {
         if constexpr (KN) {
             // dk = rn (sum dS x_i - rn^2 (sum dS x_i . x_j) x_j); the lanes of a
-            // slot hold disjoint query sets, so their sums are added first
-            msdd += __shfl_xor(msdd, 16);
-            msdd += __shfl_xor(msdd, 32);
-            const float pr = mrn * mrn * msdd;
+            // key hold disjoint query sets, so their sums are added first
+            float sd = msdd;
+            sd += __shfl_xor(sd, 16);
+            sd += __shfl_xor(sd, 32);
+            const float pr = mrn * mrn * sd;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 const uint2 w = *(const uint2*)(X + (int64_t)mpos * D + 16 * dt + 4 * gq);
@@ -743,122 +824,98 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_run_kernel(const uint16_t* __
                 dk[dt] = (dk[dt] - pr * xm) * mrn;
             }
         }
+        uint16_t* const xs = &sm.xq[me][4 * gq];
+        uint16_t* const vs = &sm.vr[me][4 * gq];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            const uint2 w = *(const uint2*)&sm.xq[me][16 * dt + 4 * gq];
+            const uint2 w = *(const uint2*)(xs + 16 * dt);
             const f32x4 dq = {__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
                               __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
             const f32x4 a = (dq + dk[dt]) * scale;
             const f32x4 b = dvv[dt];
-            *(uint2*)(dx_r + row + 16 * dt + 4 * gq) =
-                make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
-            *(uint2*)(dv_r + row + 16 * dt + 4 * gq) =
-                make_uint2(pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3]));
+            *(uint2*)(xs + 16 * dt) = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+            *(uint2*)(vs + 16 * dt) = make_uint2(pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3]));
+        }
+        // the wave's own rows only: its LDS writes above land before these reads
+        constexpr int PCS = D / 8, RPI = 64 / PCS;   // 16-byte pieces per row, rows per store
+        const int pc = lane % PCS;
+#pragma unroll
+        for (int k = 0; k < 16 / RPI; ++k) {
+            const int item = 16 * wg + RPI * k + lane / PCS;
+            const int64_t row = ((bh * L + sm.pos[t % 3][item]) * dm.nh + r) * D + 8 * pc;
+            *(u32x4*)(dx_r + row) = *(const u32x4*)&sm.xq[item][8 * pc];
+            *(u32x4*)(dv_r + row) = *(const u32x4*)&sm.vr[item][8 * pc];
         }
     };
 
-    // ---- prologue: sorted keys of chunks c0 - 1 .. c0 + 1, rows of chunks
-    // c0 - 1 and c0 (and their transposes)
+    // ---- prologue: sorted keys of chunks c0 - 1 .. c0 + 1; chunk c0 - 1's
+    // keys to the set that owns it (for chunk c0's dq), then chunk c0's rows
     if (tid < kBM)
         for (int t = max(c0 - 1, 0); t <= min(c0 + 1, clast); ++t) load_keys(t);
     __syncthreads();
     Pre pf;
     if (c0 > 0) {
         gather(c0 - 1, pf);
-        park(c0 - 1, pf);
+        park(pf);
+        __syncthreads();
+        transpose_items<D, kBwdThreads>(sm.xr, sm.xt[(c0 - 1) & 1]);
+        if (wset == ((c0 - 1) & 1)) take_keys(c0 - 1);
+        __syncthreads();
     }
     gather(c0, pf);
-    park(c0, pf);   // the same thread overwrites the output-gradient rows
+    park(pf);
     __syncthreads();
-    if (c0 > 0) transpose_items<D, kBwdThreads>(sm.xr[(c0 - 1) & 1], sm.xt[(c0 - 1) & 1]);
-    transpose_items<D, kBwdThreads>(sm.xr[c0 & 1], sm.xt[c0 & 1]);
+    transpose_items<D, kBwdThreads>(sm.xr, sm.xt[c0 & 1]);
     transpose_items<D, kBwdThreads>(sm.gr, sm.gt);
+    if (wset == (c0 & 1)) take_keys(c0);
     __syncthreads();
 
-    // One set of variables, two roles: query waves keep chunk c's qk and
-    // output-gradient fragments (fa, fb) and dq (acc); key waves keep their
-    // key chunk's qk and v fragments (fa, fb), dk (acc) and dv (acc2),
-    // carried into the next step, where the key side of pair (c + 1, c)
-    // finishes them.
-    bf16x8 fa[KSTEPS], fb[KSTEPS];
-    f32x4 acc[DT], acc2[DT];
-    int32_t mpos = 0, mbkt = -1;
-    float mrn = 1.f, msdd = 0.f;
     for (int c = c0; c <= clast; ++c) {
-        const bool mine = c < c1;          // chunk c belongs to this run
+        const bool mine = c < c1;          // chunk c's queries belong to this run
         const bool nxt = c + 1 <= clast;   // chunk c + 1 is stepped by this run
-        const int par = c & 1, s3 = c % 3;
+        const bool own = wset == (c & 1);  // this wave's keys are chunk c's (else c - 1's)
         // sorted keys of chunk c + 2 and rows of chunk c + 1 start travelling
         int32_t kp2 = 0, kb2 = -1;
         if (tid < kBM && c + 2 <= clast) read_key<PACKED>(P, Bk, (int64_t)(c + 2) * kBM + tid, kp2, kb2);
         if (nxt) gather(c + 1, pf);
-        const int mlo = sm.bkt[s3][16 * wg], mhi = sm.bkt[s3][16 * wg + 15];
-        if (qside) {
-            if (mine) {
-                // chunk c as queries against chunks c - 1 and c
-#pragma unroll
-                for (int s = 0; s < KSTEPS; ++s) {
-                    fa[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.xr[par][prow][32 * s + 8 * gq]);
-                    fb[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.gr[prow][32 * s + 8 * gq]);
-                }
-                mpos = sm.pos[s3][me];
-                mbkt = sm.bkt[s3][me];
-                const float mz = sm.zz[par][me], mD = sm.dd[par][me];
-                const bool self_only = mz < -0.5f * kSelfPenalty;
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) acc[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-                if (c > 0)
-                    query_pass(c - 1, false, fa, fb, mpos, mbkt, mz * kLog2e, mD, self_only, mlo, mhi, acc);
-                query_pass(c, true, fa, fb, mpos, mbkt, mz * kLog2e, mD, self_only, mlo, mhi, acc);
-            }
-        } else {
-            // chunk c - 1 as keys against chunk c's queries, then its rows out
-            if (c > c0) {
-                const int s3p = (c - 1) % 3;   // chunk c - 1's keys: this wave's bucket range
-                key_pass(c, false, fa, fb, mpos, mbkt, mrn, sm.bkt[s3p][16 * wg],
-                         sm.bkt[s3p][16 * wg + 15], acc, acc2, msdd);
-                write_out(mpos, mrn, msdd, acc, acc2);
-            }
-            if (mine) {
-                // chunk c as keys against its own queries
-#pragma unroll
-                for (int s = 0; s < KSTEPS; ++s) {
-                    fa[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.xr[par][prow][32 * s + 8 * gq]);
-                    fb[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)&sm.vr[par][prow][32 * s + 8 * gq]);
-                }
-                mpos = sm.pos[s3][me];
-                mbkt = sm.bkt[s3][me];
-                mrn = KN ? sm.rn[par][me] : 1.f;
-                msdd = 0.f;
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) acc[dt] = acc2[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-                key_pass(c, true, fa, fb, mpos, mbkt, mrn, mlo, mhi, acc, acc2, msdd);
-            }
+        // A
+        if (own) {
+            if (mine) key_step(c, true, true, true);
+        } else if (c > 0) {
+            key_step(c, false, c > c0, mine);
         }
-        __syncthreads();   // chunk c - 1's slot, chunk c's gradients and xq (read by the write-out) are free
-        if (qside && mine) {
+        __syncthreads();   // the dS buffer is complete
+        // B
+        if (!own && c > c0) write_out(c - 1);   // chunk c - 1 is finished
+        f32x4 dqa[TPW];
+        if (mine) dq_pass(c, dqa);
+        __syncthreads();   // xq, the row buffers, chunk c - 1's keys slot and xt slot are free
+        // C
+        if (mine) {
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-                *(uint2*)&sm.xq[me][16 * dt + 4 * gq] =
-                    make_uint2(pack_bf16x2(acc[dt][0], acc[dt][1]), pack_bf16x2(acc[dt][2], acc[dt][3]));
+            for (int j = 0; j < TPW; ++j)
+                *(uint2*)(&sm.xq[16 * dq_qt + r16][16 * dq_dt + 4 * gq] + 16 * j * RS) =
+                    make_uint2(pack_bf16x2(dqa[j][0], dqa[j][1]), pack_bf16x2(dqa[j][2], dqa[j][3]));
         }
         if (nxt) {
-            park(c + 1, pf);
+            park(pf);
             if (tid < kBM && c + 2 <= clast) {
                 sm.pos[(c + 2) % 3][tid] = kp2;
                 sm.bkt[(c + 2) % 3][tid] = kb2;
             }
         }
         __syncthreads();
+        // D
         if (nxt) {
-            transpose_items<D, kBwdThreads>(sm.xr[(c + 1) & 1], sm.xt[(c + 1) & 1]);
+            transpose_items<D, kBwdThreads>(sm.xr, sm.xt[(c + 1) & 1]);
             transpose_items<D, kBwdThreads>(sm.gr, sm.gt);
+            if (!own) take_keys(c + 1);
         }
         __syncthreads();
     }
     // a run that ends its segment finishes its last chunk here: there is no
-    // pair (c1, c1 - 1)
-    if (!qside && c1 == nchunks) write_out(mpos, mrn, msdd, acc, acc2);
+    // look-back pair for it
+    if (c1 == nchunks && wset == ((c1 - 1) & 1)) write_out(c1 - 1);
 }
 
 template <int D, typename T, bool PACKED>
