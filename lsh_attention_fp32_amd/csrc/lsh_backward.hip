@@ -466,19 +466,23 @@ __device__ __forceinline__ int phys_row(int j) {
 }
 
 // Transposes the 64 rows of `rm` (stored at phys_row(item)) into `tr`
-// ([D][TS], item order) inside LDS. The 64 lanes of a wave take the 64 items
-// at one 8-feature piece: the 16-byte reads land on distinct banks and each
-// of the 8 two-byte writes covers 128 contiguous bytes of a transposed row.
+// ([D][TS], item order) inside LDS. A thread takes items 2m and 2m + 1 at
+// one 8-feature piece and writes 8 words, each holding both items' values of
+// one feature: the 32 lanes of a piece fill 128 contiguous bytes of a
+// transposed row, and a wave's two pieces land 32 banks apart.
 template <int D, int NT>
 __device__ __forceinline__ void transpose_items(const uint16_t (*rm)[BwdRows<D>::RS],
                                                 uint16_t (*tr)[BwdRows<D>::TS]) {
-    const int item = threadIdx.x & (kBM - 1);
-    const int row = phys_row(item);
-    for (int pc = threadIdx.x >> 6; pc < D / 8; pc += NT / kBM) {
-        const u32x4 a = *(const u32x4*)&rm[row][pc * 8];
+    const int m = threadIdx.x & 31;
+    for (int pc = threadIdx.x >> 5; pc < D / 8; pc += NT / 32) {
+        const u32x4 a = *(const u32x4*)&rm[phys_row(2 * m)][pc * 8];
+        const u32x4 b = *(const u32x4*)&rm[phys_row(2 * m + 1)][pc * 8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            tr[pc * 8 + e][item] = (uint16_t)((a[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t lo = (a[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+            const uint32_t hi = (b[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+            *(uint32_t*)&tr[pc * 8 + e][2 * m] = lo | (hi << 16);
+        }
     }
 }
 
@@ -540,7 +544,7 @@ struct alignas(16) BwdRunLds {
     uint16_t xt[2][D][TS];     // qk transposed (item order), chunk t in slot t & 1
     uint16_t gt[D][TS];        // output gradients of chunk c transposed
     uint16_t ds[kBM * kDsRow + (kBM / 16) * kDsGap];   // dS of step c by [query][key]
-    uint16_t xq[kBM][RS];      // dq of the chunk whose keys finish next (bf16, item order)
+    uint16_t xq[2][kBM][RS];   // dq of chunk t in slot t & 1 (bf16, item order)
     int32_t pos[3][kBM], bkt[3][kBM];   // chunk t in slot t % 3
     float zz[kBM], dd[kBM], rn[kBM];    // chunk c's Z, D and 1 / |x|
 };
@@ -559,7 +563,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_run_kernel(const uint16_t* __
                                                               uint16_t* __restrict__ dv_r) {
     constexpr int KSTEPS = D / 32, DT = D / 16;
     constexpr int PER = kBM * (D / 8) / kBwdThreads;   // 16-byte pieces per thread and source
-    constexpr int TPW = DT / 2;                        // dq tiles (16 features x 16 queries) per wave
+    constexpr int DPW = DT / 4;   // dq feature tiles (of 16) per wave of the set computing dq
     static_assert(PER >= 1, "every thread moves a piece of each row set");
     __shared__ BwdRunLds<D> sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -586,8 +590,6 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_run_kernel(const uint16_t* __
     const float scale = 1.0f / sqrtf((float)D);
     const int me = 16 * wg + r16;   // this lane's key within its chunk
     const int prow = phys_row(me);
-    // dq tiles of this wave: feature tile dq_dt, query tiles dq_qt .. + TPW - 1
-    const int dq_dt = wave % DT, dq_qt = (wave / DT) * TPW;   // dq_qt is even
     // Per-lane LDS addresses; every tile below is a constant offset from one
     // of them (row r16, column 8 gq of the row-major and transposed buffers).
     constexpr int RS = BwdRows<D>::RS, TS = BwdRows<D>::TS;
@@ -595,11 +597,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_run_kernel(const uint16_t* __
     const uint16_t* const gr_l = &sm.gr[r16][8 * gq];
     const uint16_t* const xt_l = &sm.xt[0][r16][8 * gq];
     const uint16_t* const gt_l = &sm.gt[r16][8 * gq];
-    const uint16_t* const xtq_l = xt_l + 16 * dq_dt * TS;
+    const uint16_t* const xtq_l = xt_l + 16 * DPW * wg * TS;   // this wave's first dq feature tile
     // dS writes: query 32 qb + 8 gq + e, key me (+ 64 for chunk c's keys)
     uint16_t* const dsw_l = &sm.ds[8 * gq * kDsRow + (gq >> 1) * kDsGap + me];
-    // dS reads: query 16 qt + r16 (qt = dq_qt + j), keys 32 kb + 8 gq .. + 7
-    const uint16_t* const dsr_l = &sm.ds[(16 * dq_qt + r16) * kDsRow + dq_qt * kDsGap + 8 * gq];
+    // dS reads: query 16 qt + r16, keys 32 kb + 8 gq .. + 7
+    const uint16_t* const dsr_l = &sm.ds[r16 * kDsRow + 8 * gq];
 
     // rows of chunk t (positions in its pos slot) into registers, then LDS
     struct Pre {
@@ -754,52 +756,46 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_run_kernel(const uint16_t* __
         }
     };
 
-    // Phase B: dq^T tiles (16 features x 16 queries) of chunk c over the keys
-    // of chunks c - 1 (blocks 0, 1) and c (blocks 2, 3). A: the keys'
-    // transposed rows; B: lane (r16, gq) reads keys 32 kb + 8 gq .. + 7 of
-    // query 16 qt + r16 from the dS buffer. Lane (r16, gq) of tile j ends
-    // with features 16 dq_dt + 4 gq + i of query 16 (dq_qt + j) + r16. The
-    // blocks' bucket bounds are read together and turned into one mask, so
-    // the pass waits on LDS once for them.
-    auto dq_pass = [&](int c, f32x4(&dqa)[TPW]) {
+    // Phase B, the set that owns chunk c's keys: dq^T tiles (16 features x
+    // 16 queries) of chunk c over the keys of chunks c - 1 (blocks 0, 1) and c
+    // (blocks 2, 3); wave wg takes feature tiles DPW wg .. + DPW - 1 of all
+    // four query tiles. A: the keys' transposed rows; B: lane (r16, gq) reads
+    // keys 32 kb + 8 gq .. + 7 of query 16 qt + r16 from the dS buffer, each
+    // read serving DPW products. Lane (r16, gq) of tile (u, qt) ends with
+    // features 16 (DPW wg + u) + 4 gq + i of query 16 qt + r16, stored to xq.
+    // Every tile is computed (a skipped block left zeros in the dS buffer):
+    // without per-tile tests all operand reads issue ahead of the products.
+    auto dq_pass = [&](int c) {
+        f32x4 dqa[DPW][4];
 #pragma unroll
-        for (int j = 0; j < TPW; ++j) dqa[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        const int s3 = c % 3, sp3 = (c + 2) % 3;   // slots of chunks c and c - 1
-        int qlo[TPW], qhi[TPW], klo[4], khi[4];
+        for (int u = 0; u < DPW; ++u)
 #pragma unroll
-        for (int j = 0; j < TPW; ++j) {
-            qlo[j] = sm.bkt[s3][16 * (dq_qt + j)];
-            qhi[j] = sm.bkt[s3][16 * (dq_qt + j) + 15];
-        }
+            for (int qt = 0; qt < 4; ++qt) dqa[u][qt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            klo[kb] = sm.bkt[kb < 2 ? sp3 : s3][32 * (kb & 1)];
-            khi[kb] = sm.bkt[kb < 2 ? sp3 : s3][32 * (kb & 1) + 31];
-        }
-        uint32_t act = 0;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int j = 0; j < TPW; ++j) {
-                const bool a = (kb >= 2 || c > 0) & (klo[kb] <= qhi[j]) & (khi[kb] >= qlo[j]) &
-                               !(kb >= 2 && dm.causal && 32 * (kb & 1) > 16 * (dq_qt + j) + 15);
-                act |= (uint32_t)a << (kb * TPW + j);
-            }
-        act = __builtin_amdgcn_readfirstlane(act);
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            if (((act >> (kb * TPW)) & ((1u << TPW) - 1)) == 0) continue;
+            if (kb < 2 && c == 0) continue;   // no chunk before the first
             const int tk = kb < 2 ? c - 1 : c;
-            const bf16x8 ak = __builtin_bit_cast(
-                bf16x8, *(const u32x4*)(xtq_l + (tk & 1) * D * TS + 32 * (kb & 1)));
+            bf16x8 ak[DPW];
 #pragma unroll
-            for (int j = 0; j < TPW; ++j) {
-                if (!((act >> (kb * TPW + j)) & 1)) continue;
+            for (int u = 0; u < DPW; ++u)
+                ak[u] = __builtin_bit_cast(bf16x8, *(const u32x4*)(xtq_l + (tk & 1) * D * TS +
+                                                                   16 * u * TS + 32 * (kb & 1)));
+#pragma unroll
+            for (int qt = 0; qt < 4; ++qt) {
                 const bf16x8 bd = __builtin_bit_cast(
-                    bf16x8, *(const u32x4*)(dsr_l + j * (16 * kDsRow + kDsGap) + 32 * kb));
-                dqa[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bd, dqa[j], 0, 0, 0);
+                    bf16x8, *(const u32x4*)(dsr_l + qt * (16 * kDsRow + kDsGap) + 32 * kb));
+#pragma unroll
+                for (int u = 0; u < DPW; ++u)
+                    dqa[u][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[u], bd, dqa[u][qt], 0, 0, 0);
             }
         }
+#pragma unroll
+        for (int u = 0; u < DPW; ++u)
+#pragma unroll
+            for (int qt = 0; qt < 4; ++qt)
+                *(uint2*)&sm.xq[c & 1][16 * qt + r16][16 * (DPW * wg + u) + 4 * gq] =
+                    make_uint2(pack_bf16x2(dqa[u][qt][0], dqa[u][qt][1]),
+                               pack_bf16x2(dqa[u][qt][2], dqa[u][qt][3]));
     };
 
     // Rows (dq + dk) * scale and dv of this wave's 16 keys (chunk t). Lane
@@ -824,7 +820,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_run_kernel(const uint16_t* __
                 dk[dt] = (dk[dt] - pr * xm) * mrn;
             }
         }
-        uint16_t* const xs = &sm.xq[me][4 * gq];
+        uint16_t* const xs = &sm.xq[t & 1][me][4 * gq];
         uint16_t* const vs = &sm.vr[me][4 * gq];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
@@ -843,7 +839,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_run_kernel(const uint16_t* __
         for (int k = 0; k < 16 / RPI; ++k) {
             const int item = 16 * wg + RPI * k + lane / PCS;
             const int64_t row = ((bh * L + sm.pos[t % 3][item]) * dm.nh + r) * D + 8 * pc;
-            *(u32x4*)(dx_r + row) = *(const u32x4*)&sm.xq[item][8 * pc];
+            *(u32x4*)(dx_r + row) = *(const u32x4*)&sm.xq[t & 1][item][8 * pc];
             *(u32x4*)(dv_r + row) = *(const u32x4*)&sm.vr[item][8 * pc];
         }
     };
@@ -885,18 +881,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_run_kernel(const uint16_t* __
             key_step(c, false, c > c0, mine);
         }
         __syncthreads();   // the dS buffer is complete
-        // B
-        if (!own && c > c0) write_out(c - 1);   // chunk c - 1 is finished
-        f32x4 dqa[TPW];
-        if (mine) dq_pass(c, dqa);
-        __syncthreads();   // xq, the row buffers, chunk c - 1's keys slot and xt slot are free
-        // C
-        if (mine) {
-#pragma unroll
-            for (int j = 0; j < TPW; ++j)
-                *(uint2*)(&sm.xq[16 * dq_qt + r16][16 * dq_dt + 4 * gq] + 16 * j * RS) =
-                    make_uint2(pack_bf16x2(dqa[j][0], dqa[j][1]), pack_bf16x2(dqa[j][2], dqa[j][3]));
+        // B: one set writes chunk c - 1 out, the other computes chunk c's dq
+        if (!own) {
+            if (c > c0) write_out(c - 1);   // chunk c - 1 is finished
+        } else if (mine) {
+            dq_pass(c);
         }
+        __syncthreads();   // the row buffers, chunk c - 1's keys slot and xt slot are free
+        // C
         if (nxt) {
             park(pf);
             if (tid < kBM && c + 2 <= clast) {
