@@ -500,13 +500,18 @@ __device__ __forceinline__ void transpose_items(const uint16_t (*rm)[BwdRows<D>:
 //      transposed rows from LDS), and writes its dS (times the key's 1/|x|
 //      under key normalisation) into a [query][key] LDS buffer;
 //   B: the set owning chunk c - 1 writes that chunk's rows out ((dq + dk)
-//      scaled, and dv), its dq waiting in LDS since step c - 1; every wave
-//      then computes its share of dq for chunk c = dS x_k over the 128 keys
-//      (the keys' transposed rows and the dS buffer from LDS);
-//   C: dq of chunk c goes to LDS; chunk c + 1's rows, gathered into
-//      registers since the top of the step, are parked in LDS;
+//      scaled, and dv; its dq has waited in LDS since step c - 1), while the
+//      set owning chunk c computes chunk c's dq = dS x_k over the 128 keys
+//      (the keys' transposed rows and the dS buffer from LDS) into the other
+//      dq slot;
+//   C: chunk c + 1's rows, gathered into registers since the top of the
+//      step, are parked in LDS;
 //   D: chunk c + 1's rows are transposed, and the set that just wrote chunk
 //      c - 1 out takes chunk c + 1's keys.
+// Four barriers a step; at 64K tokens x 8 heads x 8 rounds (d 128) a step
+// takes ~10.7 K cycles: about 38 % in A, 18 % waiting at the barrier after
+// A (the two sets' key blocks skip different amounts of causal work), 24 %
+// in B and its barrier, and 21 % in C and D with theirs.
 // Every score is computed once. The first step of a run scores the look-back
 // pair for dq only (the run before finishes that chunk's dk, dv); a run that
 // does not end its segment closes with a partial step on the next chunk
