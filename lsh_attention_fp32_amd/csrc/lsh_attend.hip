@@ -539,20 +539,22 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
                 const f16x4 h = {(_Float16)o.x, (_Float16)o.y, (_Float16)o.z, (_Float16)o.w};
                 hv[dt] = __builtin_bit_cast(u32x2, h);
             }
-            const int src_a = r16 + 32 * (g & 1);   // holds features 8 (g % 2) + 0..3
-            const bool upper = g >= 2;               // wants the odd feature tile of each pair
+            // Lane (r16, g) holds A = features 32 k + 4 g .. + 3 (tile 2 k) and
+            // B = 32 k + 16 + 4 g .. + 3 (tile 2 k + 1); lane g stores features
+            // 32 k + 8 g .. + 7, i.e. A of lanes 2 g, 2 g + 1 (g < 2) or B of
+            // lanes 2 g - 4, 2 g - 3. A lane swap between the two halves of
+            // the wave (lanes 32 apart) and one between 16-lane rows do that
+            // exchange on the vector unit.
             _Float16* orow = (_Float16*)o_sorted + orow_idx * D;
 #pragma unroll
             for (int k = 0; k < DT / 2; ++k) {
-                uint32_t w[4];
-#pragma unroll
-                for (int q = 0; q < 2; ++q)
-#pragma unroll
-                    for (int h2 = 0; h2 < 2; ++h2) {
-                        const uint32_t a = __shfl(hv[2 * k][h2], src_a + 16 * q);
-                        const uint32_t b = __shfl(hv[2 * k + 1][h2], src_a + 16 * q);
-                        w[2 * q + h2] = upper ? b : a;
-                    }
+                // A of rows 0, 1 with B of rows 0, 1 | A of rows 2, 3 with B of rows 2, 3
+                const auto s0 = __builtin_amdgcn_permlane32_swap(hv[2 * k][0], hv[2 * k + 1][0], false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(hv[2 * k][1], hv[2 * k + 1][1], false, false);
+                // then rows pair up: lane g holds its 8 features' low 4 in [0], high 4 in [1]
+                const auto t0 = __builtin_amdgcn_permlane16_swap(s0[0], s0[1], false, false);
+                const auto t1 = __builtin_amdgcn_permlane16_swap(s1[0], s1[1], false, false);
+                const uint32_t w[4] = {t0[0], t1[0], t0[1], t1[1]};
                 *(u32x4*)(orow + 32 * k + 8 * g) =
                     (u32x4){(w[0] & 0xFFFEFFFEu) | pat[0], (w[1] & 0xFFFEFFFEu) | pat[1],
                             (w[2] & 0xFFFEFFFEu) | pat[2], (w[3] & 0xFFFEFFFEu) | pat[3]};
