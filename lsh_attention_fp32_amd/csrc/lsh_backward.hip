@@ -398,14 +398,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 
 // The same sum for the bf16 rows of the matrix-core pass and bf16 outputs:
 // one thread per (token, 8 features), 16-byte nontemporal loads (the rows are
-// read once), fp32 sums.
+// read once), fp32 sums. Blocks run from the last token back: the matrix-core
+// pass writes the last (batch, head) slices' rows last, and those are still
+// in the memory-side cache when this pass starts.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_reduce_bf16_kernel(const uint16_t* __restrict__ dx_r,
                                                               const uint16_t* __restrict__ dv_r,
                                                               Dims dm, uint16_t* __restrict__ dqk,
                                                               uint16_t* __restrict__ dv) {
     typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t gid = (int64_t)(gridDim.x - 1 - blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t tok = gid / (D / 8);
     const int e = 8 * (int)(gid - tok * (D / 8));
     if (tok >= dm.T) return;
