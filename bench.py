@@ -491,6 +491,9 @@ def main() -> int:
     ap.add_argument("--separate-qk", action="store_true",
                     help="time the separate-queries-and-keys ablation (lsh_attention_fwd_qk) "
                          "at the workload's shape")
+    ap.add_argument("--non-causal", action="store_true",
+                    help="with --sweep: the sixteen length-sweep points without the causal "
+                         "mask (the sweep's workloads are causal)")
     ap.add_argument("--per-head-r", action="store_true",
                     help="time the per-head rotations variant (R [H, nh, d, nb/2]); combines "
                          "with --key-norm and --train")
@@ -517,9 +520,13 @@ def main() -> int:
     lsh.load_library()
     if args.sweep:
         names = [n for n in workloads.WORKLOADS if n.startswith("sweep_")]
-        names += [n for n in workloads.WORKLOADS if not n.startswith("sweep_")]
+        if not args.non_causal:
+            names += [n for n in workloads.WORKLOADS if not n.startswith("sweep_")]
         for n in names:
             w = workloads.WORKLOADS[n]
+            if args.non_causal:
+                n = n + "_noncausal"
+                w = workloads.scaled(w, name=n, causal=False)
             r = measure(lsh, torch, w, min(args.steps, 10), args.warmup)
             line = {"workload": n, "config": w.describe(), "ms_per_step": r["ms_per_step"],
                     "tokens_per_s": w.B * w.L / (r["ms_per_step"] / 1e3),
