@@ -106,51 +106,14 @@ __global__ __launch_bounds__(kGT) void mfma_kernel(const uint16_t* __restrict__ 
     const int n0 = (int)tn * kPN;
     const int64_t m0 = tm * kPM;
 
-    // global -> register staging: row r = tid / 4 + kRows j, piece tid % 4.
-    // Each thread's six row pointers are fixed for the whole k loop; rows
-    // past M or N read the last row instead (their results are never
-    // stored), so a stage's loads are plain pointer + k, no bounds test.
-    const int pr = tid >> 2, pc = (tid & 3) * 8;
-    const uint16_t* wp[kAL];
-    const uint16_t* xp[kBL];
-#pragma unroll
-    for (int j = 0; j < kAL; ++j) wp[j] = wt.row<uint16_t>(min(n0 + pr + kRows * j, N - 1), K) + pc;
-#pragma unroll
-    for (int j = 0; j < kBL; ++j) xp[j] = x + min(m0 + pr + kRows * j, M - 1) * K + pc;
-    u32x4 ra[kAL], rb[kBL];
-    auto load_stage = [&](int k0) {
-        const bool ok = !KTAIL || k0 + pc < K;
-#pragma unroll
-        for (int j = 0; j < kAL; ++j)
-            ra[j] = ok ? *(const u32x4*)(wp[j] + k0) : (u32x4){0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int j = 0; j < kBL; ++j)
-            rb[j] = ok ? *(const u32x4*)(xp[j] + k0) : (u32x4){0u, 0u, 0u, 0u};
-    };
-    auto store_stage = [&](int buf) {
-#pragma unroll
-        for (int j = 0; j < kAL; ++j)
-            *(u32x4*)&sm.a[buf][pr + kRows * j][8 * ((pc >> 3) ^ swz(pr + kRows * j))] = ra[j];
-#pragma unroll
-        for (int j = 0; j < kBL; ++j)
-            *(u32x4*)&sm.b[buf][pr + kRows * j][8 * ((pc >> 3) ^ swz(pr + kRows * j))] = rb[j];
-    };
-
     f32x16 acc[kNB][kMB];
 #pragma unroll
     for (int i = 0; i < kNB; ++i)
 #pragma unroll
         for (int j = 0; j < kMB; ++j) acc[i][j] = (f32x16){};
-
-    // the next stage's rows travel into registers while this stage computes
     const int nstages = (K + kPK - 1) / kPK;
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
     const int fr = lane & 31, fk = 8 * (lane >> 5);
-    for (int s = 0; s < nstages; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < nstages) load_stage((s + 1) * kPK);
+    auto compute = [&](int buf) {
 #pragma unroll
         for (int kk = 0; kk < kPK; kk += 16) {
             const int q = (kk + fk) >> 3;   // logical piece of the fragment
@@ -172,8 +135,84 @@ __global__ __launch_bounds__(kGT) void mfma_kernel(const uint16_t* __restrict__ 
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j],
                                                                         0, 0, 0);
         }
-        if (s + 1 < nstages) store_stage(buf ^ 1);
+    };
+
+    // Each thread's row pointers are fixed for the whole k loop; rows past M
+    // or N read the last row instead (their results are never stored), so a
+    // stage's loads are plain pointer + k, no bounds test.
+    if constexpr (!KTAIL) {
+        // Stages go from global memory straight into LDS (one 16-byte piece
+        // per lane, a wave's 64 pieces landing on 16 consecutive 64-byte rows
+        // in lane order): no staging registers, no LDS store instructions.
+        // Lane l of wave w fills row 16 w + l / 4 (+ kRows j) at position
+        // l % 4, which holds logical piece (l % 4) ^ swz(row) = (l % 4) ^ (l / 16),
+        // so it loads that piece. Stage s + 1 is in flight while stage s
+        // computes; the barrier at the end of a stage waits for it.
+        const int wv = __builtin_amdgcn_readfirstlane(wave);
+        const int pr = 16 * wv + (lane >> 2), pq = 8 * ((lane & 3) ^ (lane >> 4));
+        const uint16_t* wp[kAL];
+        const uint16_t* xp[kBL];
+#pragma unroll
+        for (int j = 0; j < kAL; ++j) wp[j] = wt.row<uint16_t>(min(n0 + pr + kRows * j, N - 1), K) + pq;
+#pragma unroll
+        for (int j = 0; j < kBL; ++j) xp[j] = x + min(m0 + pr + kRows * j, M - 1) * K + pq;
+        typedef __attribute__((address_space(3))) void* lds_ptr;
+        auto load_stage = [&](int k0, int buf) {
+#pragma unroll
+            for (int j = 0; j < kAL; ++j)
+                __builtin_amdgcn_global_load_lds((const void*)(wp[j] + k0),
+                                                 (lds_ptr)&sm.a[buf][16 * wv + kRows * j][0], 16, 0, 0);
+#pragma unroll
+            for (int j = 0; j < kBL; ++j)
+                __builtin_amdgcn_global_load_lds((const void*)(xp[j] + k0),
+                                                 (lds_ptr)&sm.b[buf][16 * wv + kRows * j][0], 16, 0, 0);
+        };
+        load_stage(0, 0);
         __syncthreads();
+        for (int s = 0; s < nstages; ++s) {
+            if (s + 1 < nstages) load_stage((s + 1) * kPK, (s + 1) & 1);
+            compute(s & 1);
+            __syncthreads();
+        }
+    } else {
+        // K not a multiple of kPK: register staging, the last stage's missing
+        // pieces masked to zero (row r = tid / 4 + kRows j, piece tid % 4)
+        const int pr = tid >> 2, pc = (tid & 3) * 8;
+        const uint16_t* wp[kAL];
+        const uint16_t* xp[kBL];
+#pragma unroll
+        for (int j = 0; j < kAL; ++j) wp[j] = wt.row<uint16_t>(min(n0 + pr + kRows * j, N - 1), K) + pc;
+#pragma unroll
+        for (int j = 0; j < kBL; ++j) xp[j] = x + min(m0 + pr + kRows * j, M - 1) * K + pc;
+        u32x4 ra[kAL], rb[kBL];
+        auto load_stage = [&](int k0) {
+            const bool ok = k0 + pc < K;
+#pragma unroll
+            for (int j = 0; j < kAL; ++j)
+                ra[j] = ok ? *(const u32x4*)(wp[j] + k0) : (u32x4){0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int j = 0; j < kBL; ++j)
+                rb[j] = ok ? *(const u32x4*)(xp[j] + k0) : (u32x4){0u, 0u, 0u, 0u};
+        };
+        auto store_stage = [&](int buf) {
+#pragma unroll
+            for (int j = 0; j < kAL; ++j)
+                *(u32x4*)&sm.a[buf][pr + kRows * j][8 * ((pc >> 3) ^ swz(pr + kRows * j))] = ra[j];
+#pragma unroll
+            for (int j = 0; j < kBL; ++j)
+                *(u32x4*)&sm.b[buf][pr + kRows * j][8 * ((pc >> 3) ^ swz(pr + kRows * j))] = rb[j];
+        };
+        // the next stage's rows travel into registers while this stage computes
+        load_stage(0);
+        store_stage(0);
+        __syncthreads();
+        for (int s = 0; s < nstages; ++s) {
+            const int buf = s & 1;
+            if (s + 1 < nstages) load_stage((s + 1) * kPK);
+            compute(buf);
+            if (s + 1 < nstages) store_stage(buf ^ 1);
+            __syncthreads();
+        }
     }
 
     // The results go out through LDS, one half of the tokens at a time: the
