@@ -758,21 +758,30 @@ __global__ __launch_bounds__(256) void hash_scan_kernel(const T* __restrict__ qk
         }
         __syncthreads();
         if (it >= gn) continue;
-        uint64_t best = 0;
-#pragma unroll 2
-        for (int u = 0; u < kHashColTile / 4; ++u) {
-            const int c = cq + 4 * u, col = t * kHashColTile + c;
-            double p = 0.0;
-#pragma unroll 4
-            for (int k = 0; k < D; k += 4) {
-                const f32x4 a = *(const f32x4*)&xs[it][k];
-                const f32x4 b = *(const f32x4*)&rtile[c][k];
+        // The thread's columns cq, cq + 4, ..., each summed in k order in its
+        // own fp64 chain; the chains are independent, so the additions of one
+        // wait behind those of the others instead of behind their own.
+        constexpr int NC = kHashColTile / 4;
+        double p[NC];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) p += (double)a[e] * (double)b[e];
+        for (int u = 0; u < NC; ++u) p[u] = 0.0;
+#pragma unroll 2
+        for (int k = 0; k < D; k += 4) {
+            const f32x4 a = *(const f32x4*)&xs[it][k];
+#pragma unroll
+            for (int u = 0; u < NC; ++u) {
+                const f32x4 b = *(const f32x4*)&rtile[cq + 4 * u][k];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) p[u] += (double)a[e] * (double)b[e];
             }
+        }
+        uint64_t best = 0;
+#pragma unroll
+        for (int u = 0; u < NC; ++u) {
+            const int col = t * kHashColTile + cq + 4 * u;
             if (col < half) {
-                const int bucket = col + (p < 0.0 ? half : 0);
-                const uint64_t key = (__double_as_longlong(fabs(p)) & ~0xFFFull) |
+                const int bucket = col + (p[u] < 0.0 ? half : 0);
+                const uint64_t key = (__double_as_longlong(fabs(p[u])) & ~0xFFFull) |
                                      (uint64_t)(4095 - bucket);
                 best = key > best ? key : best;
             }
