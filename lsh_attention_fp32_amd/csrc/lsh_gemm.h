@@ -79,10 +79,10 @@ inline int64_t mfma_grid(int ntn, int64_t ntm) {
 
 // Waves kWN (n) x 2 (m); each wave owns 32 kNB outputs x 64 tokens (kNB x 2
 // blocks of 32 x 32 accumulators). A stage moves 256 + 128 rows of 64 bytes
-// from HBM into LDS (kAL + kBL 16-byte loads per thread, issued before the
-// current stage's matrix work and stored after it). K and N must be
-// multiples of 8; KTAIL: K is not a multiple of kPK, so the last stage masks
-// its missing pieces.
+// into LDS (kAL + kBL 16-byte pieces per thread, issued before the current
+// stage's matrix work): straight from global memory into LDS when K is a
+// multiple of kPK, else through registers with the last stage's missing
+// pieces masked (KTAIL). K and N must be multiples of 8.
 template <class Out, bool KTAIL>
 __global__ __launch_bounds__(kGT) void mfma_kernel(const uint16_t* __restrict__ x, Weights wt,
                                                    int64_t M, int N, int K, int ntn, int64_t ntm,
