@@ -19,6 +19,9 @@
 //           with equal buckets are grouped by a ballot match, so ranks are
 //           exact and the LDS counter of a hot bucket is bumped once per wave
 //           step (skewed buckets do not serialise on LDS atomics).
+// A segment of one tile (L <= 4096) is its own tile: the tile-local order the
+// scatter builds is the segment's order, so the count and prefix launches are
+// skipped and the scatter alone sorts it.
 #include <mutex>
 
 #include "lsh_internal.h"
@@ -176,7 +179,7 @@ __device__ __forceinline__ void block_exclusive_scan(int32_t* a, int n, int32_t*
 // in their sorted order in LDS, then written out with consecutive threads on
 // consecutive slots, so each (tile, bucket) run leaves as one contiguous
 // piece instead of one 4-byte store per element at scattered slots.
-template <bool PACKED, bool STAGED>
+template <bool PACKED, bool STAGED, bool ONE_TILE>
 __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __restrict__ buckets,
                                                            const int32_t* __restrict__ prefix,
                                                            const int32_t* __restrict__ totals,
@@ -190,6 +193,7 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __rest
     extern __shared__ int32_t sh[];
     __shared__ int32_t wsum[4];
     static_assert(!PACKED || STAGED, "packed keys are staged");
+    static_assert(!ONE_TILE || STAGED, "a one-tile segment is sorted in its staged order");
     constexpr int SUB = kSortTile / kSortWaves;
     // Workgroups are dealt round-robin over the L2 domains (id % kScatterXcds):
     // every tile of a segment gets the same residue, so one L2 collects the
@@ -219,8 +223,9 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __rest
 
     // First slot of this tile's run of every bucket: exclusive scan over
     // buckets of the segment totals, plus this bucket's count in the earlier
-    // tiles (both read with coalesced loads).
-    {
+    // tiles (both read with coalesced loads). A one-tile segment needs
+    // neither: its slots are the tile-local ones.
+    if constexpr (!ONE_TILE) {
         const int32_t* tot = totals + seg * nb;
         const int32_t* pre = prefix + (seg * ntiles + tile) * nb;
         for (int b = threadIdx.x; b < nb; b += 256) {
@@ -262,7 +267,7 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __rest
         block_exclusive_scan(lstart, nb, wsum);
         for (int b = threadIdx.x; b < nb; b += 256) {
             int32_t run = lstart[b];
-            start[b] -= run;
+            start[b] = ONE_TILE ? 0 : start[b] - run;
             for (int w = 0; w < kSortWaves; ++w) {
                 const int32_t c = sh[w * nb + b];
                 sh[w * nb + b] = run;
@@ -325,27 +330,35 @@ hipError_t launch_sort(const int32_t* buckets, const Dims& d, int32_t* perm, int
         (int32_t*)((char*)ws + align_up(sizeof(int32_t) * (size_t)d.segs * d.nb * ntiles, 256));
     const dim3 grid = grid_split((unsigned)ntiles, d.segs);
     hipError_t e;
-    sort_count_kernel<<<grid, 256, sizeof(int32_t) * d.nb, st>>>(buckets, d, ntiles, counts);
-    if ((e = mark(st, ev, nev, names, "sort_count")) != hipSuccess) return e;
-    sort_prefix_kernel<<<grid_split((unsigned)((d.nb + 255) / 256), d.segs), 256, 0, st>>>(
-        counts, totals, d.nb, ntiles, d.segs);
-    if ((e = mark(st, ev, nev, names, "sort_prefix")) != hipSuccess) return e;
     // staged needs positions below 2^kPackPosBits (a packed key per element)
     const bool staged = packed_sort_keys(d);
     if (packed && !staged) return hipErrorInvalidValue;
+    const bool one = staged && ntiles == 1;
+    if (!one) {
+        sort_count_kernel<<<grid, 256, sizeof(int32_t) * d.nb, st>>>(buckets, d, ntiles, counts);
+        if ((e = mark(st, ev, nev, names, "sort_count")) != hipSuccess) return e;
+        sort_prefix_kernel<<<grid_split((unsigned)((d.nb + 255) / 256), d.segs), 256, 0, st>>>(
+            counts, totals, d.nb, ntiles, d.segs);
+        if ((e = mark(st, ev, nev, names, "sort_prefix")) != hipSuccess) return e;
+    }
     static_assert(kSortTile >= kMaxBuckets, "the staged keys' space first holds nb starts");
     const size_t lds = sizeof(int32_t) * ((kSortWaves + 1) * d.nb + (staged ? kSortTile : 0));
     const int64_t sgroups = (d.segs + kScatterXcds - 1) / kScatterXcds;
     const unsigned sgrid = (unsigned)(sgroups * kScatterXcds * ntiles);
-    if (packed)
-        sort_scatter_kernel<true, true><<<sgrid, 256, lds, st>>>(buckets, counts, totals, d,
-                                                                 ntiles, nbits, perm, nullptr);
+#define LSH_SCATTER(P, S, O, INV)                                                            \
+    sort_scatter_kernel<P, S, O><<<sgrid, 256, lds, st>>>(buckets, counts, totals, d, ntiles, \
+                                                          nbits, perm, INV)
+    if (packed && one)
+        LSH_SCATTER(true, true, true, nullptr);
+    else if (packed)
+        LSH_SCATTER(true, true, false, nullptr);
+    else if (one)
+        LSH_SCATTER(false, true, true, inv);
     else if (staged)
-        sort_scatter_kernel<false, true><<<sgrid, 256, lds, st>>>(buckets, counts, totals, d,
-                                                                  ntiles, nbits, perm, inv);
+        LSH_SCATTER(false, true, false, inv);
     else
-        sort_scatter_kernel<false, false><<<sgrid, 256, lds, st>>>(buckets, counts, totals, d,
-                                                                   ntiles, nbits, perm, inv);
+        LSH_SCATTER(false, false, false, inv);
+#undef LSH_SCATTER
     return mark(st, ev, nev, names, "sort_scatter");
 }
 
