@@ -145,27 +145,52 @@ __global__ __launch_bounds__(256) void rmax_kernel(const float* __restrict__ R, 
 //            v_mfma_f32_32x32x16_f16: for (round, tile, k-step), 64 lanes of 8
 //            values, lane l holding column tile*32 + l%32 and
 //            k = kstep*16 + 8*(l/32) + e.
+//
+// ONE: a round is a single tile (n_buckets <= 64). Then the workgroup takes
+// max|R| from its own tile, stores the three bounds without atomics, and
+// workgroup (0, 0) clears what rmax_kernel clears otherwise, so rmax_kernel
+// is not launched.
+template <bool ONE>
 __global__ __launch_bounds__(256) void rprep_kernel(const float* __restrict__ R, int d, int half,
                                                     int ntiles, int nh,
                                                     const float* __restrict__ tmax,
                                                     float* __restrict__ rnorm,
                                                     float* __restrict__ rt,
-                                                    uint16_t* __restrict__ rfrag) {
+                                                    uint16_t* __restrict__ rfrag,
+                                                    int32_t* __restrict__ counter,
+                                                    int32_t* __restrict__ scount) {
     __shared__ float tile[128][kHashColTile + 1];
+    __shared__ float wmax[4];
     const int t = blockIdx.x;
     const int r = (int)block_y();   // R round, of nh
     if (r >= nh) return;
+    if (ONE && t == 0 && r == 0) {
+        if (threadIdx.x < 4) counter[threadIdx.x] = 0;
+        for (int i = threadIdx.x; i < nh; i += 256) scount[i] = 0;
+    }
     const float* Rr = R + (int64_t)r * d * half;
     const int col0 = t * kHashColTile;
+    float m = 0.f;
 #pragma unroll 8
     for (int idx = threadIdx.x; idx < d * kHashColTile; idx += 256) {
         const int k = idx / kHashColTile, c = idx % kHashColTile;
-        tile[k][c] = (col0 + c < half) ? Rr[(int64_t)k * half + col0 + c] : 0.f;
+        const float a = (col0 + c < half) ? Rr[(int64_t)k * half + col0 + c] : 0.f;
+        tile[k][c] = a;
+        m = fmaxf(m, fabsf(a));
     }
-    // max |R| of the round from the per-tile maxima (every workgroup of the
-    // round reads the same values, so all agree on the scale)
+    // max |R| of the round: from this tile when it is the round, else from the
+    // per-tile maxima (every workgroup of the round reads the same values, so
+    // all agree on the scale)
     float M = 0.f;
-    for (int i = 0; i < ntiles; ++i) M = fmaxf(M, tmax[(int64_t)r * ntiles + i]);
+    if constexpr (ONE) {
+        for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+        if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+        __syncthreads();
+        M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    } else {
+        (void)m;
+        for (int i = 0; i < ntiles; ++i) M = fmaxf(M, tmax[(int64_t)r * ntiles + i]);
+    }
     __syncthreads();
     const int e = 15 - __builtin_amdgcn_frexp_expf(M);   // M * 2^e in [2^14, 2^15)
 
@@ -209,7 +234,10 @@ __global__ __launch_bounds__(256) void rprep_kernel(const float* __restrict__ R,
         if (threadIdx.x < 3) {
             const float v = fmaxf(fmaxf(wn[threadIdx.x][0], wn[threadIdx.x][1]),
                                   fmaxf(wn[threadIdx.x][2], wn[threadIdx.x][3]));
-            atomicMax((int*)&rnorm[threadIdx.x * nh + r], __float_as_int(v));
+            if constexpr (ONE)
+                rnorm[threadIdx.x * nh + r] = v;
+            else
+                atomicMax((int*)&rnorm[threadIdx.x * nh + r], __float_as_int(v));
         }
     }
     float* dst = rt + ((int64_t)r * ntiles * kHashColTile + col0) * d;
@@ -850,10 +878,15 @@ hipError_t launch_hash(const void* qk, const float* R, const Dims& d, int32_t* b
     const int ntiles = hash_ntiles(d);
     hipError_t e;
     const dim3 pgrid = grid_split((unsigned)ntiles, d.nr);   // every R round
-    rmax_kernel<<<pgrid, 256, 0, st>>>(R, d.d, half, ntiles, d.nr, w.tmax, w.counter, w.rnorm,
-                                       w.scount);
-    rprep_kernel<<<pgrid, 256, 0, st>>>(R, d.d, half, ntiles, d.nr, w.tmax, w.rnorm, w.rt,
-                                        w.rfrag);
+    if (ntiles == 1) {
+        rprep_kernel<true><<<pgrid, 256, 0, st>>>(R, d.d, half, ntiles, d.nr, w.tmax, w.rnorm,
+                                                  w.rt, w.rfrag, w.counter, w.scount);
+    } else {
+        rmax_kernel<<<pgrid, 256, 0, st>>>(R, d.d, half, ntiles, d.nr, w.tmax, w.counter,
+                                           w.rnorm, w.scount);
+        rprep_kernel<false><<<pgrid, 256, 0, st>>>(R, d.d, half, ntiles, d.nr, w.tmax, w.rnorm,
+                                                   w.rt, w.rfrag, w.counter, w.scount);
+    }
     if ((e = mark(st, ev, nev, names, "hash_prep")) != hipSuccess) return e;
     if (d.dtype == LSH_BF16) {
         // two 32-token fragments per wave (32 and 128 tokens per wave measured
