@@ -81,7 +81,8 @@ def forward_roofline(w, ms_per_step):
     """Whole-forward floor: for each step of the method the larger of its
     flops at the matching peak and its algorithmic HBM bytes at 8 TB/s
     (hash: read qk, write the ids; sort: read ids, write keys; chunk pass:
-    gather rows, write per-round rows; combine: read them, write out)."""
+    gather rows, write per-round rows; combine: read them, write out; with
+    one round on the bf16 path the chunk pass writes the output itself)."""
     e = 2 if w.dtype == "bf16" else 4
     T = w.B * w.H * w.L
     TR = T * w.n_hashes
@@ -96,6 +97,10 @@ def forward_roofline(w, ms_per_step):
         "combine": (3.0 * w.n_hashes * d * T, PEAK_FP32_TFLOPS,
                     T * (w.n_hashes * (2 * d if compact else 4 * d + 8) + d * e)),
     }
+    if compact and w.n_hashes == 1:
+        # one round: its output is the forward's, written by the chunk pass
+        # (d e bytes per token instead of the fp16 row), and nothing is combined
+        steps["combine"] = (0.0, 1.0, 0.0)
     per = {}
     for k, (flops, peak, nbytes) in steps.items():
         t_c = flops / (peak * 1e12) * 1e3

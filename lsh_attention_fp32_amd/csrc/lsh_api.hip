@@ -188,12 +188,16 @@ int run_fwd(const void* qk, const void* v, const float* R, const lsh_shape_t* sh
     float* lse = (float*)(base + f.lse);
     const HashWorkspace hw = carve_hash_workspace(base + f.hash, d);
     // the compact path (bf16 I/O) takes the matrix-core hash, which also
-    // produces max|v| for the scale of the fp16 per-round outputs
+    // produces max|v| for the scale of the fp16 per-round outputs. With one
+    // round that round's output is the forward's (weight 1): the chunk pass
+    // writes it in bf16 straight into out and no combine runs -- except in
+    // the training forward, whose combine also writes Z.
     const bool compact = compact_o_sorted(d);
-    const OSorted o{base + f.o, compact, hw.vmax};
+    const bool direct = compact && d.nh == 1 && !z;
+    const OSorted o{direct ? out : base + f.o, compact, hw.vmax, direct};
     hipError_t e;
     if ((e = checked(launch_hash(qk, R, d, buckets, hw, st, ev, nev, names,
-                                 compact ? v : nullptr))) != hipSuccess)
+                                 compact && !direct ? v : nullptr))) != hipSuccess)
         return hip_fail(e, "hash");
     // the fp16 by-position form un-sorts in the chunk pass, so the sort can
     // hand it packed keys and skip the inverse permutation
@@ -211,7 +215,8 @@ int run_fwd(const void* qk, const void* v, const float* R, const lsh_shape_t* sh
     if ((e = checked(launch_attend(qk, v, buckets, perm, d, o, lse, st, ev, nev, names, packed,
                                    rn))) != hipSuccess)
         return hip_fail(e, "chunk_attend");
-    if ((e = checked(launch_combine(o, lse, inv, d, out, st, ev, nev, names, z))) != hipSuccess)
+    if (!direct &&
+        (e = checked(launch_combine(o, lse, inv, d, out, st, ev, nev, names, z))) != hipSuccess)
         return hip_fail(e, "unsort_combine");
     if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "launch");
     return LSH_OK;

@@ -186,6 +186,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kM = 64;            // chunk length of the matrix-core kernel
 constexpr int kWin = 2 * kM;      // keys in a window
@@ -227,6 +228,7 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
                                                           Dims dm, int nruns, int run_len,
                                                           void* __restrict__ o_sorted,
                                                           const uint32_t* __restrict__ vmax,
+                                                          const int direct,
                                                           float* __restrict__ lse_sorted,
                                                           const float* __restrict__ rn,
                                                           const uint16_t* __restrict__ qsep,
@@ -255,7 +257,7 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
     const uint16_t* V = v + bh * L * D;
     const float c_log2 = 1.4426950408889634f / sqrtf((float)D);   // log2(e) / sqrt(d)
     const float pen2 = kSelfPenalty * 1.4426950408889634f;
-    const float oscale = HALF ? o_scale(*vmax) : 1.0f;
+    const float oscale = HALF && !direct ? o_scale(*vmax) : 1.0f;
 
     // sorted key of a slot: the position (plain perm) or bucket:position (packed)
     auto key_pos = [&](int32_t k) -> int { return PACKED ? (int)((uint32_t)k & kPackPosMask) : k; };
@@ -532,12 +534,19 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 pat[i] = ((lb >> (4 * g + i)) & 1u) | (((lb >> (16 + 4 * g + i)) & 1u) << 16);
+            // With one round the row is the forward's output (weight 1): it is
+            // written in bf16, unscaled, without the lse bits, into [B,H,L,d].
             u32x2 hv[DT];
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 const f32x4 o = oacc[dt] * inv;
-                const f16x4 h = {(_Float16)o.x, (_Float16)o.y, (_Float16)o.z, (_Float16)o.w};
-                hv[dt] = __builtin_bit_cast(u32x2, h);
+                if (direct) {
+                    const bf16x4 h = {(__bf16)o.x, (__bf16)o.y, (__bf16)o.z, (__bf16)o.w};
+                    hv[dt] = __builtin_bit_cast(u32x2, h);
+                } else {
+                    const f16x4 h = {(_Float16)o.x, (_Float16)o.y, (_Float16)o.z, (_Float16)o.w};
+                    hv[dt] = __builtin_bit_cast(u32x2, h);
+                }
             }
             // Lane (r16, g) holds A = features 32 k + 4 g .. + 3 (tile 2 k) and
             // B = 32 k + 16 + 4 g .. + 3 (tile 2 k + 1); lane g stores features
@@ -556,8 +565,9 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
                 const auto t1 = __builtin_amdgcn_permlane16_swap(s1[0], s1[1], false, false);
                 const uint32_t w[4] = {t0[0], t1[0], t0[1], t1[1]};
                 *(u32x4*)(orow + 32 * k + 8 * g) =
-                    (u32x4){(w[0] & 0xFFFEFFFEu) | pat[0], (w[1] & 0xFFFEFFFEu) | pat[1],
-                            (w[2] & 0xFFFEFFFEu) | pat[2], (w[3] & 0xFFFEFFFEu) | pat[3]};
+                    direct ? (u32x4){w[0], w[1], w[2], w[3]}
+                           : (u32x4){(w[0] & 0xFFFEFFFEu) | pat[0], (w[1] & 0xFFFEFFFEu) | pat[1],
+                                     (w[2] & 0xFFFEFFFEu) | pat[2], (w[3] & 0xFFFEFFFEu) | pat[3]};
             }
         } else {
             const float inv = sumr > 0.f ? 1.0f / sumr : 0.f;
@@ -610,6 +620,8 @@ hipError_t launch_attend(const void* qk, const void* v, const int32_t* buckets,
                          hipStream_t st, hipEvent_t* ev, int* nev, const char** names,
                          bool packed, const float* rn, const SepQK* sep) {
     if (packed && !(o.half && d.dtype == LSH_BF16 && d.m == kM)) return hipErrorInvalidValue;
+    if (o.direct && !(o.half && d.nh == 1 && d.dtype == LSH_BF16 && d.m == kM && !sep))
+        return hipErrorInvalidValue;
     if (sep && d.key_norm) return hipErrorInvalidValue;
     if (d.dtype == LSH_BF16 && d.m == kM) {
         const int nchunks = d.L / kM;
@@ -622,7 +634,7 @@ hipError_t launch_attend(const void* qk, const void* v, const int32_t* buckets,
         const int32_t* bq = sep ? sep->buckets_q : nullptr;
         const int32_t* pq = sep ? sep->perm_q : nullptr;
 #define LSH_ATTEND_ARGS(VM, RN) \
-    x, vv, buckets, perm, d, nruns, run_len, o.ptr, VM, lse_sorted, RN, qs, bq, pq
+    x, vv, buckets, perm, d, nruns, run_len, o.ptr, VM, (int)o.direct, lse_sorted, RN, qs, bq, pq
 #define LSH_ATTEND_LAUNCH(DD, HH, PP, VM)                                                      \
     (sep ? attend_mfma_kernel<DD, HH, PP, 0, true><<<grid, 256, 0, st>>>(                      \
                LSH_ATTEND_ARGS(VM, nullptr))                                                   \

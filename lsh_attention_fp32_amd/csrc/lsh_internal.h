@@ -159,6 +159,7 @@ struct OSorted {
     void* ptr;                  // float* or _Float16*
     bool half;                  // fp16 by position
     const uint32_t* vmax;       // bf16 bit pattern of max|v| (used when half)
+    bool direct = false;        // half with one round: ptr is the bf16 output [B,H,L,d]
 };
 
 // True when the fused forward can keep o_sorted in scaled fp16.

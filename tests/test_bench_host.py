@@ -47,6 +47,19 @@ def test_headline_forward_floor():
     assert fr["frac"] == pytest.approx(fr["t_roof_ms"])   # at 1 ms per step
 
 
+def test_one_round_floor_has_no_combine():
+    """With one round on the bf16 path the chunk pass writes the output
+    itself: the floor counts no combine step, and the chunk step's write is
+    the same 2 d bytes per token-round as the fp16 row it replaces."""
+    w = workloads.WORKLOADS["sweep_b64_l1k_nh1"]
+    fr = bench.forward_roofline(w, 1.0)
+    assert fr["steps"]["combine"]["roof_ms"] == 0.0
+    w8 = workloads.WORKLOADS["sweep_b64_l1k_nh8"]
+    assert bench.forward_roofline(w8, 1.0)["steps"]["combine"]["roof_ms"] > 0.0
+    assert fr["steps"]["chunk"]["roof_ms"] == pytest.approx(
+        bench.forward_roofline(w8, 1.0)["steps"]["chunk"]["roof_ms"] / 8)
+
+
 def test_noncausal_sweep_workloads_differ_only_in_the_mask():
     for name, w in workloads.WORKLOADS.items():
         if not name.startswith("sweep_"):
