@@ -202,7 +202,11 @@ int lsh_unsort_combine(const float *o_sorted, const float *lse_sorted, const int
 
 /* Whole forward: steps 1-5 on `stream`, intermediates in `ws`
  * (at least lsh_workspace_size("fwd") bytes; the first int32 of ws is the
- * hash stage's re-decided count, as in lsh_hash). */
+ * hash stage's re-decided count, as in lsh_hash). The launches depend on the
+ * shape: with bf16 I/O, chunk 64 and one hash round the chunk pass writes
+ * out itself (the combine's weight is 1) and no combine kernel runs; a
+ * segment of at most 4096 positions is sorted by one kernel instead of
+ * three; n_buckets <= 64 prepares R in one kernel instead of two. */
 int lsh_attention_fwd(const void *qk, const void *v, const float *R, const lsh_shape_t *shape,
                       void *out, void *ws, size_t ws_bytes, void *stream);
 
