@@ -161,8 +161,14 @@ __global__ __launch_bounds__(256) void attend_valu_kernel(const T* __restrict__ 
 //
 // A workgroup (4 waves) walks a run of consecutive chunks of one (batch, head,
 // round) segment. LDS holds a ring of two chunks: the qk rows (row-major,
-// padded) and the v rows transposed (vt[feature][key]), keys indexed in ring
-// order (slot * 64 + row) -- the window of chunk c is simply both ring slots.
+// padded) and the v rows, keys indexed in ring order (slot * 64 + row) --
+// the window of chunk c is simply both ring slots. The v rows feed the
+// A operand of O^T = V^T P^T, which wants 8 consecutive keys of one feature
+// per lane. At d = 128 the rows are stored as gathered (row-major) and two
+// transposing LDS reads (ds_read_b64_tr_b16) take each operand from them; at
+// d = 64 they are stored transposed (vt[feature][key]) and one 16-byte read
+// does (measured: the transposing reads save the chunk pass 6 % at d = 128
+// and cost it 3-4 % at d = 64).
 // Each chunk's rows are gathered from HBM once, into registers, while the
 // previous chunk(s) are being computed (kDepth chunks in flight; one measures
 // as fast as two or three at 64K tokens), and serve as the look-back of the
@@ -187,6 +193,8 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 constexpr int kM = 64;            // chunk length of the matrix-core kernel
 constexpr int kWin = 2 * kM;      // keys in a window
@@ -204,9 +212,17 @@ static_assert(kDepth >= 1 && kDepth <= 3, "key buffers hold four chunks");
 template <int D>
 struct alignas(16) AttendLds {
     static constexpr int KS = D + 8;       // padded row of qk (bf16 elements)
-    static constexpr int VS = kWin + 8;    // padded row of vt (bf16 elements)
+    static constexpr bool TRV = D == 128;  // v rows row-major, read transposed
+    // TRV: v rows D + 16 elements apart, and 64 more after every 8 rows. A
+    // transposing read takes 4 rows x 4 eight-byte pieces per 16 lanes: the
+    // row step (8 banks) spreads them over 32 banks, and the extra 128 bytes
+    // per 8 rows put the next 16 lanes (8 rows on) on the other 32.
+    static constexpr int VRS = D + 16;
+    static constexpr int vr_off(int r) { return r * VRS + (r >> 3) * 64; }
+    // else: vt[feature][key], rows of VS elements
+    static constexpr int VS = kWin + 8;
     uint16_t k[2][kM][KS];
-    uint16_t vt[D][VS];
+    uint16_t vb[TRV ? kWin * VRS + (kWin / 8) * 64 : D * VS];
     int32_t pos[kWin];
     int32_t bkt[kWin];
     float rn[kWin];         // key scale (key normalisation): 1 / |x_j|
@@ -237,7 +253,6 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
     constexpr int PIECES = D / 8;              // 16-byte pieces per row
     constexpr int QPT = kM * PIECES / 256;     // qk pieces per thread
     constexpr int QROWS = 256 / PIECES;        // rows covered per pass
-    constexpr int VPT = D / 64;                // (key pair, 8 features) items per thread
     constexpr int KSTEPS = D / 32;
     constexpr int DT = D / 16;                 // output feature tiles
     __shared__ AttendLds<D> sm;
@@ -262,12 +277,36 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
     // sorted key of a slot: the position (plain perm) or bucket:position (packed)
     auto key_pos = [&](int32_t k) -> int { return PACKED ? (int)((uint32_t)k & kPackPosMask) : k; };
 
+    // A operand of O^T = V^T P^T for key block kb (32 keys) and feature tile
+    // dt: lane (g, r16) needs feature 16 dt + r16 of ring keys 32 kb + 8 g ..
+    // + 7. In each 16-lane group, lane r16 addresses ring key 32 kb + 8 g +
+    // 4 h + r16 / 4 at features 16 dt + 4 (r16 % 4) .. + 3; the transposing
+    // read hands lane r16 feature 16 dt + r16 of those four keys, and h = 0, 1
+    // give the 8 keys. Row 32 kb + 8 g + 4 h + r16 / 4 lies in 8-row block
+    // 4 kb + g, so every address is this lane's base plus a constant.
+    // (Without TRV: one 16-byte read of vt[16 dt + r16][32 kb + 8 g].)
+    const uint16_t* vr_l = AttendLds<D>::TRV
+        ? sm.vb + (8 * g + (r16 >> 2)) * AttendLds<D>::VRS + 64 * g + 4 * (r16 & 3)
+        : sm.vb + r16 * AttendLds<D>::VS + 8 * g;
+    auto v_frag = [&](int kb, int dt) -> u32x4 {
+        if constexpr (AttendLds<D>::TRV) {
+            const uint16_t* p = vr_l + 32 * kb * AttendLds<D>::VRS + 256 * kb + 16 * dt;
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+            const v4i16 hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 4 * AttendLds<D>::VRS));
+            const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+            return (u32x4){a.x, a.y, b.x, b.y};
+        } else {
+            return *(const u32x4*)(vr_l + 16 * dt * AttendLds<D>::VS + 32 * kb);
+        }
+    };
+
     // One chunk's rows in flight: gathered from HBM into registers (positions
     // from an LDS key buffer), parked in the LDS ring when the chunk's turn
     // comes. Two sets keep two chunks in flight behind the one computing.
     struct Rows {
         u32x4 q[QPT];
-        u32x4 v[VPT][2];
+        u32x4 v[QPT];
         int32_t pos, bkt;   // position and bucket of row tid (threads < 64)
         float rn;           // and its 1 / |x| (KN == 1)
     };
@@ -277,11 +316,20 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
             const int row = tid / PIECES + QROWS * j;
             rw.q[j] = *(const u32x4*)(X + (int64_t)key_pos(kl[row]) * D + (tid % PIECES) * 8);
         }
+        if constexpr (AttendLds<D>::TRV) {
 #pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            const int pr = tid & 31, ddg = (tid >> 5) + 8 * j;
-            rw.v[j][0] = *(const u32x4*)(V + (int64_t)key_pos(kl[2 * pr]) * D + ddg * 8);
-            rw.v[j][1] = *(const u32x4*)(V + (int64_t)key_pos(kl[2 * pr + 1]) * D + ddg * 8);
+            for (int j = 0; j < QPT; ++j) {
+                const int row = tid / PIECES + QROWS * j;
+                rw.v[j] = *(const u32x4*)(V + (int64_t)key_pos(kl[row]) * D + (tid % PIECES) * 8);
+            }
+        } else {
+            // keys 2 pr and 2 pr + 1, features 8 ddg .. + 7
+#pragma unroll
+            for (int j = 0; j < QPT / 2; ++j) {
+                const int pr = tid & 31, ddg = (tid >> 5) + 8 * j;
+                rw.v[2 * j] = *(const u32x4*)(V + (int64_t)key_pos(kl[2 * pr]) * D + ddg * 8);
+                rw.v[2 * j + 1] = *(const u32x4*)(V + (int64_t)key_pos(kl[2 * pr + 1]) * D + ddg * 8);
+            }
         }
         if (tid < kM) {
             const int32_t k = kl[tid];
@@ -310,14 +358,23 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
                 if (tid % PIECES == 0) sm.rn[slot * kM + row] = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
             }
         }
+        if constexpr (AttendLds<D>::TRV) {
 #pragma unroll
-        for (int j = 0; j < VPT; ++j) {
-            const int pr = tid & 31, ddg = (tid >> 5) + 8 * j;
+            for (int j = 0; j < QPT; ++j) {
+                const int row = tid / PIECES + QROWS * j;
+                *(u32x4*)&sm.vb[AttendLds<D>::vr_off(slot * kM + row) + (tid % PIECES) * 8] = rw.v[j];
+            }
+        } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t lo = (rw.v[j][0][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-                const uint32_t hi = (rw.v[j][1][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-                *(uint32_t*)&sm.vt[ddg * 8 + e][slot * kM + 2 * pr] = lo | (hi << 16);
+            for (int j = 0; j < QPT / 2; ++j) {
+                const int pr = tid & 31, ddg = (tid >> 5) + 8 * j;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t lo = (rw.v[2 * j][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                    const uint32_t hi = (rw.v[2 * j + 1][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                    *(uint32_t*)&sm.vb[(ddg * 8 + e) * AttendLds<D>::VS + slot * kM + 2 * pr] =
+                        lo | (hi << 16);
+                }
             }
         }
         if (tid < kM) {
@@ -368,7 +425,14 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
             store_rows(rw[0], slot);
         } else {
             for (int k = tid; k < kM * AttendLds<D>::KS; k += 256) (&sm.k[slot][0][0])[k] = 0;
-            for (int k = tid; k < D * kM; k += 256) sm.vt[k / kM][slot * kM + k % kM] = 0;
+            if constexpr (AttendLds<D>::TRV) {
+                for (int k = tid; k < kM * PIECES; k += 256)
+                    *(u32x4*)&sm.vb[AttendLds<D>::vr_off(slot * kM + k / PIECES) + (k % PIECES) * 8] =
+                        (u32x4){0u, 0u, 0u, 0u};
+            } else {
+                for (int k = tid; k < D * kM; k += 256)
+                    sm.vb[(k / kM) * AttendLds<D>::VS + slot * kM + k % kM] = 0;
+            }
             if (tid < kM) {
                 sm.pos[slot * kM + tid] = 0;
                 sm.bkt[slot * kM + tid] = -1;   // never equal to a bucket id
@@ -503,7 +567,7 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(const uint16_t* __rest
                                                            osum, 0, 0, 0);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                const u32x4 af = *(const u32x4*)&sm.vt[dt * 16 + r16][32 * kb + 8 * g];
+                const u32x4 af = v_frag(kb, dt);
                 oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af),
                                                                    bfr, oacc[dt], 0, 0, 0);
             }
