@@ -451,11 +451,20 @@ constexpr int kBM = 64;   // chunk length of the matrix-core passes
 template <int D>
 struct BwdRows {
     static constexpr int RS = D + 8;     // padded row (bf16): rows 4 banks apart
-    static constexpr int TS = kBM + 8;   // padded transposed row (bf16)
+    // qk and output-gradient rows (bf16): rows 8 banks apart, and rows whose
+    // index has bit 3 set 4 banks further on. 16 consecutive rows read 16
+    // bytes each at one column (a score tile's A operand) then cover the 64
+    // banks once, and so do 8 consecutive rows read 8 bytes each at four
+    // neighbouring 4-column chunks (a transposing read of 32 lanes).
+    static constexpr int XS = D + 16;
+    static constexpr int xrow(int r) { return r * XS + 8 * ((r >> 3) & 1); }
 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 // LDS row of item j (of a 64-item chunk) in the row-major buffers of the
 // fused kernel. A score tile (block kb, half h) reads item
@@ -467,25 +476,23 @@ __device__ __forceinline__ int phys_row(int j) {
     return (j & ~31) | (((j >> 3) & 3) << 2) | (((j >> 2) & 1) << 4) | (j & 3);
 }
 
-// Transposes the 64 rows of `rm` (stored at phys_row(item)) into `tr`
-// ([D][TS], item order) inside LDS. A thread takes items 2m and 2m + 1 at
-// one 8-feature piece and writes 8 words, each holding both items' values of
-// one feature: the 32 lanes of a piece fill 128 contiguous bytes of a
-// transposed row, and a wave's two pieces land 32 banks apart.
-template <int D, int NT>
-__device__ __forceinline__ void transpose_items(const uint16_t (*rm)[BwdRows<D>::RS],
-                                                uint16_t (*tr)[BwdRows<D>::TS]) {
-    const int m = threadIdx.x & 31;
-    for (int pc = threadIdx.x >> 5; pc < D / 8; pc += NT / 32) {
-        const u32x4 a = *(const u32x4*)&rm[phys_row(2 * m)][pc * 8];
-        const u32x4 b = *(const u32x4*)&rm[phys_row(2 * m + 1)][pc * 8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t lo = (a[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-            const uint32_t hi = (b[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-            *(uint32_t*)&tr[pc * 8 + e][2 * m] = lo | (hi << 16);
-        }
-    }
+// A transposed operand straight from row-major rows: the A operand of a
+// 16 x 16 x 32 product whose rows m are 16 features and whose k runs over
+// the items 32 kb + 8 gq + e (e < 8) of a row buffer laid out by phys_row
+// and xrow. Items 8 gq + 0 .. 3 of a block sit on four consecutive rows
+// (4 gq .. 4 gq + 3), items 8 gq + 4 .. 7 on the four rows 16 further on.
+// ds_read_b64_tr_b16 hands lane j of a 16-lane group element j % 4 of the
+// 8-byte pieces that lanes j / 4 + 4 i (i < 4) address: with lane r16 of
+// group gq addressing row 4 gq + r16 / 4 at columns 4 (r16 % 4) .. + 3, lane
+// r16 receives column r16 of those four rows, k-elements 0 .. 3, and the
+// read 16 rows on gives elements 4 .. 7. `p` is that lane's address in the
+// block (tile column 0).
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const uint16_t* p) {
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 16 * BwdRows<D>::XS));
+    const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+    return __builtin_bit_cast(bf16x8, (u32x4){a.x, a.y, b.x, b.y});
 }
 
 // ---------------------------------------------------------------------------
@@ -499,21 +506,23 @@ __device__ __forceinline__ void transpose_items(const uint16_t (*rm)[BwdRows<D>:
 //   A: scores its 16 keys against chunk c's 64 queries (S and dP tiles with
 //      the queries' rows from LDS), forms the pair weights P and dS in the
 //      lanes of its keys, adds dk += dS^T x_q and dv += P^T g_q (the queries'
-//      transposed rows from LDS), and writes its dS (times the key's 1/|x|
-//      under key normalisation) into a [query][key] LDS buffer;
+//      rows from LDS, read transposed), and writes its dS (times the key's
+//      1/|x| under key normalisation) into a [query][key] LDS buffer;
 //   B: the set owning chunk c - 1 writes that chunk's rows out ((dq + dk)
 //      scaled, and dv; its dq has waited in LDS since step c - 1), while the
 //      set owning chunk c computes chunk c's dq = dS x_k over the 128 keys
-//      (the keys' transposed rows and the dS buffer from LDS) into the other
-//      dq slot;
+//      (the keys' rows, read transposed, and the dS buffer from LDS) into
+//      the other dq slot;
 //   C: chunk c + 1's rows, gathered into registers since the top of the
 //      step, are parked in LDS;
-//   D: chunk c + 1's rows are transposed, and the set that just wrote chunk
-//      c - 1 out takes chunk c + 1's keys.
-// Four barriers a step; at 64K tokens x 8 heads x 8 rounds (d 128) a step
-// takes ~10.7 K cycles: about 38 % in A, 18 % waiting at the barrier after
-// A (the two sets' key blocks skip different amounts of causal work), 24 %
-// in B and its barrier, and 21 % in C and D with theirs.
+//   D: the set that just wrote chunk c - 1 out takes chunk c + 1's keys and
+//      goes straight on to step c + 1 (it reads nothing the next step's A
+//      writes, and the next writes to what it reads follow that step's
+//      first barrier).
+// Three barriers a step. The qk rows of chunks c - 1 and c stay in a
+// two-slot ring, so the operands that run over queries or keys (x^T, g^T)
+// come from the row-major rows by transposing reads, with no transposed
+// copy and no pass to make one.
 // Every score is computed once. The first step of a run scores the look-back
 // pair for dq only (the run before finishes that chunk's dk, dv); a run that
 // does not end its segment closes with a partial step on the next chunk
@@ -544,12 +553,12 @@ constexpr int kDsGap = 16;    // bf16 elements after every 16 rows
 
 template <int D>
 struct alignas(16) BwdRunLds {
-    static constexpr int RS = BwdRows<D>::RS, TS = BwdRows<D>::TS;
-    uint16_t xr[kBM][RS];      // qk rows of chunk c (phys_row order)
+    static constexpr int RS = BwdRows<D>::RS;
+    static constexpr int XS = BwdRows<D>::XS;
+    // qk rows of chunk t in slot t & 1 (item j at row phys_row(j), row r at xrow(r))
+    uint16_t xr[2][kBM * XS];
+    uint16_t gr[kBM * XS];     // output-gradient rows of chunk c (same layout)
     uint16_t vr[kBM][RS];      // v rows of chunk c (phys_row order)
-    uint16_t gr[kBM][RS];      // output-gradient rows of chunk c (phys_row order)
-    uint16_t xt[2][D][TS];     // qk transposed (item order), chunk t in slot t & 1
-    uint16_t gt[D][TS];        // output gradients of chunk c transposed
     uint16_t ds[kBM * kDsRow + (kBM / 16) * kDsGap];   // dS of step c by [query][key]
     uint16_t xq[2][kBM][RS];   // dq of chunk t in slot t & 1 (bf16, item order)
     int32_t pos[3][kBM], bkt[3][kBM];   // chunk t in slot t % 3
@@ -598,13 +607,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_run_kernel(const uint16_t* __
     const int me = 16 * wg + r16;   // this lane's key within its chunk
     const int prow = phys_row(me);
     // Per-lane LDS addresses; every tile below is a constant offset from one
-    // of them (row r16, column 8 gq of the row-major and transposed buffers).
-    constexpr int RS = BwdRows<D>::RS, TS = BwdRows<D>::TS;
-    const uint16_t* const xr_l = &sm.xr[r16][8 * gq];
-    const uint16_t* const gr_l = &sm.gr[r16][8 * gq];
-    const uint16_t* const xt_l = &sm.xt[0][r16][8 * gq];
-    const uint16_t* const gt_l = &sm.gt[r16][8 * gq];
-    const uint16_t* const xtq_l = xt_l + 16 * DPW * wg * TS;   // this wave's first dq feature tile
+    // of them: row r16 at column 8 gq for the row reads, row 4 gq + r16 / 4
+    // at column 4 (r16 % 4) for the transposing reads (tr_operand).
+    constexpr int XS = BwdRows<D>::XS, SLOT = kBM * XS;
+    const uint16_t* const xr_l = sm.xr[0] + BwdRows<D>::xrow(r16) + 8 * gq;
+    const uint16_t* const gr_l = sm.gr + BwdRows<D>::xrow(r16) + 8 * gq;
+    const int trow = 4 * gq + (r16 >> 2);
+    const uint16_t* const xtr_l = sm.xr[0] + BwdRows<D>::xrow(trow) + 4 * (r16 & 3);
+    const uint16_t* const gtr_l = sm.gr + BwdRows<D>::xrow(trow) + 4 * (r16 & 3);
+    const uint16_t* const xtq_l = xtr_l + 16 * DPW * wg;   // this wave's first dq feature tile
     // dS writes: query 32 qb + 8 gq + e, key me (+ 64 for chunk c's keys)
     uint16_t* const dsw_l = &sm.ds[8 * gq * kDsRow + (gq >> 1) * kDsGap + me];
     // dS reads: query 16 qt + r16, keys 32 kb + 8 gq .. + 7
@@ -632,13 +643,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_run_kernel(const uint16_t* __
             pf.rn = KN ? rn[p] : 1.f;
         }
     };
-    auto park = [&](const Pre& pf) {
+    auto park = [&](int t, const Pre& pf) {
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
             const int i = tid + kBwdThreads * k, row = phys_row(i / (D / 8)), pc = i % (D / 8);
-            *(u32x4*)&sm.xr[row][pc * 8] = pf.x[k];
+            *(u32x4*)(sm.xr[t & 1] + BwdRows<D>::xrow(row) + pc * 8) = pf.x[k];
             *(u32x4*)&sm.vr[row][pc * 8] = pf.v[k];
-            *(u32x4*)&sm.gr[row][pc * 8] = pf.g[k];
+            *(u32x4*)(sm.gr + BwdRows<D>::xrow(row) + pc * 8) = pf.g[k];
         }
         if (tid < kBM) {
             sm.zz[tid] = pf.z;
@@ -660,9 +671,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_run_kernel(const uint16_t* __
     float mrn = 1.f, msdd = 0.f;
     // take the keys of chunk t (its rows parked in xr, vr; its keys in slot t % 3)
     auto take_keys = [&](int t) {
+        const uint16_t* const xk = sm.xr[t & 1] + BwdRows<D>::xrow(prow) + 8 * gq;
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
-            kf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(&sm.xr[prow][8 * gq] + 32 * s));
+            kf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(xk + 32 * s));
             vf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(&sm.vr[prow][8 * gq] + 32 * s));
         }
         mpos = sm.pos[t % 3][me];
@@ -682,7 +694,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_run_kernel(const uint16_t* __
         const int s3 = c % 3, par = c & 1;
         const int klo = __builtin_amdgcn_readlane(mbkt, 0);
         const int khi = __builtin_amdgcn_readlane(mbkt, 15);
-        const uint16_t* const xtc = xt_l + par * D * TS;   // chunk c's transposed qk
+        const uint16_t* const xrc = xr_l + par * SLOT;    // chunk c's qk rows
+        const uint16_t* const xtc = xtr_l + par * SLOT;   // the same, transposing reads
         uint16_t* const dsw = dsw_l + (own ? kBM : 0);      // chunk c's keys: columns 64..127
         // both query blocks' bucket bounds first, then one wave-uniform mask
         // (non-short-circuit & and |: the loads are all issued before any test)
@@ -710,8 +723,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_run_kernel(const uint16_t* __
 #pragma unroll
                     for (int s = 0; s < KSTEPS; ++s) {
                         // A row r16 of the tile: LDS row 32 qb + 16 h + r16
-                        const int off = (32 * qb + 16 * h) * RS + 32 * s;
-                        const bf16x8 qa = __builtin_bit_cast(bf16x8, *(const u32x4*)(xr_l + off));
+                        const int off = (32 * qb + 16 * h) * XS + 32 * s;
+                        const bf16x8 qa = __builtin_bit_cast(bf16x8, *(const u32x4*)(xrc + off));
                         const bf16x8 ga = __builtin_bit_cast(bf16x8, *(const u32x4*)(gr_l + off));
                         sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[s], sacc, 0, 0, 0);
                         pacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga, vf[s], pacc, 0, 0, 0);
@@ -745,9 +758,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_run_kernel(const uint16_t* __
                     const bf16x8 bd = __builtin_bit_cast(bf16x8, dsfrag);
 #pragma unroll
                     for (int dt = 0; dt < DT; ++dt) {
-                        const int off = 16 * dt * TS + 32 * qb;
-                        const bf16x8 aq = __builtin_bit_cast(bf16x8, *(const u32x4*)(xtc + off));
-                        const bf16x8 ag = __builtin_bit_cast(bf16x8, *(const u32x4*)(gt_l + off));
+                        const int off = 32 * qb * XS + 16 * dt;
+                        const bf16x8 aq = tr_operand<D>(xtc + off);
+                        const bf16x8 ag = tr_operand<D>(gtr_l + off);
                         dk[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, bd, dk[dt], 0, 0, 0);
                         dvv[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ag, bp, dvv[dt], 0, 0, 0);
                     }
@@ -766,7 +779,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_run_kernel(const uint16_t* __
     // Phase B, the set that owns chunk c's keys: dq^T tiles (16 features x
     // 16 queries) of chunk c over the keys of chunks c - 1 (blocks 0, 1) and c
     // (blocks 2, 3); wave wg takes feature tiles DPW wg .. + DPW - 1 of all
-    // four query tiles. A: the keys' transposed rows; B: lane (r16, gq) reads
+    // four query tiles. A: the keys' rows read transposed; B: lane (r16, gq) reads
     // keys 32 kb + 8 gq .. + 7 of query 16 qt + r16 from the dS buffer, each
     // read serving DPW products. Lane (r16, gq) of tile (u, qt) ends with
     // features 16 (DPW wg + u) + 4 gq + i of query 16 qt + r16, stored to xq.
@@ -785,8 +798,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_run_kernel(const uint16_t* __
             bf16x8 ak[DPW];
 #pragma unroll
             for (int u = 0; u < DPW; ++u)
-                ak[u] = __builtin_bit_cast(bf16x8, *(const u32x4*)(xtq_l + (tk & 1) * D * TS +
-                                                                   16 * u * TS + 32 * (kb & 1)));
+                ak[u] = tr_operand<D>(xtq_l + (tk & 1) * SLOT + 32 * (kb & 1) * XS + 16 * u);
 #pragma unroll
             for (int qt = 0; qt < 4; ++qt) {
                 const bf16x8 bd = __builtin_bit_cast(
@@ -859,19 +871,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_run_kernel(const uint16_t* __
     Pre pf;
     if (c0 > 0) {
         gather(c0 - 1, pf);
-        park(pf);
+        park(c0 - 1, pf);
         __syncthreads();
-        transpose_items<D, kBwdThreads>(sm.xr, sm.xt[(c0 - 1) & 1]);
         if (wset == ((c0 - 1) & 1)) take_keys(c0 - 1);
-        __syncthreads();
+        __syncthreads();   // v rows and 1 / |x| read before chunk c0's are parked
     }
     gather(c0, pf);
-    park(pf);
+    park(c0, pf);
     __syncthreads();
-    transpose_items<D, kBwdThreads>(sm.xr, sm.xt[c0 & 1]);
-    transpose_items<D, kBwdThreads>(sm.gr, sm.gt);
     if (wset == (c0 & 1)) take_keys(c0);
-    __syncthreads();
 
     for (int c = c0; c <= clast; ++c) {
         const bool mine = c < c1;          // chunk c's queries belong to this run
@@ -894,10 +902,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_run_kernel(const uint16_t* __
         } else if (mine) {
             dq_pass(c);
         }
-        __syncthreads();   // the row buffers, chunk c - 1's keys slot and xt slot are free
+        __syncthreads();   // the row buffers, chunk c - 1's keys slot and qk slot are free
         // C
         if (nxt) {
-            park(pf);
+            park(c + 1, pf);
             if (tid < kBM && c + 2 <= clast) {
                 sm.pos[(c + 2) % 3][tid] = kp2;
                 sm.bkt[(c + 2) % 3][tid] = kb2;
@@ -905,12 +913,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_run_kernel(const uint16_t* __
         }
         __syncthreads();
         // D
-        if (nxt) {
-            transpose_items<D, kBwdThreads>(sm.xr, sm.xt[(c + 1) & 1]);
-            transpose_items<D, kBwdThreads>(sm.gr, sm.gt);
-            if (!own) take_keys(c + 1);
-        }
-        __syncthreads();
+        if (nxt && !own) take_keys(c + 1);
     }
     // a run that ends its segment finishes its last chunk here: there is no
     // look-back pair for it
