@@ -59,8 +59,7 @@ static size_t rt_elems(const Dims& d) {
 
 size_t hash_workspace_bytes(const Dims& d) {
     size_t b = 256;                                              // counter
-    b += align_up(sizeof(float) * 3 * d.nr, 256);                // rnorm, rnorm_s, resn_s
-    b += align_up(sizeof(float) * d.nr * hash_ntiles(d), 256);   // tmax
+    b += align_up(sizeof(float) * 3 * d.nr * hash_ntiles(d), 256);   // tnorm
     b += align_up(sizeof(uint16_t) * rfrag_elems(d), 256);       // rfrag
     b += align_up(sizeof(float) * rt_elems(d), 256);             // rt
     b += align_up(sizeof(RefineItem) * (size_t)queue_tokens(d) * d.nh, 256);   // queue
@@ -77,12 +76,8 @@ HashWorkspace carve_hash_workspace(void* ws, const Dims& d) {
     w.counter = (int32_t*)p;
     w.vmax = (uint32_t*)(p + 3 * sizeof(int32_t));
     p += 256;
-    w.rnorm = (float*)p;
-    w.rnorm_s = w.rnorm + d.nr;
-    w.resn_s = w.rnorm + 2 * d.nr;
-    p += align_up(sizeof(float) * 3 * d.nr, 256);
-    w.tmax = (float*)p;
-    p += align_up(sizeof(float) * d.nr * hash_ntiles(d), 256);
+    w.tnorm = (float*)p;
+    p += align_up(sizeof(float) * 3 * d.nr * hash_ntiles(d), 256);
     w.rfrag = (uint16_t*)p;
     p += align_up(sizeof(uint16_t) * rfrag_elems(d), 256);
     w.rt = (float*)p;
@@ -100,71 +95,37 @@ HashWorkspace carve_hash_workspace(void* ws, const Dims& d) {
 }
 
 // ------------------------------------------------------------------ R prep
-// One workgroup per (32-column tile, round): max |R| over the tile, written to
-// tmax[round * ntiles + tile] (no atomics, so nothing to clear first).
-// Workgroup (0, 0) also clears the re-decision count, max|v| and the per-round
-// norms and list counts that later passes fold into.
-__global__ __launch_bounds__(256) void rmax_kernel(const float* __restrict__ R, int d, int half,
-                                                   int ntiles, int nh, float* __restrict__ tmax,
-                                                   int32_t* __restrict__ counter,
-                                                   float* __restrict__ rnorm,
-                                                   int32_t* __restrict__ scount) {
-    __shared__ float wmax[4];
-    const int t = blockIdx.x;
-    const int r = (int)block_y();   // R round, of nh
-    if (r >= nh) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (t == 0 && r == 0) {
-        if (threadIdx.x < 4) counter[threadIdx.x] = 0;
-        for (int i = threadIdx.x; i < 3 * nh; i += 256) rnorm[i] = 0.f;
-        for (int i = threadIdx.x; i < nh; i += 256) scount[i] = 0;
-    }
-    const float* Rr = R + (int64_t)r * d * half;
-    const int col0 = t * kHashColTile;
-    float m = 0.f;
-#pragma unroll 8
-    for (int idx = threadIdx.x; idx < d * kHashColTile; idx += 256) {
-        const int k = idx / kHashColTile, c = idx % kHashColTile;
-        if (col0 + c < half) m = fmaxf(m, fabsf(Rr[(int64_t)k * half + col0 + c]));
-    }
-    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    if (lane == 0) wmax[wave] = m;
-    __syncthreads();
-    if (threadIdx.x == 0)
-        tmax[(int64_t)r * ntiles + t] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-}
-
 // One workgroup per (round, 32-column tile) of R, staged through LDS:
-//  * e_r from max|R| of the round (the per-tile maxima of rmax_kernel);
-//  * rnorm / rnorm_s / resn_s: column norms (sums of squares in fp32, then
-//    rounded up), folded by an atomic max on the bits of non-negative floats,
-//    which is order independent;
+//  * e_r from max|R| of the round: a round of one tile (n_buckets <= 64,
+//    ONE) takes it from the tile it stages; otherwise every workgroup of the
+//    round reads the whole round (L2 hits after the first), so all agree on
+//    the scale without a launch of its own;
+//  * tnorm[bound][round][tile]: the tile's largest column 2-norm of R, of
+//    R_s and of the residual (sums of squares in fp32, then rounded up),
+//    stored without atomics; readers take the maximum over the round's tiles;
 //  * rt    = R transposed to [round][column][k] in fp32 (padded columns are 0),
 //            read by the fp64 re-decision;
 //  * rfrag = fp16(R * 2^e_r) in the A-operand order of
 //            v_mfma_f32_32x32x16_f16: for (round, tile, k-step), 64 lanes of 8
 //            values, lane l holding column tile*32 + l%32 and
 //            k = kstep*16 + 8*(l/32) + e.
-//
-// ONE: a round is a single tile (n_buckets <= 64). Then the workgroup takes
-// max|R| from its own tile, stores the three bounds without atomics, and
-// workgroup (0, 0) clears what rmax_kernel clears otherwise, so rmax_kernel
-// is not launched.
+// Workgroup (0, 0) also clears the re-decision count, max|v| and the
+// per-round list counts, which later passes fill in.
 template <bool ONE>
 __global__ __launch_bounds__(256) void rprep_kernel(const float* __restrict__ R, int d, int half,
                                                     int ntiles, int nh,
-                                                    const float* __restrict__ tmax,
-                                                    float* __restrict__ rnorm,
+                                                    float* __restrict__ tnorm,
                                                     float* __restrict__ rt,
                                                     uint16_t* __restrict__ rfrag,
                                                     int32_t* __restrict__ counter,
                                                     int32_t* __restrict__ scount) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
     __shared__ float tile[128][kHashColTile + 1];
     __shared__ float wmax[4];
     const int t = blockIdx.x;
     const int r = (int)block_y();   // R round, of nh
     if (r >= nh) return;
-    if (ONE && t == 0 && r == 0) {
+    if (t == 0 && r == 0) {
         if (threadIdx.x < 4) counter[threadIdx.x] = 0;
         for (int i = threadIdx.x; i < nh; i += 256) scount[i] = 0;
     }
@@ -179,19 +140,22 @@ __global__ __launch_bounds__(256) void rprep_kernel(const float* __restrict__ R,
         m = fmaxf(m, fabsf(a));
     }
     // max |R| of the round: from this tile when it is the round, else from the
-    // per-tile maxima (every workgroup of the round reads the same values, so
-    // all agree on the scale)
-    float M = 0.f;
-    if constexpr (ONE) {
-        for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-        if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
-        __syncthreads();
-        M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-    } else {
-        (void)m;
-        for (int i = 0; i < ntiles; ++i) M = fmaxf(M, tmax[(int64_t)r * ntiles + i]);
+    // whole round (a contiguous d * half floats, 16-byte aligned as R and d
+    // are), read the same way by every workgroup of the round
+    if constexpr (!ONE) {
+        m = 0.f;
+        const f32x4* R4 = (const f32x4*)Rr;
+        const int n4 = d * half / 4;
+#pragma unroll 8
+        for (int i = threadIdx.x; i < n4; i += 256) {
+            const f32x4 q = R4[i];
+            m = fmaxf(m, fmaxf(fmaxf(fabsf(q[0]), fabsf(q[1])), fmaxf(fabsf(q[2]), fabsf(q[3]))));
+        }
     }
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
     __syncthreads();
+    const float M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
     const int e = 15 - __builtin_amdgcn_frexp_expf(M);   // M * 2^e in [2^14, 2^15)
 
     {   // 8 threads per column, d/8 rows each
@@ -231,14 +195,10 @@ __global__ __launch_bounds__(256) void rprep_kernel(const float* __restrict__ R,
             wn[2][wave] = n2;
         }
         __syncthreads();
-        if (threadIdx.x < 3) {
-            const float v = fmaxf(fmaxf(wn[threadIdx.x][0], wn[threadIdx.x][1]),
-                                  fmaxf(wn[threadIdx.x][2], wn[threadIdx.x][3]));
-            if constexpr (ONE)
-                rnorm[threadIdx.x * nh + r] = v;
-            else
-                atomicMax((int*)&rnorm[threadIdx.x * nh + r], __float_as_int(v));
-        }
+        if (threadIdx.x < 3)
+            tnorm[((int64_t)threadIdx.x * nh + r) * ntiles + t] =
+                fmaxf(fmaxf(wn[threadIdx.x][0], wn[threadIdx.x][1]),
+                      fmaxf(wn[threadIdx.x][2], wn[threadIdx.x][3]));
     }
     float* dst = rt + ((int64_t)r * ntiles * kHashColTile + col0) * d;
     for (int idx = threadIdx.x; idx < d * kHashColTile; idx += 256) {
@@ -402,7 +362,7 @@ __device__ __forceinline__ void refine_region(const T* __restrict__ qk,
 template <int D, int TOKF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void hash_mfma_kernel(const uint16_t* __restrict__ qk,
                                                         const u32x4* __restrict__ rfrag,
-                                                        const float* __restrict__ rnorm, Dims dm,
+                                                        const float* __restrict__ tnorm, Dims dm,
                                                         int32_t* __restrict__ buckets,
                                                         RefineItem* __restrict__ queue,
                                                         int32_t* __restrict__ rcount,
@@ -586,7 +546,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void h
             }
         }
         if (t != ntiles - 1) return;
-        const float rn_s = rnorm[dm.nr + vr0 + r], res_s = rnorm[2 * dm.nr + vr0 + r];
+        // the round's bounds: the largest over its column tiles
+        float rn_s = 0.f, res_s = 0.f;
+        for (int i = 0; i < ntiles; ++i) {
+            rn_s = fmaxf(rn_s, tnorm[((int64_t)dm.nr + vr0 + r) * ntiles + i]);
+            res_s = fmaxf(res_s, tnorm[(2 * (int64_t)dm.nr + vr0 + r) * ntiles + i]);
+        }
         const float Ea = 2.f * (res_s + kAcc * rn_s), Eb = 2.f * kFlushX * rn_s;
 #pragma unroll
         for (int f = 0; f < TOKF; ++f) {
@@ -664,7 +629,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void h
 template <int D, typename T, bool PH>
 __global__ __launch_bounds__(256) void hash_valu_kernel(const T* __restrict__ qk,
                                                         const float* __restrict__ R,
-                                                        const float* __restrict__ rnorm, Dims dm,
+                                                        const float* __restrict__ tnorm, Dims dm,
                                                         int32_t* __restrict__ buckets,
                                                         RefineItem* __restrict__ queue,
                                                         int32_t* __restrict__ rcount,
@@ -710,7 +675,10 @@ __global__ __launch_bounds__(256) void hash_valu_kernel(const T* __restrict__ qk
     if (half == 1) { v2 = 0.f; v3 = 0.f; i2 = 0; }     // a single column: compare with -p only
     if (half == 2) v3 = 0.f;
     const float xn = sqrtf(xn2) * (1.0f + (float)(D + 4) * kTwoM24);
-    const float thr = 2.f * kCoef * xn * rnorm[rr] + v1 * 9.5367431640625e-7f + 1e-30f;
+    const int ntiles = (half + kHashColTile - 1) / kHashColTile;
+    float rn = 0.f;   // the round's largest column norm, over its tiles
+    for (int i = 0; i < ntiles; ++i) rn = fmaxf(rn, tnorm[(int64_t)rr * ntiles + i]);
+    const float thr = 2.f * kCoef * xn * rn + v1 * 9.5367431640625e-7f + 1e-30f;
     int mode = classify(v1, v2, v3, thr);
     if (half == 1) mode = (v1 > thr) ? -1 : 1;
     int64_t item = 0;
@@ -734,25 +702,46 @@ __global__ __launch_bounds__(256) void hash_valu_kernel(const T* __restrict__ qk
 // atomic max. Key = bits of |p| (a non-negative double, so integer order is
 // float order) with the low 12 bits replaced by 4095 - bucket: equal |p| then
 // prefer the lower bucket index, and values closer than 2^-40 relative count
-// as equal.
+// as equal. A round of one tile (n_buckets <= 64) is all in one workgroup, so
+// the item's bucket is stored at once and no finishing pass is needed.
+// The extra row of blocks (y = number of R rounds) sums the queue regions'
+// counts into the public count.
 template <int D, typename T>
 __global__ __launch_bounds__(256) void hash_scan_kernel(const T* __restrict__ qk,
                                                         const float* __restrict__ rt, Dims dm,
                                                         const int32_t* __restrict__ scount,
                                                         const int32_t* __restrict__ slist,
                                                         uint64_t* __restrict__ sbest,
-                                                        int64_t cap) {
+                                                        int64_t cap, int32_t* __restrict__ buckets,
+                                                        const int32_t* __restrict__ rcount,
+                                                        int64_t nregions,
+                                                        int32_t* __restrict__ counter) {
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     constexpr int G = 64;
     constexpr int S = D + 4;      // row stride: 16-byte aligned rows, rows 4 banks apart
     __shared__ __attribute__((aligned(16))) float rtile[kHashColTile][S];
     __shared__ __attribute__((aligned(16))) float xs[G][S];
     __shared__ int64_t xrow[G];   // element offset of each item's row of x
+    __shared__ int32_t xitem[G];  // each item's flat bucket index
     // x: (column tile, group stride); y/z: R round
     const int ntiles = (dm.nb / 2 + kHashColTile - 1) / kHashColTile;
     const int t = blockIdx.x % ntiles, zg = blockIdx.x / ntiles, Z = gridDim.x / ntiles;
     const int r = (int)block_y();
-    if (r >= dm.nr) return;
+    if (r > dm.nr) return;
+    if (r == dm.nr) {
+        // the public count: the queue regions' two counts, summed
+        if (blockIdx.x != 0) return;
+        __shared__ int32_t part[4];
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        int32_t c = 0;
+#pragma unroll 16
+        for (int64_t i = threadIdx.x; i < 2 * nregions; i += 256) c += rcount[i];
+        for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+        if (lane == 0) part[wave] = c;
+        __syncthreads();
+        if (threadIdx.x == 0) counter[0] = part[0] + part[1] + part[2] + part[3];
+        return;
+    }
     const int half = dm.nb / 2;
     const int hpad = ((half + kHashColTile - 1) / kHashColTile) * kHashColTile;
     const int n = min(scount[r], (int)cap);
@@ -770,12 +759,14 @@ __global__ __launch_bounds__(256) void hash_scan_kernel(const T* __restrict__ qk
         __syncthreads();
         if (threadIdx.x < G) {
             int64_t off = -1;
+            int32_t item = 0;
             if ((int)threadIdx.x < gn) {
-                const int32_t item = slist[(int64_t)r * cap + g0 + threadIdx.x];
+                item = slist[(int64_t)r * cap + g0 + threadIdx.x];
                 const int pos = item % dm.L, bh = item / dm.L / dm.nh;
                 off = ((int64_t)bh * dm.L + pos) * D;
             }
             xrow[threadIdx.x] = off;
+            xitem[threadIdx.x] = item;
         }
         __syncthreads();
 #pragma unroll 8
@@ -818,36 +809,24 @@ __global__ __launch_bounds__(256) void hash_scan_kernel(const T* __restrict__ qk
             const uint64_t o = __shfl_xor(best, off);
             best = o > best ? o : best;
         }
-        if (cq == 0) atomicMax((unsigned long long*)&sbest[(int64_t)r * cap + g0 + it], best);
+        if (cq == 0) {
+            if (ntiles == 1)
+                buckets[xitem[it]] = 4095 - (int)(best & 0xFFFull);
+            else
+                atomicMax((unsigned long long*)&sbest[(int64_t)r * cap + g0 + it], best);
+        }
     }
 }
 
-// The listed items take the bucket of their best key; the last row of
-// workgroups sums the region counts into the public count.
+// The listed items take the bucket of their best key (rounds of more than one
+// column tile, whose tiles were scanned by different workgroups).
 __global__ __launch_bounds__(256) void hash_scan_finish_kernel(const int32_t* __restrict__ scount,
                                                                const int32_t* __restrict__ slist,
                                                                const uint64_t* __restrict__ sbest,
-                                                               int64_t cap,
-                                                               int32_t* __restrict__ buckets,
-                                                               const int32_t* __restrict__ rcount,
-                                                               int64_t nregions, int nr,
-                                                               int32_t* __restrict__ counter) {
-    const int r = (int)block_y();   // R rounds 0 .. nr-1, then the count
-    if (r > nr) return;
-    if (r == nr) {
-        // the public count: the queue regions' two counts, summed
-        if (blockIdx.x != 0) return;
-        __shared__ int32_t part[4];
-        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-        int32_t c = 0;
-#pragma unroll 16
-        for (int64_t i = threadIdx.x; i < 2 * nregions; i += 256) c += rcount[i];
-        for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
-        if (lane == 0) part[wave] = c;
-        __syncthreads();
-        if (threadIdx.x == 0) counter[0] = part[0] + part[1] + part[2] + part[3];
-        return;
-    }
+                                                               int64_t cap, int nr,
+                                                               int32_t* __restrict__ buckets) {
+    const int r = (int)block_y();   // R round
+    if (r >= nr) return;
     const int n = min(scount[r], (int)cap);
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
         buckets[slist[(int64_t)r * cap + i]] = 4095 - (int)(sbest[(int64_t)r * cap + i] & 0xFFFull);
@@ -861,13 +840,18 @@ static hipError_t launch_scan(const T* qk, const Dims& d, int32_t* buckets, cons
     const int64_t cap = queue_tokens(d);
     // enough groups for a few thousand listed items per round; more loop
     const unsigned z = (unsigned)std::min<int64_t>(16, (cap + 63) / 64);
-    const dim3 sgrid = grid_split((unsigned)hash_ntiles(d) * z, d.nr);
+    // one row of blocks per R round, and one more for the public count
+    const dim3 sgrid = grid_split((unsigned)hash_ntiles(d) * z, (int64_t)d.nr + 1);
     if (d.d == 64)
-        hash_scan_kernel<64, T><<<sgrid, 256, 0, st>>>(qk, w.rt, d, w.scount, w.slist, w.sbest, cap);
+        hash_scan_kernel<64, T><<<sgrid, 256, 0, st>>>(qk, w.rt, d, w.scount, w.slist, w.sbest, cap,
+                                                       buckets, w.rcount, nregions, w.counter);
     else
-        hash_scan_kernel<128, T><<<sgrid, 256, 0, st>>>(qk, w.rt, d, w.scount, w.slist, w.sbest, cap);
-    hash_scan_finish_kernel<<<grid_split(4, (int64_t)d.nr + 1), 256, 0, st>>>(
-        w.scount, w.slist, w.sbest, cap, buckets, w.rcount, nregions, d.nr, w.counter);
+        hash_scan_kernel<128, T><<<sgrid, 256, 0, st>>>(qk, w.rt, d, w.scount, w.slist, w.sbest,
+                                                        cap, buckets, w.rcount, nregions,
+                                                        w.counter);
+    if (hash_ntiles(d) > 1)
+        hash_scan_finish_kernel<<<grid_split(4, d.nr), 256, 0, st>>>(w.scount, w.slist, w.sbest,
+                                                                     cap, d.nr, buckets);
     return mark(st, ev, nev, names, "hash_refine_scan");
 }
 
@@ -878,15 +862,12 @@ hipError_t launch_hash(const void* qk, const float* R, const Dims& d, int32_t* b
     const int ntiles = hash_ntiles(d);
     hipError_t e;
     const dim3 pgrid = grid_split((unsigned)ntiles, d.nr);   // every R round
-    if (ntiles == 1) {
-        rprep_kernel<true><<<pgrid, 256, 0, st>>>(R, d.d, half, ntiles, d.nr, w.tmax, w.rnorm,
-                                                  w.rt, w.rfrag, w.counter, w.scount);
-    } else {
-        rmax_kernel<<<pgrid, 256, 0, st>>>(R, d.d, half, ntiles, d.nr, w.tmax, w.counter,
-                                           w.rnorm, w.scount);
-        rprep_kernel<false><<<pgrid, 256, 0, st>>>(R, d.d, half, ntiles, d.nr, w.tmax, w.rnorm,
-                                                   w.rt, w.rfrag, w.counter, w.scount);
-    }
+    if (ntiles == 1)
+        rprep_kernel<true><<<pgrid, 256, 0, st>>>(R, d.d, half, ntiles, d.nr, w.tnorm, w.rt,
+                                                  w.rfrag, w.counter, w.scount);
+    else
+        rprep_kernel<false><<<pgrid, 256, 0, st>>>(R, d.d, half, ntiles, d.nr, w.tnorm, w.rt,
+                                                   w.rfrag, w.counter, w.scount);
     if ((e = mark(st, ev, nev, names, "hash_prep")) != hipSuccess) return e;
     if (d.dtype == LSH_BF16) {
         // two 32-token fragments per wave (32 and 128 tokens per wave measured
@@ -904,11 +885,11 @@ hipError_t launch_hash(const void* qk, const float* R, const Dims& d, int32_t* b
         const int64_t cap = queue_tokens(d);
         if (d.d == 64)
             hash_mfma_kernel<64, TOKF><<<grid, 256, 0, st>>>(
-                x, (const u32x4*)w.rfrag, w.rnorm, d, buckets, w.queue, w.rcount,
+                x, (const u32x4*)w.rfrag, w.tnorm, d, buckets, w.queue, w.rcount,
                 (const uint16_t*)v_for_max, w.vmax, w.rt, w.scount, w.slist, w.sbest, cap);
         else
             hash_mfma_kernel<128, TOKF><<<grid, 256, 0, st>>>(
-                x, (const u32x4*)w.rfrag, w.rnorm, d, buckets, w.queue, w.rcount,
+                x, (const u32x4*)w.rfrag, w.tnorm, d, buckets, w.queue, w.rcount,
                 (const uint16_t*)v_for_max, w.vmax, w.rt, w.scount, w.slist, w.sbest, cap);
         if ((e = mark(st, ev, nev, names, "hash_fast_mfma")) != hipSuccess) return e;
         return launch_scan(x, d, buckets, w, (int64_t)grid * 4, st, ev, nev, names);
@@ -917,7 +898,7 @@ hipError_t launch_hash(const void* qk, const float* R, const Dims& d, int32_t* b
         dim3 grid((unsigned)((d.T + 255) / 256), (unsigned)d.nh);
         const int64_t cap = queue_tokens(d);
 #define LSH_HASH_VALU(DD, PH)                                                                  \
-    hash_valu_kernel<DD, float, PH><<<grid, 256, 0, st>>>(x, R, w.rnorm, d, buckets, w.queue,   \
+    hash_valu_kernel<DD, float, PH><<<grid, 256, 0, st>>>(x, R, w.tnorm, d, buckets, w.queue,   \
                                                           w.rcount, w.rt, w.scount, w.slist,   \
                                                           w.sbest, cap)
         if (d.d == 64) {

@@ -91,17 +91,14 @@ __host__ __device__ inline int r_round(const Dims& d, int64_t bh, int r) {
 struct HashWorkspace {
     int32_t* counter;     // [0]: items re-decided (the public count)
     uint32_t* vmax;       // max|v| (bf16 bits) when the fast pass is asked to fold it in
-    // Per R-round bounds, each [nr] and contiguous, rounded up (atomic max over
-    // column tiles). With R_s = R * 2^e_r, e_r the power of two that brings
-    // max|R| of round r into [2^14, 2^15):
-    //   rnorm   max column 2-norm of R
-    //   rnorm_s max column 2-norm of R_s
-    //   resn_s  max column 2-norm of R_s - fp16(R_s), plus the fp16 subnormal
-    //           elements a matrix core may flush
-    float* rnorm;
-    float* rnorm_s;
-    float* resn_s;
-    float* tmax;          // [nr][ntiles] max |R| per column tile
+    // Per (bound, R round, 32-column tile) bounds, [3][nr][ntiles], each rounded
+    // up; a round's bound is the largest over its tiles. With R_s = R * 2^e_r,
+    // e_r the power of two that brings max|R| of round r into [2^14, 2^15):
+    //   bound 0  largest column 2-norm of R
+    //   bound 1  largest column 2-norm of R_s
+    //   bound 2  largest column 2-norm of R_s - fp16(R_s), plus the fp16
+    //            subnormal elements a matrix core may flush
+    float* tnorm;
     uint16_t* rfrag;      // fp16(R_s) in matrix-core fragment order
     float* rt;            // R transposed to [nr][ntiles*32][d], fp32
     RefineItem* queue;    // [queue_tokens * nh]

@@ -319,6 +319,87 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __rest
     }
 }
 
+// A segment of at most kWaveSeg positions (and at most kWaveSegBuckets
+// buckets) is sorted by one wave on its own, four segments per workgroup and
+// no workgroup barrier: the wave ranks its elements with the ballot match of
+// the scatter, keeping the bucket counts in its own LDS slice; one wave-wide
+// exclusive scan over the buckets turns the counts into run starts; each
+// element's key goes to its slot in a wave-private LDS staging row, which is
+// then written out in slot order. (Through the one-tile scatter such a
+// segment kept one of the workgroup's four waves busy.)
+constexpr int kWaveSeg = kSortTile / kSortWaves;   // 1024
+constexpr int kWaveSegBuckets = 1024;
+
+template <bool PACKED>
+__global__ __launch_bounds__(256) void sort_wave_kernel(const int32_t* __restrict__ buckets,
+                                                        Dims dm, int nbits,
+                                                        int32_t* __restrict__ perm,
+                                                        int32_t* __restrict__ inv) {
+    extern __shared__ int32_t sh[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t seg = (int64_t)blockIdx.x * kSortWaves + wave;
+    if (seg >= dm.segs) return;   // the whole wave leaves; no workgroup barrier follows
+    const int nb = dm.nb, L = dm.L;
+    int32_t* cnt = sh + wave * (kWaveSegBuckets + kWaveSeg);
+    int32_t* lkeys = cnt + kWaveSegBuckets;
+    const int32_t* src = buckets + seg * L;
+    constexpr int STEPS = kWaveSeg / kWave;
+    int kb[STEPS], rank[STEPS];
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+        const int i = s * kWave + lane;
+        kb[s] = i < L ? clamp_bucket(src[i], nb) : 0;
+    }
+    for (int b = lane; b < nb; b += kWave) cnt[b] = 0;
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+        if (s * kWave >= L) break;   // wave-uniform
+        const bool active = s * kWave + lane < L;
+        const uint64_t m = match_bucket(kb[s], nbits, active);
+        rank[s] = cnt[kb[s]] + __popcll(m & lanes_below_s(lane));
+        __builtin_amdgcn_wave_barrier();
+        if (active && (__ffsll((long long)m) - 1) == lane) cnt[kb[s]] += __popcll(m);
+        __builtin_amdgcn_wave_barrier();
+    }
+    // counts -> run starts: each lane takes a contiguous run of buckets
+    const int per = (nb + kWave - 1) / kWave;
+    const int b0 = lane * per;
+    int32_t mine = 0;
+    for (int j = 0; j < per; ++j)
+        if (b0 + j < nb) mine += cnt[b0 + j];
+    int32_t incl = mine;
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int32_t o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+    }
+    int32_t run = incl - mine;
+    __builtin_amdgcn_wave_barrier();
+    for (int j = 0; j < per; ++j)
+        if (b0 + j < nb) {
+            const int32_t c = cnt[b0 + j];
+            cnt[b0 + j] = run;
+            run += c;
+        }
+    __builtin_amdgcn_wave_barrier();
+    int32_t* I = PACKED ? nullptr : inv + seg * L;
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+        const int i = s * kWave + lane;
+        if (i < L) {
+            const int32_t slot = cnt[kb[s]] + rank[s];
+            lkeys[slot] = (int32_t)(((uint32_t)kb[s] << kPackPosBits) | (uint32_t)i);
+            if constexpr (!PACKED) I[i] = slot;
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    int32_t* P = perm + seg * L;
+    for (int i = lane; i < L; i += kWave) {
+        const uint32_t key = (uint32_t)lkeys[i];
+        P[i] = PACKED ? (int32_t)key : (int32_t)(key & kPackPosMask);
+    }
+}
+
 hipError_t launch_sort(const int32_t* buckets, const Dims& d, int32_t* perm, int32_t* inv,
                        void* ws, hipStream_t st, hipEvent_t* ev, int* nev, const char** names,
                        bool packed) {
@@ -334,6 +415,16 @@ hipError_t launch_sort(const int32_t* buckets, const Dims& d, int32_t* perm, int
     const bool staged = packed_sort_keys(d);
     if (packed && !staged) return hipErrorInvalidValue;
     const bool one = staged && ntiles == 1;
+    if (staged && d.L <= kWaveSeg && d.nb <= kWaveSegBuckets) {
+        static_assert(kWaveSeg <= (1 << kPackPosBits), "wave segments use packed keys");
+        const unsigned wgrid = (unsigned)((d.segs + kSortWaves - 1) / kSortWaves);
+        const size_t wlds = sizeof(int32_t) * kSortWaves * (kWaveSegBuckets + kWaveSeg);
+        if (packed)
+            sort_wave_kernel<true><<<wgrid, 256, wlds, st>>>(buckets, d, nbits, perm, nullptr);
+        else
+            sort_wave_kernel<false><<<wgrid, 256, wlds, st>>>(buckets, d, nbits, perm, inv);
+        return mark(st, ev, nev, names, "sort_scatter");
+    }
     if (!one) {
         sort_count_kernel<<<grid, 256, sizeof(int32_t) * d.nb, st>>>(buckets, d, ntiles, counts);
         if ((e = mark(st, ev, nev, names, "sort_count")) != hipSuccess) return e;

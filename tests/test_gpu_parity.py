@@ -101,23 +101,36 @@ def test_hash_glossary_example_on_gpu():
     assert f"{float(near):.0%}" == "72%" and f"{float(far):.0%}" == "9%"
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-def test_hash_exact_ties_and_zero_rows(dtype):
+@pytest.mark.parametrize("dtype,d,nb", [("bf16", 64, 32), ("fp32", 64, 32), ("bf16", 128, 4096),
+                                        ("fp32", 128, 2048), ("bf16", 64, 1024)])
+def test_hash_exact_ties_and_zero_rows(dtype, d, nb):
     """Duplicate columns of R give exact ties (lowest index of [p, -p] wins);
-    zero vectors tie everywhere (bucket 0)."""
-    w = _wl(dtype, L=256, d=64, nb=32, nh=2, m=1)
+    zero vectors tie everywhere (bucket 0). Three equal columns that a row
+    points along leave the fast pass no two candidates, so those rows take the
+    full scan over every column of the round (several 256-column passes of a
+    wave at the larger bucket counts)."""
+    w = _wl(dtype, L=256, d=d, nb=nb, nh=2, m=1)
     qk, v, R, qk_t, v_t, R_t = _tensors(w)
+    half = nb // 2
     R[:, :, 9] = R[:, :, 3]
     R[1, :, 12] = -R[1, :, 5]
+    c1, c2, c3 = half // 4 + 2, half // 2 + 2, half - 2   # clear of columns 3, 5, 9, 12
+    R[:, :, c2] = R[:, :, c1]
+    R[:, :, c3] = R[:, :, c1]
     qk[0, 0, :17] = 0.0
+    qk[0, 0, 17:21] = R[0, :, c1]
+    qk[0, 1, 17:21] = -R[1, :, c1]
     dt = qk_t.dtype
     qk_t = torch.from_numpy(qk).to(DEV, dt)
     R_t = torch.from_numpy(R).to(DEV)
-    buckets, refined = lsh.hash(qk_t, R_t, 32)
-    ref, margin = _oracle_hash(qk, R, 32)
+    buckets, refined = lsh.hash(qk_t, R_t, nb)
+    if dtype == "bf16":   # the oracle sees the rows the GPU hashed
+        qk = qk_t.float().cpu().numpy()
+    ref, margin = _oracle_hash(qk, R, nb)
     assert np.array_equal(buckets.cpu().numpy(), ref)
     assert (ref[0, 0, :, :17] == 0).all()
-    assert refined >= 2 * 17
+    assert (ref[0, 0, 0, 17:21] == c1).all() and (ref[0, 1, 1, 17:21] == c1 + half).all()
+    assert refined >= 2 * 17 + 8
 
 
 # the last three cases span many sort tiles (64K, 64K plus a ragged tail, 96K)
@@ -129,10 +142,16 @@ SORT_CASES = [("uniform", 1024, 4096 + 192), ("uniform", 64, 4096 * 3), ("skewed
 # domains in groups of eight, so the second group is partial, over four
 # tiles with a ragged last one
 SORT_CASES_12 = [("uniform", 512, 3 * 4096 + 64), ("skewed", 1024, 3 * 4096 + 64)]
+# segments of at most 1024 positions are sorted one per wave, four per
+# workgroup: 15 segments (B 1, H 3, 5 rounds) leave the last workgroup
+# three waves short; 2048 buckets take the one-tile scatter instead
+SORT_CASES_WAVE = [("uniform", 32, 1024), ("skewed", 1024, 1000), ("constant", 16, 576),
+                   ("uniform", 2, 64), ("uniform", 2048, 1024)]
 
 
 @pytest.mark.parametrize("kind,nb,L,bhn", [c + ((1, 2, 3),) for c in SORT_CASES] +
-                         [c + ((1, 3, 4),) for c in SORT_CASES_12])
+                         [c + ((1, 3, 4),) for c in SORT_CASES_12] +
+                         [c + ((1, 3, 5),) for c in SORT_CASES_WAVE])
 def test_sort_matches_oracle(kind, nb, L, bhn):
     rng = np.random.default_rng(nb + L)
     B, H, nh = bhn
