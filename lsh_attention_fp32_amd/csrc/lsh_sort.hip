@@ -117,6 +117,56 @@ __global__ __launch_bounds__(256) void sort_count_kernel(const int32_t* __restri
         counts[(seg * ntiles + tile) * dm.nb + b] = hist[b];
 }
 
+// A segment of at most kCPTiles tiles (and kCPBuckets buckets) counts and
+// prefixes in one workgroup of 1024 threads, so neither the per-tile counts
+// nor a second launch go through global memory first: every element adds
+// one to its tile's row of an LDS histogram [tile][bucket] (plain LDS
+// atomics, as in sort_count_kernel), then one thread per bucket walks the
+// tiles and writes the earlier-tile counts and the segment total, the same
+// outputs as sort_count_kernel followed by sort_prefix_kernel. Longer
+// segments keep the two launches, which spread a segment over one workgroup
+// per tile: at 16K positions the fused kernel takes 11 us against 16 us for
+// the pair, at 64K 29 us against 18 us (64 segments fill 64 compute units).
+constexpr int kCPThreads = 1024;
+constexpr int kCPTiles = 4;
+constexpr int kCPBuckets = 2048;
+
+__global__ __launch_bounds__(kCPThreads) void sort_count_prefix_kernel(
+    const int32_t* __restrict__ buckets, Dims dm, int ntiles, int32_t* __restrict__ counts,
+    int32_t* __restrict__ totals) {
+    extern __shared__ int32_t hist[];   // [ntiles][nb]
+    const int64_t seg = block_y();
+    if (seg >= dm.segs) return;
+    const int nb = dm.nb, L = dm.L;
+    for (int i = threadIdx.x; i < ntiles * nb; i += kCPThreads) hist[i] = 0;
+    __syncthreads();
+    const int32_t* src = buckets + seg * L;
+    constexpr int U = 8;   // loads in flight per thread
+    for (int i0 = 0; i0 < L; i0 += U * kCPThreads) {
+        int b[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + u * kCPThreads + threadIdx.x;
+            b[u] = i < L ? clamp_bucket(src[i], nb) : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + u * kCPThreads + threadIdx.x;
+            if (b[u] >= 0) atomicAdd(&hist[(i / kSortTile) * nb + b[u]], 1);
+        }
+    }
+    __syncthreads();
+    for (int b = threadIdx.x; b < nb; b += kCPThreads) {
+        int32_t run = 0;
+        for (int t = 0; t < ntiles; ++t) {
+            const int32_t c = hist[t * nb + b];
+            counts[(seg * ntiles + t) * nb + b] = run;
+            run += c;
+        }
+        totals[seg * nb + b] = run;
+    }
+}
+
 // counts[seg][t][b] -> number of b in tiles 0 .. t-1 of the segment (in
 // place); totals[seg][b] = number of b in the segment. One thread per bucket,
 // so every tile's row is read and written with coalesced accesses; the loads
@@ -425,7 +475,12 @@ hipError_t launch_sort(const int32_t* buckets, const Dims& d, int32_t* perm, int
             sort_wave_kernel<false><<<wgrid, 256, wlds, st>>>(buckets, d, nbits, perm, inv);
         return mark(st, ev, nev, names, "sort_scatter");
     }
-    if (!one) {
+    if (!one && ntiles <= kCPTiles && d.nb <= kCPBuckets) {
+        sort_count_prefix_kernel<<<grid_split(1, d.segs), kCPThreads,
+                                   sizeof(int32_t) * ntiles * d.nb, st>>>(buckets, d, ntiles,
+                                                                          counts, totals);
+        if ((e = mark(st, ev, nev, names, "sort_count")) != hipSuccess) return e;
+    } else if (!one) {
         sort_count_kernel<<<grid, 256, sizeof(int32_t) * d.nb, st>>>(buckets, d, ntiles, counts);
         if ((e = mark(st, ev, nev, names, "sort_count")) != hipSuccess) return e;
         sort_prefix_kernel<<<grid_split((unsigned)((d.nb + 255) / 256), d.segs), 256, 0, st>>>(
