@@ -482,6 +482,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void h
     }
 
     for (int i = threadIdx.x; i < TILE_U4; i += 256) lds[0][i] = rf[i];
+    // each round's two certification bounds (R_s norm, residual norm): the
+    // largest over the round's column tiles, once per workgroup, in LDS
+    // (dynamic: 2 * n_hashes floats)
+    extern __shared__ float rbound[];
+    for (int i = threadIdx.x; i < 2 * dm.nh; i += 256) {
+        const int b = 1 + i / dm.nh, rr = vr0 + i % dm.nh;
+        const float* tb = tnorm + ((int64_t)b * dm.nr + rr) * ntiles;
+        float m = 0.f;
+        for (int j = 0; j < ntiles; ++j) m = fmaxf(m, tb[j]);
+        rbound[i] = m;
+    }
     __syncthreads();
     if (v && threadIdx.x == 0)
         atomicMax(vmax, max(max(wvmax[0], wvmax[1]), max(wvmax[2], wvmax[3])));
@@ -546,12 +557,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void h
             }
         }
         if (t != ntiles - 1) return;
-        // the round's bounds: the largest over its column tiles
-        float rn_s = 0.f, res_s = 0.f;
-        for (int i = 0; i < ntiles; ++i) {
-            rn_s = fmaxf(rn_s, tnorm[((int64_t)dm.nr + vr0 + r) * ntiles + i]);
-            res_s = fmaxf(res_s, tnorm[(2 * (int64_t)dm.nr + vr0 + r) * ntiles + i]);
-        }
+        const float rn_s = rbound[r], res_s = rbound[dm.nh + r];
         const float Ea = 2.f * (res_s + kAcc * rn_s), Eb = 2.f * kFlushX * rn_s;
 #pragma unroll
         for (int f = 0; f < TOKF; ++f) {
@@ -882,13 +888,14 @@ hipError_t launch_hash(const void* qk, const float* R, const Dims& d, int32_t* b
                                   ? (unsigned)((int64_t)d.B * d.H * ((d.L + per_wg - 1) / per_wg))
                                   : (unsigned)((d.T + per_wg - 1) / per_wg);
         const uint16_t* x = (const uint16_t*)qk;
+        const size_t rb_lds = sizeof(float) * 2 * d.nh;   // per-round bounds
         const int64_t cap = queue_tokens(d);
         if (d.d == 64)
-            hash_mfma_kernel<64, TOKF><<<grid, 256, 0, st>>>(
+            hash_mfma_kernel<64, TOKF><<<grid, 256, rb_lds, st>>>(
                 x, (const u32x4*)w.rfrag, w.tnorm, d, buckets, w.queue, w.rcount,
                 (const uint16_t*)v_for_max, w.vmax, w.rt, w.scount, w.slist, w.sbest, cap);
         else
-            hash_mfma_kernel<128, TOKF><<<grid, 256, 0, st>>>(
+            hash_mfma_kernel<128, TOKF><<<grid, 256, rb_lds, st>>>(
                 x, (const u32x4*)w.rfrag, w.tnorm, d, buckets, w.queue, w.rcount,
                 (const uint16_t*)v_for_max, w.vmax, w.rt, w.scount, w.slist, w.sbest, cap);
         if ((e = mark(st, ev, nev, names, "hash_fast_mfma")) != hipSuccess) return e;
