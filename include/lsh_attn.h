@@ -206,8 +206,9 @@ int lsh_unsort_combine(const float *o_sorted, const float *lse_sorted, const int
  * shape: with bf16 I/O, chunk 64 and one hash round the chunk pass writes
  * out itself (the combine's weight is 1) and no combine kernel runs; a
  * segment of at most 4096 positions is sorted by one kernel instead of
- * three; with n_buckets <= 64 the hash's full scans store their buckets
- * themselves and no finishing kernel runs. */
+ * three, and one of two to four tiles (4096 < L <= 16384, n_buckets <=
+ * 2048) by two; with n_buckets <= 64 the hash's full scans store their
+ * buckets themselves and no finishing kernel runs. */
 int lsh_attention_fwd(const void *qk, const void *v, const float *R, const lsh_shape_t *shape,
                       void *out, void *ws, size_t ws_bytes, void *stream);
 

@@ -261,8 +261,14 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __rest
     // run starts are computed) and stay in registers.
     const int32_t* src = buckets + seg * dm.L;
     const int64_t tbeg = (int64_t)tile * kSortTile;
-    const int64_t wbeg = tbeg + (int64_t)wave * SUB;
-    const int64_t wend = min(wbeg + (int64_t)SUB, (int64_t)dm.L);
+    // a one-tile segment shorter than the tile spreads over all four waves
+    // (whole 64-element steps each), so each wave's ranking chain is a quarter
+    // of the segment instead of one wave doing up to SUB elements
+    const int sub = ONE_TILE ? (int)min((int64_t)SUB, (dm.L + kSortWaves * kWave - 1) /
+                                                            (kSortWaves * kWave) * kWave)
+                             : SUB;
+    const int64_t wbeg = tbeg + (int64_t)wave * sub;
+    const int64_t wend = min(wbeg + (int64_t)sub, (int64_t)dm.L);
     constexpr int STEPS = SUB / kWave;
     int kb[STEPS], rank[STEPS];
 #pragma unroll
@@ -295,6 +301,7 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __rest
     // adds the (wave, bucket) run start and stores.
 #pragma unroll
     for (int s = 0; s < STEPS; ++s) {
+        if (wbeg + s * kWave >= wend) break;   // wave-uniform
         const bool active = wbeg + s * kWave + lane < wend;
         const uint64_t m = match_bucket(kb[s], nbits, active);
         rank[s] = mine[kb[s]] + __popcll(m & lanes_below_s(lane));
@@ -376,9 +383,14 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __rest
 // exclusive scan over the buckets turns the counts into run starts; each
 // element's key goes to its slot in a wave-private LDS staging row, which is
 // then written out in slot order. (Through the one-tile scatter such a
-// segment kept one of the workgroup's four waves busy.)
+// segment kept one of the workgroup's four waves busy.) Used when there are
+// more than kWaveSortSegs segments; fewer go to the one-tile scatter, whose
+// four waves split a segment so each ranking chain is a quarter as long (at
+// 64 x 1K positions the sort takes 9.7 against 16.2 us with one round, 16.4
+// against 17.9 with four, 23.4 against 20.7 with eight).
 constexpr int kWaveSeg = kSortTile / kSortWaves;   // 1024
 constexpr int kWaveSegBuckets = 1024;
+constexpr int64_t kWaveSortSegs = 2048;   // eight segments per compute unit
 
 template <bool PACKED>
 __global__ __launch_bounds__(256) void sort_wave_kernel(const int32_t* __restrict__ buckets,
@@ -465,7 +477,7 @@ hipError_t launch_sort(const int32_t* buckets, const Dims& d, int32_t* perm, int
     const bool staged = packed_sort_keys(d);
     if (packed && !staged) return hipErrorInvalidValue;
     const bool one = staged && ntiles == 1;
-    if (staged && d.L <= kWaveSeg && d.nb <= kWaveSegBuckets) {
+    if (staged && d.L <= kWaveSeg && d.nb <= kWaveSegBuckets && d.segs > kWaveSortSegs) {
         static_assert(kWaveSeg <= (1 << kPackPosBits), "wave segments use packed keys");
         const unsigned wgrid = (unsigned)((d.segs + kSortWaves - 1) / kSortWaves);
         const size_t wlds = sizeof(int32_t) * kSortWaves * (kWaveSegBuckets + kWaveSeg);

@@ -142,16 +142,22 @@ SORT_CASES = [("uniform", 1024, 4096 + 192), ("uniform", 64, 4096 * 3), ("skewed
 # domains in groups of eight, so the second group is partial, over four
 # tiles with a ragged last one
 SORT_CASES_12 = [("uniform", 512, 3 * 4096 + 64), ("skewed", 1024, 3 * 4096 + 64)]
-# segments of at most 1024 positions are sorted one per wave, four per
-# workgroup: 15 segments (B 1, H 3, 5 rounds) leave the last workgroup
-# three waves short; 2048 buckets take the one-tile scatter instead
+# a one-tile segment (at most 4096 positions) is spread over the scatter's
+# four waves: 15 segments (B 1, H 3, 5 rounds) of 64 ... 3000 positions;
+# with more than 2048 segments of at most 1024 positions, each is sorted by
+# one wave, four per workgroup (2112 segments: B 1, H 64, 33 rounds, so the
+# last workgroup is the grid's partial one)
 SORT_CASES_WAVE = [("uniform", 32, 1024), ("skewed", 1024, 1000), ("constant", 16, 576),
-                   ("uniform", 2, 64), ("uniform", 2048, 1024)]
+                   ("uniform", 2, 64), ("uniform", 2048, 1024), ("uniform", 64, 3000)]
+
+
+SORT_CASES_MANY = [("uniform", 64, 256), ("skewed", 1024, 200), ("constant", 16, 1024)]
 
 
 @pytest.mark.parametrize("kind,nb,L,bhn", [c + ((1, 2, 3),) for c in SORT_CASES] +
                          [c + ((1, 3, 4),) for c in SORT_CASES_12] +
-                         [c + ((1, 3, 5),) for c in SORT_CASES_WAVE])
+                         [c + ((1, 3, 5),) for c in SORT_CASES_WAVE] +
+                         [c + ((1, 64, 33),) for c in SORT_CASES_MANY])
 def test_sort_matches_oracle(kind, nb, L, bhn):
     rng = np.random.default_rng(nb + L)
     B, H, nh = bhn
