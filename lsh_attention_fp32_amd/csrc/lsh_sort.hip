@@ -196,12 +196,13 @@ __global__ __launch_bounds__(256) void sort_prefix_kernel(int32_t* __restrict__ 
 
 constexpr int kScatterXcds = 8;   // L2 domains of the chip
 
-// Exclusive scan of a[0..n) in LDS by the 256 threads of the workgroup (each
+// Exclusive scan of a[0..n) in LDS by the T threads of the workgroup (each
 // takes a contiguous chunk, then a wave scan and the earlier waves' sums).
 // Ends with a barrier; a[] is read and written only between barriers.
+template <int T>
 __device__ __forceinline__ void block_exclusive_scan(int32_t* a, int n, int32_t* wsum) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int per = (n + 255) / 256;
+    const int per = (n + T - 1) / T;
     const int b0 = threadIdx.x * per;
     int32_t mine = 0;
     for (int j = 0; j < per; ++j)
@@ -229,22 +230,24 @@ __device__ __forceinline__ void block_exclusive_scan(int32_t* a, int n, int32_t*
 // in their sorted order in LDS, then written out with consecutive threads on
 // consecutive slots, so each (tile, bucket) run leaves as one contiguous
 // piece instead of one 4-byte store per element at scattered slots.
-template <bool PACKED, bool STAGED, bool ONE_TILE>
-__global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __restrict__ buckets,
+// W waves per workgroup share a tile, each ranking a contiguous 1/W of it.
+template <bool PACKED, bool STAGED, bool ONE_TILE, int W>
+__global__ __launch_bounds__(64 * W) void sort_scatter_kernel(const int32_t* __restrict__ buckets,
                                                            const int32_t* __restrict__ prefix,
                                                            const int32_t* __restrict__ totals,
                                                            Dims dm, int ntiles, int nbits,
                                                            int32_t* __restrict__ perm,
                                                            int32_t* __restrict__ inv) {
-    // LDS: [kSortWaves][nb] per-wave counts, then run starts; [nb] the tile's
+    constexpr int T = 64 * W;
+    // LDS: [W][nb] per-wave counts, then run starts; [nb] the tile's
     // first slot of each bucket (later: slot minus tile-local index); STAGED:
     // [kSortTile] the tile's keys in sorted order, whose first nb entries
     // hold the tile-local bucket starts before the keys are written
     extern __shared__ int32_t sh[];
-    __shared__ int32_t wsum[4];
+    __shared__ int32_t wsum[W];
     static_assert(!PACKED || STAGED, "packed keys are staged");
     static_assert(!ONE_TILE || STAGED, "a one-tile segment is sorted in its staged order");
-    constexpr int SUB = kSortTile / kSortWaves;
+    constexpr int SUB = kSortTile / W;
     // Workgroups are dealt round-robin over the L2 domains (id % kScatterXcds):
     // every tile of a segment gets the same residue, so one L2 collects the
     // segment's writes and hands whole lines to memory.
@@ -254,19 +257,17 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __rest
     if (seg >= dm.segs) return;   // the grid is rounded up to whole domain groups
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nb = dm.nb;
-    int32_t* start = sh + kSortWaves * nb;
+    int32_t* start = sh + W * nb;
     int32_t* lkeys = start + nb;
 
-    // The wave's 1024 bucket ids are loaded first (all in flight while the
+    // The wave's bucket ids (at most SUB) are loaded first (all in flight while the
     // run starts are computed) and stay in registers.
     const int32_t* src = buckets + seg * dm.L;
     const int64_t tbeg = (int64_t)tile * kSortTile;
-    // a one-tile segment shorter than the tile spreads over all four waves
-    // (whole 64-element steps each), so each wave's ranking chain is a quarter
-    // of the segment instead of one wave doing up to SUB elements
-    const int sub = ONE_TILE ? (int)min((int64_t)SUB, (dm.L + kSortWaves * kWave - 1) /
-                                                            (kSortWaves * kWave) * kWave)
-                             : SUB;
+    // a one-tile segment shorter than the tile spreads over all W waves
+    // (whole 64-element steps each), so each wave's ranking chain is 1/W of
+    // the segment instead of one wave doing up to SUB elements
+    const int sub = ONE_TILE ? (int)min((int64_t)SUB, (dm.L + T - 1) / T * kWave) : SUB;
     const int64_t wbeg = tbeg + (int64_t)wave * sub;
     const int64_t wend = min(wbeg + (int64_t)sub, (int64_t)dm.L);
     constexpr int STEPS = SUB / kWave;
@@ -284,16 +285,16 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __rest
     if constexpr (!ONE_TILE) {
         const int32_t* tot = totals + seg * nb;
         const int32_t* pre = prefix + (seg * ntiles + tile) * nb;
-        for (int b = threadIdx.x; b < nb; b += 256) {
+        for (int b = threadIdx.x; b < nb; b += T) {
             start[b] = tot[b];
             sh[b] = pre[b];
         }
         __syncthreads();
-        block_exclusive_scan(start, nb, wsum);
-        for (int b = threadIdx.x; b < nb; b += 256) start[b] += sh[b];
+        block_exclusive_scan<T>(start, nb, wsum);
+        for (int b = threadIdx.x; b < nb; b += T) start[b] += sh[b];
     }
     __syncthreads();
-    for (int k = threadIdx.x; k < kSortWaves * nb; k += 256) sh[k] = 0;
+    for (int k = threadIdx.x; k < W * nb; k += T) sh[k] = 0;
     __syncthreads();
     int32_t* mine = sh + wave * nb;
     // Pass 1 ranks every element among the wave's earlier elements of its
@@ -315,17 +316,17 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __rest
         // tile-local start of every bucket (scan of the tile's counts), then
         // each (wave, bucket) run's local start; start[] becomes slot - local
         int32_t* lstart = lkeys;
-        for (int b = threadIdx.x; b < nb; b += 256) {
+        for (int b = threadIdx.x; b < nb; b += T) {
             int32_t c = 0;
-            for (int w = 0; w < kSortWaves; ++w) c += sh[w * nb + b];
+            for (int w = 0; w < W; ++w) c += sh[w * nb + b];
             lstart[b] = c;
         }
         __syncthreads();
-        block_exclusive_scan(lstart, nb, wsum);
-        for (int b = threadIdx.x; b < nb; b += 256) {
+        block_exclusive_scan<T>(lstart, nb, wsum);
+        for (int b = threadIdx.x; b < nb; b += T) {
             int32_t run = lstart[b];
             start[b] = ONE_TILE ? 0 : start[b] - run;
-            for (int w = 0; w < kSortWaves; ++w) {
+            for (int w = 0; w < W; ++w) {
                 const int32_t c = sh[w * nb + b];
                 sh[w * nb + b] = run;
                 run += c;
@@ -345,16 +346,16 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(const int32_t* __rest
         __syncthreads();
         int32_t* P = perm + seg * dm.L;
         const int n = (int)min((int64_t)kSortTile, (int64_t)dm.L - tbeg);
-        for (int i = threadIdx.x; i < n; i += 256) {
+        for (int i = threadIdx.x; i < n; i += T) {
             const uint32_t key = (uint32_t)lkeys[i];
             const int32_t slot = i + start[key >> kPackPosBits];
             P[slot] = PACKED ? (int32_t)key : (int32_t)(key & kPackPosMask);
         }
     } else {
         // first slot of each (wave, bucket) run
-        for (int b = threadIdx.x; b < nb; b += 256) {
+        for (int b = threadIdx.x; b < nb; b += T) {
             int32_t run = start[b];
-            for (int w = 0; w < kSortWaves; ++w) {
+            for (int w = 0; w < W; ++w) {
                 const int32_t c = sh[w * nb + b];
                 sh[w * nb + b] = run;
                 run += c;
@@ -462,6 +463,22 @@ __global__ __launch_bounds__(256) void sort_wave_kernel(const int32_t* __restric
     }
 }
 
+// Waves per scatter workgroup: more waves shorten each wave's ranking chain
+// (a tile's elements are split among them) at the cost of W per-wave count
+// rows of nb entries to clear, scan and walk, and of fewer workgroups per
+// compute unit. Chosen from same-box measurements of the scatter (4 / 8 / 16
+// waves): 16 x 4K positions, 128 buckets, one round 19.0 / 13.1 / 10.9 us,
+// eight rounds 23.7 / 20.7 / 23.3; 8 x 8 x 4K, 64 buckets 19.2 / 13.7 / 11.3;
+// 64 x 1K, 32 buckets 10.0 / 8.8 / 9.4; four-tile segments at 4 x 16K, 512
+// buckets 18.6 / 13.2 (8 waves); 16-tile segments at 64K, 1024 buckets
+// 29.7 / 32.1 (8 waves).
+static int scatter_waves(const Dims& d, bool one) {
+    const int64_t wgs = d.segs * sort_ntiles(d);
+    if (one && d.L >= 2048 && d.nb <= 512 && wgs <= 4096) return 16;
+    if (d.nb <= 512 || (one && d.nb <= 1024)) return 8;
+    return 4;
+}
+
 hipError_t launch_sort(const int32_t* buckets, const Dims& d, int32_t* perm, int32_t* inv,
                        void* ws, hipStream_t st, hipEvent_t* ev, int* nev, const char** names,
                        bool packed) {
@@ -500,22 +517,33 @@ hipError_t launch_sort(const int32_t* buckets, const Dims& d, int32_t* perm, int
         if ((e = mark(st, ev, nev, names, "sort_prefix")) != hipSuccess) return e;
     }
     static_assert(kSortTile >= kMaxBuckets, "the staged keys' space first holds nb starts");
-    const size_t lds = sizeof(int32_t) * ((kSortWaves + 1) * d.nb + (staged ? kSortTile : 0));
     const int64_t sgroups = (d.segs + kScatterXcds - 1) / kScatterXcds;
     const unsigned sgrid = (unsigned)(sgroups * kScatterXcds * ntiles);
-#define LSH_SCATTER(P, S, O, INV)                                                            \
-    sort_scatter_kernel<P, S, O><<<sgrid, 256, lds, st>>>(buckets, counts, totals, d, ntiles, \
-                                                          nbits, perm, INV)
+    const int W = scatter_waves(d, one);
+#define LSH_SCATTER(P, S, O, INV, WW)                                                          \
+    sort_scatter_kernel<P, S, O, WW>                                                           \
+        <<<sgrid, 64 * WW, sizeof(int32_t) * ((WW + 1) * d.nb + (S ? kSortTile : 0)), st>>>( \
+            buckets, counts, totals, d, ntiles, nbits, perm, INV)
+#define LSH_SCATTER_W(P, S, O, INV)          \
+    do {                                     \
+        if (W == 16)                         \
+            LSH_SCATTER(P, S, O, INV, 16);   \
+        else if (W == 8)                     \
+            LSH_SCATTER(P, S, O, INV, 8);    \
+        else                                 \
+            LSH_SCATTER(P, S, O, INV, 4);    \
+    } while (0)
     if (packed && one)
-        LSH_SCATTER(true, true, true, nullptr);
+        LSH_SCATTER_W(true, true, true, nullptr);
     else if (packed)
-        LSH_SCATTER(true, true, false, nullptr);
+        LSH_SCATTER_W(true, true, false, nullptr);
     else if (one)
-        LSH_SCATTER(false, true, true, inv);
+        LSH_SCATTER_W(false, true, true, inv);
     else if (staged)
-        LSH_SCATTER(false, true, false, inv);
+        LSH_SCATTER_W(false, true, false, inv);
     else
-        LSH_SCATTER(false, false, false, inv);
+        LSH_SCATTER(false, false, false, inv, 4);
+#undef LSH_SCATTER_W
 #undef LSH_SCATTER
     return mark(st, ev, nev, names, "sort_scatter");
 }
