@@ -200,9 +200,15 @@ constexpr int kM = 64;            // chunk length of the matrix-core kernel
 constexpr int kWin = 2 * kM;      // keys in a window
 // Chunks per workgroup: 32 where the grid still holds at least eight
 // workgroups per compute unit (2 % less chunk-pass time than 16 at 64K tokens
-// x 8 heads x 8 rounds; 8 and 64 are slower), else 16.
+// x 8 heads x 8 rounds; 8 and 64 are slower), else 16 where it holds four,
+// else 8. Same-box A/B of 16 against 8 (and 4) where 16 leaves two
+// workgroups per compute unit, all one-round shapes: 64 x 1K 52.6 -> 43.3 us
+// (47.0 with 4), 16 x 4K 54.4 -> 45.1, 4 x 16K 56.0 -> 46.9, 1 x 64K 57.3 ->
+// 47.6; where 16 already gives four per unit (two rounds at 64 x 1K and
+// 16 x 4K, 8 x 8 x 4K with four rounds) 8 is 1-4 % slower.
 inline int attend_run_len(int64_t segs, int nchunks) {
-    return segs * ((nchunks + 31) / 32) >= 8 * 256 ? 32 : 16;
+    if (segs * ((nchunks + 31) / 32) >= 8 * 256) return 32;
+    return segs * ((nchunks + 15) / 16) >= 4 * 256 ? 16 : 8;
 }
 // Chunks whose gathers are in flight behind the one computing: one measures
 // as fast as two or three at 64K tokens and holds the fewest registers.
