@@ -117,15 +117,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 // mantissa bits: word j of the group holds bit j in its low half and bit
 // 16 + j in its high half. The thread owning 16-byte piece q of a row has
 // words j = 4 (q % 4) .. +3; the four threads of a quad together see one
-// whole group, so two DPP swaps assemble the value.
-template <int D, typename T>
+// whole group, so two DPP swaps assemble the value. G rounds' loads are
+// issued together (2, 4 or 8: the round count rounded up, at most 8), so few
+// rounds do not load and weigh padding rows.
+template <int D, typename T, int G>
 __global__ __launch_bounds__(256) void combine_bypos_kernel(const _Float16* __restrict__ o_pos,
                                                             const uint32_t* __restrict__ vmax,
                                                             Dims dm, T* __restrict__ out,
                                                             float* __restrict__ z) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     constexpr int TPT = D / 8;   // threads per token, one 16-byte piece each
-    constexpr int G = 8;         // rounds whose loads are issued together
     // Blocks run from the last token back: the chunk pass finishes with the
     // last (batch, head) slices, whose rows are then still in the memory-side
     // cache when this pass starts.
@@ -196,10 +197,18 @@ static void launch_t(const OSorted& o, const float* lse, const int32_t* inv, con
     const unsigned grid = (unsigned)((d.T * (d.d / 8) + 255) / 256);
     if (o.half) {
         const _Float16* op = (const _Float16*)o.ptr;
-        if (d.d == 64)
-            combine_bypos_kernel<64, T><<<grid, 256, 0, st>>>(op, o.vmax, d, out, z);
-        else
-            combine_bypos_kernel<128, T><<<grid, 256, 0, st>>>(op, o.vmax, d, out, z);
+#define LSH_BYPOS(DD, GG) combine_bypos_kernel<DD, T, GG><<<grid, 256, 0, st>>>(op, o.vmax, d, out, z)
+        const int g = d.nh <= 2 ? 2 : d.nh <= 4 ? 4 : 8;
+        if (d.d == 64) {
+            if (g == 2) LSH_BYPOS(64, 2);
+            else if (g == 4) LSH_BYPOS(64, 4);
+            else LSH_BYPOS(64, 8);
+        } else {
+            if (g == 2) LSH_BYPOS(128, 2);
+            else if (g == 4) LSH_BYPOS(128, 4);
+            else LSH_BYPOS(128, 8);
+        }
+#undef LSH_BYPOS
     } else {
         const float* op = (const float*)o.ptr;
         if (d.d == 64)
