@@ -471,11 +471,12 @@ __global__ __launch_bounds__(256) void sort_wave_kernel(const int32_t* __restric
 // eight rounds 23.7 / 20.7 / 23.3; 8 x 8 x 4K, 64 buckets 19.2 / 13.7 / 11.3;
 // 64 x 1K, 32 buckets 10.0 / 8.8 / 9.4; four-tile segments at 4 x 16K, 512
 // buckets 18.6 / 13.2 (8 waves); 16-tile segments at 64K, 1024 buckets
-// 29.7 / 32.1 (8 waves).
+// 29.7 / 32.1 (8 waves); 16-tile segments at 64K, 2048 buckets (whole sort)
+// 43.9 / 35.5 us on 128 workgroups, 44.8 / 37.2 on 256, 48.9 / 53.1 on 512.
 static int scatter_waves(const Dims& d, bool one) {
     const int64_t wgs = d.segs * sort_ntiles(d);
     if (one && d.L >= 2048 && d.nb <= 512 && wgs <= 4096) return 16;
-    if (d.nb <= 512 || (one && d.nb <= 1024)) return 8;
+    if (d.nb <= 512 || (one && d.nb <= 1024) || (wgs <= 256 && d.nb <= 2048)) return 8;
     return 4;
 }
 
