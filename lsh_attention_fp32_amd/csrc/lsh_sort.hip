@@ -15,13 +15,17 @@
 //   scatter per tile: the slot where each of its (tile, bucket) runs starts
 //           is the exclusive scan of the segment's totals plus the tile's
 //           prefix -- 2 nb values read per tile, whatever the number of
-//           tiles -- then each wave ranks its 1024 elements in order; lanes
-//           with equal buckets are grouped by a ballot match, so ranks are
-//           exact and the LDS counter of a hot bucket is bumped once per wave
-//           step (skewed buckets do not serialise on LDS atomics).
+//           tiles -- then each of its 4, 8 or 16 waves ranks its share of
+//           the tile in order; lanes with equal buckets are grouped by a
+//           ballot match, so ranks are exact and the LDS counter of a hot
+//           bucket is bumped once per wave step (skewed buckets do not
+//           serialise on LDS atomics).
 // A segment of one tile (L <= 4096) is its own tile: the tile-local order the
 // scatter builds is the segment's order, so the count and prefix launches are
-// skipped and the scatter alone sorts it.
+// skipped and the scatter alone sorts it. A segment of two to four tiles
+// counts and prefixes in one launch (sort_count_prefix_kernel), and many
+// segments of at most 1024 positions are sorted one per wave
+// (sort_wave_kernel).
 #include <mutex>
 
 #include "lsh_internal.h"
