@@ -721,7 +721,8 @@ __global__ __launch_bounds__(256) void hash_scan_kernel(const T* __restrict__ qk
                                                         int64_t cap, int32_t* __restrict__ buckets,
                                                         const int32_t* __restrict__ rcount,
                                                         int64_t nregions,
-                                                        int32_t* __restrict__ counter) {
+                                                        int32_t* __restrict__ counter,
+                                                        int spec) {
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     constexpr int G = 64;
     constexpr int S = D + 4;      // row stride: 16-byte aligned rows, rows 4 banks apart
@@ -750,36 +751,83 @@ __global__ __launch_bounds__(256) void hash_scan_kernel(const T* __restrict__ qk
     }
     const int half = dm.nb / 2;
     const int hpad = ((half + kHashColTile - 1) / kHashColTile) * kHashColTile;
-    const int n = min(scount[r], (int)cap);
     const int64_t first = (int64_t)zg * G;
+    // With spec (a launch of few workgroups, each on the critical path), the
+    // first group's list entries are read together with the list count
+    // (entries up to the list's capacity are in bounds; those past the count
+    // are never used), and its x rows are requested together with the R tile,
+    // so the group starts after two dependent memory round trips, not four.
+    // (In a launch of thousands of mostly idle workgroups the extra reads cost
+    // more than they save.) Thread i gathers 16-byte piece i % QPR of rows
+    // i / QPR + u * (256 / QPR).
+    constexpr int QPR = D / 4, JPT = G * QPR / 256;
+    const int j0 = threadIdx.x / QPR, kq = 4 * (threadIdx.x % QPR);
+    const int32_t* lr = slist + (int64_t)r * cap;
+    int32_t pit[JPT];
+    int32_t myitem = 0;
+    if (spec) {
+#pragma unroll
+        for (int u = 0; u < JPT; ++u) {
+            const int64_t e = first + j0 + u * (256 / QPR);
+            pit[u] = e < cap ? lr[e] : 0;
+        }
+        if (threadIdx.x < G && first + threadIdx.x < cap) myitem = lr[first + threadIdx.x];
+    }
+    const int n = min(scount[r], (int)cap);
     if (first >= n) return;
-    const float* Rt = rt + ((int64_t)r * hpad + (int64_t)t * kHashColTile) * D;
+    if (!spec) {
+        const float* Rt = rt + ((int64_t)r * hpad + (int64_t)t * kHashColTile) * D;
 #pragma unroll 4
-    for (int i = threadIdx.x; i < kHashColTile * D / 4; i += 256) {
-        const int c = i / (D / 4), k = 4 * (i % (D / 4));
-        *(f32x4*)&rtile[c][k] = *(const f32x4*)(Rt + (int64_t)c * D + k);
+        for (int i = threadIdx.x; i < kHashColTile * D / 4; i += 256) {
+            const int c = i / (D / 4), k = 4 * (i % (D / 4));
+            *(f32x4*)&rtile[c][k] = *(const f32x4*)(Rt + (int64_t)c * D + k);
+        }
+    } else {
+        const int gn = (int)min((int64_t)G, n - first);
+        f32x4 xv[JPT];
+#pragma unroll
+        for (int u = 0; u < JPT; ++u) {
+            const int j = j0 + u * (256 / QPR);
+            xv[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            if (j < gn) {
+                const int pos = pit[u] % dm.L, bh = pit[u] / dm.L / dm.nh;
+                xv[u] = IO<T>::load4(qk, ((int64_t)bh * dm.L + pos) * D + kq);
+            }
+        }
+        const float* Rt = rt + ((int64_t)r * hpad + (int64_t)t * kHashColTile) * D;
+#pragma unroll 4
+        for (int i = threadIdx.x; i < kHashColTile * D / 4; i += 256) {
+            const int c = i / (D / 4), k = 4 * (i % (D / 4));
+            *(f32x4*)&rtile[c][k] = *(const f32x4*)(Rt + (int64_t)c * D + k);
+        }
+#pragma unroll
+        for (int u = 0; u < JPT; ++u) *(f32x4*)&xs[j0 + u * (256 / QPR)][kq] = xv[u];
+        if (threadIdx.x < G) xitem[threadIdx.x] = (int)threadIdx.x < gn ? myitem : 0;
     }
     const int it = threadIdx.x >> 2, cq = threadIdx.x & 3;   // item, column quarter
     for (int64_t g0 = first; g0 < n; g0 += (int64_t)Z * G) {
         const int gn = (int)min((int64_t)G, n - g0);
-        __syncthreads();
-        if (threadIdx.x < G) {
-            int64_t off = -1;
-            int32_t item = 0;
-            if ((int)threadIdx.x < gn) {
-                item = slist[(int64_t)r * cap + g0 + threadIdx.x];
-                const int pos = item % dm.L, bh = item / dm.L / dm.nh;
-                off = ((int64_t)bh * dm.L + pos) * D;
+        if (g0 != first || !spec) {   // groups whose rows are not gathered yet
+            __syncthreads();
+            if (threadIdx.x < G) {
+                int64_t off = -1;
+                int32_t item = 0;
+                if ((int)threadIdx.x < gn) {
+                    item = lr[g0 + threadIdx.x];
+                    const int pos = item % dm.L, bh = item / dm.L / dm.nh;
+                    off = ((int64_t)bh * dm.L + pos) * D;
+                }
+                xrow[threadIdx.x] = off;
+                xitem[threadIdx.x] = item;
             }
-            xrow[threadIdx.x] = off;
-            xitem[threadIdx.x] = item;
-        }
-        __syncthreads();
+            __syncthreads();
 #pragma unroll 8
-        for (int i = threadIdx.x; i < G * D / 4; i += 256) {
-            const int j = i / (D / 4), k = 4 * (i % (D / 4));
-            const int64_t off = xrow[j];
-            *(f32x4*)&xs[j][k] = off >= 0 ? IO<T>::load4(qk, off + k) : (f32x4){0.f, 0.f, 0.f, 0.f};
+            for (int i = threadIdx.x; i < G * D / 4; i += 256) {
+                const int j = i / (D / 4), k = 4 * (i % (D / 4));
+                const int64_t off = xrow[j];
+                *(f32x4*)&xs[j][k] =
+                    off >= 0 ? IO<T>::load4(qk, off + k) : (f32x4){0.f, 0.f, 0.f, 0.f};
+            }
         }
         __syncthreads();
         if (it >= gn) continue;
@@ -848,13 +896,16 @@ static hipError_t launch_scan(const T* qk, const Dims& d, int32_t* buckets, cons
     const unsigned z = (unsigned)std::min<int64_t>(16, (cap + 63) / 64);
     // one row of blocks per R round, and one more for the public count
     const dim3 sgrid = grid_split((unsigned)hash_ntiles(d) * z, (int64_t)d.nr + 1);
+    // prefetch the first group when the launch is small (at most 512 blocks)
+    const int spec = (int64_t)hash_ntiles(d) * z * d.nr <= 512;
     if (d.d == 64)
         hash_scan_kernel<64, T><<<sgrid, 256, 0, st>>>(qk, w.rt, d, w.scount, w.slist, w.sbest, cap,
-                                                       buckets, w.rcount, nregions, w.counter);
+                                                       buckets, w.rcount, nregions, w.counter,
+                                                       spec);
     else
         hash_scan_kernel<128, T><<<sgrid, 256, 0, st>>>(qk, w.rt, d, w.scount, w.slist, w.sbest,
                                                         cap, buckets, w.rcount, nregions,
-                                                        w.counter);
+                                                        w.counter, spec);
     if (hash_ntiles(d) > 1)
         hash_scan_finish_kernel<<<grid_split(4, d.nr), 256, 0, st>>>(w.scount, w.slist, w.sbest,
                                                                      cap, d.nr, buckets);

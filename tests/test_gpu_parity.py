@@ -133,6 +133,23 @@ def test_hash_exact_ties_and_zero_rows(dtype, d, nb):
     assert refined >= 2 * 17 + 8
 
 
+@pytest.mark.parametrize("dtype,nb", [("bf16", 64), ("fp32", 64), ("bf16", 1024)])
+def test_hash_many_full_scans(dtype, nb):
+    """2500 zero rows tie in every column of both rounds: more full-scan items
+    in one round than the scan kernel's first group pass covers (16 groups of
+    64), so its later-group path runs too; every other row as the oracle."""
+    w = _wl(dtype, L=4096, H=1, d=64, nb=nb, nh=2, m=1)
+    qk, v, R, qk_t, v_t, R_t = _tensors(w)
+    qk[0, 0, :2500] = 0.0
+    qk_t = torch.from_numpy(qk).to(DEV, qk_t.dtype)
+    buckets, refined = lsh.hash(qk_t, R_t, nb)
+    ref, margin = _oracle_hash(qk, R, nb)
+    near, differ = _check_buckets(buckets.cpu().numpy(), ref, margin)
+    assert (buckets.cpu().numpy()[0, 0, :, :2500] == 0).all()
+    assert refined >= 2 * 2500
+    print(f"many full scans {dtype} nb={nb}: re-decided {refined}, near-ties {near}, differ {differ}")
+
+
 # the last three cases span many sort tiles (64K, 64K plus a ragged tail, 96K)
 SORT_CASES = [("uniform", 1024, 4096 + 192), ("uniform", 64, 4096 * 3), ("skewed", 256, 16384),
               ("constant", 64, 5000 // 8 * 8), ("uniform", 4096, 8192), ("uniform", 2, 100),
