@@ -1,0 +1,114 @@
+"""The fused forward against the oracle on seeded random shapes.
+
+The forward picks its kernels and launch widths from the shape (one or
+several sort launches, the scatter's wave count, the chunk pass's run length,
+the combine's round group). The hand-picked cases elsewhere name each choice;
+these draws, from one fixed seed over the sizes the boundary accepts, meet
+combinations none of them names: odd bucket counts, one to nine rounds, chunk
+lengths from 16 to 128, ragged chunk counts, both I/O dtypes and both method
+flags. Each case compares every (batch, head) slice whose bucket ids equal the
+oracle's (a near-tie may go either way: the hash tests bound those) with the
+oracle's output, at the bars of the other parity tests: max-abs 1e-4 for fp32
+I/O, 2e-2 for bf16.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import oracle
+
+lsh = pytest.importorskip("lsh_attention_fp32_amd")
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL = {"fp32": 1e-4, "bf16": 2e-2}
+
+
+# Three families: small problems over the whole range of sizes; many short
+# segments (hundreds to a few thousand (batch, head, round) triples, where
+# the sort and chunk launches switch to their many-segment forms); and long
+# sequences spanning several sort tiles.
+FAMILIES = {
+    "small": dict(n=32, m=(16, 32, 64, 64, 64, 128), chunks=(1, 40), nh=(1, 9), B=(1, 3),
+                  H=(1, 4), cap=120_000),
+    "many": dict(n=12, m=(32, 64, 64), chunks=(1, 12), nh=(8, 32), B=(1, 4), H=(16, 64),
+                 cap=1_500_000),
+    "long": dict(n=8, m=(64, 64, 128), chunks=(64, 320), nh=(1, 4), B=(1, 2), H=(1, 2),
+                 cap=400_000),
+}
+
+
+def _draw(family, seed):
+    f = FAMILIES[family]
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < f["n"]:
+        dtype = "fp32" if rng.random() < 0.25 else "bf16"
+        d = int(rng.choice([64, 128]))
+        m = int(rng.choice(f["m"]))
+        L = m * int(rng.integers(f["chunks"][0], f["chunks"][1] + 1))
+        nb = 2 * int(round(np.exp(rng.uniform(0.0, np.log(2048.0)))))   # 2 ... 4096
+        nh = int(rng.integers(f["nh"][0], f["nh"][1] + 1))
+        B = int(rng.integers(f["B"][0], f["B"][1] + 1))
+        H = int(rng.integers(f["H"][0], f["H"][1] + 1))
+        causal = bool(rng.integers(0, 2))
+        dist = "clusters" if rng.random() < 0.3 else "normal"
+        per_head = bool(rng.random() < 0.25)
+        key_norm = bool(rng.random() < 0.25)
+        # token-rounds, and the oracle's multiply-adds (a few seconds at most)
+        if B * H * nh * L > f["cap"] or B * H * nh * L * (nb + 4 * m) * d > 4e10:
+            continue
+        i = len(cases)
+        name = (f"{family}{i}_{dtype}_b{B}h{H}l{L}d{d}_nb{nb}nh{nh}m{m}"
+                f"{'_causal' if causal else ''}{'_perhead' if per_head else ''}"
+                f"{'_keynorm' if key_norm else ''}_{dist}")
+        w = workloads.Workload(name, B, H, L, d, dtype, nb, nh, m, causal, seed + 1 + i, dist)
+        cases.append((w, per_head, key_norm))
+    return cases
+
+
+CASES = _draw("small", 20261204) + _draw("many", 20261205) + _draw("long", 20261206)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lsh.load_library()
+
+
+@pytest.mark.parametrize("w,per_head,key_norm", CASES, ids=[c[0].name for c in CASES])
+def test_random_shape_forward_matches_oracle(w, per_head, key_norm):
+    qk, v, R = workloads.make_inputs(w)
+    if per_head:
+        R = np.random.default_rng(w.seed + 1).standard_normal(
+            (w.H, w.n_hashes, w.d, w.n_buckets // 2), dtype=np.float32)
+    dt = torch.float32 if w.dtype == "fp32" else torch.bfloat16
+    qk_t = torch.from_numpy(qk).to(DEV, dt)
+    v_t = torch.from_numpy(v).to(DEV, dt)
+    R_t = torch.from_numpy(R).to(DEV)
+    ref, extra = oracle.forward(qk, v, R, w.n_buckets, w.chunk_len, w.causal, return_all=True,
+                                key_norm=key_norm)
+    buckets, _ = lsh.hash(qk_t, R_t, w.n_buckets)
+    gb = buckets.cpu().numpy()
+    differ = gb != extra["buckets"]
+    assert not np.any(differ & (extra["margin"] >= 1e-9)), "bucket ids differ above margin 1e-9"
+    out = torch.full_like(qk_t, float("nan"))
+    lsh.attention_fwd(qk_t, v_t, R_t, w.n_buckets, w.chunk_len, w.causal, out=out,
+                      key_norm=key_norm)
+    got = out.float().cpu().numpy()
+    assert np.isfinite(got).all()
+    worst, compared = 0.0, 0
+    for b in range(w.B):
+        for h in range(w.H):
+            if differ[b, h].any():
+                continue
+            compared += 1
+            worst = max(worst, float(np.abs(got[b, h] - ref[b, h]).max()))
+    print(f"{w.name}: slices compared {compared} of {w.B * w.H}, max |err| {worst:.2e}")
+    assert compared >= 1
+    assert worst <= TOL[w.dtype]
