@@ -9,7 +9,9 @@ lengths from 16 to 128, ragged chunk counts, both I/O dtypes and both method
 flags. Each case compares every (batch, head) slice whose bucket ids equal the
 oracle's (a near-tie may go either way: the hash tests bound those) with the
 oracle's output, at the bars of the other parity tests: max-abs 1e-4 for fp32
-I/O, 2e-2 for bf16.
+I/O, 2e-2 for bf16. A fourth family runs the training forward and the
+backward against the oracle's gradients, relative to the largest gradient
+entry of each slice at the same bars.
 """
 from __future__ import annotations
 
@@ -39,6 +41,9 @@ FAMILIES = {
                  cap=1_500_000),
     "long": dict(n=8, m=(64, 64, 128), chunks=(64, 320), nh=(1, 4), B=(1, 2), H=(1, 2),
                  cap=400_000),
+    # the backward: training forward and gradients
+    "bwd": dict(n=16, m=(16, 32, 64, 64, 64, 128), chunks=(1, 40), nh=(1, 8), B=(1, 3),
+                H=(1, 6), cap=60_000),
 }
 
 
@@ -72,6 +77,7 @@ def _draw(family, seed):
 
 
 CASES = _draw("small", 20261204) + _draw("many", 20261205) + _draw("long", 20261206)
+BWD_CASES = _draw("bwd", 20261207)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -110,5 +116,46 @@ def test_random_shape_forward_matches_oracle(w, per_head, key_norm):
             compared += 1
             worst = max(worst, float(np.abs(got[b, h] - ref[b, h]).max()))
     print(f"{w.name}: slices compared {compared} of {w.B * w.H}, max |err| {worst:.2e}")
+    assert compared >= 1
+    assert worst <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("w,per_head,key_norm", BWD_CASES, ids=[c[0].name for c in BWD_CASES])
+def test_random_shape_backward_matches_oracle(w, per_head, key_norm):
+    qk, v, R = workloads.make_inputs(w)
+    if per_head:
+        R = np.random.default_rng(w.seed + 1).standard_normal(
+            (w.H, w.n_hashes, w.d, w.n_buckets // 2), dtype=np.float32)
+    g = np.random.default_rng(w.seed + 2).standard_normal(qk.shape, dtype=np.float32)
+    if w.dtype == "bf16":
+        g = workloads.round_to_bf16(g)
+    dt = torch.float32 if w.dtype == "fp32" else torch.bfloat16
+    qk_t = torch.from_numpy(qk).to(DEV, dt)
+    v_t = torch.from_numpy(v).to(DEV, dt)
+    R_t = torch.from_numpy(R).to(DEV)
+    g_t = torch.from_numpy(g).to(DEV, dt)
+    _, extra = oracle.forward(qk, v, R, w.n_buckets, w.chunk_len, w.causal, return_all=True,
+                              key_norm=key_norm)
+    ref_dqk, ref_dv = oracle.backward(qk, v, R, g, w.n_buckets, w.chunk_len, w.causal,
+                                      key_norm=key_norm)
+    out, state = lsh.attention_fwd_train(qk_t, v_t, R_t, w.n_buckets, w.chunk_len, w.causal,
+                                         key_norm=key_norm)
+    dqk, dv = lsh.attention_bwd(qk_t, v_t, out, g_t, state, w.n_buckets, w.n_hashes,
+                                w.chunk_len, w.causal, key_norm=key_norm)
+    gb, _ = lsh.hash(qk_t, R_t, w.n_buckets)
+    differ = gb.cpu().numpy() != extra["buckets"]
+    assert not np.any(differ & (extra["margin"] >= 1e-9)), "bucket ids differ above margin 1e-9"
+    got_dqk = dqk.float().cpu().numpy()
+    got_dv = dv.float().cpu().numpy()
+    assert np.isfinite(got_dqk).all() and np.isfinite(got_dv).all()
+    worst, compared = 0.0, 0
+    for b in range(w.B):
+        for h in range(w.H):
+            if differ[b, h].any():
+                continue
+            compared += 1
+            for got, ref in ((got_dqk[b, h], ref_dqk[b, h]), (got_dv[b, h], ref_dv[b, h])):
+                worst = max(worst, float(np.abs(got - ref).max()) / float(np.abs(ref).max()))
+    print(f"{w.name}: slices compared {compared} of {w.B * w.H}, worst relative {worst:.2e}")
     assert compared >= 1
     assert worst <= TOL[w.dtype]
