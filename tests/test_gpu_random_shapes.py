@@ -11,7 +11,9 @@ oracle's (a near-tie may go either way: the hash tests bound those) with the
 oracle's output, at the bars of the other parity tests: max-abs 1e-4 for fp32
 I/O, 2e-2 for bf16. A fourth family runs the training forward and the
 backward against the oracle's gradients, relative to the largest gradient
-entry of each slice at the same bars.
+entry of each slice at the same bars; a fifth, separate queries and keys
+against the oracle's forward for that variant, where a query whose windows
+hold no key of its bucket gets a zero row.
 """
 from __future__ import annotations
 
@@ -44,6 +46,9 @@ FAMILIES = {
     # the backward: training forward and gradients
     "bwd": dict(n=16, m=(16, 32, 64, 64, 64, 128), chunks=(1, 40), nh=(1, 8), B=(1, 3),
                 H=(1, 6), cap=60_000),
+    # separate queries and keys (key normalisation does not apply there)
+    "sep": dict(n=16, m=(16, 32, 64, 64, 64, 128), chunks=(1, 40), nh=(1, 9), B=(1, 3),
+                H=(1, 6), cap=120_000),
 }
 
 
@@ -63,7 +68,7 @@ def _draw(family, seed):
         causal = bool(rng.integers(0, 2))
         dist = "clusters" if rng.random() < 0.3 else "normal"
         per_head = bool(rng.random() < 0.25)
-        key_norm = bool(rng.random() < 0.25)
+        key_norm = bool(rng.random() < 0.25) and family != "sep"
         # token-rounds, and the oracle's multiply-adds (a few seconds at most)
         if B * H * nh * L > f["cap"] or B * H * nh * L * (nb + 4 * m) * d > 4e10:
             continue
@@ -78,6 +83,7 @@ def _draw(family, seed):
 
 CASES = _draw("small", 20261204) + _draw("many", 20261205) + _draw("long", 20261206)
 BWD_CASES = _draw("bwd", 20261207)
+SEP_CASES = [(w, ph) for w, ph, _ in _draw("sep", 20261208)]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -157,5 +163,47 @@ def test_random_shape_backward_matches_oracle(w, per_head, key_norm):
             for got, ref in ((got_dqk[b, h], ref_dqk[b, h]), (got_dv[b, h], ref_dv[b, h])):
                 worst = max(worst, float(np.abs(got - ref).max()) / float(np.abs(ref).max()))
     print(f"{w.name}: slices compared {compared} of {w.B * w.H}, worst relative {worst:.2e}")
+    assert compared >= 1
+    assert worst <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("w,per_head", SEP_CASES, ids=[c[0].name for c in SEP_CASES])
+def test_random_shape_separate_qk_matches_oracle(w, per_head):
+    q, k, v, R = workloads.make_separate_inputs(w)
+    if per_head:
+        R = np.random.default_rng(w.seed + 1).standard_normal(
+            (w.H, w.n_hashes, w.d, w.n_buckets // 2), dtype=np.float32)
+    dt = torch.float32 if w.dtype == "fp32" else torch.bfloat16
+    q_t = torch.from_numpy(q).to(DEV, dt)
+    k_t = torch.from_numpy(k).to(DEV, dt)
+    v_t = torch.from_numpy(v).to(DEV, dt)
+    R_t = torch.from_numpy(R).to(DEV)
+    ref, extra = oracle.forward_qk(q, k, v, R, w.n_buckets, w.chunk_len, w.causal,
+                                   return_all=True)
+    gq, _ = lsh.hash(q_t, R_t, w.n_buckets)
+    gk, _ = lsh.hash(k_t, R_t, w.n_buckets)
+    differ = np.zeros((w.B, w.H), bool)
+    for g, side in ((gq, "q"), (gk, "k")):
+        d = g.cpu().numpy() != extra[f"buckets_{side}"]
+        assert not np.any(d & (extra[f"margin_{side}"] >= 1e-9)), \
+            f"{side} bucket ids differ above margin 1e-9"
+        differ |= d.any(axis=(2, 3))
+    out = torch.full_like(q_t, float("nan"))
+    lsh.attention_fwd_qk(q_t, k_t, v_t, R_t, w.n_buckets, w.chunk_len, w.causal, out=out)
+    got = out.float().cpu().numpy()
+    assert np.isfinite(got).all()
+    # positions none of whose rounds has a key: zero rows on both sides
+    none = np.isneginf(np.take_along_axis(extra["lse"], extra["inv_q"].astype(np.int64),
+                                          axis=3)).all(axis=2)
+    worst, compared = 0.0, 0
+    for b in range(w.B):
+        for h in range(w.H):
+            if differ[b, h]:
+                continue
+            compared += 1
+            worst = max(worst, float(np.abs(got[b, h] - ref[b, h]).max()))
+            assert np.all(got[b, h][none[b, h]] == 0)
+    print(f"{w.name}: slices compared {compared} of {w.B * w.H}, queries with no key "
+          f"{int(none.sum())}, max |err| {worst:.2e}")
     assert compared >= 1
     assert worst <= TOL[w.dtype]
