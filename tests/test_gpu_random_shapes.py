@@ -13,7 +13,9 @@ I/O, 2e-2 for bf16. A fourth family runs the training forward and the
 backward against the oracle's gradients, relative to the largest gradient
 entry of each slice at the same bars; a fifth, separate queries and keys
 against the oracle's forward for that variant, where a query whose windows
-hold no key of its bucket gets a zero row.
+hold no key of its bucket gets a zero row. The sort entry point on its
+own, bit-exact against the oracle, takes a sixth family of random lengths,
+bucket counts and id distributions.
 """
 from __future__ import annotations
 
@@ -84,6 +86,33 @@ def _draw(family, seed):
 CASES = _draw("small", 20261204) + _draw("many", 20261205) + _draw("long", 20261206)
 BWD_CASES = _draw("bwd", 20261207)
 SEP_CASES = [(w, ph) for w, ph, _ in _draw("sep", 20261208)]
+
+
+def _draw_sort(n, seed, H=(1, 8), nh=(1, 8), Lmax=98304, max_slots=3_000_000, tag="sort"):
+    """(name, B, H, nh, L, nb, kind, seed): lengths 1 to Lmax and bucket counts
+    2 to 4096, both log-uniform, ids uniform, skewed (30 % in one bucket) or
+    all equal."""
+    Hr, nhr = H, nh
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        B = int(rng.integers(1, 4))
+        H = int(rng.integers(Hr[0], Hr[1] + 1))
+        nh = int(rng.integers(nhr[0], nhr[1] + 1))
+        L = int(round(np.exp(rng.uniform(0.0, np.log(float(Lmax))))))
+        nb = 2 * int(round(np.exp(rng.uniform(0.0, np.log(2048.0)))))
+        kind = str(rng.choice(["uniform", "uniform", "skewed", "constant"]))
+        if B * H * nh * L > max_slots:
+            continue
+        i = len(cases)
+        cases.append((f"{tag}{i}_{kind}_b{B}h{H}nh{nh}l{L}_nb{nb}", B, H, nh, L, nb, kind,
+                      seed + 1 + i))
+    return cases
+
+
+# the second family: hundreds to thousands of short segments
+SORT_CASES = (_draw_sort(24, 20261209) +
+              _draw_sort(8, 20261210, H=(16, 64), nh=(8, 32), Lmax=1024, tag="sortmany"))
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -207,3 +236,24 @@ def test_random_shape_separate_qk_matches_oracle(w, per_head):
           f"{int(none.sum())}, max |err| {worst:.2e}")
     assert compared >= 1
     assert worst <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("name,B,H,nh,L,nb,kind,seed", SORT_CASES, ids=[c[0] for c in SORT_CASES])
+def test_random_shape_sort_matches_oracle(name, B, H, nh, L, nb, kind, seed):
+    rng = np.random.default_rng(seed)
+    shape = (B, H, nh, L)
+    if kind == "uniform":
+        b = rng.integers(0, nb, shape)
+    elif kind == "skewed":
+        b = np.where(rng.random(shape) < 0.3, nb // 3, rng.integers(0, nb, shape))
+    else:
+        b = np.full(shape, int(rng.integers(0, nb)))
+    b = b.astype(np.int32)
+    perm, inv = lsh.sort(torch.from_numpy(b).to(DEV), nb)
+    perm, inv = perm.cpu().numpy(), inv.cpu().numpy()
+    for bi in range(B):
+        for h in range(H):
+            for r in range(nh):
+                p_ref, i_ref = oracle.sort(b[bi, h, r])
+                assert np.array_equal(perm[bi, h, r], p_ref), (bi, h, r)
+                assert np.array_equal(inv[bi, h, r], i_ref), (bi, h, r)
