@@ -15,7 +15,9 @@ entry of each slice at the same bars; a fifth, separate queries and keys
 against the oracle's forward for that variant, where a query whose windows
 hold no key of its bucket gets a zero row. The sort entry point on its
 own, bit-exact against the oracle, takes a sixth family of random lengths,
-bucket counts and id distributions.
+bucket counts and id distributions; the projections and the chunked
+feed-forward take random widths, row counts and chunkings, at the bars their
+own tests derive from the arithmetic.
 """
 from __future__ import annotations
 
@@ -257,3 +259,83 @@ def test_random_shape_sort_matches_oracle(name, B, H, nh, L, nb, kind, seed):
                 p_ref, i_ref = oracle.sort(b[bi, h, r])
                 assert np.array_equal(perm[bi, h, r], p_ref), (bi, h, r)
                 assert np.array_equal(inv[bi, h, r], i_ref), (bi, h, r)
+
+
+def _draw_dense(n, seed, kind):
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        dtype = "fp32" if rng.random() < 0.3 else "bf16"
+        dm = 8 * int(rng.integers(1, 129))
+        if kind == "proj":
+            # token counts: half log-uniform (small and ragged), half several tiles
+            B = int(rng.integers(1, 4))
+            L = (int(round(np.exp(rng.uniform(0.0, np.log(1500.0))))) if rng.random() < 0.5
+                 else int(rng.integers(256, 1501)))
+            H, d = int(rng.integers(1, 9)), int(rng.choice([64, 128]))
+            if B * L * dm * H * d > 3e9:
+                continue
+            cases.append((f"proj{len(cases)}_{dtype}_b{B}l{L}dm{dm}h{H}d{d}", dtype, B, L, dm, H,
+                          d, seed + 1 + len(cases)))
+        else:
+            rows = (int(round(np.exp(rng.uniform(0.0, np.log(3000.0))))) if rng.random() < 0.5
+                    else int(rng.integers(256, 3001)))
+            dff = 8 * int(rng.integers(1, 513))
+            chunk = int(rng.integers(1, rows + 1))
+            bias = bool(rng.integers(0, 2))
+            if rows * dm * dff > 6e9:
+                continue
+            cases.append((f"ffn{len(cases)}_{dtype}_rows{rows}dm{dm}dff{dff}c{chunk}"
+                          f"{'_bias' if bias else ''}", dtype, rows, dm, dff, chunk, bias,
+                          seed + 1 + len(cases)))
+    return cases
+
+
+PROJ_CASES = _draw_dense(12, 20261211, "proj")
+FFN_CASES = _draw_dense(12, 20261212, "ffn")
+
+
+def _io(a, dtype):
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return workloads.round_to_bf16(a) if dtype == "bf16" else a
+
+
+@pytest.mark.parametrize("name,dtype,B,L,dm,H,d,seed", PROJ_CASES, ids=[c[0] for c in PROJ_CASES])
+def test_random_shape_projection_matches_oracle(name, dtype, B, L, dm, H, d, seed):
+    rng = np.random.default_rng(seed)
+    x = _io(rng.standard_normal((B, L, dm), dtype=np.float32), dtype)
+    w_qk = _io(rng.standard_normal((H * d, dm), dtype=np.float32) / np.sqrt(dm), dtype)
+    w_v = _io(rng.standard_normal((H * d, dm), dtype=np.float32) / np.sqrt(dm), dtype)
+    dt = torch.float32 if dtype == "fp32" else torch.bfloat16
+    qk_t, v_t = lsh.qkv_project(*(torch.from_numpy(a).to(DEV, dt) for a in (x, w_qk, w_v)), H)
+    ref_qk, ref_v = oracle.project(x, w_qk, w_v, H)
+    # sum_k |x_k w_k| per output: the scale of the fp32 accumulation error;
+    # bf16 outputs are rounded once more (2^-9 relative)
+    mag_qk, mag_v = oracle.project(np.abs(x), np.abs(w_qk), np.abs(w_v), H)
+    rel = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -23
+    for got_t, ref, mag in ((qk_t, ref_qk, mag_qk), (v_t, ref_v, mag_v)):
+        got = got_t.float().cpu().numpy()
+        assert np.isfinite(got).all()
+        assert np.all(np.abs(got - ref) <= rel * np.abs(ref) + 2.0 ** -16 * mag)
+
+
+@pytest.mark.parametrize("name,dtype,rows,dm,dff,chunk,bias,seed", FFN_CASES,
+                         ids=[c[0] for c in FFN_CASES])
+def test_random_shape_ffn_matches_oracle(name, dtype, rows, dm, dff, chunk, bias, seed):
+    rng = np.random.default_rng(seed)
+    x = _io(rng.standard_normal((rows, dm), dtype=np.float32), dtype)
+    w1 = _io(rng.standard_normal((dff, dm), dtype=np.float32) / np.sqrt(dm), dtype)
+    w2 = _io(rng.standard_normal((dm, dff), dtype=np.float32) / np.sqrt(dff), dtype)
+    b1 = _io(rng.standard_normal(dff, dtype=np.float32) * 0.1, dtype) if bias else None
+    b2 = _io(rng.standard_normal(dm, dtype=np.float32) * 0.1, dtype) if bias else None
+    dt = torch.float32 if dtype == "fp32" else torch.bfloat16
+    dev = [None if a is None else torch.from_numpy(a).to(DEV, dt) for a in (x, w1, b1, w2, b2)]
+    got = lsh.ffn(*dev, chunk).float().cpu().numpy()
+    ref = oracle.ffn(x, w1, b1, w2, b2, chunk)
+    # hidden activations and output rounded to the I/O dtype, fp32 sums:
+    # |gpu - ref| <= rel (|ref| + sum_f |h_f w2[o, f]|) + 1e-6
+    h = x.astype(np.float64) @ w1.T.astype(np.float64) + (0.0 if b1 is None else b1)
+    S = np.maximum(h, 0.0) @ np.abs(w2.astype(np.float64)).T
+    rel = 2.0 ** -8 if dtype == "bf16" else 2e-5
+    assert np.isfinite(got).all()
+    assert np.all(np.abs(got - ref) <= rel * (np.abs(ref) + S) + 1e-6)
