@@ -17,7 +17,9 @@ hold no key of its bucket gets a zero row. The sort entry point on its
 own, bit-exact against the oracle, takes a sixth family of random lengths,
 bucket counts and id distributions; the projections and the chunked
 feed-forward take random widths, row counts and chunkings, at the bars their
-own tests derive from the arithmetic.
+own tests derive from the arithmetic. Last, the hash on random shapes with
+planted exact ties (duplicated columns of R, rows along them, zero rows),
+where the first of the tied buckets must win as in the oracle.
 """
 from __future__ import annotations
 
@@ -339,3 +341,60 @@ def test_random_shape_ffn_matches_oracle(name, dtype, rows, dm, dff, chunk, bias
     rel = 2.0 ** -8 if dtype == "bf16" else 2e-5
     assert np.isfinite(got).all()
     assert np.all(np.abs(got - ref) <= rel * (np.abs(ref) + S) + 1e-6)
+
+
+def _draw_ties(n=10, seed=20261213):
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        dtype = "fp32" if rng.random() < 0.3 else "bf16"
+        d = int(rng.choice([64, 128]))
+        nb = 2 * int(round(np.exp(rng.uniform(np.log(2.0), np.log(2048.0)))))   # 4 ... 4096
+        nh = int(rng.integers(1, 5))
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+        L = int(round(np.exp(rng.uniform(np.log(64.0), np.log(8192.0)))))
+        if B * H * nh * L * nb * d > 2e10:
+            continue
+        i = len(cases)
+        cases.append((f"ties{i}_{dtype}_b{B}h{H}l{L}d{d}_nb{nb}nh{nh}",
+                      workloads.Workload(f"ties{i}", B, H, L, d, dtype, nb, nh, 1, False,
+                                         seed + 1 + i)))
+    return cases
+
+
+TIE_CASES = _draw_ties()
+
+
+@pytest.mark.parametrize("name,w", TIE_CASES, ids=[c[0] for c in TIE_CASES])
+def test_random_shape_hash_exact_ties(name, w):
+    qk, _, R = workloads.make_inputs(w)
+    rng = np.random.default_rng(w.seed + 3)
+    half = w.n_buckets // 2
+    # per round, up to four columns copied onto later ones: exact ties
+    pairs = []
+    for r in range(w.n_hashes):
+        for _ in range(min(4, half // 2)):
+            c1, c2 = sorted(int(c) for c in rng.choice(half, 2, replace=False))
+            R[r, :, c2] = R[r, :, c1]
+            pairs.append((r, c1))
+    # rows: 10 % zero (every column ties), 10 % along a copied column (+ or -)
+    kind = rng.random((w.B, w.H, w.L))
+    qk[kind < 0.1] = 0.0
+    along = (kind >= 0.1) & (kind < 0.2)
+    for b, h, l in zip(*np.nonzero(along)):
+        r, c = pairs[int(rng.integers(0, len(pairs)))]
+        qk[b, h, l] = R[r, :, c] * (1.0 if rng.random() < 0.5 else -1.0)
+    dt = torch.float32 if w.dtype == "fp32" else torch.bfloat16
+    qk_t = torch.from_numpy(qk).to(DEV, dt)
+    qk = qk_t.float().cpu().numpy()   # the rows as the GPU holds them
+    buckets, refined = lsh.hash(qk_t, torch.from_numpy(R).to(DEV), w.n_buckets)
+    got = buckets.cpu().numpy()
+    ties = 0
+    for b in range(w.B):
+        for h in range(w.H):
+            ref, margin = oracle.hash(qk[b, h], R, w.n_buckets)
+            ok = (got[b, h] == ref) | ((margin > 0) & (margin < 1e-9))
+            assert ok.all(), (b, h, np.argwhere(~ok)[:4].tolist())
+            ties += int((margin == 0).sum())
+    print(f"{name}: exact ties {ties}, re-decided {refined}")
+    assert ties > 0
